@@ -1,0 +1,161 @@
+"""TEST INFRASTRUCTURE ONLY: the fp64 CPU oracle.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports it, and it imports nothing from them.
+
+The arithmetic lives in ``linattn_oracle.c`` (plain C, double precision,
+sequential token loops, OpenMP only across independent heads).  This module
+builds it with gcc when ``liboracle.so`` is missing and marshals arrays.
+
+Functions and what pins them (the pins are in ``tests/test_oracle_pins.py``):
+
+``la_forward``   -- normalized causal ELU+1 linear attention, write-then-read.
+    Pinned by the seed-7 run printed on the LinearMem page (§04), the
+    quadratic masked form on small inputs (brute force), the T = 1 and
+    identical-key closed forms, the LA-SSM page's 4-token additive example
+    and the memory-capacity page's two-entry example (identity feature map,
+    no normaliser), causality and resume invariants.
+``delta_forward`` -- delta-rule fast weight.  Pinned by the LA-SSM page's
+    4-token delta example (every intermediate state), the LinearMem memory
+    experiment (same key, half beta, crosstalk), the exact-overwrite
+    invariant, the EMA closed form, the dense triangular-solve form via
+    LAPACK, the orthonormal-key reduction to the additive memory and the
+    Kaczmarz limit equal to the memory-capacity page's least-squares W*.
+    The per-token query read o_t = S_t^T q_t is this build's reading (the
+    pages print no such sequence): parity of that read is pinned only by the
+    dense form and the orthonormal-key reduction.
+``la_decode_step`` -- one in-place step; pinned by equality with one token of
+    ``la_forward`` continued from the same state.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "linattn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+PHI_ELU1 = 0
+PHI_IDENTITY = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
+           "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                build()
+            lib = ctypes.CDLL(_LIB_PATH)
+            dp = ctypes.POINTER(ctypes.c_double)
+            i = ctypes.c_int
+            lib.la_ref_forward.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp,
+                                           i, i, i, i, i, ctypes.c_double, i, i]
+            lib.la_ref_forward.restype = None
+            lib.delta_ref_forward.argtypes = [dp, dp, dp, dp, dp, dp, dp,
+                                              i, i, i, i, i]
+            lib.delta_ref_forward.restype = None
+            lib.la_ref_decode_step.argtypes = [dp, dp, dp, dp, dp, dp,
+                                               i, i, i, i, ctypes.c_double]
+            lib.la_ref_decode_step.restype = None
+            lib.oracle_phi.argtypes = [dp, dp, ctypes.c_long]
+            lib.oracle_phi.restype = None
+            lib.oracle_num_threads.argtypes = []
+            lib.oracle_num_threads.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _f64(x):
+    """Exact upcast to a contiguous float64 array (torch or numpy input)."""
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor: bf16/fp32 -> fp64 is exact
+        x = x.detach().to("cpu").double().contiguous().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def phi(x):
+    x = _f64(x)
+    y = np.empty_like(x)
+    _load().oracle_phi(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def la_forward(q, k, v, S0=None, z0=None, eps=1e-6,
+               feature=PHI_ELU1, normalize=True):
+    """q, k: [B,H,T,dk]; v: [B,H,T,dv] -> (o [B,H,T,dv], S [B,H,dk,dv], z [B,H,dk])."""
+    q, k, v, S0, z0 = map(_f64, (q, k, v, S0, z0))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and v.shape[:3] == (B, H, T)
+    if S0 is not None:
+        assert S0.shape == (B, H, dk, dv)
+    if z0 is not None:
+        assert z0.shape == (B, H, dk)
+    o = np.empty((B, H, T, dv))
+    S = np.empty((B, H, dk, dv))
+    z = np.empty((B, H, dk))
+    _load().la_ref_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(S0), _ptr(z0),
+                           _ptr(o), _ptr(S), _ptr(z), B, H, T, dk, dv,
+                           float(eps), int(feature), 1 if normalize else 0)
+    return o, S, z
+
+
+def delta_forward(q, k, v, beta, S0=None):
+    """q, k: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T] -> (o [B,H,T,dv], S [B,H,dk,dv])."""
+    q, k, v, beta, S0 = map(_f64, (q, k, v, beta, S0))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and v.shape[:3] == (B, H, T) and beta.shape == (B, H, T)
+    if S0 is not None:
+        assert S0.shape == (B, H, dk, dv)
+    o = np.empty((B, H, T, dv))
+    S = np.empty((B, H, dk, dv))
+    _load().delta_ref_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0),
+                              _ptr(o), _ptr(S), B, H, T, dk, dv)
+    return o, S
+
+
+def la_decode_step(q, k, v, S, z, eps=1e-6):
+    """One step on copies of (S, z).  q, k: [N,H,dk]; v: [N,H,dv];
+    S: [N,H,dk,dv]; z: [N,H,dk] -> (o [N,H,dv], S_new, z_new)."""
+    q, k, v = map(_f64, (q, k, v))
+    S = _f64(S).copy()
+    z = _f64(z).copy()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    assert S.shape == (N, H, dk, dv) and z.shape == (N, H, dk)
+    o = np.empty((N, H, dv))
+    _load().la_ref_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z),
+                               _ptr(o), N, H, dk, dv, float(eps))
+    return o, S, z

@@ -1,0 +1,204 @@
+/*
+ * TEST INFRASTRUCTURE ONLY -- the fp64 CPU oracle for causal kernelized linear
+ * attention and the delta-rule fast-weight memory.
+ *
+ * Only tests/, the smoke check and the benchmark's CPU-baseline leg may load
+ * this library.  The product path (the HIP library) never links, calls or
+ * includes anything here, and this file includes nothing from it.
+ *
+ * Every function is the plain sequential token recurrence in double
+ * precision, one (batch, head) pair at a time, written from these pages:
+ *
+ *   [LinearMem]  "AIGC 基本功｜线性、循环与记忆架构-LinearMem" (jefxiong.cn)
+ *   [LA-SSM]     "线性注意力与 SSM:两条技术路线的完整推导" (ggaaooppeenngg.github.io)
+ *   [Recurrence] "手撕：递推与记忆模型" (wineandchord.com)
+ *
+ * Layouts (all row-major, contiguous, host memory, caller-owned):
+ *   q, k   [B][H][T][dk]      v, o  [B][H][T][dv]      beta [B][H][T]
+ *   S      [B][H][dk][dv]     (key-first, as [LinearMem] §03 defines S_t)
+ *   z      [B][H][dk]
+ * A NULL S0 / z0 means a zero initial state.  A NULL S_out / z_out means the
+ * final state is not returned.  Nothing is allocated that outlives a call.
+ *
+ * Parity pins: every function here is checked in tests/ against values the
+ * pages print, brute-force forms and closed-form invariants (see the module
+ * docstring of oracle/__init__.py for the list).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_PHI_ELU1 0     /* phi(u) = u + 1 for u > 0, exp(u) otherwise */
+#define ORACLE_PHI_IDENTITY 1 /* phi(u) = u (plain outer-product memory)    */
+
+/* [LinearMem] §03 "从检索权重开始": the elementwise ELU+1 feature map, with
+ * the two branches exactly as the page states them (u > 0 -> u + 1,
+ * u <= 0 -> exp(u)).  Both branches give 1 at u = 0. */
+static double phi_elu1(double u) { return u > 0.0 ? u + 1.0 : exp(u); }
+
+static double feature(double u, int mode) {
+    return mode == ORACLE_PHI_IDENTITY ? u : phi_elu1(u);
+}
+
+/*
+ * Normalized causal linear attention, write-then-read.
+ *
+ * [LinearMem] §03 "把历史和移到 query 外面": S_t = S_{t-1} + phi(k_t) v_t^T,
+ * z_t = z_{t-1} + phi(k_t), S_0 = 0, z_0 = 0, and the read-out
+ * o_t^T = phi(q_t)^T S_t / (phi(q_t)^T z_t + eps).  The same section fixes the
+ * order: the current token is written before the current query reads.
+ * [LinearMem] §04 shows the same loop in NumPy (state kept in float64).
+ *
+ * Test-only modes reproduce the additive memory of the worked examples:
+ *   feature   = ORACLE_PHI_IDENTITY drops the feature map,
+ *   normalize = 0 returns the raw read phi(q_t)^T S_t (no z, no eps).
+ * With S0/z0 given, the same recurrence continues from them (an initial
+ * state is handed in and the final one returned, [Recurrence] "Selective
+ * scan" / "Delta-rule fast weight").
+ */
+void la_ref_forward(const double* q, const double* k, const double* v,
+                    const double* S0, const double* z0,
+                    double* o, double* S_out, double* z_out,
+                    int B, int H, int T, int dk, int dv, double eps,
+                    int feature_mode, int normalize) {
+    const long heads = (long)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long h = 0; h < heads; ++h) {
+        double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+        double* z = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* fk = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* fq = (double*)malloc(sizeof(double) * (size_t)dk);
+        for (long i = 0; i < (long)dk * dv; ++i) S[i] = S0 ? S0[h * dk * dv + i] : 0.0;
+        for (int i = 0; i < dk; ++i) z[i] = z0 ? z0[h * dk + i] : 0.0;
+        const double* qh = q + h * (long)T * dk;
+        const double* kh = k + h * (long)T * dk;
+        const double* vh = v + h * (long)T * dv;
+        double* oh = o + h * (long)T * dv;
+        for (int t = 0; t < T; ++t) {
+            for (int i = 0; i < dk; ++i) {
+                fk[i] = feature(kh[(long)t * dk + i], feature_mode);
+                fq[i] = feature(qh[(long)t * dk + i], feature_mode);
+            }
+            /* write: S += phi(k_t) v_t^T, z += phi(k_t) */
+            for (int i = 0; i < dk; ++i) {
+                for (int j = 0; j < dv; ++j) S[(long)i * dv + j] += fk[i] * vh[(long)t * dv + j];
+                z[i] += fk[i];
+            }
+            /* read: phi(q_t)^T S_t / (phi(q_t)^T z_t + eps) */
+            double den = 0.0;
+            for (int i = 0; i < dk; ++i) den += fq[i] * z[i];
+            den += eps;
+            for (int j = 0; j < dv; ++j) {
+                double num = 0.0;
+                for (int i = 0; i < dk; ++i) num += fq[i] * S[(long)i * dv + j];
+                oh[(long)t * dv + j] = normalize ? num / den : num;
+            }
+        }
+        if (S_out) memcpy(S_out + h * (long)dk * dv, S, sizeof(double) * (size_t)dk * dv);
+        if (z_out) memcpy(z_out + h * (long)dk, z, sizeof(double) * (size_t)dk);
+        free(S); free(z); free(fk); free(fq);
+    }
+}
+
+/*
+ * Delta-rule fast-weight memory, write-then-read.
+ *
+ * [LinearMem] §03 "从累加改成纠错": one gradient step of size beta_t on
+ * 0.5 * ||S^T k_t - v_t||^2 gives S_t = S_{t-1} + beta_t k_t (v_t^T - k_t^T S_{t-1});
+ * no feature map, no normaliser z.  [Recurrence] "Delta-rule fast weight"
+ * writes the same update with a per-token beta and an optional initial state.
+ *
+ * The pages print no per-token query read for a whole sequence; this oracle
+ * reads o_t = S_t^T q_t after the write, the same write-then-read order
+ * [LinearMem] §03 fixes for linear attention (raw q, no normaliser).
+ */
+void delta_ref_forward(const double* q, const double* k, const double* v,
+                       const double* beta, const double* S0,
+                       double* o, double* S_out,
+                       int B, int H, int T, int dk, int dv) {
+    const long heads = (long)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long h = 0; h < heads; ++h) {
+        double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+        double* u = (double*)malloc(sizeof(double) * (size_t)dv);
+        for (long i = 0; i < (long)dk * dv; ++i) S[i] = S0 ? S0[h * dk * dv + i] : 0.0;
+        const double* qh = q + h * (long)T * dk;
+        const double* kh = k + h * (long)T * dk;
+        const double* vh = v + h * (long)T * dv;
+        const double* bh = beta + h * (long)T;
+        double* oh = o + h * (long)T * dv;
+        for (int t = 0; t < T; ++t) {
+            const double* kt = kh + (long)t * dk;
+            /* correction u = v_t - S_{t-1}^T k_t (new value minus the prediction) */
+            for (int j = 0; j < dv; ++j) {
+                double pred = 0.0;
+                for (int i = 0; i < dk; ++i) pred += kt[i] * S[(long)i * dv + j];
+                u[j] = vh[(long)t * dv + j] - pred;
+            }
+            /* write: S += beta_t k_t u^T */
+            for (int i = 0; i < dk; ++i) {
+                const double bk = bh[t] * kt[i];
+                for (int j = 0; j < dv; ++j) S[(long)i * dv + j] += bk * u[j];
+            }
+            /* read: o_t = S_t^T q_t */
+            for (int j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < dk; ++i) acc += qh[(long)t * dk + i] * S[(long)i * dv + j];
+                oh[(long)t * dv + j] = acc;
+            }
+        }
+        if (S_out) memcpy(S_out + h * (long)dk * dv, S, sizeof(double) * (size_t)dk * dv);
+        free(S); free(u);
+    }
+}
+
+/*
+ * One decode step of normalized linear attention on a resident state,
+ * updated in place: S += phi(k) v^T, z += phi(k), then
+ * o = phi(q)^T S / (phi(q)^T z + eps).  [LinearMem] §03 (the recurrence and
+ * read-out) and §05 (inference keeps the matrix and normaliser state and
+ * updates it in place, one token at a time).
+ *   q, k [N][H][dk]   v, o [N][H][dv]   S [N][H][dk][dv]   z [N][H][dk]
+ */
+void la_ref_decode_step(const double* q, const double* k, const double* v,
+                        double* S, double* z, double* o,
+                        int N, int H, int dk, int dv, double eps) {
+    const long states = (long)N * H;
+#pragma omp parallel for schedule(static)
+    for (long s = 0; s < states; ++s) {
+        const double* qs = q + s * dk;
+        const double* ks = k + s * dk;
+        const double* vs = v + s * dv;
+        double* Ss = S + s * (long)dk * dv;
+        double* zs = z + s * dk;
+        double den = 0.0;
+        for (int i = 0; i < dk; ++i) {
+            const double f = phi_elu1(ks[i]);
+            for (int j = 0; j < dv; ++j) Ss[(long)i * dv + j] += f * vs[j];
+            zs[i] += f;
+        }
+        for (int i = 0; i < dk; ++i) den += phi_elu1(qs[i]) * zs[i];
+        den += eps;
+        for (int j = 0; j < dv; ++j) {
+            double num = 0.0;
+            for (int i = 0; i < dk; ++i) num += phi_elu1(qs[i]) * Ss[(long)i * dv + j];
+            o[s * dv + j] = num / den;
+        }
+    }
+}
+
+/* The feature map alone, so tests can pin its branches directly. */
+void oracle_phi(const double* x, double* y, long n) {
+    for (long i = 0; i < n; ++i) y[i] = phi_elu1(x[i]);
+}
+
+/* Threads OpenMP will use for the loops above (1 when built without it). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

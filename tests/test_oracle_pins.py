@@ -1,0 +1,427 @@
+"""Pins for the fp64 oracle (CPU only).
+
+Each test ties the oracle to something other than itself: values the pages
+print (fixtures under tests/golden/, each with its citation), closed forms,
+brute-force forms on tiny inputs, and invariants.  Together they are chosen
+so that a plausible mistake (dropped eps or z, read-before-write, a wrong
+branch of the feature map, a transposed state, a wrong sign or a misplaced
+beta in the delta correction) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import forms
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        return json.load(f)
+
+
+def _h(x):
+    """Add the batch and head axes: [T, d] -> [1, 1, T, d]."""
+    return np.asarray(x, dtype=np.float64)[None, None]
+
+
+def _la1(q, k, v, **kw):
+    o, S, z = oracle.la_forward(_h(q), _h(k), _h(v), **kw)
+    return o[0, 0], S[0, 0], z[0, 0]
+
+
+def _delta1(q, k, v, beta, S0=None):
+    o, S = oracle.delta_forward(_h(q), _h(k), _h(v), np.asarray(beta, dtype=np.float64)[None, None],
+                                None if S0 is None else S0[None, None])
+    return o[0, 0], S[0, 0]
+
+
+# ----------------------------------------------------------------- feature map
+
+def test_phi_values_printed_on_lassm_page():
+    # "线性注意力与 SSM" §1.2: ELU(0)+1 = 1 and ELU(-3)+1 = e^-3 (about 0.05).
+    y = oracle.phi([0.0, -3.0, 2.5, -0.0])
+    assert y[0] == 1.0
+    assert y[1] == math.exp(-3.0) and abs(y[1] - 0.05) < 0.001
+    assert y[2] == 3.5          # positive branch: u + 1
+    assert y[3] == 1.0
+
+
+def test_phi_positive_everywhere():
+    x = np.linspace(-700.0, 50.0, 10001)
+    y = oracle.phi(x)
+    assert np.all(y > 0)
+    assert np.all(np.diff(y) > 0)  # strictly increasing through the branch change
+
+
+# ------------------------------------------------- LinearMem printed seed-7 run
+
+def _seed7_inputs():
+    rng = np.random.default_rng(7)
+    q = rng.normal(size=(8, 4))
+    k = rng.normal(size=(8, 4))
+    v = rng.normal(size=(8, 3))
+    return q, k, v
+
+
+def test_seed7_printed_run():
+    g = _golden("linearmem_seed7_run.json")
+    q, k, v = _seed7_inputs()
+    o, S, z = _la1(q, k, v, eps=1e-6)
+    assert list(o.shape) == g["output_shape"]
+    assert list(S.shape) == g["state_shape"]
+    assert list(z.shape) == g["normalizer_shape"]
+    np.testing.assert_allclose(o[:2], np.array(g["first_two_outputs_8dp"]), rtol=0, atol=5.1e-9)
+    assert abs(o.min() - g["output_min"]) <= 1e-14
+    assert abs(o.max() - g["output_max"]) <= 1e-14
+    # the page's own acceptance: explicit and recurrent agree below 1e-12
+    assert np.max(np.abs(forms.la_quadratic(q, k, v) - o)) < 1e-12
+
+
+def test_seed7_future_leak():
+    g = _golden("linearmem_seed7_run.json")
+    q, k, v = _seed7_inputs()
+    o, _, _ = _la1(q, k, v)
+    v2 = v.copy()
+    v2[-1] += 100.0
+    o2, _, _ = _la1(q, k, v2)
+    assert float(np.max(np.abs(o2[:-1] - o[:-1]))) == g["future_leak_error"]
+    assert np.max(np.abs(o2[-1] - o[-1])) > 1.0
+
+
+# ------------------------------------------------------- LA brute force / forms
+
+@pytest.mark.parametrize("T,dk,dv,seed,init", [
+    (1, 4, 3, 0, False), (2, 3, 5, 1, False), (17, 8, 4, 2, False),
+    (64, 16, 16, 3, False), (33, 5, 7, 4, True), (64, 8, 12, 5, True)])
+def test_la_matches_quadratic_masked_form(T, dk, dv, seed, init):
+    rng = np.random.default_rng(seed)
+    q, k = rng.normal(size=(T, dk)), rng.normal(size=(T, dk))
+    v = rng.normal(size=(T, dv))
+    S0 = rng.normal(size=(dk, dv)) if init else None
+    z0 = rng.uniform(0.5, 2.0, size=dk) if init else None
+    o, S, z = _la1(q, k, v, S0=None if S0 is None else S0[None, None],
+                   z0=None if z0 is None else z0[None, None])
+    ref = forms.la_quadratic(q, k, v, S0, z0)
+    np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-12)
+    fk = forms.phi(k)
+    S_ref = fk.T @ v + (0 if S0 is None else S0)
+    z_ref = fk.sum(axis=0) + (0 if z0 is None else z0)
+    np.testing.assert_allclose(S, S_ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(z, z_ref, rtol=1e-12, atol=1e-12)
+
+
+def test_la_single_token_closed_form_exposes_eps():
+    # T = 1: o_1 = v_1 * w / (w + eps) with w = phi(q).phi(k).  With very
+    # negative q and k, w is ~1e-10 and eps dominates the denominator.
+    dk = 4
+    q = np.full((1, dk), -12.0)
+    k = np.full((1, dk), -12.0)
+    v = np.array([[1.5, -2.0, 0.25]])
+    w = dk * math.exp(-12.0) * math.exp(-12.0)
+    o, _, _ = _la1(q, k, v, eps=1e-6)
+    np.testing.assert_allclose(o[0], v[0] * w / (w + 1e-6), rtol=1e-13)
+    assert abs(o[0, 0]) < 1e-3  # would be 1.5 without eps
+
+
+def test_la_identical_keys_running_mean():
+    # All keys equal: o_t = (sum_{i<=t} v_i) w / (t w + eps), w = phi(q_t).phi(k).
+    rng = np.random.default_rng(11)
+    T, dk, dv = 20, 6, 5
+    q = rng.normal(size=(T, dk))
+    k = np.tile(rng.normal(size=(1, dk)), (T, 1))
+    v = rng.normal(size=(T, dv))
+    o, _, _ = _la1(q, k, v)
+    fk = np.array([x + 1 if x > 0 else math.exp(x) for x in k[0]])
+    for t in range(T):
+        fq = np.array([x + 1 if x > 0 else math.exp(x) for x in q[t]])
+        w = float(fq @ fk)
+        ref = v[:t + 1].sum(axis=0) * w / ((t + 1) * w + 1e-6)
+        np.testing.assert_allclose(o[t], ref, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("T", [1, 7, 37])
+def test_la_chunked_equals_recurrent_every_chunk_size(T):
+    rng = np.random.default_rng(100 + T)
+    dk, dv = 6, 5
+    q, k = rng.normal(size=(T, dk)), rng.normal(size=(T, dk))
+    v = rng.normal(size=(T, dv))
+    S0, z0 = rng.normal(size=(dk, dv)), rng.uniform(0.5, 2.0, size=dk)
+    o, S, z = _la1(q, k, v, S0=S0[None, None], z0=z0[None, None])
+    for C in range(1, T + 1):
+        oc, Sc, zc = forms.la_chunked(q, k, v, C, S0, z0)
+        np.testing.assert_allclose(oc, o, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(Sc, S, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(zc, z, rtol=1e-12, atol=1e-12)
+
+
+def test_la_causality_every_position():
+    rng = np.random.default_rng(12)
+    T, dk, dv = 24, 4, 3
+    q, k, v = rng.normal(size=(T, dk)), rng.normal(size=(T, dk)), rng.normal(size=(T, dv))
+    o, _, _ = _la1(q, k, v)
+    for s in (0, 5, 23):
+        for which in ("q", "k", "v"):
+            qq, kk, vv = q.copy(), k.copy(), v.copy()
+            {"q": qq, "k": kk, "v": vv}[which][s] += 100.0
+            o2, _, _ = _la1(qq, kk, vv)
+            assert np.array_equal(o2[:s], o[:s])
+            assert not np.array_equal(o2[s], o[s])
+
+
+def test_la_resume_equals_one_call():
+    rng = np.random.default_rng(13)
+    T, T1, dk, dv = 40, 17, 5, 6
+    q, k, v = rng.normal(size=(T, dk)), rng.normal(size=(T, dk)), rng.normal(size=(T, dv))
+    o, S, z = _la1(q, k, v)
+    oa, Sa, za = _la1(q[:T1], k[:T1], v[:T1])
+    ob, Sb, zb = _la1(q[T1:], k[T1:], v[T1:], S0=Sa[None, None], z0=za[None, None])
+    np.testing.assert_allclose(np.concatenate([oa, ob]), o, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(Sb, S, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(zb, z, rtol=1e-13, atol=1e-13)
+
+
+def test_la_heads_are_independent():
+    rng = np.random.default_rng(14)
+    B, H, T, dk, dv = 2, 3, 9, 4, 5
+    q, k = rng.normal(size=(B, H, T, dk)), rng.normal(size=(B, H, T, dk))
+    v = rng.normal(size=(B, H, T, dv))
+    o, S, z = oracle.la_forward(q, k, v)
+    for b in range(B):
+        for h in range(H):
+            oh, Sh, zh = _la1(q[b, h], k[b, h], v[b, h])
+            assert np.array_equal(oh, o[b, h]) and np.array_equal(Sh, S[b, h])
+            assert np.array_equal(zh, z[b, h])
+
+
+# ------------------------------------ additive memory worked examples (pages)
+
+def test_additive_four_token_example_lassm():
+    g = _golden("lassm_four_token_example.json")
+    keys, values = np.array(g["keys"]), np.array(g["values"])
+    for t in range(1, 5):
+        _, S, _ = _la1(keys[:t], keys[:t], values[:t], feature=oracle.PHI_IDENTITY, normalize=False)
+        np.testing.assert_allclose(S, np.array(g["additive_states_value_first"][t - 1]).T, atol=1e-15)
+    # query with k_1 after all four writes
+    q = keys.copy()
+    q[-1] = keys[0]
+    o, _, _ = _la1(q, keys, values, feature=oracle.PHI_IDENTITY, normalize=False)
+    np.testing.assert_allclose(o[-1], g["additive_read_k1"], atol=1e-15)
+
+
+def test_two_entry_example_memory_capacity():
+    g = _golden("memory_capacity_two_entry.json")
+    keys, values = np.array(g["keys"]), np.array(g["values"])
+    q = np.array([keys[0], keys[0]])
+    o, S, _ = _la1(q, keys, values, feature=oracle.PHI_IDENTITY, normalize=False)
+    np.testing.assert_allclose(S, np.array(g["W_value_first"]).T, atol=1e-15)
+    np.testing.assert_allclose(o[-1], g["read_A"], atol=1e-15)
+    q = np.array([keys[1], keys[1]])
+    o, _, _ = _la1(q, keys, values, feature=oracle.PHI_IDENTITY, normalize=False)
+    np.testing.assert_allclose(o[-1], g["read_B"], atol=1e-15)
+
+
+def test_memory_experiment_additive_same_key():
+    g = _golden("linearmem_memory_experiment.json")
+    key, values = np.array(g["key"]), np.array(g["values"])
+    keys = np.array([key, key])
+    o, _, _ = _la1(keys, keys, values, feature=oracle.PHI_IDENTITY, normalize=False)
+    np.testing.assert_allclose(o[-1] / 2.0, g["additive_same_key_read_divided_by_writes"], atol=1e-15)
+
+
+# ---------------------------------------------------------------- delta rule
+
+def test_delta_four_token_example_lassm():
+    g = _golden("lassm_four_token_example.json")
+    keys, values = np.array(g["keys"]), np.array(g["values"])
+    ones = np.ones(4)
+    for t in range(1, 5):
+        _, S = _delta1(keys[:t], keys[:t], values[:t], ones[:t])
+        np.testing.assert_allclose(S, np.array(g["delta_states_value_first"][t - 1]).T, atol=1e-14)
+    q = keys.copy()
+    q[-1] = keys[0]
+    o, _ = _delta1(q, keys, values, ones)
+    np.testing.assert_allclose(o[-1], g["delta_read_k1"], atol=1e-14)
+
+
+def test_memory_experiment_delta_same_key_and_half_beta():
+    g = _golden("linearmem_memory_experiment.json")
+    key, values = np.array(g["key"]), np.array(g["values"])
+    keys = np.array([key, key])
+    o, _ = _delta1(keys, keys, values, [1.0, 1.0])
+    assert o[-1].tolist() == g["delta_same_key_read_beta1"]
+    o, _ = _delta1(keys, keys, values, [0.5, 0.5])
+    assert o[-1].tolist() == g["delta_same_key_read_beta_half"]
+
+
+def test_memory_experiment_crosstalk():
+    g = _golden("linearmem_memory_experiment.json")
+    key, values = np.array(g["key"]), np.array(g["values"])
+    for rho in g["crosstalk_rhos"]:
+        k2 = np.array([rho, math.sqrt(1.0 - rho ** 2)])
+        keys = np.array([key, k2])
+        q = np.array([key, key])  # read the old key after both writes
+        o, _ = _delta1(q, keys, values, [1.0, 1.0])
+        np.testing.assert_allclose(o[-1], [1.0 - rho ** 2, rho], rtol=0, atol=2e-16)
+        if rho == 0.9:
+            assert o[-1][0] == g["crosstalk_rho_0.9_raw_first_component"]
+
+
+def test_delta_exact_overwrite_bitwise_basis_keys():
+    # LinearMem §03: with a unit key and beta = 1 the read of k_t right after the
+    # write returns v_t.  Basis keys and dyadic values make it bit-exact.
+    rng = np.random.default_rng(21)
+    T, dk, dv = 32, 8, 6
+    idx = rng.integers(0, dk, size=T)
+    keys = np.eye(dk)[idx]
+    values = rng.integers(-64, 64, size=(T, dv)) / 8.0
+    S0 = rng.integers(-64, 64, size=(dk, dv)) / 16.0
+    o, _ = _delta1(keys, keys, values, np.ones(T), S0=S0)
+    assert np.array_equal(o, values)
+
+
+def test_delta_overwrite_invariant_general_beta():
+    # k_t^T S_t = (1 - beta_t) k_t^T S_{t-1} + beta_t v_t^T for unit k_t.
+    rng = np.random.default_rng(22)
+    T, dk, dv = 12, 5, 4
+    k = rng.normal(size=(T, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    q, v = rng.normal(size=(T, dk)), rng.normal(size=(T, dv))
+    beta = rng.uniform(0.05, 1.0, size=T)
+    S0 = rng.normal(size=(dk, dv))
+    prev = S0
+    for t in range(1, T + 1):
+        _, S = _delta1(q[:t], k[:t], v[:t], beta[:t], S0=S0)
+        lhs = k[t - 1] @ S
+        rhs = (1 - beta[t - 1]) * (k[t - 1] @ prev) + beta[t - 1] * v[t - 1]
+        np.testing.assert_allclose(lhs, rhs, rtol=1e-13, atol=1e-14)
+        prev = S
+    o, _ = _delta1(k, k, v, np.ones(T), S0=S0)  # beta = 1: read returns v_t
+    np.testing.assert_allclose(o, v, rtol=1e-13, atol=1e-13)
+
+
+def test_delta_identical_key_is_ema():
+    rng = np.random.default_rng(23)
+    T, dk, dv, b = 30, 6, 3, 0.3
+    key = rng.normal(size=dk)
+    key /= np.linalg.norm(key)
+    keys = np.tile(key, (T, 1))
+    v = rng.normal(size=(T, dv))
+    o, _ = _delta1(keys, keys, v, np.full(T, b))
+    ema = np.zeros(dv)
+    for t in range(T):
+        ema = (1 - b) * ema + b * v[t]
+        np.testing.assert_allclose(o[t], ema, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("T,dk,dv,seed,init", [
+    (1, 4, 3, 0, False), (9, 3, 5, 1, True), (64, 16, 8, 2, False), (48, 8, 8, 3, True)])
+def test_delta_matches_dense_triangular_solve(T, dk, dv, seed, init):
+    rng = np.random.default_rng(seed)
+    k = rng.normal(size=(T, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    q, v = rng.normal(size=(T, dk)), rng.normal(size=(T, dv))
+    beta = 1.0 / (1.0 + np.exp(-rng.normal(size=T)))
+    S0 = rng.normal(size=(dk, dv)) if init else None
+    o, S = _delta1(q, k, v, beta, S0=S0)
+    O_ref, S_ref = forms.delta_dense(q, k, v, beta, S0)
+    np.testing.assert_allclose(o, O_ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(S, S_ref, rtol=1e-11, atol=1e-12)
+
+
+def test_delta_orthonormal_keys_reduce_to_additive():
+    rng = np.random.default_rng(24)
+    dk, dv, T = 8, 5, 8
+    Qm, _ = np.linalg.qr(rng.normal(size=(dk, dk)))
+    keys = Qm.T[:T]
+    q, v = rng.normal(size=(T, dk)), rng.normal(size=(T, dv))
+    od, Sd = _delta1(q, keys, v, np.ones(T))
+    oa, Sa, _ = _la1(q, keys, v, feature=oracle.PHI_IDENTITY, normalize=False)
+    np.testing.assert_allclose(Sd, Sa, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(od, oa, rtol=1e-12, atol=1e-13)
+
+
+def test_delta_repeated_sweeps_reach_least_squares_w_star():
+    # memory-capacity page: for the two-entry example the least-squares write is
+    # W* = [[1, -0.75], [0, 1.25]]; repeated beta = 1 delta sweeps over the two
+    # pairs (Kaczmarz projections) converge to it.
+    g = _golden("memory_capacity_two_entry.json")
+    keys, values = np.array(g["keys"]), np.array(g["values"])
+    sweeps = 200
+    K = np.tile(keys, (sweeps, 1))
+    V = np.tile(values, (sweeps, 1))
+    _, S = _delta1(K, K, V, np.ones(2 * sweeps))
+    np.testing.assert_allclose(S, np.array(g["least_squares_W_star_value_first"]).T, atol=1e-12)
+
+
+@pytest.mark.parametrize("T", [1, 6, 29])
+def test_delta_chunked_equals_recurrent_every_chunk_size(T):
+    rng = np.random.default_rng(200 + T)
+    dk, dv = 6, 4
+    k = rng.normal(size=(T, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    q, v = rng.normal(size=(T, dk)), rng.normal(size=(T, dv))
+    beta = rng.uniform(0.0, 1.0, size=T)
+    S0 = rng.normal(size=(dk, dv))
+    o, S = _delta1(q, k, v, beta, S0=S0)
+    for C in range(1, T + 1):
+        oc, Sc = forms.delta_chunked(q, k, v, beta, C, S0)
+        np.testing.assert_allclose(oc, o, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(Sc, S, rtol=1e-11, atol=1e-12)
+
+
+def test_delta_causality_and_resume():
+    rng = np.random.default_rng(25)
+    T, dk, dv = 20, 4, 3
+    k = rng.normal(size=(T, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    q, v, beta = rng.normal(size=(T, dk)), rng.normal(size=(T, dv)), rng.uniform(size=T)
+    o, S = _delta1(q, k, v, beta)
+    for s in (0, 9, 19):
+        vv = v.copy()
+        vv[s] += 100.0
+        o2, _ = _delta1(q, k, vv, beta)
+        assert np.array_equal(o2[:s], o[:s]) and not np.array_equal(o2[s], o[s])
+    T1 = 7
+    oa, Sa = _delta1(q[:T1], k[:T1], v[:T1], beta[:T1])
+    ob, Sb = _delta1(q[T1:], k[T1:], v[T1:], beta[T1:], S0=Sa)
+    np.testing.assert_allclose(np.concatenate([oa, ob]), o, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(Sb, S, rtol=1e-13, atol=1e-14)
+
+
+# -------------------------------------------------------------------- decode
+
+def test_decode_step_equals_one_token_of_forward():
+    rng = np.random.default_rng(31)
+    N, H, dk, dv = 3, 2, 8, 6
+    S0 = rng.normal(scale=0.01, size=(N, H, dk, dv))
+    z0 = rng.normal(scale=0.01, size=(N, H, dk))
+    q, k, v = rng.normal(size=(N, H, dk)), rng.normal(size=(N, H, dk)), rng.normal(size=(N, H, dv))
+    o, S, z = oracle.la_decode_step(q, k, v, S0, z0)
+    of, Sf, zf = oracle.la_forward(q[:, :, None], k[:, :, None], v[:, :, None], S0=S0, z0=z0)
+    np.testing.assert_allclose(o, of[:, :, 0], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(S, Sf, rtol=1e-15, atol=1e-16)
+    np.testing.assert_allclose(z, zf, rtol=1e-15, atol=1e-16)
+
+
+def test_decode_chain_equals_forward_over_the_same_tokens():
+    rng = np.random.default_rng(32)
+    N, H, dk, dv, steps = 2, 2, 4, 3, 25
+    S = rng.normal(scale=0.01, size=(N, H, dk, dv))
+    z = rng.normal(scale=0.01, size=(N, H, dk))
+    q, k = rng.normal(size=(steps, N, H, dk)), rng.normal(size=(steps, N, H, dk))
+    v = rng.normal(size=(steps, N, H, dv))
+    of, Sf, zf = oracle.la_forward(q.transpose(1, 2, 0, 3), k.transpose(1, 2, 0, 3),
+                                   v.transpose(1, 2, 0, 3), S0=S, z0=z)
+    outs = []
+    for t in range(steps):
+        o, S, z = oracle.la_decode_step(q[t], k[t], v[t], S, z)
+        outs.append(o)
+    np.testing.assert_allclose(np.stack(outs, 2), of, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(S, Sf, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(z, zf, rtol=1e-12, atol=1e-13)
