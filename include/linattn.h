@@ -1,0 +1,125 @@
+/*
+ * linattn.h -- C ABI of the MI355X (gfx950) causal linear-attention library.
+ *
+ * Three operations, each a hand-written HIP path:
+ *   la_forward      chunked prefill of causal ELU+1 linear attention
+ *   delta_forward   chunked prefill of the delta-rule fast-weight memory
+ *   la_decode_step  one-token decode of ELU+1 linear attention on a resident state
+ *
+ * Pages the definitions come from:
+ *   [LinearMem]  "AIGC 基本功｜线性、循环与记忆架构-LinearMem"
+ *   [Recurrence] "手撕：递推与记忆模型"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are contiguous, row-major, in DEVICE memory of the current HIP
+ *   device.  q, k, v, beta and o have the element type `dtype` (LA_F32 =
+ *   IEEE fp32, LA_BF16 = bfloat16 bits); states S and z are always fp32.
+ * - Shapes: q, k [B][H][T][dk]; v, o [B][H][T][dv]; beta [B][H][T];
+ *   S [B][H][dk][dv] (key-first: S = sum phi(k) v^T, read as phi(q)^T S,
+ *   [LinearMem] §03); z [B][H][dk].  Decode uses N in place of B and no T.
+ * - Ownership: the caller owns every buffer, including the workspace.  The
+ *   library allocates no device memory and keeps no state between calls;
+ *   nothing carries over from one call to the next unless passed in as an
+ *   initial state ([LinearMem] §05: reset per request by zeroing a slot).
+ * - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *   stream) and the call returns without synchronising.  Execution-time
+ *   faults surface at the caller's next synchronisation.
+ * - Validation first: arguments are checked before anything is launched; on
+ *   any non-OK status nothing has been enqueued and no buffer was written.
+ *   la_last_error() then describes the problem (per calling thread).
+ * - Supported: dk, dv in {64, 128}; chunk == 64; dtype LA_BF16 everywhere and
+ *   LA_F32 for la_forward (dk = 128 with dv = 128 excluded) and la_decode_step.
+ *   Other valid-but-unsupported sizes return LA_ERR_UNSUPPORTED.
+ * - Non-finite inputs are not checked and propagate.
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+typedef enum {
+    LA_OK = 0,
+    LA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, eps <= 0, bad dtype or chunk */
+    LA_ERR_UNSUPPORTED = 2, /* a valid configuration this build has no kernel for           */
+    LA_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than the *_workspace_bytes query   */
+    LA_ERR_HIP = 4          /* a HIP launch failed; la_last_error() has the HIP message      */
+} la_status;
+
+/*
+ * Bytes of device workspace la_forward needs for these sizes; 0 if the
+ * sizes are invalid.  The workspace holds one fp32 (S, z) per head and
+ * segment of the sequence; its contents are scratch (no need to clear).
+ */
+size_t la_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
+
+/*
+ * Causal ELU+1 linear attention over a whole sequence (prefill).
+ * [LinearMem] §03: phi(u) = u + 1 (u > 0), exp(u) (u <= 0);
+ *   S_t = S_{t-1} + phi(k_t) v_t^T,  z_t = z_{t-1} + phi(k_t),
+ *   o_t^T = phi(q_t)^T S_t / (phi(q_t)^T z_t + eps)     (write, then read).
+ * S0, z0   initial state; NULL means zero (the page's S_0 = 0, z_0 = 0).
+ * o        [B][H][T][dv] output, dtype.
+ * S_out, z_out  final state S_T, z_T (fp32); NULL means not returned.  They
+ *          may alias S0, z0 (continue a sequence in place, the initial/final
+ *          state hand-off of [Recurrence] "Chunked scan").
+ * eps      > 0; the pages use 1e-6.
+ * chunk    tokens per chunk (64).
+ * Errors: LA_ERR_INVALID_ARG (q, k, v or o NULL; B, H, T, dk, dv < 1; eps not
+ * > 0 or not finite; chunk < 1; dtype unknown), LA_ERR_UNSUPPORTED,
+ * LA_ERR_WORKSPACE, LA_ERR_HIP.
+ */
+la_status la_forward(const void* q, const void* k, const void* v,
+                     const float* S0, const float* z0,
+                     void* o, float* S_out, float* z_out,
+                     int B, int H, int T, int dk, int dv, int dtype, float eps, int chunk,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace delta_forward needs; 0 if the sizes are invalid. */
+size_t delta_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
+
+/*
+ * Delta-rule fast-weight memory over a whole sequence (prefill).
+ * [LinearMem] §03 "从累加改成纠错" and [Recurrence] "Delta-rule fast weight":
+ *   S_t = S_{t-1} + beta_t k_t (v_t^T - k_t^T S_{t-1})
+ * with no feature map and no normaliser.  The output is the write-then-read
+ * query read o_t = S_t^T q_t (raw q).  Keys are used as given: the exact
+ * overwrite property needs unit keys, which the caller provides.
+ * beta     [B][H][T], dtype: the final per-token step size (no transform).
+ * S0       initial state, NULL = zero.  S_out final state (may alias S0), or NULL.
+ * Errors: as la_forward (beta NULL is LA_ERR_INVALID_ARG).
+ */
+la_status delta_forward(const void* q, const void* k, const void* v, const void* beta,
+                        const float* S0, void* o, float* S_out,
+                        int B, int H, int T, int dk, int dv, int dtype, int chunk,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step of ELU+1 linear attention on a resident fp32 state,
+ * updated IN PLACE ([LinearMem] §03 recurrence; §05 in-place inference update):
+ *   S <- S + phi(k) v^T,  z <- z + phi(k),  o = phi(q)^T S / (phi(q)^T z + eps).
+ * q, k [N][H][dk]; v, o [N][H][dv] (dtype); S [N][H][dk][dv], z [N][H][dk] fp32.
+ * Errors: LA_ERR_INVALID_ARG (a pointer NULL, N, H, dk, dv < 1, eps not > 0,
+ * dtype unknown), LA_ERR_UNSUPPORTED, LA_ERR_HIP.
+ */
+la_status la_decode_step(const void* q, const void* k, const void* v,
+                         float* S, float* z, void* o,
+                         int N, int H, int dk, int dv, int dtype, float eps, void* stream);
+
+/* Static text for a status code. */
+const char* la_status_string(int status);
+
+/* Detail for the last non-OK status returned on the calling thread ("" if none). */
+const char* la_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

@@ -1,0 +1,118 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, and rejects invalid arguments before touching the device.
+
+No case here reaches a kernel launch: each call carries at least one argument
+that validation rejects (fake but aligned pointers are never dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from weight_recurrent_memory_amd import binding as lin
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linattn.h")
+P = ctypes.c_void_p(0x10000)  # aligned, never dereferenced
+ST = {n: i for i, n in enumerate(["OK", "INVALID_ARG", "UNSUPPORTED", "WORKSPACE", "HIP"])}
+
+
+def _declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_three_operations():
+    fns = _declared_functions()
+    for name in ("la_forward", "delta_forward", "la_decode_step"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol():
+    L = lin.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def _la(**kw):
+    a = dict(q=P, k=P, v=P, S0=None, z0=None, o=P, S_out=None, z_out=None, B=1, H=1, T=8, dk=64, dv=64,
+             dtype=1, eps=1e-6, chunk=64, ws=P, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lin.lib().la_forward(a["q"], a["k"], a["v"], a["S0"], a["z0"], a["o"], a["S_out"], a["z_out"],
+                                a["B"], a["H"], a["T"], a["dk"], a["dv"], a["dtype"], a["eps"], a["chunk"],
+                                a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), "INVALID_ARG"), (dict(o=None), "INVALID_ARG"), (dict(T=0), "INVALID_ARG"),
+    (dict(B=-1), "INVALID_ARG"), (dict(dk=0), "INVALID_ARG"), (dict(chunk=0), "INVALID_ARG"),
+    (dict(eps=0.0), "INVALID_ARG"), (dict(eps=-1.0), "INVALID_ARG"), (dict(eps=float("nan")), "INVALID_ARG"),
+    (dict(eps=float("inf")), "INVALID_ARG"), (dict(dtype=7), "INVALID_ARG"),
+    (dict(dk=96), "UNSUPPORTED"), (dict(dv=32), "UNSUPPORTED"), (dict(chunk=32), "UNSUPPORTED"),
+    (dict(dtype=0, dk=128, dv=128), "UNSUPPORTED"),
+    (dict(q=ctypes.c_void_p(0x10002)), "INVALID_ARG"),
+    (dict(ws=None), "WORKSPACE"), (dict(wsb=16), "WORKSPACE"), (dict(ws=ctypes.c_void_p(0x10004)), "WORKSPACE"),
+])
+def test_la_forward_rejects(kw, status):
+    assert _la(**kw) == ST[status]
+    assert lin.lib().la_last_error().decode()
+
+
+def _delta(**kw):
+    a = dict(q=P, k=P, v=P, beta=P, S0=None, o=P, S_out=None, B=1, H=1, T=8, dk=128, dv=128, dtype=1,
+             chunk=64, ws=P, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lin.lib().delta_forward(a["q"], a["k"], a["v"], a["beta"], a["S0"], a["o"], a["S_out"], a["B"],
+                                   a["H"], a["T"], a["dk"], a["dv"], a["dtype"], a["chunk"], a["ws"],
+                                   a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(beta=None), "INVALID_ARG"), (dict(T=0), "INVALID_ARG"), (dict(chunk=-3), "INVALID_ARG"),
+    (dict(dtype=3), "INVALID_ARG"), (dict(dk=100), "UNSUPPORTED"), (dict(dtype=0), "UNSUPPORTED"),
+    (dict(ws=None), "WORKSPACE"), (dict(wsb=0), "WORKSPACE"),
+])
+def test_delta_forward_rejects(kw, status):
+    assert _delta(**kw) == ST[status]
+
+
+def _dec(**kw):
+    a = dict(q=P, k=P, v=P, S=P, z=P, o=P, N=4, H=2, dk=128, dv=128, dtype=1, eps=1e-6, stream=None)
+    a.update(kw)
+    if "eps_only" in a:
+        a["eps"] = a.pop("eps_only")
+    return lin.lib().la_decode_step(a["q"], a["k"], a["v"], a["S"], a["z"], a["o"], a["N"], a["H"], a["dk"],
+                                    a["dv"], a["dtype"], a["eps"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(S=None), "INVALID_ARG"), (dict(z=None), "INVALID_ARG"), (dict(N=0), "INVALID_ARG"),
+    (dict(eps=0.0), "INVALID_ARG"), (dict(dtype=2), "INVALID_ARG"), (dict(dk=48), "UNSUPPORTED"),
+    (dict(S=ctypes.c_void_p(0x10008)), "INVALID_ARG"),
+])
+def test_decode_rejects(kw, status):
+    assert _dec(**kw) == ST[status]
+
+
+def test_workspace_queries():
+    L = lin.lib()
+    assert L.la_forward_workspace_bytes(0, 1, 8, 64, 64, 64) == 0
+    assert L.la_forward_workspace_bytes(1, 1, 8, 96, 64, 64) == 0
+    n = L.la_forward_workspace_bytes(4, 8, 8192, 64, 64, 64)
+    assert n > 0 and n % 16 == 0
+    assert L.delta_forward_workspace_bytes(2, 16, 16384, 128, 128, 64) > 0
+
+
+def test_status_strings():
+    L = lin.lib()
+    assert [L.la_status_string(i).decode() for i in range(5)] == [
+        "LA_OK", "LA_ERR_INVALID_ARG", "LA_ERR_UNSUPPORTED", "LA_ERR_WORKSPACE", "LA_ERR_HIP"]
+
+
+def test_python_binding_raises_value_error():
+    import torch
+    q = torch.zeros((1, 1, 4, 64), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        lin.la_forward(q, q, q)

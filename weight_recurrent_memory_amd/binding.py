@@ -1,0 +1,198 @@
+"""Thin Python binding of the C ABI in include/linattn.h.
+
+The functions carry the ABI's names and do argument marshalling only:
+shape/dtype bookkeeping, output and workspace allocation with torch (device
+memory), the current HIP stream, and status -> exception mapping.  Every step
+of the computation runs in the HIP library; if ``liblinattn.so`` is missing
+or fails to load, every call raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblinattn.so")
+
+LA_F32, LA_BF16 = 0, 1
+LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = range(5)
+CHUNK = 64
+
+_lock = threading.Lock()
+_lib = None
+
+
+class LinAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class UnsupportedError(LinAttnError, NotImplementedError):
+    pass
+
+
+def lib():
+    """The loaded HIP library (ctypes).  Raises if it is not built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with "
+                    "`python -m weight_recurrent_memory_amd.build_lib` (hipcc, gfx950)")
+            L = ctypes.CDLL(LIB_PATH)
+            vp, fp, i, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+            L.la_forward_workspace_bytes.argtypes = [i, i, i, i, i, i]
+            L.la_forward_workspace_bytes.restype = sz
+            L.delta_forward_workspace_bytes.argtypes = [i, i, i, i, i, i]
+            L.delta_forward_workspace_bytes.restype = sz
+            L.la_forward.argtypes = [vp, vp, vp, fp, fp, vp, fp, fp, i, i, i, i, i, i,
+                                     ctypes.c_float, i, vp, sz, vp]
+            L.la_forward.restype = i
+            L.delta_forward.argtypes = [vp, vp, vp, vp, fp, vp, fp, i, i, i, i, i, i, i, vp, sz, vp]
+            L.delta_forward.restype = i
+            L.la_decode_step.argtypes = [vp, vp, vp, fp, fp, vp, i, i, i, i, i, ctypes.c_float, vp]
+            L.la_decode_step.restype = i
+            L.la_status_string.argtypes = [i]
+            L.la_status_string.restype = ctypes.c_char_p
+            L.la_last_error.argtypes = []
+            L.la_last_error.restype = ctypes.c_char_p
+            _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status == LA_OK:
+        return
+    L = lib()
+    msg = "%s: %s" % (L.la_status_string(status).decode(), L.la_last_error().decode())
+    if status == LA_ERR_INVALID_ARG:
+        raise ValueError(msg)
+    if status == LA_ERR_UNSUPPORTED:
+        raise UnsupportedError(status, msg)
+    raise LinAttnError(status, msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    if t.dtype == torch.float32:
+        return LA_F32
+    raise ValueError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype, shape, device):
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def la_forward_workspace_bytes(B, H, T, dk, dv, chunk=CHUNK) -> int:
+    return int(lib().la_forward_workspace_bytes(B, H, T, dk, dv, chunk))
+
+
+def delta_forward_workspace_bytes(B, H, T, dk, dv, chunk=CHUNK) -> int:
+    return int(lib().delta_forward_workspace_bytes(B, H, T, dk, dv, chunk))
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def la_forward(q, k, v, S0=None, z0=None, eps=1e-6, chunk=CHUNK, *, o=None, S_out=None,
+               z_out=None, workspace=None, return_state=True):
+    """Causal ELU+1 linear attention prefill.  q, k: [B,H,T,dk]; v: [B,H,T,dv]
+    (bf16 or fp32, CUDA/HIP tensors).  Returns (o, S_T, z_T); S_T/z_T are fp32
+    and None when return_state is False.  S_out/z_out may be S0/z0."""
+    code = _dtype_code(q)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(k, "k", q.dtype, (B, H, T, dk), dev)
+    _need(v, "v", q.dtype, (B, H, T, dv), dev)
+    _need(q, "q", q.dtype, (B, H, T, dk), dev)
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (B, H, dk, dv), dev)
+    if z0 is not None:
+        _need(z0, "z0", torch.float32, (B, H, dk), dev)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
+    _need(o, "o", q.dtype, (B, H, T, dv), dev)
+    if return_state:
+        if S_out is None:
+            S_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        if z_out is None:
+            z_out = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+        _need(S_out, "S_out", torch.float32, (B, H, dk, dv), dev)
+        _need(z_out, "z_out", torch.float32, (B, H, dk), dev)
+    ws, wsb = _workspace(la_forward_workspace_bytes(B, H, T, dk, dv, chunk), dev, workspace)
+    _check(lib().la_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(S0), _ptr(z0), _ptr(o), _ptr(S_out),
+                            _ptr(z_out), B, H, T, dk, dv, code, float(eps), int(chunk),
+                            _ptr(ws), wsb, _stream(dev)))
+    return o, S_out, z_out
+
+
+def delta_forward(q, k, v, beta, S0=None, chunk=CHUNK, *, o=None, S_out=None, workspace=None,
+                  return_state=True):
+    """Delta-rule prefill.  q, k: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T].
+    Returns (o, S_T)."""
+    code = _dtype_code(q)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(k, "k", q.dtype, (B, H, T, dk), dev)
+    _need(v, "v", q.dtype, (B, H, T, dv), dev)
+    _need(beta, "beta", q.dtype, (B, H, T), dev)
+    _need(q, "q", q.dtype, (B, H, T, dk), dev)
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (B, H, dk, dv), dev)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
+    _need(o, "o", q.dtype, (B, H, T, dv), dev)
+    if return_state:
+        if S_out is None:
+            S_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        _need(S_out, "S_out", torch.float32, (B, H, dk, dv), dev)
+    ws, wsb = _workspace(delta_forward_workspace_bytes(B, H, T, dk, dv, chunk), dev, workspace)
+    _check(lib().delta_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_out),
+                               B, H, T, dk, dv, code, int(chunk), _ptr(ws), wsb,
+                               _stream(dev)))
+    return o, S_out
+
+
+def la_decode_step(q, k, v, S, z, eps=1e-6, *, o=None):
+    """One decode step; S [N,H,dk,dv] and z [N,H,dk] (fp32) are updated in
+    place.  q, k: [N,H,dk]; v: [N,H,dv].  Returns o [N,H,dv]."""
+    code = _dtype_code(q)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(k, "k", q.dtype, (N, H, dk), dev)
+    _need(v, "v", q.dtype, (N, H, dv), dev)
+    _need(S, "S", torch.float32, (N, H, dk, dv), dev)
+    _need(z, "z", torch.float32, (N, H, dk), dev)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    _need(o, "o", q.dtype, (N, H, dv), dev)
+    _check(lib().la_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z), _ptr(o), N, H, dk, dv,
+                                code, float(eps), _stream(dev)))
+    return o

@@ -1,0 +1,175 @@
+// C ABI of the library (declared in include/linattn.h): argument validation,
+// launch planning and dispatch to the gfx950 kernels.  Validation runs before
+// any HIP call, so an invalid call touches neither the device nor a buffer.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+#include "linattn.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+la_status fail(la_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+la_status ok() {
+    g_err[0] = '\0';
+    return LA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool supported_dim(int d) { return d == 64 || d == 128; }
+
+// Segments per head: enough (head, segment) workgroups to give every one of
+// the 256 compute units about four, never more segments than chunks.
+la::LaPlan plan_segments(int HT, int T, int chunk, int target_groups) {
+    const int nch = (T + chunk - 1) / chunk;
+    long want = (target_groups + (long)HT - 1) / HT;
+    if (want > nch) want = nch;
+    if (want < 1) want = 1;
+    const int cps = (int)((nch + want - 1) / want);
+    la::LaPlan p;
+    p.L = cps * chunk;
+    p.G = (T + p.L - 1) / p.L;
+    return p;
+}
+
+constexpr int kLaTargetGroups = 1024;
+constexpr int kDeltaTargetGroups = 512;
+
+// Shared shape checks of the two prefill calls.  Returns LA_OK or a status.
+la_status check_prefill(const char* fn, int B, int H, int T, int dk, int dv, int dtype, int chunk) {
+    if (B < 1 || H < 1 || T < 1 || dk < 1 || dv < 1)
+        return fail(LA_ERR_INVALID_ARG, "%s: sizes must be >= 1 (B=%d H=%d T=%d dk=%d dv=%d)", fn, B,
+                    H, T, dk, dv);
+    if (chunk < 1) return fail(LA_ERR_INVALID_ARG, "%s: chunk must be positive (got %d)", fn, chunk);
+    if (dtype != LA_F32 && dtype != LA_BF16)
+        return fail(LA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    if ((long)B * H > (1L << 24))
+        return fail(LA_ERR_UNSUPPORTED, "%s: B*H = %ld heads exceeds 2^24", fn, (long)B * H);
+    if (!supported_dim(dk) || !supported_dim(dv))
+        return fail(LA_ERR_UNSUPPORTED, "%s: dk=%d dv=%d not in {64, 128}", fn, dk, dv);
+    if (chunk != la::kChunk)
+        return fail(LA_ERR_UNSUPPORTED, "%s: chunk=%d not supported (only %d)", fn, chunk, la::kChunk);
+    return LA_OK;
+}
+
+size_t la_ws_bytes(int B, int H, int T, int dk, int dv, int chunk) {
+    const int HT = B * H;
+    const la::LaPlan p = plan_segments(HT, T, chunk, kLaTargetGroups);
+    return sizeof(float) * (size_t)HT * p.G * ((size_t)dk * dv + dk);
+}
+
+size_t delta_ws_bytes(int B, int H, int T, int dk, int dv, int chunk) {
+    const int HT = B * H;
+    const la::LaPlan p = plan_segments(HT, T, chunk, kDeltaTargetGroups);
+    return sizeof(float) * la::delta_ws_floats(HT, dk, dv, p);
+}
+
+la_status hip_status(const char* fn, hipError_t e) {
+    if (e == hipSuccess) return ok();
+    return fail(LA_ERR_HIP, "%s: HIP error %d: %s", fn, (int)e, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* la_status_string(int status) {
+    switch (status) {
+        case LA_OK: return "LA_OK";
+        case LA_ERR_INVALID_ARG: return "LA_ERR_INVALID_ARG";
+        case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED";
+        case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE";
+        case LA_ERR_HIP: return "LA_ERR_HIP";
+        default: return "LA_ERR_UNKNOWN";
+    }
+}
+
+const char* la_last_error(void) { return g_err; }
+
+size_t la_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {
+    if (check_prefill("la_forward_workspace_bytes", B, H, T, dk, dv, LA_BF16, chunk) != LA_OK) return 0;
+    return la_ws_bytes(B, H, T, dk, dv, chunk);
+}
+
+size_t delta_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {
+    if (check_prefill("delta_forward_workspace_bytes", B, H, T, dk, dv, LA_BF16, chunk) != LA_OK) return 0;
+    return delta_ws_bytes(B, H, T, dk, dv, chunk);
+}
+
+la_status la_forward(const void* q, const void* k, const void* v, const float* S0, const float* z0,
+                     void* o, float* S_out, float* z_out, int B, int H, int T, int dk, int dv,
+                     int dtype, float eps, int chunk, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    const char* fn = "la_forward";
+    if (!q || !k || !v || !o) return fail(LA_ERR_INVALID_ARG, "%s: q, k, v and o must be non-NULL", fn);
+    if (!(eps > 0.f) || !isfinite(eps))
+        return fail(LA_ERR_INVALID_ARG, "%s: eps must be finite and > 0 (got %g)", fn, (double)eps);
+    la_status st = check_prefill(fn, B, H, T, dk, dv, dtype, chunk);
+    if (st != LA_OK) return st;
+    if (dtype == LA_F32 && la::la_lds_bytes(dk, dv, dtype) > 160 * 1024)
+        return fail(LA_ERR_UNSUPPORTED, "%s: fp32 with dk=%d dv=%d exceeds the 160 KiB LDS", fn, dk, dv);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(LA_ERR_INVALID_ARG, "%s: q, k, v and o must be 16-byte aligned", fn);
+    const size_t need = la_ws_bytes(B, H, T, dk, dv, chunk);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
+        return fail(LA_ERR_WORKSPACE, "%s: workspace of %zu bytes (16-byte aligned) required, got %zu", fn,
+                    need, workspace ? workspace_bytes : (size_t)0);
+    const la::LaPlan plan = plan_segments(B * H, T, chunk, kLaTargetGroups);
+    return hip_status(fn, la::launch_la_forward(q, k, v, S0, z0, o, S_out, z_out, B * H, T, dk, dv, dtype,
+                                                eps, plan, static_cast<float*>(workspace),
+                                                static_cast<hipStream_t>(stream)));
+}
+
+la_status delta_forward(const void* q, const void* k, const void* v, const void* beta, const float* S0,
+                        void* o, float* S_out, int B, int H, int T, int dk, int dv, int dtype, int chunk,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "delta_forward";
+    if (!q || !k || !v || !beta || !o)
+        return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, beta and o must be non-NULL", fn);
+    la_status st = check_prefill(fn, B, H, T, dk, dv, dtype, chunk);
+    if (st != LA_OK) return st;
+    if (dtype != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "%s: only bf16 inputs are supported", fn);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(LA_ERR_INVALID_ARG, "%s: q, k, v and o must be 16-byte aligned", fn);
+    const size_t need = delta_ws_bytes(B, H, T, dk, dv, chunk);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
+        return fail(LA_ERR_WORKSPACE, "%s: workspace of %zu bytes (16-byte aligned) required, got %zu", fn,
+                    need, workspace ? workspace_bytes : (size_t)0);
+    const la::LaPlan plan = plan_segments(B * H, T, chunk, kDeltaTargetGroups);
+    return hip_status(fn, la::launch_delta_forward(q, k, v, beta, S0, o, S_out, B * H, T, dk, dv, dtype, plan,
+                                                   static_cast<float*>(workspace),
+                                                   static_cast<hipStream_t>(stream)));
+}
+
+la_status la_decode_step(const void* q, const void* k, const void* v, float* S, float* z, void* o, int N,
+                         int H, int dk, int dv, int dtype, float eps, void* stream) {
+    const char* fn = "la_decode_step";
+    if (!q || !k || !v || !S || !z || !o)
+        return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, S, z and o must be non-NULL", fn);
+    if (N < 1 || H < 1 || dk < 1 || dv < 1)
+        return fail(LA_ERR_INVALID_ARG, "%s: sizes must be >= 1 (N=%d H=%d dk=%d dv=%d)", fn, N, H, dk, dv);
+    if (!(eps > 0.f) || !isfinite(eps))
+        return fail(LA_ERR_INVALID_ARG, "%s: eps must be finite and > 0 (got %g)", fn, (double)eps);
+    if (dtype != LA_F32 && dtype != LA_BF16) return fail(LA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    if (!supported_dim(dk) || !supported_dim(dv))
+        return fail(LA_ERR_UNSUPPORTED, "%s: dk=%d dv=%d not in {64, 128}", fn, dk, dv);
+    if ((long)N * H > 0x7fffffffL) return fail(LA_ERR_UNSUPPORTED, "%s: N*H exceeds 2^31-1", fn);
+    if (!aligned16(S)) return fail(LA_ERR_INVALID_ARG, "%s: S must be 16-byte aligned", fn);
+    return hip_status(fn, la::launch_la_decode(q, k, v, S, z, o, N * H, dk, dv, dtype, eps,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,120 @@
+// Device helpers shared by the gfx950 kernels: element types, the ELU+1
+// feature map, bf16 rounding and 16x16 MFMA fragments.
+//
+// MFMA fragment convention used by every kernel in this library
+// ------------------------------------------------------------
+// A 16x16 output tile of v_mfma_f32_16x16x{32_bf16,4_f32} lives in a wave as
+// four floats per lane: lane l, register r holds row 4*(l/16)+r, column l%16.
+// An A operand supplies, per lane, row l%16; a B operand supplies column l%16;
+// each lane group g = l/16 carries a slice of the contraction index.  Which
+// logical contraction index sits in which (group, slot) is a free choice as
+// long as A and B agree; every kernel here uses the mapping
+//     bf16 (k-block of 32):  slot s of group g  <->  k = 4g+s      (s < 4)
+//                                                   k = 16+4g+s-4  (s >= 4)
+//     f32  (k-block of 16):  MFMA number s, group g  <->  k = 4g+s
+// so that the four registers of an output tile (rows 4g..4g+3) are exactly an
+// operand slice: an accumulator computed as a transposed tile feeds the next
+// contraction without leaving registers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16_t;  // raw bfloat16 bits in global memory
+
+// ---------------------------------------------------------------- scalars
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ __bf16 f32_to_bf(float f) {
+    bf16_t b = f32_to_bf16(f);
+    return __builtin_bit_cast(__bf16, b);
+}
+
+// ELU+1 feature map, "AIGC 基本功｜线性、循环与记忆架构-LinearMem" §03:
+// u + 1 for u > 0, exp(u) otherwise.  expf is HIP's device exponential.
+__device__ __forceinline__ float phi(float u) { return u > 0.f ? u + 1.f : __expf(u); }
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float load(const float* p, long i) { return p[i]; }
+    static __device__ __forceinline__ void store(float* p, long i, float x) { p[i] = x; }
+};
+template <> struct Elem<bf16_t> {
+    static __device__ __forceinline__ float load(const bf16_t* p, long i) { return bf16_to_f32(p[i]); }
+    static __device__ __forceinline__ void store(bf16_t* p, long i, float x) { p[i] = f32_to_bf16(x); }
+};
+
+// ---------------------------------------------------------------- MFMA
+
+// Operand element type in LDS: bf16 for bf16 inputs, fp32 for fp32 inputs.
+template <typename TIn> struct Mma;
+
+template <> struct Mma<bf16_t> {
+    typedef __bf16 op_t;          // LDS element
+    static constexpr int KB = 32; // contraction per MFMA instruction
+    typedef v8bf frag;
+
+    // Fragment from a row of an LDS matrix whose contraction index is
+    // contiguous; `row` points at the start of the k-block.
+    static __device__ __forceinline__ frag load(const op_t* row, int g) {
+        v4bf lo = *reinterpret_cast<const v4bf*>(row + 4 * g);
+        v4bf hi = *reinterpret_cast<const v4bf*>(row + 16 + 4 * g);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    static __device__ __forceinline__ frag ones() {
+        __bf16 o = __builtin_bit_cast(__bf16, (bf16_t)0x3f80);
+        return frag{o, o, o, o, o, o, o, o};
+    }
+    static __device__ __forceinline__ frag zero() {
+        __bf16 o = __builtin_bit_cast(__bf16, (bf16_t)0);
+        return frag{o, o, o, o, o, o, o, o};
+    }
+    // A-operand fragment from two adjacent output tiles (contraction rows
+    // 0..15 in t0, 16..31 in t1), scaled elementwise by nothing.
+    static __device__ __forceinline__ frag from_tiles(v4f t0, v4f t1) {
+        return frag{f32_to_bf(t0[0]), f32_to_bf(t0[1]), f32_to_bf(t0[2]), f32_to_bf(t0[3]),
+                    f32_to_bf(t1[0]), f32_to_bf(t1[1]), f32_to_bf(t1[2]), f32_to_bf(t1[3])};
+    }
+    static __device__ __forceinline__ void mma(v4f& acc, const frag& a, const frag& b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+    static __device__ __forceinline__ op_t cvt(float x) { return f32_to_bf(x); }
+};
+
+template <> struct Mma<float> {
+    typedef float op_t;
+    static constexpr int KB = 16;
+    typedef v4f frag;
+    static __device__ __forceinline__ frag load(const op_t* row, int g) {
+        return *reinterpret_cast<const v4f*>(row + 4 * g);
+    }
+    static __device__ __forceinline__ frag ones() { return frag{1.f, 1.f, 1.f, 1.f}; }
+    static __device__ __forceinline__ frag zero() { return frag{0.f, 0.f, 0.f, 0.f}; }
+    static __device__ __forceinline__ frag from_tiles(v4f t0, v4f) { return t0; }
+    static __device__ __forceinline__ void mma(v4f& acc, const frag& a, const frag& b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
+    }
+    static __device__ __forceinline__ op_t cvt(float x) { return x; }
+};
+
+__device__ __forceinline__ v4f zero4() { return v4f{0.f, 0.f, 0.f, 0.f}; }
+
+}  // namespace la

@@ -1,0 +1,38 @@
+// Internal launcher interface between the C ABI (api.hip) and the kernels.
+// Not installed; the public interface is include/linattn.h.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace la {
+
+constexpr int kChunk = 64;  // tokens per chunk in every prefill kernel
+
+struct LaPlan {
+    int G;  // segments per head
+    int L;  // tokens per segment (a multiple of kChunk); the last may be ragged
+};
+
+// Linear attention prefill: segment sums -> exclusive prefix -> chunked outputs.
+// dtype 0 = fp32, 1 = bf16 (raw bits).  ws holds HT*G*(dk*dv+dk) floats.
+hipError_t launch_la_forward(const void* q, const void* k, const void* v,
+                             const float* S0, const float* z0, void* o,
+                             float* S_out, float* z_out, int HT, int T, int dk,
+                             int dv, int dtype, float eps, const LaPlan& plan,
+                             float* ws, hipStream_t stream);
+size_t la_lds_bytes(int dk, int dv, int dtype);
+
+// Delta-rule prefill: segment affine maps -> serial composition -> chunked outputs.
+hipError_t launch_delta_forward(const void* q, const void* k, const void* v,
+                                const void* beta, const float* S0, void* o,
+                                float* S_out, int HT, int T, int dk, int dv,
+                                int dtype, const LaPlan& plan, float* ws,
+                                hipStream_t stream);
+size_t delta_ws_floats(int HT, int dk, int dv, const LaPlan& plan);
+
+// Linear attention decode step on a resident fp32 state (in place).
+hipError_t launch_la_decode(const void* q, const void* k, const void* v, float* S,
+                            float* z, void* o, int NH, int dk, int dv, int dtype,
+                            float eps, hipStream_t stream);
+
+}  // namespace la

@@ -1,0 +1,107 @@
+"""Seeded synthetic workloads (input generation only; none of the method's
+arithmetic lives here).  Tests, the benchmark and the oracle's callers all
+draw their inputs from this module.
+
+Distributions follow the pages' settings: N(0, 1) draws for q, k, v
+("AIGC 基本功｜线性、循环与记忆架构-LinearMem", §04 script), unit keys
+(Gaussian, then normalised per token: same page §03, the delta rule assumes
+unit keys), beta through a sigmoid (same page §08: the final per-token step
+size after the model's transform), d = 64 / 128 with lengths up to 65536
+(same page §01 ledger).  bf16 inputs are fp32 draws rounded to nearest even.
+Generation runs on the device the tensors are wanted on, with a
+torch.Generator seeded per workload.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str        # "la", "delta" or "decode"
+    B: int           # batch (decode: sequences N)
+    H: int
+    T: int           # tokens (decode: number of steps)
+    dk: int
+    dv: int
+    dtype: torch.dtype
+    seed: int
+
+
+# The five configurations the measurements and parity tests are quoted on.
+LA_FP32_SMALL = Workload("la_fp32_b1_h1_t1024_d64", "la", 1, 1, 1024, 64, 64, torch.float32, 1)
+LA_BF16_PREFILL = Workload("la_bf16_b4_h8_t8192_d64", "la", 4, 8, 8192, 64, 64, torch.bfloat16, 2)
+DELTA_BF16_PREFILL = Workload("delta_bf16_b2_h16_t16384_d128", "delta", 2, 16, 16384, 128, 128,
+                              torch.bfloat16, 3)
+LA_BF16_LONG = Workload("la_bf16_b1_h32_t65536_d64", "la", 1, 32, 65536, 64, 64, torch.bfloat16, 4)
+DECODE_BF16 = Workload("decode_bf16_n256_h32_d128_1000steps", "decode", 256, 32, 1000, 128, 128,
+                       torch.bfloat16, 5)
+ALL = (LA_FP32_SMALL, LA_BF16_PREFILL, DELTA_BF16_PREFILL, LA_BF16_LONG, DECODE_BF16)
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=torch.device(device))
+    g.manual_seed(seed)
+    return g
+
+
+def _normal(shape, g, device, std=1.0):
+    x = torch.empty(shape, dtype=torch.float32, device=device)
+    x.normal_(mean=0.0, std=std, generator=g)
+    return x
+
+
+def la_inputs(B, H, T, dk, dv, dtype, seed, device="cpu"):
+    """q, k, v ~ N(0, 1), rounded to `dtype`."""
+    g = _gen(seed, device)
+    q = _normal((B, H, T, dk), g, device).to(dtype)
+    k = _normal((B, H, T, dk), g, device).to(dtype)
+    v = _normal((B, H, T, dv), g, device).to(dtype)
+    return q, k, v
+
+
+def unit_rows(x: torch.Tensor) -> torch.Tensor:
+    """Scale each last-axis vector to unit L2 norm (input preparation)."""
+    return x / x.norm(dim=-1, keepdim=True)
+
+
+def delta_inputs(B, H, T, dk, dv, dtype, seed, device="cpu"):
+    """q, k: N(0, 1) normalised per token; v ~ N(0, 1); beta = sigmoid(N(0, 1))."""
+    g = _gen(seed, device)
+    k = unit_rows(_normal((B, H, T, dk), g, device)).to(dtype)
+    q = unit_rows(_normal((B, H, T, dk), g, device)).to(dtype)
+    v = _normal((B, H, T, dv), g, device).to(dtype)
+    beta = torch.sigmoid(_normal((B, H, T), g, device)).to(dtype)
+    return q, k, v, beta
+
+
+def decode_state(N, H, dk, dv, seed, device="cpu", std=0.01):
+    """Resident fp32 state S, z ~ N(0, std^2)."""
+    g = _gen(seed, device)
+    S = _normal((N, H, dk, dv), g, device, std)
+    z = _normal((N, H, dk), g, device, std)
+    return S, z
+
+
+def decode_tokens(steps, N, H, dk, dv, dtype, seed, device="cpu"):
+    """Per-step q, k [steps, N, H, dk] and v [steps, N, H, dv] ~ N(0, 1)."""
+    g = _gen(seed + 1000003, device)
+    q = _normal((steps, N, H, dk), g, device).to(dtype)
+    k = _normal((steps, N, H, dk), g, device).to(dtype)
+    v = _normal((steps, N, H, dv), g, device).to(dtype)
+    return q, k, v
+
+
+def make(w: Workload, device="cpu"):
+    """All inputs of a workload on `device`."""
+    if w.kind == "la":
+        return la_inputs(w.B, w.H, w.T, w.dk, w.dv, w.dtype, w.seed, device)
+    if w.kind == "delta":
+        return delta_inputs(w.B, w.H, w.T, w.dk, w.dv, w.dtype, w.seed, device)
+    if w.kind == "decode":
+        S, z = decode_state(w.B, w.H, w.dk, w.dv, w.seed, device)
+        return (S, z) + decode_tokens(w.T, w.B, w.H, w.dk, w.dv, w.dtype, w.seed, device)
+    raise ValueError(w.kind)
