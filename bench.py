@@ -1,0 +1,265 @@
+"""Benchmark of the MI355X linear-attention library (one GPU).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one la_forward call over the bf16 prefill workload B=4, H=8,
+T=8192, d=64 (chunk 64, fp32 state): the whole hot path of that workload.
+The line printed is one JSON object:
+
+* value / unit: prefill tokens per second (B*T per step) of the timed steps;
+* roofline: HBM roofline of the la_forward call -- algorithmic bytes (inputs
+  read once, outputs and final state written once) over the mean duration
+  measured with HIP events on the launch stream;
+* cpu_baseline: the fp64 oracle (C, OpenMP over heads) timed on the host on
+  the same workload;
+* extra: the other measured paths -- the long-stream LA workload, the delta
+  rule workload and the 1000-step decode chain (state-update GB/s) -- each
+  with its own roofline fraction.
+
+Inputs are synthetic (seeded, generated on the device) and rotate among
+several copies so that each step reads data evicted from the 256 MB
+Infinity Cache.  --gpus above 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFS = 2516.6  # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
+METRIC = "prefill tokens/sec (MFMA % peak); decode state-update GB/s (% HBM peak)"
+
+
+def la_bytes(B, H, T, dk, dv, el):
+    return B * H * T * (2 * dk + dv) * el + B * H * T * dv * el + B * H * (dk * dv + dk) * 4
+
+
+def la_flops(B, H, T, dk, dv, C=64):
+    # per token-head at chunk C: (C+1)(dk+dv) + 4 dk dv (causal half of the
+    # intra-chunk products, the inter-chunk read and the state update)
+    return B * H * T * ((C + 1) * (dk + dv) + 4 * dk * dv)
+
+
+def delta_bytes(B, H, T, dk, dv, el):
+    return B * H * T * (2 * dk + dv) * el + B * H * T * el + B * H * T * dv * el + B * H * dk * dv * 4
+
+
+def delta_flops(B, H, T, dk, dv, C=64):
+    return B * H * T * ((C - 1) * dk + C * C // 3 + (C + 1) * (dk + 2 * dv) + 6 * dk * dv)
+
+
+def decode_bytes(N, H, dk, dv, el):
+    return N * H * (2 * dk * dv * 4 + 2 * dk * 4 + (2 * dk + dv) * el + dv * el)
+
+
+def _events(n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def time_calls(fn, n_calls, warmup, stream):
+    """Run fn(i) warmup + n_calls times; returns (wall seconds of the timed
+    calls, per-call event durations in ms)."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    starts, ends = _events(n_calls), _events(n_calls)
+    t0 = time.perf_counter()
+    for i in range(n_calls):
+        starts[i].record(stream)
+        fn(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+
+def bench_la(w, steps, warmup, copies, lin, wl):
+    dev = torch.device("cuda:0")
+    el = 2 if w.dtype == torch.bfloat16 else 4
+    sets = [wl.la_inputs(w.B, w.H, w.T, w.dk, w.dv, w.dtype, w.seed + 17 * i, dev) for i in range(copies)]
+    outs = [torch.empty((w.B, w.H, w.T, w.dv), dtype=w.dtype, device=dev) for _ in range(copies)]
+    S = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    z = torch.empty((w.B, w.H, w.dk), dtype=torch.float32, device=dev)
+    ws = torch.empty(lin.la_forward_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        q, k, v = sets[i % copies]
+        lin.la_forward(q, k, v, eps=1e-6, o=outs[i % copies], S_out=S, z_out=z, workspace=ws)
+
+    stream = torch.cuda.current_stream(dev)
+    wall, ev = time_calls(step, steps, warmup, stream)
+    nbytes = la_bytes(w.B, w.H, w.T, w.dk, w.dv, el)
+    mean_ms = sum(ev) / len(ev)
+    return {
+        "wall_s": wall, "ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms,
+        "event_ms_min": min(ev), "tokens_per_s": w.B * w.T * steps / wall,
+        "bytes": nbytes, "flops": la_flops(w.B, w.H, w.T, w.dk, w.dv),
+        "gbs": nbytes / (mean_ms * 1e-3) / 1e9,
+        "tflops": la_flops(w.B, w.H, w.T, w.dk, w.dv) / (mean_ms * 1e-3) / 1e12,
+    }
+
+
+def bench_delta(w, steps, warmup, copies, lin, wl):
+    dev = torch.device("cuda:0")
+    el = 2
+    sets = [wl.delta_inputs(w.B, w.H, w.T, w.dk, w.dv, w.dtype, w.seed + 17 * i, dev) for i in range(copies)]
+    outs = [torch.empty((w.B, w.H, w.T, w.dv), dtype=w.dtype, device=dev) for _ in range(copies)]
+    S = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(lin.delta_forward_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        q, k, v, beta = sets[i % copies]
+        lin.delta_forward(q, k, v, beta, o=outs[i % copies], S_out=S, workspace=ws)
+
+    wall, ev = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
+    nbytes = delta_bytes(w.B, w.H, w.T, w.dk, w.dv, el)
+    fl = delta_flops(w.B, w.H, w.T, w.dk, w.dv)
+    mean_ms = sum(ev) / len(ev)
+    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "tokens_per_s": w.B * w.T * steps / wall,
+            "bytes": nbytes, "flops": fl, "gbs": nbytes / (mean_ms * 1e-3) / 1e9,
+            "tflops": fl / (mean_ms * 1e-3) / 1e12}
+
+
+def bench_decode(w, lin, wl, n_steps=None):
+    dev = torch.device("cuda:0")
+    S, z, Q, K, V = wl.make(w, dev)
+    n = w.T if n_steps is None else n_steps
+    o = torch.empty((w.B, w.H, w.dv), dtype=w.dtype, device=dev)
+
+    def step(i):
+        lin.la_decode_step(Q[i % w.T], K[i % w.T], V[i % w.T], S, z, eps=1e-6, o=o)
+
+    wall, ev = time_calls(step, n, 10, torch.cuda.current_stream(dev))
+    per = decode_bytes(w.B, w.H, w.dk, w.dv, 2)
+    mean_ms = sum(ev) / len(ev)
+    return {"steps": n, "ms_per_step": 1e3 * wall / n, "event_ms_mean": mean_ms, "bytes_per_step": per,
+            "gbs_wall": per * n / wall / 1e9, "gbs": per / (mean_ms * 1e-3) / 1e9}
+
+
+def cpu_baseline(w, oracle, wl, heads=None):
+    """The fp64 oracle on the host, same workload recipe (generated on the CPU)."""
+    q, k, v = wl.la_inputs(w.B, w.H, w.T, w.dk, w.dv, w.dtype, w.seed, "cpu")
+    BH = w.B * w.H
+    heads = BH if heads is None else heads
+    flat = lambda t: t.reshape(BH, *t.shape[2:])[:heads][None]
+    qs, ks, vs = (oracle._f64(flat(t)) for t in (q, k, v))
+    t0 = time.perf_counter()
+    oracle.la_forward(qs, ks, vs, eps=1e-6)
+    dt = time.perf_counter() - t0
+    tokens = w.T * heads / w.H  # token rate scaled to the metric's B*T per step
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{heads} of {BH} heads x T={w.T} (all heads = the whole workload), one pass; "
+                      f"{dt:.2f} s wall", "seconds": dt}
+
+
+def calibrate_copy(nbytes=1 << 30):
+    """A plain device copy of known size, for scaling FETCH_SIZE/WRITE_SIZE."""
+    dev = torch.device("cuda:0")
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": nbytes, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--copies", type=int, default=4, help="input copies rotated through (cache eviction)")
+    ap.add_argument("--only", choices=["all", "la", "la_long", "delta", "decode"], default="all")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} refused: this build runs on one GPU "
+              "(sharding is described, not run)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+
+    from weight_recurrent_memory_amd import binding as lin
+    from weight_recurrent_memory_amd import workloads as wl
+
+    lin.lib()  # fail loudly if the HIP library is missing
+    w = wl.LA_BF16_PREFILL
+    main_res = None
+    extra = {}
+    if args.only in ("all", "la"):
+        main_res = bench_la(w, args.steps, args.warmup, args.copies, lin, wl)
+    if args.only in ("all", "la_long"):
+        wl_ = wl.LA_BF16_LONG
+        r = bench_la(wl_, max(3, args.steps // 10), 2, 2, lin, wl)
+        extra[wl_.name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
+                           "hbm_gbs": r["gbs"], "hbm_frac": r["gbs"] / HBM_PEAK_GBS,
+                           "mfma_tflops": r["tflops"], "mfma_frac": r["tflops"] / BF16_MFMA_PEAK_TFS}
+    if args.only in ("all", "delta"):
+        wd = wl.DELTA_BF16_PREFILL
+        try:
+            r = bench_delta(wd, max(3, args.steps // 5), 2, 2, lin, wl)
+            extra[wd.name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
+                              "hbm_gbs": r["gbs"], "hbm_frac": r["gbs"] / HBM_PEAK_GBS,
+                              "mfma_tflops": r["tflops"], "mfma_frac": r["tflops"] / BF16_MFMA_PEAK_TFS}
+        except lin.LinAttnError as e:
+            extra[wd.name] = {"error": str(e)}
+    if args.only in ("all", "decode"):
+        wdec = wl.DECODE_BF16
+        r = bench_decode(wdec, lin, wl)
+        extra[wdec.name] = {"state_update_gbs": r["gbs"], "hbm_frac": r["gbs"] / HBM_PEAK_GBS,
+                            "gbs_wall_incl_launch_gaps": r["gbs_wall"], "us_per_step": 1e3 * r["event_ms_mean"],
+                            "steps": r["steps"], "bytes_per_step": r["bytes_per_step"]}
+
+    if main_res is None:
+        print(json.dumps({"extra": extra}))
+        return
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle  # test infrastructure, used only for this CPU baseline leg
+        cpu = cpu_baseline(w, oracle, wl)
+
+    gbs = main_res["gbs"]
+    line = {
+        "metric": METRIC,
+        "value": main_res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q,k,v; generated on device; %d rotating copies)" % args.copies,
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv, "chunk": 64,
+                   "state": "fp32"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "la_forward (la_segsum + la_segscan + la_segout)",
+                     "algorithmic_bytes_per_launch": main_res["bytes"],
+                     "event_ms_mean": main_res["event_ms_mean"],
+                     "mfma_tflops": main_res["tflops"], "mfma_frac": main_res["tflops"] / BF16_MFMA_PEAK_TFS},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
