@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.hpp"
+
 namespace la {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -116,5 +118,73 @@ template <> struct Mma<float> {
 };
 
 __device__ __forceinline__ v4f zero4() { return v4f{0.f, 0.f, 0.f, 0.f}; }
+
+// 16-byte global loads of a chunk of rows [c0, c0+n) of a [T][D] matrix.
+template <typename TIn, int D, int NT>
+struct ChunkRegs {
+    static constexpr int VEC = 16 / sizeof(TIn);
+    static constexpr int NV = kChunk * D / (NT * VEC);
+    static_assert(NV * NT * VEC == kChunk * D, "chunk must split evenly");
+    uint4 r[NV];
+
+    __device__ __forceinline__ void load(const TIn* base, int c0, int n, int tid) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int idx = j * NT + tid;
+            const int row = idx / (D / VEC);
+            const int col = (idx % (D / VEC)) * VEC;
+            if (row < n)
+                r[j] = *reinterpret_cast<const uint4*>(base + (long)(c0 + row) * D + col);
+            else
+                r[j] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+    static __device__ __forceinline__ int row_of(int j, int tid) { return (j * NT + tid) / (D / VEC); }
+    static __device__ __forceinline__ int col_of(int j, int tid) { return ((j * NT + tid) % (D / VEC)) * VEC; }
+
+    __device__ __forceinline__ float get(int j, int e) const {
+        const uint32_t w[4] = {r[j].x, r[j].y, r[j].z, r[j].w};
+        if constexpr (sizeof(TIn) == 2) {
+            const uint32_t x = w[e >> 1];
+            return __uint_as_float((e & 1) ? (x & 0xffff0000u) : (x << 16));
+        } else {
+            return __uint_as_float(w[e]);
+        }
+    }
+};
+
+// Write a staged chunk into LDS: row-major [CH][LD] and/or transposed [D][LT].
+// apply_phi maps through the feature map; rows >= n were loaded as zero and
+// are stored as zero (not phi(0) = 1) so padding never enters a sum.
+template <typename TIn, int D, int NT, bool ROWMAJOR, bool TRANSPOSED>
+__device__ __forceinline__ void stage(const ChunkRegs<TIn, D, NT>& cr, bool apply_phi, int n, int tid,
+                                      typename Mma<TIn>::op_t* rm, int ld_rm,
+                                      typename Mma<TIn>::op_t* tr, int ld_tr) {
+    using M = Mma<TIn>;
+    using op = typename M::op_t;
+    constexpr int VEC = ChunkRegs<TIn, D, NT>::VEC;
+#pragma unroll
+    for (int j = 0; j < ChunkRegs<TIn, D, NT>::NV; ++j) {
+        const int row = ChunkRegs<TIn, D, NT>::row_of(j, tid);
+        const int col = ChunkRegs<TIn, D, NT>::col_of(j, tid);
+        op vals[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            float x = cr.get(j, e);
+            if (apply_phi) x = (row < n) ? phi(x) : 0.f;
+            vals[e] = M::cvt(x);
+        }
+        if constexpr (ROWMAJOR) {
+            op* dst = rm + row * ld_rm + col;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) dst[e] = vals[e];
+        }
+        if constexpr (TRANSPOSED) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) tr[(col + e) * ld_tr + row] = vals[e];
+        }
+    }
+}
+
 
 }  // namespace la

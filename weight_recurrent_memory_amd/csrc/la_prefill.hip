@@ -30,73 +30,6 @@ namespace {
 constexpr int CH = kChunk;
 constexpr int NTHR = 256;  // four waves; wave w owns query rows 16w..16w+15
 
-// 16-byte global loads of a chunk of rows [c0, c0+n) of a [T][D] matrix.
-template <typename TIn, int D>
-struct ChunkRegs {
-    static constexpr int VEC = 16 / sizeof(TIn);
-    static constexpr int NV = CH * D / (NTHR * VEC);
-    static_assert(NV * NTHR * VEC == CH * D, "chunk must split evenly");
-    uint4 r[NV];
-
-    __device__ __forceinline__ void load(const TIn* base, int c0, int n, int tid) {
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const int idx = j * NTHR + tid;
-            const int row = idx / (D / VEC);
-            const int col = (idx % (D / VEC)) * VEC;
-            if (row < n)
-                r[j] = *reinterpret_cast<const uint4*>(base + (long)(c0 + row) * D + col);
-            else
-                r[j] = make_uint4(0u, 0u, 0u, 0u);
-        }
-    }
-    static __device__ __forceinline__ int row_of(int j, int tid) { return (j * NTHR + tid) / (D / VEC); }
-    static __device__ __forceinline__ int col_of(int j, int tid) { return ((j * NTHR + tid) % (D / VEC)) * VEC; }
-
-    __device__ __forceinline__ float get(int j, int e) const {
-        const uint32_t w[4] = {r[j].x, r[j].y, r[j].z, r[j].w};
-        if constexpr (sizeof(TIn) == 2) {
-            const uint32_t x = w[e >> 1];
-            return __uint_as_float((e & 1) ? (x & 0xffff0000u) : (x << 16));
-        } else {
-            return __uint_as_float(w[e]);
-        }
-    }
-};
-
-// Write a staged chunk into LDS: row-major [CH][LD] and/or transposed [D][LT].
-// apply_phi maps through the feature map; rows >= n were loaded as zero and
-// are stored as zero (not phi(0) = 1) so padding never enters a sum.
-template <typename TIn, int D, bool ROWMAJOR, bool TRANSPOSED>
-__device__ __forceinline__ void stage(const ChunkRegs<TIn, D>& cr, bool apply_phi, int n, int tid,
-                                      typename Mma<TIn>::op_t* rm, int ld_rm,
-                                      typename Mma<TIn>::op_t* tr, int ld_tr) {
-    using M = Mma<TIn>;
-    using op = typename M::op_t;
-    constexpr int VEC = ChunkRegs<TIn, D>::VEC;
-#pragma unroll
-    for (int j = 0; j < ChunkRegs<TIn, D>::NV; ++j) {
-        const int row = ChunkRegs<TIn, D>::row_of(j, tid);
-        const int col = ChunkRegs<TIn, D>::col_of(j, tid);
-        op vals[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            float x = cr.get(j, e);
-            if (apply_phi) x = (row < n) ? phi(x) : 0.f;
-            vals[e] = M::cvt(x);
-        }
-        if constexpr (ROWMAJOR) {
-            op* dst = rm + row * ld_rm + col;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) dst[e] = vals[e];
-        }
-        if constexpr (TRANSPOSED) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) tr[(col + e) * ld_tr + row] = vals[e];
-        }
-    }
-}
-
 template <typename TIn, int DK, int DV>
 struct Layout {
     using op = typename Mma<TIn>::op_t;
@@ -134,12 +67,12 @@ __global__ __launch_bounds__(NTHR) void la_segsum_kernel(const TIn* __restrict__
     const int t_end = min((seg + 1) * L, T);
     for (int c0 = seg * L; c0 < t_end; c0 += CH) {
         const int n = min(CH, t_end - c0);
-        ChunkRegs<TIn, DK> kr;
-        ChunkRegs<TIn, DV> vr;
+        ChunkRegs<TIn, DK, NTHR> kr;
+        ChunkRegs<TIn, DV, NTHR> vr;
         kr.load(kh, c0, n, tid);
         vr.load(vh, c0, n, tid);
-        stage<TIn, DK, false, true>(kr, true, n, tid, nullptr, 0, Kt, LY::LT);
-        stage<TIn, DV, false, true>(vr, false, n, tid, nullptr, 0, Vt, LY::LT);
+        stage<TIn, DK, NTHR, false, true>(kr, true, n, tid, nullptr, 0, Kt, LY::LT);
+        stage<TIn, DV, NTHR, false, true>(vr, false, n, tid, nullptr, 0, Vt, LY::LT);
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < LY::RTW; ++i) {
@@ -249,14 +182,14 @@ __global__ __launch_bounds__(NTHR) void la_segout_kernel(const TIn* __restrict__
     for (int c0 = seg * L; c0 < t_end; c0 += CH) {
         const int n = min(CH, t_end - c0);
         {
-            ChunkRegs<TIn, DK> qr, kr;
-            ChunkRegs<TIn, DV> vr;
+            ChunkRegs<TIn, DK, NTHR> qr, kr;
+            ChunkRegs<TIn, DV, NTHR> vr;
             qr.load(qh, c0, n, tid);
             kr.load(kh, c0, n, tid);
             vr.load(vh, c0, n, tid);
-            stage<TIn, DK, true, false>(qr, true, n, tid, Qs, LQ, nullptr, 0);
-            stage<TIn, DK, true, true>(kr, true, n, tid, Ks, LQ, Kt, LT);
-            stage<TIn, DV, false, true>(vr, false, n, tid, nullptr, 0, Vt, LT);
+            stage<TIn, DK, NTHR, true, false>(qr, true, n, tid, Qs, LQ, nullptr, 0);
+            stage<TIn, DK, NTHR, true, true>(kr, true, n, tid, Ks, LQ, Kt, LT);
+            stage<TIn, DV, NTHR, false, true>(vr, false, n, tid, nullptr, 0, Vt, LT);
         }
         // state before this chunk -> St (transposed, operand precision)
 #pragma unroll
