@@ -34,18 +34,10 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
     return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// fp32 -> bf16, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
-}
-
-__device__ __forceinline__ __bf16 f32_to_bf(float f) {
-    bf16_t b = f32_to_bf16(f);
-    return __builtin_bit_cast(__bf16, b);
-}
+// fp32 -> bf16, round to nearest even: a plain conversion, which gfx950
+// executes as v_cvt_pk_bf16_f32 (NaN stays NaN, no branches).
+__device__ __forceinline__ __bf16 f32_to_bf(float f) { return static_cast<__bf16>(f); }
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, f32_to_bf(f)); }
 
 // ELU+1 feature map, "AIGC 基本功｜线性、循环与记忆架构-LinearMem" §03:
 // u + 1 for u > 0, exp(u) otherwise.  expf is HIP's device exponential.
