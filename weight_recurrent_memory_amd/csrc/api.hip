@@ -45,7 +45,6 @@ la::LaPlan plan_segments(int HT, int T, int chunk, int target_groups) {
     return p;
 }
 
-constexpr int kLaTargetGroups = 1024;
 constexpr int kDeltaTargetGroups = 512;
 
 // Shared shape checks of the two prefill calls.  Returns LA_OK or a status.
@@ -65,10 +64,8 @@ la_status check_prefill(const char* fn, int B, int H, int T, int dk, int dv, int
     return LA_OK;
 }
 
-size_t la_ws_bytes(int B, int H, int T, int dk, int dv, int chunk) {
-    const int HT = B * H;
-    const la::LaPlan p = plan_segments(HT, T, chunk, kLaTargetGroups);
-    return sizeof(float) * (size_t)HT * p.G * ((size_t)dk * dv + dk);
+size_t la_ws_bytes(int B, int H, int T, int dk, int dv, int) {
+    return sizeof(float) * la::la_ws_floats(B * H, T, dk, dv);
 }
 
 size_t delta_ws_bytes(int B, int H, int T, int dk, int dv, int chunk) {
@@ -127,7 +124,7 @@ la_status la_forward(const void* q, const void* k, const void* v, const float* S
     if (!workspace || workspace_bytes < need || !aligned16(workspace))
         return fail(LA_ERR_WORKSPACE, "%s: workspace of %zu bytes (16-byte aligned) required, got %zu", fn,
                     need, workspace ? workspace_bytes : (size_t)0);
-    const la::LaPlan plan = plan_segments(B * H, T, chunk, kLaTargetGroups);
+    const la::LaPlan plan = la::la_plan(B * H, T, dk, dv);
     return hip_status(fn, la::launch_la_forward(q, k, v, S0, z0, o, S_out, z_out, B * H, T, dk, dv, dtype,
                                                 eps, plan, static_cast<float*>(workspace),
                                                 static_cast<hipStream_t>(stream)));

@@ -40,8 +40,15 @@ __device__ __forceinline__ __bf16 f32_to_bf(float f) { return static_cast<__bf16
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, f32_to_bf(f)); }
 
 // ELU+1 feature map, "AIGC 基本功｜线性、循环与记忆架构-LinearMem" §03:
-// u + 1 for u > 0, exp(u) otherwise.  expf is HIP's device exponential.
-__device__ __forceinline__ float phi(float u) { return u > 0.f ? u + 1.f : __expf(u); }
+// u + 1 for u > 0, e^u otherwise.  e^u is evaluated as 2^(u log2 e) with the
+// hardware base-2 exponential (v_exp_f32, about 1 ulp); for u <= 0 the
+// result lies in (0, 1] and underflows to 0 below about -87.
+__device__ __forceinline__ float phi(float u) {
+    return u > 0.f ? u + 1.f : __builtin_amdgcn_exp2f(u * 1.4426950408889634f);
+}
+
+// 1/x with the hardware reciprocal (v_rcp_f32, about 1 ulp).
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 template <typename T> struct Elem;
 template <> struct Elem<float> {
@@ -70,6 +77,21 @@ template <> struct Mma<bf16_t> {
         v4bf hi = *reinterpret_cast<const v4bf*>(row + 16 + 4 * g);
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
+    // Fragment whose contraction index runs down the ROWS of a row-major
+    // [k][n] LDS matrix (row stride ld elements): rows k0..k0+31, columns
+    // n0..n0+15, as an A operand (n = m) or a B operand.  Two gfx950
+    // transpose reads: within each 16-lane group, destination lane i, slot s
+    // receives element (i & 3) of source lane 4s + (i >> 2); so source lane j
+    // of group g points at row k0 + 4g + (j >> 2), columns n0 + 4(j & 3).
+    static __device__ __forceinline__ frag load_tr(const op_t* base, int ld, int k0, int n0, int lane) {
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) v4s lds_v4s;
+        const int g = lane >> 4, j = lane & 15;
+        const op_t* p0 = base + (k0 + 4 * g + (j >> 2)) * ld + n0 + 4 * (j & 3);
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p0));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p0 + 16 * ld));
+        return __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
     static __device__ __forceinline__ frag ones() {
         __bf16 o = __builtin_bit_cast(__bf16, (bf16_t)0x3f80);
         return frag{o, o, o, o, o, o, o, o};
@@ -97,6 +119,13 @@ template <> struct Mma<float> {
     static __device__ __forceinline__ frag load(const op_t* row, int g) {
         return *reinterpret_cast<const v4f*>(row + 4 * g);
     }
+    // Contraction down the rows of a row-major [k][n] matrix: four scalar
+    // reads (lane i of group g reads rows k0+4g..k0+4g+3 at column n0+i).
+    static __device__ __forceinline__ frag load_tr(const op_t* base, int ld, int k0, int n0, int lane) {
+        const int g = lane >> 4, i = lane & 15;
+        const op_t* p = base + (k0 + 4 * g) * ld + n0 + i;
+        return frag{p[0], p[ld], p[2 * ld], p[3 * ld]};
+    }
     static __device__ __forceinline__ frag ones() { return frag{1.f, 1.f, 1.f, 1.f}; }
     static __device__ __forceinline__ frag zero() { return frag{0.f, 0.f, 0.f, 0.f}; }
     static __device__ __forceinline__ frag from_tiles(v4f t0, v4f) { return t0; }
@@ -110,6 +139,14 @@ template <> struct Mma<float> {
 };
 
 __device__ __forceinline__ v4f zero4() { return v4f{0.f, 0.f, 0.f, 0.f}; }
+
+// The wave's index in its workgroup, as a value the compiler knows to be
+// uniform across the wave.  MFMA instructions ignore the EXEC mask, so a
+// condition guarding an MFMA must compile to a scalar branch that skips it;
+// a condition the compiler believes divergent becomes an EXEC-masked block in
+// which the MFMA still executes (with stale operands).  Every wave-level
+// condition in these kernels derives from this value.
+__device__ __forceinline__ int wave_id(int tid) { return __builtin_amdgcn_readfirstlane(tid >> 6); }
 
 // 16-byte global loads of a chunk of rows [c0, c0+n) of a [T][D] matrix.
 template <typename TIn, int D, int NT>
@@ -144,6 +181,35 @@ struct ChunkRegs {
         }
     }
 };
+
+// Write a staged chunk into LDS row-major ([CH][ld], 16-byte stores).
+// apply_phi maps through the feature map; rows >= n were loaded as zero and
+// are stored as zero (not phi(0) = 1) so padding never enters a sum.
+template <typename TIn, int D, int NT>
+__device__ __forceinline__ void stage_rows(const ChunkRegs<TIn, D, NT>& cr, bool apply_phi, int n, int tid,
+                                           typename Mma<TIn>::op_t* rm, int ld) {
+    using M = Mma<TIn>;
+    using op = typename M::op_t;
+    constexpr int VEC = ChunkRegs<TIn, D, NT>::VEC;
+#pragma unroll
+    for (int j = 0; j < ChunkRegs<TIn, D, NT>::NV; ++j) {
+        const int row = ChunkRegs<TIn, D, NT>::row_of(j, tid);
+        const int col = ChunkRegs<TIn, D, NT>::col_of(j, tid);
+        uint4* dst = reinterpret_cast<uint4*>(rm + row * ld + col);
+        if (!apply_phi) {  // operand type == input type: copy the bits
+            *dst = cr.r[j];
+            continue;
+        }
+        op vals[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) vals[e] = M::cvt(phi(cr.get(j, e)));
+        if (n < kChunk && row >= n) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) vals[e] = M::cvt(0.f);
+        }
+        *dst = *reinterpret_cast<const uint4*>(vals);
+    }
+}
 
 // Write a staged chunk into LDS: row-major [CH][LD] and/or transposed [D][LT].
 // apply_phi maps through the feature map; rows >= n were loaded as zero and

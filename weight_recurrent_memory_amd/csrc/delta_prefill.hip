@@ -94,7 +94,8 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     float* Af = reinterpret_cast<float*>(smem + Y::KS + Y::QS + Y::XT + Y::KT + Y::VT + Y::UT + Y::TS);
     float* Bs = Af + CH * LF;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, li = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
+    const int w = wave_id(tid);
     int head, seg, part;
     if constexpr (OUT) {
         head = blockIdx.x / G;
@@ -372,7 +373,8 @@ __global__ __launch_bounds__(256) void delta_compose_kernel(const float* __restr
                                                             int G) {
     constexpr int RPW = DK / 64;  // row tiles per wave
     __shared__ float Sb[DK][17];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, li = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
+    const int w = wave_id(tid);
     const int ct = blockIdx.x, head = blockIdx.y, col = 16 * ct + li;
     v4f acc[RPW];
 #pragma unroll

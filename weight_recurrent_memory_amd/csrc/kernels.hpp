@@ -13,14 +13,19 @@ struct LaPlan {
     int L;  // tokens per segment (a multiple of kChunk); the last may be ragged
 };
 
-// Linear attention prefill: segment sums -> exclusive prefix -> chunked outputs.
-// dtype 0 = fp32, 1 = bf16 (raw bits).  ws holds HT*G*(dk*dv+dk) floats.
+// Linear attention prefill: one fused launch (segment aggregate, look-back,
+// chunked outputs) after a flag-clearing launch.  dtype 0 = fp32, 1 = bf16
+// (raw bits).  ws holds la_ws_floats(...) floats: the look-back flags, then
+// per-(head, segment) aggregate and inclusive states.
 hipError_t launch_la_forward(const void* q, const void* k, const void* v,
                              const float* S0, const float* z0, void* o,
                              float* S_out, float* z_out, int HT, int T, int dk,
                              int dv, int dtype, float eps, const LaPlan& plan,
                              float* ws, hipStream_t stream);
 size_t la_lds_bytes(int dk, int dv, int dtype);
+LaPlan la_plan(int HT, int T, int dk, int dv);
+size_t la_flag_words(int HT, int G);
+size_t la_ws_floats(int HT, int T, int dk, int dv);
 
 // Delta-rule prefill: segment affine maps -> serial composition -> chunked outputs.
 hipError_t launch_delta_forward(const void* q, const void* k, const void* v,
