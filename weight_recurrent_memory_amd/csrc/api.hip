@@ -61,6 +61,9 @@ la_status check_prefill(const char* fn, int B, int H, int T, int dk, int dv, int
         return fail(LA_ERR_UNSUPPORTED, "%s: dk=%d dv=%d not in {64, 128}", fn, dk, dv);
     if (chunk != la::kChunk)
         return fail(LA_ERR_UNSUPPORTED, "%s: chunk=%d not supported (only %d)", fn, chunk, la::kChunk);
+    const long elem = dtype == LA_BF16 ? 2 : 4;
+    if (((long)T + la::kChunk) * (dk > dv ? dk : dv) * elem >= (1L << 31))
+        return fail(LA_ERR_UNSUPPORTED, "%s: T=%d too long (one head's rows must span < 2 GiB)", fn, T);
     return LA_OK;
 }
 

@@ -27,6 +27,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16_t;  // raw bfloat16 bits in global memory
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- scalars
 
@@ -38,6 +39,11 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
 // executes as v_cvt_pk_bf16_f32 (NaN stays NaN, no branches).
 __device__ __forceinline__ __bf16 f32_to_bf(float f) { return static_cast<__bf16>(f); }
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, f32_to_bf(f)); }
+// Two floats -> two bf16 in one 32-bit word (one v_cvt_pk_bf16_f32), a first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, v2bf{f32_to_bf(a), f32_to_bf(b)});
+}
 
 // ELU+1 feature map, "AIGC 基本功｜线性、循环与记忆架构-LinearMem" §03:
 // u + 1 for u > 0, e^u otherwise.  e^u is evaluated as 2^(u log2 e) with the
@@ -49,6 +55,26 @@ __device__ __forceinline__ float phi(float u) {
 
 // 1/x with the hardware reciprocal (v_rcp_f32, about 1 ulp).
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// ---------------------------------------------------------------- buffers
+//
+// Raw buffer resources give branch-free edges: a load whose byte offset is
+// at or beyond the resource's size returns zero without touching memory, and
+// such a store is dropped.  Word 3 selects the 32-bit data format that
+// untyped buffer access needs on this architecture family.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferWord3);
+}
+__device__ __forceinline__ v4u buf_load16(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+// Non-temporal (streaming) 16-byte store: for results this kernel never reads.
+__device__ __forceinline__ void buf_store16_nt(rsrc_t r, uint32_t off, v4u x) {
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, /*nt*/ 2);
+}
 
 template <typename T> struct Elem;
 template <> struct Elem<float> {
@@ -106,6 +132,21 @@ template <> struct Mma<bf16_t> {
         return frag{f32_to_bf(t0[0]), f32_to_bf(t0[1]), f32_to_bf(t0[2]), f32_to_bf(t0[3]),
                     f32_to_bf(t1[0]), f32_to_bf(t1[1]), f32_to_bf(t1[2]), f32_to_bf(t1[3])};
     }
+    // Fragment of 16 contiguous bytes: slot s of group g <-> k = 8g + s.  Used
+    // where both operands are rows with a contiguous contraction index.
+    static __device__ __forceinline__ frag load16(const op_t* row, int g) {
+        return *reinterpret_cast<const frag*>(row + 8 * g);
+    }
+    // phi of 16 raw input bytes (8 bf16) in the load16 slot order.
+    static __device__ __forceinline__ frag phi_frag(v4u raw) {
+        frag f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t w = raw[e >> 1];
+            f[e] = f32_to_bf(phi(__uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16))));
+        }
+        return f;
+    }
     static __device__ __forceinline__ void mma(v4f& acc, const frag& a, const frag& b) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
     }
@@ -129,6 +170,11 @@ template <> struct Mma<float> {
     static __device__ __forceinline__ frag ones() { return frag{1.f, 1.f, 1.f, 1.f}; }
     static __device__ __forceinline__ frag zero() { return frag{0.f, 0.f, 0.f, 0.f}; }
     static __device__ __forceinline__ frag from_tiles(v4f t0, v4f) { return t0; }
+    static __device__ __forceinline__ frag load16(const op_t* row, int g) { return load(row, g); }
+    static __device__ __forceinline__ frag phi_frag(v4u raw) {
+        return frag{phi(__uint_as_float(raw[0])), phi(__uint_as_float(raw[1])), phi(__uint_as_float(raw[2])),
+                    phi(__uint_as_float(raw[3]))};
+    }
     static __device__ __forceinline__ void mma(v4f& acc, const frag& a, const frag& b) {
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
@@ -166,6 +212,18 @@ struct ChunkRegs {
                 r[j] = *reinterpret_cast<const uint4*>(base + (long)(c0 + row) * D + col);
             else
                 r[j] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+    // Same rows through a buffer resource: rows past the resource's end read
+    // as zero (no row guard, no branch).
+    __device__ __forceinline__ void load_buf(rsrc_t rs, int c0, int tid) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int idx = j * NT + tid;
+            const int row = idx / (D / VEC);
+            const int col = (idx % (D / VEC)) * VEC;
+            const v4u x = buf_load16(rs, (uint32_t)(((c0 + row) * D + col) * (int)sizeof(TIn)));
+            r[j] = make_uint4(x[0], x[1], x[2], x[3]);
         }
     }
     static __device__ __forceinline__ int row_of(int j, int tid) { return (j * NT + tid) / (D / VEC); }
@@ -208,6 +266,43 @@ __device__ __forceinline__ void stage_rows(const ChunkRegs<TIn, D, NT>& cr, bool
             for (int e = 0; e < VEC; ++e) vals[e] = M::cvt(0.f);
         }
         *dst = *reinterpret_cast<const uint4*>(vals);
+    }
+}
+
+// Branch-free variant of stage_rows for the feature-mapped operand: rows >= n
+// are stored as zero by a select, so the code stays one basic block.
+template <typename TIn, int D, int NT>
+__device__ __forceinline__ void stage_rows_phi(const ChunkRegs<TIn, D, NT>& cr, int n, int tid,
+                                               typename Mma<TIn>::op_t* rm, int ld) {
+    using M = Mma<TIn>;
+    using op = typename M::op_t;
+    constexpr int VEC = ChunkRegs<TIn, D, NT>::VEC;
+#pragma unroll
+    for (int j = 0; j < ChunkRegs<TIn, D, NT>::NV; ++j) {
+        const int row = ChunkRegs<TIn, D, NT>::row_of(j, tid);
+        const int col = ChunkRegs<TIn, D, NT>::col_of(j, tid);
+        op vals[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) vals[e] = M::cvt(phi(cr.get(j, e)));
+        uint4 x = *reinterpret_cast<const uint4*>(vals);
+        const bool keep = row < n;
+        x.x = keep ? x.x : 0u;
+        x.y = keep ? x.y : 0u;
+        x.z = keep ? x.z : 0u;
+        x.w = keep ? x.w : 0u;
+        *reinterpret_cast<uint4*>(rm + row * ld + col) = x;
+    }
+}
+
+// Raw copy of a staged chunk into LDS (operand type == input type).
+template <typename TIn, int D, int NT>
+__device__ __forceinline__ void stage_rows_raw(const ChunkRegs<TIn, D, NT>& cr, int tid,
+                                               typename Mma<TIn>::op_t* rm, int ld) {
+#pragma unroll
+    for (int j = 0; j < ChunkRegs<TIn, D, NT>::NV; ++j) {
+        const int row = ChunkRegs<TIn, D, NT>::row_of(j, tid);
+        const int col = ChunkRegs<TIn, D, NT>::col_of(j, tid);
+        *reinterpret_cast<uint4*>(rm + row * ld + col) = cr.r[j];
     }
 }
 

@@ -19,6 +19,8 @@
 // segment g is S0 + sum_{g' < g} (segment sum of g'); workgroups find it by
 // decoupled look-back over their predecessors' published sums (one launch,
 // after a launch that clears the look-back flags).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -38,6 +40,15 @@ struct Layout {
     static constexpr int NCT = DV / 16 + 1;      // value column tiles + the ones/z tile
     static constexpr int RTW = DK / 64;          // dk row tiles per wave (4 waves)
     static constexpr int E = DK * DV + DK;       // floats per (head, segment) state
+    static constexpr int KSZ = CH * LQ;          // elements of one phi(K) chunk buffer
+    static constexpr int VSZ = CH * LV;          // elements of one V chunk buffer
+    static constexpr int SSZ = (DV + 16) * LQ;   // elements of one S^T buffer
+    static constexpr int bytes(int nst) { return (int)sizeof(op) * (2 * KSZ + 2 * VSZ + nst * SSZ); }
+    // S^T is double-buffered (one barrier per chunk) unless that costs a
+    // workgroup of residency or does not fit at all.
+    static constexpr int kLds = 160 * 1024;
+    static constexpr int NST = (2 * bytes(2) <= kLds) ? 2 : (2 * bytes(1) <= kLds) ? 1 : (bytes(2) <= kLds) ? 2 : 1;
+    static constexpr int LDS_BYTES = bytes(NST);
 };
 
 // ------------------------------------------------------------- la_fused
@@ -51,11 +62,11 @@ struct Layout {
 //      walk, an aggregate is added and the walk continues;
 //   3. publish its own inclusive state (flag 2);
 //   4. run the chunk loop from that state, writing the outputs.
-// Published states are written and read with relaxed agent-scope atomics
-// (coherent across the chip's L2s); the flag is stored only after the data
-// stores have completed.  Every wait is bounded: a workgroup that times out
-// recomputes its incoming state from the inputs (sum over all earlier
-// tokens), so progress never depends on the dispatch order.
+// Published states are written and read with accesses coherent across the
+// chip's L2s; the flag is stored only after the data stores have completed.
+// Every wait is bounded: a workgroup that times out recomputes its incoming
+// state from the inputs (sum over all earlier tokens), so progress never
+// depends on the dispatch order.
 
 enum : int { kFlagNone = 0, kFlagAggregate = 1, kFlagInclusive = 2 };
 constexpr int kPollLimit = 4000;  // polls of one window before giving up (~ms)
@@ -66,12 +77,47 @@ __device__ __forceinline__ int load_flag(const int* p) {
 __device__ __forceinline__ void store_flag(int* p, int v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float load_coherent(const float* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+
+// Published (head, segment) states use a tile-native layout, so that each
+// lane moves its four floats of a 16x16 tile in one 16-byte access: tile
+// (wave w, row tile i, value tile c) occupies 256 floats, lane l's four at 4l;
+// the z column follows the dk x dv block, four floats per (w, i, lane group).
+// The accesses are coherent across the chip's L2s (cache policy sc1: stores
+// write through, loads miss any stale line), like the relaxed agent-scope
+// atomics that carry the flags.
+template <int DK, int DV>
+struct Published {
+    static constexpr int RTW = DK / 64, NVT = DV / 16, NCT = NVT + 1, E = DK * DV + DK;
+    static __device__ __forceinline__ uint32_t tile_off(int w, int i, int c, int lane) {
+        return (uint32_t)((((w * RTW + i) * NVT + c) * 256 + lane * 4) * 4);
+    }
+    static __device__ __forceinline__ uint32_t z_off(int w, int i, int g) {
+        return (uint32_t)((DK * DV + (w * RTW + i) * 16 + g * 4) * 4);
+    }
+    static __device__ __forceinline__ void store(float* base, const v4f (&X)[RTW][NCT], int w, int lane) {
+        const rsrc_t rs = make_rsrc(base, E * 4);
+#pragma unroll
+        for (int i = 0; i < RTW; ++i) {
+#pragma unroll
+            for (int c = 0; c < NVT; ++c)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, X[i][c]), rs, tile_off(w, i, c, lane), 0,
+                                                       /*sc1*/ 16);
+            if ((lane & 15) == 0)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, X[i][NCT - 1]), rs,
+                                                       z_off(w, i, lane >> 4), 0, /*sc1*/ 16);
+        }
+    }
+    static __device__ __forceinline__ void load(const float* base, v4f (&X)[RTW][NCT], int w, int lane) {
+        const rsrc_t rs = make_rsrc(base, E * 4);
+#pragma unroll
+        for (int i = 0; i < RTW; ++i) {
+#pragma unroll
+            for (int c = 0; c < NVT; ++c)
+                X[i][c] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rs, tile_off(w, i, c, lane), 0, 16));
+            X[i][NCT - 1] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rs, z_off(w, i, lane >> 4), 0, 16));
+        }
+    }
+};
 
 // acc += phi(K)^T [V | 1] over tokens [t0, t1), next chunk's loads in flight.
 template <typename TIn, int DK, int DV>
@@ -113,6 +159,194 @@ __device__ __forceinline__ void accumulate_kv(const TIn* kh, const TIn* vh, int 
     }
 }
 
+// Registers of one output-pass chunk in flight: phi(K) and V rows for the
+// LDS staging, and this wave's raw query fragments (rows 16w + lane % 16).
+template <typename TIn, int DK, int DV>
+struct OutChunk {
+    static constexpr int QF = DK / Mma<TIn>::KB;
+    ChunkRegs<TIn, DK, NTHR> kr;
+    ChunkRegs<TIn, DV, NTHR> vr;
+    v4u qraw[QF];
+    __device__ __forceinline__ void load(rsrc_t rq, rsrc_t rk, rsrc_t rv, int c0, int w, int tid) {
+        constexpr int KB = Mma<TIn>::KB;
+        const int lane = tid & 63, g = lane >> 4, li = lane & 15;
+        kr.load_buf(rk, c0, tid);
+        vr.load_buf(rv, c0, tid);
+#pragma unroll
+        for (int kk = 0; kk < QF; ++kk)
+            qraw[kk] = buf_load16(rq, (uint32_t)(((c0 + 16 * w + li) * DK + kk * KB + g * (KB / 4)) * (int)sizeof(TIn)));
+    }
+};
+
+// ------------------------------------------------------------- output pass
+//
+// The chunk loop of one wave (W = its index, a compile-time constant so the
+// body is straight-line code).  Wave W owns query rows 16W..16W+15 of every
+// chunk and dk rows 16 W RTW .. of the state.  Per chunk (state S entering it):
+//   P^T  = phi(K) phi(Q_W)^T, keys > query zeroed          (16x16 tiles)
+//   N^T  = [V | 1]^T P^T + [S | z]^T phi(Q_W)^T            (transposed outputs)
+//   O_W  = N^T / den, stored straight from registers
+//   S   += phi(K)^T [V | 1]                                  (this wave's rows)
+// phi(Q_W) fragments come from global memory in registers; phi(K), V and the
+// bf16 copy of S^T are shared through LDS.  The LDS chunk buffers are double
+// buffered: while the matrix cores work on chunk c, the same instruction
+// stream stages chunk c + 1 (its loads were issued one chunk earlier) and
+// issues the loads of chunk c + 2, so one barrier per chunk suffices.
+template <typename TIn, int DK, int DV, int W>
+__device__ __forceinline__ void output_pass(rsrc_t rq, rsrc_t rk, rsrc_t rv, rsrc_t ro, int t_beg, int t_end,
+                                            float eps, v4f (&S)[Layout<TIn, DK, DV>::RTW][Layout<TIn, DK, DV>::NCT],
+                                            OutChunk<TIn, DK, DV>& in, typename Mma<TIn>::op_t* lds, int tid) {
+    using M = Mma<TIn>;
+    using op = typename M::op_t;
+    using frag = typename M::frag;
+    using LY = Layout<TIn, DK, DV>;
+    constexpr int LQ = LY::LQ, LV = LY::LV, NCT = LY::NCT, RTW = LY::RTW, NST = LY::NST;
+    constexpr int NVT = DV / 16;            // value column tiles
+    constexpr int KB = M::KB;               // contraction per fragment
+    constexpr int KT = KB / 16;             // 16-row tiles per fragment
+    constexpr int QF = DK / KB;             // phi(Q) fragments per lane
+    constexpr int NJ = W / KT + 1;          // key fragments reaching query block W
+    constexpr int NJC = CH / KB;            // key fragments per chunk
+    constexpr int SZ = (int)sizeof(TIn);
+    // V^T fragments are kept for the state update when they fit in 32 VGPRs.
+    constexpr bool kKeepV = NVT * NJC * (int)(sizeof(frag) / 4) <= 32;
+    const int lane = tid & 63, g = lane >> 4, li = lane & 15;
+    op* Kb = lds;
+    op* Vb = lds + 2 * LY::KSZ;
+    op* Sb = Vb + 2 * LY::VSZ;
+
+    frag qf[2][QF];
+    auto load_chunk = [&](int c0) { in.load(rq, rk, rv, c0, W, tid); };
+    auto write_st = [&](op* st) {
+#pragma unroll
+        for (int i = 0; i < RTW; ++i)
+#pragma unroll
+            for (int c = 0; c < NCT; ++c) {
+                op* dst = &st[(16 * c + li) * LQ + 16 * (W * RTW + i) + 4 * g];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[r] = M::cvt(S[i][c][r]);
+            }
+    };
+    // Stage chunk c0 (already in registers) into buffer set b.
+    auto stage = [&](auto bconst, int c0) {
+        constexpr int b = decltype(bconst)::value;
+        stage_rows_phi<TIn, DK, NTHR>(in.kr, t_end - c0, tid, Kb + b * LY::KSZ, LQ);
+        stage_rows_raw<TIn, DV, NTHR>(in.vr, tid, Vb + b * LY::VSZ, LV);
+#pragma unroll
+        for (int kk = 0; kk < QF; ++kk) qf[b][kk] = M::phi_frag(in.qraw[kk]);
+    };
+
+    // prologue (chunk t_beg arrives in registers): chunk t_beg staged, chunk
+    // t_beg + CH in flight
+    stage(std::integral_constant<int, 0>{}, t_beg);
+    write_st(Sb);
+    load_chunk(t_beg + CH);
+    __syncthreads();
+
+    auto iter = [&](auto bconst, int c0) {
+        constexpr int b = decltype(bconst)::value;
+        const op* Kc = Kb + b * LY::KSZ;
+        const op* Vc = Vb + b * LY::VSZ;
+        const op* Sc = Sb + (NST == 2 ? b : 0) * LY::SSZ;
+
+        // P^T tiles: keys 16kb.. x this wave's queries
+        v4f Pt[W + 1];
+#pragma unroll
+        for (int kb = 0; kb <= W; ++kb) {
+            Pt[kb] = zero4();
+#pragma unroll
+            for (int kk = 0; kk < QF; ++kk)
+                M::mma(Pt[kb], M::load16(&Kc[(16 * kb + li) * LQ + kk * KB], g), qf[b][kk]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (4 * g + r > li) Pt[W][r] = 0.f;
+        frag pf[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            pf[j] = M::from_tiles(Pt[KT * j], (KT * j + 1 <= W) ? Pt[(KT * j + 1) <= W ? KT * j + 1 : W] : zero4());
+
+        frag vf[kKeepV ? NVT : 1][NJC];
+        if constexpr (kKeepV) {
+#pragma unroll
+            for (int c = 0; c < NVT; ++c)
+#pragma unroll
+                for (int j = 0; j < NJC; ++j) vf[c][j] = M::load_tr(Vc, LV, j * KB, 16 * c, lane);
+        }
+        auto vfrag = [&](int c, int j) -> frag {
+            if constexpr (kKeepV) return vf[c][j];
+            else return M::load_tr(Vc, LV, j * KB, 16 * c, lane);
+        };
+
+        // denominator: 1^T P^T + z^T phi(Q)^T (all 16 rows of the tile equal)
+        v4f D = zero4();
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) M::mma(D, M::ones(), pf[j]);
+#pragma unroll
+        for (int kk = 0; kk < QF; ++kk) M::mma(D, M::load16(&Sc[(DV + li) * LQ + kk * KB], g), qf[b][kk]);
+        const float inv = fast_rcp(D[0] + eps);
+
+        // numerator tiles, normalised and stored from registers
+        const int orow = c0 + 16 * W + li;
+        auto num_tile = [&](int c) {
+            v4f N = zero4();
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) M::mma(N, vfrag(c, j), pf[j]);
+#pragma unroll
+            for (int kk = 0; kk < QF; ++kk) M::mma(N, M::load16(&Sc[(16 * c + li) * LQ + kk * KB], g), qf[b][kk]);
+            return N * inv;
+        };
+        if constexpr (SZ == 2) {
+            // Tiles c, c+1: lane holds columns 4g..4g+3 of each for query li.
+            // One row-pair swap gives every lane 8 consecutive columns:
+            // even groups columns 16c + 8(g/2).., odd groups 16(c+1) + 8(g/2)..
+#pragma unroll
+            for (int c = 0; c < NVT; c += 2) {
+                const v4f n0 = num_tile(c), n1 = num_tile(c + 1);
+                uint32_t a0 = pack_bf16x2(n0[0], n0[1]), a1 = pack_bf16x2(n0[2], n0[3]);
+                uint32_t b0 = pack_bf16x2(n1[0], n1[1]), b1 = pack_bf16x2(n1[2], n1[3]);
+                const auto s0 = __builtin_amdgcn_permlane16_swap(a0, b0, false, false);
+                const auto s1 = __builtin_amdgcn_permlane16_swap(a1, b1, false, false);
+                const v4u x = v4u{(uint32_t)s0[0], (uint32_t)s1[0], (uint32_t)s0[1], (uint32_t)s1[1]};
+                const int col = 16 * c + 16 * (g & 1) + 8 * (g >> 1);
+                buf_store16_nt(ro, (uint32_t)((orow * DV + col) * SZ), x);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < NVT; ++c) {
+                const v4f n = num_tile(c);
+                buf_store16_nt(ro, (uint32_t)((orow * DV + 16 * c + 4 * g) * SZ),
+                               v4u{__float_as_uint(n[0]), __float_as_uint(n[1]), __float_as_uint(n[2]),
+                                   __float_as_uint(n[3])});
+            }
+        }
+
+        // state update with this chunk (this wave's dk rows)
+#pragma unroll
+        for (int j = 0; j < NJC; ++j)
+#pragma unroll
+            for (int i = 0; i < RTW; ++i) {
+                const frag a = M::load_tr(Kc, LQ, j * KB, 16 * (W * RTW + i), lane);
+#pragma unroll
+                for (int c = 0; c < NCT; ++c) M::mma(S[i][c], a, c < NVT ? vfrag(c, j) : M::ones());
+            }
+
+        // next chunk: stage it, start the one after (reads past the segment
+        // end return zero without memory traffic)
+        stage(std::integral_constant<int, b ^ 1>{}, c0 + CH);
+        load_chunk(c0 + 2 * CH);
+        if constexpr (NST == 1) __syncthreads();  // all reads of S^T done
+        write_st(Sb + (NST == 2 ? (b ^ 1) : 0) * LY::SSZ);
+        __syncthreads();
+    };
+    for (int c0 = t_beg;; c0 += 2 * CH) {
+        iter(std::integral_constant<int, 0>{}, c0);
+        if (c0 + CH >= t_end) break;
+        iter(std::integral_constant<int, 1>{}, c0 + CH);
+        if (c0 + 2 * CH >= t_end) break;
+    }
+}
+
 template <typename TIn, int DK, int DV>
 __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ q,
                                                         const TIn* __restrict__ k,
@@ -125,22 +359,17 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
     using M = Mma<TIn>;
     using op = typename M::op_t;
     using LY = Layout<TIn, DK, DV>;
-    constexpr int LQ = LY::LQ, LV = LY::LV, NCT = LY::NCT, RTW = LY::RTW, E = LY::E;
-    constexpr int VEC = 16 / sizeof(TIn);
-    __shared__ __align__(16) op Qs[CH * LQ];
-    __shared__ __align__(16) op Ks[CH * LQ];
-    __shared__ __align__(16) op Vs[CH * LV];
-    __shared__ __align__(16) op St[(DV + 16) * LQ];
-    __shared__ __align__(16) op Os[CH * LV];
+    constexpr int NCT = LY::NCT, RTW = LY::RTW, E = LY::E;
+    __shared__ __align__(16) op lds[LY::LDS_BYTES / sizeof(op)];
+    op* Ks = lds;                    // phase 1 uses the first phi(K) and V buffers
+    op* Vs = lds + 2 * LY::KSZ;
     __shared__ int lb_count, lb_timeout;   // look-back result (wave 0 -> block)
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int w = wave_id(tid);
     const int head = blockIdx.x % HT, seg = blockIdx.x / HT;
-    const TIn* qh = q + (long)head * T * DK;
     const TIn* kh = k + (long)head * T * DK;
     const TIn* vh = v + (long)head * T * DV;
-    TIn* oh = o + (long)head * T * DV;
     const int t_beg = seg * L, t_end = min((seg + 1) * L, T);
     int* hflags = flags + (long)head * G;
 
@@ -158,6 +387,16 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
         for (int c = 0; c < NCT; ++c) A[i][c] = zero4();
     accumulate_kv<TIn, DK, DV>(kh, vh, t_beg, t_end, A, Ks, Vs, tid);
 
+    // The first chunk of the output pass is fetched now, so its latency
+    // overlaps the look-back.  Buffer resources end at the segment end: reads
+    // past it are zero, writes past it are dropped.
+    const rsrc_t rq = make_rsrc(q + (long)head * T * DK, (uint32_t)t_end * DK * sizeof(TIn));
+    const rsrc_t rk = make_rsrc(kh, (uint32_t)t_end * DK * sizeof(TIn));
+    const rsrc_t rv = make_rsrc(vh, (uint32_t)t_end * DV * sizeof(TIn));
+    const rsrc_t ro = make_rsrc(o + (long)head * T * DV, (uint32_t)t_end * DV * sizeof(TIn));
+    OutChunk<TIn, DK, DV> first;
+    first.load(rq, rk, rv, t_beg, w, tid);
+
     // ---- 2. publish the aggregate, then walk back for the incoming state
     v4f S[RTW][NCT];
 #pragma unroll
@@ -172,15 +411,9 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
                 else { if (z0) x = z0[(long)head * DK + (e - DK * DV)]; }
                 S[i][c][r] = seg == 0 ? x : 0.f;
             }
+    using PUB = Published<DK, DV>;
     if (seg > 0 && seg + 1 < G) {
-        float* dst = agg + ((long)head * G + seg) * E;
-#pragma unroll
-        for (int i = 0; i < RTW; ++i)
-#pragma unroll
-            for (int c = 0; c < NCT; ++c)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (c < NCT - 1 || li == 0) store_coherent(dst + state_index(i, c, r), A[i][c][r]);
+        PUB::store(agg + ((long)head * G + seg) * E, A, w, lane);
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (tid == 0) store_flag(&hflags[seg], kFlagAggregate);
@@ -231,21 +464,23 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
             // S_in = incl[j*] + agg[j*+1] + ... + agg[seg-1], left to right: the
             // same rounding as the left-to-right sum from S0, whatever j* is,
             // so results do not depend on timing.
-            const float* src = incl + ((long)head * G + jstar) * E;
+            PUB::load(incl + ((long)head * G + jstar) * E, S, w, lane);
+            // Aggregates in batches: every load of a batch is issued before
+            // the first add, so the walk costs one memory latency per batch.
+            constexpr int BATCH = 4;
+            for (int p = jstar + 1; p < seg; p += BATCH) {
+                v4f t[BATCH][RTW][NCT];
 #pragma unroll
-            for (int i = 0; i < RTW; ++i)
+                for (int u = 0; u < BATCH; ++u)
+                    if (p + u < seg) PUB::load(agg + ((long)head * G + p + u) * E, t[u], w, lane);
 #pragma unroll
-                for (int c = 0; c < NCT; ++c)
+                for (int u = 0; u < BATCH; ++u)
+                    if (p + u < seg) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) S[i][c][r] = load_coherent(src + state_index(i, c, r));
-            for (int p = jstar + 1; p < seg; ++p) {
-                const float* a = agg + ((long)head * G + p) * E;
+                        for (int i = 0; i < RTW; ++i)
 #pragma unroll
-                for (int i = 0; i < RTW; ++i)
-#pragma unroll
-                    for (int c = 0; c < NCT; ++c)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) S[i][c][r] += load_coherent(a + state_index(i, c, r));
+                            for (int c = 0; c < NCT; ++c) S[i][c] += t[u][i][c];
+                    }
             }
         } else {
             // recompute the incoming state from the inputs
@@ -267,14 +502,12 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
 
     // ---- 3. publish the inclusive state (or the final state, last segment)
     if (seg + 1 < G) {
-        float* dst = incl + ((long)head * G + seg) * E;
+        v4f X[RTW][NCT];
 #pragma unroll
         for (int i = 0; i < RTW; ++i)
 #pragma unroll
-            for (int c = 0; c < NCT; ++c)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (c < NCT - 1 || li == 0) store_coherent(dst + state_index(i, c, r), S[i][c][r] + A[i][c][r]);
+            for (int c = 0; c < NCT; ++c) X[i][c] = S[i][c] + A[i][c];
+        PUB::store(incl + ((long)head * G + seg) * E, X, w, lane);
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (tid == 0) store_flag(&hflags[seg], kFlagInclusive);
@@ -293,100 +526,11 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
     }
 
     // ---- 4. the chunk loop from the incoming state
-    ChunkRegs<TIn, DK, NTHR> qr, kr;
-    ChunkRegs<TIn, DV, NTHR> vr;
-    int c0 = t_beg;
-    qr.load(qh, c0, min(CH, t_end - c0), tid);
-    kr.load(kh, c0, min(CH, t_end - c0), tid);
-    vr.load(vh, c0, min(CH, t_end - c0), tid);
-    for (; c0 < t_end; c0 += CH) {
-        const int n = min(CH, t_end - c0);
-        stage_rows<TIn, DK, NTHR>(qr, true, n, tid, Qs, LQ);
-        stage_rows<TIn, DK, NTHR>(kr, true, n, tid, Ks, LQ);
-        stage_rows<TIn, DV, NTHR>(vr, false, n, tid, Vs, LV);
-#pragma unroll
-        for (int i = 0; i < RTW; ++i) {
-            const int rt = w * RTW + i;
-#pragma unroll
-            for (int c = 0; c < NCT; ++c) {
-                op* dst = &St[(16 * c + li) * LQ + 16 * rt + 4 * g];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) dst[r] = M::cvt(S[i][c][r]);
-            }
-        }
-        if (c0 + CH < t_end) {
-            const int n1 = min(CH, t_end - c0 - CH);
-            qr.load(qh, c0 + CH, n1, tid);
-            kr.load(kh, c0 + CH, n1, tid);
-            vr.load(vh, c0 + CH, n1, tid);
-        }
-        __syncthreads();
-
-        v4f Pt[CH / 16];
-#pragma unroll
-        for (int kb = 0; kb < CH / 16; ++kb) {
-            Pt[kb] = zero4();
-            if (kb <= w) {
-#pragma unroll
-                for (int kk = 0; kk < DK / M::KB; ++kk) {
-                    const typename M::frag a = M::load(&Ks[(16 * kb + li) * LQ + kk * M::KB], g);
-                    const typename M::frag b = M::load(&Qs[(16 * w + li) * LQ + kk * M::KB], g);
-                    M::mma(Pt[kb], a, b);
-                }
-                if (kb == w) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (4 * g + r > li) Pt[kb][r] = 0.f;
-                }
-            }
-        }
-        v4f N[NCT];
-#pragma unroll
-        for (int c = 0; c < NCT; ++c) {
-            N[c] = zero4();
-#pragma unroll
-            for (int j = 0; j < CH / M::KB; ++j) {
-                if (j * M::KB > 16 * w + 15) continue;
-                const typename M::frag a = (c < DV / 16) ? M::load_tr(Vs, LV, j * M::KB, 16 * c, lane) : M::ones();
-                const typename M::frag b =
-                    M::from_tiles(Pt[j * M::KB / 16], Pt[j * M::KB / 16 + (M::KB / 16 - 1)]);
-                M::mma(N[c], a, b);
-            }
-#pragma unroll
-            for (int kk = 0; kk < DK / M::KB; ++kk) {
-                const typename M::frag a = M::load(&St[(16 * c + li) * LQ + kk * M::KB], g);
-                const typename M::frag b = M::load(&Qs[(16 * w + li) * LQ + kk * M::KB], g);
-                M::mma(N[c], a, b);
-            }
-        }
-        {
-            const float inv = fast_rcp(N[NCT - 1][0] + eps);
-#pragma unroll
-            for (int c = 0; c < DV / 16; ++c) {
-                op* dst = &Os[(16 * w + li) * LV + 16 * c + 4 * g];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) dst[r] = M::cvt(N[c][r] * inv);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < CH / M::KB; ++j) {
-#pragma unroll
-            for (int i = 0; i < RTW; ++i) {
-                const typename M::frag a = M::load_tr(Ks, LQ, j * M::KB, 16 * (w * RTW + i), lane);
-#pragma unroll
-                for (int c = 0; c < NCT; ++c) {
-                    const typename M::frag b = (c < DV / 16) ? M::load_tr(Vs, LV, j * M::KB, 16 * c, lane)
-                                                             : M::ones();
-                    M::mma(S[i][c], a, b);
-                }
-            }
-        }
-        __syncthreads();
-        for (int idx = tid; idx < n * (DV / VEC); idx += NTHR) {
-            const int row = idx / (DV / VEC), col = (idx % (DV / VEC)) * VEC;
-            *reinterpret_cast<uint4*>(oh + (long)(c0 + row) * DV + col) =
-                *reinterpret_cast<const uint4*>(&Os[row * LV + col]);
-        }
+    switch (w) {
+        case 0: output_pass<TIn, DK, DV, 0>(rq, rk, rv, ro, t_beg, t_end, eps, S, first, lds, tid); break;
+        case 1: output_pass<TIn, DK, DV, 1>(rq, rk, rv, ro, t_beg, t_end, eps, S, first, lds, tid); break;
+        case 2: output_pass<TIn, DK, DV, 2>(rq, rk, rv, ro, t_beg, t_end, eps, S, first, lds, tid); break;
+        default: output_pass<TIn, DK, DV, 3>(rq, rk, rv, ro, t_beg, t_end, eps, S, first, lds, tid); break;
     }
 }
 
@@ -437,9 +581,18 @@ size_t la_ws_floats(int HT, int T, int dk, int dv) {
 }
 
 size_t la_lds_bytes(int dk, int dv, int dtype) {
-    const size_t el = dtype == 1 ? 2 : 4;
-    const size_t pad = 16 / el;
-    return el * ((size_t)2 * CH * (dk + pad) + (size_t)2 * CH * (dv + pad) + (size_t)(dv + 16) * (dk + pad));
+#define LDS_CASE(TY, DT, A, B) \
+    if (dtype == DT && dk == A && dv == B) return Layout<TY, A, B>::LDS_BYTES;
+    LDS_CASE(bf16_t, 1, 64, 64)
+    LDS_CASE(bf16_t, 1, 64, 128)
+    LDS_CASE(bf16_t, 1, 128, 64)
+    LDS_CASE(bf16_t, 1, 128, 128)
+    LDS_CASE(float, 0, 64, 64)
+    LDS_CASE(float, 0, 64, 128)
+    LDS_CASE(float, 0, 128, 64)
+    LDS_CASE(float, 0, 128, 128)
+#undef LDS_CASE
+    return (size_t)1 << 30;
 }
 
 hipError_t launch_la_forward(const void* q, const void* k, const void* v, const float* S0,
