@@ -240,37 +240,10 @@ struct ChunkRegs {
     }
 };
 
-// Write a staged chunk into LDS row-major ([CH][ld], 16-byte stores).
-// apply_phi maps through the feature map; rows >= n were loaded as zero and
-// are stored as zero (not phi(0) = 1) so padding never enters a sum.
-template <typename TIn, int D, int NT>
-__device__ __forceinline__ void stage_rows(const ChunkRegs<TIn, D, NT>& cr, bool apply_phi, int n, int tid,
-                                           typename Mma<TIn>::op_t* rm, int ld) {
-    using M = Mma<TIn>;
-    using op = typename M::op_t;
-    constexpr int VEC = ChunkRegs<TIn, D, NT>::VEC;
-#pragma unroll
-    for (int j = 0; j < ChunkRegs<TIn, D, NT>::NV; ++j) {
-        const int row = ChunkRegs<TIn, D, NT>::row_of(j, tid);
-        const int col = ChunkRegs<TIn, D, NT>::col_of(j, tid);
-        uint4* dst = reinterpret_cast<uint4*>(rm + row * ld + col);
-        if (!apply_phi) {  // operand type == input type: copy the bits
-            *dst = cr.r[j];
-            continue;
-        }
-        op vals[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) vals[e] = M::cvt(phi(cr.get(j, e)));
-        if (n < kChunk && row >= n) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) vals[e] = M::cvt(0.f);
-        }
-        *dst = *reinterpret_cast<const uint4*>(vals);
-    }
-}
-
-// Branch-free variant of stage_rows for the feature-mapped operand: rows >= n
-// are stored as zero by a select, so the code stays one basic block.
+// Write a staged chunk of the feature-mapped operand into LDS row-major
+// ([CH][ld], 16-byte stores).  Rows >= n are stored as zero (not phi(0) = 1)
+// by a select, so padding never enters a sum and the code stays one basic
+// block.
 template <typename TIn, int D, int NT>
 __device__ __forceinline__ void stage_rows_phi(const ChunkRegs<TIn, D, NT>& cr, int n, int tid,
                                                typename Mma<TIn>::op_t* rm, int ld) {

@@ -119,28 +119,38 @@ struct Published {
     }
 };
 
-// acc += phi(K)^T [V | 1] over tokens [t0, t1), next chunk's loads in flight.
+// acc += phi(K)^T [V | 1] over tokens [t0, t1).  NPF chunks are in flight
+// ahead of the one being staged (a streaming reduction needs that many bytes
+// outstanding to cover the memory latency); the two LDS chunk buffers
+// alternate, so one barrier per chunk suffices.  Rows at or past t1 read as
+// zero through the buffer resources.
 template <typename TIn, int DK, int DV>
 __device__ __forceinline__ void accumulate_kv(const TIn* kh, const TIn* vh, int t0, int t1,
                                               v4f (&acc)[Layout<TIn, DK, DV>::RTW][Layout<TIn, DK, DV>::NCT],
-                                              typename Mma<TIn>::op_t* Ks, typename Mma<TIn>::op_t* Vs,
-                                              int tid) {
+                                              typename Mma<TIn>::op_t* Kb, typename Mma<TIn>::op_t* Vb, int tid) {
     using M = Mma<TIn>;
     using LY = Layout<TIn, DK, DV>;
+    constexpr int NPF = (DK + DV) * sizeof(TIn) <= 256 ? 4 : 2;
+    constexpr int NVT = DV / 16;
     const int lane = tid & 63, w = wave_id(tid);
     if (t0 >= t1) return;
-    ChunkRegs<TIn, DK, NTHR> kr;
-    ChunkRegs<TIn, DV, NTHR> vr;
-    kr.load(kh, t0, min(CH, t1 - t0), tid);
-    vr.load(vh, t0, min(CH, t1 - t0), tid);
-    for (int c0 = t0; c0 < t1; c0 += CH) {
-        const int n = min(CH, t1 - c0);
-        stage_rows<TIn, DK, NTHR>(kr, true, n, tid, Ks, LY::LQ);
-        stage_rows<TIn, DV, NTHR>(vr, false, n, tid, Vs, LY::LV);
-        if (c0 + CH < t1) {
-            kr.load(kh, c0 + CH, min(CH, t1 - c0 - CH), tid);
-            vr.load(vh, c0 + CH, min(CH, t1 - c0 - CH), tid);
-        }
+    const rsrc_t rk = make_rsrc(kh, (uint32_t)t1 * DK * sizeof(TIn));
+    const rsrc_t rv = make_rsrc(vh, (uint32_t)t1 * DV * sizeof(TIn));
+    ChunkRegs<TIn, DK, NTHR> kr[NPF];
+    ChunkRegs<TIn, DV, NTHR> vr[NPF];
+#pragma unroll
+    for (int p = 0; p < NPF; ++p) {
+        kr[p].load_buf(rk, t0 + p * CH, tid);
+        vr[p].load_buf(rv, t0 + p * CH, tid);
+    }
+    auto body = [&](auto slot, int c0) {
+        constexpr int sl = decltype(slot)::value, b = sl & 1;
+        typename M::op_t* Ks = Kb + b * LY::KSZ;
+        typename M::op_t* Vs = Vb + b * LY::VSZ;
+        stage_rows_phi<TIn, DK, NTHR>(kr[sl], t1 - c0, tid, Ks, LY::LQ);
+        stage_rows_raw<TIn, DV, NTHR>(vr[sl], tid, Vs, LY::LV);
+        kr[sl].load_buf(rk, c0 + NPF * CH, tid);
+        vr[sl].load_buf(rv, c0 + NPF * CH, tid);
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < CH / M::KB; ++j) {
@@ -148,15 +158,23 @@ __device__ __forceinline__ void accumulate_kv(const TIn* kh, const TIn* vh, int 
             for (int i = 0; i < LY::RTW; ++i) {
                 const typename M::frag a = M::load_tr(Ks, LY::LQ, j * M::KB, 16 * (w * LY::RTW + i), lane);
 #pragma unroll
-                for (int c = 0; c < LY::NCT; ++c) {
-                    const typename M::frag b = (c < DV / 16) ? M::load_tr(Vs, LY::LV, j * M::KB, 16 * c, lane)
-                                                             : M::ones();
-                    M::mma(acc[i][c], a, b);
-                }
+                for (int c = 0; c < LY::NCT; ++c)
+                    M::mma(acc[i][c], a, c < NVT ? M::load_tr(Vs, LY::LV, j * M::KB, 16 * c, lane) : M::ones());
             }
         }
-        __syncthreads();
+    };
+    // Whole groups of NPF chunks, with no exit inside a group: the wait
+    // counts then stay exact across the loop's back edge (a group reaching
+    // past t1 stages zero rows, which add nothing).
+    for (int c0 = t0; c0 < t1; c0 += NPF * CH) {
+        body(std::integral_constant<int, 0>{}, c0);
+        body(std::integral_constant<int, 1>{}, c0 + CH);
+        if constexpr (NPF == 4) {
+            body(std::integral_constant<int, 2>{}, c0 + 2 * CH);
+            body(std::integral_constant<int, 3>{}, c0 + 3 * CH);
+        }
     }
+    __syncthreads();  // the caller reuses the buffers
 }
 
 // Registers of one output-pass chunk in flight: phi(K) and V rows for the
@@ -339,11 +357,12 @@ __device__ __forceinline__ void output_pass(rsrc_t rq, rsrc_t rk, rsrc_t rv, rsr
         write_st(Sb + (NST == 2 ? (b ^ 1) : 0) * LY::SSZ);
         __syncthreads();
     };
-    for (int c0 = t_beg;; c0 += 2 * CH) {
+    // Pairs of chunks with no exit between them, so the wait counts stay
+    // exact across the back edge; a chunk past t_end reads zeros, adds
+    // nothing to the state and has its stores dropped.
+    for (int c0 = t_beg; c0 < t_end; c0 += 2 * CH) {
         iter(std::integral_constant<int, 0>{}, c0);
-        if (c0 + CH >= t_end) break;
         iter(std::integral_constant<int, 1>{}, c0 + CH);
-        if (c0 + 2 * CH >= t_end) break;
     }
 }
 
@@ -361,8 +380,8 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
     using LY = Layout<TIn, DK, DV>;
     constexpr int NCT = LY::NCT, RTW = LY::RTW, E = LY::E;
     __shared__ __align__(16) op lds[LY::LDS_BYTES / sizeof(op)];
-    op* Ks = lds;                    // phase 1 uses the first phi(K) and V buffers
-    op* Vs = lds + 2 * LY::KSZ;
+    op* Kb = lds;                    // the two phi(K) chunk buffers, then the two V buffers
+    op* Vb = lds + 2 * LY::KSZ;
     __shared__ int lb_count, lb_timeout;   // look-back result (wave 0 -> block)
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
@@ -385,7 +404,7 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
     for (int i = 0; i < RTW; ++i)
 #pragma unroll
         for (int c = 0; c < NCT; ++c) A[i][c] = zero4();
-    accumulate_kv<TIn, DK, DV>(kh, vh, t_beg, t_end, A, Ks, Vs, tid);
+    accumulate_kv<TIn, DK, DV>(kh, vh, t_beg, t_end, A, Kb, Vb, tid);
 
     // The first chunk of the output pass is fetched now, so its latency
     // overlaps the look-back.  Buffer resources end at the segment end: reads
@@ -467,7 +486,7 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
             PUB::load(incl + ((long)head * G + jstar) * E, S, w, lane);
             // Aggregates in batches: every load of a batch is issued before
             // the first add, so the walk costs one memory latency per batch.
-            constexpr int BATCH = 4;
+            constexpr int BATCH = 160 / (RTW * NCT * 4) >= 8 ? 8 : 160 / (RTW * NCT * 4) >= 2 ? 160 / (RTW * NCT * 4) : 1;
             for (int p = jstar + 1; p < seg; p += BATCH) {
                 v4f t[BATCH][RTW][NCT];
 #pragma unroll
@@ -496,7 +515,7 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
                         else { if (z0) x = z0[(long)head * DK + (e - DK * DV)]; }
                         S[i][c][r] = x;
                     }
-            accumulate_kv<TIn, DK, DV>(kh, vh, 0, t_beg, S, Ks, Vs, tid);
+            accumulate_kv<TIn, DK, DV>(kh, vh, 0, t_beg, S, Kb, Vb, tid);
         }
     }
 
