@@ -19,9 +19,11 @@
  *   S [B][H][dk][dv] (key-first: S = sum phi(k) v^T, read as phi(q)^T S,
  *   [LinearMem] §03); z [B][H][dk].  Decode uses N in place of B and no T.
  * - Ownership: the caller owns every buffer, including the workspace.  The
- *   library allocates no device memory and keeps no state between calls;
- *   nothing carries over from one call to the next unless passed in as an
- *   initial state ([LinearMem] §05: reset per request by zeroing a slot).
+ *   library allocates no device memory; its only state between calls is a
+ *   process-wide counter that tags la_forward's look-back flags.  No result
+ *   carries over from one call to the next unless passed in as an initial
+ *   state ([LinearMem] §05: reset per request by zeroing a slot).  One
+ *   workspace must not serve two calls that may run at the same time.
  * - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null
  *   stream) and the call returns without synchronising.  Execution-time
  *   faults surface at the caller's next synchronisation.
@@ -54,8 +56,11 @@ typedef enum {
 
 /*
  * Bytes of device workspace la_forward needs for these sizes; 0 if the
- * sizes are invalid.  The workspace holds one fp32 (S, z) per head and
- * segment of the sequence; its contents are scratch (no need to clear).
+ * sizes are invalid.  The workspace holds 64-bit look-back flags and two fp32
+ * (S, z) per head and segment of the sequence.  Its contents need no
+ * initialisation: each flag carries the tag of the call that wrote it, and a
+ * call recorded into a HIP graph (replayed with one tag) clears the flags in
+ * a launch of its own first.
  */
 size_t la_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
 

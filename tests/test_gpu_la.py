@@ -142,3 +142,60 @@ def test_la_heads_isolated_and_plan_independent():
     o2, S2, _ = _run(q, k, v2)
     assert torch.equal(o2[:, :6], o[:, :6]) and torch.equal(o2[:, 7:], o[:, 7:])
     assert torch.equal(S2[:, :6], S[:, :6])
+
+
+def test_la_workspace_leftovers_ignored():
+    """Look-back flags carry a per-call tag: whatever an earlier call (or other
+    data) left in the workspace must not change the result."""
+    B, H, T, dk, dv = 2, 3, 5000, 64, 64
+    print(f"la_forward workspace reuse B={B} H={H} T={T}", flush=True)
+    qa, ka, va = wl.la_inputs(B, H, T, dk, dv, torch.bfloat16, seed=31, device=DEV)
+    qb, kb, vb = wl.la_inputs(B, H, T, dk, dv, torch.bfloat16, seed=32, device=DEV)
+    nb = lin.la_forward_workspace_bytes(B, H, T, dk, dv)
+    ref = lin.la_forward(qb, kb, vb, eps=EPS, workspace=torch.zeros(nb, dtype=torch.uint8, device=DEV))
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    for fill in (0xFF, 0x01, None):
+        if fill is None:
+            ws.copy_(torch.randint(0, 256, (nb,), dtype=torch.uint8, device=DEV))
+        else:
+            ws.fill_(fill)
+        lin.la_forward(qa, ka, va, eps=EPS, workspace=ws)  # leaves its flags and states
+        got = lin.la_forward(qb, kb, vb, eps=EPS, workspace=ws)
+        torch.cuda.synchronize()
+        for g, r in zip(got, ref):
+            assert torch.equal(g, r)
+
+
+def test_la_graph_replays_match_eager():
+    """A la_forward recorded into a graph (one tag for every replay) clears its
+    flags in-graph; each replay, with eager calls on the same workspace in
+    between, must equal the eager result for its inputs."""
+    B, H, T, dk, dv = 1, 4, 3000, 64, 64
+    print(f"la_forward graph replay B={B} H={H} T={T}", flush=True)
+    sets = [wl.la_inputs(B, H, T, dk, dv, torch.bfloat16, seed=40 + i, device=DEV) for i in range(3)]
+    nb = lin.la_forward_workspace_bytes(B, H, T, dk, dv)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    sq, sk, sv = (t.clone() for t in sets[0])
+    o = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=DEV)
+    S = torch.empty((B, H, dk, dv), dtype=torch.float32, device=DEV)
+    z = torch.empty((B, H, dk), dtype=torch.float32, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside capture
+        lin.la_forward(sq, sk, sv, eps=EPS, o=o, S_out=S, z_out=z, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lin.la_forward(sq, sk, sv, eps=EPS, o=o, S_out=S, z_out=z, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        q, k, v = sets[rep % 3]
+        want = lin.la_forward(q, k, v, eps=EPS, workspace=torch.empty(nb, dtype=torch.uint8, device=DEV))
+        lin.la_forward(*sets[(rep + 1) % 3], eps=EPS, workspace=ws)  # eager use of the graph's workspace
+        sq.copy_(q), sk.copy_(k), sv.copy_(v)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, ref in zip((o, S, z), want):
+            assert torch.equal(got, ref), f"replay {rep}"

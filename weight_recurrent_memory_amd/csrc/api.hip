@@ -6,6 +6,10 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <atomic>
+#include <chrono>
+#include <random>
+
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
@@ -77,6 +81,31 @@ size_t delta_ws_bytes(int B, int H, int T, int dk, int dv, int chunk) {
     return sizeof(float) * la::delta_ws_floats(HT, dk, dv, p);
 }
 
+// Tags for the look-back flags of la_forward: a process-wide counter from a
+// random 62-bit start, so a flag word left in a reused workspace by any
+// earlier call (or found there as leftover data) does not carry the tag of
+// the current call.  Zero is never used (a cleared word is absent).
+unsigned long long next_tag() {
+    static std::atomic<unsigned long long> counter{[] {
+        std::random_device rd;
+        const unsigned long long t = (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+        return ((unsigned long long)rd() << 32) ^ (unsigned long long)rd() ^ (t * 0x9E3779B97F4A7C15ull);
+    }()};
+    constexpr unsigned long long mask = (1ull << 62) - 1;
+    unsigned long long t;
+    do t = counter.fetch_add(1, std::memory_order_relaxed) & mask;
+    while (t == 0 || t == mask);  // an all-ones word (e.g. 0xFF fill) never matches
+    return t;
+}
+
+// A launch recorded into a graph is replayed with the same tag, so such
+// launches clear the flags first.  If the capture state cannot be read, clear.
+bool stream_capturing(hipStream_t s) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &st) != hipSuccess) return true;
+    return st != hipStreamCaptureStatusNone;
+}
+
 la_status hip_status(const char* fn, hipError_t e) {
     if (e == hipSuccess) return ok();
     return fail(LA_ERR_HIP, "%s: HIP error %d: %s", fn, (int)e, hipGetErrorString(e));
@@ -128,9 +157,10 @@ la_status la_forward(const void* q, const void* k, const void* v, const float* S
         return fail(LA_ERR_WORKSPACE, "%s: workspace of %zu bytes (16-byte aligned) required, got %zu", fn,
                     need, workspace ? workspace_bytes : (size_t)0);
     const la::LaPlan plan = la::la_plan(B * H, T, dk, dv);
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
     return hip_status(fn, la::launch_la_forward(q, k, v, S0, z0, o, S_out, z_out, B * H, T, dk, dv, dtype,
-                                                eps, plan, static_cast<float*>(workspace),
-                                                static_cast<hipStream_t>(stream)));
+                                                eps, plan, static_cast<float*>(workspace), next_tag(),
+                                                stream_capturing(hs), hs));
 }
 
 la_status delta_forward(const void* q, const void* k, const void* v, const void* beta, const float* S0,

@@ -14,14 +14,17 @@ struct LaPlan {
 };
 
 // Linear attention prefill: one fused launch (segment aggregate, look-back,
-// chunked outputs) after a flag-clearing launch.  dtype 0 = fp32, 1 = bf16
-// (raw bits).  ws holds la_ws_floats(...) floats: the look-back flags, then
-// per-(head, segment) aggregate and inclusive states.
+// chunked outputs).  dtype 0 = fp32, 1 = bf16 (raw bits).  ws holds
+// la_ws_floats(...) floats: the look-back flags, then per-(head, segment)
+// aggregate and inclusive states.  tag (nonzero, < 2^62) must differ from the
+// tag of every earlier call that used ws, unless clear_flags is set (a
+// flag-clearing launch first, for launches recorded into a graph).
 hipError_t launch_la_forward(const void* q, const void* k, const void* v,
                              const float* S0, const float* z0, void* o,
                              float* S_out, float* z_out, int HT, int T, int dk,
                              int dv, int dtype, float eps, const LaPlan& plan,
-                             float* ws, hipStream_t stream);
+                             float* ws, unsigned long long tag, bool clear_flags,
+                             hipStream_t stream);
 size_t la_lds_bytes(int dk, int dv, int dtype);
 LaPlan la_plan(int HT, int T, int dk, int dv);
 size_t la_flag_words(int HT, int G);

@@ -17,8 +17,9 @@
 // Sequence parallelism: each head's tokens are cut into G segments, one
 // workgroup each.  Because the state update is additive, the state entering
 // segment g is S0 + sum_{g' < g} (segment sum of g'); workgroups find it by
-// decoupled look-back over their predecessors' published sums (one launch,
-// after a launch that clears the look-back flags).
+// decoupled look-back over their predecessors' published sums (one launch).
+// Every flag word carries the tag of the call that wrote it, so flags left
+// by earlier calls read as absent and no clearing launch is needed.
 #include <type_traits>
 
 #include "common.hpp"
@@ -71,11 +72,14 @@ struct Layout {
 enum : int { kFlagNone = 0, kFlagAggregate = 1, kFlagInclusive = 2 };
 constexpr int kPollLimit = 4000;  // polls of one window before giving up (~ms)
 
-__device__ __forceinline__ int load_flag(const int* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// A flag word is (tag << 2) | state; a word with another call's tag is absent.
+typedef unsigned long long flag_t;
+__device__ __forceinline__ int load_flag(const flag_t* p, flag_t tag) {
+    const flag_t f = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return (f >> 2) == tag ? (int)(f & 3) : kFlagNone;
 }
-__device__ __forceinline__ void store_flag(int* p, int v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void store_flag(flag_t* p, flag_t tag, int state) {
+    __hip_atomic_store(p, (tag << 2) | (flag_t)state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Published (head, segment) states use a tile-native layout, so that each
@@ -372,7 +376,7 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
                                                         const TIn* __restrict__ v,
                                                         const float* S0, const float* z0,
                                                         TIn* __restrict__ o, float* S_out, float* z_out,
-                                                        int* __restrict__ flags, float* __restrict__ agg,
+                                                        flag_t* __restrict__ flags, flag_t tag, float* __restrict__ agg,
                                                         float* __restrict__ incl, int T, int L, int G,
                                                         int HT, float eps) {
     using M = Mma<TIn>;
@@ -390,7 +394,7 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
     const TIn* kh = k + (long)head * T * DK;
     const TIn* vh = v + (long)head * T * DV;
     const int t_beg = seg * L, t_end = min((seg + 1) * L, T);
-    int* hflags = flags + (long)head * G;
+    flag_t* hflags = flags + (long)head * G;
 
     // element of the (dk x (dv + 1)) state held in tile (i, c), register r
     auto row_of = [&](int i, int r) { return 16 * (w * RTW + i) + 4 * g + r; };
@@ -435,7 +439,7 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
         PUB::store(agg + ((long)head * G + seg) * E, A, w, lane);
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (tid == 0) store_flag(&hflags[seg], kFlagAggregate);
+        if (tid == 0) store_flag(&hflags[seg], tag, kFlagAggregate);
     }
     if (seg > 0) {
         // Find j*, the nearest predecessor whose inclusive state is published
@@ -450,7 +454,7 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
                 const int p = base - lane;
                 int polls = 0, found = -1, to = 0;
                 while (true) {
-                    const int f = p >= 0 ? load_flag(&hflags[p]) : kFlagNone;
+                    const int f = p >= 0 ? load_flag(&hflags[p], tag) : kFlagNone;
                     const unsigned long long incl_mask = __ballot(p >= 0 && f == kFlagInclusive);
                     const unsigned long long ready_mask = __ballot(p < 0 || f != kFlagNone);
                     const int live = __popcll(__ballot(p >= 0));
@@ -529,7 +533,7 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
         PUB::store(incl + ((long)head * G + seg) * E, X, w, lane);
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (tid == 0) store_flag(&hflags[seg], kFlagInclusive);
+        if (tid == 0) store_flag(&hflags[seg], tag, kFlagInclusive);
     } else {
 #pragma unroll
         for (int i = 0; i < RTW; ++i)
@@ -553,31 +557,36 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
     }
 }
 
-__global__ void la_flags_clear_kernel(int* flags, int n) {
+// Zeroes the flag words: used where the launch is recorded into a graph, whose
+// replays all carry the same tag.
+__global__ void la_flags_clear_kernel(flag_t* flags, int n) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) flags[i] = kFlagNone;
+    if (i < n) flags[i] = 0;
 }
 
 template <typename TIn, int DK, int DV>
 hipError_t launch_typed(const void* q, const void* k, const void* v, const float* S0,
                         const float* z0, void* o, float* S_out, float* z_out, int HT, int T,
-                        float eps, const LaPlan& plan, float* ws, hipStream_t stream) {
+                        float eps, const LaPlan& plan, float* ws, unsigned long long tag, bool clear_flags,
+                        hipStream_t stream) {
     const int G = plan.G, L = plan.L;
-    int* flags = reinterpret_cast<int*>(ws);
+    flag_t* flags = reinterpret_cast<flag_t*>(ws);
     float* agg = ws + la_flag_words(HT, G);
     float* incl = agg + (size_t)HT * G * (DK * DV + DK);
-    la_flags_clear_kernel<<<dim3((HT * G + 255) / 256), dim3(256), 0, stream>>>(flags, HT * G);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    if (clear_flags) {
+        la_flags_clear_kernel<<<dim3((HT * G + 255) / 256), dim3(256), 0, stream>>>(flags, HT * G);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
     la_fused_kernel<TIn, DK, DV><<<dim3(HT * G), dim3(NTHR), 0, stream>>>(
         static_cast<const TIn*>(q), static_cast<const TIn*>(k), static_cast<const TIn*>(v), S0, z0,
-        static_cast<TIn*>(o), S_out, z_out, flags, agg, incl, T, L, G, HT, eps);
+        static_cast<TIn*>(o), S_out, z_out, flags, (flag_t)tag, agg, incl, T, L, G, HT, eps);
     return hipGetLastError();
 }
 
 }  // namespace
 
-size_t la_flag_words(int HT, int G) { return ((size_t)HT * G + 63) / 64 * 64; }
+size_t la_flag_words(int HT, int G) { return ((size_t)HT * G * 2 + 63) / 64 * 64; }  // 64-bit flags, in floats
 
 LaPlan la_plan(int HT, int T, int dk, int dv) {
     // Enough (head, segment) workgroups for two per compute unit, and segments
@@ -617,11 +626,11 @@ size_t la_lds_bytes(int dk, int dv, int dtype) {
 hipError_t launch_la_forward(const void* q, const void* k, const void* v, const float* S0,
                              const float* z0, void* o, float* S_out, float* z_out, int HT, int T,
                              int dk, int dv, int dtype, float eps, const LaPlan& plan, float* ws,
-                             hipStream_t stream) {
+                             unsigned long long tag, bool clear_flags, hipStream_t stream) {
 #define LA_CASE(TY, DT, A, B)                                                                  \
     if (dtype == DT && dk == A && dv == B)                                                     \
         return launch_typed<TY, A, B>(q, k, v, S0, z0, o, S_out, z_out, HT, T, eps, plan, ws, \
-                                      stream);
+                                      tag, clear_flags, stream);
     LA_CASE(bf16_t, 1, 64, 64)
     LA_CASE(bf16_t, 1, 64, 128)
     LA_CASE(bf16_t, 1, 128, 64)
