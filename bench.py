@@ -37,6 +37,34 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFS = 2516.6  # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
 METRIC = "prefill tokens/sec (MFMA % peak); decode state-update GB/s (% HBM peak)"
 
+# HBM traffic of one la_fused_kernel launch on the bf16 prefill workload:
+# rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch, mean of the
+# dispatches of `bench.py --only la --steps 5 --warmup 2 --no-cpu`), each
+# scaled by what the same counter reads for a 1 GiB device copy
+# (`bench.py --calibrate-copy`: FETCH_SIZE 524302 KiB -> x2.0, WRITE_SIZE
+# 1048576 KiB -> x1.0).  Valid only for the kernel sources it was measured
+# on (their SHA-256 below); the roofline reports null traffic otherwise.
+LA_TRAFFIC = {
+    "sources": ["weight_recurrent_memory_amd/csrc/la_prefill.hip",
+                "weight_recurrent_memory_amd/csrc/common.hpp",
+                "weight_recurrent_memory_amd/csrc/kernels.hpp"],
+    "sha256": "e811d2b1245c91fcd7910f7f183efd8343efc6fafb7f09881d7ce4dd7de582ec",
+    "fetch_kib": 86745.0, "fetch_scale": 2.0,
+    "write_kib": 56814.0, "write_scale": 1.0,
+}
+
+
+def la_traffic_bytes():
+    import hashlib
+    h = hashlib.sha256()
+    for f in LA_TRAFFIC["sources"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != LA_TRAFFIC["sha256"]:
+        return None
+    return 1024 * (LA_TRAFFIC["fetch_kib"] * LA_TRAFFIC["fetch_scale"]
+                   + LA_TRAFFIC["write_kib"] * LA_TRAFFIC["write_scale"])
+
 
 def la_bytes(B, H, T, dk, dv, el):
     return B * H * T * (2 * dk + dv) * el + B * H * T * dv * el + B * H * (dk * dv + dk) * 4
@@ -66,19 +94,22 @@ def _events(n):
 
 def time_calls(fn, n_calls, warmup, stream):
     """Run fn(i) warmup + n_calls times; returns (wall seconds of the timed
-    calls, per-call event durations in ms)."""
+    calls, mean device time per call in ms).  The device time comes from two
+    HIP events on the launch stream around the whole timed region, so it is
+    the average launch duration including the gaps between launches, and the
+    host's own per-call overhead overlaps the device work."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    starts, ends = _events(n_calls), _events(n_calls)
+    start, end = _events(2)
     t0 = time.perf_counter()
+    start.record(stream)
     for i in range(n_calls):
-        starts[i].record(stream)
         fn(i)
-        ends[i].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall, start.elapsed_time(end) / n_calls
 
 
 def bench_la(w, steps, warmup, copies, lin, wl):
@@ -95,12 +126,11 @@ def bench_la(w, steps, warmup, copies, lin, wl):
         lin.la_forward(q, k, v, eps=1e-6, o=outs[i % copies], S_out=S, z_out=z, workspace=ws)
 
     stream = torch.cuda.current_stream(dev)
-    wall, ev = time_calls(step, steps, warmup, stream)
+    wall, mean_ms = time_calls(step, steps, warmup, stream)
     nbytes = la_bytes(w.B, w.H, w.T, w.dk, w.dv, el)
-    mean_ms = sum(ev) / len(ev)
     return {
         "wall_s": wall, "ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms,
-        "event_ms_min": min(ev), "tokens_per_s": w.B * w.T * steps / wall,
+        "tokens_per_s": w.B * w.T * steps / wall,
         "bytes": nbytes, "flops": la_flops(w.B, w.H, w.T, w.dk, w.dv),
         "gbs": nbytes / (mean_ms * 1e-3) / 1e9,
         "tflops": la_flops(w.B, w.H, w.T, w.dk, w.dv) / (mean_ms * 1e-3) / 1e12,
@@ -119,10 +149,9 @@ def bench_delta(w, steps, warmup, copies, lin, wl):
         q, k, v, beta = sets[i % copies]
         lin.delta_forward(q, k, v, beta, o=outs[i % copies], S_out=S, workspace=ws)
 
-    wall, ev = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
+    wall, mean_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
     nbytes = delta_bytes(w.B, w.H, w.T, w.dk, w.dv, el)
     fl = delta_flops(w.B, w.H, w.T, w.dk, w.dv)
-    mean_ms = sum(ev) / len(ev)
     return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "tokens_per_s": w.B * w.T * steps / wall,
             "bytes": nbytes, "flops": fl, "gbs": nbytes / (mean_ms * 1e-3) / 1e9,
             "tflops": fl / (mean_ms * 1e-3) / 1e12}
@@ -137,9 +166,8 @@ def bench_decode(w, lin, wl, n_steps=None):
     def step(i):
         lin.la_decode_step(Q[i % w.T], K[i % w.T], V[i % w.T], S, z, eps=1e-6, o=o)
 
-    wall, ev = time_calls(step, n, 10, torch.cuda.current_stream(dev))
+    wall, mean_ms = time_calls(step, n, 10, torch.cuda.current_stream(dev))
     per = decode_bytes(w.B, w.H, w.dk, w.dv, 2)
-    mean_ms = sum(ev) / len(ev)
     return {"steps": n, "ms_per_step": 1e3 * wall / n, "event_ms_mean": mean_ms, "bytes_per_step": per,
             "gbs_wall": per * n / wall / 1e9, "gbs": per / (mean_ms * 1e-3) / 1e9}
 
@@ -234,6 +262,7 @@ def main():
         cpu = cpu_baseline(w, oracle, wl)
 
     gbs = main_res["gbs"]
+    traffic = la_traffic_bytes()
     line = {
         "metric": METRIC,
         "value": main_res["tokens_per_s"],
@@ -250,8 +279,9 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv, "chunk": 64,
                    "state": "fp32"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "la_forward (la_segsum + la_segscan + la_segout)",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "traffic_unit": "bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
+                     "kernel": "la_fused_kernel<bf16, 64, 64> (the one launch of la_forward)",
                      "algorithmic_bytes_per_launch": main_res["bytes"],
                      "event_ms_mean": main_res["event_ms_mean"],
                      "mfma_tflops": main_res["tflops"], "mfma_frac": main_res["tflops"] / BF16_MFMA_PEAK_TFS},
