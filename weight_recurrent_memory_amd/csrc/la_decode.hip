@@ -3,7 +3,8 @@
 // §03 for the recurrence and read-out, §05 for the in-place inference update):
 //   S <- S + phi(k) v^T,  z <- z + phi(k),  o = phi(q)^T S / (phi(q)^T z + eps).
 //
-// The step is a streaming read-modify-write of S (dk*dv floats per state):
+// The step is a streaming read-modify-write of S (dk*dv floats per state,
+// written back with non-temporal stores):
 // one workgroup per (sequence, head) state.  Thread t owns four consecutive
 // value columns (one 16-byte vector) of every R-th state row, so each wave
 // reads and writes whole 512-byte (dv = 128) or 256-byte (dv = 64) rows.  The
@@ -69,7 +70,9 @@ __global__ __launch_bounds__(NTHR) void la_decode_kernel(const TIn* __restrict__
         const int row = rg + R * m;
         const float f = fk[row];
         v4f x = st[m] + f * vv;
-        *reinterpret_cast<v4f*>(Ss + (long)row * DV + 4 * cg) = x;
+        // streaming store: a 1 GB state set does not fit the Infinity Cache, so
+        // keeping the written lines there only costs write-backs later
+        __builtin_nontemporal_store(x, reinterpret_cast<v4f*>(Ss + (long)row * DV + 4 * cg));
         acc += fq[row] * x;
     }
     part[rg][cg] = acc;
