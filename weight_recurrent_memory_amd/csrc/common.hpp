@@ -279,38 +279,4 @@ __device__ __forceinline__ void stage_rows_raw(const ChunkRegs<TIn, D, NT>& cr, 
     }
 }
 
-// Write a staged chunk into LDS: row-major [CH][LD] and/or transposed [D][LT].
-// apply_phi maps through the feature map; rows >= n were loaded as zero and
-// are stored as zero (not phi(0) = 1) so padding never enters a sum.
-template <typename TIn, int D, int NT, bool ROWMAJOR, bool TRANSPOSED>
-__device__ __forceinline__ void stage(const ChunkRegs<TIn, D, NT>& cr, bool apply_phi, int n, int tid,
-                                      typename Mma<TIn>::op_t* rm, int ld_rm,
-                                      typename Mma<TIn>::op_t* tr, int ld_tr) {
-    using M = Mma<TIn>;
-    using op = typename M::op_t;
-    constexpr int VEC = ChunkRegs<TIn, D, NT>::VEC;
-#pragma unroll
-    for (int j = 0; j < ChunkRegs<TIn, D, NT>::NV; ++j) {
-        const int row = ChunkRegs<TIn, D, NT>::row_of(j, tid);
-        const int col = ChunkRegs<TIn, D, NT>::col_of(j, tid);
-        op vals[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            float x = cr.get(j, e);
-            if (apply_phi) x = (row < n) ? phi(x) : 0.f;
-            vals[e] = M::cvt(x);
-        }
-        if constexpr (ROWMAJOR) {
-            op* dst = rm + row * ld_rm + col;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) dst[e] = vals[e];
-        }
-        if constexpr (TRANSPOSED) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) tr[(col + e) * ld_tr + row] = vals[e];
-        }
-    }
-}
-
-
 }  // namespace la

@@ -40,18 +40,19 @@ constexpr int NWV = 8;
 template <int DK, int NS, bool OUT>
 struct DL {
     static constexpr int LQ = DK + 8;  // bf16 rows with k = dk
+    static constexpr int LV = NS + 8;  // bf16 rows of V
     static constexpr int LT = CH + 8;  // bf16 rows with k = token
     static constexpr int LF = CH + 4;  // fp32 rows of the C x C work matrix
-    static constexpr int KS = CH * LQ * 2;          // K_c rows; later W rows
+    static constexpr int KS = CH * LQ * 2;          // K_c rows (read transposed too)
+    static constexpr int WS = CH * LQ * 2;          // W rows
     static constexpr int QS = OUT ? CH * LQ * 2 : 0;
     static constexpr int XT = NS * LQ * 2;          // state^T (bf16)
-    static constexpr int KT = DK * LT * 2;          // K_c^T
-    static constexpr int VT = NS * LT * 2;          // V_c^T
+    static constexpr int VS = CH * LV * 2;          // V_c rows (read transposed)
     static constexpr int UT = NS * LT * 2;          // (beta o U)^T
     static constexpr int TS = CH * LT * 2;          // T (bf16)
     static constexpr int AF = CH * LF * 4;          // A, then T blocks (fp32)
     static constexpr int BS = CH * 4;               // beta (fp32)
-    static constexpr int TOTAL = KS + QS + XT + KT + VT + UT + TS + AF + BS;
+    static constexpr int TOTAL = KS + WS + QS + XT + VS + UT + TS + AF + BS;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
     // state tiles (DK/16 x NS/16) over eight waves
     static constexpr int XR = DK / 16;
@@ -83,15 +84,16 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     typedef M::frag frag;
     constexpr int LQ = Y::LQ, LT = Y::LT, LF = Y::LF;
     __shared__ __align__(16) unsigned char smem[Y::TOTAL];
-    __bf16* Ks = reinterpret_cast<__bf16*>(smem);
-    __bf16* Ws = Ks;  // W rows reuse the K rows once the Gram and P tiles are done
-    __bf16* Qs = reinterpret_cast<__bf16*>(smem + Y::KS);
-    __bf16* Xt = reinterpret_cast<__bf16*>(smem + Y::KS + Y::QS);
-    __bf16* Kt = reinterpret_cast<__bf16*>(smem + Y::KS + Y::QS + Y::XT);
-    __bf16* Vt = reinterpret_cast<__bf16*>(smem + Y::KS + Y::QS + Y::XT + Y::KT);
-    __bf16* Ut = reinterpret_cast<__bf16*>(smem + Y::KS + Y::QS + Y::XT + Y::KT + Y::VT);
-    __bf16* Ts = reinterpret_cast<__bf16*>(smem + Y::KS + Y::QS + Y::XT + Y::KT + Y::VT + Y::UT);
-    float* Af = reinterpret_cast<float*>(smem + Y::KS + Y::QS + Y::XT + Y::KT + Y::VT + Y::UT + Y::TS);
+    constexpr int LV = Y::LV;
+    unsigned char* sp = smem;
+    __bf16* Ks = reinterpret_cast<__bf16*>(sp);  sp += Y::KS;
+    __bf16* Ws = reinterpret_cast<__bf16*>(sp);  sp += Y::WS;
+    __bf16* Qs = reinterpret_cast<__bf16*>(sp);  sp += Y::QS;
+    __bf16* Xt = reinterpret_cast<__bf16*>(sp);  sp += Y::XT;
+    __bf16* Vs = reinterpret_cast<__bf16*>(sp);  sp += Y::VS;
+    __bf16* Ut = reinterpret_cast<__bf16*>(sp);  sp += Y::UT;
+    __bf16* Ts = reinterpret_cast<__bf16*>(sp);  sp += Y::TS;
+    float* Af = reinterpret_cast<float*>(sp);
     float* Bs = Af + CH * LF;
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
@@ -134,21 +136,28 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     }
 
     const int t_end = min((seg + 1) * L, T);
+    // The next chunk's rows are loaded into registers while this one is
+    // processed; rows past the segment end load as zero.
+    ChunkRegs<bf16_t, DK, NT> kr, qr;
+    ChunkRegs<bf16_t, NS, NT> vr;
+    float bnext = 0.f;
+    auto load_chunk = [&](int c) {
+        const int nn = min(CH, t_end - c);
+        kr.load(kh, c, nn, tid);
+        if constexpr (OUT) qr.load(qh, c, nn, tid);
+        if (has_v) vr.load(vh, c, nn, tid);
+        if (tid < CH) bnext = tid < nn ? bf16_to_f32(bh[c + tid]) : 0.f;
+    };
+    load_chunk(seg * L);
     for (int c0 = seg * L; c0 < t_end; c0 += CH) {
         const int n = min(CH, t_end - c0);
-        // ---- stage the chunk; the state goes to LDS as bf16, transposed
-        {
-            ChunkRegs<bf16_t, DK, NT> kr;
-            kr.load(kh, c0, n, tid);
-            ChunkRegs<bf16_t, DK, NT> qr;
-            if constexpr (OUT) qr.load(qh, c0, n, tid);
-            ChunkRegs<bf16_t, NS, NT> vr;
-            if (has_v) vr.load(vh, c0, n, tid);
-            if (tid < CH) Bs[tid] = tid < n ? bf16_to_f32(bh[c0 + tid]) : 0.f;
-            stage<bf16_t, DK, NT, true, true>(kr, false, n, tid, Ks, LQ, Kt, LT);
-            if constexpr (OUT) stage<bf16_t, DK, NT, true, false>(qr, false, n, tid, Qs, LQ, nullptr, 0);
-            if (has_v) stage<bf16_t, NS, NT, false, true>(vr, false, n, tid, nullptr, 0, Vt, LT);
-        }
+        // ---- stage the chunk (row-major; transposed operands are read with
+        // transpose loads); the state goes to LDS as bf16, transposed
+        stage_rows_raw<bf16_t, DK, NT>(kr, tid, Ks, LQ);
+        if constexpr (OUT) stage_rows_raw<bf16_t, DK, NT>(qr, tid, Qs, LQ);
+        if (has_v) stage_rows_raw<bf16_t, NS, NT>(vr, tid, Vs, LV);
+        if (tid < CH) Bs[tid] = bnext;
+        if (c0 + CH < t_end) load_chunk(c0 + CH);
 #pragma unroll
         for (int c = 0; c < Y::X_CPW; ++c) {
             __bf16* dst = &Xt[(16 * (xc0 + c) + li) * LQ + 16 * xrt + 4 * g];
@@ -275,7 +284,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
             v4f acc = zero4();
 #pragma unroll
             for (int kb = 0; kb < CH / 32; ++kb) {
-                const frag a = M::load(&Kt[(16 * dkt + li) * LT + 32 * kb], g);
+                const frag a = M::load_tr(Ks, LQ, 32 * kb, 16 * dkt, lane);
                 const frag b = M::load(&Ts[(16 * tt + li) * LT + 32 * kb], g);
                 M::mma(acc, a, b);
             }
@@ -292,7 +301,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
                 for (int kb = 0; kb < CH / 32; ++kb) {
                     if (32 * kb > 16 * ort + 15) continue;  // T is lower triangular
                     const frag a = M::load(&Ts[(16 * ort + li) * LT + 32 * kb], g);
-                    const frag b = M::load(&Vt[(16 * (oc0 + c) + li) * LT + 32 * kb], g);
+                    const frag b = M::load_tr(Vs, LV, 32 * kb, 16 * (oc0 + c), lane);
                     M::mma(U[c], a, b);
                 }
             }
@@ -323,7 +332,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         for (int c = 0; c < Y::X_CPW; ++c) {
 #pragma unroll
             for (int kb = 0; kb < CH / 32; ++kb) {
-                const frag a = M::load(&Kt[(16 * xrt + li) * LT + 32 * kb], g);
+                const frag a = M::load_tr(Ks, LQ, 32 * kb, 16 * xrt, lane);
                 const frag b = M::load(&Ut[(16 * (xc0 + c) + li) * LT + 32 * kb], g);
                 M::mma(X[c], a, b);
             }
