@@ -21,8 +21,9 @@
 // Sequence parallelism.  Over a segment of chunks the rule is affine in the
 // incoming state: S_out = M_g S_in + N_g.  Running the same chunk recurrence
 // on a state started at 0 with the segment's values gives N_g; running it on a
-// state started at I with zero values gives M_g (each state column evolves
-// independently, so the two are separate workgroups).  Three launches:
+// state started at I with zero values gives M_g.  Each state column evolves
+// independently, so both ride in one workgroup as extra columns and share the
+// chunk's T and W.  Three launches:
 //   delta_chunk<MAP>  (M_g, N_g) for every segment but the last
 //   delta_compose     S_in(g+1) = M_g S_in(g) + N_g, fp32 MFMA, serial in g
 //   delta_chunk<OUT>  the chunk loop from S_in(g), writing O (and S_T last)
@@ -46,22 +47,21 @@ struct DL {
     static constexpr int KS = CH * LQ * 2;          // K_c rows (read transposed too)
     static constexpr int WS = CH * LQ * 2;          // W rows
     static constexpr int QS = OUT ? CH * LQ * 2 : 0;
-    static constexpr int XT = NS * LQ * 2;          // state^T (bf16)
     static constexpr int VS = CH * LV * 2;          // V_c rows (read transposed)
-    static constexpr int UT = NS * LT * 2;          // (beta o U)^T
     static constexpr int TS = CH * LT * 2;          // T (bf16)
+    static constexpr int PS = OUT ? CH * LT * 2 : 0;  // tril(Q K^T), rows = queries
     static constexpr int AF = CH * LF * 4;          // A, then T blocks (fp32)
     static constexpr int BS = CH * 4;               // beta (fp32)
-    static constexpr int TOTAL = KS + WS + QS + XT + VS + UT + TS + AF + BS;
+    static constexpr int TOTAL = KS + WS + QS + VS + TS + PS + AF + BS;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
-    // state tiles (DK/16 x NS/16) over eight waves
-    static constexpr int XR = DK / 16;
-    static constexpr int XC = NS / 16;
-    static constexpr int X_CPW = XR * XC / NWV;
-    // C x NS tiles (4 x XC) over eight waves: row tile w%4, half the columns
-    static constexpr int O_CPW = XC / 2;
-    // W^T tiles (XR x 4) over eight waves
-    static constexpr int W_TPW = 4 * XR / NWV;
+    static constexpr int XR = DK / 16;              // dk row tiles of a state column
+    // State column tiles: OUT carries S (NS columns); MAP carries N (NS
+    // columns, zero start, with values) and M (DK columns, identity start, no
+    // values).  Wave w owns tiles w, w + 8, ...
+    static constexpr int NCN = NS / 16;
+    static constexpr int NCT = OUT ? NCN : NCN + DK / 16;
+    static constexpr int SLOTS = (NCT + NWV - 1) / NWV;
+    static constexpr int W_TPW = 4 * XR / NWV;      // W^T tiles per wave
 };
 
 // The ten lower 16x16 tiles of a 64x64 matrix: diagonal first.
@@ -72,67 +72,65 @@ __device__ __forceinline__ void lower_tile(int id, int& i, int& j) {
     else { i = 3; j = 0; }                         // (3,0)
 }
 
+// One workgroup runs one segment's chunk loop.  The state-dependent part of
+// a chunk is column-parallel (state columns evolve independently), so each
+// wave owns whole state columns and keeps them, its corrections U and its
+// outputs in registers:
+//   U[:, c]  = U_v[:, c] - W S[:, c]            (W S from registers: S tiles are B operands)
+//   O^T[c]   = S[:, c]^T Q^T + (beta o U[:, c])^T P^T   (OUT; S before the update)
+//   S[:, c] += K^T (beta o U[:, c])
+// The shared, state-free part (A, P, T, W) is computed by all waves through
+// LDS.  MAP runs N and M in the same workgroup, so T and W are built once.
 template <int DK, int NS, bool OUT>
 __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ beta, bf16_t* __restrict__ o, const float* __restrict__ state_in,
-    float* __restrict__ map_n, float* __restrict__ map_m, float* __restrict__ S_out, int T, int L,
-    int G, int part_base) {
+    float* __restrict__ map_n, float* __restrict__ map_m, float* __restrict__ S_out, int T, int L, int G) {
     using Y = DL<DK, NS, OUT>;
     using M = Mma<bf16_t>;
     using MF = Mma<float>;
     typedef M::frag frag;
-    constexpr int LQ = Y::LQ, LT = Y::LT, LF = Y::LF;
+    constexpr int LQ = Y::LQ, LV = Y::LV, LT = Y::LT, LF = Y::LF, XR = Y::XR, SLOTS = Y::SLOTS;
     __shared__ __align__(16) unsigned char smem[Y::TOTAL];
-    constexpr int LV = Y::LV;
     unsigned char* sp = smem;
     __bf16* Ks = reinterpret_cast<__bf16*>(sp);  sp += Y::KS;
     __bf16* Ws = reinterpret_cast<__bf16*>(sp);  sp += Y::WS;
     __bf16* Qs = reinterpret_cast<__bf16*>(sp);  sp += Y::QS;
-    __bf16* Xt = reinterpret_cast<__bf16*>(sp);  sp += Y::XT;
     __bf16* Vs = reinterpret_cast<__bf16*>(sp);  sp += Y::VS;
-    __bf16* Ut = reinterpret_cast<__bf16*>(sp);  sp += Y::UT;
     __bf16* Ts = reinterpret_cast<__bf16*>(sp);  sp += Y::TS;
+    __bf16* Ps = reinterpret_cast<__bf16*>(sp);  sp += Y::PS;
     float* Af = reinterpret_cast<float*>(sp);
     float* Bs = Af + CH * LF;
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int w = wave_id(tid);
-    int head, seg, part;
-    if constexpr (OUT) {
-        head = blockIdx.x / G;
-        seg = blockIdx.x % G;
-        part = 0;
-    } else {
-        head = blockIdx.x / (G - 1);
-        seg = blockIdx.x % (G - 1);
-        part = part_base + blockIdx.y;  // 0: N_g (values, zero start); 1: M_g (identity start)
-    }
-    const bool has_v = OUT || part == 0;
+    const int G1 = OUT ? G : G - 1;  // workgroups per head
+    const int head = blockIdx.x / G1, seg = blockIdx.x % G1;
     const bf16_t* kh = k + (long)head * T * DK;
     const bf16_t* qh = q + (long)head * T * DK;
     const bf16_t* vh = v + (long)head * T * NS;
     const bf16_t* bh = beta + (long)head * T;
 
-    // state tiles owned by this wave: row tile xrt, column tiles xc0 .. xc0+X_CPW-1
-    const int xrt = w % Y::XR, xc0 = (w / Y::XR) * Y::X_CPW;
-    // C x NS tiles owned by this wave: row tile ort, column tiles oc0 ..
-    const int ort = w % 4, oc0 = (w / 4) * Y::O_CPW;
-
-    v4f X[Y::X_CPW];
+    // this wave's state column tiles: slot j holds tile id w + 8j (if < NCT);
+    // ids below NCN are columns of S (OUT) or N (MAP), the rest columns of M
+    v4f X[SLOTS][XR];
 #pragma unroll
-    for (int c = 0; c < Y::X_CPW; ++c) {
+    for (int j = 0; j < SLOTS; ++j) {
+        const int id = w + NWV * j;
+        const bool is_m = id >= Y::NCN;
+        const int col = 16 * (is_m ? id - Y::NCN : id) + li;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * xrt + 4 * g + r, col = 16 * (xc0 + c) + li;
-            float x = 0.f;
-            if constexpr (OUT) {
-                x = state_in[((long)(head * G + seg) * DK + row) * NS + col];
-            } else {
-                if (part == 1) x = (row == col) ? 1.f : 0.f;
+        for (int i = 0; i < XR; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * i + 4 * g + r;
+                float x = 0.f;
+                if (id < Y::NCT) {
+                    if constexpr (OUT) x = state_in[((long)(head * G + seg) * DK + row) * NS + col];
+                    else x = (is_m && row == col) ? 1.f : 0.f;
+                }
+                X[j][i][r] = x;
             }
-            X[c][r] = x;
-        }
     }
 
     const int t_end = min((seg + 1) * L, T);
@@ -145,77 +143,69 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         const int nn = min(CH, t_end - c);
         kr.load(kh, c, nn, tid);
         if constexpr (OUT) qr.load(qh, c, nn, tid);
-        if (has_v) vr.load(vh, c, nn, tid);
+        vr.load(vh, c, nn, tid);
         if (tid < CH) bnext = tid < nn ? bf16_to_f32(bh[c + tid]) : 0.f;
     };
     load_chunk(seg * L);
+    // Upper tiles of P (keys after every query of the tile) are read as zero
+    // operands and never written: clear them once.
+    if constexpr (OUT) {
+        for (int e = tid; e < 6 * 256; e += NT) {
+            const int tile = e >> 8, r = (e >> 4) & 15, c = e & 15;
+            const int bi = tile < 3 ? 0 : tile < 5 ? 1 : 2;
+            const int bj = tile < 3 ? tile + 1 : tile < 5 ? tile - 1 : 3;
+            Ps[(16 * bi + r) * LT + 16 * bj + c] = M::cvt(0.f);
+        }
+    }
     for (int c0 = seg * L; c0 < t_end; c0 += CH) {
         const int n = min(CH, t_end - c0);
-        // ---- stage the chunk (row-major; transposed operands are read with
-        // transpose loads); the state goes to LDS as bf16, transposed
+        // ---- stage the chunk row-major (transposed operands are read with
+        // transpose loads)
         stage_rows_raw<bf16_t, DK, NT>(kr, tid, Ks, LQ);
         if constexpr (OUT) stage_rows_raw<bf16_t, DK, NT>(qr, tid, Qs, LQ);
-        if (has_v) stage_rows_raw<bf16_t, NS, NT>(vr, tid, Vs, LV);
+        stage_rows_raw<bf16_t, NS, NT>(vr, tid, Vs, LV);
         if (tid < CH) Bs[tid] = bnext;
         if (c0 + CH < t_end) load_chunk(c0 + CH);
-#pragma unroll
-        for (int c = 0; c < Y::X_CPW; ++c) {
-            __bf16* dst = &Xt[(16 * (xc0 + c) + li) * LQ + 16 * xrt + 4 * g];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dst[r] = M::cvt(X[c][r]);
-        }
         __syncthreads();
 
-        // ---- A = tril_{-1}(K K^T) diag(beta) into Af (lower tiles only)
-#pragma unroll
-        for (int rep = 0; rep < 2; ++rep) {
-            const int id = w + NWV * rep;
+        // ---- A = tril_{-1}(K K^T) diag(beta) (fp32) and, for outputs, the
+        // causal scores P = tril(Q K^T) (bf16, rows = queries), computed as
+        // transposed tiles so each lane writes four consecutive keys
+        constexpr int NTILE = OUT ? 20 : 10;
+        for (int id = w; id < NTILE; id += NWV) {
+            int bi, bj;
+            lower_tile(id % 10, bi, bj);
+            v4f acc = zero4();
             if (id < 10) {
-                int bi, bj;
-                lower_tile(id, bi, bj);
-                v4f acc = zero4();
 #pragma unroll
-                for (int kb = 0; kb < DK / 32; ++kb) {
-                    const frag a = M::load(&Ks[(16 * bi + li) * LQ + 32 * kb], g);
-                    const frag b = M::load(&Ks[(16 * bj + li) * LQ + 32 * kb], g);
-                    M::mma(acc, a, b);
-                }
+                for (int kb = 0; kb < DK / 32; ++kb)
+                    M::mma(acc, M::load(&Ks[(16 * bi + li) * LQ + 32 * kb], g), M::load(&Ks[(16 * bj + li) * LQ + 32 * kb], g));
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int t = 16 * bi + 4 * g + r, i = 16 * bj + li;
                     Af[t * LF + i] = (i < t) ? Bs[i] * acc[r] : 0.f;
                 }
+            } else {
+                // keys of tile bj (rows) x queries of tile bi (columns)
+#pragma unroll
+                for (int kb = 0; kb < DK / 32; ++kb)
+                    M::mma(acc, M::load(&Ks[(16 * bj + li) * LQ + 32 * kb], g), M::load(&Qs[(16 * bi + li) * LQ + 32 * kb], g));
+                __bf16* dst = &Ps[(16 * bi + li) * LT + 16 * bj + 4 * g];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[r] = M::cvt((bi == bj && 4 * g + r > li) ? 0.f : acc[r]);
             }
         }
-        // ---- P^T tiles (keys x this wave's queries) and O = Q S
-        v4f Pt[4];
-        v4f Oacc[Y::O_CPW];
+        // outputs, first half: O^T = S^T Q^T with the state entering the chunk
+        v4f Oq[OUT ? 4 : 1];
         if constexpr (OUT) {
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-                Pt[kt] = zero4();
-                if (kt <= ort) {
+            for (int qt = 0; qt < 4; ++qt) {
+                Oq[qt] = zero4();
+                if (w < Y::NCT) {
 #pragma unroll
-                    for (int kb = 0; kb < DK / 32; ++kb) {
-                        const frag a = M::load(&Ks[(16 * kt + li) * LQ + 32 * kb], g);
-                        const frag b = M::load(&Qs[(16 * ort + li) * LQ + 32 * kb], g);
-                        M::mma(Pt[kt], a, b);
-                    }
-                    if (kt == ort) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (4 * g + r > li) Pt[kt][r] = 0.f;
-                    }
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < Y::O_CPW; ++c) {
-                Oacc[c] = zero4();
-#pragma unroll
-                for (int kb = 0; kb < DK / 32; ++kb) {
-                    const frag a = M::load(&Qs[(16 * ort + li) * LQ + 32 * kb], g);
-                    const frag b = M::load(&Xt[(16 * (oc0 + c) + li) * LQ + 32 * kb], g);
-                    M::mma(Oacc[c], a, b);
+                    for (int kb = 0; kb < DK / 32; ++kb)
+                        M::mma(Oq[qt], M::from_tiles(X[0][2 * kb], X[0][2 * kb + 1]),
+                               M::load(&Qs[(16 * qt + li) * LQ + 32 * kb], g));
                 }
             }
         }
@@ -241,8 +231,9 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         }
         __syncthreads();
 
-        // ---- off-diagonal blocks, by distance from the diagonal.  T_ij
-        // (i > j) is stored in the (unused) upper block at rows 16j, cols 16i.
+        // ---- off-diagonal blocks, by distance from the diagonal:
+        // T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj, stored (i > j) in the unused
+        // upper block at rows 16j, cols 16i.
 #pragma unroll
         for (int dist = 1; dist < 4; ++dist) {
             if (w >= 1 && w <= 4 - dist) {
@@ -276,100 +267,109 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         }
         __syncthreads();
 
-        // ---- W = T K (written transposed-computed so rows land as 8-byte
-        // stores) and U_v = T V
+        // ---- W = T K (computed as transposed tiles, rows land as 8-byte
+        // stores) and this wave's U_v = T V columns
 #pragma unroll
         for (int c = 0; c < Y::W_TPW; ++c) {
-            const int dkt = w % Y::XR, tt = (w / Y::XR) * Y::W_TPW + c;
+            const int dkt = w % XR, tt = (w / XR) * Y::W_TPW + c;
             v4f acc = zero4();
 #pragma unroll
             for (int kb = 0; kb < CH / 32; ++kb) {
-                const frag a = M::load_tr(Ks, LQ, 32 * kb, 16 * dkt, lane);
-                const frag b = M::load(&Ts[(16 * tt + li) * LT + 32 * kb], g);
-                M::mma(acc, a, b);
+                if (32 * kb > 16 * tt + 15) continue;  // T is lower triangular
+                M::mma(acc, M::load_tr(Ks, LQ, 32 * kb, 16 * dkt, lane), M::load(&Ts[(16 * tt + li) * LT + 32 * kb], g));
             }
             __bf16* dst = &Ws[(16 * tt + li) * LQ + 16 * dkt + 4 * g];
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[r] = M::cvt(acc[r]);
         }
-        v4f U[Y::O_CPW];
+        v4f U[SLOTS][4];
 #pragma unroll
-        for (int c = 0; c < Y::O_CPW; ++c) {
-            U[c] = zero4();
-            if (has_v) {
+        for (int j = 0; j < SLOTS; ++j) {
+            const int id = w + NWV * j;
 #pragma unroll
-                for (int kb = 0; kb < CH / 32; ++kb) {
-                    if (32 * kb > 16 * ort + 15) continue;  // T is lower triangular
-                    const frag a = M::load(&Ts[(16 * ort + li) * LT + 32 * kb], g);
-                    const frag b = M::load_tr(Vs, LV, 32 * kb, 16 * (oc0 + c), lane);
-                    M::mma(U[c], a, b);
+            for (int tt = 0; tt < 4; ++tt) {
+                U[j][tt] = zero4();
+                if (id < Y::NCN) {
+#pragma unroll
+                    for (int kb = 0; kb < CH / 32; ++kb) {
+                        if (32 * kb > 16 * tt + 15) continue;
+                        M::mma(U[j][tt], M::load(&Ts[(16 * tt + li) * LT + 32 * kb], g),
+                               M::load_tr(Vs, LV, 32 * kb, 16 * id, lane));
+                    }
                 }
             }
         }
         __syncthreads();
 
-        // ---- U = U_v - W S, then (beta o U)^T to LDS
+        // ---- the state chain, per owned column tile
 #pragma unroll
-        for (int c = 0; c < Y::O_CPW; ++c) {
-            v4f ws_ = zero4();
+        for (int j = 0; j < SLOTS; ++j) {
+            const int id = w + NWV * j;
+            if (id >= Y::NCT) continue;
+            // U = U_v - W S, then beta o U
 #pragma unroll
-            for (int kb = 0; kb < DK / 32; ++kb) {
-                const frag a = M::load(&Ws[(16 * ort + li) * LQ + 32 * kb], g);
-                const frag b = M::load(&Xt[(16 * (oc0 + c) + li) * LQ + 32 * kb], g);
-                M::mma(ws_, a, b);
+            for (int tt = 0; tt < 4; ++tt) {
+                v4f ws_ = zero4();
+#pragma unroll
+                for (int kb = 0; kb < DK / 32; ++kb)
+                    M::mma(ws_, M::load(&Ws[(16 * tt + li) * LQ + 32 * kb], g),
+                           M::from_tiles(X[j][2 * kb], X[j][2 * kb + 1]));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) U[j][tt][r] = Bs[16 * tt + 4 * g + r] * (U[j][tt][r] - ws_[r]);
             }
-            __bf16* dst = &Ut[(16 * (oc0 + c) + li) * LT + 16 * ort + 4 * g];
+            if constexpr (OUT) {
+                // outputs, second half: O^T += (beta o U)^T P^T, stored
+                bf16_t* oh = o + ((long)head * T + c0) * NS + 16 * id + 4 * g;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                U[c][r] -= ws_[r];
-                dst[r] = M::cvt(Bs[16 * ort + 4 * g + r] * U[c][r]);
+                for (int qt = 0; qt < 4; ++qt) {
+#pragma unroll
+                    for (int kb = 0; kb < CH / 32; ++kb) {
+                        if (32 * kb > 16 * qt + 15) continue;  // keys after these queries
+                        M::mma(Oq[qt], M::from_tiles(U[j][2 * kb], U[j][2 * kb + 1]),
+                               M::load(&Ps[(16 * qt + li) * LT + 32 * kb], g));
+                    }
+                    const int t = 16 * qt + li;
+                    if (t < n) {
+                        uint2 pk;
+                        pk.x = pack_bf16x2(Oq[qt][0], Oq[qt][1]);
+                        pk.y = pack_bf16x2(Oq[qt][2], Oq[qt][3]);
+                        *reinterpret_cast<uint2*>(oh + (long)t * NS) = pk;
+                    }
+                }
             }
+            // S += K^T (beta o U)
+#pragma unroll
+            for (int i = 0; i < XR; ++i)
+#pragma unroll
+                for (int kb = 0; kb < CH / 32; ++kb)
+                    M::mma(X[j][i], M::load_tr(Ks, LQ, 32 * kb, 16 * i, lane),
+                           M::from_tiles(U[j][2 * kb], U[j][2 * kb + 1]));
         }
         __syncthreads();
+    }
 
-        // ---- S += K^T (beta o U);  O = Q S + tril(Q K^T) (beta o U)
+    // ---- the segment's result: S_T (OUT, last segment) or the maps (MAP)
 #pragma unroll
-        for (int c = 0; c < Y::X_CPW; ++c) {
-#pragma unroll
-            for (int kb = 0; kb < CH / 32; ++kb) {
-                const frag a = M::load_tr(Ks, LQ, 32 * kb, 16 * xrt, lane);
-                const frag b = M::load(&Ut[(16 * (xc0 + c) + li) * LT + 32 * kb], g);
-                M::mma(X[c], a, b);
-            }
-        }
+    for (int j = 0; j < SLOTS; ++j) {
+        const int id = w + NWV * j;
+        if (id >= Y::NCT) continue;
+        const bool is_m = id >= Y::NCN;
+        float* dst;
+        int ld, col;
         if constexpr (OUT) {
-            bf16_t* oh = o + ((long)head * T + c0) * NS;
-#pragma unroll
-            for (int c = 0; c < Y::O_CPW; ++c) {
-#pragma unroll
-                for (int j = 0; j < CH / 32; ++j) {
-                    if (32 * j > 16 * ort + 15) continue;  // keys after these queries
-                    const frag a = M::from_tiles(Pt[2 * j], Pt[2 * j + 1]);
-                    const frag b = M::load(&Ut[(16 * (oc0 + c) + li) * LT + 32 * j], g);
-                    M::mma(Oacc[c], a, b);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * ort + 4 * g + r;
-                    if (t < n) oh[(long)t * NS + 16 * (oc0 + c) + li] = f32_to_bf16(Oacc[c][r]);
-                }
-            }
+            if (seg != G - 1 || !S_out) continue;
+            dst = S_out + (long)head * DK * NS;
+            ld = NS;
+            col = 16 * id + li;
+        } else {
+            dst = is_m ? map_m + (long)(head * G + seg) * DK * DK : map_n + (long)(head * G + seg) * DK * NS;
+            ld = is_m ? DK : NS;
+            col = 16 * (is_m ? id - Y::NCN : id) + li;
         }
-        __syncthreads();
-    }
-
-    float* dst = nullptr;
-    if constexpr (OUT) {
-        if (seg == G - 1 && S_out) dst = S_out + (long)head * DK * NS;
-    } else {
-        dst = (part == 0 ? map_n : map_m) + (long)(head * G + seg) * DK * NS;
-    }
-    if (dst) {
 #pragma unroll
-        for (int c = 0; c < Y::X_CPW; ++c)
+        for (int i = 0; i < XR; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                dst[(16 * xrt + 4 * g + r) * NS + 16 * (xc0 + c) + li] = X[c][r];
+            for (int r = 0; r < 4; ++r) dst[(16 * i + 4 * g + r) * ld + col] = X[j][i][r];
     }
 }
 
@@ -445,22 +445,14 @@ hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const
     float* state_in = map_m + (size_t)HT * G * DK * DK;
     hipError_t err;
     if (G > 1) {
-        if constexpr (DK == DV) {
-            delta_chunk_kernel<DK, DK, false><<<dim3(HT * (G - 1), 2), dim3(NT), 0, stream>>>(
-                q, k, v, beta, nullptr, nullptr, map_n, map_m, nullptr, T, L, G, 0);
-        } else {
-            delta_chunk_kernel<DK, DV, false><<<dim3(HT * (G - 1), 1), dim3(NT), 0, stream>>>(
-                q, k, v, beta, nullptr, nullptr, map_n, map_m, nullptr, T, L, G, 0);
-            if ((err = hipGetLastError()) != hipSuccess) return err;
-            delta_chunk_kernel<DK, DK, false><<<dim3(HT * (G - 1), 1), dim3(NT), 0, stream>>>(
-                q, k, v, beta, nullptr, nullptr, map_n, map_m, nullptr, T, L, G, 1);
-        }
+        delta_chunk_kernel<DK, DV, false><<<dim3(HT * (G - 1)), dim3(NT), 0, stream>>>(
+            q, k, v, beta, nullptr, nullptr, map_n, map_m, nullptr, T, L, G);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     delta_compose_kernel<DK, DV><<<dim3(DV / 16, HT), dim3(256), 0, stream>>>(map_n, map_m, S0, state_in, G);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     delta_chunk_kernel<DK, DV, true><<<dim3(HT * G), dim3(NT), 0, stream>>>(
-        q, k, v, beta, o, state_in, nullptr, nullptr, S_out, T, L, G, 0);
+        q, k, v, beta, o, state_in, nullptr, nullptr, S_out, T, L, G);
     return hipGetLastError();
 }
 
