@@ -147,8 +147,14 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         if (tid < CH) bnext = tid < nn ? bf16_to_f32(bh[c + tid]) : 0.f;
     };
     load_chunk(seg * L);
-    // Upper tiles of P (keys after every query of the tile) are read as zero
-    // operands and never written: clear them once.
+    // Upper blocks of T and, for outputs, of P (keys after every query of
+    // the tile) are read as zero operands and never written: clear them once.
+    for (int e = tid; e < 6 * 256; e += NT) {
+        const int tile = e >> 8, r = (e >> 4) & 15, c = e & 15;
+        const int bi = tile < 3 ? 0 : tile < 5 ? 1 : 2;
+        const int bj = tile < 3 ? tile + 1 : tile < 5 ? tile - 1 : 3;
+        Ts[(16 * bi + r) * LT + 16 * bj + c] = M::cvt(0.f);
+    }
     if constexpr (OUT) {
         for (int e = tid; e < 6 * 256; e += NT) {
             const int tile = e >> 8, r = (e >> 4) & 15, c = e & 15;
@@ -195,24 +201,31 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
                 for (int r = 0; r < 4; ++r) dst[r] = M::cvt((bi == bj && 4 * g + r > li) ? 0.f : acc[r]);
             }
         }
-        // outputs, first half: O^T = S^T Q^T with the state entering the chunk
-        v4f Oq[OUT ? 4 : 1];
-        if constexpr (OUT) {
-#pragma unroll
-            for (int qt = 0; qt < 4; ++qt) {
-                Oq[qt] = zero4();
-                if (w < Y::NCT) {
-#pragma unroll
-                    for (int kb = 0; kb < DK / 32; ++kb)
-                        M::mma(Oq[qt], M::from_tiles(X[0][2 * kb], X[0][2 * kb + 1]),
-                               M::load(&Qs[(16 * qt + li) * LQ + 32 * kb], g));
-                }
-            }
-        }
         __syncthreads();
 
+        // outputs, first half: O^T = S^T Q^T with the state entering the chunk
+        // (waves 1.. here, while wave 0 inverts the diagonal blocks; wave 0
+        // while waves 1..3 build the off-diagonal blocks)
+        v4f Oq[OUT ? 4 : 1];
+        auto out_first_half = [&]() {
+            if constexpr (OUT) {
+#pragma unroll
+                for (int qt = 0; qt < 4; ++qt) {
+                    Oq[qt] = zero4();
+                    if (w < Y::NCT) {
+#pragma unroll
+                        for (int kb = 0; kb < DK / 32; ++kb)
+                            M::mma(Oq[qt], M::from_tiles(X[0][2 * kb], X[0][2 * kb + 1]),
+                                   M::load(&Qs[(16 * qt + li) * LQ + 32 * kb], g));
+                    }
+                }
+            }
+        };
+        if (w != 0) out_first_half();
+
         // ---- diagonal blocks of T: (I + A_bb)^{-1} by forward substitution.
-        // Wave 0, lane 16b+j holds column j of block b in registers.
+        // Wave 0, lane 16b+j holds column j of block b in registers; the
+        // block goes to Af (fp32, for the off-diagonal blocks) and Ts (bf16).
         if (w == 0) {
             const int b = g, j = li;
             float d[16];
@@ -227,9 +240,13 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
                 if (i > j) d[i] = -s;
             }
 #pragma unroll
-            for (int m = 0; m < 16; ++m) Af[(16 * b + m) * LF + 16 * b + j] = d[m];
+            for (int m = 0; m < 16; ++m) {
+                Af[(16 * b + m) * LF + 16 * b + j] = d[m];
+                Ts[(16 * b + m) * LT + 16 * b + j] = M::cvt(d[m]);
+            }
         }
         __syncthreads();
+        if (w == 0) out_first_half();
 
         // ---- off-diagonal blocks, by distance from the diagonal:
         // T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj, stored (i > j) in the unused
@@ -252,20 +269,13 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
                 const v4f a = *reinterpret_cast<const v4f*>(&Af[(16 * i + li) * LF + 16 * i + 4 * g]);
                 MF::mma(Tij, a, P);  // an output tile is already in B-operand layout
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Af[(16 * j + 4 * g + r) * LF + 16 * i + li] = -Tij[r];
+                for (int r = 0; r < 4; ++r) {
+                    Af[(16 * j + 4 * g + r) * LF + 16 * i + li] = -Tij[r];
+                    Ts[(16 * i + 4 * g + r) * LT + 16 * j + li] = M::cvt(-Tij[r]);  // T[t][k]: t in block i, k in j
+                }
             }
             __syncthreads();
         }
-
-        // ---- T to bf16, lower triangular, rows t, k = i
-        for (int e = tid; e < CH * CH; e += NT) {
-            const int t = e / CH, i = e % CH, bt = t / 16, bi = i / 16;
-            float x = 0.f;
-            if (bt == bi) x = Af[t * LF + i];
-            else if (bt > bi) x = Af[(16 * bi + t % 16) * LF + 16 * bt + i % 16];
-            Ts[t * LT + i] = M::cvt(x);
-        }
-        __syncthreads();
 
         // ---- W = T K (computed as transposed tiles, rows land as 8-byte
         // stores) and this wave's U_v = T V columns
