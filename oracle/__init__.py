@@ -27,6 +27,11 @@ Functions and what pins them (the pins are in ``tests/test_oracle_pins.py``):
     dense form and the orthonormal-key reduction.
 ``la_decode_step`` -- one in-place step; pinned by equality with one token of
     ``la_forward`` continued from the same state.
+``delta_decode_step`` -- one in-place delta-rule step.  Pinned by the LA-SSM
+    page's 4-token delta example replayed one step at a time (every
+    intermediate state and the final read of k_1), the bit-exact overwrite
+    with basis keys and beta = 1, beta = 0 leaving the state unchanged, and
+    a step chain equal to ``delta_forward`` over the same tokens.
 """
 from __future__ import annotations
 
@@ -77,6 +82,8 @@ def _load():
             lib.la_ref_decode_step.argtypes = [dp, dp, dp, dp, dp, dp,
                                                i, i, i, i, ctypes.c_double]
             lib.la_ref_decode_step.restype = None
+            lib.delta_ref_decode_step.argtypes = [dp, dp, dp, dp, dp, dp, i, i, i, i]
+            lib.delta_ref_decode_step.restype = None
             lib.oracle_phi.argtypes = [dp, dp, ctypes.c_long]
             lib.oracle_phi.restype = None
             lib.oracle_num_threads.argtypes = []
@@ -159,3 +166,18 @@ def la_decode_step(q, k, v, S, z, eps=1e-6):
     _load().la_ref_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z),
                                _ptr(o), N, H, dk, dv, float(eps))
     return o, S, z
+
+
+def delta_decode_step(q, k, v, beta, S):
+    """One delta-rule step on a copy of S.  q, k: [N,H,dk]; v: [N,H,dv];
+    beta: [N,H]; S: [N,H,dk,dv] -> (o [N,H,dv], S_new)."""
+    q, k, v, beta = map(_f64, (q, k, v, beta))
+    S = _f64(S).copy()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and v.shape == (N, H, dv) and beta.shape == (N, H)
+    assert S.shape == (N, H, dk, dv)
+    o = np.empty((N, H, dv))
+    _load().delta_ref_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S), _ptr(o),
+                                  N, H, dk, dv)
+    return o, S

@@ -188,6 +188,39 @@ void la_ref_decode_step(const double* q, const double* k, const double* v,
     }
 }
 
+/*
+ * One decode step of the delta-rule fast-weight memory on a resident state,
+ * updated in place ([LinearMem] §03 "从累加改成纠错" and [Recurrence]
+ * "Delta-rule fast weight" for the write; §05 for updating the inference
+ * state in place): the correction u = v - S^T k (the new value minus what the
+ * memory predicts for k), then S += beta k u^T, then the write-then-read
+ * output o = S^T q with the updated state.
+ *   q, k [N][H][dk]   v, o [N][H][dv]   beta [N][H]   S [N][H][dk][dv]
+ */
+void delta_ref_decode_step(const double* q, const double* k, const double* v,
+                           const double* beta, double* S, double* o,
+                           int N, int H, int dk, int dv) {
+    const long states = (long)N * H;
+#pragma omp parallel for schedule(static)
+    for (long s = 0; s < states; ++s) {
+        const double* qs = q + s * dk;
+        const double* ks = k + s * dk;
+        const double* vs = v + s * dv;
+        double* Ss = S + s * (long)dk * dv;
+        for (int j = 0; j < dv; ++j) {
+            double pred = 0.0;
+            for (int i = 0; i < dk; ++i) pred += ks[i] * Ss[(long)i * dv + j];
+            const double u = vs[j] - pred;
+            for (int i = 0; i < dk; ++i) Ss[(long)i * dv + j] += beta[s] * ks[i] * u;
+        }
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i) acc += qs[i] * Ss[(long)i * dv + j];
+            o[s * dv + j] = acc;
+        }
+    }
+}
+
 /* The feature map alone, so tests can pin its branches directly. */
 void oracle_phi(const double* x, double* y, long n) {
     for (long i = 0; i < n; ++i) y[i] = phi_elu1(x[i]);

@@ -425,3 +425,60 @@ def test_decode_chain_equals_forward_over_the_same_tokens():
     np.testing.assert_allclose(np.stack(outs, 2), of, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(S, Sf, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(z, zf, rtol=1e-12, atol=1e-13)
+
+
+def _dstep(q, k, v, beta, S):
+    """One delta decode step on a single state: vectors -> (o, S)."""
+    o, S = oracle.delta_decode_step(np.asarray(q, float)[None, None], np.asarray(k, float)[None, None],
+                                    np.asarray(v, float)[None, None], np.array([[beta]], float),
+                                    np.asarray(S, float)[None, None])
+    return o[0, 0], S[0, 0]
+
+
+def test_delta_decode_four_token_example_lassm():
+    # LA-SSM page §1.3: the delta rule with beta = 1 over four tokens, every
+    # intermediate state printed (value-first there, hence the transposes).
+    g = _golden("lassm_four_token_example.json")
+    keys, values = np.array(g["keys"]), np.array(g["values"])
+    S = np.zeros((2, 2))
+    for t in range(4):
+        q = keys[0] if t == 3 else keys[t]
+        o, S = _dstep(q, keys[t], values[t], 1.0, S)
+        np.testing.assert_allclose(S, np.array(g["delta_states_value_first"][t]).T, atol=1e-14)
+    np.testing.assert_allclose(o, g["delta_read_k1"], atol=1e-14)
+
+
+def test_delta_decode_exact_overwrite_and_zero_beta():
+    # Unit (basis) key with beta = 1: reading the same key right after the
+    # write returns the new value exactly; beta = 0 leaves the state alone.
+    rng = np.random.default_rng(41)
+    dk, dv = 8, 5
+    S0 = rng.integers(-64, 64, size=(dk, dv)) / 16.0
+    for i in range(dk):
+        key = np.eye(dk)[i]
+        val = rng.integers(-64, 64, size=dv) / 8.0
+        o, S1 = _dstep(key, key, val, 1.0, S0)
+        assert np.array_equal(o, val)
+        assert np.array_equal(np.delete(S1, i, axis=0), np.delete(S0, i, axis=0))
+        q = rng.normal(size=dk)
+        o0, S2 = _dstep(q, rng.normal(size=dk), rng.normal(size=dv), 0.0, S0)
+        assert np.array_equal(S2, S0)
+        np.testing.assert_allclose(o0, S0.T @ q, rtol=1e-15, atol=1e-15)
+
+
+def test_delta_decode_chain_equals_forward_over_the_same_tokens():
+    rng = np.random.default_rng(42)
+    N, H, dk, dv, steps = 2, 3, 5, 4, 30
+    S = rng.normal(scale=0.1, size=(N, H, dk, dv))
+    k = rng.normal(size=(steps, N, H, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    q, v = rng.normal(size=(steps, N, H, dk)), rng.normal(size=(steps, N, H, dv))
+    beta = rng.uniform(0.0, 1.0, size=(steps, N, H))
+    of, Sf = oracle.delta_forward(q.transpose(1, 2, 0, 3), k.transpose(1, 2, 0, 3), v.transpose(1, 2, 0, 3),
+                                  beta.transpose(1, 2, 0), S0=S)
+    outs = []
+    for t in range(steps):
+        o, S = oracle.delta_decode_step(q[t], k[t], v[t], beta[t], S)
+        outs.append(o)
+    np.testing.assert_allclose(np.stack(outs, 2), of, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(S, Sf, rtol=1e-12, atol=1e-13)
