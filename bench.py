@@ -13,8 +13,8 @@ The line printed is one JSON object:
 * cpu_baseline: the fp64 oracle (C, OpenMP over heads) timed on the host on
   the same workload;
 * extra: the other measured paths -- the long-stream LA workload, the delta
-  rule workload and the 1000-step decode chain (state-update GB/s) -- each
-  with its own roofline fraction.
+  rule workload and the 1000-step decode chains of both rules (state-update
+  GB/s) -- each with its own roofline fraction.
 
 Inputs are synthetic (seeded, generated on the device) and rotate among
 several copies so that each step reads data evicted from the 256 MB
@@ -86,6 +86,11 @@ def delta_flops(B, H, T, dk, dv, C=64):
 
 def decode_bytes(N, H, dk, dv, el):
     return N * H * (2 * dk * dv * 4 + 2 * dk * 4 + (2 * dk + dv) * el + dv * el)
+
+
+def delta_decode_bytes(N, H, dk, dv, el):
+    # S read and written (fp32); q, k, v, beta read; o written
+    return N * H * (2 * dk * dv * 4 + (2 * dk + dv + 1) * el + dv * el)
 
 
 def _events(n):
@@ -172,6 +177,22 @@ def bench_decode(w, lin, wl, n_steps=None):
             "gbs_wall": per * n / wall / 1e9, "gbs": per / (mean_ms * 1e-3) / 1e9}
 
 
+def bench_delta_decode(w, lin, wl, n_steps=None):
+    dev = torch.device("cuda:0")
+    S, Q, K, V, Bt = wl.make(w, dev)
+    n = w.T if n_steps is None else n_steps
+    o = torch.empty((w.B, w.H, w.dv), dtype=w.dtype, device=dev)
+
+    def step(i):
+        j = i % w.T
+        lin.delta_decode_step(Q[j], K[j], V[j], Bt[j], S, o=o)
+
+    wall, mean_ms = time_calls(step, n, 10, torch.cuda.current_stream(dev))
+    per = delta_decode_bytes(w.B, w.H, w.dk, w.dv, 2)
+    return {"steps": n, "ms_per_step": 1e3 * wall / n, "event_ms_mean": mean_ms, "bytes_per_step": per,
+            "gbs_wall": per * n / wall / 1e9, "gbs": per / (mean_ms * 1e-3) / 1e9}
+
+
 def cpu_baseline(w, oracle, wl, heads=None):
     """The fp64 oracle on the host, same workload recipe (generated on the CPU)."""
     q, k, v = wl.la_inputs(w.B, w.H, w.T, w.dk, w.dv, w.dtype, w.seed, "cpu")
@@ -205,7 +226,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=4, help="input copies rotated through (cache eviction)")
-    ap.add_argument("--only", choices=["all", "la", "la_long", "delta", "decode"], default="all")
+    ap.add_argument("--only", choices=["all", "la", "la_long", "delta", "decode", "delta_decode"], default="all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
@@ -251,6 +272,13 @@ def main():
         extra[wdec.name] = {"state_update_gbs": r["gbs"], "hbm_frac": r["gbs"] / HBM_PEAK_GBS,
                             "gbs_wall_incl_launch_gaps": r["gbs_wall"], "us_per_step": 1e3 * r["event_ms_mean"],
                             "steps": r["steps"], "bytes_per_step": r["bytes_per_step"]}
+
+    if args.only in ("all", "delta_decode"):
+        wdd = wl.DELTA_DECODE_BF16
+        r = bench_delta_decode(wdd, lin, wl)
+        extra[wdd.name] = {"state_update_gbs": r["gbs"], "hbm_frac": r["gbs"] / HBM_PEAK_GBS,
+                           "gbs_wall_incl_launch_gaps": r["gbs_wall"], "us_per_step": 1e3 * r["event_ms_mean"],
+                           "steps": r["steps"], "bytes_per_step": r["bytes_per_step"]}
 
     if main_res is None:
         print(json.dumps({"extra": extra}))

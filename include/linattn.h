@@ -1,10 +1,11 @@
 /*
  * linattn.h -- C ABI of the MI355X (gfx950) causal linear-attention library.
  *
- * Three operations, each a hand-written HIP path:
- *   la_forward      chunked prefill of causal ELU+1 linear attention
- *   delta_forward   chunked prefill of the delta-rule fast-weight memory
- *   la_decode_step  one-token decode of ELU+1 linear attention on a resident state
+ * Four operations, each a hand-written HIP path:
+ *   la_forward         chunked prefill of causal ELU+1 linear attention
+ *   delta_forward      chunked prefill of the delta-rule fast-weight memory
+ *   la_decode_step     one-token decode of ELU+1 linear attention on a resident state
+ *   delta_decode_step  one-token decode of the delta rule on a resident state
  *
  * Pages the definitions come from:
  *   [LinearMem]  "AIGC 基本功｜线性、循环与记忆架构-LinearMem"
@@ -31,7 +32,8 @@
  *   any non-OK status nothing has been enqueued and no buffer was written.
  *   la_last_error() then describes the problem (per calling thread).
  * - Supported: dk, dv in {64, 128}; chunk == 64; dtype LA_BF16 everywhere and
- *   LA_F32 for la_forward (dk = 128 with dv = 128 excluded) and la_decode_step.
+ *   LA_F32 for la_forward (dk = 128 with dv = 128 excluded) and both decode
+ *   steps.
  *   Other valid-but-unsupported sizes return LA_ERR_UNSUPPORTED.
  * - Non-finite inputs are not checked and propagate.
  */
@@ -122,6 +124,21 @@ const char* la_status_string(int status);
 
 /* Detail for the last non-OK status returned on the calling thread ("" if none). */
 const char* la_last_error(void);
+
+/*
+ * One decode step of the delta-rule fast-weight memory on a resident fp32
+ * state, updated IN PLACE ([LinearMem] §03 "从累加改成纠错", [Recurrence]
+ * "Delta-rule fast weight"; [LinearMem] §05 in-place inference update):
+ *   u = v - S^T k,  S <- S + beta k u^T,  o = S^T q   (write, then read),
+ * the single-token form of delta_forward (no feature map, no normaliser;
+ * keys used as given).
+ * q, k [N][H][dk]; v, o [N][H][dv]; beta [N][H] (dtype); S [N][H][dk][dv] fp32.
+ * Errors: LA_ERR_INVALID_ARG (a pointer NULL, N, H, dk, dv < 1, dtype
+ * unknown, S not 16-byte aligned), LA_ERR_UNSUPPORTED (dk or dv not in
+ * {64, 128}), LA_ERR_HIP.
+ */
+la_status delta_decode_step(const void* q, const void* k, const void* v, const void* beta, float* S,
+                            void* o, int N, int H, int dk, int dv, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

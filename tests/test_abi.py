@@ -24,9 +24,9 @@ def _declared_functions():
     return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)))
 
 
-def test_header_declares_the_three_operations():
+def test_header_declares_the_operations():
     fns = _declared_functions()
-    for name in ("la_forward", "delta_forward", "la_decode_step"):
+    for name in ("la_forward", "delta_forward", "la_decode_step", "delta_decode_step"):
         assert name in fns
 
 
@@ -94,6 +94,23 @@ def _dec(**kw):
 ])
 def test_decode_rejects(kw, status):
     assert _dec(**kw) == ST[status]
+
+
+def _ddec(**kw):
+    a = dict(q=P, k=P, v=P, beta=P, S=P, o=P, N=4, H=2, dk=128, dv=128, dtype=1, stream=None)
+    a.update(kw)
+    return lin.lib().delta_decode_step(a["q"], a["k"], a["v"], a["beta"], a["S"], a["o"], a["N"], a["H"],
+                                       a["dk"], a["dv"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(beta=None), "INVALID_ARG"), (dict(S=None), "INVALID_ARG"), (dict(o=None), "INVALID_ARG"),
+    (dict(H=0), "INVALID_ARG"), (dict(dtype=5), "INVALID_ARG"), (dict(dv=96), "UNSUPPORTED"),
+    (dict(S=ctypes.c_void_p(0x10004)), "INVALID_ARG"),
+])
+def test_delta_decode_rejects(kw, status):
+    assert _ddec(**kw) == ST[status]
+    assert lin.lib().la_last_error().decode()
 
 
 def test_workspace_queries():

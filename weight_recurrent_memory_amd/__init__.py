@@ -4,7 +4,8 @@ Public API (same names as the C ABI in include/linattn.h):
     la_forward(q, k, v, S0=None, z0=None, eps=1e-6) -> (o, S_T, z_T)
     delta_forward(q, k, v, beta, S0=None) -> (o, S_T)
     la_decode_step(q, k, v, S, z, eps=1e-6) -> o        (S, z updated in place)
+    delta_decode_step(q, k, v, beta, S) -> o             (S updated in place)
 """
 from .binding import (  # noqa: F401
     CHUNK, LA_BF16, LA_F32, LinAttnError, UnsupportedError, delta_forward,
-    delta_forward_workspace_bytes, la_decode_step, la_forward, la_forward_workspace_bytes, lib)
+    delta_decode_step, delta_forward_workspace_bytes, la_decode_step, la_forward, la_forward_workspace_bytes, lib)

@@ -57,6 +57,8 @@ def lib():
             L.delta_forward.restype = i
             L.la_decode_step.argtypes = [vp, vp, vp, fp, fp, vp, i, i, i, i, i, ctypes.c_float, vp]
             L.la_decode_step.restype = i
+            L.delta_decode_step.argtypes = [vp, vp, vp, vp, fp, vp, i, i, i, i, i, vp]
+            L.delta_decode_step.restype = i
             L.la_status_string.argtypes = [i]
             L.la_status_string.restype = ctypes.c_char_p
             L.la_last_error.argtypes = []
@@ -195,4 +197,24 @@ def la_decode_step(q, k, v, S, z, eps=1e-6, *, o=None):
     _need(o, "o", q.dtype, (N, H, dv), dev)
     _check(lib().la_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z), _ptr(o), N, H, dk, dv,
                                 code, float(eps), _stream(dev)))
+    return o
+
+
+def delta_decode_step(q, k, v, beta, S, *, o=None):
+    """One delta-rule decode step; S [N,H,dk,dv] (fp32) is updated in place.
+    q, k: [N,H,dk]; v: [N,H,dv]; beta: [N,H] (same dtype as q).  Returns
+    o [N,H,dv] = S_new^T q."""
+    code = _dtype_code(q)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(k, "k", q.dtype, (N, H, dk), dev)
+    _need(v, "v", q.dtype, (N, H, dv), dev)
+    _need(beta, "beta", q.dtype, (N, H), dev)
+    _need(S, "S", torch.float32, (N, H, dk, dv), dev)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    _need(o, "o", q.dtype, (N, H, dv), dev)
+    _check(lib().delta_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S), _ptr(o), N, H, dk, dv,
+                                   code, _stream(dev)))
     return o

@@ -49,7 +49,7 @@ la::LaPlan plan_segments(int HT, int T, int chunk, int target_groups) {
     return p;
 }
 
-constexpr int kDeltaTargetGroups = 512;
+constexpr int kDeltaTargetGroups = 256;  // one 8-wave workgroup per CU (LDS and registers allow one)
 
 // Shared shape checks of the two prefill calls.  Returns LA_OK or a status.
 la_status check_prefill(const char* fn, int B, int H, int T, int dk, int dv, int dtype, int chunk) {
@@ -200,6 +200,22 @@ la_status la_decode_step(const void* q, const void* k, const void* v, float* S, 
     if (!aligned16(S)) return fail(LA_ERR_INVALID_ARG, "%s: S must be 16-byte aligned", fn);
     return hip_status(fn, la::launch_la_decode(q, k, v, S, z, o, N * H, dk, dv, dtype, eps,
                                                static_cast<hipStream_t>(stream)));
+}
+
+la_status delta_decode_step(const void* q, const void* k, const void* v, const void* beta, float* S, void* o,
+                            int N, int H, int dk, int dv, int dtype, void* stream) {
+    const char* fn = "delta_decode_step";
+    if (!q || !k || !v || !beta || !S || !o)
+        return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, beta, S and o must be non-NULL", fn);
+    if (N < 1 || H < 1 || dk < 1 || dv < 1)
+        return fail(LA_ERR_INVALID_ARG, "%s: sizes must be >= 1 (N=%d H=%d dk=%d dv=%d)", fn, N, H, dk, dv);
+    if (dtype != LA_F32 && dtype != LA_BF16) return fail(LA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    if (!supported_dim(dk) || !supported_dim(dv))
+        return fail(LA_ERR_UNSUPPORTED, "%s: dk=%d dv=%d not in {64, 128}", fn, dk, dv);
+    if ((long)N * H > 0x7fffffffL) return fail(LA_ERR_UNSUPPORTED, "%s: N*H exceeds 2^31-1", fn);
+    if (!aligned16(S)) return fail(LA_ERR_INVALID_ARG, "%s: S must be 16-byte aligned", fn);
+    return hip_status(fn, la::launch_delta_decode(q, k, v, beta, S, o, N * H, dk, dv, dtype,
+                                                  static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -1,0 +1,134 @@
+// Delta-rule fast-weight memory, single-token decode step on a resident fp32
+// state, updated in place ("AIGC 基本功｜线性、循环与记忆架构-LinearMem" §03
+// "从累加改成纠错" and "手撕：递推与记忆模型" "Delta-rule fast weight" for the
+// write; §05 of the first page for the in-place inference update):
+//   u = v - S^T k,   S <- S + beta k u^T,   o = S^T q   (write, then read).
+//
+// Like the linear-attention decode step this is a streaming read-modify-write
+// of S (dk*dv floats per state, one workgroup per (sequence, head) state), but
+// the write needs S^T k over the whole old state first.  Thread t owns four
+// consecutive value columns (one 16-byte vector) of every R-th state row and
+// keeps them in registers: it folds its rows into partial S^T k and S^T q,
+// the partials meet in LDS, each thread sums the ones of its columns, and
+// then updates its registers and streams them back.  The read uses the old
+// state: o = S^T q + beta u (k . q).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace la {
+
+namespace {
+
+constexpr int NTHR = 256;
+
+template <typename TIn, int DK, int DV>
+__global__ __launch_bounds__(NTHR) void delta_decode_kernel(const TIn* __restrict__ q,
+                                                            const TIn* __restrict__ k,
+                                                            const TIn* __restrict__ v,
+                                                            const TIn* __restrict__ beta,
+                                                            float* __restrict__ S, TIn* __restrict__ o) {
+    constexpr int CG = DV / 4;    // 16-byte column groups per row
+    constexpr int R = NTHR / CG;  // row groups
+    constexpr int RPT = DK / R;   // rows per thread
+    static_assert(RPT * R == DK && CG * 4 == DV && DK <= NTHR, "shape");
+    __shared__ float fk[DK], fq[DK];
+    __shared__ v4f part_k[R][CG], part_q[R][CG];
+    __shared__ float kq_part[NTHR / 64];
+
+    const int tid = threadIdx.x;
+    const int cg = tid % CG, rg = tid / CG;
+    const long s = blockIdx.x;
+    float* Ss = S + s * DK * DV;
+
+    // the state loads first: they do not depend on q, k, v
+    v4f st[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+        st[m] = *reinterpret_cast<const v4f*>(Ss + (long)(rg + R * m) * DV + 4 * cg);
+
+    float kq = 0.f;
+    if (tid < DK) {
+        const float kv = Elem<TIn>::load(k, s * DK + tid);
+        const float qv = Elem<TIn>::load(q, s * DK + tid);
+        fk[tid] = kv;
+        fq[tid] = qv;
+        kq = kv * qv;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) kq += __shfl_xor(kq, off);
+    if ((tid & 63) == 0) kq_part[tid >> 6] = kq;
+    const float b = Elem<TIn>::load(beta, s);
+    const v4f vv = v4f{Elem<TIn>::load(v, s * DV + 4 * cg + 0), Elem<TIn>::load(v, s * DV + 4 * cg + 1),
+                       Elem<TIn>::load(v, s * DV + 4 * cg + 2), Elem<TIn>::load(v, s * DV + 4 * cg + 3)};
+    __syncthreads();
+
+    // partial S^T k and S^T q over this thread's rows
+    v4f pk = zero4(), pq = zero4();
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int row = rg + R * m;
+        pk += fk[row] * st[m];
+        pq += fq[row] * st[m];
+    }
+    part_k[rg][cg] = pk;
+    part_q[rg][cg] = pq;
+    __syncthreads();
+
+    // every thread sums the partials of its own columns (broadcast reads)
+    v4f pred = zero4(), sq = zero4();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        pred += part_k[r][cg];
+        sq += part_q[r][cg];
+    }
+    const v4f u = vv - pred;
+    const v4f bu = b * u;
+
+    // write: S += beta k u^T, streamed back (the state set does not fit the
+    // Infinity Cache, so keeping its lines there would only cost write-backs)
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int row = rg + R * m;
+        const v4f x = st[m] + fk[row] * bu;
+        __builtin_nontemporal_store(x, reinterpret_cast<v4f*>(Ss + (long)row * DV + 4 * cg));
+    }
+
+    // read with the updated state: o = S^T q + beta u (k . q)
+    if (rg == 0) {
+        float kqs = 0.f;
+#pragma unroll
+        for (int i = 0; i < NTHR / 64; ++i) kqs += kq_part[i];
+        const v4f out = sq + kqs * bu;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Elem<TIn>::store(o, s * DV + 4 * cg + e, out[e]);
+    }
+}
+
+template <typename TIn, int DK, int DV>
+hipError_t launch_typed(const void* q, const void* k, const void* v, const void* beta, float* S, void* o,
+                        int NH, hipStream_t stream) {
+    delta_decode_kernel<TIn, DK, DV><<<dim3(NH), dim3(NTHR), 0, stream>>>(
+        static_cast<const TIn*>(q), static_cast<const TIn*>(k), static_cast<const TIn*>(v),
+        static_cast<const TIn*>(beta), S, static_cast<TIn*>(o));
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_delta_decode(const void* q, const void* k, const void* v, const void* beta, float* S,
+                               void* o, int NH, int dk, int dv, int dtype, hipStream_t stream) {
+#define DEC_CASE(TY, DT, A, B) \
+    if (dtype == DT && dk == A && dv == B) return launch_typed<TY, A, B>(q, k, v, beta, S, o, NH, stream);
+    DEC_CASE(bf16_t, 1, 64, 64)
+    DEC_CASE(bf16_t, 1, 64, 128)
+    DEC_CASE(bf16_t, 1, 128, 64)
+    DEC_CASE(bf16_t, 1, 128, 128)
+    DEC_CASE(float, 0, 64, 64)
+    DEC_CASE(float, 0, 64, 128)
+    DEC_CASE(float, 0, 128, 64)
+    DEC_CASE(float, 0, 128, 128)
+#undef DEC_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace la

@@ -38,6 +38,10 @@ hipError_t launch_delta_forward(const void* q, const void* k, const void* v,
                                 hipStream_t stream);
 size_t delta_ws_floats(int HT, int dk, int dv, const LaPlan& plan);
 
+// Delta-rule decode step on a resident fp32 state (in place).
+hipError_t launch_delta_decode(const void* q, const void* k, const void* v, const void* beta, float* S,
+                               void* o, int NH, int dk, int dv, int dtype, hipStream_t stream);
+
 // Linear attention decode step on a resident fp32 state (in place).
 hipError_t launch_la_decode(const void* q, const void* k, const void* v, float* S,
                             float* z, void* o, int NH, int dk, int dv, int dtype,

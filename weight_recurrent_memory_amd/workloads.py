@@ -21,7 +21,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str        # "la", "delta" or "decode"
+    kind: str        # "la", "delta", "decode" or "delta_decode"
     B: int           # batch (decode: sequences N)
     H: int
     T: int           # tokens (decode: number of steps)
@@ -40,6 +40,9 @@ LA_BF16_LONG = Workload("la_bf16_b1_h32_t65536_d64", "la", 1, 32, 65536, 64, 64,
 DECODE_BF16 = Workload("decode_bf16_n256_h32_d128_1000steps", "decode", 256, 32, 1000, 128, 128,
                        torch.bfloat16, 5)
 ALL = (LA_FP32_SMALL, LA_BF16_PREFILL, DELTA_BF16_PREFILL, LA_BF16_LONG, DECODE_BF16)
+# The delta-rule decode step on the decode configuration's states and steps.
+DELTA_DECODE_BF16 = Workload("delta_decode_bf16_n256_h32_d128_1000steps", "delta_decode", 256, 32, 1000, 128,
+                             128, torch.bfloat16, 6)
 
 
 def _gen(seed: int, device) -> torch.Generator:
@@ -95,6 +98,17 @@ def decode_tokens(steps, N, H, dk, dv, dtype, seed, device="cpu"):
     return q, k, v
 
 
+def delta_decode_tokens(steps, N, H, dk, dv, dtype, seed, device="cpu"):
+    """Per-step q, k [steps, N, H, dk] (N(0, 1) normalised per token),
+    v [steps, N, H, dv] ~ N(0, 1) and beta [steps, N, H] = sigmoid(N(0, 1))."""
+    g = _gen(seed + 1000003, device)
+    k = unit_rows(_normal((steps, N, H, dk), g, device)).to(dtype)
+    q = unit_rows(_normal((steps, N, H, dk), g, device)).to(dtype)
+    v = _normal((steps, N, H, dv), g, device).to(dtype)
+    beta = torch.sigmoid(_normal((steps, N, H), g, device)).to(dtype)
+    return q, k, v, beta
+
+
 def make(w: Workload, device="cpu"):
     """All inputs of a workload on `device`."""
     if w.kind == "la":
@@ -104,4 +118,7 @@ def make(w: Workload, device="cpu"):
     if w.kind == "decode":
         S, z = decode_state(w.B, w.H, w.dk, w.dv, w.seed, device)
         return (S, z) + decode_tokens(w.T, w.B, w.H, w.dk, w.dv, w.dtype, w.seed, device)
+    if w.kind == "delta_decode":
+        S, _ = decode_state(w.B, w.H, w.dk, w.dv, w.seed, device, std=0.1)
+        return (S,) + delta_decode_tokens(w.T, w.B, w.H, w.dk, w.dv, w.dtype, w.seed, device)
     raise ValueError(w.kind)
