@@ -135,16 +135,21 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
 
     const int t_end = min((seg + 1) * L, T);
     // The next chunk's rows are loaded into registers while this one is
-    // processed; rows past the segment end load as zero.
+    // processed.  Buffer resources end at the segment end: rows past it read
+    // as zero with no guard (a guard would make the load's result wanted at
+    // once), so the loads stay in flight until the chunk is staged.
+    const rsrc_t rk = make_rsrc(kh, (uint32_t)t_end * DK * 2);
+    const rsrc_t rq = make_rsrc(qh, (uint32_t)t_end * DK * 2);
+    const rsrc_t rv = make_rsrc(vh, (uint32_t)t_end * NS * 2);
+    const rsrc_t rb = make_rsrc(bh, (uint32_t)t_end * 2);
     ChunkRegs<bf16_t, DK, NT> kr, qr;
     ChunkRegs<bf16_t, NS, NT> vr;
-    float bnext = 0.f;
+    unsigned short bnext = 0;
     auto load_chunk = [&](int c) {
-        const int nn = min(CH, t_end - c);
-        kr.load(kh, c, nn, tid);
-        if constexpr (OUT) qr.load(qh, c, nn, tid);
-        vr.load(vh, c, nn, tid);
-        if (tid < CH) bnext = tid < nn ? bf16_to_f32(bh[c + tid]) : 0.f;
+        kr.load_buf(rk, c, tid);
+        if constexpr (OUT) qr.load_buf(rq, c, tid);
+        vr.load_buf(rv, c, tid);
+        if (tid < CH) bnext = __builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(c + tid) * 2, 0, 0);
     };
     load_chunk(seg * L);
     // Upper blocks of T and, for outputs, of P (keys after every query of
@@ -170,7 +175,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         stage_rows_raw<bf16_t, DK, NT>(kr, tid, Ks, LQ);
         if constexpr (OUT) stage_rows_raw<bf16_t, DK, NT>(qr, tid, Qs, LQ);
         stage_rows_raw<bf16_t, NS, NT>(vr, tid, Vs, LV);
-        if (tid < CH) Bs[tid] = bnext;
+        if (tid < CH) Bs[tid] = bf16_to_f32(bnext);
         if (c0 + CH < t_end) load_chunk(c0 + CH);
         __syncthreads();
 
