@@ -48,9 +48,9 @@ LA_TRAFFIC = {
     "sources": ["weight_recurrent_memory_amd/csrc/la_prefill.hip",
                 "weight_recurrent_memory_amd/csrc/common.hpp",
                 "weight_recurrent_memory_amd/csrc/kernels.hpp"],
-    "sha256": "e811d2b1245c91fcd7910f7f183efd8343efc6fafb7f09881d7ce4dd7de582ec",
-    "fetch_kib": 86745.0, "fetch_scale": 2.0,
-    "write_kib": 56814.0, "write_scale": 1.0,
+    "sha256": "4314bf120cb6071d41530235a9ac88072c13011e2d7a5861a02b4a02eae82607",
+    "fetch_kib": 86749.0, "fetch_scale": 2.0,
+    "write_kib": 56819.0, "write_scale": 1.0,
 }
 
 
