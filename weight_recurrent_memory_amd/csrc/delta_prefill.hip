@@ -51,8 +51,10 @@ struct DL {
     static constexpr int TS = CH * LT * 2;          // T (bf16)
     static constexpr int PS = OUT ? CH * LT * 2 : 0;  // tril(Q K^T), rows = queries
     static constexpr int AF = CH * LF * 4;          // A, then T blocks (fp32)
+    static constexpr int AD = 4 * 256 * 4;          // diagonal blocks of A, transposed (fp32)
+    static constexpr int YF = 4 * 256 * 4;          // A_BL T_TL tiles of the inverse (fp32)
     static constexpr int BS = CH * 4;               // beta (fp32)
-    static constexpr int TOTAL = KS + WS + QS + VS + TS + PS + AF + BS;
+    static constexpr int TOTAL = KS + WS + QS + VS + TS + PS + AF + AD + YF + BS;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
     static constexpr int XR = DK / 16;              // dk row tiles of a state column
     // State column tiles: OUT carries S (NS columns); MAP carries N (NS
@@ -65,7 +67,7 @@ struct DL {
 };
 
 // The ten lower 16x16 tiles of a 64x64 matrix: diagonal first.
-__device__ __forceinline__ void lower_tile(int id, int& i, int& j) {
+__host__ __device__ constexpr void lower_tile(int id, int& i, int& j) {
     if (id < 4) { i = id; j = id; }                // (0,0) (1,1) (2,2) (3,3)
     else if (id < 7) { i = id - 3; j = id - 4; }   // (1,0) (2,1) (3,2)
     else if (id < 9) { i = id - 5; j = id - 7; }   // (2,0) (3,1)
@@ -100,7 +102,9 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     __bf16* Ts = reinterpret_cast<__bf16*>(sp);  sp += Y::TS;
     __bf16* Ps = reinterpret_cast<__bf16*>(sp);  sp += Y::PS;
     float* Af = reinterpret_cast<float*>(sp);
-    float* Bs = Af + CH * LF;
+    float* Ad = Af + CH * LF;
+    float* Yf = Ad + 4 * 256;
+    float* Bs = Yf + 4 * 256;
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int w = wave_id(tid);
@@ -182,29 +186,60 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         // ---- A = tril_{-1}(K K^T) diag(beta) (fp32) and, for outputs, the
         // causal scores P = tril(Q K^T) (bf16, rows = queries), computed as
         // transposed tiles so each lane writes four consecutive keys
-        constexpr int NTILE = OUT ? 20 : 10;
-        for (int id = w; id < NTILE; id += NWV) {
-            int bi, bj;
-            lower_tile(id % 10, bi, bj);
-            v4f acc = zero4();
-            if (id < 10) {
+        // Wave w builds tiles w, w + 8, w + 16 (compile-time ids, so the
+        // loads of all its tiles can be issued up front).  Diagonal blocks of
+        // A also go to Ad transposed (row m = column m of the block), for the
+        // column-oriented substitution below.
+        auto ap_tile = [&](auto idc) {
+            constexpr int id = decltype(idc)::value;
+            constexpr int NTILE = OUT ? 20 : 10;
+            if constexpr (id < NTILE) {
+                constexpr int bi = id % 10 < 4 ? id % 10 : id % 10 < 7 ? id % 10 - 3 : id % 10 < 9 ? id % 10 - 5 : 3;
+                constexpr int bj = id % 10 < 4 ? id % 10 : id % 10 < 7 ? id % 10 - 4 : id % 10 < 9 ? id % 10 - 7 : 0;
+                v4f acc = zero4();
+                if constexpr (id < 10) {
 #pragma unroll
-                for (int kb = 0; kb < DK / 32; ++kb)
-                    M::mma(acc, M::load(&Ks[(16 * bi + li) * LQ + 32 * kb], g), M::load(&Ks[(16 * bj + li) * LQ + 32 * kb], g));
+                    for (int kb = 0; kb < DK / 32; ++kb)
+                        M::mma(acc, M::load(&Ks[(16 * bi + li) * LQ + 32 * kb], g),
+                               M::load(&Ks[(16 * bj + li) * LQ + 32 * kb], g));
+                    v4f a;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * bi + 4 * g + r, i = 16 * bj + li;
-                    Af[t * LF + i] = (i < t) ? Bs[i] * acc[r] : 0.f;
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = 16 * bi + 4 * g + r, i = 16 * bj + li;
+                        a[r] = (i < t) ? Bs[i] * acc[r] : 0.f;
+                        Af[t * LF + i] = a[r];
+                    }
+                    if constexpr (bi == bj) *reinterpret_cast<v4f*>(&Ad[bi * 256 + li * 16 + 4 * g]) = a;
+                } else {
+                    // keys of tile bj (rows) x queries of tile bi (columns)
+#pragma unroll
+                    for (int kb = 0; kb < DK / 32; ++kb)
+                        M::mma(acc, M::load(&Ks[(16 * bj + li) * LQ + 32 * kb], g),
+                               M::load(&Qs[(16 * bi + li) * LQ + 32 * kb], g));
+                    uint2 pk;
+                    pk.x = pack_bf16x2((bi == bj && 4 * g + 0 > li) ? 0.f : acc[0],
+                                       (bi == bj && 4 * g + 1 > li) ? 0.f : acc[1]);
+                    pk.y = pack_bf16x2((bi == bj && 4 * g + 2 > li) ? 0.f : acc[2],
+                                       (bi == bj && 4 * g + 3 > li) ? 0.f : acc[3]);
+                    *reinterpret_cast<uint2*>(&Ps[(16 * bi + li) * LT + 16 * bj + 4 * g]) = pk;
                 }
-            } else {
-                // keys of tile bj (rows) x queries of tile bi (columns)
-#pragma unroll
-                for (int kb = 0; kb < DK / 32; ++kb)
-                    M::mma(acc, M::load(&Ks[(16 * bj + li) * LQ + 32 * kb], g), M::load(&Qs[(16 * bi + li) * LQ + 32 * kb], g));
-                __bf16* dst = &Ps[(16 * bi + li) * LT + 16 * bj + 4 * g];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) dst[r] = M::cvt((bi == bj && 4 * g + r > li) ? 0.f : acc[r]);
             }
+        };
+        auto ap_wave = [&](auto wc) {
+            constexpr int W = decltype(wc)::value;
+            ap_tile(std::integral_constant<int, W>{});
+            ap_tile(std::integral_constant<int, W + 8>{});
+            ap_tile(std::integral_constant<int, W + 16>{});
+        };
+        switch (w) {
+            case 0: ap_wave(std::integral_constant<int, 0>{}); break;
+            case 1: ap_wave(std::integral_constant<int, 1>{}); break;
+            case 2: ap_wave(std::integral_constant<int, 2>{}); break;
+            case 3: ap_wave(std::integral_constant<int, 3>{}); break;
+            case 4: ap_wave(std::integral_constant<int, 4>{}); break;
+            case 5: ap_wave(std::integral_constant<int, 5>{}); break;
+            case 6: ap_wave(std::integral_constant<int, 6>{}); break;
+            default: ap_wave(std::integral_constant<int, 7>{}); break;
         }
         __syncthreads();
 
@@ -228,21 +263,22 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         };
         if (w != 0) out_first_half();
 
-        // ---- diagonal blocks of T: (I + A_bb)^{-1} by forward substitution.
-        // Wave 0, lane 16b+j holds column j of block b in registers; the
-        // block goes to Af (fp32, for the off-diagonal blocks) and Ts (bf16).
+        // ---- diagonal blocks of T: (I + A_bb)^{-1} by forward substitution,
+        // column-oriented: wave 0, lane 16b+j holds column j of block b; at
+        // step m every later entry takes its A_bb[i][m] d[m] term at once, so
+        // the dependent chain is one multiply-add per step.  The block goes
+        // to Af (fp32, for the off-diagonal blocks) and Ts (bf16).
         if (w == 0) {
             const int b = g, j = li;
             float d[16];
 #pragma unroll
             for (int m = 0; m < 16; ++m) d[m] = (m == j) ? 1.f : 0.f;
 #pragma unroll
-            for (int i = 1; i < 16; ++i) {
-                const float* arow = &Af[(16 * b + i) * LF + 16 * b];
-                float s = 0.f;
+            for (int m = 0; m < 15; ++m) {
+                const v4f* col = reinterpret_cast<const v4f*>(&Ad[b * 256 + m * 16]);  // A_bb[.][m]
+                const v4f c[4] = {col[0], col[1], col[2], col[3]};
 #pragma unroll
-                for (int m = 0; m < i; ++m) s += arow[m] * d[m];
-                if (i > j) d[i] = -s;
+                for (int i = m + 1; i < 16; ++i) d[i] -= c[i >> 2][i & 3] * d[m];
             }
 #pragma unroll
             for (int m = 0; m < 16; ++m) {
@@ -253,34 +289,72 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         __syncthreads();
         if (w == 0) out_first_half();
 
-        // ---- off-diagonal blocks, by distance from the diagonal:
-        // T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj, stored (i > j) in the unused
-        // upper block at rows 16j, cols 16i.
+        // ---- off-diagonal blocks by 2x2 block doubling.  The inverse of a
+        // block lower-triangular [[M11, 0], [M21, M22]] is [[M11^-1, 0],
+        // [-M22^-1 M21 M11^-1, M22^-1]]: first the two 32x32 diagonal blocks
+        // (T10 = -D1 A10 D0, T32 = -D3 A32 D2), then the lower-left 32x32
+        // block -T_BR (A_BL T_TL) in two steps of four 16x16 tiles.  Blocks:
+        // D_b at rows 16b, cols 16b of Af; A_ij (i > j) at rows 16i, cols 16j;
+        // T10 and T32 stored at rows 16j, cols 16i (the unused upper half).
+        auto rowA = [&](int r0, int c0) {  // row-layout operand of the block at (r0, c0)
+            return *reinterpret_cast<const v4f*>(&Af[(r0 + li) * LF + c0 + 4 * g]);
+        };
+        auto colB = [&](int r0, int c0) {  // output-layout operand of the block at (r0, c0)
+            v4f bb;
 #pragma unroll
-        for (int dist = 1; dist < 4; ++dist) {
-            if (w >= 1 && w <= 4 - dist) {
-                const int j = w - 1, i = j + dist;
-                v4f P = zero4();
-                for (int m = j; m < i; ++m) {
-                    // A_im (lower block) times T_mj (diagonal D_j when m == j,
-                    // else the stored block at rows 16j, cols 16m)
-                    const v4f a = *reinterpret_cast<const v4f*>(&Af[(16 * i + li) * LF + 16 * m + 4 * g]);
-                    v4f bb;
+            for (int s2 = 0; s2 < 4; ++s2) bb[s2] = Af[(r0 + 4 * g + s2) * LF + c0 + li];
+            return bb;
+        };
+        auto yB = [&](int t) {
+            v4f bb;
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) bb[s] = Af[(16 * j + 4 * g + s) * LF + 16 * m + li];
-                    MF::mma(P, a, bb);
-                }
-                v4f Tij = zero4();
-                const v4f a = *reinterpret_cast<const v4f*>(&Af[(16 * i + li) * LF + 16 * i + 4 * g]);
-                MF::mma(Tij, a, P);  // an output tile is already in B-operand layout
+            for (int s2 = 0; s2 < 4; ++s2) bb[s2] = Yf[t * 256 + (4 * g + s2) * 16 + li];
+            return bb;
+        };
+        auto put_T = [&](int bi, int bj, const v4f& x) {  // T block (bi, bj), bi > bj, to Ts (bf16)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    Af[(16 * j + 4 * g + r) * LF + 16 * i + li] = -Tij[r];
-                    Ts[(16 * i + 4 * g + r) * LT + 16 * j + li] = M::cvt(-Tij[r]);  // T[t][k]: t in block i, k in j
-                }
-            }
-            __syncthreads();
+            for (int r = 0; r < 4; ++r) Ts[(16 * bi + 4 * g + r) * LT + 16 * bj + li] = M::cvt(x[r]);
+        };
+        if (w == 1 || w == 2) {
+            const int lo = w == 1 ? 0 : 32;  // T10 (w 1) or T32 (w 2)
+            v4f P = zero4(), X = zero4();
+            MF::mma(P, rowA(lo + 16, lo), colB(lo, lo));
+            MF::mma(X, rowA(lo + 16, lo + 16), P);
+            X = -X;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Af[(lo + 4 * g + r) * LF + lo + 16 + li] = X[r];
+            put_T(lo / 16 + 1, lo / 16, X);
         }
+        __syncthreads();
+        if (w >= 1 && w <= 4) {
+            // Y = A_BL T_TL: Y00 = A20 D0 + A21 T10, Y01 = A21 D1,
+            // Y10 = A30 D0 + A31 T10, Y11 = A31 D1
+            const int t = w - 1, yr = t >> 1, yc = t & 1;
+            v4f Y = zero4();
+            if (yc == 0) {
+                MF::mma(Y, rowA(32 + 16 * yr, 0), colB(0, 0));
+                MF::mma(Y, rowA(32 + 16 * yr, 16), colB(0, 16));
+            } else {
+                MF::mma(Y, rowA(32 + 16 * yr, 16), colB(16, 16));
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Yf[t * 256 + (4 * g + r) * 16 + li] = Y[r];
+        }
+        __syncthreads();
+        if (w >= 1 && w <= 4) {
+            // T20 = -D2 Y00, T21 = -D2 Y01, T30 = -(T32 Y00 + D3 Y10),
+            // T31 = -(T32 Y01 + D3 Y11)
+            const int t = w - 1, xr = t >> 1, xc = t & 1;
+            v4f X = zero4();
+            if (xr == 0) {
+                MF::mma(X, rowA(32, 32), yB(xc));
+            } else {
+                MF::mma(X, rowA(32, 48), yB(xc));
+                MF::mma(X, rowA(48, 48), yB(2 + xc));
+            }
+            put_T(2 + xr, xc, -X);
+        }
+        __syncthreads();
 
         // ---- W = T K (computed as transposed tiles, rows land as 8-byte
         // stores) and this wave's U_v = T V columns
