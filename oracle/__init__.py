@@ -27,6 +27,15 @@ Functions and what pins them (the pins are in ``tests/test_oracle_pins.py``):
     dense form and the orthonormal-key reduction.
 ``la_decode_step`` -- one in-place step; pinned by equality with one token of
     ``la_forward`` continued from the same state.
+``gated_delta_forward`` / ``gated_delta_decode_step`` -- the delta rule with a
+    forgetting gate applied before the correction (LinearMem §03, the
+    Gated DeltaNet rule).  Pinned by the LinearMem gate reads (identity
+    state, key (1, 0) written with beta = 1: the orthogonal key reads [0, 0.8]
+    with alpha = 0.8, §06, and [0, 1] with alpha = 1, §09), alpha = 1 equal to the ungated functions bit for
+    bit, beta = 0 reducing to pure decay (S_T = prod(alpha) S_0), a dense
+    form with decay products solved by LAPACK, the exact overwrite after the
+    decay, the step chain equal to the sequence form, and the order check
+    (decaying after the correction gives a different, wrong state).
 ``delta_decode_step`` -- one in-place delta-rule step.  Pinned by the LA-SSM
     page's 4-token delta example replayed one step at a time (every
     intermediate state and the final read of k_1), the bit-exact overwrite
@@ -84,6 +93,10 @@ def _load():
             lib.la_ref_decode_step.restype = None
             lib.delta_ref_decode_step.argtypes = [dp, dp, dp, dp, dp, dp, i, i, i, i]
             lib.delta_ref_decode_step.restype = None
+            lib.gated_delta_ref_forward.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i, i, i, i, i]
+            lib.gated_delta_ref_forward.restype = None
+            lib.gated_delta_ref_decode_step.argtypes = [dp, dp, dp, dp, dp, dp, dp, i, i, i, i]
+            lib.gated_delta_ref_decode_step.restype = None
             lib.oracle_phi.argtypes = [dp, dp, ctypes.c_long]
             lib.oracle_phi.restype = None
             lib.oracle_num_threads.argtypes = []
@@ -180,4 +193,35 @@ def delta_decode_step(q, k, v, beta, S):
     o = np.empty((N, H, dv))
     _load().delta_ref_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S), _ptr(o),
                                   N, H, dk, dv)
+    return o, S
+
+
+def gated_delta_forward(q, k, v, beta, alpha, S0=None):
+    """The gated delta rule.  q, k: [B,H,T,dk]; v: [B,H,T,dv]; beta, alpha:
+    [B,H,T] -> (o [B,H,T,dv], S [B,H,dk,dv])."""
+    q, k, v, beta, alpha, S0 = map(_f64, (q, k, v, beta, alpha, S0))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and v.shape[:3] == (B, H, T)
+    assert beta.shape == (B, H, T) and alpha.shape == (B, H, T)
+    if S0 is not None:
+        assert S0.shape == (B, H, dk, dv)
+    o = np.empty((B, H, T, dv))
+    S = np.empty((B, H, dk, dv))
+    _load().gated_delta_ref_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S0),
+                                    _ptr(o), _ptr(S), B, H, T, dk, dv)
+    return o, S
+
+
+def gated_delta_decode_step(q, k, v, beta, alpha, S):
+    """One gated delta step on a copy of S.  q, k: [N,H,dk]; v: [N,H,dv];
+    beta, alpha: [N,H]; S: [N,H,dk,dv] -> (o [N,H,dv], S_new)."""
+    q, k, v, beta, alpha = map(_f64, (q, k, v, beta, alpha))
+    S = _f64(S).copy()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    assert beta.shape == (N, H) and alpha.shape == (N, H) and S.shape == (N, H, dk, dv)
+    o = np.empty((N, H, dv))
+    _load().gated_delta_ref_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S),
+                                        _ptr(o), N, H, dk, dv)
     return o, S

@@ -102,21 +102,24 @@ void la_ref_forward(const double* q, const double* k, const double* v,
 }
 
 /*
- * Delta-rule fast-weight memory, write-then-read.
+ * Delta-rule fast-weight memory with an optional forgetting gate, write then
+ * read.
  *
- * [LinearMem] §03 "从累加改成纠错": one gradient step of size beta_t on
- * 0.5 * ||S^T k_t - v_t||^2 gives S_t = S_{t-1} + beta_t k_t (v_t^T - k_t^T S_{t-1});
- * no feature map, no normaliser z.  [Recurrence] "Delta-rule fast weight"
- * writes the same update with a per-token beta and an optional initial state.
- *
- * The pages print no per-token query read for a whole sequence; this oracle
- * reads o_t = S_t^T q_t after the write, the same write-then-read order
- * [LinearMem] §03 fixes for linear attention (raw q, no normaliser).
+ * [LinearMem] §03 "从累加改成纠错" and [Recurrence] "Delta-rule fast weight":
+ * the write is S_t = S_{t-1} + beta_t k_t (v_t - S_{t-1}^T k_t)^T, the
+ * correction being the new value minus what the memory predicts for k_t.
+ * The same §03 then adds a forgetting coefficient alpha_t applied to the old
+ * state BEFORE the correction is computed (Gated DeltaNet's rule):
+ *   decayed = alpha_t S_{t-1},  u_t = v_t - decayed^T k_t,
+ *   S_t = decayed + beta_t k_t u_t^T,
+ * with the page's warning that the order (decay first, then the error) is
+ * part of the rule.  alpha == NULL means alpha_t = 1 (the plain delta rule).
+ * The per-token read o_t = S_t^T q_t (after the write) is this oracle's
+ * reading: the pages print no sequence of query reads for this rule.
  */
-void delta_ref_forward(const double* q, const double* k, const double* v,
-                       const double* beta, const double* S0,
-                       double* o, double* S_out,
-                       int B, int H, int T, int dk, int dv) {
+static void delta_gated_forward(const double* q, const double* k, const double* v,
+                                const double* beta, const double* alpha, const double* S0,
+                                double* o, double* S_out, int B, int H, int T, int dk, int dv) {
     const long heads = (long)B * H;
 #pragma omp parallel for schedule(dynamic, 1)
     for (long h = 0; h < heads; ++h) {
@@ -127,10 +130,14 @@ void delta_ref_forward(const double* q, const double* k, const double* v,
         const double* kh = k + h * (long)T * dk;
         const double* vh = v + h * (long)T * dv;
         const double* bh = beta + h * (long)T;
+        const double* ah = alpha ? alpha + h * (long)T : NULL;
         double* oh = o + h * (long)T * dv;
         for (int t = 0; t < T; ++t) {
             const double* kt = kh + (long)t * dk;
-            /* correction u = v_t - S_{t-1}^T k_t (new value minus the prediction) */
+            /* forget first: the correction is taken against the decayed state */
+            if (ah)
+                for (long i = 0; i < (long)dk * dv; ++i) S[i] *= ah[t];
+            /* correction u = v_t - S^T k_t (new value minus the prediction) */
             for (int j = 0; j < dv; ++j) {
                 double pred = 0.0;
                 for (int i = 0; i < dk; ++i) pred += kt[i] * S[(long)i * dv + j];
@@ -151,6 +158,22 @@ void delta_ref_forward(const double* q, const double* k, const double* v,
         if (S_out) memcpy(S_out + h * (long)dk * dv, S, sizeof(double) * (size_t)dk * dv);
         free(S); free(u);
     }
+}
+
+/* The plain delta rule (no gate). */
+void delta_ref_forward(const double* q, const double* k, const double* v,
+                       const double* beta, const double* S0,
+                       double* o, double* S_out,
+                       int B, int H, int T, int dk, int dv) {
+    delta_gated_forward(q, k, v, beta, NULL, S0, o, S_out, B, H, T, dk, dv);
+}
+
+/* The gated delta rule: alpha [B][H][T], the per-token forgetting factor. */
+void gated_delta_ref_forward(const double* q, const double* k, const double* v,
+                             const double* beta, const double* alpha, const double* S0,
+                             double* o, double* S_out,
+                             int B, int H, int T, int dk, int dv) {
+    delta_gated_forward(q, k, v, beta, alpha, S0, o, S_out, B, H, T, dk, dv);
 }
 
 /*
@@ -197,9 +220,9 @@ void la_ref_decode_step(const double* q, const double* k, const double* v,
  * output o = S^T q with the updated state.
  *   q, k [N][H][dk]   v, o [N][H][dv]   beta [N][H]   S [N][H][dk][dv]
  */
-void delta_ref_decode_step(const double* q, const double* k, const double* v,
-                           const double* beta, double* S, double* o,
-                           int N, int H, int dk, int dv) {
+static void delta_gated_decode_step(const double* q, const double* k, const double* v,
+                                    const double* beta, const double* alpha, double* S, double* o,
+                                    int N, int H, int dk, int dv) {
     const long states = (long)N * H;
 #pragma omp parallel for schedule(static)
     for (long s = 0; s < states; ++s) {
@@ -207,6 +230,8 @@ void delta_ref_decode_step(const double* q, const double* k, const double* v,
         const double* ks = k + s * dk;
         const double* vs = v + s * dv;
         double* Ss = S + s * (long)dk * dv;
+        if (alpha)  /* forget first */
+            for (long i = 0; i < (long)dk * dv; ++i) Ss[i] *= alpha[s];
         for (int j = 0; j < dv; ++j) {
             double pred = 0.0;
             for (int i = 0; i < dk; ++i) pred += ks[i] * Ss[(long)i * dv + j];
@@ -219,6 +244,19 @@ void delta_ref_decode_step(const double* q, const double* k, const double* v,
             o[s * dv + j] = acc;
         }
     }
+}
+
+void delta_ref_decode_step(const double* q, const double* k, const double* v,
+                           const double* beta, double* S, double* o,
+                           int N, int H, int dk, int dv) {
+    delta_gated_decode_step(q, k, v, beta, NULL, S, o, N, H, dk, dv);
+}
+
+/* The gated form of the step above: S is first scaled by alpha [N][H]. */
+void gated_delta_ref_decode_step(const double* q, const double* k, const double* v,
+                                 const double* beta, const double* alpha, double* S, double* o,
+                                 int N, int H, int dk, int dv) {
+    delta_gated_decode_step(q, k, v, beta, alpha, S, o, N, H, dk, dv);
 }
 
 /* The feature map alone, so tests can pin its branches directly. */

@@ -52,6 +52,24 @@ def delta_dense(q, k, v, beta, S0=None):
     return O, S
 
 
+def gated_delta_dense(q, k, v, beta, alpha, S0=None):
+    """The gated delta rule over a whole sequence as one linear system.
+    With g_t = alpha_1 ... alpha_t, unrolling decay-then-correct gives
+    (I + A) U = V - diag(g) K S0 with A[t][i] = (g_t / g_i) beta_i k_t . k_i
+    (i < t); then o_t = g_t S0^T q_t + sum_{i<=t} (g_t / g_i) beta_i (k_i . q_t) u_i
+    and S_T = g_T S0 + sum_i (g_T / g_i) beta_i k_i u_i^T."""
+    T, dk = k.shape
+    dv = v.shape[1]
+    S0 = np.zeros((dk, dv)) if S0 is None else S0
+    g = np.cumprod(alpha)
+    ratio = g[:, None] / g[None, :]                       # g_t / g_i
+    A = np.tril(ratio * (k @ k.T), -1) * beta[None, :]
+    U = np.linalg.solve(np.eye(T) + A, v - g[:, None] * (k @ S0))
+    O = g[:, None] * (q @ S0) + (np.tril(ratio * (q @ k.T)) * beta[None, :]) @ U
+    S = g[-1] * S0 + k.T @ ((g[-1] / g * beta)[:, None] * U)
+    return O, S
+
+
 def la_chunked(q, k, v, C, S0=None, z0=None, eps=1e-6):
     T, dk = q.shape
     dv = v.shape[1]

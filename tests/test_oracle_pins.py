@@ -482,3 +482,98 @@ def test_delta_decode_chain_equals_forward_over_the_same_tokens():
         outs.append(o)
     np.testing.assert_allclose(np.stack(outs, 2), of, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(S, Sf, rtol=1e-12, atol=1e-13)
+
+
+# ----------------------------------------------------------------- gated delta
+
+def _gdelta1(q, k, v, beta, alpha, S0=None):
+    o, S = oracle.gated_delta_forward(_h(q), _h(k), _h(v), np.asarray(beta, dtype=np.float64)[None, None],
+                                      np.asarray(alpha, dtype=np.float64)[None, None],
+                                      None if S0 is None else S0[None, None])
+    return o[0, 0], S[0, 0]
+
+
+def test_gated_delta_gate_reads_printed_on_linearmem():
+    # LinearMem §06 / §09: identity state, write key (1, 0) -> value (0, 1)
+    # with beta = 1 and forgetting factor alpha, then read the orthogonal key
+    # (0, 1): [0, 0.8] for alpha = 0.8, [0, 1] for alpha = 1.
+    g = _golden("linearmem_memory_experiment.json")
+    key, values = np.array(g["key"]), np.array(g["values"])
+    q = np.array([0.0, 1.0])
+    for alpha, want in ((0.8, g["gated_unrelated_key_read_alpha_0.8"]), (1.0, g["gated_unrelated_key_read_alpha_1"])):
+        o, _ = _gdelta1([q], [key], [values[1]], [1.0], [alpha], S0=np.eye(2))
+        np.testing.assert_allclose(o[0], want, atol=1e-15)
+        od, _ = oracle.gated_delta_decode_step(q[None, None], key[None, None], values[1][None, None],
+                                               np.ones((1, 1)), np.full((1, 1), alpha), np.eye(2)[None, None])
+        np.testing.assert_allclose(od[0, 0], want, atol=1e-15)
+
+
+def test_gated_delta_alpha_one_is_the_delta_rule_bitwise():
+    rng = np.random.default_rng(51)
+    B, H, T, dk, dv = 2, 2, 40, 6, 5
+    q, k, v = rng.normal(size=(B, H, T, dk)), rng.normal(size=(B, H, T, dk)), rng.normal(size=(B, H, T, dv))
+    beta = rng.uniform(size=(B, H, T))
+    S0 = rng.normal(size=(B, H, dk, dv))
+    o1, S1 = oracle.delta_forward(q, k, v, beta, S0)
+    o2, S2 = oracle.gated_delta_forward(q, k, v, beta, np.ones((B, H, T)), S0)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+
+
+def test_gated_delta_zero_beta_is_pure_decay():
+    rng = np.random.default_rng(52)
+    T, dk, dv = 20, 4, 3
+    q, k, v = rng.normal(size=(T, dk)), rng.normal(size=(T, dk)), rng.normal(size=(T, dv))
+    alpha = rng.uniform(0.5, 1.0, size=T)
+    S0 = rng.normal(size=(dk, dv))
+    o, S = _gdelta1(q, k, v, np.zeros(T), alpha, S0=S0)
+    g = np.cumprod(alpha)
+    np.testing.assert_allclose(S, g[-1] * S0, rtol=1e-13)
+    np.testing.assert_allclose(o, g[:, None] * (q @ S0), rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("T,dk,dv,seed,init", [(1, 3, 2, 1, False), (17, 5, 4, 2, True), (64, 8, 8, 3, True)])
+def test_gated_delta_matches_dense_form(T, dk, dv, seed, init):
+    rng = np.random.default_rng(60 + seed)
+    k = rng.normal(size=(T, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    q, v = rng.normal(size=(T, dk)), rng.normal(size=(T, dv))
+    beta, alpha = rng.uniform(size=T), rng.uniform(0.6, 1.0, size=T)
+    S0 = rng.normal(size=(dk, dv)) if init else None
+    o, S = _gdelta1(q, k, v, beta, alpha, S0=S0)
+    rO, rS = forms.gated_delta_dense(q, k, v, beta, alpha, S0)
+    np.testing.assert_allclose(o, rO, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(S, rS, rtol=1e-10, atol=1e-12)
+
+
+def test_gated_delta_decay_comes_before_the_correction():
+    # The page: decay first, then the error against the decayed state; the
+    # other order is a different rule.  Exact overwrite holds only for the
+    # page's order: with a unit basis key and beta = 1 the key reads back its
+    # new value whatever alpha is (dyadic values, bit-exact).
+    rng = np.random.default_rng(53)
+    dk, dv = 6, 4
+    S0 = rng.integers(-64, 64, size=(dk, dv)) / 16.0
+    key = np.eye(dk)[2]
+    val = rng.integers(-64, 64, size=dv) / 8.0
+    o, S = _gdelta1([key], [key], [val], [1.0], [0.5], S0=S0)
+    assert np.array_equal(o[0], val)
+    other = 0.5 * (S0 + np.outer(key, val - key @ S0))  # correct first, then decay
+    assert not np.allclose(S, other)
+
+
+def test_gated_delta_decode_chain_equals_forward():
+    rng = np.random.default_rng(54)
+    N, H, dk, dv, steps = 2, 2, 5, 4, 30
+    S = rng.normal(scale=0.1, size=(N, H, dk, dv))
+    k = rng.normal(size=(steps, N, H, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    q, v = rng.normal(size=(steps, N, H, dk)), rng.normal(size=(steps, N, H, dv))
+    beta, alpha = rng.uniform(size=(steps, N, H)), rng.uniform(0.7, 1.0, size=(steps, N, H))
+    tr = lambda x: x.transpose(1, 2, 0, 3) if x.ndim == 4 else x.transpose(1, 2, 0)
+    of, Sf = oracle.gated_delta_forward(tr(q), tr(k), tr(v), tr(beta), tr(alpha), S0=S)
+    outs = []
+    for t in range(steps):
+        o, S = oracle.gated_delta_decode_step(q[t], k[t], v[t], beta[t], alpha[t], S)
+        outs.append(o)
+    np.testing.assert_allclose(np.stack(outs, 2), of, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(S, Sf, rtol=1e-12, atol=1e-13)
