@@ -1,11 +1,13 @@
 /*
  * linattn.h -- C ABI of the MI355X (gfx950) causal linear-attention library.
  *
- * Four operations, each a hand-written HIP path:
- *   la_forward         chunked prefill of causal ELU+1 linear attention
- *   delta_forward      chunked prefill of the delta-rule fast-weight memory
- *   la_decode_step     one-token decode of ELU+1 linear attention on a resident state
- *   delta_decode_step  one-token decode of the delta rule on a resident state
+ * Six operations, each a hand-written HIP path:
+ *   la_forward               chunked prefill of causal ELU+1 linear attention
+ *   delta_forward            chunked prefill of the delta-rule fast-weight memory
+ *   gated_delta_forward      the same with a per-token forgetting gate
+ *   la_decode_step           one-token decode of ELU+1 linear attention on a resident state
+ *   delta_decode_step        one-token decode of the delta rule on a resident state
+ *   gated_delta_decode_step  the same with a forgetting gate
  *
  * Pages the definitions come from:
  *   [LinearMem]  "AIGC 基本功｜线性、循环与记忆架构-LinearMem"
@@ -32,8 +34,8 @@
  *   any non-OK status nothing has been enqueued and no buffer was written.
  *   la_last_error() then describes the problem (per calling thread).
  * - Supported: dk, dv in {64, 128}; chunk == 64; dtype LA_BF16 everywhere and
- *   LA_F32 for la_forward (dk = 128 with dv = 128 excluded) and both decode
- *   steps.
+ *   LA_F32 for la_forward (dk = 128 with dv = 128 excluded) and the decode
+ *   steps.  Forgetting gates alpha are fp32 for every dtype.
  *   Other valid-but-unsupported sizes return LA_ERR_UNSUPPORTED.
  * - Non-finite inputs are not checked and propagate.
  */
@@ -139,6 +141,36 @@ const char* la_last_error(void);
  */
 la_status delta_decode_step(const void* q, const void* k, const void* v, const void* beta, float* S,
                             void* o, int N, int H, int dk, int dv, int dtype, void* stream);
+
+/*
+ * The gated delta rule over a whole sequence (prefill).  [LinearMem] §03:
+ * the old state is first decayed by a forgetting factor, then corrected
+ * against the decayed state (the order matters; this is the Gated DeltaNet
+ * rule):
+ *   S~ = alpha_t S_{t-1},  S_t = S~ + beta_t k_t (v_t^T - k_t^T S~),  o_t = S_t^T q_t.
+ * alpha    [B][H][T] fp32 (whatever dtype is), each in (0, 1]; alpha = 1 is
+ *          delta_forward.  A factor below e^-20 acts as e^-20 (a decay far
+ *          below fp32 resolution, so alpha = 0 is an effective reset).
+ * Other arguments, the workspace (size from delta_forward_workspace_bytes)
+ * and the errors are those of delta_forward; alpha NULL is
+ * LA_ERR_INVALID_ARG.
+ */
+la_status gated_delta_forward(const void* q, const void* k, const void* v, const void* beta,
+                              const float* alpha, const float* S0, void* o, float* S_out,
+                              int B, int H, int T, int dk, int dv, int dtype, int chunk,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step of the gated delta rule on a resident fp32 state, updated
+ * IN PLACE ([LinearMem] §03; §05 in-place inference update):
+ *   S~ = alpha S,  u = v - S~^T k,  S <- S~ + beta k u^T,  o = S^T q.
+ * alpha    [N][H] fp32 (whatever dtype is); alpha = 0 resets exactly.
+ * Other arguments and the errors are those of delta_decode_step; alpha NULL
+ * is LA_ERR_INVALID_ARG.
+ */
+la_status gated_delta_decode_step(const void* q, const void* k, const void* v, const void* beta,
+                                  const float* alpha, float* S, void* o,
+                                  int N, int H, int dk, int dv, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

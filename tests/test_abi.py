@@ -26,7 +26,8 @@ def _declared_functions():
 
 def test_header_declares_the_operations():
     fns = _declared_functions()
-    for name in ("la_forward", "delta_forward", "la_decode_step", "delta_decode_step"):
+    for name in ("la_forward", "delta_forward", "la_decode_step", "delta_decode_step", "gated_delta_forward",
+                 "gated_delta_decode_step"):
         assert name in fns
 
 
@@ -111,6 +112,41 @@ def _ddec(**kw):
 def test_delta_decode_rejects(kw, status):
     assert _ddec(**kw) == ST[status]
     assert lin.lib().la_last_error().decode()
+
+
+def _gdelta(**kw):
+    a = dict(q=P, k=P, v=P, beta=P, alpha=P, S0=None, o=P, S_out=None, B=1, H=1, T=8, dk=128, dv=128, dtype=1,
+             chunk=64, ws=P, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lin.lib().gated_delta_forward(a["q"], a["k"], a["v"], a["beta"], a["alpha"], a["S0"], a["o"],
+                                         a["S_out"], a["B"], a["H"], a["T"], a["dk"], a["dv"], a["dtype"],
+                                         a["chunk"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(alpha=None), "INVALID_ARG"), (dict(beta=None), "INVALID_ARG"), (dict(T=0), "INVALID_ARG"),
+    (dict(alpha=ctypes.c_void_p(0x10002)), "INVALID_ARG"), (dict(dk=100), "UNSUPPORTED"),
+    (dict(dtype=0), "UNSUPPORTED"), (dict(ws=None), "WORKSPACE"), (dict(wsb=0), "WORKSPACE"),
+])
+def test_gated_delta_forward_rejects(kw, status):
+    assert _gdelta(**kw) == ST[status]
+    assert lin.lib().la_last_error().decode().startswith("gated_delta_forward")
+
+
+def _gddec(**kw):
+    a = dict(q=P, k=P, v=P, beta=P, alpha=P, S=P, o=P, N=4, H=2, dk=128, dv=128, dtype=1, stream=None)
+    a.update(kw)
+    return lin.lib().gated_delta_decode_step(a["q"], a["k"], a["v"], a["beta"], a["alpha"], a["S"], a["o"],
+                                             a["N"], a["H"], a["dk"], a["dv"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(alpha=None), "INVALID_ARG"), (dict(S=None), "INVALID_ARG"), (dict(N=0), "INVALID_ARG"),
+    (dict(dtype=5), "INVALID_ARG"), (dict(dk=32), "UNSUPPORTED"), (dict(S=ctypes.c_void_p(0x10004)), "INVALID_ARG"),
+])
+def test_gated_delta_decode_rejects(kw, status):
+    assert _gddec(**kw) == ST[status]
+    assert lin.lib().la_last_error().decode().startswith("gated_delta_decode_step")
 
 
 def test_workspace_queries():

@@ -59,6 +59,10 @@ def lib():
             L.la_decode_step.restype = i
             L.delta_decode_step.argtypes = [vp, vp, vp, vp, fp, vp, i, i, i, i, i, vp]
             L.delta_decode_step.restype = i
+            L.gated_delta_forward.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, i, i, i, i, i, i, i, vp, sz, vp]
+            L.gated_delta_forward.restype = i
+            L.gated_delta_decode_step.argtypes = [vp, vp, vp, vp, fp, fp, vp, i, i, i, i, i, vp]
+            L.gated_delta_decode_step.restype = i
             L.la_status_string.argtypes = [i]
             L.la_status_string.restype = ctypes.c_char_p
             L.la_last_error.argtypes = []
@@ -157,6 +161,17 @@ def delta_forward(q, k, v, beta, S0=None, chunk=CHUNK, *, o=None, S_out=None, wo
                   return_state=True):
     """Delta-rule prefill.  q, k: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T].
     Returns (o, S_T)."""
+    return _delta_forward(q, k, v, beta, None, S0, chunk, o, S_out, workspace, return_state)
+
+
+def gated_delta_forward(q, k, v, beta, alpha, S0=None, chunk=CHUNK, *, o=None, S_out=None, workspace=None,
+                        return_state=True):
+    """Gated delta-rule prefill: alpha [B,H,T] fp32 forgetting factors in
+    (0, 1], applied to the state before each correction.  Returns (o, S_T)."""
+    return _delta_forward(q, k, v, beta, alpha, S0, chunk, o, S_out, workspace, return_state)
+
+
+def _delta_forward(q, k, v, beta, alpha, S0, chunk, o, S_out, workspace, return_state):
     code = _dtype_code(q)
     B, H, T, dk = q.shape
     dv = v.shape[-1]
@@ -165,6 +180,8 @@ def delta_forward(q, k, v, beta, S0=None, chunk=CHUNK, *, o=None, S_out=None, wo
     _need(v, "v", q.dtype, (B, H, T, dv), dev)
     _need(beta, "beta", q.dtype, (B, H, T), dev)
     _need(q, "q", q.dtype, (B, H, T, dk), dev)
+    if alpha is not None:
+        _need(alpha, "alpha", torch.float32, (B, H, T), dev)
     if S0 is not None:
         _need(S0, "S0", torch.float32, (B, H, dk, dv), dev)
     if o is None:
@@ -175,9 +192,13 @@ def delta_forward(q, k, v, beta, S0=None, chunk=CHUNK, *, o=None, S_out=None, wo
             S_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
         _need(S_out, "S_out", torch.float32, (B, H, dk, dv), dev)
     ws, wsb = _workspace(delta_forward_workspace_bytes(B, H, T, dk, dv, chunk), dev, workspace)
-    _check(lib().delta_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_out),
-                               B, H, T, dk, dv, code, int(chunk), _ptr(ws), wsb,
-                               _stream(dev)))
+    if alpha is None:
+        _check(lib().delta_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_out),
+                                   B, H, T, dk, dv, code, int(chunk), _ptr(ws), wsb, _stream(dev)))
+    else:
+        _check(lib().gated_delta_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S0), _ptr(o),
+                                         _ptr(S_out), B, H, T, dk, dv, code, int(chunk), _ptr(ws), wsb,
+                                         _stream(dev)))
     return o, S_out
 
 
@@ -204,6 +225,16 @@ def delta_decode_step(q, k, v, beta, S, *, o=None):
     """One delta-rule decode step; S [N,H,dk,dv] (fp32) is updated in place.
     q, k: [N,H,dk]; v: [N,H,dv]; beta: [N,H] (same dtype as q).  Returns
     o [N,H,dv] = S_new^T q."""
+    return _delta_decode(q, k, v, beta, None, S, o)
+
+
+def gated_delta_decode_step(q, k, v, beta, alpha, S, *, o=None):
+    """One gated delta-rule decode step: S (fp32, in place) is decayed by
+    alpha [N,H] (fp32) before the correction.  Returns o [N,H,dv]."""
+    return _delta_decode(q, k, v, beta, alpha, S, o)
+
+
+def _delta_decode(q, k, v, beta, alpha, S, o):
     code = _dtype_code(q)
     N, H, dk = q.shape
     dv = v.shape[-1]
@@ -212,9 +243,15 @@ def delta_decode_step(q, k, v, beta, S, *, o=None):
     _need(v, "v", q.dtype, (N, H, dv), dev)
     _need(beta, "beta", q.dtype, (N, H), dev)
     _need(S, "S", torch.float32, (N, H, dk, dv), dev)
+    if alpha is not None:
+        _need(alpha, "alpha", torch.float32, (N, H), dev)
     if o is None:
         o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
     _need(o, "o", q.dtype, (N, H, dv), dev)
-    _check(lib().delta_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S), _ptr(o), N, H, dk, dv,
-                                   code, _stream(dev)))
+    if alpha is None:
+        _check(lib().delta_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S), _ptr(o), N, H, dk, dv,
+                                       code, _stream(dev)))
+    else:
+        _check(lib().gated_delta_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S), _ptr(o),
+                                             N, H, dk, dv, code, _stream(dev)))
     return o

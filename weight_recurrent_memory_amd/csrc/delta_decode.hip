@@ -12,6 +12,10 @@
 // the partials meet in LDS, each thread sums the ones of its columns, and
 // then updates its registers and streams them back.  The read uses the old
 // state: o = S^T q + beta u (k . q).
+//
+// Gated form (LinearMem §03, the Gated DeltaNet rule): the old state is first
+// decayed by alpha, S~ = alpha S, and the step above runs on S~.  Here alpha
+// scales the two reductions and the state as it is written back.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -21,11 +25,12 @@ namespace {
 
 constexpr int NTHR = 256;
 
-template <typename TIn, int DK, int DV>
+template <typename TIn, int DK, int DV, bool GATED>
 __global__ __launch_bounds__(NTHR) void delta_decode_kernel(const TIn* __restrict__ q,
                                                             const TIn* __restrict__ k,
                                                             const TIn* __restrict__ v,
                                                             const TIn* __restrict__ beta,
+                                                            const float* __restrict__ alpha,
                                                             float* __restrict__ S, TIn* __restrict__ o) {
     constexpr int CG = DV / 4;    // 16-byte column groups per row
     constexpr int R = NTHR / CG;  // row groups
@@ -58,6 +63,7 @@ __global__ __launch_bounds__(NTHR) void delta_decode_kernel(const TIn* __restric
     for (int off = 32; off > 0; off >>= 1) kq += __shfl_xor(kq, off);
     if ((tid & 63) == 0) kq_part[tid >> 6] = kq;
     const float b = Elem<TIn>::load(beta, s);
+    const float a = GATED ? alpha[s] : 1.f;
     const v4f vv = v4f{Elem<TIn>::load(v, s * DV + 4 * cg + 0), Elem<TIn>::load(v, s * DV + 4 * cg + 1),
                        Elem<TIn>::load(v, s * DV + 4 * cg + 2), Elem<TIn>::load(v, s * DV + 4 * cg + 3)};
     __syncthreads();
@@ -81,6 +87,10 @@ __global__ __launch_bounds__(NTHR) void delta_decode_kernel(const TIn* __restric
         pred += part_k[r][cg];
         sq += part_q[r][cg];
     }
+    if constexpr (GATED) {  // reductions over the decayed state
+        pred *= a;
+        sq *= a;
+    }
     const v4f u = vv - pred;
     const v4f bu = b * u;
 
@@ -89,7 +99,7 @@ __global__ __launch_bounds__(NTHR) void delta_decode_kernel(const TIn* __restric
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int row = rg + R * m;
-        const v4f x = st[m] + fk[row] * bu;
+        const v4f x = (GATED ? a * st[m] : st[m]) + fk[row] * bu;
         __builtin_nontemporal_store(x, reinterpret_cast<v4f*>(Ss + (long)row * DV + 4 * cg));
     }
 
@@ -105,20 +115,26 @@ __global__ __launch_bounds__(NTHR) void delta_decode_kernel(const TIn* __restric
 }
 
 template <typename TIn, int DK, int DV>
-hipError_t launch_typed(const void* q, const void* k, const void* v, const void* beta, float* S, void* o,
-                        int NH, hipStream_t stream) {
-    delta_decode_kernel<TIn, DK, DV><<<dim3(NH), dim3(NTHR), 0, stream>>>(
-        static_cast<const TIn*>(q), static_cast<const TIn*>(k), static_cast<const TIn*>(v),
-        static_cast<const TIn*>(beta), S, static_cast<TIn*>(o));
+hipError_t launch_typed(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
+                        float* S, void* o, int NH, hipStream_t stream) {
+    if (alpha)
+        delta_decode_kernel<TIn, DK, DV, true><<<dim3(NH), dim3(NTHR), 0, stream>>>(
+            static_cast<const TIn*>(q), static_cast<const TIn*>(k), static_cast<const TIn*>(v),
+            static_cast<const TIn*>(beta), alpha, S, static_cast<TIn*>(o));
+    else
+        delta_decode_kernel<TIn, DK, DV, false><<<dim3(NH), dim3(NTHR), 0, stream>>>(
+            static_cast<const TIn*>(q), static_cast<const TIn*>(k), static_cast<const TIn*>(v),
+            static_cast<const TIn*>(beta), nullptr, S, static_cast<TIn*>(o));
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_delta_decode(const void* q, const void* k, const void* v, const void* beta, float* S,
-                               void* o, int NH, int dk, int dv, int dtype, hipStream_t stream) {
+hipError_t launch_delta_decode(const void* q, const void* k, const void* v, const void* beta,
+                               const float* alpha, float* S, void* o, int NH, int dk, int dv, int dtype,
+                               hipStream_t stream) {
 #define DEC_CASE(TY, DT, A, B) \
-    if (dtype == DT && dk == A && dv == B) return launch_typed<TY, A, B>(q, k, v, beta, S, o, NH, stream);
+    if (dtype == DT && dk == A && dv == B) return launch_typed<TY, A, B>(q, k, v, beta, alpha, S, o, NH, stream);
     DEC_CASE(bf16_t, 1, 64, 64)
     DEC_CASE(bf16_t, 1, 64, 128)
     DEC_CASE(bf16_t, 1, 128, 64)

@@ -27,6 +27,20 @@
 //   delta_chunk<MAP>  (M_g, N_g) for every segment but the last
 //   delta_compose     S_in(g+1) = M_g S_in(g) + N_g, fp32 MFMA, serial in g
 //   delta_chunk<OUT>  the chunk loop from S_in(g), writing O (and S_T last)
+//
+// Forgetting gate (LinearMem §03: decay the old state by alpha_t, then take
+// the error against the decayed state; the Gated DeltaNet rule):
+//   S_t = alpha_t S_{t-1} + beta_t k_t (v_t - alpha_t S_{t-1}^T k_t)^T.
+// With chunk-local products gamma_t = alpha_{c0} ... alpha_t the chunk's
+// state is S_t = gamma_t S + sum_{i<=t} (gamma_t/gamma_i) beta_i k_i u_i^T, so
+// the same scheme holds with decay ratios folded in:
+//   A[t][i] = (gamma_t/gamma_i) beta_i (k_t . k_i),     W = T diag(gamma) K,
+//   O = diag(gamma) Q S + (tril(Q K^T) o Gamma)(beta o U),  Gamma[t][i] = gamma_t/gamma_i,
+//   S' = gamma_C S + K^T diag(beta gamma_C / gamma) U.
+// Ratios are exponentials of differences of chunk-local cumulative log-gates
+// (each log clamped at -20), so no ratio divides by an underflowed product.
+// The segment maps stay affine in the incoming state, so the three launches
+// are unchanged.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -38,7 +52,7 @@ constexpr int CH = kChunk;
 constexpr int NT = 512;  // eight waves
 constexpr int NWV = 8;
 
-template <int DK, int NS, bool OUT>
+template <int DK, int NS, bool OUT, bool GATED>
 struct DL {
     static constexpr int LQ = DK + 8;  // bf16 rows with k = dk
     static constexpr int LV = NS + 8;  // bf16 rows of V
@@ -53,7 +67,7 @@ struct DL {
     static constexpr int AF = CH * LF * 4;          // A, then T blocks (fp32)
     static constexpr int AD = 4 * 256 * 4;          // diagonal blocks of A, transposed (fp32)
     static constexpr int YF = 4 * 256 * 4;          // A_BL T_TL tiles of the inverse (fp32)
-    static constexpr int BS = CH * 4;               // beta (fp32)
+    static constexpr int BS = CH * 4 * (GATED ? 4 : 1);  // beta; gated: log-gates, gamma, gamma_C/gamma (fp32)
     static constexpr int TOTAL = KS + WS + QS + VS + TS + PS + AF + AD + YF + BS;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
     static constexpr int XR = DK / 16;              // dk row tiles of a state column
@@ -83,12 +97,13 @@ __host__ __device__ constexpr void lower_tile(int id, int& i, int& j) {
 //   S[:, c] += K^T (beta o U[:, c])
 // The shared, state-free part (A, P, T, W) is computed by all waves through
 // LDS.  MAP runs N and M in the same workgroup, so T and W are built once.
-template <int DK, int NS, bool OUT>
+template <int DK, int NS, bool OUT, bool GATED>
 __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const bf16_t* __restrict__ beta, bf16_t* __restrict__ o, const float* __restrict__ state_in,
-    float* __restrict__ map_n, float* __restrict__ map_m, float* __restrict__ S_out, int T, int L, int G) {
-    using Y = DL<DK, NS, OUT>;
+    const bf16_t* __restrict__ beta, const float* __restrict__ alpha, bf16_t* __restrict__ o,
+    const float* __restrict__ state_in, float* __restrict__ map_n, float* __restrict__ map_m,
+    float* __restrict__ S_out, int T, int L, int G) {
+    using Y = DL<DK, NS, OUT, GATED>;
     using M = Mma<bf16_t>;
     using MF = Mma<float>;
     typedef M::frag frag;
@@ -105,6 +120,9 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     float* Ad = Af + CH * LF;
     float* Yf = Ad + 4 * 256;
     float* Bs = Yf + 4 * 256;
+    float* Gl = Bs + CH;  // gated: chunk-local cumulative log-gate
+    float* Ge = Gl + CH;  //        gamma_t = exp(Gl[t])
+    float* Gc = Ge + CH;  //        gamma_C / gamma_t
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int w = wave_id(tid);
@@ -146,14 +164,19 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     const rsrc_t rq = make_rsrc(qh, (uint32_t)t_end * DK * 2);
     const rsrc_t rv = make_rsrc(vh, (uint32_t)t_end * NS * 2);
     const rsrc_t rb = make_rsrc(bh, (uint32_t)t_end * 2);
+    const rsrc_t ra = make_rsrc(GATED ? alpha + (long)head * T : nullptr, GATED ? (uint32_t)t_end * 4 : 0u);
     ChunkRegs<bf16_t, DK, NT> kr, qr;
     ChunkRegs<bf16_t, NS, NT> vr;
     unsigned short bnext = 0;
+    unsigned anext = 0;
     auto load_chunk = [&](int c) {
         kr.load_buf(rk, c, tid);
         if constexpr (OUT) qr.load_buf(rq, c, tid);
         vr.load_buf(rv, c, tid);
-        if (tid < CH) bnext = __builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(c + tid) * 2, 0, 0);
+        if (tid < CH) {
+            bnext = __builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(c + tid) * 2, 0, 0);
+            if constexpr (GATED) anext = __builtin_amdgcn_raw_buffer_load_b32(ra, (uint32_t)(c + tid) * 4, 0, 0);
+        }
     };
     load_chunk(seg * L);
     // Upper blocks of T and, for outputs, of P (keys after every query of
@@ -179,7 +202,23 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         stage_rows_raw<bf16_t, DK, NT>(kr, tid, Ks, LQ);
         if constexpr (OUT) stage_rows_raw<bf16_t, DK, NT>(qr, tid, Qs, LQ);
         stage_rows_raw<bf16_t, NS, NT>(vr, tid, Vs, LV);
-        if (tid < CH) Bs[tid] = bf16_to_f32(bnext);
+        if (tid < CH) {  // wave 0
+            Bs[tid] = bf16_to_f32(bnext);
+            if constexpr (GATED) {
+                // inclusive scan of the log-gates over the chunk; tokens past
+                // the segment end count as alpha = 1, so gamma_C = gamma_{n-1}
+                float lg = tid < n ? fmaxf(logf(__uint_as_float(anext)), -20.f) : 0.f;
+#pragma unroll
+                for (int off = 1; off < CH; off <<= 1) {
+                    const float y = __shfl_up(lg, off);
+                    lg += lane >= off ? y : 0.f;
+                }
+                const float lend = __shfl(lg, CH - 1);
+                Gl[tid] = lg;
+                Ge[tid] = expf(lg);
+                Gc[tid] = expf(lend - lg);
+            }
+        }
         if (c0 + CH < t_end) load_chunk(c0 + CH);
         __syncthreads();
 
@@ -206,7 +245,10 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int t = 16 * bi + 4 * g + r, i = 16 * bj + li;
-                        a[r] = (i < t) ? Bs[i] * acc[r] : 0.f;
+                        float x = Bs[i] * acc[r];
+                        // (above the diagonal the ratio may overflow: the select drops it)
+                        if constexpr (GATED) x *= __expf(Gl[t] - Gl[i]);
+                        a[r] = (i < t) ? x : 0.f;
                         Af[t * LF + i] = a[r];
                     }
                     if constexpr (bi == bj) *reinterpret_cast<v4f*>(&Ad[bi * 256 + li * 16 + 4 * g]) = a;
@@ -216,6 +258,11 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
                     for (int kb = 0; kb < DK / 32; ++kb)
                         M::mma(acc, M::load(&Ks[(16 * bj + li) * LQ + 32 * kb], g),
                                M::load(&Qs[(16 * bi + li) * LQ + 32 * kb], g));
+                    if constexpr (GATED) {  // gamma_query / gamma_key
+                        const float gq = Gl[16 * bi + li];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[r] *= __expf(gq - Gl[16 * bj + 4 * g + r]);
+                    }
                     uint2 pk;
                     pk.x = pack_bf16x2((bi == bj && 4 * g + 0 > li) ? 0.f : acc[0],
                                        (bi == bj && 4 * g + 1 > li) ? 0.f : acc[1]);
@@ -258,6 +305,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
                             M::mma(Oq[qt], M::from_tiles(X[0][2 * kb], X[0][2 * kb + 1]),
                                    M::load(&Qs[(16 * qt + li) * LQ + 32 * kb], g));
                     }
+                    if constexpr (GATED) Oq[qt] *= Ge[16 * qt + li];  // diag(gamma) Q S
                 }
             }
         };
@@ -365,7 +413,17 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
 #pragma unroll
             for (int kb = 0; kb < CH / 32; ++kb) {
                 if (32 * kb > 16 * tt + 15) continue;  // T is lower triangular
-                M::mma(acc, M::load_tr(Ks, LQ, 32 * kb, 16 * dkt, lane), M::load(&Ts[(16 * tt + li) * LT + 32 * kb], g));
+                frag tf = M::load(&Ts[(16 * tt + li) * LT + 32 * kb], g);
+                if constexpr (GATED) {  // T diag(gamma): column s of T scaled by gamma_s
+                    const v4f e0 = *reinterpret_cast<const v4f*>(&Ge[32 * kb + 4 * g]);
+                    const v4f e1 = *reinterpret_cast<const v4f*>(&Ge[32 * kb + 16 + 4 * g]);
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2) {
+                        tf[s2] = M::cvt((float)tf[s2] * e0[s2]);
+                        tf[4 + s2] = M::cvt((float)tf[4 + s2] * e1[s2]);
+                    }
+                }
+                M::mma(acc, M::load_tr(Ks, LQ, 32 * kb, 16 * dkt, lane), tf);
             }
             __bf16* dst = &Ws[(16 * tt + li) * LQ + 16 * dkt + 4 * g];
 #pragma unroll
@@ -426,7 +484,16 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
                     }
                 }
             }
-            // S += K^T (beta o U)
+            // S += K^T (beta o U); gated: S = gamma_C S + K^T (beta gamma_C / gamma o U)
+            if constexpr (GATED) {
+                const float gend = Ge[CH - 1];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) U[j][tt][r] *= Gc[16 * tt + 4 * g + r];
+#pragma unroll
+                for (int i = 0; i < XR; ++i) X[j][i] *= gend;
+            }
 #pragma unroll
             for (int i = 0; i < XR; ++i)
 #pragma unroll
@@ -524,24 +591,24 @@ __global__ __launch_bounds__(256) void delta_compose_kernel(const float* __restr
     }
 }
 
-template <int DK, int DV>
+template <int DK, int DV, bool GATED>
 hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* beta,
-                        const float* S0, bf16_t* o, float* S_out, int HT, int T, const LaPlan& plan,
-                        float* ws, hipStream_t stream) {
+                        const float* alpha, const float* S0, bf16_t* o, float* S_out, int HT, int T,
+                        const LaPlan& plan, float* ws, hipStream_t stream) {
     const int G = plan.G, L = plan.L;
     float* map_n = ws;
     float* map_m = map_n + (size_t)HT * G * DK * DV;
     float* state_in = map_m + (size_t)HT * G * DK * DK;
     hipError_t err;
     if (G > 1) {
-        delta_chunk_kernel<DK, DV, false><<<dim3(HT * (G - 1)), dim3(NT), 0, stream>>>(
-            q, k, v, beta, nullptr, nullptr, map_n, map_m, nullptr, T, L, G);
+        delta_chunk_kernel<DK, DV, false, GATED><<<dim3(HT * (G - 1)), dim3(NT), 0, stream>>>(
+            q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, T, L, G);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     delta_compose_kernel<DK, DV><<<dim3(DV / 16, HT), dim3(256), 0, stream>>>(map_n, map_m, S0, state_in, G);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    delta_chunk_kernel<DK, DV, true><<<dim3(HT * G), dim3(NT), 0, stream>>>(
-        q, k, v, beta, o, state_in, nullptr, nullptr, S_out, T, L, G);
+    delta_chunk_kernel<DK, DV, true, GATED><<<dim3(HT * G), dim3(NT), 0, stream>>>(
+        q, k, v, beta, alpha, o, state_in, nullptr, nullptr, S_out, T, L, G);
     return hipGetLastError();
 }
 
@@ -552,16 +619,18 @@ size_t delta_ws_floats(int HT, int dk, int dv, const LaPlan& plan) {
 }
 
 hipError_t launch_delta_forward(const void* q, const void* k, const void* v, const void* beta,
-                                const float* S0, void* o, float* S_out, int HT, int T, int dk, int dv,
-                                int dtype, const LaPlan& plan, float* ws, hipStream_t stream) {
+                                const float* alpha, const float* S0, void* o, float* S_out, int HT, int T,
+                                int dk, int dv, int dtype, const LaPlan& plan, float* ws, hipStream_t stream) {
     if (dtype != 1) return hipErrorInvalidValue;
     const bf16_t* qb = static_cast<const bf16_t*>(q);
     const bf16_t* kb = static_cast<const bf16_t*>(k);
     const bf16_t* vb = static_cast<const bf16_t*>(v);
     const bf16_t* bb = static_cast<const bf16_t*>(beta);
     bf16_t* ob = static_cast<bf16_t*>(o);
-#define DELTA_CASE(A, B) \
-    if (dk == A && dv == B) return launch_typed<A, B>(qb, kb, vb, bb, S0, ob, S_out, HT, T, plan, ws, stream);
+#define DELTA_CASE(A, B)                                                                              \
+    if (dk == A && dv == B)                                                                           \
+        return alpha ? launch_typed<A, B, true>(qb, kb, vb, bb, alpha, S0, ob, S_out, HT, T, plan, ws, stream) \
+                     : launch_typed<A, B, false>(qb, kb, vb, bb, nullptr, S0, ob, S_out, HT, T, plan, ws, stream);
     DELTA_CASE(64, 64)
     DELTA_CASE(64, 128)
     DELTA_CASE(128, 64)

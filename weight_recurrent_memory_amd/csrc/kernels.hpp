@@ -30,17 +30,20 @@ LaPlan la_plan(int HT, int T, int dk, int dv);
 size_t la_flag_words(int HT, int G);
 size_t la_ws_floats(int HT, int T, int dk, int dv);
 
-// Delta-rule prefill: segment affine maps -> serial composition -> chunked outputs.
+// Delta-rule prefill: segment affine maps -> serial composition -> chunked
+// outputs.  alpha (fp32 [HT][T]) selects the gated rule; NULL = ungated.
 hipError_t launch_delta_forward(const void* q, const void* k, const void* v,
-                                const void* beta, const float* S0, void* o,
-                                float* S_out, int HT, int T, int dk, int dv,
+                                const void* beta, const float* alpha, const float* S0,
+                                void* o, float* S_out, int HT, int T, int dk, int dv,
                                 int dtype, const LaPlan& plan, float* ws,
                                 hipStream_t stream);
 size_t delta_ws_floats(int HT, int dk, int dv, const LaPlan& plan);
 
-// Delta-rule decode step on a resident fp32 state (in place).
-hipError_t launch_delta_decode(const void* q, const void* k, const void* v, const void* beta, float* S,
-                               void* o, int NH, int dk, int dv, int dtype, hipStream_t stream);
+// Delta-rule decode step on a resident fp32 state (in place); alpha (fp32
+// [NH]) selects the gated rule, NULL = ungated.
+hipError_t launch_delta_decode(const void* q, const void* k, const void* v, const void* beta,
+                               const float* alpha, float* S, void* o, int NH, int dk, int dv, int dtype,
+                               hipStream_t stream);
 
 // Linear attention decode step on a resident fp32 state (in place).
 hipError_t launch_la_decode(const void* q, const void* k, const void* v, float* S,

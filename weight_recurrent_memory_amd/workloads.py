@@ -7,7 +7,10 @@ Distributions follow the pages' settings: N(0, 1) draws for q, k, v
 (Gaussian, then normalised per token: same page §03, the delta rule assumes
 unit keys), beta through a sigmoid (same page §08: the final per-token step
 size after the model's transform), d = 64 / 128 with lengths up to 65536
-(same page §01 ledger).  bf16 inputs are fp32 draws rounded to nearest even.
+(same page §01 ledger).  Forgetting gates take the Mamba-2 form of the
+"线性注意力与 SSM" page (§2.9, and §3 on Mamba-2), alpha = exp(-Delta a)
+with Delta = softplus(N(0, 1)) and a = 1/16: alpha lies in about (0.83,
+0.997), median about 0.96.  bf16 inputs are fp32 draws rounded to nearest even.
 Generation runs on the device the tensors are wanted on, with a
 torch.Generator seeded per workload.
 """
@@ -21,7 +24,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str        # "la", "delta", "decode" or "delta_decode"
+    kind: str        # "la", "delta", "decode", "delta_decode", "gated_delta", "gated_delta_decode"
     B: int           # batch (decode: sequences N)
     H: int
     T: int           # tokens (decode: number of steps)
@@ -43,6 +46,12 @@ ALL = (LA_FP32_SMALL, LA_BF16_PREFILL, DELTA_BF16_PREFILL, LA_BF16_LONG, DECODE_
 # The delta-rule decode step on the decode configuration's states and steps.
 DELTA_DECODE_BF16 = Workload("delta_decode_bf16_n256_h32_d128_1000steps", "delta_decode", 256, 32, 1000, 128,
                              128, torch.bfloat16, 6)
+# The gated delta rule on the delta prefill and decode configurations.
+GATED_DELTA_BF16_PREFILL = Workload("gated_delta_bf16_b2_h16_t16384_d128", "gated_delta", 2, 16, 16384, 128, 128,
+                                    torch.bfloat16, 7)
+GATED_DELTA_DECODE_BF16 = Workload("gated_delta_decode_bf16_n256_h32_d128_1000steps", "gated_delta_decode", 256,
+                                   32, 1000, 128, 128, torch.bfloat16, 8)
+GATE_RATE = 1.0 / 16
 
 
 def _gen(seed: int, device) -> torch.Generator:
@@ -109,6 +118,12 @@ def delta_decode_tokens(steps, N, H, dk, dv, dtype, seed, device="cpu"):
     return q, k, v, beta
 
 
+def gates(shape, seed, device="cpu", rate=GATE_RATE):
+    """Forgetting factors alpha = exp(-softplus(N(0, 1)) * rate), fp32."""
+    g = _gen(seed + 2000003, device)
+    return torch.exp(-torch.nn.functional.softplus(_normal(shape, g, device)) * rate)
+
+
 def make(w: Workload, device="cpu"):
     """All inputs of a workload on `device`."""
     if w.kind == "la":
@@ -121,4 +136,11 @@ def make(w: Workload, device="cpu"):
     if w.kind == "delta_decode":
         S, _ = decode_state(w.B, w.H, w.dk, w.dv, w.seed, device, std=0.1)
         return (S,) + delta_decode_tokens(w.T, w.B, w.H, w.dk, w.dv, w.dtype, w.seed, device)
+    if w.kind == "gated_delta":
+        return delta_inputs(w.B, w.H, w.T, w.dk, w.dv, w.dtype, w.seed, device) + (
+            gates((w.B, w.H, w.T), w.seed, device),)
+    if w.kind == "gated_delta_decode":
+        S, _ = decode_state(w.B, w.H, w.dk, w.dv, w.seed, device, std=0.1)
+        return (S,) + delta_decode_tokens(w.T, w.B, w.H, w.dk, w.dv, w.dtype, w.seed, device) + (
+            gates((w.T, w.B, w.H), w.seed, device),)
     raise ValueError(w.kind)
