@@ -13,8 +13,8 @@ The line printed is one JSON object:
 * cpu_baseline: the fp64 oracle (C, OpenMP over heads) timed on the host on
   the same workload;
 * extra: the other measured paths -- the long-stream LA workload, the delta
-  rule workload and the 1000-step decode chains of both rules (state-update
-  GB/s) -- each with its own roofline fraction.
+  rule and gated delta rule prefills and the 1000-step decode chains of the
+  three rules (state-update GB/s) -- each with its own roofline fraction.
 
 Inputs are synthetic (seeded, generated on the device) and rotate among
 several copies so that each step reads data evicted from the 256 MB
@@ -48,9 +48,9 @@ LA_TRAFFIC = {
     "sources": ["weight_recurrent_memory_amd/csrc/la_prefill.hip",
                 "weight_recurrent_memory_amd/csrc/common.hpp",
                 "weight_recurrent_memory_amd/csrc/kernels.hpp"],
-    "sha256": "4314bf120cb6071d41530235a9ac88072c13011e2d7a5861a02b4a02eae82607",
-    "fetch_kib": 86749.0, "fetch_scale": 2.0,
-    "write_kib": 56819.0, "write_scale": 1.0,
+    "sha256": "76c1977a0deec08c1d2e7bcd02abfa8cf1f8b7d3ad500ecc2b9b3b7c114d2888",
+    "fetch_kib": 86720.0, "fetch_scale": 2.0,
+    "write_kib": 56826.0, "write_scale": 1.0,
 }
 
 
@@ -76,8 +76,10 @@ def la_flops(B, H, T, dk, dv, C=64):
     return B * H * T * ((C + 1) * (dk + dv) + 4 * dk * dv)
 
 
-def delta_bytes(B, H, T, dk, dv, el):
-    return B * H * T * (2 * dk + dv) * el + B * H * T * el + B * H * T * dv * el + B * H * dk * dv * 4
+def delta_bytes(B, H, T, dk, dv, el, gated=False):
+    # q, k, v, beta read, o written, final state written; gated: alpha (fp32) read
+    return (B * H * T * (2 * dk + dv) * el + B * H * T * el + B * H * T * dv * el + B * H * dk * dv * 4
+            + (B * H * T * 4 if gated else 0))
 
 
 def delta_flops(B, H, T, dk, dv, C=64):
@@ -88,9 +90,9 @@ def decode_bytes(N, H, dk, dv, el):
     return N * H * (2 * dk * dv * 4 + 2 * dk * 4 + (2 * dk + dv) * el + dv * el)
 
 
-def delta_decode_bytes(N, H, dk, dv, el):
-    # S read and written (fp32); q, k, v, beta read; o written
-    return N * H * (2 * dk * dv * 4 + (2 * dk + dv + 1) * el + dv * el)
+def delta_decode_bytes(N, H, dk, dv, el, gated=False):
+    # S read and written (fp32); q, k, v, beta read; o written; gated: alpha (fp32) read
+    return N * H * (2 * dk * dv * 4 + (2 * dk + dv + 1) * el + dv * el + (4 if gated else 0))
 
 
 def _events(n):
@@ -143,19 +145,26 @@ def bench_la(w, steps, warmup, copies, lin, wl):
 
 
 def bench_delta(w, steps, warmup, copies, lin, wl):
+    """delta_forward, or gated_delta_forward for a gated workload."""
     dev = torch.device("cuda:0")
     el = 2
-    sets = [wl.delta_inputs(w.B, w.H, w.T, w.dk, w.dv, w.dtype, w.seed + 17 * i, dev) for i in range(copies)]
+    gated = w.kind == "gated_delta"
+    sets = [wl.delta_inputs(w.B, w.H, w.T, w.dk, w.dv, w.dtype, w.seed + 17 * i, dev)
+            + ((wl.gates((w.B, w.H, w.T), w.seed + 17 * i, dev),) if gated else ()) for i in range(copies)]
     outs = [torch.empty((w.B, w.H, w.T, w.dv), dtype=w.dtype, device=dev) for _ in range(copies)]
     S = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
     ws = torch.empty(lin.delta_forward_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv), dtype=torch.uint8, device=dev)
 
     def step(i):
-        q, k, v, beta = sets[i % copies]
-        lin.delta_forward(q, k, v, beta, o=outs[i % copies], S_out=S, workspace=ws)
+        if gated:
+            q, k, v, beta, alpha = sets[i % copies]
+            lin.gated_delta_forward(q, k, v, beta, alpha, o=outs[i % copies], S_out=S, workspace=ws)
+        else:
+            q, k, v, beta = sets[i % copies]
+            lin.delta_forward(q, k, v, beta, o=outs[i % copies], S_out=S, workspace=ws)
 
     wall, mean_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
-    nbytes = delta_bytes(w.B, w.H, w.T, w.dk, w.dv, el)
+    nbytes = delta_bytes(w.B, w.H, w.T, w.dk, w.dv, el, gated)
     fl = delta_flops(w.B, w.H, w.T, w.dk, w.dv)
     return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "tokens_per_s": w.B * w.T * steps / wall,
             "bytes": nbytes, "flops": fl, "gbs": nbytes / (mean_ms * 1e-3) / 1e9,
@@ -178,17 +187,25 @@ def bench_decode(w, lin, wl, n_steps=None):
 
 
 def bench_delta_decode(w, lin, wl, n_steps=None):
+    """delta_decode_step, or gated_delta_decode_step for a gated workload."""
     dev = torch.device("cuda:0")
-    S, Q, K, V, Bt = wl.make(w, dev)
+    gated = w.kind == "gated_delta_decode"
+    if gated:
+        S, Q, K, V, Bt, At = wl.make(w, dev)
+    else:
+        S, Q, K, V, Bt = wl.make(w, dev)
     n = w.T if n_steps is None else n_steps
     o = torch.empty((w.B, w.H, w.dv), dtype=w.dtype, device=dev)
 
     def step(i):
         j = i % w.T
-        lin.delta_decode_step(Q[j], K[j], V[j], Bt[j], S, o=o)
+        if gated:
+            lin.gated_delta_decode_step(Q[j], K[j], V[j], Bt[j], At[j], S, o=o)
+        else:
+            lin.delta_decode_step(Q[j], K[j], V[j], Bt[j], S, o=o)
 
     wall, mean_ms = time_calls(step, n, 10, torch.cuda.current_stream(dev))
-    per = delta_decode_bytes(w.B, w.H, w.dk, w.dv, 2)
+    per = delta_decode_bytes(w.B, w.H, w.dk, w.dv, 2, gated)
     return {"steps": n, "ms_per_step": 1e3 * wall / n, "event_ms_mean": mean_ms, "bytes_per_step": per,
             "gbs_wall": per * n / wall / 1e9, "gbs": per / (mean_ms * 1e-3) / 1e9}
 
@@ -226,7 +243,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=4, help="input copies rotated through (cache eviction)")
-    ap.add_argument("--only", choices=["all", "la", "la_long", "delta", "decode", "delta_decode"], default="all")
+    ap.add_argument("--only", choices=["all", "la", "la_long", "delta", "gated_delta", "decode", "delta_decode",
+                                       "gated_delta_decode"], default="all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
@@ -257,8 +275,9 @@ def main():
         extra[wl_.name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
                            "hbm_gbs": r["gbs"], "hbm_frac": r["gbs"] / HBM_PEAK_GBS,
                            "mfma_tflops": r["tflops"], "mfma_frac": r["tflops"] / BF16_MFMA_PEAK_TFS}
-    if args.only in ("all", "delta"):
-        wd = wl.DELTA_BF16_PREFILL
+    for key, wd in (("delta", wl.DELTA_BF16_PREFILL), ("gated_delta", wl.GATED_DELTA_BF16_PREFILL)):
+        if args.only not in ("all", key):
+            continue
         try:
             r = bench_delta(wd, max(3, args.steps // 5), 2, 2, lin, wl)
             extra[wd.name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
@@ -273,8 +292,9 @@ def main():
                             "gbs_wall_incl_launch_gaps": r["gbs_wall"], "us_per_step": 1e3 * r["event_ms_mean"],
                             "steps": r["steps"], "bytes_per_step": r["bytes_per_step"]}
 
-    if args.only in ("all", "delta_decode"):
-        wdd = wl.DELTA_DECODE_BF16
+    for key, wdd in (("delta_decode", wl.DELTA_DECODE_BF16), ("gated_delta_decode", wl.GATED_DELTA_DECODE_BF16)):
+        if args.only not in ("all", key):
+            continue
         r = bench_delta_decode(wdd, lin, wl)
         extra[wdd.name] = {"state_update_gbs": r["gbs"], "hbm_frac": r["gbs"] / HBM_PEAK_GBS,
                            "gbs_wall_incl_launch_gaps": r["gbs_wall"], "us_per_step": 1e3 * r["event_ms_mean"],

@@ -63,12 +63,13 @@ struct DL {
     static constexpr int QS = OUT ? CH * LQ * 2 : 0;
     static constexpr int VS = CH * LV * 2;          // V_c rows (read transposed)
     static constexpr int TS = CH * LT * 2;          // T (bf16)
+    static constexpr int TG = GATED ? CH * LT * 2 : 0;  // gated: T diag(gamma) (bf16)
     static constexpr int PS = OUT ? CH * LT * 2 : 0;  // tril(Q K^T), rows = queries
     static constexpr int AF = CH * LF * 4;          // A, then T blocks (fp32)
     static constexpr int AD = 4 * 256 * 4;          // diagonal blocks of A, transposed (fp32)
     static constexpr int YF = 4 * 256 * 4;          // A_BL T_TL tiles of the inverse (fp32)
     static constexpr int BS = CH * 4 * (GATED ? 4 : 1);  // beta; gated: log-gates, gamma, gamma_C/gamma (fp32)
-    static constexpr int TOTAL = KS + WS + QS + VS + TS + PS + AF + AD + YF + BS;
+    static constexpr int TOTAL = KS + WS + QS + VS + TS + TG + PS + AF + AD + YF + BS;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
     static constexpr int XR = DK / 16;              // dk row tiles of a state column
     // State column tiles: OUT carries S (NS columns); MAP carries N (NS
@@ -115,6 +116,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     __bf16* Qs = reinterpret_cast<__bf16*>(sp);  sp += Y::QS;
     __bf16* Vs = reinterpret_cast<__bf16*>(sp);  sp += Y::VS;
     __bf16* Ts = reinterpret_cast<__bf16*>(sp);  sp += Y::TS;
+    __bf16* Tg = reinterpret_cast<__bf16*>(sp);  sp += Y::TG;
     __bf16* Ps = reinterpret_cast<__bf16*>(sp);  sp += Y::PS;
     float* Af = reinterpret_cast<float*>(sp);
     float* Ad = Af + CH * LF;
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     ChunkRegs<bf16_t, NS, NT> vr;
     unsigned short bnext = 0;
     unsigned anext = 0;
-    auto load_chunk = [&](int c) {
+    auto load_chunk = [&](int c, int tid) {
         kr.load_buf(rk, c, tid);
         if constexpr (OUT) qr.load_buf(rq, c, tid);
         vr.load_buf(rv, c, tid);
@@ -178,7 +180,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
             if constexpr (GATED) anext = __builtin_amdgcn_raw_buffer_load_b32(ra, (uint32_t)(c + tid) * 4, 0, 0);
         }
     };
-    load_chunk(seg * L);
+    load_chunk(seg * L, tid);
     // Upper blocks of T and, for outputs, of P (keys after every query of
     // the tile) are read as zero operands and never written: clear them once.
     for (int e = tid; e < 6 * 256; e += NT) {
@@ -186,6 +188,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         const int bi = tile < 3 ? 0 : tile < 5 ? 1 : 2;
         const int bj = tile < 3 ? tile + 1 : tile < 5 ? tile - 1 : 3;
         Ts[(16 * bi + r) * LT + 16 * bj + c] = M::cvt(0.f);
+        if constexpr (GATED) Tg[(16 * bi + r) * LT + 16 * bj + c] = M::cvt(0.f);
     }
     if constexpr (OUT) {
         for (int e = tid; e < 6 * 256; e += NT) {
@@ -196,6 +199,14 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         }
     }
     for (int c0 = seg * L; c0 < t_end; c0 += CH) {
+        // Gated: the lane indices are re-derived from an opaque copy every
+        // chunk.  Otherwise the many per-lane LDS addresses built from them
+        // are hoisted out of the loop and held, then spilled, for its whole
+        // length; recomputed here they live only next to their uses.  (The
+        // ungated kernels fit with hoisted addresses and run faster so.)
+        int tid_v = threadIdx.x;
+        if constexpr (GATED) asm volatile("" : "+v"(tid_v));
+        const int tid = tid_v, lane = tid & 63, g = lane >> 4, li = lane & 15;
         const int n = min(CH, t_end - c0);
         // ---- stage the chunk row-major (transposed operands are read with
         // transpose loads)
@@ -219,7 +230,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
                 Gc[tid] = expf(lend - lg);
             }
         }
-        if (c0 + CH < t_end) load_chunk(c0 + CH);
+        if (c0 + CH < t_end) load_chunk(c0 + CH, tid);
         __syncthreads();
 
         // ---- A = tril_{-1}(K K^T) diag(beta) (fp32) and, for outputs, the
@@ -328,10 +339,12 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
 #pragma unroll
                 for (int i = m + 1; i < 16; ++i) d[i] -= c[i >> 2][i & 3] * d[m];
             }
+            const float gj = GATED ? Ge[16 * b + j] : 1.f;
 #pragma unroll
             for (int m = 0; m < 16; ++m) {
                 Af[(16 * b + m) * LF + 16 * b + j] = d[m];
                 Ts[(16 * b + m) * LT + 16 * b + j] = M::cvt(d[m]);
+                if constexpr (GATED) Tg[(16 * b + m) * LT + 16 * b + j] = M::cvt(d[m] * gj);
             }
         }
         __syncthreads();
@@ -362,6 +375,11 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         auto put_T = [&](int bi, int bj, const v4f& x) {  // T block (bi, bj), bi > bj, to Ts (bf16)
 #pragma unroll
             for (int r = 0; r < 4; ++r) Ts[(16 * bi + 4 * g + r) * LT + 16 * bj + li] = M::cvt(x[r]);
+            if constexpr (GATED) {  // and T diag(gamma) to Tg
+                const float gc = Ge[16 * bj + li];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Tg[(16 * bi + 4 * g + r) * LT + 16 * bj + li] = M::cvt(x[r] * gc);
+            }
         };
         if (w == 1 || w == 2) {
             const int lo = w == 1 ? 0 : 32;  // T10 (w 1) or T32 (w 2)
@@ -404,8 +422,9 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         }
         __syncthreads();
 
-        // ---- W = T K (computed as transposed tiles, rows land as 8-byte
-        // stores) and this wave's U_v = T V columns
+        // ---- W = T K (gated: T diag(gamma) K, from Tg; computed as
+        // transposed tiles, rows land as 8-byte stores) and this wave's
+        // U_v = T V columns
 #pragma unroll
         for (int c = 0; c < Y::W_TPW; ++c) {
             const int dkt = w % XR, tt = (w / XR) * Y::W_TPW + c;
@@ -413,17 +432,8 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
 #pragma unroll
             for (int kb = 0; kb < CH / 32; ++kb) {
                 if (32 * kb > 16 * tt + 15) continue;  // T is lower triangular
-                frag tf = M::load(&Ts[(16 * tt + li) * LT + 32 * kb], g);
-                if constexpr (GATED) {  // T diag(gamma): column s of T scaled by gamma_s
-                    const v4f e0 = *reinterpret_cast<const v4f*>(&Ge[32 * kb + 4 * g]);
-                    const v4f e1 = *reinterpret_cast<const v4f*>(&Ge[32 * kb + 16 + 4 * g]);
-#pragma unroll
-                    for (int s2 = 0; s2 < 4; ++s2) {
-                        tf[s2] = M::cvt((float)tf[s2] * e0[s2]);
-                        tf[4 + s2] = M::cvt((float)tf[4 + s2] * e1[s2]);
-                    }
-                }
-                M::mma(acc, M::load_tr(Ks, LQ, 32 * kb, 16 * dkt, lane), tf);
+                M::mma(acc, M::load_tr(Ks, LQ, 32 * kb, 16 * dkt, lane),
+                       M::load(&(GATED ? Tg : Ts)[(16 * tt + li) * LT + 32 * kb], g));
             }
             __bf16* dst = &Ws[(16 * tt + li) * LQ + 16 * dkt + 4 * g];
 #pragma unroll
