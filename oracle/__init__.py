@@ -36,6 +36,16 @@ Functions and what pins them (the pins are in ``tests/test_oracle_pins.py``):
     form with decay products solved by LAPACK, the exact overwrite after the
     decay, the step chain equal to the sequence form, and the order check
     (decaying after the correction gives a different, wrong state).
+``ssd_forward`` / ``ssd_decode_step`` -- scalar-decay memory, the Mamba-2 /
+    SSD form (LA-SSM §3): S_t = alpha_t S_{t-1} + k_t v_t^T, o_t = S_t^T q_t.
+    Pinned by the Recurrence page's explicit mixing matrix of the selective
+    scan (d_k = d_v = 1: M[j][i] = c_j b_i prod_{i<s<=j} a_s), a brute-force
+    sum of decayed outer products at larger sizes, alpha = 1 equal bit for
+    bit to the additive memory (identity map, no normaliser), the page's
+    chunked scan (state handed across chunk boundaries) equal to one pass,
+    the LinearMem decay read ([0, 0.8] at alpha = 0.8 on an identity state
+    for an orthogonal key, §06), and the step chain equal to the sequence
+    form.
 ``delta_decode_step`` -- one in-place delta-rule step.  Pinned by the LA-SSM
     page's 4-token delta example replayed one step at a time (every
     intermediate state and the final read of k_1), the bit-exact overwrite
@@ -97,6 +107,10 @@ def _load():
             lib.gated_delta_ref_forward.restype = None
             lib.gated_delta_ref_decode_step.argtypes = [dp, dp, dp, dp, dp, dp, dp, i, i, i, i]
             lib.gated_delta_ref_decode_step.restype = None
+            lib.ssd_ref_forward.argtypes = [dp, dp, dp, dp, dp, dp, dp, i, i, i, i, i]
+            lib.ssd_ref_forward.restype = None
+            lib.ssd_ref_decode_step.argtypes = [dp, dp, dp, dp, dp, dp, i, i, i, i]
+            lib.ssd_ref_decode_step.restype = None
             lib.oracle_phi.argtypes = [dp, dp, ctypes.c_long]
             lib.oracle_phi.restype = None
             lib.oracle_num_threads.argtypes = []
@@ -224,4 +238,34 @@ def gated_delta_decode_step(q, k, v, beta, alpha, S):
     o = np.empty((N, H, dv))
     _load().gated_delta_ref_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S),
                                         _ptr(o), N, H, dk, dv)
+    return o, S
+
+
+def ssd_forward(q, k, v, alpha, S0=None):
+    """Scalar-decay memory (Mamba-2 / SSD form).  q, k: [B,H,T,dk]; v: [B,H,T,dv];
+    alpha: [B,H,T] -> (o [B,H,T,dv], S [B,H,dk,dv])."""
+    q, k, v, alpha, S0 = map(_f64, (q, k, v, alpha, S0))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and v.shape[:3] == (B, H, T) and alpha.shape == (B, H, T)
+    if S0 is not None:
+        assert S0.shape == (B, H, dk, dv)
+    o = np.empty((B, H, T, dv))
+    S = np.empty((B, H, dk, dv))
+    _load().ssd_ref_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(S0), _ptr(o), _ptr(S),
+                            B, H, T, dk, dv)
+    return o, S
+
+
+def ssd_decode_step(q, k, v, alpha, S):
+    """One scalar-decay step on a copy of S.  q, k: [N,H,dk]; v: [N,H,dv];
+    alpha: [N,H]; S: [N,H,dk,dv] -> (o [N,H,dv], S_new)."""
+    q, k, v, alpha = map(_f64, (q, k, v, alpha))
+    S = _f64(S).copy()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and v.shape == (N, H, dv) and alpha.shape == (N, H)
+    assert S.shape == (N, H, dk, dv)
+    o = np.empty((N, H, dv))
+    _load().ssd_ref_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(S), _ptr(o), N, H, dk, dv)
     return o, S

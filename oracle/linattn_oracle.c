@@ -259,6 +259,70 @@ void gated_delta_ref_decode_step(const double* q, const double* k, const double*
     delta_gated_decode_step(q, k, v, beta, alpha, S, o, N, H, dk, dv);
 }
 
+/*
+ * Scalar-decay linear memory, the Mamba-2 / SSD form ([LA-SSM] §3 "Mamba 一族",
+ * Mamba-2 paragraph: the outer-product state with a scalar decay alpha_t on
+ * the old state; written key-first here):
+ *   S_t = alpha_t S_{t-1} + k_t v_t^T,    o_t = S_t^T q_t    (write, then read).
+ * No feature map, no normaliser, no correction.  With d_k = d_v = 1 this is
+ * the elementwise recurrence of [Recurrence] "Selective scan" with a = alpha,
+ * b = k, x = v, c = q.  alpha [B][H][T].
+ */
+void ssd_ref_forward(const double* q, const double* k, const double* v, const double* alpha,
+                     const double* S0, double* o, double* S_out,
+                     int B, int H, int T, int dk, int dv) {
+    const long heads = (long)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long h = 0; h < heads; ++h) {
+        double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+        for (long i = 0; i < (long)dk * dv; ++i) S[i] = S0 ? S0[h * dk * dv + i] : 0.0;
+        const double* qh = q + h * (long)T * dk;
+        const double* kh = k + h * (long)T * dk;
+        const double* vh = v + h * (long)T * dv;
+        const double* ah = alpha + h * (long)T;
+        double* oh = o + h * (long)T * dv;
+        for (int t = 0; t < T; ++t) {
+            const double* kt = kh + (long)t * dk;
+            const double* vt = vh + (long)t * dv;
+            const double* qt = qh + (long)t * dk;
+            /* decay the old state, then add the outer product */
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j)
+                    S[(long)i * dv + j] = ah[t] * S[(long)i * dv + j] + kt[i] * vt[j];
+            /* read with the updated state */
+            for (int j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < dk; ++i) acc += qt[i] * S[(long)i * dv + j];
+                oh[(long)t * dv + j] = acc;
+            }
+        }
+        if (S_out) memcpy(S_out + h * (long)dk * dv, S, sizeof(double) * (size_t)dk * dv);
+        free(S);
+    }
+}
+
+/* One step of the rule above on a resident state S [N][H][dk][dv], in place;
+ * alpha [N][H]. */
+void ssd_ref_decode_step(const double* q, const double* k, const double* v, const double* alpha,
+                         double* S, double* o, int N, int H, int dk, int dv) {
+    const long states = (long)N * H;
+#pragma omp parallel for schedule(static)
+    for (long s = 0; s < states; ++s) {
+        double* Ss = S + s * (long)dk * dv;
+        const double* ks = k + s * (long)dk;
+        const double* vs = v + s * (long)dv;
+        const double* qs = q + s * (long)dk;
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j)
+                Ss[(long)i * dv + j] = alpha[s] * Ss[(long)i * dv + j] + ks[i] * vs[j];
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i) acc += qs[i] * Ss[(long)i * dv + j];
+            o[s * (long)dv + j] = acc;
+        }
+    }
+}
+
 /* The feature map alone, so tests can pin its branches directly. */
 void oracle_phi(const double* x, double* y, long n) {
     for (long i = 0; i < n; ++i) y[i] = phi_elu1(x[i]);

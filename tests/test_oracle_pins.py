@@ -577,3 +577,101 @@ def test_gated_delta_decode_chain_equals_forward():
         outs.append(o)
     np.testing.assert_allclose(np.stack(outs, 2), of, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(S, Sf, rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------- scalar decay (SSD)
+
+def _ssd1(q, k, v, alpha, S0=None):
+    o, S = oracle.ssd_forward(_h(q), _h(k), _h(v), np.asarray(alpha, dtype=np.float64)[None, None],
+                              None if S0 is None else S0[None, None])
+    return o[0, 0], S[0, 0]
+
+
+def test_ssd_scalar_case_is_the_explicit_mixing_matrix():
+    # "手撕：递推与记忆模型" "Selective scan": with h_t = a_t h_{t-1} + b_t x_t and
+    # y_t = c_t h_t, output j weighs input i (i <= j) by c_j b_i prod_{i<s<=j} a_s.
+    # d_k = d_v = 1 maps a -> alpha, b -> k, x -> v, c -> q.
+    rng = np.random.default_rng(70)
+    T = 6
+    a = 1.0 / (1.0 + np.exp(-rng.normal(size=T)))
+    b, c, x = rng.normal(size=T), rng.normal(size=T), rng.normal(size=T)
+    M = np.zeros((T, T))
+    for j in range(T):
+        for i in range(j + 1):
+            w = c[j] * b[i]
+            for s in range(i + 1, j + 1):
+                w *= a[s]
+            M[j, i] = w
+    o, S = _ssd1(c[:, None], b[:, None], x[:, None], a)
+    np.testing.assert_allclose(o[:, 0], M @ x, rtol=1e-13, atol=1e-15)
+    # the final state is the last output divided by its read weight
+    np.testing.assert_allclose(S[0, 0] * c[-1], (M @ x)[-1], rtol=1e-13)
+
+
+@pytest.mark.parametrize("T,dk,dv,seed", [(1, 3, 2, 1), (9, 4, 5, 2), (40, 6, 3, 3)])
+def test_ssd_is_the_sum_of_decayed_outer_products(T, dk, dv, seed):
+    # S_t = (prod_{s<=t} alpha_s) S_0 + sum_{i<=t} (prod_{i<s<=t} alpha_s) k_i v_i^T
+    rng = np.random.default_rng(80 + seed)
+    q, k, v = rng.normal(size=(T, dk)), rng.normal(size=(T, dk)), rng.normal(size=(T, dv))
+    alpha = rng.uniform(0.3, 1.0, size=T)
+    S0 = rng.normal(size=(dk, dv))
+    o, S = _ssd1(q, k, v, alpha, S0=S0)
+    for t in range(T):
+        St = np.prod(alpha[:t + 1]) * S0
+        for i in range(t + 1):
+            St = St + np.prod(alpha[i + 1:t + 1]) * np.outer(k[i], v[i])
+        np.testing.assert_allclose(o[t], q[t] @ St, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(S, St, rtol=1e-12, atol=1e-13)
+
+
+def test_ssd_alpha_one_is_the_additive_memory_bitwise():
+    rng = np.random.default_rng(71)
+    B, H, T, dk, dv = 2, 2, 30, 5, 4
+    q, k, v = rng.normal(size=(B, H, T, dk)), rng.normal(size=(B, H, T, dk)), rng.normal(size=(B, H, T, dv))
+    S0 = rng.normal(size=(B, H, dk, dv))
+    o1, S1 = oracle.ssd_forward(q, k, v, np.ones((B, H, T)), S0)
+    o2, S2, _ = oracle.la_forward(q, k, v, S0=S0, feature=oracle.PHI_IDENTITY, normalize=False)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+
+
+def test_ssd_chunked_scan_equals_one_pass():
+    # "手撕：递推与记忆模型" "Chunked scan": only the final state crosses a chunk
+    # boundary; the chunked run equals the full run.
+    rng = np.random.default_rng(72)
+    B, H, T, dk, dv = 1, 3, 23, 4, 4
+    q, k, v = rng.normal(size=(B, H, T, dk)), rng.normal(size=(B, H, T, dk)), rng.normal(size=(B, H, T, dv))
+    alpha = rng.uniform(0.2, 1.0, size=(B, H, T))
+    full, Sf = oracle.ssd_forward(q, k, v, alpha)
+    outs, S = [], None
+    for s in range(0, T, 4):
+        o, S = oracle.ssd_forward(q[:, :, s:s + 4], k[:, :, s:s + 4], v[:, :, s:s + 4], alpha[:, :, s:s + 4], S)
+        outs.append(o)
+    assert np.array_equal(np.concatenate(outs, 2), full) and np.array_equal(S, Sf)
+
+
+def test_ssd_decay_reaches_an_orthogonal_key_linearmem():
+    # LinearMem §06: decay scales the whole state, including maps of keys
+    # orthogonal to the one written: identity state, alpha = 0.8, write key
+    # (1, 0) -> (0, 1), read (0, 1) -> [0, 0.8].  The write term adds
+    # (k . q) v = 0, so the scalar-decay rule gives the page's read too.
+    g = _golden("linearmem_memory_experiment.json")
+    o, S = _ssd1([[0.0, 1.0]], [g["key"]], [g["values"][1]], [0.8], S0=np.eye(2))
+    np.testing.assert_allclose(o[0], g["gated_unrelated_key_read_alpha_0.8"], atol=1e-15)
+
+
+def test_ssd_decode_chain_equals_forward_and_zero_alpha_resets():
+    rng = np.random.default_rng(73)
+    N, H, dk, dv, steps = 2, 2, 4, 3, 25
+    S = rng.normal(size=(N, H, dk, dv))
+    q, k, v = rng.normal(size=(steps, N, H, dk)), rng.normal(size=(steps, N, H, dk)), rng.normal(size=(steps, N, H, dv))
+    alpha = rng.uniform(0.5, 1.0, size=(steps, N, H))
+    tr = lambda x: x.transpose(1, 2, 0, 3) if x.ndim == 4 else x.transpose(1, 2, 0)
+    of, Sf = oracle.ssd_forward(tr(q), tr(k), tr(v), tr(alpha), S0=S)
+    outs = []
+    for t in range(steps):
+        o, S = oracle.ssd_decode_step(q[t], k[t], v[t], alpha[t], S)
+        outs.append(o)
+    np.testing.assert_allclose(np.stack(outs, 2), of, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(S, Sf, rtol=1e-12, atol=1e-13)
+    o, S2 = oracle.ssd_decode_step(q[0], k[0], v[0], np.zeros((N, H)), S)
+    assert np.array_equal(S2, k[0][..., :, None] * v[0][..., None, :])
