@@ -1,17 +1,20 @@
 /*
  * linattn.h -- C ABI of the MI355X (gfx950) causal linear-attention library.
  *
- * Six operations, each a hand-written HIP path:
+ * Eight operations, each a hand-written HIP path:
  *   la_forward               chunked prefill of causal ELU+1 linear attention
  *   delta_forward            chunked prefill of the delta-rule fast-weight memory
  *   gated_delta_forward      the same with a per-token forgetting gate
+ *   ssd_forward              chunked prefill of the scalar-decay memory (Mamba-2 / SSD form)
  *   la_decode_step           one-token decode of ELU+1 linear attention on a resident state
  *   delta_decode_step        one-token decode of the delta rule on a resident state
  *   gated_delta_decode_step  the same with a forgetting gate
+ *   ssd_decode_step          one-token decode of the scalar-decay memory
  *
  * Pages the definitions come from:
  *   [LinearMem]  "AIGC 基本功｜线性、循环与记忆架构-LinearMem"
  *   [Recurrence] "手撕：递推与记忆模型"
+ *   [LA-SSM]     "线性注意力与 SSM:两条技术路线的完整推导"
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -171,6 +174,42 @@ la_status gated_delta_forward(const void* q, const void* k, const void* v, const
 la_status gated_delta_decode_step(const void* q, const void* k, const void* v, const void* beta,
                                   const float* alpha, float* S, void* o,
                                   int N, int H, int dk, int dv, int dtype, void* stream);
+
+/* Bytes of device workspace ssd_forward needs; 0 if the sizes are invalid. */
+size_t ssd_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
+
+/*
+ * Scalar-decay linear memory over a whole sequence (prefill): the Mamba-2 /
+ * SSD form of [LA-SSM] §3 (the outer-product state of linear attention with
+ * a scalar decay on the old state), written key-first:
+ *   S_t = alpha_t S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t   (write, then read),
+ * no feature map, no normaliser.  With dk = dv = 1 it is the selective scan
+ * of [Recurrence] "Selective scan" (a = alpha, b = k, x = v, c = q).
+ * alpha    [B][H][T] fp32 (whatever dtype is), each in (0, 1]; a factor
+ *          below e^-20 acts as e^-20 (an effective reset).
+ * S0       initial state, NULL = zero; 16-byte aligned.  S_out final state
+ *          (may alias S0), or NULL.
+ * Supported: dtype LA_BF16; dk, dv in {64, 128}; chunk 64.
+ * Errors: LA_ERR_INVALID_ARG (q, k, v, alpha or o NULL; sizes < 1; chunk < 1;
+ * dtype unknown; misaligned pointers), LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE,
+ * LA_ERR_HIP.
+ */
+la_status ssd_forward(const void* q, const void* k, const void* v, const float* alpha,
+                      const float* S0, void* o, float* S_out,
+                      int B, int H, int T, int dk, int dv, int dtype, int chunk,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step of the scalar-decay memory on a resident fp32 state,
+ * updated IN PLACE ([LA-SSM] §3; [LinearMem] §05 in-place inference update):
+ *   S <- alpha S + k v^T,   o = S^T q.
+ * q, k [N][H][dk]; v, o [N][H][dv] (dtype); alpha [N][H] fp32 (alpha = 0
+ * resets exactly); S [N][H][dk][dv] fp32, 16-byte aligned.
+ * Errors: LA_ERR_INVALID_ARG (a pointer NULL, sizes < 1, dtype unknown, S
+ * misaligned), LA_ERR_UNSUPPORTED (dk or dv not in {64, 128}), LA_ERR_HIP.
+ */
+la_status ssd_decode_step(const void* q, const void* k, const void* v, const float* alpha, float* S,
+                          void* o, int N, int H, int dk, int dv, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,7 @@ def _declared_functions():
 def test_header_declares_the_operations():
     fns = _declared_functions()
     for name in ("la_forward", "delta_forward", "la_decode_step", "delta_decode_step", "gated_delta_forward",
-                 "gated_delta_decode_step"):
+                 "gated_delta_decode_step", "ssd_forward", "ssd_decode_step"):
         assert name in fns
 
 
@@ -149,6 +149,41 @@ def test_gated_delta_decode_rejects(kw, status):
     assert lin.lib().la_last_error().decode().startswith("gated_delta_decode_step")
 
 
+def _ssd(**kw):
+    a = dict(q=P, k=P, v=P, alpha=P, S0=None, o=P, S_out=None, B=1, H=1, T=8, dk=64, dv=64, dtype=1, chunk=64,
+             ws=P, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lin.lib().ssd_forward(a["q"], a["k"], a["v"], a["alpha"], a["S0"], a["o"], a["S_out"], a["B"], a["H"],
+                                 a["T"], a["dk"], a["dv"], a["dtype"], a["chunk"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(alpha=None), "INVALID_ARG"), (dict(q=None), "INVALID_ARG"), (dict(H=0), "INVALID_ARG"),
+    (dict(alpha=ctypes.c_void_p(0x10002)), "INVALID_ARG"), (dict(S0=ctypes.c_void_p(0x10004)), "INVALID_ARG"),
+    (dict(dv=100), "UNSUPPORTED"), (dict(dtype=0), "UNSUPPORTED"), (dict(chunk=128), "UNSUPPORTED"),
+    (dict(ws=None), "WORKSPACE"), (dict(wsb=8), "WORKSPACE"),
+])
+def test_ssd_forward_rejects(kw, status):
+    assert _ssd(**kw) == ST[status]
+    assert lin.lib().la_last_error().decode().startswith("ssd_forward")
+
+
+def _ssd_dec(**kw):
+    a = dict(q=P, k=P, v=P, alpha=P, S=P, o=P, N=4, H=2, dk=128, dv=128, dtype=1, stream=None)
+    a.update(kw)
+    return lin.lib().ssd_decode_step(a["q"], a["k"], a["v"], a["alpha"], a["S"], a["o"], a["N"], a["H"], a["dk"],
+                                     a["dv"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(alpha=None), "INVALID_ARG"), (dict(S=None), "INVALID_ARG"), (dict(N=0), "INVALID_ARG"),
+    (dict(dtype=9), "INVALID_ARG"), (dict(dk=256), "UNSUPPORTED"), (dict(S=ctypes.c_void_p(0x10008)), "INVALID_ARG"),
+])
+def test_ssd_decode_rejects(kw, status):
+    assert _ssd_dec(**kw) == ST[status]
+    assert lin.lib().la_last_error().decode().startswith("ssd_decode_step")
+
+
 def test_workspace_queries():
     L = lin.lib()
     assert L.la_forward_workspace_bytes(0, 1, 8, 64, 64, 64) == 0
@@ -156,6 +191,8 @@ def test_workspace_queries():
     n = L.la_forward_workspace_bytes(4, 8, 8192, 64, 64, 64)
     assert n > 0 and n % 16 == 0
     assert L.delta_forward_workspace_bytes(2, 16, 16384, 128, 128, 64) > 0
+    assert L.ssd_forward_workspace_bytes(4, 8, 8192, 64, 64, 64) > 0
+    assert L.ssd_forward_workspace_bytes(4, 8, 8192, 64, 32, 64) == 0
 
 
 def test_status_strings():

@@ -7,8 +7,11 @@ Public API (same names as the C ABI in include/linattn.h):
     delta_decode_step(q, k, v, beta, S) -> o             (S updated in place)
     gated_delta_forward(q, k, v, beta, alpha, S0=None) -> (o, S_T)
     gated_delta_decode_step(q, k, v, beta, alpha, S) -> o (S updated in place)
+    ssd_forward(q, k, v, alpha, S0=None) -> (o, S_T)
+    ssd_decode_step(q, k, v, alpha, S) -> o               (S updated in place)
 """
 from .binding import (  # noqa: F401
     CHUNK, LA_BF16, LA_F32, LinAttnError, UnsupportedError, delta_forward,
     delta_decode_step, delta_forward_workspace_bytes, gated_delta_decode_step, gated_delta_forward,
-    la_decode_step, la_forward, la_forward_workspace_bytes, lib)
+    la_decode_step, la_forward, la_forward_workspace_bytes, lib, ssd_decode_step, ssd_forward,
+    ssd_forward_workspace_bytes)

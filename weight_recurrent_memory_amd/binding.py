@@ -63,6 +63,12 @@ def lib():
             L.gated_delta_forward.restype = i
             L.gated_delta_decode_step.argtypes = [vp, vp, vp, vp, fp, fp, vp, i, i, i, i, i, vp]
             L.gated_delta_decode_step.restype = i
+            L.ssd_forward_workspace_bytes.argtypes = [i, i, i, i, i, i]
+            L.ssd_forward_workspace_bytes.restype = sz
+            L.ssd_forward.argtypes = [vp, vp, vp, fp, fp, vp, fp, i, i, i, i, i, i, i, vp, sz, vp]
+            L.ssd_forward.restype = i
+            L.ssd_decode_step.argtypes = [vp, vp, vp, fp, fp, vp, i, i, i, i, i, vp]
+            L.ssd_decode_step.restype = i
             L.la_status_string.argtypes = [i]
             L.la_status_string.restype = ctypes.c_char_p
             L.la_last_error.argtypes = []
@@ -254,4 +260,54 @@ def _delta_decode(q, k, v, beta, alpha, S, o):
     else:
         _check(lib().gated_delta_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S), _ptr(o),
                                              N, H, dk, dv, code, _stream(dev)))
+    return o
+
+
+def ssd_forward_workspace_bytes(B, H, T, dk, dv, chunk=CHUNK) -> int:
+    return int(lib().ssd_forward_workspace_bytes(B, H, T, dk, dv, chunk))
+
+
+def ssd_forward(q, k, v, alpha, S0=None, chunk=CHUNK, *, o=None, S_out=None, workspace=None, return_state=True):
+    """Scalar-decay (Mamba-2 / SSD form) prefill: S_t = alpha_t S_{t-1} + k_t v_t^T,
+    o_t = S_t^T q_t.  q, k: [B,H,T,dk]; v: [B,H,T,dv] (bf16); alpha: [B,H,T]
+    fp32.  Returns (o, S_T)."""
+    code = _dtype_code(q)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(k, "k", q.dtype, (B, H, T, dk), dev)
+    _need(v, "v", q.dtype, (B, H, T, dv), dev)
+    _need(alpha, "alpha", torch.float32, (B, H, T), dev)
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (B, H, dk, dv), dev)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
+    _need(o, "o", q.dtype, (B, H, T, dv), dev)
+    if return_state:
+        if S_out is None:
+            S_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        _need(S_out, "S_out", torch.float32, (B, H, dk, dv), dev)
+    ws, wsb = _workspace(ssd_forward_workspace_bytes(B, H, T, dk, dv, chunk), dev, workspace)
+    _check(lib().ssd_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(S0), _ptr(o), _ptr(S_out), B, H, T, dk,
+                             dv, code, int(chunk), _ptr(ws), wsb, _stream(dev)))
+    return o, S_out
+
+
+def ssd_decode_step(q, k, v, alpha, S, *, o=None):
+    """One scalar-decay decode step; S [N,H,dk,dv] (fp32) is updated in place:
+    S <- alpha S + k v^T.  q, k: [N,H,dk]; v: [N,H,dv]; alpha: [N,H] fp32.
+    Returns o [N,H,dv] = S_new^T q."""
+    code = _dtype_code(q)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(k, "k", q.dtype, (N, H, dk), dev)
+    _need(v, "v", q.dtype, (N, H, dv), dev)
+    _need(alpha, "alpha", torch.float32, (N, H), dev)
+    _need(S, "S", torch.float32, (N, H, dk, dv), dev)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    _need(o, "o", q.dtype, (N, H, dv), dev)
+    _check(lib().ssd_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(S), _ptr(o), N, H, dk, dv, code,
+                                 _stream(dev)))
     return o

@@ -75,6 +75,11 @@ size_t la_ws_bytes(int B, int H, int T, int dk, int dv, int) {
     return sizeof(float) * la::la_ws_floats(B * H, T, dk, dv);
 }
 
+size_t ssd_ws_bytes(int B, int H, int T, int dk, int dv, int) {
+    const int HT = B * H;
+    return sizeof(float) * la::ssd_ws_floats(HT, dk, dv, la::la_plan(HT, T, dk, dv));
+}
+
 size_t delta_ws_bytes(int B, int H, int T, int dk, int dv, int chunk) {
     const int HT = B * H;
     const la::LaPlan p = plan_segments(HT, T, chunk, kDeltaTargetGroups);
@@ -136,6 +141,11 @@ size_t la_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk
 size_t delta_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {
     if (check_prefill("delta_forward_workspace_bytes", B, H, T, dk, dv, LA_BF16, chunk) != LA_OK) return 0;
     return delta_ws_bytes(B, H, T, dk, dv, chunk);
+}
+
+size_t ssd_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {
+    if (check_prefill("ssd_forward_workspace_bytes", B, H, T, dk, dv, LA_BF16, chunk) != LA_OK) return 0;
+    return ssd_ws_bytes(B, H, T, dk, dv, chunk);
 }
 
 la_status la_forward(const void* q, const void* k, const void* v, const float* S0, const float* z0,
@@ -260,6 +270,36 @@ la_status gated_delta_decode_step(const void* q, const void* k, const void* v, c
     if (!q || !k || !v || !beta || !alpha || !S || !o)
         return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, beta, alpha, S and o must be non-NULL", fn);
     return delta_decode_impl(fn, q, k, v, beta, alpha, S, o, N, H, dk, dv, dtype, stream);
+}
+
+la_status ssd_forward(const void* q, const void* k, const void* v, const float* alpha, const float* S0, void* o,
+                      float* S_out, int B, int H, int T, int dk, int dv, int dtype, int chunk, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    const char* fn = "ssd_forward";
+    if (!q || !k || !v || !alpha || !o)
+        return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, alpha and o must be non-NULL", fn);
+    la_status st = check_prefill(fn, B, H, T, dk, dv, dtype, chunk);
+    if (st != LA_OK) return st;
+    if (dtype != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "%s: only bf16 inputs are supported", fn);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(LA_ERR_INVALID_ARG, "%s: q, k, v and o must be 16-byte aligned", fn);
+    if ((reinterpret_cast<uintptr_t>(alpha) & 3u) || !aligned16(S0))
+        return fail(LA_ERR_INVALID_ARG, "%s: alpha must be 4-byte and S0 16-byte aligned", fn);
+    const size_t need = ssd_ws_bytes(B, H, T, dk, dv, chunk);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
+        return fail(LA_ERR_WORKSPACE, "%s: workspace of %zu bytes (16-byte aligned) required, got %zu", fn,
+                    need, workspace ? workspace_bytes : (size_t)0);
+    const la::LaPlan plan = la::la_plan(B * H, T, dk, dv);
+    return hip_status(fn, la::launch_ssd_forward(q, k, v, alpha, S0, o, S_out, B * H, T, dk, dv, dtype, plan,
+                                                 static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
+}
+
+la_status ssd_decode_step(const void* q, const void* k, const void* v, const float* alpha, float* S, void* o,
+                          int N, int H, int dk, int dv, int dtype, void* stream) {
+    const char* fn = "ssd_decode_step";
+    if (!q || !k || !v || !alpha || !S || !o)
+        return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, alpha, S and o must be non-NULL", fn);
+    return delta_decode_impl(fn, q, k, v, nullptr, alpha, S, o, N, H, dk, dv, dtype, stream);
 }
 
 }  // extern "C"

@@ -16,6 +16,9 @@
 // Gated form (LinearMem §03, the Gated DeltaNet rule): the old state is first
 // decayed by alpha, S~ = alpha S, and the step above runs on S~.  Here alpha
 // scales the two reductions and the state as it is written back.
+//
+// Scalar-decay form ("线性注意力与 SSM" §3, Mamba-2): S <- alpha S + k v^T,
+// o = S^T q = alpha S^T q + (k . q) v: no correction, so S^T k is not needed.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -25,7 +28,9 @@ namespace {
 
 constexpr int NTHR = 256;
 
-template <typename TIn, int DK, int DV, bool GATED>
+enum : int { kRuleDelta = 0, kRuleGatedDelta = 1, kRuleSsd = 2 };
+
+template <typename TIn, int DK, int DV, int RULE>
 __global__ __launch_bounds__(NTHR) void delta_decode_kernel(const TIn* __restrict__ q,
                                                             const TIn* __restrict__ k,
                                                             const TIn* __restrict__ v,
@@ -40,6 +45,7 @@ __global__ __launch_bounds__(NTHR) void delta_decode_kernel(const TIn* __restric
     __shared__ v4f part_k[R][CG], part_q[R][CG];
     __shared__ float kq_part[NTHR / 64];
 
+    constexpr bool GATED = RULE != kRuleDelta, SSD = RULE == kRuleSsd;
     const int tid = threadIdx.x;
     const int cg = tid % CG, rg = tid / CG;
     const long s = blockIdx.x;
@@ -62,7 +68,7 @@ __global__ __launch_bounds__(NTHR) void delta_decode_kernel(const TIn* __restric
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) kq += __shfl_xor(kq, off);
     if ((tid & 63) == 0) kq_part[tid >> 6] = kq;
-    const float b = Elem<TIn>::load(beta, s);
+    const float b = SSD ? 1.f : Elem<TIn>::load(beta, s);
     const float a = GATED ? alpha[s] : 1.f;
     const v4f vv = v4f{Elem<TIn>::load(v, s * DV + 4 * cg + 0), Elem<TIn>::load(v, s * DV + 4 * cg + 1),
                        Elem<TIn>::load(v, s * DV + 4 * cg + 2), Elem<TIn>::load(v, s * DV + 4 * cg + 3)};
@@ -73,10 +79,10 @@ __global__ __launch_bounds__(NTHR) void delta_decode_kernel(const TIn* __restric
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int row = rg + R * m;
-        pk += fk[row] * st[m];
+        if constexpr (!SSD) pk += fk[row] * st[m];
         pq += fq[row] * st[m];
     }
-    part_k[rg][cg] = pk;
+    if constexpr (!SSD) part_k[rg][cg] = pk;
     part_q[rg][cg] = pq;
     __syncthreads();
 
@@ -84,7 +90,7 @@ __global__ __launch_bounds__(NTHR) void delta_decode_kernel(const TIn* __restric
     v4f pred = zero4(), sq = zero4();
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        pred += part_k[r][cg];
+        if constexpr (!SSD) pred += part_k[r][cg];
         sq += part_q[r][cg];
     }
     if constexpr (GATED) {  // reductions over the decayed state
@@ -114,17 +120,24 @@ __global__ __launch_bounds__(NTHR) void delta_decode_kernel(const TIn* __restric
     }
 }
 
+template <typename TIn, int DK, int DV, int RULE>
+void launch_rule(const void* q, const void* k, const void* v, const void* beta, const float* alpha, float* S,
+                 void* o, int NH, hipStream_t stream) {
+    delta_decode_kernel<TIn, DK, DV, RULE><<<dim3(NH), dim3(NTHR), 0, stream>>>(
+        static_cast<const TIn*>(q), static_cast<const TIn*>(k), static_cast<const TIn*>(v),
+        static_cast<const TIn*>(beta), alpha, S, static_cast<TIn*>(o));
+}
+
+// beta NULL (with alpha) selects the scalar-decay rule; alpha NULL the plain delta rule.
 template <typename TIn, int DK, int DV>
 hipError_t launch_typed(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
                         float* S, void* o, int NH, hipStream_t stream) {
-    if (alpha)
-        delta_decode_kernel<TIn, DK, DV, true><<<dim3(NH), dim3(NTHR), 0, stream>>>(
-            static_cast<const TIn*>(q), static_cast<const TIn*>(k), static_cast<const TIn*>(v),
-            static_cast<const TIn*>(beta), alpha, S, static_cast<TIn*>(o));
+    if (!alpha)
+        launch_rule<TIn, DK, DV, kRuleDelta>(q, k, v, beta, nullptr, S, o, NH, stream);
+    else if (beta)
+        launch_rule<TIn, DK, DV, kRuleGatedDelta>(q, k, v, beta, alpha, S, o, NH, stream);
     else
-        delta_decode_kernel<TIn, DK, DV, false><<<dim3(NH), dim3(NTHR), 0, stream>>>(
-            static_cast<const TIn*>(q), static_cast<const TIn*>(k), static_cast<const TIn*>(v),
-            static_cast<const TIn*>(beta), nullptr, S, static_cast<TIn*>(o));
+        launch_rule<TIn, DK, DV, kRuleSsd>(q, k, v, nullptr, alpha, S, o, NH, stream);
     return hipGetLastError();
 }
 

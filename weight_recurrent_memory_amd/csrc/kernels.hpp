@@ -39,8 +39,16 @@ hipError_t launch_delta_forward(const void* q, const void* k, const void* v,
                                 hipStream_t stream);
 size_t delta_ws_floats(int HT, int dk, int dv, const LaPlan& plan);
 
+// Scalar-decay (Mamba-2 / SSD) prefill: segment maps -> elementwise
+// composition -> chunked outputs.  alpha fp32 [HT][T].  Segments as la_plan.
+hipError_t launch_ssd_forward(const void* q, const void* k, const void* v, const float* alpha,
+                              const float* S0, void* o, float* S_out, int HT, int T, int dk, int dv,
+                              int dtype, const LaPlan& plan, float* ws, hipStream_t stream);
+size_t ssd_ws_floats(int HT, int dk, int dv, const LaPlan& plan);
+
 // Delta-rule decode step on a resident fp32 state (in place); alpha (fp32
-// [NH]) selects the gated rule, NULL = ungated.
+// [NH]) selects the gated rule, NULL = ungated; beta NULL with alpha given
+// selects the scalar-decay rule (no correction).
 hipError_t launch_delta_decode(const void* q, const void* k, const void* v, const void* beta,
                                const float* alpha, float* S, void* o, int NH, int dk, int dv, int dtype,
                                hipStream_t stream);

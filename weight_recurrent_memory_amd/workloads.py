@@ -24,7 +24,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str        # "la", "delta", "decode", "delta_decode", "gated_delta", "gated_delta_decode"
+    kind: str        # "la", "delta", "gated_delta", "ssd", or one of those + "_decode" ("decode" = LA)
     B: int           # batch (decode: sequences N)
     H: int
     T: int           # tokens (decode: number of steps)
@@ -51,6 +51,10 @@ GATED_DELTA_BF16_PREFILL = Workload("gated_delta_bf16_b2_h16_t16384_d128", "gate
                                     torch.bfloat16, 7)
 GATED_DELTA_DECODE_BF16 = Workload("gated_delta_decode_bf16_n256_h32_d128_1000steps", "gated_delta_decode", 256,
                                    32, 1000, 128, 128, torch.bfloat16, 8)
+# The scalar-decay (Mamba-2 / SSD form) rule on the LA prefill configuration.
+SSD_BF16_PREFILL = Workload("ssd_bf16_b4_h8_t8192_d64", "ssd", 4, 8, 8192, 64, 64, torch.bfloat16, 9)
+SSD_DECODE_BF16 = Workload("ssd_decode_bf16_n256_h32_d128_1000steps", "ssd_decode", 256, 32, 1000, 128, 128,
+                           torch.bfloat16, 10)
 GATE_RATE = 1.0 / 16
 
 
@@ -139,6 +143,13 @@ def make(w: Workload, device="cpu"):
     if w.kind == "gated_delta":
         return delta_inputs(w.B, w.H, w.T, w.dk, w.dv, w.dtype, w.seed, device) + (
             gates((w.B, w.H, w.T), w.seed, device),)
+    if w.kind == "ssd":
+        return la_inputs(w.B, w.H, w.T, w.dk, w.dv, w.dtype, w.seed, device) + (
+            gates((w.B, w.H, w.T), w.seed, device),)
+    if w.kind == "ssd_decode":
+        S, _ = decode_state(w.B, w.H, w.dk, w.dv, w.seed, device, std=0.1)
+        return (S,) + decode_tokens(w.T, w.B, w.H, w.dk, w.dv, w.dtype, w.seed, device) + (
+            gates((w.T, w.B, w.H), w.seed, device),)
     if w.kind == "gated_delta_decode":
         S, _ = decode_state(w.B, w.H, w.dk, w.dv, w.seed, device, std=0.1)
         return (S,) + delta_decode_tokens(w.T, w.B, w.H, w.dk, w.dv, w.dtype, w.seed, device) + (
