@@ -12,9 +12,10 @@ The line printed is one JSON object:
   measured with HIP events on the launch stream;
 * cpu_baseline: the fp64 oracle (C, OpenMP over heads) timed on the host on
   the same workload;
-* extra: the other measured paths -- the long-stream LA workload, the delta
-  rule and gated delta rule prefills and the 1000-step decode chains of the
-  three rules (state-update GB/s) -- each with its own roofline fraction.
+* extra: the other measured paths -- the long-stream LA workload, the delta,
+  gated delta and scalar-decay (SSD) prefills and the 1000-step decode chains
+  of the four rules (state-update GB/s) -- each with its own roofline
+  fraction.
 
 Inputs are synthetic (seeded, generated on the device) and rotate among
 several copies so that each step reads data evicted from the 256 MB
@@ -86,6 +87,16 @@ def delta_flops(B, H, T, dk, dv, C=64):
     return B * H * T * ((C - 1) * dk + C * C // 3 + (C + 1) * (dk + 2 * dv) + 6 * dk * dv)
 
 
+def ssd_bytes(B, H, T, dk, dv, el):
+    # q, k, v and alpha (fp32) read once, o written once, the final state written
+    return B * H * T * (2 * dk + dv) * el + B * H * T * 4 + B * H * T * dv * el + B * H * dk * dv * 4
+
+
+def ssd_flops(B, H, T, dk, dv, C=64):
+    # per token-head: causal half of Q K^T and of P V, the state read and the update
+    return B * H * T * ((C + 1) * (dk + dv) + 4 * dk * dv)
+
+
 def decode_bytes(N, H, dk, dv, el):
     return N * H * (2 * dk * dv * 4 + 2 * dk * 4 + (2 * dk + dv) * el + dv * el)
 
@@ -93,6 +104,11 @@ def decode_bytes(N, H, dk, dv, el):
 def delta_decode_bytes(N, H, dk, dv, el, gated=False):
     # S read and written (fp32); q, k, v, beta read; o written; gated: alpha (fp32) read
     return N * H * (2 * dk * dv * 4 + (2 * dk + dv + 1) * el + dv * el + (4 if gated else 0))
+
+
+def ssd_decode_bytes(N, H, dk, dv, el):
+    # S read and written (fp32); q, k, v, alpha (fp32) read; o written
+    return N * H * (2 * dk * dv * 4 + (2 * dk + dv) * el + 4 + dv * el)
 
 
 def _events(n):
@@ -171,6 +187,43 @@ def bench_delta(w, steps, warmup, copies, lin, wl):
             "tflops": fl / (mean_ms * 1e-3) / 1e12}
 
 
+def bench_ssd(w, steps, warmup, copies, lin, wl):
+    dev = torch.device("cuda:0")
+    el = 2
+    sets = [wl.la_inputs(w.B, w.H, w.T, w.dk, w.dv, w.dtype, w.seed + 17 * i, dev)
+            + (wl.gates((w.B, w.H, w.T), w.seed + 17 * i, dev),) for i in range(copies)]
+    outs = [torch.empty((w.B, w.H, w.T, w.dv), dtype=w.dtype, device=dev) for _ in range(copies)]
+    S = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(lin.ssd_forward_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        q, k, v, alpha = sets[i % copies]
+        lin.ssd_forward(q, k, v, alpha, o=outs[i % copies], S_out=S, workspace=ws)
+
+    wall, mean_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
+    nbytes = ssd_bytes(w.B, w.H, w.T, w.dk, w.dv, el)
+    fl = ssd_flops(w.B, w.H, w.T, w.dk, w.dv)
+    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "tokens_per_s": w.B * w.T * steps / wall,
+            "bytes": nbytes, "flops": fl, "gbs": nbytes / (mean_ms * 1e-3) / 1e9,
+            "tflops": fl / (mean_ms * 1e-3) / 1e12}
+
+
+def bench_ssd_decode(w, lin, wl, n_steps=None):
+    dev = torch.device("cuda:0")
+    S, Q, K, V, At = wl.make(w, dev)
+    n = w.T if n_steps is None else n_steps
+    o = torch.empty((w.B, w.H, w.dv), dtype=w.dtype, device=dev)
+
+    def step(i):
+        j = i % w.T
+        lin.ssd_decode_step(Q[j], K[j], V[j], At[j], S, o=o)
+
+    wall, mean_ms = time_calls(step, n, 10, torch.cuda.current_stream(dev))
+    per = ssd_decode_bytes(w.B, w.H, w.dk, w.dv, 2)
+    return {"steps": n, "ms_per_step": 1e3 * wall / n, "event_ms_mean": mean_ms, "bytes_per_step": per,
+            "gbs_wall": per * n / wall / 1e9, "gbs": per / (mean_ms * 1e-3) / 1e9}
+
+
 def bench_decode(w, lin, wl, n_steps=None):
     dev = torch.device("cuda:0")
     S, z, Q, K, V = wl.make(w, dev)
@@ -243,8 +296,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=4, help="input copies rotated through (cache eviction)")
-    ap.add_argument("--only", choices=["all", "la", "la_long", "delta", "gated_delta", "decode", "delta_decode",
-                                       "gated_delta_decode"], default="all")
+    ap.add_argument("--only", choices=["all", "la", "la_long", "delta", "gated_delta", "ssd", "decode", "delta_decode",
+                                       "gated_delta_decode", "ssd_decode"], default="all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
@@ -285,6 +338,12 @@ def main():
                               "mfma_tflops": r["tflops"], "mfma_frac": r["tflops"] / BF16_MFMA_PEAK_TFS}
         except lin.LinAttnError as e:
             extra[wd.name] = {"error": str(e)}
+    if args.only in ("all", "ssd"):
+        ws_ = wl.SSD_BF16_PREFILL
+        r = bench_ssd(ws_, max(3, args.steps // 2), 3, args.copies, lin, wl)
+        extra[ws_.name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
+                           "hbm_gbs": r["gbs"], "hbm_frac": r["gbs"] / HBM_PEAK_GBS,
+                           "mfma_tflops": r["tflops"], "mfma_frac": r["tflops"] / BF16_MFMA_PEAK_TFS}
     if args.only in ("all", "decode"):
         wdec = wl.DECODE_BF16
         r = bench_decode(wdec, lin, wl)
@@ -297,6 +356,12 @@ def main():
             continue
         r = bench_delta_decode(wdd, lin, wl)
         extra[wdd.name] = {"state_update_gbs": r["gbs"], "hbm_frac": r["gbs"] / HBM_PEAK_GBS,
+                           "gbs_wall_incl_launch_gaps": r["gbs_wall"], "us_per_step": 1e3 * r["event_ms_mean"],
+                           "steps": r["steps"], "bytes_per_step": r["bytes_per_step"]}
+    if args.only in ("all", "ssd_decode"):
+        wsd = wl.SSD_DECODE_BF16
+        r = bench_ssd_decode(wsd, lin, wl)
+        extra[wsd.name] = {"state_update_gbs": r["gbs"], "hbm_frac": r["gbs"] / HBM_PEAK_GBS,
                            "gbs_wall_incl_launch_gaps": r["gbs_wall"], "us_per_step": 1e3 * r["event_ms_mean"],
                            "steps": r["steps"], "bytes_per_step": r["bytes_per_step"]}
 

@@ -177,21 +177,38 @@ __global__ __launch_bounds__(NTHR) void ssd_segment_kernel(const bf16_t* __restr
 }
 
 // S_in(0) = S0 (or 0); S_in(g+1) = 2^(l_g) S_in(g) + N_g.  Elementwise: thread
-// i of the grid owns four consecutive state elements of one head.
+// i of the grid owns four consecutive state elements of one head.  The
+// segments are taken in batches whose loads are all issued before the first
+// combine, so the serial chain costs one memory latency per batch.
 template <int E>
 __global__ __launch_bounds__(256) void ssd_compose_kernel(const float* __restrict__ map_n,
                                                           const float* __restrict__ map_l, const float* S0,
                                                           float* __restrict__ state_in, int HT, int G) {
+    constexpr int BATCH = 8;
     const long idx = (long)blockIdx.x * 256 + threadIdx.x;  // 4-float group
     if (idx >= (long)HT * (E / 4)) return;
     const int head = (int)(idx / (E / 4));
     const int e = (int)(idx % (E / 4)) * 4;
+    const float* nh = map_n + (long)head * G * E + e;
+    const float* lh = map_l + (long)head * G;
+    float* sh = state_in + (long)head * G * E + e;
     v4f s = S0 ? *reinterpret_cast<const v4f*>(S0 + (long)head * E + e) : zero4();
-    for (int gi = 0; gi < G; ++gi) {
-        *reinterpret_cast<v4f*>(state_in + ((long)head * G + gi) * E + e) = s;
-        if (gi + 1 < G)
-            s = exp2_hw(map_l[head * G + gi]) * s +
-                *reinterpret_cast<const v4f*>(map_n + ((long)head * G + gi) * E + e);
+    *reinterpret_cast<v4f*>(sh) = s;
+    for (int g0 = 0; g0 + 1 < G; g0 += BATCH) {
+        v4f n[BATCH];
+        float l[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u)
+            if (g0 + u + 1 < G) {
+                n[u] = *reinterpret_cast<const v4f*>(nh + (long)(g0 + u) * E);
+                l[u] = lh[g0 + u];
+            }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u)
+            if (g0 + u + 1 < G) {
+                s = exp2_hw(l[u]) * s + n[u];
+                *reinterpret_cast<v4f*>(sh + (long)(g0 + u + 1) * E) = s;
+            }
     }
 }
 
