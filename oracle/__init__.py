@@ -46,6 +46,15 @@ Functions and what pins them (the pins are in ``tests/test_oracle_pins.py``):
     the LinearMem decay read ([0, 0.8] at alpha = 0.8 on an identity state
     for an orthogonal key, §06), and the step chain equal to the sequence
     form.
+``delta_forward_ex`` / ``delta_decode_step_ex`` -- either delta rule with
+    the input transforms of a serving stack (LinearMem §05 and §08: q/k L2
+    normalisation and beta = sigmoid(logit) in the kernel) and the
+    Recurrence page's read-then-write prediction k_t^T S~_{t-1} as an extra
+    output.  Pinned by closed forms of the transforms (a 3-4-5 row, unit
+    norms, a zero row, sigmoid(0) = 1/2 and its symmetry), the LA-SSM
+    four-token delta example's predictions read off its printed states, the
+    exact recall of a basis key's stored value, pred + correction = v, and
+    the flags reducing to the plain functions on pre-transformed inputs.
 ``delta_decode_step`` -- one in-place delta-rule step.  Pinned by the LA-SSM
     page's 4-token delta example replayed one step at a time (every
     intermediate state and the final read of k_1), the bit-exact overwrite
@@ -111,6 +120,14 @@ def _load():
             lib.ssd_ref_forward.restype = None
             lib.ssd_ref_decode_step.argtypes = [dp, dp, dp, dp, dp, dp, i, i, i, i]
             lib.ssd_ref_decode_step.restype = None
+            lib.delta_ref_forward_ex.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, i, i, i, i, i]
+            lib.delta_ref_forward_ex.restype = None
+            lib.delta_ref_decode_step_ex.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i, i, i, i]
+            lib.delta_ref_decode_step_ex.restype = None
+            lib.oracle_l2_normalize_rows.argtypes = [dp, dp, ctypes.c_long, i]
+            lib.oracle_l2_normalize_rows.restype = None
+            lib.oracle_sigmoid.argtypes = [dp, dp, ctypes.c_long]
+            lib.oracle_sigmoid.restype = None
             lib.oracle_phi.argtypes = [dp, dp, ctypes.c_long]
             lib.oracle_phi.restype = None
             lib.oracle_num_threads.argtypes = []
@@ -269,3 +286,64 @@ def ssd_decode_step(q, k, v, alpha, S):
     o = np.empty((N, H, dv))
     _load().ssd_ref_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(S), _ptr(o), N, H, dk, dv)
     return o, S
+
+
+def l2_normalize_rows(x):
+    """x / ||x|| over the last axis (a zero row stays zero)."""
+    x = _f64(x)
+    y = np.empty_like(x)
+    _load().oracle_l2_normalize_rows(_ptr(x), _ptr(y), x.size // x.shape[-1], x.shape[-1])
+    return y
+
+
+def sigmoid(x):
+    x = _f64(x)
+    y = np.empty_like(x)
+    _load().oracle_sigmoid(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def _pre(q, k, beta, normalize_qk, beta_logits):
+    q, k, beta = map(_f64, (q, k, beta))
+    if normalize_qk:
+        q, k = l2_normalize_rows(q), l2_normalize_rows(k)
+    if beta_logits:
+        beta = sigmoid(beta)
+    return q, k, beta
+
+
+def delta_forward_ex(q, k, v, beta, alpha=None, S0=None, normalize_qk=False, beta_logits=False):
+    """The delta rule, gated when alpha is given, after the optional input
+    transforms; returns (o, S_T, pred) with pred the read-then-write
+    predictions [B,H,T,dv]."""
+    q, k, beta = _pre(q, k, beta, normalize_qk, beta_logits)
+    v, alpha, S0 = map(_f64, (v, alpha, S0))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and v.shape[:3] == (B, H, T) and beta.shape == (B, H, T)
+    if alpha is not None:
+        assert alpha.shape == (B, H, T)
+    if S0 is not None:
+        assert S0.shape == (B, H, dk, dv)
+    o = np.empty((B, H, T, dv))
+    S = np.empty((B, H, dk, dv))
+    pred = np.empty((B, H, T, dv))
+    _load().delta_ref_forward_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S0), _ptr(o), _ptr(S),
+                                 _ptr(pred), B, H, T, dk, dv)
+    return o, S, pred
+
+
+def delta_decode_step_ex(q, k, v, beta, S, alpha=None, normalize_qk=False, beta_logits=False):
+    """One delta step (gated when alpha is given) on a copy of S after the
+    optional input transforms; returns (o, S_new, pred)."""
+    q, k, beta = _pre(q, k, beta, normalize_qk, beta_logits)
+    v, alpha = map(_f64, (v, alpha))
+    S = _f64(S).copy()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and v.shape == (N, H, dv) and beta.shape == (N, H) and S.shape == (N, H, dk, dv)
+    o = np.empty((N, H, dv))
+    pred = np.empty((N, H, dv))
+    _load().delta_ref_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S), _ptr(o), _ptr(pred),
+                                     N, H, dk, dv)
+    return o, S, pred

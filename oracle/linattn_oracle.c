@@ -116,10 +116,14 @@ void la_ref_forward(const double* q, const double* k, const double* v,
  * part of the rule.  alpha == NULL means alpha_t = 1 (the plain delta rule).
  * The per-token read o_t = S_t^T q_t (after the write) is this oracle's
  * reading: the pages print no sequence of query reads for this rule.
+ * pred (optional, [B][H][T][dv]) receives the prediction decayed^T k_t made
+ * before each write: the "read" sequence of [Recurrence] "Delta-rule fast
+ * weight", which reads first and then writes with the error.
  */
 static void delta_gated_forward(const double* q, const double* k, const double* v,
                                 const double* beta, const double* alpha, const double* S0,
-                                double* o, double* S_out, int B, int H, int T, int dk, int dv) {
+                                double* o, double* S_out, double* pred_out,
+                                int B, int H, int T, int dk, int dv) {
     const long heads = (long)B * H;
 #pragma omp parallel for schedule(dynamic, 1)
     for (long h = 0; h < heads; ++h) {
@@ -142,6 +146,7 @@ static void delta_gated_forward(const double* q, const double* k, const double* 
                 double pred = 0.0;
                 for (int i = 0; i < dk; ++i) pred += kt[i] * S[(long)i * dv + j];
                 u[j] = vh[(long)t * dv + j] - pred;
+                if (pred_out) pred_out[(h * (long)T + t) * dv + j] = pred;
             }
             /* write: S += beta_t k_t u^T */
             for (int i = 0; i < dk; ++i) {
@@ -165,7 +170,7 @@ void delta_ref_forward(const double* q, const double* k, const double* v,
                        const double* beta, const double* S0,
                        double* o, double* S_out,
                        int B, int H, int T, int dk, int dv) {
-    delta_gated_forward(q, k, v, beta, NULL, S0, o, S_out, B, H, T, dk, dv);
+    delta_gated_forward(q, k, v, beta, NULL, S0, o, S_out, NULL, B, H, T, dk, dv);
 }
 
 /* The gated delta rule: alpha [B][H][T], the per-token forgetting factor. */
@@ -173,7 +178,15 @@ void gated_delta_ref_forward(const double* q, const double* k, const double* v,
                              const double* beta, const double* alpha, const double* S0,
                              double* o, double* S_out,
                              int B, int H, int T, int dk, int dv) {
-    delta_gated_forward(q, k, v, beta, alpha, S0, o, S_out, B, H, T, dk, dv);
+    delta_gated_forward(q, k, v, beta, alpha, S0, o, S_out, NULL, B, H, T, dk, dv);
+}
+
+/* Either rule (alpha NULL = ungated) with the optional prediction output. */
+void delta_ref_forward_ex(const double* q, const double* k, const double* v,
+                          const double* beta, const double* alpha, const double* S0,
+                          double* o, double* S_out, double* pred,
+                          int B, int H, int T, int dk, int dv) {
+    delta_gated_forward(q, k, v, beta, alpha, S0, o, S_out, pred, B, H, T, dk, dv);
 }
 
 /*
@@ -222,7 +235,7 @@ void la_ref_decode_step(const double* q, const double* k, const double* v,
  */
 static void delta_gated_decode_step(const double* q, const double* k, const double* v,
                                     const double* beta, const double* alpha, double* S, double* o,
-                                    int N, int H, int dk, int dv) {
+                                    double* pred_out, int N, int H, int dk, int dv) {
     const long states = (long)N * H;
 #pragma omp parallel for schedule(static)
     for (long s = 0; s < states; ++s) {
@@ -235,6 +248,7 @@ static void delta_gated_decode_step(const double* q, const double* k, const doub
         for (int j = 0; j < dv; ++j) {
             double pred = 0.0;
             for (int i = 0; i < dk; ++i) pred += ks[i] * Ss[(long)i * dv + j];
+            if (pred_out) pred_out[s * dv + j] = pred;
             const double u = vs[j] - pred;
             for (int i = 0; i < dk; ++i) Ss[(long)i * dv + j] += beta[s] * ks[i] * u;
         }
@@ -249,14 +263,42 @@ static void delta_gated_decode_step(const double* q, const double* k, const doub
 void delta_ref_decode_step(const double* q, const double* k, const double* v,
                            const double* beta, double* S, double* o,
                            int N, int H, int dk, int dv) {
-    delta_gated_decode_step(q, k, v, beta, NULL, S, o, N, H, dk, dv);
+    delta_gated_decode_step(q, k, v, beta, NULL, S, o, NULL, N, H, dk, dv);
 }
 
 /* The gated form of the step above: S is first scaled by alpha [N][H]. */
 void gated_delta_ref_decode_step(const double* q, const double* k, const double* v,
                                  const double* beta, const double* alpha, double* S, double* o,
                                  int N, int H, int dk, int dv) {
-    delta_gated_decode_step(q, k, v, beta, alpha, S, o, N, H, dk, dv);
+    delta_gated_decode_step(q, k, v, beta, alpha, S, o, NULL, N, H, dk, dv);
+}
+
+/* Either step (alpha NULL = ungated) with the optional prediction output [N][H][dv]. */
+void delta_ref_decode_step_ex(const double* q, const double* k, const double* v,
+                              const double* beta, const double* alpha, double* S, double* o,
+                              double* pred, int N, int H, int dk, int dv) {
+    delta_gated_decode_step(q, k, v, beta, alpha, S, o, pred, N, H, dk, dv);
+}
+
+/*
+ * Input transforms that a serving stack applies before the rule
+ * ([LinearMem] §05: FLA hands the q/k L2 normalisation and the beta
+ * transform to the kernel; §08: the model predicts a raw gate, and the
+ * kernel applies a sigmoid to it):
+ *   l2 rows:  y = x / ||x||_2 per row of d (a zero row stays zero);
+ *   sigmoid:  y = 1 / (1 + e^-x).
+ */
+void oracle_l2_normalize_rows(const double* x, double* y, long rows, int d) {
+    for (long r = 0; r < rows; ++r) {
+        double ss = 0.0;
+        for (int i = 0; i < d; ++i) ss += x[r * d + i] * x[r * d + i];
+        const double n = sqrt(ss);
+        for (int i = 0; i < d; ++i) y[r * d + i] = n > 0.0 ? x[r * d + i] / n : 0.0;
+    }
+}
+
+void oracle_sigmoid(const double* x, double* y, long n) {
+    for (long i = 0; i < n; ++i) y[i] = 1.0 / (1.0 + exp(-x[i]));
 }
 
 /*

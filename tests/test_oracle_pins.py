@@ -675,3 +675,78 @@ def test_ssd_decode_chain_equals_forward_and_zero_alpha_resets():
     np.testing.assert_allclose(S, Sf, rtol=1e-12, atol=1e-13)
     o, S2 = oracle.ssd_decode_step(q[0], k[0], v[0], np.zeros((N, H)), S)
     assert np.array_equal(S2, k[0][..., :, None] * v[0][..., None, :])
+
+
+# ------------------------------------------- input transforms and predictions
+
+def test_l2_normalize_rows_closed_forms():
+    y = oracle.l2_normalize_rows(np.array([[3.0, 4.0], [0.0, 0.0], [-5.0, 12.0]]))
+    np.testing.assert_allclose(y, [[0.6, 0.8], [0.0, 0.0], [-5 / 13, 12 / 13]], rtol=1e-15, atol=0)
+    x = np.random.default_rng(90).normal(size=(50, 17)) * np.arange(1, 51)[:, None]
+    y = oracle.l2_normalize_rows(x)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=1), 1.0, rtol=1e-14)
+    assert np.all(np.sign(y) == np.sign(x))
+
+
+def test_sigmoid_closed_forms():
+    x = np.array([0.0, math.log(3.0), -math.log(3.0), 40.0, -40.0])
+    y = oracle.sigmoid(x)
+    np.testing.assert_allclose(y[:3], [0.5, 0.75, 0.25], rtol=1e-15)
+    assert abs(y[3] - 1.0) < 1e-16 and 0.0 < y[4] < 1e-17
+    xs = np.random.default_rng(91).normal(size=100) * 5
+    np.testing.assert_allclose(oracle.sigmoid(xs) + oracle.sigmoid(-xs), 1.0, rtol=1e-15)
+    assert np.all(np.diff(oracle.sigmoid(np.sort(xs))) >= 0)
+
+
+def test_delta_predictions_printed_lassm():
+    # LA-SSM §1.3: before each write the walk-through prints the prediction
+    # S_{t-1} k_t and the correction u_t (beta = 1, four tokens).
+    g = _golden("lassm_four_token_example.json")
+    keys, values = np.array(g["keys"]), np.array(g["values"])
+    o, S, pred = oracle.delta_forward_ex(_h(keys), _h(keys), _h(values), np.ones((1, 1, 4)))
+    np.testing.assert_allclose(pred[0, 0], g["delta_predictions"], atol=1e-14)
+    np.testing.assert_allclose(values - pred[0, 0], g["delta_corrections"], atol=1e-14)
+    # the same through the step form
+    St = np.zeros((1, 1, 2, 2))
+    for t in range(4):
+        _, St, p = oracle.delta_decode_step_ex(keys[t][None, None], keys[t][None, None], values[t][None, None],
+                                               np.ones((1, 1)), St)
+        np.testing.assert_allclose(p[0, 0], g["delta_predictions"][t], atol=1e-14)
+
+
+def test_delta_prediction_recalls_a_basis_key_exactly():
+    # A basis key written with beta = 1 stores its value exactly; writing the
+    # same key later first predicts that value, bit for bit.
+    rng = np.random.default_rng(92)
+    dk, dv = 6, 4
+    keys = np.eye(dk)[[2, 4, 2]]
+    values = rng.integers(-64, 64, size=(3, dv)) / 8.0
+    _, _, pred = oracle.delta_forward_ex(_h(keys), _h(keys), _h(values), np.ones((1, 1, 3)))
+    assert np.array_equal(pred[0, 0, 2], values[0])
+    assert np.array_equal(pred[0, 0, 1], np.zeros(dv))
+
+
+def test_gated_prediction_reads_the_decayed_state():
+    # LinearMem gate setup: identity state, alpha = 0.8, key (1, 0): the
+    # prediction is taken from the decayed state, 0.8 k^T I = [0.8, 0].
+    g = _golden("linearmem_memory_experiment.json")
+    k = np.array(g["key"])[None, None, None]
+    v = np.array(g["values"][1])[None, None, None]
+    _, _, pred = oracle.delta_forward_ex(k, k, v, np.ones((1, 1, 1)), alpha=np.full((1, 1, 1), 0.8),
+                                         S0=np.eye(2)[None, None])
+    np.testing.assert_allclose(pred[0, 0, 0], [0.8, 0.0], rtol=1e-15)
+
+
+def test_transform_flags_reduce_to_the_plain_rule():
+    rng = np.random.default_rng(93)
+    B, H, T, dk, dv = 1, 2, 20, 5, 3
+    q, k, v = rng.normal(size=(B, H, T, dk)) * 3, rng.normal(size=(B, H, T, dk)) * 2, rng.normal(size=(B, H, T, dv))
+    logits = rng.normal(size=(B, H, T))
+    alpha = rng.uniform(0.5, 1.0, size=(B, H, T))
+    o, S, pred = oracle.delta_forward_ex(q, k, v, logits, alpha=alpha, normalize_qk=True, beta_logits=True)
+    qn, kn = oracle.l2_normalize_rows(q), oracle.l2_normalize_rows(k)
+    o2, S2 = oracle.gated_delta_forward(qn, kn, v, oracle.sigmoid(logits), alpha)
+    assert np.array_equal(o, o2) and np.array_equal(S, S2)
+    # from a zero state the first prediction is zero
+    _, _, p3 = oracle.delta_forward_ex(qn[:, :, :1], kn[:, :, :1], v[:, :, :1], np.ones((B, H, 1)))
+    assert np.array_equal(p3, np.zeros_like(p3))
