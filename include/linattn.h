@@ -10,6 +10,9 @@
  *   delta_decode_step        one-token decode of the delta rule on a resident state
  *   gated_delta_decode_step  the same with a forgetting gate
  *   ssd_decode_step          one-token decode of the scalar-decay memory
+ * and two delta-rule calls with serving options (input transforms, the
+ * read-then-write prediction as an extra output): delta_forward_ex,
+ * delta_decode_step_ex.
  *
  * Pages the definitions come from:
  *   [LinearMem]  "AIGC 基本功｜线性、循环与记忆架构-LinearMem"
@@ -52,6 +55,17 @@ extern "C" {
 #endif
 
 typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+/*
+ * Input transforms of the delta-rule *_ex calls (bit flags).  [LinearMem]
+ * §05: FLA hands the q/k L2 normalisation and the gate and beta transforms
+ * to the kernel; §08: production models predict a raw gate that a
+ * non-linearity in the kernel turns into the step size.
+ *   LA_NORMALIZE_QK  each q_t and k_t is scaled to unit L2 norm before use
+ *                    (a zero vector stays zero);
+ *   LA_BETA_SIGMOID  beta holds logits; the rule uses sigmoid(beta).
+ */
+enum { LA_NORMALIZE_QK = 1, LA_BETA_SIGMOID = 2 };
 
 typedef enum {
     LA_OK = 0,
@@ -144,6 +158,31 @@ const char* la_last_error(void);
  */
 la_status delta_decode_step(const void* q, const void* k, const void* v, const void* beta, float* S,
                             void* o, int N, int H, int dk, int dv, int dtype, void* stream);
+
+/*
+ * delta_forward / gated_delta_forward with serving options: alpha NULL is the
+ * plain delta rule, non-NULL the gated rule (fp32 [B][H][T]); `flags` selects
+ * the input transforms above; `pred` (optional, [B][H][T][dv], dtype)
+ * receives the prediction made before each write,
+ *   pred_t = (alpha_t S_{t-1})^T k_t = v_t - u_t,
+ * the read-then-write sequence of [Recurrence] "Delta-rule fast weight"
+ * (whose reference loop returns these reads).  Errors: as delta_forward, plus
+ * LA_ERR_INVALID_ARG for unknown flags or a misaligned pred.
+ */
+la_status delta_forward_ex(const void* q, const void* k, const void* v, const void* beta,
+                           const float* alpha, const float* S0, void* o, float* S_out,
+                           void* pred, int flags,
+                           int B, int H, int T, int dk, int dv, int dtype, int chunk,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * delta_decode_step / gated_delta_decode_step with the same options: alpha
+ * NULL = plain rule, else fp32 [N][H]; flags as above; pred (optional,
+ * [N][H][dv], dtype) = (alpha S)^T k, the prediction before the write.
+ */
+la_status delta_decode_step_ex(const void* q, const void* k, const void* v, const void* beta,
+                               const float* alpha, float* S, void* o, void* pred, int flags,
+                               int N, int H, int dk, int dv, int dtype, void* stream);
 
 /*
  * The gated delta rule over a whole sequence (prefill).  [LinearMem] §03:

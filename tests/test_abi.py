@@ -27,7 +27,8 @@ def _declared_functions():
 def test_header_declares_the_operations():
     fns = _declared_functions()
     for name in ("la_forward", "delta_forward", "la_decode_step", "delta_decode_step", "gated_delta_forward",
-                 "gated_delta_decode_step", "ssd_forward", "ssd_decode_step"):
+                 "gated_delta_decode_step", "ssd_forward", "ssd_decode_step", "delta_forward_ex",
+                 "delta_decode_step_ex"):
         assert name in fns
 
 
@@ -182,6 +183,42 @@ def _ssd_dec(**kw):
 def test_ssd_decode_rejects(kw, status):
     assert _ssd_dec(**kw) == ST[status]
     assert lin.lib().la_last_error().decode().startswith("ssd_decode_step")
+
+
+def _dex(**kw):
+    a = dict(q=P, k=P, v=P, beta=P, alpha=None, S0=None, o=P, S_out=None, pred=None, flags=3, B=1, H=1, T=8, dk=128,
+             dv=128, dtype=1, chunk=64, ws=P, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lin.lib().delta_forward_ex(a["q"], a["k"], a["v"], a["beta"], a["alpha"], a["S0"], a["o"], a["S_out"],
+                                      a["pred"], a["flags"], a["B"], a["H"], a["T"], a["dk"], a["dv"], a["dtype"],
+                                      a["chunk"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=4), "INVALID_ARG"), (dict(flags=-1), "INVALID_ARG"), (dict(beta=None), "INVALID_ARG"),
+    (dict(pred=ctypes.c_void_p(0x10001)), "INVALID_ARG"), (dict(T=0), "INVALID_ARG"), (dict(dk=32), "UNSUPPORTED"),
+    (dict(dtype=0), "UNSUPPORTED"), (dict(ws=None), "WORKSPACE"),
+])
+def test_delta_forward_ex_rejects(kw, status):
+    assert _dex(**kw) == ST[status]
+    assert lin.lib().la_last_error().decode().startswith("delta_forward_ex")
+
+
+def _ddex(**kw):
+    a = dict(q=P, k=P, v=P, beta=P, alpha=None, S=P, o=P, pred=None, flags=1, N=4, H=2, dk=128, dv=128, dtype=1,
+             stream=None)
+    a.update(kw)
+    return lin.lib().delta_decode_step_ex(a["q"], a["k"], a["v"], a["beta"], a["alpha"], a["S"], a["o"], a["pred"],
+                                          a["flags"], a["N"], a["H"], a["dk"], a["dv"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=8), "INVALID_ARG"), (dict(beta=None), "INVALID_ARG"), (dict(S=None), "INVALID_ARG"),
+    (dict(N=0), "INVALID_ARG"), (dict(dv=48), "UNSUPPORTED"),
+])
+def test_delta_decode_step_ex_rejects(kw, status):
+    assert _ddex(**kw) == ST[status]
+    assert lin.lib().la_last_error().decode().startswith("delta_decode_step_ex")
 
 
 def test_workspace_queries():

@@ -1,0 +1,113 @@
+"""GPU parity tests of the delta-rule calls with serving options (through the
+C ABI): in-kernel q/k L2 normalisation, beta = sigmoid(logit), and the
+read-then-write predictions as an extra output."""
+import pytest
+import torch
+
+import oracle
+from tests.parity import TOL, assert_parity, to64
+from weight_recurrent_memory_amd import binding as lin
+from weight_recurrent_memory_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _raw_inputs(B, H, T, dk, dv, seed):
+    """q, k N(0, 1) scaled by 3 and 2 (not normalised), v N(0, 1), beta logits N(0, 1)."""
+    q, k, v = wl.la_inputs(B, H, T, dk, dv, torch.float32, seed=seed, device=DEV)
+    logits = wl.la_inputs(B, H, T, 1, 1, torch.float32, seed=seed + 1, device=DEV)[0][..., 0]
+    bf = lambda x: x.to(torch.bfloat16)
+    return bf(3 * q), bf(2 * k), bf(v), bf(logits)
+
+
+CASES = [
+    # B, H, T, dk, dv, gated, normalize, logits, init
+    (1, 1, 1, 128, 128, False, True, True, True),
+    (1, 2, 63, 64, 64, True, True, False, False),
+    (2, 1, 65, 128, 64, False, False, True, True),
+    (1, 2, 300, 64, 128, True, True, True, True),
+    (1, 1, 1000, 128, 128, False, False, False, False),
+    (1, 3, 2100, 128, 128, True, True, True, True),
+]
+
+
+@pytest.mark.parametrize("B,H,T,dk,dv,gated,norm,logits,init", CASES)
+def test_delta_forward_ex_parity(B, H, T, dk, dv, gated, norm, logits, init):
+    print(f"delta_forward_ex B={B} H={H} T={T} dk={dk} dv={dv} gated={gated} norm={norm} logits={logits}",
+          flush=True)
+    q, k, v, b = _raw_inputs(B, H, T, dk, dv, seed=5000 + T)
+    if not logits:
+        b = torch.sigmoid(b.float()).to(torch.bfloat16)
+    if not norm:
+        q, k = wl.unit_rows(q.float()).to(torch.bfloat16), wl.unit_rows(k.float()).to(torch.bfloat16)
+    alpha = wl.gates((B, H, T), seed=T, device=DEV, rate=1 / 4) if gated else None
+    S0 = wl.decode_state(B, H, dk, dv, seed=81, device=DEV, std=0.5)[0] if init else None
+    o, S, pred = lin.delta_forward_ex(q, k, v, b, alpha, S0, normalize_qk=norm, beta_logits=logits, return_pred=True)
+    torch.cuda.synchronize()
+    ro, rS, rp = oracle.delta_forward_ex(q, k, v, b, alpha, S0, normalize_qk=norm, beta_logits=logits)
+    tol = TOL[torch.bfloat16]
+    assert_parity(o, ro, tol, "o")
+    assert_parity(S, rS, tol, "S_T")
+    assert_parity(pred, rp, tol, "pred")
+
+
+def test_delta_forward_ex_without_options_is_delta_forward_bitwise():
+    q, k, v, beta = wl.delta_inputs(1, 4, 2500, 128, 128, torch.bfloat16, seed=51, device=DEV)
+    S0, _ = wl.decode_state(1, 4, 128, 128, seed=52, device=DEV, std=0.3)
+    alpha = wl.gates((1, 4, 2500), seed=53, device=DEV)
+    o1, S1, _ = lin.delta_forward_ex(q, k, v, beta, None, S0, return_pred=True)
+    o2, S2 = lin.delta_forward(q, k, v, beta, S0)
+    o3, S3, _ = lin.delta_forward_ex(q, k, v, beta, alpha, S0, return_pred=True)
+    o4, S4 = lin.gated_delta_forward(q, k, v, beta, alpha, S0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    assert torch.equal(o3, o4) and torch.equal(S3, S4)
+
+
+def test_delta_forward_ex_config_sampled_heads():
+    w = wl.DELTA_BF16_PREFILL
+    print(f"delta_forward_ex on {w.name} with raw q/k and beta logits", flush=True)
+    q, k, v, b = _raw_inputs(w.B, w.H, w.T, w.dk, w.dv, seed=54)
+    o, S, pred = lin.delta_forward_ex(q, k, v, b, normalize_qk=True, beta_logits=True, return_pred=True)
+    torch.cuda.synchronize()
+    heads = [0, 31]
+    flat = lambda t: t.reshape(w.B * w.H, *t.shape[2:])[heads][None]
+    ro, rS, rp = oracle.delta_forward_ex(flat(q), flat(k), flat(v), flat(b), normalize_qk=True, beta_logits=True)
+    tol = TOL[torch.bfloat16]
+    assert_parity(flat(o), ro, tol, "o")
+    assert_parity(flat(S), rS, tol, "S_T")
+    assert_parity(flat(pred), rp, tol, "pred")
+
+
+@pytest.mark.parametrize("N,H,dk,dv,dtype,gated,norm,logits", [
+    (2, 3, 64, 64, torch.bfloat16, False, True, True), (3, 2, 128, 128, torch.bfloat16, True, True, False),
+    (4, 1, 64, 128, torch.float32, True, False, True), (2, 2, 128, 64, torch.float32, False, True, True)])
+def test_delta_decode_step_ex_parity(N, H, dk, dv, dtype, gated, norm, logits):
+    print(f"delta_decode_step_ex N={N} H={H} dk={dk} dv={dv} {dtype} gated={gated} norm={norm} logits={logits}",
+          flush=True)
+    S, _ = wl.decode_state(N, H, dk, dv, seed=34, device=DEV, std=0.3)
+    q, k, v = (t[0] for t in wl.decode_tokens(1, N, H, dk, dv, dtype, seed=35, device=DEV))
+    b = wl.decode_tokens(1, N, H, 1, 1, dtype, seed=36, device=DEV)[0][0][..., 0]
+    if not logits:
+        b = torch.sigmoid(b.float()).to(dtype)
+    alpha = wl.gates((N, H), seed=37, device=DEV, rate=1 / 2) if gated else None
+    S_ref = to64(S)
+    o, pred = lin.delta_decode_step_ex(q, k, v, b, S, alpha, normalize_qk=norm, beta_logits=logits,
+                                       return_pred=True)
+    torch.cuda.synchronize()
+    ro, rS, rp = oracle.delta_decode_step_ex(q, k, v, b, S_ref, alpha, normalize_qk=norm, beta_logits=logits)
+    assert_parity(o, ro, TOL[dtype], "o")
+    assert_parity(pred, rp, TOL[dtype], "pred")
+    assert_parity(S, rS, 1e-5, "S")
+
+
+def test_delta_decode_step_ex_without_options_is_bitwise_equal():
+    N, H, d = 3, 4, 128
+    S, _ = wl.decode_state(N, H, d, d, seed=38, device=DEV, std=0.3)
+    q, k, v, beta = (t[0] for t in wl.delta_decode_tokens(1, N, H, d, d, torch.bfloat16, seed=39, device=DEV))
+    S2 = S.clone()
+    o1, p1 = lin.delta_decode_step_ex(q, k, v, beta, S, return_pred=True)
+    o2 = lin.delta_decode_step(q, k, v, beta, S2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S, S2)

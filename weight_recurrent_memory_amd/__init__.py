@@ -9,9 +9,12 @@ Public API (same names as the C ABI in include/linattn.h):
     gated_delta_decode_step(q, k, v, beta, alpha, S) -> o (S updated in place)
     ssd_forward(q, k, v, alpha, S0=None) -> (o, S_T)
     ssd_decode_step(q, k, v, alpha, S) -> o               (S updated in place)
+    delta_forward_ex / delta_decode_step_ex: the delta rules with in-kernel q/k
+        L2 normalisation, beta = sigmoid(logit) and the read-then-write predictions
 """
 from .binding import (  # noqa: F401
-    CHUNK, LA_BF16, LA_F32, LinAttnError, UnsupportedError, delta_forward,
+    CHUNK, LA_BETA_SIGMOID, LA_BF16, LA_F32, LA_NORMALIZE_QK, LinAttnError, UnsupportedError, delta_decode_step_ex,
+    delta_forward, delta_forward_ex,
     delta_decode_step, delta_forward_workspace_bytes, gated_delta_decode_step, gated_delta_forward,
     la_decode_step, la_forward, la_forward_workspace_bytes, lib, ssd_decode_step, ssd_forward,
     ssd_forward_workspace_bytes)

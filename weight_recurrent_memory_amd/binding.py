@@ -18,6 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblinattn.so")
 
 LA_F32, LA_BF16 = 0, 1
+LA_NORMALIZE_QK, LA_BETA_SIGMOID = 1, 2
 LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = range(5)
 CHUNK = 64
 
@@ -69,6 +70,10 @@ def lib():
             L.ssd_forward.restype = i
             L.ssd_decode_step.argtypes = [vp, vp, vp, fp, fp, vp, i, i, i, i, i, vp]
             L.ssd_decode_step.restype = i
+            L.delta_forward_ex.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]
+            L.delta_forward_ex.restype = i
+            L.delta_decode_step_ex.argtypes = [vp, vp, vp, vp, fp, fp, vp, vp, i, i, i, i, i, i, vp]
+            L.delta_decode_step_ex.restype = i
             L.la_status_string.argtypes = [i]
             L.la_status_string.restype = ctypes.c_char_p
             L.la_last_error.argtypes = []
@@ -311,3 +316,72 @@ def ssd_decode_step(q, k, v, alpha, S, *, o=None):
     _check(lib().ssd_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(S), _ptr(o), N, H, dk, dv, code,
                                  _stream(dev)))
     return o
+
+
+def _flags(normalize_qk, beta_logits):
+    return (LA_NORMALIZE_QK if normalize_qk else 0) | (LA_BETA_SIGMOID if beta_logits else 0)
+
+
+def delta_forward_ex(q, k, v, beta, alpha=None, S0=None, chunk=CHUNK, *, normalize_qk=False, beta_logits=False,
+                     return_pred=False, o=None, S_out=None, pred=None, workspace=None):
+    """Delta-rule prefill with serving options: gated when alpha ([B,H,T]
+    fp32) is given; q/k L2-normalised in the kernel with normalize_qk; beta
+    read as logits with beta_logits; with return_pred the read-then-write
+    predictions [B,H,T,dv] are returned too.  Returns (o, S_T[, pred])."""
+    code = _dtype_code(q)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(k, "k", q.dtype, (B, H, T, dk), dev)
+    _need(v, "v", q.dtype, (B, H, T, dv), dev)
+    _need(beta, "beta", q.dtype, (B, H, T), dev)
+    if alpha is not None:
+        _need(alpha, "alpha", torch.float32, (B, H, T), dev)
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (B, H, dk, dv), dev)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
+    _need(o, "o", q.dtype, (B, H, T, dv), dev)
+    if S_out is None:
+        S_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _need(S_out, "S_out", torch.float32, (B, H, dk, dv), dev)
+    if return_pred:
+        if pred is None:
+            pred = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
+        _need(pred, "pred", q.dtype, (B, H, T, dv), dev)
+    else:
+        pred = None
+    ws, wsb = _workspace(delta_forward_workspace_bytes(B, H, T, dk, dv, chunk), dev, workspace)
+    _check(lib().delta_forward_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S0), _ptr(o),
+                                  _ptr(S_out), _ptr(pred), _flags(normalize_qk, beta_logits), B, H, T, dk, dv, code,
+                                  int(chunk), _ptr(ws), wsb, _stream(dev)))
+    return (o, S_out, pred) if return_pred else (o, S_out)
+
+
+def delta_decode_step_ex(q, k, v, beta, S, alpha=None, *, normalize_qk=False, beta_logits=False,
+                         return_pred=False, o=None, pred=None):
+    """One delta-rule decode step with serving options (see delta_forward_ex);
+    S is updated in place.  Returns o, or (o, pred) with return_pred."""
+    code = _dtype_code(q)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(k, "k", q.dtype, (N, H, dk), dev)
+    _need(v, "v", q.dtype, (N, H, dv), dev)
+    _need(beta, "beta", q.dtype, (N, H), dev)
+    _need(S, "S", torch.float32, (N, H, dk, dv), dev)
+    if alpha is not None:
+        _need(alpha, "alpha", torch.float32, (N, H), dev)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    _need(o, "o", q.dtype, (N, H, dv), dev)
+    if return_pred:
+        if pred is None:
+            pred = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+        _need(pred, "pred", q.dtype, (N, H, dv), dev)
+    else:
+        pred = None
+    _check(lib().delta_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S), _ptr(o),
+                                      _ptr(pred), _flags(normalize_qk, beta_logits), N, H, dk, dv, code,
+                                      _stream(dev)))
+    return (o, pred) if return_pred else o

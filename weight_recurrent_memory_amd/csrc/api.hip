@@ -177,31 +177,38 @@ la_status la_forward(const void* q, const void* k, const void* v, const float* S
 
 namespace {
 
-// delta_forward and gated_delta_forward: alpha NULL selects the ungated rule.
+constexpr int kKnownFlags = LA_NORMALIZE_QK | LA_BETA_SIGMOID;
+static_assert(LA_NORMALIZE_QK == la::kNormQK && LA_BETA_SIGMOID == la::kBetaSigmoid, "flag values");
+
+// The delta-rule prefills: alpha NULL selects the ungated rule.
 la_status delta_forward_impl(const char* fn, const void* q, const void* k, const void* v, const void* beta,
-                             const float* alpha, const float* S0, void* o, float* S_out, int B, int H, int T,
-                             int dk, int dv, int dtype, int chunk, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+                             const float* alpha, const float* S0, void* o, float* S_out, void* pred, int flags,
+                             int B, int H, int T, int dk, int dv, int dtype, int chunk, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    if (flags & ~kKnownFlags) return fail(LA_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, flags);
     la_status st = check_prefill(fn, B, H, T, dk, dv, dtype, chunk);
     if (st != LA_OK) return st;
     if (dtype != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "%s: only bf16 inputs are supported", fn);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return fail(LA_ERR_INVALID_ARG, "%s: q, k, v and o must be 16-byte aligned", fn);
-    if ((reinterpret_cast<uintptr_t>(beta) & 1u) || (reinterpret_cast<uintptr_t>(alpha) & 3u))
-        return fail(LA_ERR_INVALID_ARG, "%s: beta and alpha must be aligned to their element size", fn);
+    if ((reinterpret_cast<uintptr_t>(beta) & 1u) || (reinterpret_cast<uintptr_t>(alpha) & 3u) ||
+        (reinterpret_cast<uintptr_t>(pred) & 1u))
+        return fail(LA_ERR_INVALID_ARG, "%s: beta, alpha and pred must be aligned to their element size", fn);
     const size_t need = delta_ws_bytes(B, H, T, dk, dv, chunk);
     if (!workspace || workspace_bytes < need || !aligned16(workspace))
         return fail(LA_ERR_WORKSPACE, "%s: workspace of %zu bytes (16-byte aligned) required, got %zu", fn,
                     need, workspace ? workspace_bytes : (size_t)0);
     const la::LaPlan plan = plan_segments(B * H, T, chunk, kDeltaTargetGroups);
-    return hip_status(fn, la::launch_delta_forward(q, k, v, beta, alpha, S0, o, S_out, B * H, T, dk, dv, dtype,
-                                                   plan, static_cast<float*>(workspace),
+    return hip_status(fn, la::launch_delta_forward(q, k, v, beta, alpha, S0, o, S_out, pred, flags, B * H, T, dk,
+                                                   dv, dtype, plan, static_cast<float*>(workspace),
                                                    static_cast<hipStream_t>(stream)));
 }
 
+// The decode steps of the three rules: alpha NULL = delta, beta NULL = scalar decay.
 la_status delta_decode_impl(const char* fn, const void* q, const void* k, const void* v, const void* beta,
-                            const float* alpha, float* S, void* o, int N, int H, int dk, int dv, int dtype,
-                            void* stream) {
+                            const float* alpha, float* S, void* o, void* pred, int flags, int N, int H, int dk,
+                            int dv, int dtype, void* stream) {
+    if (flags & ~kKnownFlags) return fail(LA_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, flags);
     if (N < 1 || H < 1 || dk < 1 || dv < 1)
         return fail(LA_ERR_INVALID_ARG, "%s: sizes must be >= 1 (N=%d H=%d dk=%d dv=%d)", fn, N, H, dk, dv);
     if (dtype != LA_F32 && dtype != LA_BF16) return fail(LA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
@@ -209,7 +216,7 @@ la_status delta_decode_impl(const char* fn, const void* q, const void* k, const 
         return fail(LA_ERR_UNSUPPORTED, "%s: dk=%d dv=%d not in {64, 128}", fn, dk, dv);
     if ((long)N * H > 0x7fffffffL) return fail(LA_ERR_UNSUPPORTED, "%s: N*H exceeds 2^31-1", fn);
     if (!aligned16(S)) return fail(LA_ERR_INVALID_ARG, "%s: S must be 16-byte aligned", fn);
-    return hip_status(fn, la::launch_delta_decode(q, k, v, beta, alpha, S, o, N * H, dk, dv, dtype,
+    return hip_status(fn, la::launch_delta_decode(q, k, v, beta, alpha, S, o, pred, flags, N * H, dk, dv, dtype,
                                                   static_cast<hipStream_t>(stream)));
 }
 
@@ -223,8 +230,8 @@ la_status delta_forward(const void* q, const void* k, const void* v, const void*
     const char* fn = "delta_forward";
     if (!q || !k || !v || !beta || !o)
         return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, beta and o must be non-NULL", fn);
-    return delta_forward_impl(fn, q, k, v, beta, nullptr, S0, o, S_out, B, H, T, dk, dv, dtype, chunk, workspace,
-                              workspace_bytes, stream);
+    return delta_forward_impl(fn, q, k, v, beta, nullptr, S0, o, S_out, nullptr, 0, B, H, T, dk, dv, dtype, chunk,
+                              workspace, workspace_bytes, stream);
 }
 
 la_status gated_delta_forward(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
@@ -233,8 +240,18 @@ la_status gated_delta_forward(const void* q, const void* k, const void* v, const
     const char* fn = "gated_delta_forward";
     if (!q || !k || !v || !beta || !alpha || !o)
         return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, beta, alpha and o must be non-NULL", fn);
-    return delta_forward_impl(fn, q, k, v, beta, alpha, S0, o, S_out, B, H, T, dk, dv, dtype, chunk, workspace,
-                              workspace_bytes, stream);
+    return delta_forward_impl(fn, q, k, v, beta, alpha, S0, o, S_out, nullptr, 0, B, H, T, dk, dv, dtype, chunk,
+                              workspace, workspace_bytes, stream);
+}
+
+la_status delta_forward_ex(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
+                           const float* S0, void* o, float* S_out, void* pred, int flags, int B, int H, int T, int dk,
+                           int dv, int dtype, int chunk, void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "delta_forward_ex";
+    if (!q || !k || !v || !beta || !o)
+        return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, beta and o must be non-NULL", fn);
+    return delta_forward_impl(fn, q, k, v, beta, alpha, S0, o, S_out, pred, flags, B, H, T, dk, dv, dtype, chunk,
+                              workspace, workspace_bytes, stream);
 }
 
 la_status la_decode_step(const void* q, const void* k, const void* v, float* S, float* z, void* o, int N,
@@ -260,7 +277,7 @@ la_status delta_decode_step(const void* q, const void* k, const void* v, const v
     const char* fn = "delta_decode_step";
     if (!q || !k || !v || !beta || !S || !o)
         return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, beta, S and o must be non-NULL", fn);
-    return delta_decode_impl(fn, q, k, v, beta, nullptr, S, o, N, H, dk, dv, dtype, stream);
+    return delta_decode_impl(fn, q, k, v, beta, nullptr, S, o, nullptr, 0, N, H, dk, dv, dtype, stream);
 }
 
 la_status gated_delta_decode_step(const void* q, const void* k, const void* v, const void* beta,
@@ -269,7 +286,16 @@ la_status gated_delta_decode_step(const void* q, const void* k, const void* v, c
     const char* fn = "gated_delta_decode_step";
     if (!q || !k || !v || !beta || !alpha || !S || !o)
         return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, beta, alpha, S and o must be non-NULL", fn);
-    return delta_decode_impl(fn, q, k, v, beta, alpha, S, o, N, H, dk, dv, dtype, stream);
+    return delta_decode_impl(fn, q, k, v, beta, alpha, S, o, nullptr, 0, N, H, dk, dv, dtype, stream);
+}
+
+la_status delta_decode_step_ex(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
+                               float* S, void* o, void* pred, int flags, int N, int H, int dk, int dv, int dtype,
+                               void* stream) {
+    const char* fn = "delta_decode_step_ex";
+    if (!q || !k || !v || !beta || !S || !o)
+        return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, beta, S and o must be non-NULL", fn);
+    return delta_decode_impl(fn, q, k, v, beta, alpha, S, o, pred, flags, N, H, dk, dv, dtype, stream);
 }
 
 la_status ssd_forward(const void* q, const void* k, const void* v, const float* alpha, const float* S0, void* o,
@@ -299,7 +325,7 @@ la_status ssd_decode_step(const void* q, const void* k, const void* v, const flo
     const char* fn = "ssd_decode_step";
     if (!q || !k || !v || !alpha || !S || !o)
         return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, alpha, S and o must be non-NULL", fn);
-    return delta_decode_impl(fn, q, k, v, nullptr, alpha, S, o, N, H, dk, dv, dtype, stream);
+    return delta_decode_impl(fn, q, k, v, nullptr, alpha, S, o, nullptr, 0, N, H, dk, dv, dtype, stream);
 }
 
 }  // extern "C"

@@ -19,6 +19,11 @@
 //
 // Scalar-decay form ("线性注意力与 SSM" §3, Mamba-2): S <- alpha S + k v^T,
 // o = S^T q = alpha S^T q + (k . q) v: no correction, so S^T k is not needed.
+//
+// Serving input transforms (flags; LinearMem §05, §08): kNormQK scales q and
+// k to unit L2 norm (applied as factors on the reductions and the write),
+// kBetaSigmoid reads beta as a logit.  pred (optional) receives the
+// prediction (decayed S)^T k made before the write.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -30,20 +35,23 @@ constexpr int NTHR = 256;
 
 enum : int { kRuleDelta = 0, kRuleGatedDelta = 1, kRuleSsd = 2 };
 
-template <typename TIn, int DK, int DV, int RULE>
+// NORM (the q/k L2 normalisation) is a template parameter: as a runtime
+// option it costs the kernel about 60 registers and half its occupancy.
+template <typename TIn, int DK, int DV, int RULE, bool NORM>
 __global__ __launch_bounds__(NTHR) void delta_decode_kernel(const TIn* __restrict__ q,
                                                             const TIn* __restrict__ k,
                                                             const TIn* __restrict__ v,
                                                             const TIn* __restrict__ beta,
                                                             const float* __restrict__ alpha,
-                                                            float* __restrict__ S, TIn* __restrict__ o) {
+                                                            float* __restrict__ S, TIn* __restrict__ o,
+                                                            TIn* __restrict__ pred_out, int flags) {
     constexpr int CG = DV / 4;    // 16-byte column groups per row
     constexpr int R = NTHR / CG;  // row groups
     constexpr int RPT = DK / R;   // rows per thread
     static_assert(RPT * R == DK && CG * 4 == DV && DK <= NTHR, "shape");
     __shared__ float fk[DK], fq[DK];
     __shared__ v4f part_k[R][CG], part_q[R][CG];
-    __shared__ float kq_part[NTHR / 64];
+    __shared__ float kq_part[NTHR / 64], kk_part[NTHR / 64], qq_part[NTHR / 64];
 
     constexpr bool GATED = RULE != kRuleDelta, SSD = RULE == kRuleSsd;
     const int tid = threadIdx.x;
@@ -57,18 +65,33 @@ __global__ __launch_bounds__(NTHR) void delta_decode_kernel(const TIn* __restric
     for (int m = 0; m < RPT; ++m)
         st[m] = *reinterpret_cast<const v4f*>(Ss + (long)(rg + R * m) * DV + 4 * cg);
 
-    float kq = 0.f;
+    float kq = 0.f, kk = 0.f, qq = 0.f;
     if (tid < DK) {
         const float kv = Elem<TIn>::load(k, s * DK + tid);
         const float qv = Elem<TIn>::load(q, s * DK + tid);
         fk[tid] = kv;
         fq[tid] = qv;
         kq = kv * qv;
+        kk = kv * kv;
+        qq = qv * qv;
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) kq += __shfl_xor(kq, off);
-    if ((tid & 63) == 0) kq_part[tid >> 6] = kq;
-    const float b = SSD ? 1.f : Elem<TIn>::load(beta, s);
+    for (int off = 32; off > 0; off >>= 1) {
+        kq += __shfl_xor(kq, off);
+        if constexpr (NORM) {
+            kk += __shfl_xor(kk, off);
+            qq += __shfl_xor(qq, off);
+        }
+    }
+    if ((tid & 63) == 0) {
+        kq_part[tid >> 6] = kq;
+        if constexpr (NORM) {
+            kk_part[tid >> 6] = kk;
+            qq_part[tid >> 6] = qq;
+        }
+    }
+    const float braw = SSD ? 1.f : Elem<TIn>::load(beta, s);
+    const float b = (!SSD && (flags & kBetaSigmoid)) ? 1.f / (1.f + __expf(-braw)) : braw;
     const float a = GATED ? alpha[s] : 1.f;
     const v4f vv = v4f{Elem<TIn>::load(v, s * DV + 4 * cg + 0), Elem<TIn>::load(v, s * DV + 4 * cg + 1),
                        Elem<TIn>::load(v, s * DV + 4 * cg + 2), Elem<TIn>::load(v, s * DV + 4 * cg + 3)};
@@ -93,10 +116,20 @@ __global__ __launch_bounds__(NTHR) void delta_decode_kernel(const TIn* __restric
         if constexpr (!SSD) pred += part_k[r][cg];
         sq += part_q[r][cg];
     }
-    if constexpr (GATED) {  // reductions over the decayed state
-        pred *= a;
-        sq *= a;
+    // unit-norm factors of k and q (1 without the transform; a zero row stays zero)
+    float rk = 1.f, rq = 1.f;
+    if constexpr (NORM) {
+        float ks = 0.f, qs = 0.f;
+#pragma unroll
+        for (int i = 0; i < NTHR / 64; ++i) {
+            ks += kk_part[i];
+            qs += qq_part[i];
+        }
+        rk = ks > 0.f ? __builtin_amdgcn_rsqf(ks) : 0.f;
+        rq = qs > 0.f ? __builtin_amdgcn_rsqf(qs) : 0.f;
     }
+    pred *= (GATED ? a : 1.f) * rk;  // reductions over the decayed state
+    sq *= (GATED ? a : 1.f) * rq;
     const v4f u = vv - pred;
     const v4f bu = b * u;
 
@@ -105,7 +138,7 @@ __global__ __launch_bounds__(NTHR) void delta_decode_kernel(const TIn* __restric
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int row = rg + R * m;
-        const v4f x = (GATED ? a * st[m] : st[m]) + fk[row] * bu;
+        const v4f x = (GATED ? a * st[m] : st[m]) + (fk[row] * rk) * bu;
         __builtin_nontemporal_store(x, reinterpret_cast<v4f*>(Ss + (long)row * DV + 4 * cg));
     }
 
@@ -114,40 +147,54 @@ __global__ __launch_bounds__(NTHR) void delta_decode_kernel(const TIn* __restric
         float kqs = 0.f;
 #pragma unroll
         for (int i = 0; i < NTHR / 64; ++i) kqs += kq_part[i];
-        const v4f out = sq + kqs * bu;
+        const v4f out = sq + (kqs * rk * rq) * bu;
 #pragma unroll
         for (int e = 0; e < 4; ++e) Elem<TIn>::store(o, s * DV + 4 * cg + e, out[e]);
+        if (!SSD && pred_out) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Elem<TIn>::store(pred_out, s * DV + 4 * cg + e, pred[e]);
+        }
     }
+}
+
+template <typename TIn, int DK, int DV, int RULE, bool NORM>
+void launch_one(const void* q, const void* k, const void* v, const void* beta, const float* alpha, float* S,
+                void* o, void* pred, int flags, int NH, hipStream_t stream) {
+    delta_decode_kernel<TIn, DK, DV, RULE, NORM><<<dim3(NH), dim3(NTHR), 0, stream>>>(
+        static_cast<const TIn*>(q), static_cast<const TIn*>(k), static_cast<const TIn*>(v),
+        static_cast<const TIn*>(beta), alpha, S, static_cast<TIn*>(o), static_cast<TIn*>(pred), flags);
 }
 
 template <typename TIn, int DK, int DV, int RULE>
 void launch_rule(const void* q, const void* k, const void* v, const void* beta, const float* alpha, float* S,
-                 void* o, int NH, hipStream_t stream) {
-    delta_decode_kernel<TIn, DK, DV, RULE><<<dim3(NH), dim3(NTHR), 0, stream>>>(
-        static_cast<const TIn*>(q), static_cast<const TIn*>(k), static_cast<const TIn*>(v),
-        static_cast<const TIn*>(beta), alpha, S, static_cast<TIn*>(o));
+                 void* o, void* pred, int flags, int NH, hipStream_t stream) {
+    if (flags & kNormQK)
+        launch_one<TIn, DK, DV, RULE, true>(q, k, v, beta, alpha, S, o, pred, flags, NH, stream);
+    else
+        launch_one<TIn, DK, DV, RULE, false>(q, k, v, beta, alpha, S, o, pred, flags, NH, stream);
 }
 
 // beta NULL (with alpha) selects the scalar-decay rule; alpha NULL the plain delta rule.
 template <typename TIn, int DK, int DV>
 hipError_t launch_typed(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
-                        float* S, void* o, int NH, hipStream_t stream) {
+                        float* S, void* o, void* pred, int flags, int NH, hipStream_t stream) {
     if (!alpha)
-        launch_rule<TIn, DK, DV, kRuleDelta>(q, k, v, beta, nullptr, S, o, NH, stream);
+        launch_rule<TIn, DK, DV, kRuleDelta>(q, k, v, beta, nullptr, S, o, pred, flags, NH, stream);
     else if (beta)
-        launch_rule<TIn, DK, DV, kRuleGatedDelta>(q, k, v, beta, alpha, S, o, NH, stream);
+        launch_rule<TIn, DK, DV, kRuleGatedDelta>(q, k, v, beta, alpha, S, o, pred, flags, NH, stream);
     else
-        launch_rule<TIn, DK, DV, kRuleSsd>(q, k, v, nullptr, alpha, S, o, NH, stream);
+        launch_one<TIn, DK, DV, kRuleSsd, false>(q, k, v, nullptr, alpha, S, o, nullptr, 0, NH, stream);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_delta_decode(const void* q, const void* k, const void* v, const void* beta,
-                               const float* alpha, float* S, void* o, int NH, int dk, int dv, int dtype,
-                               hipStream_t stream) {
-#define DEC_CASE(TY, DT, A, B) \
-    if (dtype == DT && dk == A && dv == B) return launch_typed<TY, A, B>(q, k, v, beta, alpha, S, o, NH, stream);
+                               const float* alpha, float* S, void* o, void* pred, int flags, int NH, int dk,
+                               int dv, int dtype, hipStream_t stream) {
+#define DEC_CASE(TY, DT, A, B)             \
+    if (dtype == DT && dk == A && dv == B) \
+        return launch_typed<TY, A, B>(q, k, v, beta, alpha, S, o, pred, flags, NH, stream);
     DEC_CASE(bf16_t, 1, 64, 64)
     DEC_CASE(bf16_t, 1, 64, 128)
     DEC_CASE(bf16_t, 1, 128, 64)

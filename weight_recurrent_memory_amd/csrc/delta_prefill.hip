@@ -41,6 +41,14 @@
 // (each log clamped at -20), so no ratio divides by an underflowed product.
 // The segment maps stay affine in the incoming state, so the three launches
 // are unchanged.
+//
+// Serving input transforms (LinearMem §05 and §08: the L2 normalisation of
+// q and k and the beta transform run inside the kernel): with kNormQK each
+// staged q and k row is scaled to unit L2 norm; with kBetaSigmoid beta holds
+// logits and is passed through a sigmoid.  pred (optional) receives the
+// prediction made before each write, v_t - u_t = (decayed S_{t-1})^T k_t
+// ("手撕：递推与记忆模型", "Delta-rule fast weight", which reads first and
+// then writes with the error).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -81,6 +89,34 @@ struct DL {
     static constexpr int W_TPW = 4 * XR / NWV;      // W^T tiles per wave
 };
 
+// Chunk rows of a [T][D] bf16 matrix into LDS scaled to unit L2 norm (a zero
+// row stays zero).  The D/8 threads holding a row are consecutive lanes, so
+// the row's sum of squares is a shuffle reduction within their group.
+template <int D>
+__device__ __forceinline__ void stage_rows_l2(const ChunkRegs<bf16_t, D, NT>& cr, int tid, __bf16* rm, int ld) {
+    constexpr int TPR = D / 8;
+#pragma unroll
+    for (int j = 0; j < ChunkRegs<bf16_t, D, NT>::NV; ++j) {
+        const int row = ChunkRegs<bf16_t, D, NT>::row_of(j, tid);
+        const int col = ChunkRegs<bf16_t, D, NT>::col_of(j, tid);
+        float x[8], ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            x[e] = cr.get(j, e);
+            ss += x[e] * x[e];
+        }
+#pragma unroll
+        for (int m = 1; m < TPR; m <<= 1) ss += __shfl_xor(ss, m);
+        const float inv = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;
+        uint4 y;
+        y.x = pack_bf16x2(x[0] * inv, x[1] * inv);
+        y.y = pack_bf16x2(x[2] * inv, x[3] * inv);
+        y.z = pack_bf16x2(x[4] * inv, x[5] * inv);
+        y.w = pack_bf16x2(x[6] * inv, x[7] * inv);
+        *reinterpret_cast<uint4*>(rm + row * ld + col) = y;
+    }
+}
+
 // The ten lower 16x16 tiles of a 64x64 matrix: diagonal first.
 __host__ __device__ constexpr void lower_tile(int id, int& i, int& j) {
     if (id < 4) { i = id; j = id; }                // (0,0) (1,1) (2,2) (3,3)
@@ -103,7 +139,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ beta, const float* __restrict__ alpha, bf16_t* __restrict__ o,
     const float* __restrict__ state_in, float* __restrict__ map_n, float* __restrict__ map_m,
-    float* __restrict__ S_out, int T, int L, int G) {
+    float* __restrict__ S_out, bf16_t* __restrict__ pred, int flags, int T, int L, int G) {
     using Y = DL<DK, NS, OUT, GATED>;
     using M = Mma<bf16_t>;
     using MF = Mma<float>;
@@ -210,11 +246,17 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         const int n = min(CH, t_end - c0);
         // ---- stage the chunk row-major (transposed operands are read with
         // transpose loads)
-        stage_rows_raw<bf16_t, DK, NT>(kr, tid, Ks, LQ);
-        if constexpr (OUT) stage_rows_raw<bf16_t, DK, NT>(qr, tid, Qs, LQ);
+        if (flags & kNormQK) {
+            stage_rows_l2<DK>(kr, tid, Ks, LQ);
+            if constexpr (OUT) stage_rows_l2<DK>(qr, tid, Qs, LQ);
+        } else {
+            stage_rows_raw<bf16_t, DK, NT>(kr, tid, Ks, LQ);
+            if constexpr (OUT) stage_rows_raw<bf16_t, DK, NT>(qr, tid, Qs, LQ);
+        }
         stage_rows_raw<bf16_t, NS, NT>(vr, tid, Vs, LV);
         if (tid < CH) {  // wave 0
-            Bs[tid] = bf16_to_f32(bnext);
+            const float braw = bf16_to_f32(bnext);
+            Bs[tid] = (flags & kBetaSigmoid) ? 1.f / (1.f + __expf(-braw)) : braw;
             if constexpr (GATED) {
                 // inclusive scan of the log-gates over the chunk; tokens past
                 // the segment end count as alpha = 1, so gamma_C = gamma_{n-1}
@@ -463,7 +505,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         for (int j = 0; j < SLOTS; ++j) {
             const int id = w + NWV * j;
             if (id >= Y::NCT) continue;
-            // U = U_v - W S, then beta o U
+            // U = U_v - W S, then beta o U (and, if wanted, the predictions V - U)
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 v4f ws_ = zero4();
@@ -472,7 +514,21 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
                     M::mma(ws_, M::load(&Ws[(16 * tt + li) * LQ + 32 * kb], g),
                            M::from_tiles(X[j][2 * kb], X[j][2 * kb + 1]));
 #pragma unroll
-                for (int r = 0; r < 4; ++r) U[j][tt][r] = Bs[16 * tt + 4 * g + r] * (U[j][tt][r] - ws_[r]);
+                for (int r = 0; r < 4; ++r) U[j][tt][r] -= ws_[r];
+                if constexpr (OUT) {
+                    if (pred) {  // rows past the segment end are dropped by the resource
+                        const rsrc_t rp = make_rsrc(pred + (long)head * T * NS, (uint32_t)t_end * NS * 2);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int t = 16 * tt + 4 * g + r;
+                            const float pv = (float)Vs[t * LV + 16 * id + li] - U[j][tt][r];
+                            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(pv), rp,
+                                                                  (uint32_t)(((c0 + t) * NS + 16 * id + li) * 2), 0, 0);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) U[j][tt][r] *= Bs[16 * tt + 4 * g + r];
             }
             if constexpr (OUT) {
                 // outputs, second half: O^T += (beta o U)^T P^T, stored
@@ -603,8 +659,8 @@ __global__ __launch_bounds__(256) void delta_compose_kernel(const float* __restr
 
 template <int DK, int DV, bool GATED>
 hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* beta,
-                        const float* alpha, const float* S0, bf16_t* o, float* S_out, int HT, int T,
-                        const LaPlan& plan, float* ws, hipStream_t stream) {
+                        const float* alpha, const float* S0, bf16_t* o, float* S_out, bf16_t* pred, int flags,
+                        int HT, int T, const LaPlan& plan, float* ws, hipStream_t stream) {
     const int G = plan.G, L = plan.L;
     float* map_n = ws;
     float* map_m = map_n + (size_t)HT * G * DK * DV;
@@ -612,13 +668,13 @@ hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const
     hipError_t err;
     if (G > 1) {
         delta_chunk_kernel<DK, DV, false, GATED><<<dim3(HT * (G - 1)), dim3(NT), 0, stream>>>(
-            q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, T, L, G);
+            q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, nullptr, flags, T, L, G);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     delta_compose_kernel<DK, DV><<<dim3(DV / 16, HT), dim3(256), 0, stream>>>(map_n, map_m, S0, state_in, G);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     delta_chunk_kernel<DK, DV, true, GATED><<<dim3(HT * G), dim3(NT), 0, stream>>>(
-        q, k, v, beta, alpha, o, state_in, nullptr, nullptr, S_out, T, L, G);
+        q, k, v, beta, alpha, o, state_in, nullptr, nullptr, S_out, pred, flags, T, L, G);
     return hipGetLastError();
 }
 
@@ -629,18 +685,22 @@ size_t delta_ws_floats(int HT, int dk, int dv, const LaPlan& plan) {
 }
 
 hipError_t launch_delta_forward(const void* q, const void* k, const void* v, const void* beta,
-                                const float* alpha, const float* S0, void* o, float* S_out, int HT, int T,
-                                int dk, int dv, int dtype, const LaPlan& plan, float* ws, hipStream_t stream) {
+                                const float* alpha, const float* S0, void* o, float* S_out, void* pred, int flags,
+                                int HT, int T, int dk, int dv, int dtype, const LaPlan& plan, float* ws,
+                                hipStream_t stream) {
     if (dtype != 1) return hipErrorInvalidValue;
     const bf16_t* qb = static_cast<const bf16_t*>(q);
     const bf16_t* kb = static_cast<const bf16_t*>(k);
     const bf16_t* vb = static_cast<const bf16_t*>(v);
     const bf16_t* bb = static_cast<const bf16_t*>(beta);
     bf16_t* ob = static_cast<bf16_t*>(o);
-#define DELTA_CASE(A, B)                                                                              \
-    if (dk == A && dv == B)                                                                           \
-        return alpha ? launch_typed<A, B, true>(qb, kb, vb, bb, alpha, S0, ob, S_out, HT, T, plan, ws, stream) \
-                     : launch_typed<A, B, false>(qb, kb, vb, bb, nullptr, S0, ob, S_out, HT, T, plan, ws, stream);
+    bf16_t* pb = static_cast<bf16_t*>(pred);
+#define DELTA_CASE(A, B)                                                                                      \
+    if (dk == A && dv == B)                                                                                   \
+        return alpha ? launch_typed<A, B, true>(qb, kb, vb, bb, alpha, S0, ob, S_out, pb, flags, HT, T, plan, ws, \
+                                                stream)                                                       \
+                     : launch_typed<A, B, false>(qb, kb, vb, bb, nullptr, S0, ob, S_out, pb, flags, HT, T, plan,  \
+                                                 ws, stream);
     DELTA_CASE(64, 64)
     DELTA_CASE(64, 128)
     DELTA_CASE(128, 64)

@@ -30,12 +30,18 @@ LaPlan la_plan(int HT, int T, int dk, int dv);
 size_t la_flag_words(int HT, int G);
 size_t la_ws_floats(int HT, int T, int dk, int dv);
 
+// Input-transform flags of the delta-rule kernels (same values as the ABI's).
+constexpr int kNormQK = 1;        // q, k rows scaled to unit L2 norm in the kernel
+constexpr int kBetaSigmoid = 2;   // beta holds logits; the kernel applies a sigmoid
+
 // Delta-rule prefill: segment affine maps -> serial composition -> chunked
 // outputs.  alpha (fp32 [HT][T]) selects the gated rule; NULL = ungated.
+// pred (optional, [HT][T][dv] in the input dtype) receives the prediction
+// made before each write.
 hipError_t launch_delta_forward(const void* q, const void* k, const void* v,
                                 const void* beta, const float* alpha, const float* S0,
-                                void* o, float* S_out, int HT, int T, int dk, int dv,
-                                int dtype, const LaPlan& plan, float* ws,
+                                void* o, float* S_out, void* pred, int flags, int HT, int T,
+                                int dk, int dv, int dtype, const LaPlan& plan, float* ws,
                                 hipStream_t stream);
 size_t delta_ws_floats(int HT, int dk, int dv, const LaPlan& plan);
 
@@ -50,8 +56,8 @@ size_t ssd_ws_floats(int HT, int dk, int dv, const LaPlan& plan);
 // [NH]) selects the gated rule, NULL = ungated; beta NULL with alpha given
 // selects the scalar-decay rule (no correction).
 hipError_t launch_delta_decode(const void* q, const void* k, const void* v, const void* beta,
-                               const float* alpha, float* S, void* o, int NH, int dk, int dv, int dtype,
-                               hipStream_t stream);
+                               const float* alpha, float* S, void* o, void* pred, int flags, int NH, int dk,
+                               int dv, int dtype, hipStream_t stream);
 
 // Linear attention decode step on a resident fp32 state (in place).
 hipError_t launch_la_decode(const void* q, const void* k, const void* v, float* S,
