@@ -10,9 +10,11 @@
  *   delta_decode_step        one-token decode of the delta rule on a resident state
  *   gated_delta_decode_step  the same with a forgetting gate
  *   ssd_decode_step          one-token decode of the scalar-decay memory
- * and two delta-rule calls with serving options (input transforms, the
+ * two delta-rule calls with serving options (input transforms, the
  * read-then-write prediction as an extra output): delta_forward_ex,
- * delta_decode_step_ex.
+ * delta_decode_step_ex; and the prefills over packed batches of
+ * variable-length sequences, each sequence starting from its own state:
+ * la_forward_packed, delta_forward_packed, ssd_forward_packed.
  *
  * Pages the definitions come from:
  *   [LinearMem]  "AIGC 基本功｜线性、循环与记忆架构-LinearMem"
@@ -249,6 +251,53 @@ la_status ssd_forward(const void* q, const void* k, const void* v, const float* 
  */
 la_status ssd_decode_step(const void* q, const void* k, const void* v, const float* alpha, float* S,
                           void* o, int N, int H, int dk, int dv, int dtype, void* stream);
+
+/*
+ * Packed batches ([LinearMem] §05: when a request ends only its own state is
+ * cleared, and samples concatenated without a reset would read one another;
+ * [Recurrence] "验证边界": state resets at request, batch and document
+ * boundaries).  N sequences of different lengths are concatenated along the
+ * token axis: q, k [H][T_total][dk]; v, o, pred [H][T_total][dv]; beta,
+ * alpha [H][T_total]; sequence n is rows cu[n] .. cu[n+1]-1 of every head.
+ * Each sequence starts from its own initial state (S0, z0 [N][H][..], NULL =
+ * zero) and returns its own final state (S_out, z_out [N][H][..]); no
+ * information crosses a sequence boundary.  Results equal the per-sequence
+ * calls.
+ * cu_seqlens       device int32 [N+1]: 0 = cu[0] < cu[1] < ... < cu[N] = T_total
+ *                  (no empty sequence); the kernels read it.
+ * cu_seqlens_host  host int32 [N+1], the same values; the call plans its
+ *                  launches from it and validates it (LA_ERR_INVALID_ARG).
+ *                  Device offsets that differ from it give wrong results but
+ *                  never an access outside the inputs, outputs or workspace.
+ * The workspace (size from the matching *_packed_workspace_bytes query, which
+ * needs only the host offsets) also holds a per-sequence segment table the
+ * call builds on the device.  Other arguments and errors are those of the
+ * uniform calls.
+ */
+size_t la_forward_packed_workspace_bytes(const int* cu_seqlens_host, int N, int H, int T_total,
+                                         int dk, int dv, int chunk);
+la_status la_forward_packed(const void* q, const void* k, const void* v,
+                            const int* cu_seqlens, const int* cu_seqlens_host, int N,
+                            const float* S0, const float* z0, void* o, float* S_out, float* z_out,
+                            int H, int T_total, int dk, int dv, int dtype, float eps, int chunk,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+size_t delta_forward_packed_workspace_bytes(const int* cu_seqlens_host, int N, int H, int T_total,
+                                            int dk, int dv, int chunk);
+/* The delta rule (alpha NULL) or the gated rule, with the options of delta_forward_ex. */
+la_status delta_forward_packed(const void* q, const void* k, const void* v, const void* beta,
+                               const float* alpha, const int* cu_seqlens, const int* cu_seqlens_host,
+                               int N, const float* S0, void* o, float* S_out, void* pred, int flags,
+                               int H, int T_total, int dk, int dv, int dtype, int chunk,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+size_t ssd_forward_packed_workspace_bytes(const int* cu_seqlens_host, int N, int H, int T_total,
+                                          int dk, int dv, int chunk);
+la_status ssd_forward_packed(const void* q, const void* k, const void* v, const float* alpha,
+                             const int* cu_seqlens, const int* cu_seqlens_host, int N,
+                             const float* S0, void* o, float* S_out,
+                             int H, int T_total, int dk, int dv, int dtype, int chunk,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

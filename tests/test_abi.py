@@ -28,7 +28,7 @@ def test_header_declares_the_operations():
     fns = _declared_functions()
     for name in ("la_forward", "delta_forward", "la_decode_step", "delta_decode_step", "gated_delta_forward",
                  "gated_delta_decode_step", "ssd_forward", "ssd_decode_step", "delta_forward_ex",
-                 "delta_decode_step_ex"):
+                 "delta_decode_step_ex", "la_forward_packed", "delta_forward_packed", "ssd_forward_packed"):
         assert name in fns
 
 
@@ -219,6 +219,49 @@ def _ddex(**kw):
 def test_delta_decode_step_ex_rejects(kw, status):
     assert _ddex(**kw) == ST[status]
     assert lin.lib().la_last_error().decode().startswith("delta_decode_step_ex")
+
+
+def _packed_la(cu_host, **kw):
+    host = (ctypes.c_int * len(cu_host))(*cu_host)
+    a = dict(q=P, k=P, v=P, cu=P, N=len(cu_host) - 1, S0=None, z0=None, o=P, S_out=None, z_out=None, H=2,
+             T=cu_host[-1], dk=64, dv=64, dtype=1, eps=1e-6, chunk=64, ws=P, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lin.lib().la_forward_packed(a["q"], a["k"], a["v"], a["cu"], ctypes.cast(host, ctypes.c_void_p), a["N"],
+                                       a["S0"], a["z0"], a["o"], a["S_out"], a["z_out"], a["H"], a["T"], a["dk"],
+                                       a["dv"], a["dtype"], a["eps"], a["chunk"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("cu_host,kw,status", [
+    ([1, 5, 9], {}, "INVALID_ARG"),              # does not start at 0
+    ([0, 5, 5, 9], {}, "INVALID_ARG"),           # an empty sequence
+    ([0, 6, 4, 9], {}, "INVALID_ARG"),           # decreasing
+    ([0, 5, 9], dict(T=10), "INVALID_ARG"),      # last offset is not T_total
+    ([0, 5, 9], dict(cu=None), "INVALID_ARG"),   # no device offsets
+    ([0, 5, 9], dict(cu=ctypes.c_void_p(0x10002)), "INVALID_ARG"),
+    ([0, 5, 9], dict(N=0), "INVALID_ARG"),
+    ([0, 5, 9], dict(dk=96), "UNSUPPORTED"),
+    ([0, 5, 9], dict(ws=None), "WORKSPACE"),
+])
+def test_la_forward_packed_rejects(cu_host, kw, status):
+    assert _packed_la(cu_host, **kw) == ST[status]
+    assert lin.lib().la_last_error().decode().startswith("la_forward_packed")
+
+
+def test_packed_workspace_queries_and_rejects():
+    L = lin.lib()
+    for fn in (L.la_forward_packed_workspace_bytes, L.delta_forward_packed_workspace_bytes,
+               L.ssd_forward_packed_workspace_bytes):
+        good = (ctypes.c_int * 4)(0, 100, 3000, 3001)
+        assert fn(ctypes.cast(good, ctypes.c_void_p), 3, 8, 3001, 128, 128, 64) > 0
+        bad = (ctypes.c_int * 4)(0, 100, 100, 3001)
+        assert fn(ctypes.cast(bad, ctypes.c_void_p), 3, 8, 3001, 128, 128, 64) == 0
+        assert fn(None, 3, 8, 3001, 128, 128, 64) == 0
+    cu = (ctypes.c_int * 3)(0, 5, 9)
+    h = ctypes.cast(cu, ctypes.c_void_p)
+    assert L.delta_forward_packed(P, P, P, P, None, P, h, 2, None, P, None, None, 4, 2, 9, 128, 128, 1, 64, P,
+                                  1 << 30, None) == ST["INVALID_ARG"]  # unknown flags
+    assert L.ssd_forward_packed(P, P, P, None, P, h, 2, None, P, None, 2, 9, 64, 64, 1, 64, P, 1 << 30,
+                                None) == ST["INVALID_ARG"]  # alpha NULL
 
 
 def test_workspace_queries():

@@ -74,6 +74,20 @@ def lib():
             L.delta_forward_ex.restype = i
             L.delta_decode_step_ex.argtypes = [vp, vp, vp, vp, fp, fp, vp, vp, i, i, i, i, i, i, vp]
             L.delta_decode_step_ex.restype = i
+            L.la_forward_packed_workspace_bytes.argtypes = [vp, i, i, i, i, i, i]
+            L.la_forward_packed_workspace_bytes.restype = sz
+            L.delta_forward_packed_workspace_bytes.argtypes = [vp, i, i, i, i, i, i]
+            L.delta_forward_packed_workspace_bytes.restype = sz
+            L.ssd_forward_packed_workspace_bytes.argtypes = [vp, i, i, i, i, i, i]
+            L.ssd_forward_packed_workspace_bytes.restype = sz
+            L.la_forward_packed.argtypes = [vp, vp, vp, vp, vp, i, fp, fp, vp, fp, fp, i, i, i, i, i,
+                                            ctypes.c_float, i, vp, sz, vp]
+            L.la_forward_packed.restype = i
+            L.delta_forward_packed.argtypes = [vp, vp, vp, vp, fp, vp, vp, i, fp, vp, fp, vp, i, i, i, i, i, i, i,
+                                               vp, sz, vp]
+            L.delta_forward_packed.restype = i
+            L.ssd_forward_packed.argtypes = [vp, vp, vp, fp, vp, vp, i, fp, vp, fp, i, i, i, i, i, i, vp, sz, vp]
+            L.ssd_forward_packed.restype = i
             L.la_status_string.argtypes = [i]
             L.la_status_string.restype = ctypes.c_char_p
             L.la_last_error.argtypes = []
@@ -385,3 +399,132 @@ def delta_decode_step_ex(q, k, v, beta, S, alpha=None, *, normalize_qk=False, be
                                       _ptr(pred), _flags(normalize_qk, beta_logits), N, H, dk, dv, code,
                                       _stream(dev)))
     return (o, pred) if return_pred else o
+
+
+# ------------------------------------------------------------ packed batches
+
+def _offsets(cu_seqlens, cu_seqlens_host, dev):
+    """(N, device offsets, host offsets) of a packed batch.  cu_seqlens is an
+    int32 device tensor [N+1]; the host copy is taken from cu_seqlens_host
+    (any int sequence) or, if None, copied from the device."""
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.device != dev:
+        raise ValueError(f"cu_seqlens must be a 1-D int32 tensor on {dev}")
+    if not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be contiguous")
+    host = cu_seqlens.cpu() if cu_seqlens_host is None else torch.as_tensor(cu_seqlens_host, dtype=torch.int32)
+    host = host.contiguous()
+    if host.numel() != cu_seqlens.numel():
+        raise ValueError("cu_seqlens_host and cu_seqlens differ in length")
+    return cu_seqlens.numel() - 1, host
+
+
+def la_forward_packed_workspace_bytes(cu_seqlens_host, H, dk, dv, chunk=CHUNK) -> int:
+    host = torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous()
+    return int(lib().la_forward_packed_workspace_bytes(_ptr(host), host.numel() - 1, H, int(host[-1]), dk, dv, chunk))
+
+
+def delta_forward_packed_workspace_bytes(cu_seqlens_host, H, dk, dv, chunk=CHUNK) -> int:
+    host = torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous()
+    return int(lib().delta_forward_packed_workspace_bytes(_ptr(host), host.numel() - 1, H, int(host[-1]), dk, dv,
+                                                          chunk))
+
+
+def ssd_forward_packed_workspace_bytes(cu_seqlens_host, H, dk, dv, chunk=CHUNK) -> int:
+    host = torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous()
+    return int(lib().ssd_forward_packed_workspace_bytes(_ptr(host), host.numel() - 1, H, int(host[-1]), dk, dv,
+                                                        chunk))
+
+
+def la_forward_packed(q, k, v, cu_seqlens, S0=None, z0=None, eps=1e-6, chunk=CHUNK, *, cu_seqlens_host=None,
+                      o=None, S_out=None, z_out=None, workspace=None):
+    """LA prefill over a packed batch: q, k [H,T_total,dk]; v [H,T_total,dv];
+    sequence n is rows cu_seqlens[n]..cu_seqlens[n+1]-1 and has its own
+    initial/final state S [N,H,dk,dv], z [N,H,dk].  Returns (o, S_out, z_out)."""
+    code = _dtype_code(q)
+    H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    N, host = _offsets(cu_seqlens, cu_seqlens_host, dev)
+    _need(k, "k", q.dtype, (H, T, dk), dev)
+    _need(v, "v", q.dtype, (H, T, dv), dev)
+    _need(q, "q", q.dtype, (H, T, dk), dev)
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (N, H, dk, dv), dev)
+    if z0 is not None:
+        _need(z0, "z0", torch.float32, (N, H, dk), dev)
+    o = torch.empty((H, T, dv), dtype=q.dtype, device=dev) if o is None else o
+    S_out = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if S_out is None else S_out
+    z_out = torch.empty((N, H, dk), dtype=torch.float32, device=dev) if z_out is None else z_out
+    _need(o, "o", q.dtype, (H, T, dv), dev)
+    _need(S_out, "S_out", torch.float32, (N, H, dk, dv), dev)
+    _need(z_out, "z_out", torch.float32, (N, H, dk), dev)
+    nb = int(lib().la_forward_packed_workspace_bytes(_ptr(host), N, H, T, dk, dv, chunk))
+    ws, wsb = _workspace(nb, dev, workspace)
+    _check(lib().la_forward_packed(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), _ptr(host), N, _ptr(S0), _ptr(z0),
+                                   _ptr(o), _ptr(S_out), _ptr(z_out), H, T, dk, dv, code, float(eps), int(chunk),
+                                   _ptr(ws), wsb, _stream(dev)))
+    return o, S_out, z_out
+
+
+def delta_forward_packed(q, k, v, beta, cu_seqlens, alpha=None, S0=None, chunk=CHUNK, *, normalize_qk=False,
+                         beta_logits=False, return_pred=False, cu_seqlens_host=None, o=None, S_out=None, pred=None,
+                         workspace=None):
+    """Delta-rule (gated when alpha [H,T_total] fp32 is given) prefill over a
+    packed batch; options as delta_forward_ex.  beta [H,T_total].  Returns
+    (o, S_out[, pred]) with S_out [N,H,dk,dv]."""
+    code = _dtype_code(q)
+    H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    N, host = _offsets(cu_seqlens, cu_seqlens_host, dev)
+    _need(k, "k", q.dtype, (H, T, dk), dev)
+    _need(v, "v", q.dtype, (H, T, dv), dev)
+    _need(beta, "beta", q.dtype, (H, T), dev)
+    _need(q, "q", q.dtype, (H, T, dk), dev)
+    if alpha is not None:
+        _need(alpha, "alpha", torch.float32, (H, T), dev)
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (N, H, dk, dv), dev)
+    o = torch.empty((H, T, dv), dtype=q.dtype, device=dev) if o is None else o
+    S_out = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if S_out is None else S_out
+    _need(o, "o", q.dtype, (H, T, dv), dev)
+    _need(S_out, "S_out", torch.float32, (N, H, dk, dv), dev)
+    if return_pred:
+        pred = torch.empty((H, T, dv), dtype=q.dtype, device=dev) if pred is None else pred
+        _need(pred, "pred", q.dtype, (H, T, dv), dev)
+    else:
+        pred = None
+    nb = int(lib().delta_forward_packed_workspace_bytes(_ptr(host), N, H, T, dk, dv, chunk))
+    ws, wsb = _workspace(nb, dev, workspace)
+    _check(lib().delta_forward_packed(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(cu_seqlens),
+                                      _ptr(host), N, _ptr(S0), _ptr(o), _ptr(S_out), _ptr(pred),
+                                      _flags(normalize_qk, beta_logits), H, T, dk, dv, code, int(chunk), _ptr(ws), wsb,
+                                      _stream(dev)))
+    return (o, S_out, pred) if return_pred else (o, S_out)
+
+
+def ssd_forward_packed(q, k, v, alpha, cu_seqlens, S0=None, chunk=CHUNK, *, cu_seqlens_host=None, o=None,
+                       S_out=None, workspace=None):
+    """Scalar-decay prefill over a packed batch: alpha [H,T_total] fp32.
+    Returns (o, S_out) with S_out [N,H,dk,dv]."""
+    code = _dtype_code(q)
+    H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    N, host = _offsets(cu_seqlens, cu_seqlens_host, dev)
+    _need(k, "k", q.dtype, (H, T, dk), dev)
+    _need(v, "v", q.dtype, (H, T, dv), dev)
+    _need(alpha, "alpha", torch.float32, (H, T), dev)
+    _need(q, "q", q.dtype, (H, T, dk), dev)
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (N, H, dk, dv), dev)
+    o = torch.empty((H, T, dv), dtype=q.dtype, device=dev) if o is None else o
+    S_out = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if S_out is None else S_out
+    _need(o, "o", q.dtype, (H, T, dv), dev)
+    _need(S_out, "S_out", torch.float32, (N, H, dk, dv), dev)
+    nb = int(lib().ssd_forward_packed_workspace_bytes(_ptr(host), N, H, T, dk, dv, chunk))
+    ws, wsb = _workspace(nb, dev, workspace)
+    _check(lib().ssd_forward_packed(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(cu_seqlens), _ptr(host), N,
+                                    _ptr(S0), _ptr(o), _ptr(S_out), H, T, dk, dv, code, int(chunk), _ptr(ws), wsb,
+                                    _stream(dev)))
+    return o, S_out

@@ -35,55 +35,153 @@ la_status ok() {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool supported_dim(int d) { return d == 64 || d == 128; }
 
-// Segments per head: enough (head, segment) workgroups to give every one of
-// the 256 compute units about four, never more segments than chunks.
-la::LaPlan plan_segments(int HT, int T, int chunk, int target_groups) {
-    const int nch = (T + chunk - 1) / chunk;
-    long want = (target_groups + (long)HT - 1) / HT;
-    if (want > nch) want = nch;
-    if (want < 1) want = 1;
-    const int cps = (int)((nch + want - 1) / want);
-    la::LaPlan p;
-    p.L = cps * chunk;
-    p.G = (T + p.L - 1) / p.L;
-    return p;
-}
+// ---------------------------------------------------------------- planning
+//
+// A prefill call's batch: uniform (B sequences of T tokens, inputs
+// [B][H][T][d]) or packed (N sequences of cu[n+1] - cu[n] tokens, inputs
+// [H][T_total][d], offsets on the device in cu_dev and on the host in
+// cu_host).
+struct Batch {
+    const int* cu_dev = nullptr;
+    const int* cu_host = nullptr;
+    int N = 0;  // sequences (B for a uniform batch)
+    int H = 0;
+    int T = 0;  // tokens per sequence (uniform) or T_total (packed)
+    bool packed() const { return cu_host != nullptr; }
+};
+
+enum Family { kFamLA, kFamDelta, kFamSsd };
 
 constexpr int kDeltaTargetGroups = 256;  // one 8-wave workgroup per CU (LDS and registers allow one)
 
-// Shared shape checks of the two prefill calls.  Returns LA_OK or a status.
-la_status check_prefill(const char* fn, int B, int H, int T, int dk, int dv, int dtype, int chunk) {
-    if (B < 1 || H < 1 || T < 1 || dk < 1 || dv < 1)
-        return fail(LA_ERR_INVALID_ARG, "%s: sizes must be >= 1 (B=%d H=%d T=%d dk=%d dv=%d)", fn, B,
-                    H, T, dk, dv);
+// Chunks per segment.  LA and SSD: enough (head, segment) workgroups for two
+// per compute unit, and segments short enough that the keys and values of
+// all resident workgroups (read twice) stay within the Infinity Cache.
+// Delta: one 8-wave workgroup per compute unit.  `work` = chunks summed over
+// the sequences of one head; `longest` = chunks of the longest sequence.
+int chunks_per_segment(Family f, long work, long longest, int H, int dk, int dv) {
+    long cps;
+    if (f == kFamDelta) {
+        cps = (work * H + kDeltaTargetGroups - 1) / kDeltaTargetGroups;
+    } else {
+        const long occ = work * H / 512;
+        const long cap = (256L * 1024) / ((long)(dk + dv) * 2 * la::kChunk);
+        cps = occ < cap ? occ : cap;
+    }
+    if (cps > longest) cps = longest;
+    return cps < 1 ? 1 : (int)cps;
+}
+
+// The segment map (device arrays filled in at launch) and the workspace layout.
+struct Plan {
+    la::SegMap sm{};
+    size_t sp_floats = 0;   // packed: the segment prefix, at the workspace start
+    size_t fam_floats = 0;  // the family's per-slot arrays after it
+    size_t bytes() const { return sizeof(float) * (sp_floats + fam_floats); }
+};
+
+Plan make_plan(Family f, const Batch& b, int dk, int dv) {
+    Plan p;
+    la::SegMap& sm = p.sm;
+    sm.N = b.N;
+    sm.H = b.H;
+    sm.T = b.T;
+    sm.hs = b.T;
+    if (!b.packed()) {
+        const int nch = (b.T + la::kChunk - 1) / la::kChunk;
+        if (f == kFamDelta) {
+            // segments per sequence: enough workgroups for about one per CU
+            const int HT = b.N * b.H;
+            long want = (kDeltaTargetGroups + (long)HT - 1) / HT;
+            if (want > nch) want = nch;
+            if (want < 1) want = 1;
+            sm.L = (int)((nch + want - 1) / want) * la::kChunk;
+        } else {
+            sm.L = la::la_plan(b.N * b.H, b.T, dk, dv).L;
+        }
+        sm.G = (b.T + sm.L - 1) / sm.L;
+        sm.NS = b.N * sm.G;
+    } else {
+        long work = 0, longest = 0;
+        for (int n = 0; n < b.N; ++n) {
+            const long c = (b.cu_host[n + 1] - b.cu_host[n] + la::kChunk - 1) / la::kChunk;
+            work += c;
+            longest = c > longest ? c : longest;
+        }
+        sm.L = chunks_per_segment(f, work, longest, b.H, dk, dv) * la::kChunk;
+        long ns = 0;
+        for (int n = 0; n < b.N; ++n) ns += (b.cu_host[n + 1] - b.cu_host[n] + sm.L - 1) / sm.L;
+        sm.NS = (int)ns;
+        p.sp_floats = ((size_t)b.N + 1 + 63) / 64 * 64;
+    }
+    const long slots = (long)sm.H * sm.NS;
+    p.fam_floats = f == kFamLA ? la::la_ws_floats(slots, dk, dv)
+                 : f == kFamDelta ? la::delta_ws_floats(slots, dk, dv)
+                                  : la::ssd_ws_floats(slots, dk, dv);
+    return p;
+}
+
+// Shape checks shared by every prefill call.  Returns LA_OK or a status.
+la_status check_batch(const char* fn, const Batch& b, int dk, int dv, int dtype, int chunk) {
+    if (b.N < 1 || b.H < 1 || b.T < 1 || dk < 1 || dv < 1)
+        return fail(LA_ERR_INVALID_ARG, "%s: sizes must be >= 1 (%s=%d H=%d T=%d dk=%d dv=%d)", fn,
+                    b.packed() ? "N" : "B", b.N, b.H, b.T, dk, dv);
     if (chunk < 1) return fail(LA_ERR_INVALID_ARG, "%s: chunk must be positive (got %d)", fn, chunk);
     if (dtype != LA_F32 && dtype != LA_BF16)
         return fail(LA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
-    if ((long)B * H > (1L << 24))
-        return fail(LA_ERR_UNSUPPORTED, "%s: B*H = %ld heads exceeds 2^24", fn, (long)B * H);
+    if (b.packed()) {
+        if (!b.cu_dev) return fail(LA_ERR_INVALID_ARG, "%s: the device sequence offsets must be non-NULL", fn);
+        if (reinterpret_cast<uintptr_t>(b.cu_dev) & 3u)
+            return fail(LA_ERR_INVALID_ARG, "%s: the device sequence offsets must be 4-byte aligned", fn);
+        if (b.cu_host[0] != 0 || b.cu_host[b.N] != b.T)
+            return fail(LA_ERR_INVALID_ARG, "%s: sequence offsets must run from 0 to T_total=%d (got %d .. %d)", fn,
+                        b.T, b.cu_host[0], b.cu_host[b.N]);
+        for (int n = 0; n < b.N; ++n)
+            if (b.cu_host[n + 1] <= b.cu_host[n])
+                return fail(LA_ERR_INVALID_ARG, "%s: sequence %d is empty or offsets decrease (%d, %d)", fn, n,
+                            b.cu_host[n], b.cu_host[n + 1]);
+    }
+    if ((long)b.N * b.H > (1L << 24))
+        return fail(LA_ERR_UNSUPPORTED, "%s: %ld (sequence, head) pairs exceed 2^24", fn, (long)b.N * b.H);
     if (!supported_dim(dk) || !supported_dim(dv))
         return fail(LA_ERR_UNSUPPORTED, "%s: dk=%d dv=%d not in {64, 128}", fn, dk, dv);
     if (chunk != la::kChunk)
         return fail(LA_ERR_UNSUPPORTED, "%s: chunk=%d not supported (only %d)", fn, chunk, la::kChunk);
     const long elem = dtype == LA_BF16 ? 2 : 4;
-    if (((long)T + la::kChunk) * (dk > dv ? dk : dv) * elem >= (1L << 31))
-        return fail(LA_ERR_UNSUPPORTED, "%s: T=%d too long (one head's rows must span < 2 GiB)", fn, T);
+    if (((long)b.T + la::kChunk) * (dk > dv ? dk : dv) * elem >= (1L << 31))
+        return fail(LA_ERR_UNSUPPORTED, "%s: T=%d too long (one head's rows must span < 2 GiB)", fn, b.T);
     return LA_OK;
 }
 
-size_t la_ws_bytes(int B, int H, int T, int dk, int dv, int) {
-    return sizeof(float) * la::la_ws_floats(B * H, T, dk, dv);
+la_status check_workspace(const char* fn, const Plan& p, const void* workspace, size_t workspace_bytes) {
+    const size_t need = p.bytes();
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
+        return fail(LA_ERR_WORKSPACE, "%s: workspace of %zu bytes (16-byte aligned) required, got %zu", fn, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    return LA_OK;
 }
 
-size_t ssd_ws_bytes(int B, int H, int T, int dk, int dv, int) {
-    const int HT = B * H;
-    return sizeof(float) * la::ssd_ws_floats(HT, dk, dv, la::la_plan(HT, T, dk, dv));
+// The workspace's family part; for a packed batch, first builds the segment
+// prefix on the device and points the map at it.
+hipError_t bind_workspace(Plan& p, const Batch& b, void* workspace, hipStream_t stream, float** fam) {
+    float* ws = static_cast<float*>(workspace);
+    if (b.packed()) {
+        int* sp = reinterpret_cast<int*>(ws);
+        const hipError_t e = la::launch_segment_prefix(b.cu_dev, b.N, b.T, p.sm.L, sp, stream);
+        if (e != hipSuccess) return e;
+        p.sm.cu = b.cu_dev;
+        p.sm.sp = sp;
+    }
+    *fam = ws + p.sp_floats;
+    return hipSuccess;
 }
 
-size_t delta_ws_bytes(int B, int H, int T, int dk, int dv, int chunk) {
-    const int HT = B * H;
-    const la::LaPlan p = plan_segments(HT, T, chunk, kDeltaTargetGroups);
-    return sizeof(float) * la::delta_ws_floats(HT, dk, dv, p);
+size_t workspace_query(const char* fn, Family f, const Batch& b, int dk, int dv, int chunk) {
+    if (b.packed() && b.N < 1) return 0;
+    Batch bb = b;
+    if (b.packed() && !bb.cu_dev) bb.cu_dev = b.cu_host;  // only its presence is checked here
+    if (check_batch(fn, bb, dk, dv, LA_BF16, chunk) != LA_OK) return 0;
+    return make_plan(f, b, dk, dv).bytes();
 }
 
 // Tags for the look-back flags of la_forward: a process-wide counter from a
@@ -116,66 +214,46 @@ la_status hip_status(const char* fn, hipError_t e) {
     return fail(LA_ERR_HIP, "%s: HIP error %d: %s", fn, (int)e, hipGetErrorString(e));
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* la_status_string(int status) {
-    switch (status) {
-        case LA_OK: return "LA_OK";
-        case LA_ERR_INVALID_ARG: return "LA_ERR_INVALID_ARG";
-        case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED";
-        case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE";
-        case LA_ERR_HIP: return "LA_ERR_HIP";
-        default: return "LA_ERR_UNKNOWN";
-    }
+Batch uniform(int B, int H, int T) {
+    Batch b;
+    b.N = B;
+    b.H = H;
+    b.T = T;
+    return b;
 }
 
-const char* la_last_error(void) { return g_err; }
-
-size_t la_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {
-    if (check_prefill("la_forward_workspace_bytes", B, H, T, dk, dv, LA_BF16, chunk) != LA_OK) return 0;
-    return la_ws_bytes(B, H, T, dk, dv, chunk);
+Batch packed(const int* cu_dev, const int* cu_host, int N, int H, int T_total) {
+    Batch b;
+    b.cu_dev = cu_dev;
+    b.cu_host = cu_host;
+    b.N = N;
+    b.H = H;
+    b.T = T_total;
+    return b;
 }
 
-size_t delta_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {
-    if (check_prefill("delta_forward_workspace_bytes", B, H, T, dk, dv, LA_BF16, chunk) != LA_OK) return 0;
-    return delta_ws_bytes(B, H, T, dk, dv, chunk);
-}
-
-size_t ssd_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {
-    if (check_prefill("ssd_forward_workspace_bytes", B, H, T, dk, dv, LA_BF16, chunk) != LA_OK) return 0;
-    return ssd_ws_bytes(B, H, T, dk, dv, chunk);
-}
-
-la_status la_forward(const void* q, const void* k, const void* v, const float* S0, const float* z0,
-                     void* o, float* S_out, float* z_out, int B, int H, int T, int dk, int dv,
-                     int dtype, float eps, int chunk, void* workspace, size_t workspace_bytes,
-                     void* stream) {
-    const char* fn = "la_forward";
+la_status la_forward_impl(const char* fn, const void* q, const void* k, const void* v, const float* S0,
+                          const float* z0, void* o, float* S_out, float* z_out, const Batch& b, int dk, int dv,
+                          int dtype, float eps, int chunk, void* workspace, size_t workspace_bytes, void* stream) {
     if (!q || !k || !v || !o) return fail(LA_ERR_INVALID_ARG, "%s: q, k, v and o must be non-NULL", fn);
     if (!(eps > 0.f) || !isfinite(eps))
         return fail(LA_ERR_INVALID_ARG, "%s: eps must be finite and > 0 (got %g)", fn, (double)eps);
-    la_status st = check_prefill(fn, B, H, T, dk, dv, dtype, chunk);
+    la_status st = check_batch(fn, b, dk, dv, dtype, chunk);
     if (st != LA_OK) return st;
     if (dtype == LA_F32 && la::la_lds_bytes(dk, dv, dtype) > 160 * 1024)
         return fail(LA_ERR_UNSUPPORTED, "%s: fp32 with dk=%d dv=%d exceeds the 160 KiB LDS", fn, dk, dv);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return fail(LA_ERR_INVALID_ARG, "%s: q, k, v and o must be 16-byte aligned", fn);
-    const size_t need = la_ws_bytes(B, H, T, dk, dv, chunk);
-    if (!workspace || workspace_bytes < need || !aligned16(workspace))
-        return fail(LA_ERR_WORKSPACE, "%s: workspace of %zu bytes (16-byte aligned) required, got %zu", fn,
-                    need, workspace ? workspace_bytes : (size_t)0);
-    const la::LaPlan plan = la::la_plan(B * H, T, dk, dv);
+    Plan plan = make_plan(kFamLA, b, dk, dv);
+    if ((st = check_workspace(fn, plan, workspace, workspace_bytes)) != LA_OK) return st;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
-    return hip_status(fn, la::launch_la_forward(q, k, v, S0, z0, o, S_out, z_out, B * H, T, dk, dv, dtype,
-                                                eps, plan, static_cast<float*>(workspace), next_tag(),
-                                                stream_capturing(hs), hs));
+    float* ws = nullptr;
+    hipError_t e = bind_workspace(plan, b, workspace, hs, &ws);
+    if (e == hipSuccess)
+        e = la::launch_la_forward(q, k, v, S0, z0, o, S_out, z_out, plan.sm, dk, dv, dtype, eps, ws, next_tag(),
+                                  stream_capturing(hs), hs);
+    return hip_status(fn, e);
 }
-
-}  // extern "C"
-
-namespace {
 
 constexpr int kKnownFlags = LA_NORMALIZE_QK | LA_BETA_SIGMOID;
 static_assert(LA_NORMALIZE_QK == la::kNormQK && LA_BETA_SIGMOID == la::kBetaSigmoid, "flag values");
@@ -183,10 +261,10 @@ static_assert(LA_NORMALIZE_QK == la::kNormQK && LA_BETA_SIGMOID == la::kBetaSigm
 // The delta-rule prefills: alpha NULL selects the ungated rule.
 la_status delta_forward_impl(const char* fn, const void* q, const void* k, const void* v, const void* beta,
                              const float* alpha, const float* S0, void* o, float* S_out, void* pred, int flags,
-                             int B, int H, int T, int dk, int dv, int dtype, int chunk, void* workspace,
+                             const Batch& b, int dk, int dv, int dtype, int chunk, void* workspace,
                              size_t workspace_bytes, void* stream) {
     if (flags & ~kKnownFlags) return fail(LA_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, flags);
-    la_status st = check_prefill(fn, B, H, T, dk, dv, dtype, chunk);
+    la_status st = check_batch(fn, b, dk, dv, dtype, chunk);
     if (st != LA_OK) return st;
     if (dtype != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "%s: only bf16 inputs are supported", fn);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
@@ -194,14 +272,35 @@ la_status delta_forward_impl(const char* fn, const void* q, const void* k, const
     if ((reinterpret_cast<uintptr_t>(beta) & 1u) || (reinterpret_cast<uintptr_t>(alpha) & 3u) ||
         (reinterpret_cast<uintptr_t>(pred) & 1u))
         return fail(LA_ERR_INVALID_ARG, "%s: beta, alpha and pred must be aligned to their element size", fn);
-    const size_t need = delta_ws_bytes(B, H, T, dk, dv, chunk);
-    if (!workspace || workspace_bytes < need || !aligned16(workspace))
-        return fail(LA_ERR_WORKSPACE, "%s: workspace of %zu bytes (16-byte aligned) required, got %zu", fn,
-                    need, workspace ? workspace_bytes : (size_t)0);
-    const la::LaPlan plan = plan_segments(B * H, T, chunk, kDeltaTargetGroups);
-    return hip_status(fn, la::launch_delta_forward(q, k, v, beta, alpha, S0, o, S_out, pred, flags, B * H, T, dk,
-                                                   dv, dtype, plan, static_cast<float*>(workspace),
-                                                   static_cast<hipStream_t>(stream)));
+    Plan plan = make_plan(kFamDelta, b, dk, dv);
+    if ((st = check_workspace(fn, plan, workspace, workspace_bytes)) != LA_OK) return st;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    float* ws = nullptr;
+    hipError_t e = bind_workspace(plan, b, workspace, hs, &ws);
+    if (e == hipSuccess)
+        e = la::launch_delta_forward(q, k, v, beta, alpha, S0, o, S_out, pred, flags, plan.sm, dk, dv, dtype, ws, hs);
+    return hip_status(fn, e);
+}
+
+la_status ssd_forward_impl(const char* fn, const void* q, const void* k, const void* v, const float* alpha,
+                           const float* S0, void* o, float* S_out, const Batch& b, int dk, int dv, int dtype,
+                           int chunk, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !alpha || !o)
+        return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, alpha and o must be non-NULL", fn);
+    la_status st = check_batch(fn, b, dk, dv, dtype, chunk);
+    if (st != LA_OK) return st;
+    if (dtype != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "%s: only bf16 inputs are supported", fn);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(LA_ERR_INVALID_ARG, "%s: q, k, v and o must be 16-byte aligned", fn);
+    if ((reinterpret_cast<uintptr_t>(alpha) & 3u) || !aligned16(S0))
+        return fail(LA_ERR_INVALID_ARG, "%s: alpha must be 4-byte and S0 16-byte aligned", fn);
+    Plan plan = make_plan(kFamSsd, b, dk, dv);
+    if ((st = check_workspace(fn, plan, workspace, workspace_bytes)) != LA_OK) return st;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    float* ws = nullptr;
+    hipError_t e = bind_workspace(plan, b, workspace, hs, &ws);
+    if (e == hipSuccess) e = la::launch_ssd_forward(q, k, v, alpha, S0, o, S_out, plan.sm, dk, dv, dtype, ws, hs);
+    return hip_status(fn, e);
 }
 
 // The decode steps of the three rules: alpha NULL = delta, beta NULL = scalar decay.
@@ -224,14 +323,83 @@ la_status delta_decode_impl(const char* fn, const void* q, const void* k, const 
 
 extern "C" {
 
+const char* la_status_string(int status) {
+    switch (status) {
+        case LA_OK: return "LA_OK";
+        case LA_ERR_INVALID_ARG: return "LA_ERR_INVALID_ARG";
+        case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED";
+        case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE";
+        case LA_ERR_HIP: return "LA_ERR_HIP";
+        default: return "LA_ERR_UNKNOWN";
+    }
+}
+
+const char* la_last_error(void) { return g_err; }
+
+// ---------------------------------------------------------------- workspace queries
+
+size_t la_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {
+    return workspace_query("la_forward_workspace_bytes", kFamLA, uniform(B, H, T), dk, dv, chunk);
+}
+
+size_t delta_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {
+    return workspace_query("delta_forward_workspace_bytes", kFamDelta, uniform(B, H, T), dk, dv, chunk);
+}
+
+size_t ssd_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {
+    return workspace_query("ssd_forward_workspace_bytes", kFamSsd, uniform(B, H, T), dk, dv, chunk);
+}
+
+size_t la_forward_packed_workspace_bytes(const int* cu_seqlens_host, int N, int H, int T_total, int dk, int dv,
+                                         int chunk) {
+    if (!cu_seqlens_host) return 0;
+    return workspace_query("la_forward_packed_workspace_bytes", kFamLA,
+                           packed(nullptr, cu_seqlens_host, N, H, T_total), dk, dv, chunk);
+}
+
+size_t delta_forward_packed_workspace_bytes(const int* cu_seqlens_host, int N, int H, int T_total, int dk, int dv,
+                                            int chunk) {
+    if (!cu_seqlens_host) return 0;
+    return workspace_query("delta_forward_packed_workspace_bytes", kFamDelta,
+                           packed(nullptr, cu_seqlens_host, N, H, T_total), dk, dv, chunk);
+}
+
+size_t ssd_forward_packed_workspace_bytes(const int* cu_seqlens_host, int N, int H, int T_total, int dk, int dv,
+                                          int chunk) {
+    if (!cu_seqlens_host) return 0;
+    return workspace_query("ssd_forward_packed_workspace_bytes", kFamSsd,
+                           packed(nullptr, cu_seqlens_host, N, H, T_total), dk, dv, chunk);
+}
+
+// ---------------------------------------------------------------- prefill
+
+la_status la_forward(const void* q, const void* k, const void* v, const float* S0, const float* z0,
+                     void* o, float* S_out, float* z_out, int B, int H, int T, int dk, int dv,
+                     int dtype, float eps, int chunk, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    return la_forward_impl("la_forward", q, k, v, S0, z0, o, S_out, z_out, uniform(B, H, T), dk, dv, dtype, eps,
+                           chunk, workspace, workspace_bytes, stream);
+}
+
+la_status la_forward_packed(const void* q, const void* k, const void* v, const int* cu_seqlens,
+                            const int* cu_seqlens_host, int N, const float* S0, const float* z0, void* o,
+                            float* S_out, float* z_out, int H, int T_total, int dk, int dv, int dtype, float eps,
+                            int chunk, void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "la_forward_packed";
+    if (!cu_seqlens_host) return fail(LA_ERR_INVALID_ARG, "%s: the host sequence offsets must be non-NULL", fn);
+    return la_forward_impl(fn, q, k, v, S0, z0, o, S_out, z_out,
+                           packed(cu_seqlens, cu_seqlens_host, N, H, T_total), dk, dv, dtype, eps, chunk, workspace,
+                           workspace_bytes, stream);
+}
+
 la_status delta_forward(const void* q, const void* k, const void* v, const void* beta, const float* S0,
                         void* o, float* S_out, int B, int H, int T, int dk, int dv, int dtype, int chunk,
                         void* workspace, size_t workspace_bytes, void* stream) {
     const char* fn = "delta_forward";
     if (!q || !k || !v || !beta || !o)
         return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, beta and o must be non-NULL", fn);
-    return delta_forward_impl(fn, q, k, v, beta, nullptr, S0, o, S_out, nullptr, 0, B, H, T, dk, dv, dtype, chunk,
-                              workspace, workspace_bytes, stream);
+    return delta_forward_impl(fn, q, k, v, beta, nullptr, S0, o, S_out, nullptr, 0, uniform(B, H, T), dk, dv, dtype,
+                              chunk, workspace, workspace_bytes, stream);
 }
 
 la_status gated_delta_forward(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
@@ -240,8 +408,8 @@ la_status gated_delta_forward(const void* q, const void* k, const void* v, const
     const char* fn = "gated_delta_forward";
     if (!q || !k || !v || !beta || !alpha || !o)
         return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, beta, alpha and o must be non-NULL", fn);
-    return delta_forward_impl(fn, q, k, v, beta, alpha, S0, o, S_out, nullptr, 0, B, H, T, dk, dv, dtype, chunk,
-                              workspace, workspace_bytes, stream);
+    return delta_forward_impl(fn, q, k, v, beta, alpha, S0, o, S_out, nullptr, 0, uniform(B, H, T), dk, dv, dtype,
+                              chunk, workspace, workspace_bytes, stream);
 }
 
 la_status delta_forward_ex(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
@@ -250,9 +418,41 @@ la_status delta_forward_ex(const void* q, const void* k, const void* v, const vo
     const char* fn = "delta_forward_ex";
     if (!q || !k || !v || !beta || !o)
         return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, beta and o must be non-NULL", fn);
-    return delta_forward_impl(fn, q, k, v, beta, alpha, S0, o, S_out, pred, flags, B, H, T, dk, dv, dtype, chunk,
-                              workspace, workspace_bytes, stream);
+    return delta_forward_impl(fn, q, k, v, beta, alpha, S0, o, S_out, pred, flags, uniform(B, H, T), dk, dv, dtype,
+                              chunk, workspace, workspace_bytes, stream);
 }
+
+la_status delta_forward_packed(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
+                               const int* cu_seqlens, const int* cu_seqlens_host, int N, const float* S0, void* o,
+                               float* S_out, void* pred, int flags, int H, int T_total, int dk, int dv, int dtype,
+                               int chunk, void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "delta_forward_packed";
+    if (!q || !k || !v || !beta || !o)
+        return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, beta and o must be non-NULL", fn);
+    if (!cu_seqlens_host) return fail(LA_ERR_INVALID_ARG, "%s: the host sequence offsets must be non-NULL", fn);
+    return delta_forward_impl(fn, q, k, v, beta, alpha, S0, o, S_out, pred, flags,
+                              packed(cu_seqlens, cu_seqlens_host, N, H, T_total), dk, dv, dtype, chunk, workspace,
+                              workspace_bytes, stream);
+}
+
+la_status ssd_forward(const void* q, const void* k, const void* v, const float* alpha, const float* S0, void* o,
+                      float* S_out, int B, int H, int T, int dk, int dv, int dtype, int chunk, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    return ssd_forward_impl("ssd_forward", q, k, v, alpha, S0, o, S_out, uniform(B, H, T), dk, dv, dtype, chunk,
+                            workspace, workspace_bytes, stream);
+}
+
+la_status ssd_forward_packed(const void* q, const void* k, const void* v, const float* alpha, const int* cu_seqlens,
+                             const int* cu_seqlens_host, int N, const float* S0, void* o, float* S_out, int H,
+                             int T_total, int dk, int dv, int dtype, int chunk, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    const char* fn = "ssd_forward_packed";
+    if (!cu_seqlens_host) return fail(LA_ERR_INVALID_ARG, "%s: the host sequence offsets must be non-NULL", fn);
+    return ssd_forward_impl(fn, q, k, v, alpha, S0, o, S_out, packed(cu_seqlens, cu_seqlens_host, N, H, T_total), dk,
+                            dv, dtype, chunk, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------- decode
 
 la_status la_decode_step(const void* q, const void* k, const void* v, float* S, float* z, void* o, int N,
                          int H, int dk, int dv, int dtype, float eps, void* stream) {
@@ -296,28 +496,6 @@ la_status delta_decode_step_ex(const void* q, const void* k, const void* v, cons
     if (!q || !k || !v || !beta || !S || !o)
         return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, beta, S and o must be non-NULL", fn);
     return delta_decode_impl(fn, q, k, v, beta, alpha, S, o, pred, flags, N, H, dk, dv, dtype, stream);
-}
-
-la_status ssd_forward(const void* q, const void* k, const void* v, const float* alpha, const float* S0, void* o,
-                      float* S_out, int B, int H, int T, int dk, int dv, int dtype, int chunk, void* workspace,
-                      size_t workspace_bytes, void* stream) {
-    const char* fn = "ssd_forward";
-    if (!q || !k || !v || !alpha || !o)
-        return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, alpha and o must be non-NULL", fn);
-    la_status st = check_prefill(fn, B, H, T, dk, dv, dtype, chunk);
-    if (st != LA_OK) return st;
-    if (dtype != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "%s: only bf16 inputs are supported", fn);
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-        return fail(LA_ERR_INVALID_ARG, "%s: q, k, v and o must be 16-byte aligned", fn);
-    if ((reinterpret_cast<uintptr_t>(alpha) & 3u) || !aligned16(S0))
-        return fail(LA_ERR_INVALID_ARG, "%s: alpha must be 4-byte and S0 16-byte aligned", fn);
-    const size_t need = ssd_ws_bytes(B, H, T, dk, dv, chunk);
-    if (!workspace || workspace_bytes < need || !aligned16(workspace))
-        return fail(LA_ERR_WORKSPACE, "%s: workspace of %zu bytes (16-byte aligned) required, got %zu", fn,
-                    need, workspace ? workspace_bytes : (size_t)0);
-    const la::LaPlan plan = la::la_plan(B * H, T, dk, dv);
-    return hip_status(fn, la::launch_ssd_forward(q, k, v, alpha, S0, o, S_out, B * H, T, dk, dv, dtype, plan,
-                                                 static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
 }
 
 la_status ssd_decode_step(const void* q, const void* k, const void* v, const float* alpha, float* S, void* o,

@@ -139,7 +139,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ beta, const float* __restrict__ alpha, bf16_t* __restrict__ o,
     const float* __restrict__ state_in, float* __restrict__ map_n, float* __restrict__ map_m,
-    float* __restrict__ S_out, bf16_t* __restrict__ pred, int flags, int T, int L, int G) {
+    float* __restrict__ S_out, bf16_t* __restrict__ pred, int flags, SegMap sm) {
     using Y = DL<DK, NS, OUT, GATED>;
     using M = Mma<bf16_t>;
     using MF = Mma<float>;
@@ -164,12 +164,19 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int w = wave_id(tid);
-    const int G1 = OUT ? G : G - 1;  // workgroups per head
-    const int head = blockIdx.x / G1, seg = blockIdx.x % G1;
-    const bf16_t* kh = k + (long)head * T * DK;
-    const bf16_t* qh = q + (long)head * T * DK;
-    const bf16_t* vh = v + (long)head * T * NS;
-    const bf16_t* bh = beta + (long)head * T;
+    // This workgroup's (head, sequence, segment).  MAP skips the last
+    // segment of every sequence; its result is the sequence's final state.
+    const int npw = OUT ? sm.NS : sm.NS - sm.N;  // workgroups per head
+    const int h = blockIdx.x / npw, wi = blockIdx.x % npw;
+    const int nseq = OUT ? sm.seq_of(wi) : sm.seq_of_inner(wi);
+    const int vs = OUT ? wi : wi + nseq;          // segment index within the head
+    const int seg = vs - sm.seg_base(nseq);       // segment index within the sequence
+    const long slot = (long)h * sm.NS + vs;       // workspace slot
+    const long row0 = h * sm.hs + sm.start(nseq); // first input row of the sequence
+    const bf16_t* kh = k + row0 * DK;
+    const bf16_t* qh = q + row0 * DK;
+    const bf16_t* vh = v + row0 * NS;
+    const bf16_t* bh = beta + row0;
 
     // this wave's state column tiles: slot j holds tile id w + 8j (if < NCT);
     // ids below NCN are columns of S (OUT) or N (MAP), the rest columns of M
@@ -186,14 +193,15 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
                 const int row = 16 * i + 4 * g + r;
                 float x = 0.f;
                 if (id < Y::NCT) {
-                    if constexpr (OUT) x = state_in[((long)(head * G + seg) * DK + row) * NS + col];
+                    if constexpr (OUT) x = state_in[(slot * DK + row) * NS + col];
                     else x = (is_m && row == col) ? 1.f : 0.f;
                 }
                 X[j][i][r] = x;
             }
     }
 
-    const int t_end = min((seg + 1) * L, T);
+    const int L = sm.L;
+    const int t_end = min((seg + 1) * L, sm.length(nseq));
     // The next chunk's rows are loaded into registers while this one is
     // processed.  Buffer resources end at the segment end: rows past it read
     // as zero with no guard (a guard would make the load's result wanted at
@@ -202,7 +210,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     const rsrc_t rq = make_rsrc(qh, (uint32_t)t_end * DK * 2);
     const rsrc_t rv = make_rsrc(vh, (uint32_t)t_end * NS * 2);
     const rsrc_t rb = make_rsrc(bh, (uint32_t)t_end * 2);
-    const rsrc_t ra = make_rsrc(GATED ? alpha + (long)head * T : nullptr, GATED ? (uint32_t)t_end * 4 : 0u);
+    const rsrc_t ra = make_rsrc(GATED ? alpha + row0 : nullptr, GATED ? (uint32_t)t_end * 4 : 0u);
     ChunkRegs<bf16_t, DK, NT> kr, qr;
     ChunkRegs<bf16_t, NS, NT> vr;
     unsigned short bnext = 0;
@@ -517,7 +525,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
                 for (int r = 0; r < 4; ++r) U[j][tt][r] -= ws_[r];
                 if constexpr (OUT) {
                     if (pred) {  // rows past the segment end are dropped by the resource
-                        const rsrc_t rp = make_rsrc(pred + (long)head * T * NS, (uint32_t)t_end * NS * 2);
+                        const rsrc_t rp = make_rsrc(pred + row0 * NS, (uint32_t)t_end * NS * 2);
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int t = 16 * tt + 4 * g + r;
@@ -532,7 +540,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
             }
             if constexpr (OUT) {
                 // outputs, second half: O^T += (beta o U)^T P^T, stored
-                bf16_t* oh = o + ((long)head * T + c0) * NS + 16 * id + 4 * g;
+                bf16_t* oh = o + (row0 + c0) * NS + 16 * id + 4 * g;
 #pragma unroll
                 for (int qt = 0; qt < 4; ++qt) {
 #pragma unroll
@@ -579,12 +587,12 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         float* dst;
         int ld, col;
         if constexpr (OUT) {
-            if (seg != G - 1 || !S_out) continue;
-            dst = S_out + (long)head * DK * NS;
+            if (seg != sm.segs(nseq) - 1 || !S_out) continue;
+            dst = S_out + ((long)nseq * sm.H + h) * DK * NS;
             ld = NS;
             col = 16 * id + li;
         } else {
-            dst = is_m ? map_m + (long)(head * G + seg) * DK * DK : map_n + (long)(head * G + seg) * DK * NS;
+            dst = is_m ? map_m + slot * DK * DK : map_n + slot * DK * NS;
             ld = is_m ? DK : NS;
             col = 16 * (is_m ? id - Y::NCN : id) + li;
         }
@@ -596,17 +604,23 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
 }
 
 // S_in(0) = S0 (or 0); S_in(g+1) = M_g S_in(g) + N_g in fp32 MFMA.  One
-// workgroup per (16-column block of the state, head); serial over segments.
+// workgroup per (16-column block of the state, sequence and head); serial
+// over the sequence's segments.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void delta_compose_kernel(const float* __restrict__ map_n,
                                                             const float* __restrict__ map_m,
                                                             const float* S0, float* __restrict__ state_in,
-                                                            int G) {
+                                                            SegMap sm) {
     constexpr int RPW = DK / 64;  // row tiles per wave
     __shared__ float Sb[DK][17];
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int w = wave_id(tid);
-    const int ct = blockIdx.x, head = blockIdx.y, col = 16 * ct + li;
+    const int ct = blockIdx.x, col = 16 * ct + li;
+    const int p = blockIdx.y, nseq = p / sm.H, h = p % sm.H;  // p = the state's index in S0
+    const long base = (long)h * sm.NS + sm.seg_base(nseq);   // slot of the sequence's first segment
+    int G = sm.segs(nseq);
+    G = G < 0 ? 0 : (G > sm.NS - sm.seg_base(nseq) ? sm.NS - sm.seg_base(nseq) : G);
+    if (G == 0) return;
     v4f acc[RPW];
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
@@ -614,16 +628,16 @@ __global__ __launch_bounds__(256) void delta_compose_kernel(const float* __restr
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * rt + 4 * g + r;
-            const float x = S0 ? S0[((long)head * DK + row) * DV + col] : 0.f;
+            const float x = S0 ? S0[((long)p * DK + row) * DV + col] : 0.f;
             acc[i][r] = x;
             Sb[row][li] = x;
-            state_in[((long)head * G * DK + row) * DV + col] = x;
+            state_in[(base * DK + row) * DV + col] = x;
         }
     }
     __syncthreads();
     for (int s = 0; s + 1 < G; ++s) {
-        const float* Mg = map_m + (long)(head * G + s) * DK * DK;
-        const float* Ng = map_n + (long)(head * G + s) * DK * DV;
+        const float* Mg = map_m + (base + s) * DK * DK;
+        const float* Ng = map_n + (base + s) * DK * DV;
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             const int rt = w * RPW + i;
@@ -650,7 +664,7 @@ __global__ __launch_bounds__(256) void delta_compose_kernel(const float* __restr
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * rt + 4 * g + r;
                 Sb[row][li] = acc[i][r];
-                state_in[(((long)head * G + s + 1) * DK + row) * DV + col] = acc[i][r];
+                state_in[((base + s + 1) * DK + row) * DV + col] = acc[i][r];
             }
         }
         __syncthreads();
@@ -660,34 +674,34 @@ __global__ __launch_bounds__(256) void delta_compose_kernel(const float* __restr
 template <int DK, int DV, bool GATED>
 hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* beta,
                         const float* alpha, const float* S0, bf16_t* o, float* S_out, bf16_t* pred, int flags,
-                        int HT, int T, const LaPlan& plan, float* ws, hipStream_t stream) {
-    const int G = plan.G, L = plan.L;
+                        const SegMap& sm, float* ws, hipStream_t stream) {
+    const size_t slots = (size_t)sm.H * sm.NS;
     float* map_n = ws;
-    float* map_m = map_n + (size_t)HT * G * DK * DV;
-    float* state_in = map_m + (size_t)HT * G * DK * DK;
+    float* map_m = map_n + slots * DK * DV;
+    float* state_in = map_m + slots * DK * DK;
     hipError_t err;
-    if (G > 1) {
-        delta_chunk_kernel<DK, DV, false, GATED><<<dim3(HT * (G - 1)), dim3(NT), 0, stream>>>(
-            q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, nullptr, flags, T, L, G);
+    if (sm.NS > sm.N) {
+        delta_chunk_kernel<DK, DV, false, GATED><<<dim3(sm.H * (sm.NS - sm.N)), dim3(NT), 0, stream>>>(
+            q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, nullptr, flags, sm);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    delta_compose_kernel<DK, DV><<<dim3(DV / 16, HT), dim3(256), 0, stream>>>(map_n, map_m, S0, state_in, G);
+    delta_compose_kernel<DK, DV><<<dim3(DV / 16, sm.N * sm.H), dim3(256), 0, stream>>>(map_n, map_m, S0, state_in,
+                                                                                      sm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    delta_chunk_kernel<DK, DV, true, GATED><<<dim3(HT * G), dim3(NT), 0, stream>>>(
-        q, k, v, beta, alpha, o, state_in, nullptr, nullptr, S_out, pred, flags, T, L, G);
+    delta_chunk_kernel<DK, DV, true, GATED><<<dim3(sm.H * sm.NS), dim3(NT), 0, stream>>>(
+        q, k, v, beta, alpha, o, state_in, nullptr, nullptr, S_out, pred, flags, sm);
     return hipGetLastError();
 }
 
 }  // namespace
 
-size_t delta_ws_floats(int HT, int dk, int dv, const LaPlan& plan) {
-    return (size_t)HT * plan.G * ((size_t)dk * dv + (size_t)dk * dk + (size_t)dk * dv);
+size_t delta_ws_floats(long slots, int dk, int dv) {
+    return (size_t)slots * ((size_t)dk * dv + (size_t)dk * dk + (size_t)dk * dv);
 }
 
 hipError_t launch_delta_forward(const void* q, const void* k, const void* v, const void* beta,
                                 const float* alpha, const float* S0, void* o, float* S_out, void* pred, int flags,
-                                int HT, int T, int dk, int dv, int dtype, const LaPlan& plan, float* ws,
-                                hipStream_t stream) {
+                                const SegMap& sm, int dk, int dv, int dtype, float* ws, hipStream_t stream) {
     if (dtype != 1) return hipErrorInvalidValue;
     const bf16_t* qb = static_cast<const bf16_t*>(q);
     const bf16_t* kb = static_cast<const bf16_t*>(k);
@@ -697,10 +711,8 @@ hipError_t launch_delta_forward(const void* q, const void* k, const void* v, con
     bf16_t* pb = static_cast<bf16_t*>(pred);
 #define DELTA_CASE(A, B)                                                                                      \
     if (dk == A && dv == B)                                                                                   \
-        return alpha ? launch_typed<A, B, true>(qb, kb, vb, bb, alpha, S0, ob, S_out, pb, flags, HT, T, plan, ws, \
-                                                stream)                                                       \
-                     : launch_typed<A, B, false>(qb, kb, vb, bb, nullptr, S0, ob, S_out, pb, flags, HT, T, plan,  \
-                                                 ws, stream);
+        return alpha ? launch_typed<A, B, true>(qb, kb, vb, bb, alpha, S0, ob, S_out, pb, flags, sm, ws, stream)   \
+                     : launch_typed<A, B, false>(qb, kb, vb, bb, nullptr, S0, ob, S_out, pb, flags, sm, ws, stream);
     DELTA_CASE(64, 64)
     DELTA_CASE(64, 128)
     DELTA_CASE(128, 64)

@@ -4,31 +4,40 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include "segments.hpp"
+
 namespace la {
 
 constexpr int kChunk = 64;  // tokens per chunk in every prefill kernel
 
 struct LaPlan {
-    int G;  // segments per head
+    int G;  // segments per sequence (uniform batches)
     int L;  // tokens per segment (a multiple of kChunk); the last may be ragged
 };
 
+// Every prefill launcher takes the (head, sequence, segment) decomposition
+// of segments.hpp; its workspaces hold one entry per (head, segment) slot,
+// H * NS slots in all.
+
 // Linear attention prefill: one fused launch (segment aggregate, look-back,
 // chunked outputs).  dtype 0 = fp32, 1 = bf16 (raw bits).  ws holds
-// la_ws_floats(...) floats: the look-back flags, then per-(head, segment)
-// aggregate and inclusive states.  tag (nonzero, < 2^62) must differ from the
-// tag of every earlier call that used ws, unless clear_flags is set (a
-// flag-clearing launch first, for launches recorded into a graph).
+// la_ws_floats(...) floats: the look-back flags, then per-slot aggregate and
+// inclusive states.  tag (nonzero, < 2^62) must differ from the tag of every
+// earlier call that used ws, unless clear_flags is set (a flag-clearing
+// launch first, for launches recorded into a graph).
 hipError_t launch_la_forward(const void* q, const void* k, const void* v,
                              const float* S0, const float* z0, void* o,
-                             float* S_out, float* z_out, int HT, int T, int dk,
-                             int dv, int dtype, float eps, const LaPlan& plan,
-                             float* ws, unsigned long long tag, bool clear_flags,
-                             hipStream_t stream);
+                             float* S_out, float* z_out, const SegMap& sm, int dk,
+                             int dv, int dtype, float eps, float* ws,
+                             unsigned long long tag, bool clear_flags, hipStream_t stream);
 size_t la_lds_bytes(int dk, int dv, int dtype);
 LaPlan la_plan(int HT, int T, int dk, int dv);
-size_t la_flag_words(int HT, int G);
-size_t la_ws_floats(int HT, int T, int dk, int dv);
+size_t la_flag_words(long slots);
+size_t la_ws_floats(long slots, int dk, int dv);
+
+// Packed batches: sp[n] = segments of sequences 0..n-1 (L tokens per
+// segment, lengths from the clamped offsets cu), n = 0..N, on the device.
+hipError_t launch_segment_prefix(const int* cu, int N, int T_total, int L, int* sp, hipStream_t stream);
 
 // Input-transform flags of the delta-rule kernels (same values as the ABI's).
 constexpr int kNormQK = 1;        // q, k rows scaled to unit L2 norm in the kernel
@@ -40,17 +49,16 @@ constexpr int kBetaSigmoid = 2;   // beta holds logits; the kernel applies a sig
 // made before each write.
 hipError_t launch_delta_forward(const void* q, const void* k, const void* v,
                                 const void* beta, const float* alpha, const float* S0,
-                                void* o, float* S_out, void* pred, int flags, int HT, int T,
-                                int dk, int dv, int dtype, const LaPlan& plan, float* ws,
-                                hipStream_t stream);
-size_t delta_ws_floats(int HT, int dk, int dv, const LaPlan& plan);
+                                void* o, float* S_out, void* pred, int flags, const SegMap& sm,
+                                int dk, int dv, int dtype, float* ws, hipStream_t stream);
+size_t delta_ws_floats(long slots, int dk, int dv);
 
 // Scalar-decay (Mamba-2 / SSD) prefill: segment maps -> elementwise
 // composition -> chunked outputs.  alpha fp32 [HT][T].  Segments as la_plan.
 hipError_t launch_ssd_forward(const void* q, const void* k, const void* v, const float* alpha,
-                              const float* S0, void* o, float* S_out, int HT, int T, int dk, int dv,
-                              int dtype, const LaPlan& plan, float* ws, hipStream_t stream);
-size_t ssd_ws_floats(int HT, int dk, int dv, const LaPlan& plan);
+                              const float* S0, void* o, float* S_out, const SegMap& sm, int dk, int dv,
+                              int dtype, float* ws, hipStream_t stream);
+size_t ssd_ws_floats(long slots, int dk, int dv);
 
 // Delta-rule decode step on a resident fp32 state (in place); alpha (fp32
 // [NH]) selects the gated rule, NULL = ungated; beta NULL with alpha given

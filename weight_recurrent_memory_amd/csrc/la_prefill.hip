@@ -14,10 +14,11 @@
 // a block of ones and S with 16 copies of z, so the denominator comes out of
 // the same MFMA chain as the numerator, in the same registers.
 //
-// Sequence parallelism: each head's tokens are cut into G segments, one
-// workgroup each.  Because the state update is additive, the state entering
-// segment g is S0 + sum_{g' < g} (segment sum of g'); workgroups find it by
-// decoupled look-back over their predecessors' published sums (one launch).
+// Sequence parallelism: the tokens of each (sequence, head) are cut into
+// segments, one workgroup each.  Because the state update is additive, the
+// state entering segment g is S0 + sum_{g' < g} (segment sum of g');
+// workgroups find it by decoupled look-back over their predecessors'
+// published sums (one launch).
 // Every flag word carries the tag of the call that wrote it, so flags left
 // by earlier calls read as absent and no clearing launch is needed.
 #include <type_traits>
@@ -54,9 +55,12 @@ struct Layout {
 
 // ------------------------------------------------------------- la_fused
 //
-// Single pass with decoupled look-back.  Workgroup b handles segment
-// b / HT of head b % HT (segment-major order, so every predecessor segment of
-// a head has a smaller block index and was dispatched earlier):
+// Single pass with decoupled look-back.  Each workgroup handles one segment
+// of one (sequence, head), numbered so that every predecessor segment of the
+// same sequence and head has a smaller block index and was dispatched
+// earlier (segment-major for a uniform batch; sequence-major for a packed
+// one, whose first segment of each sequence starts from that sequence's own
+// initial state):
 //   1. sum phi(K)^T [V | 1] over its segment (its aggregate);
 //   2. publish the aggregate (flag 1); find the state entering the segment by
 //      walking back over predecessors: an inclusive state (flag 2) ends the
@@ -377,8 +381,7 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
                                                         const float* S0, const float* z0,
                                                         TIn* __restrict__ o, float* S_out, float* z_out,
                                                         flag_t* __restrict__ flags, flag_t tag, float* __restrict__ agg,
-                                                        float* __restrict__ incl, int T, int L, int G,
-                                                        int HT, float eps) {
+                                                        float* __restrict__ incl, SegMap sm, float eps) {
     using M = Mma<TIn>;
     using op = typename M::op_t;
     using LY = Layout<TIn, DK, DV>;
@@ -390,11 +393,31 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int w = wave_id(tid);
-    const int head = blockIdx.x % HT, seg = blockIdx.x / HT;
-    const TIn* kh = k + (long)head * T * DK;
-    const TIn* vh = v + (long)head * T * DV;
-    const int t_beg = seg * L, t_end = min((seg + 1) * L, T);
-    flag_t* hflags = flags + (long)head * G;
+    // This workgroup's (head h, sequence nseq, segment seg).  Every
+    // predecessor segment of the same sequence and head has a smaller block
+    // index: uniform batches are numbered segment-major, packed ones
+    // sequence-major with the segments of a sequence consecutive.
+    int h, nseq, seg;
+    if (!sm.packed()) {
+        const int HT = sm.N * sm.H, rem = blockIdx.x % HT;
+        seg = blockIdx.x / HT;
+        nseq = rem / sm.H;
+        h = rem % sm.H;
+    } else {
+        const int vs = blockIdx.x / sm.H;
+        h = blockIdx.x % sm.H;
+        nseq = sm.seq_of(vs);
+        seg = vs - sm.seg_base(nseq);
+    }
+    const int G = sm.segs(nseq);                        // segments of this sequence
+    const long head = (long)nseq * sm.H + h;            // index of its states in S0, z0, S_out, z_out
+    const long row0 = h * sm.hs + sm.start(nseq);       // first input row of the sequence
+    const long sbase = (long)h * sm.NS + sm.seg_base(nseq);  // workspace slot of its first segment
+    const TIn* kh = k + row0 * DK;
+    const TIn* vh = v + row0 * DV;
+    const int L = sm.L;
+    const int t_beg = seg * L, t_end = min((seg + 1) * L, sm.length(nseq));
+    flag_t* hflags = flags + sbase;
 
     // element of the (dk x (dv + 1)) state held in tile (i, c), register r
     auto row_of = [&](int i, int r) { return 16 * (w * RTW + i) + 4 * g + r; };
@@ -413,10 +436,10 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
     // The first chunk of the output pass is fetched now, so its latency
     // overlaps the look-back.  Buffer resources end at the segment end: reads
     // past it are zero, writes past it are dropped.
-    const rsrc_t rq = make_rsrc(q + (long)head * T * DK, (uint32_t)t_end * DK * sizeof(TIn));
+    const rsrc_t rq = make_rsrc(q + row0 * DK, (uint32_t)t_end * DK * sizeof(TIn));
     const rsrc_t rk = make_rsrc(kh, (uint32_t)t_end * DK * sizeof(TIn));
     const rsrc_t rv = make_rsrc(vh, (uint32_t)t_end * DV * sizeof(TIn));
-    const rsrc_t ro = make_rsrc(o + (long)head * T * DV, (uint32_t)t_end * DV * sizeof(TIn));
+    const rsrc_t ro = make_rsrc(o + row0 * DV, (uint32_t)t_end * DV * sizeof(TIn));
     OutChunk<TIn, DK, DV> first;
     first.load(rq, rk, rv, t_beg, w, tid);
 
@@ -436,7 +459,7 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
             }
     using PUB = Published<DK, DV>;
     if (seg > 0 && seg + 1 < G) {
-        PUB::store(agg + ((long)head * G + seg) * E, A, w, lane);
+        PUB::store(agg + (sbase + seg) * E, A, w, lane);
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (tid == 0) store_flag(&hflags[seg], tag, kFlagAggregate);
@@ -487,7 +510,7 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
             // S_in = incl[j*] + agg[j*+1] + ... + agg[seg-1], left to right: the
             // same rounding as the left-to-right sum from S0, whatever j* is,
             // so results do not depend on timing.
-            PUB::load(incl + ((long)head * G + jstar) * E, S, w, lane);
+            PUB::load(incl + (sbase + jstar) * E, S, w, lane);
             // Aggregates in batches: every load of a batch is issued before
             // the first add, so the walk costs one memory latency per batch.
             constexpr int BATCH = 160 / (RTW * NCT * 4) >= 8 ? 8 : 160 / (RTW * NCT * 4) >= 2 ? 160 / (RTW * NCT * 4) : 1;
@@ -495,7 +518,7 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
                 v4f t[BATCH][RTW][NCT];
 #pragma unroll
                 for (int u = 0; u < BATCH; ++u)
-                    if (p + u < seg) PUB::load(agg + ((long)head * G + p + u) * E, t[u], w, lane);
+                    if (p + u < seg) PUB::load(agg + (sbase + p + u) * E, t[u], w, lane);
 #pragma unroll
                 for (int u = 0; u < BATCH; ++u)
                     if (p + u < seg) {
@@ -530,7 +553,7 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
         for (int i = 0; i < RTW; ++i)
 #pragma unroll
             for (int c = 0; c < NCT; ++c) X[i][c] = S[i][c] + A[i][c];
-        PUB::store(incl + ((long)head * G + seg) * E, X, w, lane);
+        PUB::store(incl + (sbase + seg) * E, X, w, lane);
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (tid == 0) store_flag(&hflags[seg], tag, kFlagInclusive);
@@ -566,27 +589,27 @@ __global__ void la_flags_clear_kernel(flag_t* flags, int n) {
 
 template <typename TIn, int DK, int DV>
 hipError_t launch_typed(const void* q, const void* k, const void* v, const float* S0,
-                        const float* z0, void* o, float* S_out, float* z_out, int HT, int T,
-                        float eps, const LaPlan& plan, float* ws, unsigned long long tag, bool clear_flags,
+                        const float* z0, void* o, float* S_out, float* z_out, const SegMap& sm,
+                        float eps, float* ws, unsigned long long tag, bool clear_flags,
                         hipStream_t stream) {
-    const int G = plan.G, L = plan.L;
+    const long slots = (long)sm.H * sm.NS;
     flag_t* flags = reinterpret_cast<flag_t*>(ws);
-    float* agg = ws + la_flag_words(HT, G);
-    float* incl = agg + (size_t)HT * G * (DK * DV + DK);
+    float* agg = ws + la_flag_words(slots);
+    float* incl = agg + (size_t)slots * (DK * DV + DK);
     if (clear_flags) {
-        la_flags_clear_kernel<<<dim3((HT * G + 255) / 256), dim3(256), 0, stream>>>(flags, HT * G);
+        la_flags_clear_kernel<<<dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, stream>>>(flags, (int)slots);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    la_fused_kernel<TIn, DK, DV><<<dim3(HT * G), dim3(NTHR), 0, stream>>>(
+    la_fused_kernel<TIn, DK, DV><<<dim3((unsigned)slots), dim3(NTHR), 0, stream>>>(
         static_cast<const TIn*>(q), static_cast<const TIn*>(k), static_cast<const TIn*>(v), S0, z0,
-        static_cast<TIn*>(o), S_out, z_out, flags, (flag_t)tag, agg, incl, T, L, G, HT, eps);
+        static_cast<TIn*>(o), S_out, z_out, flags, (flag_t)tag, agg, incl, sm, eps);
     return hipGetLastError();
 }
 
 }  // namespace
 
-size_t la_flag_words(int HT, int G) { return ((size_t)HT * G * 2 + 63) / 64 * 64; }  // 64-bit flags, in floats
+size_t la_flag_words(long slots) { return ((size_t)slots * 2 + 63) / 64 * 64; }  // 64-bit flags, in floats
 
 LaPlan la_plan(int HT, int T, int dk, int dv) {
     // Enough (head, segment) workgroups for two per compute unit, and segments
@@ -603,9 +626,8 @@ LaPlan la_plan(int HT, int T, int dk, int dv) {
     return p;
 }
 
-size_t la_ws_floats(int HT, int T, int dk, int dv) {
-    const LaPlan p = la_plan(HT, T, dk, dv);
-    return la_flag_words(HT, p.G) + (size_t)2 * HT * p.G * ((size_t)dk * dv + dk);
+size_t la_ws_floats(long slots, int dk, int dv) {
+    return la_flag_words(slots) + (size_t)2 * slots * ((size_t)dk * dv + dk);
 }
 
 size_t la_lds_bytes(int dk, int dv, int dtype) {
@@ -624,13 +646,12 @@ size_t la_lds_bytes(int dk, int dv, int dtype) {
 }
 
 hipError_t launch_la_forward(const void* q, const void* k, const void* v, const float* S0,
-                             const float* z0, void* o, float* S_out, float* z_out, int HT, int T,
-                             int dk, int dv, int dtype, float eps, const LaPlan& plan, float* ws,
+                             const float* z0, void* o, float* S_out, float* z_out, const SegMap& sm,
+                             int dk, int dv, int dtype, float eps, float* ws,
                              unsigned long long tag, bool clear_flags, hipStream_t stream) {
-#define LA_CASE(TY, DT, A, B)                                                                  \
-    if (dtype == DT && dk == A && dv == B)                                                     \
-        return launch_typed<TY, A, B>(q, k, v, S0, z0, o, S_out, z_out, HT, T, eps, plan, ws, \
-                                      tag, clear_flags, stream);
+#define LA_CASE(TY, DT, A, B)                                                                                \
+    if (dtype == DT && dk == A && dv == B)                                                                   \
+        return launch_typed<TY, A, B>(q, k, v, S0, z0, o, S_out, z_out, sm, eps, ws, tag, clear_flags, stream);
     LA_CASE(bf16_t, 1, 64, 64)
     LA_CASE(bf16_t, 1, 64, 128)
     LA_CASE(bf16_t, 1, 128, 64)

@@ -1,0 +1,77 @@
+// How a prefill call's tokens are cut into (head, sequence, segment) units.
+//
+// Two batch layouts share one description:
+//   uniform  q [B][H][T][d]: sequence n = batch row n, every sequence T tokens;
+//   packed   q [H][T_total][d] with sequence offsets cu[0..N] (cu[0] = 0,
+//            cu[N] = T_total): sequence n is rows cu[n] .. cu[n+1]-1 of every
+//            head, and each sequence starts from its own initial state (the
+//            per-request reset of "AIGC 基本功｜线性、循环与记忆架构-LinearMem" §05;
+//            "手撕：递推与记忆模型", "验证边界": state reset at request, batch and
+//            document boundaries).
+// In both, token t of sequence n in head h sits at row h * hs + start(n) + t
+// of the input (hs = T uniform, T_total packed; start(n) = n * H * T uniform,
+// cu[n] packed), and its initial and final states are entry n * H + h of
+// S0 / S_out.  A sequence is cut into segments of L tokens (the last one
+// ragged); sp[n] counts the segments of the sequences before n, so the
+// segments of all sequences of one head are numbered 0 .. NS - 1.
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace la {
+
+struct SegMap {
+    const int* cu;  // packed: device [N+1] sequence offsets; nullptr: uniform batch
+    const int* sp;  // packed: device [N+1] prefix sums of segments per sequence
+    int N;          // sequences (uniform: B)
+    int H;          // heads
+    int T;          // uniform: tokens per sequence; packed: T_total
+    int G;          // uniform: segments per sequence
+    int L;          // tokens per segment (a multiple of the chunk)
+    int NS;         // segments per head, all sequences
+    long hs;        // rows between consecutive heads of the input
+
+    __device__ __forceinline__ bool packed() const { return cu != nullptr; }
+    // First row (within a head) and length of sequence n.  Packed offsets are
+    // clamped into [0, T], so inconsistent offsets cannot address past the
+    // input (they give wrong, not out-of-bounds, results).
+    __device__ __forceinline__ long start(int n) const {
+        if (!packed()) return (long)n * H * T;
+        const int a = cu[n];
+        return a < 0 ? 0 : (a > T ? T : a);
+    }
+    __device__ __forceinline__ int length(int n) const {
+        if (!packed()) return T;
+        const int a = (int)start(n);
+        int b = cu[n + 1];
+        b = b < a ? a : (b > T ? T : b);
+        return b - a;
+    }
+    __device__ __forceinline__ int seg_base(int n) const { return packed() ? sp[n] : n * G; }
+    __device__ __forceinline__ int segs(int n) const { return packed() ? sp[n + 1] - sp[n] : G; }
+    // The sequence holding global segment vs (0 <= vs < NS): the largest n
+    // with seg_base(n) <= vs.
+    __device__ __forceinline__ int seq_of(int vs) const {
+        if (!packed()) return vs / G;
+        int lo = 0, hi = N - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sp[mid] <= vs) lo = mid;
+            else hi = mid - 1;
+        }
+        return lo;
+    }
+    // The sequence holding the i-th segment that is not the last of its
+    // sequence (0 <= i < NS - N): the largest n with seg_base(n) - n <= i.
+    __device__ __forceinline__ int seq_of_inner(int i) const {
+        if (!packed()) return i / (G - 1);
+        int lo = 0, hi = N - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sp[mid] - mid <= i) lo = mid;
+            else hi = mid - 1;
+        }
+        return lo;
+    }
+};
+
+}  // namespace la

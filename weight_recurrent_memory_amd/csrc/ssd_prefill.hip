@@ -93,7 +93,7 @@ __device__ __forceinline__ void stage_rows_scaled(const ChunkRegs<bf16_t, D, NTH
 template <int DK, int DV>
 __global__ __launch_bounds__(NTHR) void ssd_segment_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                                                            const float* __restrict__ alpha, float* __restrict__ map_n,
-                                                           float* __restrict__ map_l, int T, int L, int G) {
+                                                           float* __restrict__ map_l, SegMap sm) {
     using LY = SL<DK, DV>;
     using M = Mma<bf16_t>;
     typedef M::frag frag;
@@ -105,12 +105,18 @@ __global__ __launch_bounds__(NTHR) void ssd_segment_kernel(const bf16_t* __restr
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int w = wave_id(tid);
-    const int G1 = G - 1;
-    const int head = blockIdx.x / G1, seg = blockIdx.x % G1;
-    const int t0 = seg * L, t1 = min(t0 + L, T);
-    const rsrc_t rk = make_rsrc(k + (long)head * T * DK, (uint32_t)t1 * DK * 2);
-    const rsrc_t rv = make_rsrc(v + (long)head * T * DV, (uint32_t)t1 * DV * 2);
-    const rsrc_t ra = make_rsrc(alpha + (long)head * T, (uint32_t)t1 * 4);
+    // (head, sequence, segment) of this workgroup: every segment but the
+    // last of its sequence
+    const int npw = sm.NS - sm.N;
+    const int h = blockIdx.x / npw, wi = blockIdx.x % npw;
+    const int nseq = sm.seq_of_inner(wi);
+    const int vs = wi + nseq, seg = vs - sm.seg_base(nseq);
+    const long slot = (long)h * sm.NS + vs;
+    const long row0 = h * sm.hs + sm.start(nseq);
+    const int t0 = seg * sm.L, t1 = min(t0 + sm.L, sm.length(nseq));
+    const rsrc_t rk = make_rsrc(k + row0 * DK, (uint32_t)t1 * DK * 2);
+    const rsrc_t rv = make_rsrc(v + row0 * DV, (uint32_t)t1 * DV * 2);
+    const rsrc_t ra = make_rsrc(alpha + row0, (uint32_t)t1 * 4);
 
     ChunkRegs<bf16_t, DK, NTHR> kr[NPF];
     ChunkRegs<bf16_t, DV, NTHR> vr[NPF];
@@ -166,33 +172,39 @@ __global__ __launch_bounds__(NTHR) void ssd_segment_kernel(const bf16_t* __restr
         }
     }
 
-    float* dst = map_n + (long)(head * G + seg) * DK * DV;
+    float* dst = map_n + slot * DK * DV;
 #pragma unroll
     for (int i = 0; i < RTW; ++i)
 #pragma unroll
         for (int c = 0; c < NVT; ++c)
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[(16 * (w * RTW + i) + 4 * g + r) * DV + 16 * c + li] = acc[i][c][r];
-    if (tid == 0) map_l[head * G + seg] = lsum;
+    if (tid == 0) map_l[slot] = lsum;
 }
 
 // S_in(0) = S0 (or 0); S_in(g+1) = 2^(l_g) S_in(g) + N_g.  Elementwise: thread
-// i of the grid owns four consecutive state elements of one head.  The
+// i of the grid owns four consecutive state elements of one (sequence, head)
+// pair and walks that sequence's segments.  The
 // segments are taken in batches whose loads are all issued before the first
 // combine, so the serial chain costs one memory latency per batch.
 template <int E>
 __global__ __launch_bounds__(256) void ssd_compose_kernel(const float* __restrict__ map_n,
                                                           const float* __restrict__ map_l, const float* S0,
-                                                          float* __restrict__ state_in, int HT, int G) {
+                                                          float* __restrict__ state_in, SegMap sm) {
     constexpr int BATCH = 8;
     const long idx = (long)blockIdx.x * 256 + threadIdx.x;  // 4-float group
-    if (idx >= (long)HT * (E / 4)) return;
-    const int head = (int)(idx / (E / 4));
+    if (idx >= (long)sm.N * sm.H * (E / 4)) return;
+    const int p = (int)(idx / (E / 4));  // the state's index in S0: sequence * H + head
     const int e = (int)(idx % (E / 4)) * 4;
-    const float* nh = map_n + (long)head * G * E + e;
-    const float* lh = map_l + (long)head * G;
-    float* sh = state_in + (long)head * G * E + e;
-    v4f s = S0 ? *reinterpret_cast<const v4f*>(S0 + (long)head * E + e) : zero4();
+    const int nseq = p / sm.H, h = p % sm.H;
+    const long base = (long)h * sm.NS + sm.seg_base(nseq);
+    int G = sm.segs(nseq);
+    G = G < 0 ? 0 : (G > sm.NS - sm.seg_base(nseq) ? sm.NS - sm.seg_base(nseq) : G);
+    if (G == 0) return;
+    const float* nh = map_n + base * E + e;
+    const float* lh = map_l + base;
+    float* sh = state_in + base * E + e;
+    v4f s = S0 ? *reinterpret_cast<const v4f*>(S0 + (long)p * E + e) : zero4();
     *reinterpret_cast<v4f*>(sh) = s;
     for (int g0 = 0; g0 + 1 < G; g0 += BATCH) {
         v4f n[BATCH];
@@ -406,25 +418,28 @@ template <int DK, int DV>
 __global__ __launch_bounds__(NTHR) void ssd_output_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                           const bf16_t* __restrict__ v,
                                                           const float* __restrict__ alpha, bf16_t* __restrict__ o,
-                                                          const float* __restrict__ state_in, float* S_out, int T,
-                                                          int L, int G) {
+                                                          const float* __restrict__ state_in, float* S_out,
+                                                          SegMap sm) {
     using LY = SL<DK, DV>;
     constexpr int RTW = LY::RTW, NVT = LY::NVT;
     __shared__ __align__(16) __bf16 lds[LY::LDS_BYTES / 2];
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int w = wave_id(tid);
-    const int head = blockIdx.x / G, seg = blockIdx.x % G;
-    const int t_beg = seg * L, t_end = min(t_beg + L, T);
-    const rsrc_t rq = make_rsrc(q + (long)head * T * DK, (uint32_t)t_end * DK * 2);
-    const rsrc_t rk = make_rsrc(k + (long)head * T * DK, (uint32_t)t_end * DK * 2);
-    const rsrc_t rv = make_rsrc(v + (long)head * T * DV, (uint32_t)t_end * DV * 2);
-    const rsrc_t ra = make_rsrc(alpha + (long)head * T, (uint32_t)t_end * 4);
-    const rsrc_t ro = make_rsrc(o + (long)head * T * DV, (uint32_t)t_end * DV * 2);
+    const int h = blockIdx.x / sm.NS, vs = blockIdx.x % sm.NS;
+    const int nseq = sm.seq_of(vs), seg = vs - sm.seg_base(nseq);
+    const long slot = (long)h * sm.NS + vs;
+    const long row0 = h * sm.hs + sm.start(nseq);
+    const int t_beg = seg * sm.L, t_end = min(t_beg + sm.L, sm.length(nseq));
+    const rsrc_t rq = make_rsrc(q + row0 * DK, (uint32_t)t_end * DK * 2);
+    const rsrc_t rk = make_rsrc(k + row0 * DK, (uint32_t)t_end * DK * 2);
+    const rsrc_t rv = make_rsrc(v + row0 * DV, (uint32_t)t_end * DV * 2);
+    const rsrc_t ra = make_rsrc(alpha + row0, (uint32_t)t_end * 4);
+    const rsrc_t ro = make_rsrc(o + row0 * DV, (uint32_t)t_end * DV * 2);
     SsdChunk<DK, DV> first;
     first.load(rq, rk, rv, ra, t_beg, w, tid);
 
     v4f S[RTW][NVT];
-    const float* sin = state_in + (long)(head * G + seg) * DK * DV;
+    const float* sin = state_in + slot * DK * DV;
 #pragma unroll
     for (int i = 0; i < RTW; ++i)
 #pragma unroll
@@ -439,8 +454,8 @@ __global__ __launch_bounds__(NTHR) void ssd_output_kernel(const bf16_t* __restri
         default: ssd_output_pass<DK, DV, 3>(rq, rk, rv, ra, ro, t_beg, t_end, S, first, lds, tid); break;
     }
 
-    if (seg == G - 1 && S_out) {
-        float* dst = S_out + (long)head * DK * DV;
+    if (seg == sm.segs(nseq) - 1 && S_out) {
+        float* dst = S_out + ((long)nseq * sm.H + h) * DK * DV;
 #pragma unroll
         for (int i = 0; i < RTW; ++i)
 #pragma unroll
@@ -452,33 +467,34 @@ __global__ __launch_bounds__(NTHR) void ssd_output_kernel(const bf16_t* __restri
 
 template <int DK, int DV>
 hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* alpha, const float* S0,
-                        bf16_t* o, float* S_out, int HT, int T, const LaPlan& plan, float* ws, hipStream_t stream) {
-    const int G = plan.G, L = plan.L;
+                        bf16_t* o, float* S_out, const SegMap& sm, float* ws, hipStream_t stream) {
+    const size_t slots = (size_t)sm.H * sm.NS;
     constexpr int E = DK * DV;
     float* map_n = ws;
-    float* state_in = map_n + (size_t)HT * G * E;
-    float* map_l = state_in + (size_t)HT * G * E;
+    float* state_in = map_n + slots * E;
+    float* map_l = state_in + slots * E;
     hipError_t err;
-    if (G > 1) {
-        ssd_segment_kernel<DK, DV><<<dim3(HT * (G - 1)), dim3(NTHR), 0, stream>>>(k, v, alpha, map_n, map_l, T, L, G);
+    if (sm.NS > sm.N) {
+        ssd_segment_kernel<DK, DV><<<dim3(sm.H * (sm.NS - sm.N)), dim3(NTHR), 0, stream>>>(k, v, alpha, map_n, map_l,
+                                                                                          sm);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    const long groups = (long)HT * (E / 4);
+    const long groups = (long)sm.N * sm.H * (E / 4);
     ssd_compose_kernel<E><<<dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, stream>>>(map_n, map_l, S0,
-                                                                                           state_in, HT, G);
+                                                                                           state_in, sm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    ssd_output_kernel<DK, DV><<<dim3(HT * G), dim3(NTHR), 0, stream>>>(q, k, v, alpha, o, state_in, S_out, T, L, G);
+    ssd_output_kernel<DK, DV><<<dim3(sm.H * sm.NS), dim3(NTHR), 0, stream>>>(q, k, v, alpha, o, state_in, S_out, sm);
     return hipGetLastError();
 }
 
 }  // namespace
 
-size_t ssd_ws_floats(int HT, int dk, int dv, const LaPlan& plan) {
-    return (size_t)HT * plan.G * (2 * (size_t)dk * dv + 1);
+size_t ssd_ws_floats(long slots, int dk, int dv) {
+    return (size_t)slots * (2 * (size_t)dk * dv + 1);
 }
 
 hipError_t launch_ssd_forward(const void* q, const void* k, const void* v, const float* alpha, const float* S0,
-                              void* o, float* S_out, int HT, int T, int dk, int dv, int dtype, const LaPlan& plan,
+                              void* o, float* S_out, const SegMap& sm, int dk, int dv, int dtype,
                               float* ws, hipStream_t stream) {
     if (dtype != 1) return hipErrorInvalidValue;
     const bf16_t* qb = static_cast<const bf16_t*>(q);
@@ -486,7 +502,7 @@ hipError_t launch_ssd_forward(const void* q, const void* k, const void* v, const
     const bf16_t* vb = static_cast<const bf16_t*>(v);
     bf16_t* ob = static_cast<bf16_t*>(o);
 #define SSD_CASE(A, B) \
-    if (dk == A && dv == B) return launch_typed<A, B>(qb, kb, vb, alpha, S0, ob, S_out, HT, T, plan, ws, stream);
+    if (dk == A && dv == B) return launch_typed<A, B>(qb, kb, vb, alpha, S0, ob, S_out, sm, ws, stream);
     SSD_CASE(64, 64)
     SSD_CASE(64, 128)
     SSD_CASE(128, 64)
