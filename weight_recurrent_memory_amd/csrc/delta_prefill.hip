@@ -134,7 +134,7 @@ __host__ __device__ constexpr void lower_tile(int id, int& i, int& j) {
 //   S[:, c] += K^T (beta o U[:, c])
 // The shared, state-free part (A, P, T, W) is computed by all waves through
 // LDS.  MAP runs N and M in the same workgroup, so T and W are built once.
-template <int DK, int NS, bool OUT, bool GATED>
+template <int DK, int NS, bool OUT, bool GATED, bool PACKED>
 __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ beta, const float* __restrict__ alpha, bf16_t* __restrict__ o,
@@ -166,13 +166,22 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     const int w = wave_id(tid);
     // This workgroup's (head, sequence, segment).  MAP skips the last
     // segment of every sequence; its result is the sequence's final state.
-    const int npw = OUT ? sm.NS : sm.NS - sm.N;  // workgroups per head
-    const int h = blockIdx.x / npw, wi = blockIdx.x % npw;
-    const int nseq = OUT ? sm.seq_of(wi) : sm.seq_of_inner(wi);
-    const int vs = OUT ? wi : wi + nseq;          // segment index within the head
-    const int seg = vs - sm.seg_base(nseq);       // segment index within the sequence
-    const long slot = (long)h * sm.NS + vs;       // workspace slot
-    const long row0 = h * sm.hs + sm.start(nseq); // first input row of the sequence
+    int h, nseq, seg;
+    if constexpr (!PACKED) {  // (sequence, head)-major, segments consecutive
+        const int G1 = OUT ? sm.G : sm.G - 1;
+        const int vh = blockIdx.x / G1;
+        seg = blockIdx.x % G1;
+        nseq = vh / sm.H;
+        h = vh % sm.H;
+    } else {
+        const int npw = OUT ? sm.NS : sm.NS - sm.N;  // workgroups per head
+        const int wi = blockIdx.x % npw;
+        h = blockIdx.x / npw;
+        nseq = OUT ? sm.seq_of<true>(wi) : sm.seq_of_inner<true>(wi);
+        seg = (OUT ? wi : wi + nseq) - sm.seg_base<true>(nseq);
+    }
+    const long slot = sm.slot<PACKED>(nseq, h) + seg;  // workspace slot
+    const long row0 = h * sm.hs + sm.start<PACKED>(nseq); // first input row of the sequence
     const bf16_t* kh = k + row0 * DK;
     const bf16_t* qh = q + row0 * DK;
     const bf16_t* vh = v + row0 * NS;
@@ -201,7 +210,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     }
 
     const int L = sm.L;
-    const int t_end = min((seg + 1) * L, sm.length(nseq));
+    const int t_end = min((seg + 1) * L, sm.length<PACKED>(nseq));
     // The next chunk's rows are loaded into registers while this one is
     // processed.  Buffer resources end at the segment end: rows past it read
     // as zero with no guard (a guard would make the load's result wanted at
@@ -587,7 +596,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         float* dst;
         int ld, col;
         if constexpr (OUT) {
-            if (seg != sm.segs(nseq) - 1 || !S_out) continue;
+            if (seg != sm.segs<PACKED>(nseq) - 1 || !S_out) continue;
             dst = S_out + ((long)nseq * sm.H + h) * DK * NS;
             ld = NS;
             col = 16 * id + li;
@@ -606,7 +615,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
 // S_in(0) = S0 (or 0); S_in(g+1) = M_g S_in(g) + N_g in fp32 MFMA.  One
 // workgroup per (16-column block of the state, sequence and head); serial
 // over the sequence's segments.
-template <int DK, int DV>
+template <int DK, int DV, bool PACKED>
 __global__ __launch_bounds__(256) void delta_compose_kernel(const float* __restrict__ map_n,
                                                             const float* __restrict__ map_m,
                                                             const float* S0, float* __restrict__ state_in,
@@ -617,9 +626,9 @@ __global__ __launch_bounds__(256) void delta_compose_kernel(const float* __restr
     const int w = wave_id(tid);
     const int ct = blockIdx.x, col = 16 * ct + li;
     const int p = blockIdx.y, nseq = p / sm.H, h = p % sm.H;  // p = the state's index in S0
-    const long base = (long)h * sm.NS + sm.seg_base(nseq);   // slot of the sequence's first segment
-    int G = sm.segs(nseq);
-    G = G < 0 ? 0 : (G > sm.NS - sm.seg_base(nseq) ? sm.NS - sm.seg_base(nseq) : G);
+    const long base = sm.slot<PACKED>(nseq, h);  // slot of the sequence's first segment
+    int G = sm.segs<PACKED>(nseq);
+    G = G < 0 ? 0 : (G > sm.NS - sm.seg_base<PACKED>(nseq) ? sm.NS - sm.seg_base<PACKED>(nseq) : G);
     if (G == 0) return;
     v4f acc[RPW];
 #pragma unroll
@@ -671,8 +680,8 @@ __global__ __launch_bounds__(256) void delta_compose_kernel(const float* __restr
     }
 }
 
-template <int DK, int DV, bool GATED>
-hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* beta,
+template <int DK, int DV, bool GATED, bool PACKED>
+hipError_t launch_packing(const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* beta,
                         const float* alpha, const float* S0, bf16_t* o, float* S_out, bf16_t* pred, int flags,
                         const SegMap& sm, float* ws, hipStream_t stream) {
     const size_t slots = (size_t)sm.H * sm.NS;
@@ -681,16 +690,25 @@ hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const
     float* state_in = map_m + slots * DK * DK;
     hipError_t err;
     if (sm.NS > sm.N) {
-        delta_chunk_kernel<DK, DV, false, GATED><<<dim3(sm.H * (sm.NS - sm.N)), dim3(NT), 0, stream>>>(
+        delta_chunk_kernel<DK, DV, false, GATED, PACKED><<<dim3(sm.H * (sm.NS - sm.N)), dim3(NT), 0, stream>>>(
             q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, nullptr, flags, sm);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    delta_compose_kernel<DK, DV><<<dim3(DV / 16, sm.N * sm.H), dim3(256), 0, stream>>>(map_n, map_m, S0, state_in,
+    delta_compose_kernel<DK, DV, PACKED><<<dim3(DV / 16, sm.N * sm.H), dim3(256), 0, stream>>>(map_n, map_m, S0, state_in,
                                                                                       sm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    delta_chunk_kernel<DK, DV, true, GATED><<<dim3(sm.H * sm.NS), dim3(NT), 0, stream>>>(
+    delta_chunk_kernel<DK, DV, true, GATED, PACKED><<<dim3(sm.H * sm.NS), dim3(NT), 0, stream>>>(
         q, k, v, beta, alpha, o, state_in, nullptr, nullptr, S_out, pred, flags, sm);
     return hipGetLastError();
+}
+
+template <int DK, int DV, bool GATED>
+hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* beta,
+                        const float* alpha, const float* S0, bf16_t* o, float* S_out, bf16_t* pred, int flags,
+                        const SegMap& sm, float* ws, hipStream_t stream) {
+    return sm.packed()
+               ? launch_packing<DK, DV, GATED, true>(q, k, v, beta, alpha, S0, o, S_out, pred, flags, sm, ws, stream)
+               : launch_packing<DK, DV, GATED, false>(q, k, v, beta, alpha, S0, o, S_out, pred, flags, sm, ws, stream);
 }
 
 }  // namespace

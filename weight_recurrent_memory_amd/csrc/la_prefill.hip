@@ -374,7 +374,7 @@ __device__ __forceinline__ void output_pass(rsrc_t rq, rsrc_t rk, rsrc_t rv, rsr
     }
 }
 
-template <typename TIn, int DK, int DV>
+template <typename TIn, int DK, int DV, bool PACKED>
 __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ q,
                                                         const TIn* __restrict__ k,
                                                         const TIn* __restrict__ v,
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
     // index: uniform batches are numbered segment-major, packed ones
     // sequence-major with the segments of a sequence consecutive.
     int h, nseq, seg;
-    if (!sm.packed()) {
+    if constexpr (!PACKED) {
         const int HT = sm.N * sm.H, rem = blockIdx.x % HT;
         seg = blockIdx.x / HT;
         nseq = rem / sm.H;
@@ -406,17 +406,17 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
     } else {
         const int vs = blockIdx.x / sm.H;
         h = blockIdx.x % sm.H;
-        nseq = sm.seq_of(vs);
-        seg = vs - sm.seg_base(nseq);
+        nseq = sm.seq_of<PACKED>(vs);
+        seg = vs - sm.seg_base<PACKED>(nseq);
     }
-    const int G = sm.segs(nseq);                        // segments of this sequence
+    const int G = sm.segs<PACKED>(nseq);                        // segments of this sequence
     const long head = (long)nseq * sm.H + h;            // index of its states in S0, z0, S_out, z_out
-    const long row0 = h * sm.hs + sm.start(nseq);       // first input row of the sequence
-    const long sbase = (long)h * sm.NS + sm.seg_base(nseq);  // workspace slot of its first segment
+    const long row0 = h * sm.hs + sm.start<PACKED>(nseq);       // first input row of the sequence
+    const long sbase = sm.slot<PACKED>(nseq, h);  // workspace slot of its first segment
     const TIn* kh = k + row0 * DK;
     const TIn* vh = v + row0 * DV;
     const int L = sm.L;
-    const int t_beg = seg * L, t_end = min((seg + 1) * L, sm.length(nseq));
+    const int t_beg = seg * L, t_end = min((seg + 1) * L, sm.length<PACKED>(nseq));
     flag_t* hflags = flags + sbase;
 
     // element of the (dk x (dv + 1)) state held in tile (i, c), register r
@@ -601,7 +601,8 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    la_fused_kernel<TIn, DK, DV><<<dim3((unsigned)slots), dim3(NTHR), 0, stream>>>(
+    auto kern = sm.packed() ? la_fused_kernel<TIn, DK, DV, true> : la_fused_kernel<TIn, DK, DV, false>;
+    kern<<<dim3((unsigned)slots), dim3(NTHR), 0, stream>>>(
         static_cast<const TIn*>(q), static_cast<const TIn*>(k), static_cast<const TIn*>(v), S0, z0,
         static_cast<TIn*>(o), S_out, z_out, flags, (flag_t)tag, agg, incl, sm, eps);
     return hipGetLastError();

@@ -26,7 +26,7 @@ __global__ __launch_bounds__(NT) void segment_prefix_kernel(const int* __restric
     __syncthreads();
     for (int base = 0; base < N; base += NT) {
         const int n = base + tid;
-        int x = n < N ? (sm.length(n) + L - 1) / L : 0;
+        int x = n < N ? (sm.length<true>(n) + L - 1) / L : 0;
         // inclusive scan: within the wave, then across the waves' totals
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {

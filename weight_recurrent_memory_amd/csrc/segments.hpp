@@ -13,7 +13,8 @@
 // cu[n] packed), and its initial and final states are entry n * H + h of
 // S0 / S_out.  A sequence is cut into segments of L tokens (the last one
 // ragged); sp[n] counts the segments of the sequences before n, so the
-// segments of all sequences of one head are numbered 0 .. NS - 1.
+// segments of all sequences of one head are numbered 0 .. NS - 1, and the
+// call has H * NS (head, segment) units in all.
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -30,47 +31,82 @@ struct SegMap {
     int NS;         // segments per head, all sequences
     long hs;        // rows between consecutive heads of the input
 
-    __device__ __forceinline__ bool packed() const { return cu != nullptr; }
+    // Every accessor takes P = packed() as a template argument, so a uniform
+    // batch's kernels compile to plain arithmetic with no offset loads.
+    __host__ __device__ bool packed() const { return cu != nullptr; }
     // First row (within a head) and length of sequence n.  Packed offsets are
     // clamped into [0, T], so inconsistent offsets cannot address past the
     // input (they give wrong, not out-of-bounds, results).
+    template <bool P>
     __device__ __forceinline__ long start(int n) const {
-        if (!packed()) return (long)n * H * T;
-        const int a = cu[n];
-        return a < 0 ? 0 : (a > T ? T : a);
+        if constexpr (!P) {
+            return (long)n * H * T;
+        } else {
+            const int a = cu[n];
+            return a < 0 ? 0 : (a > T ? T : a);
+        }
     }
+    template <bool P>
     __device__ __forceinline__ int length(int n) const {
-        if (!packed()) return T;
-        const int a = (int)start(n);
-        int b = cu[n + 1];
-        b = b < a ? a : (b > T ? T : b);
-        return b - a;
+        if constexpr (!P) {
+            return T;
+        } else {
+            const int a = (int)start<true>(n);
+            int b = cu[n + 1];
+            b = b < a ? a : (b > T ? T : b);
+            return b - a;
+        }
     }
-    __device__ __forceinline__ int seg_base(int n) const { return packed() ? sp[n] : n * G; }
-    __device__ __forceinline__ int segs(int n) const { return packed() ? sp[n + 1] - sp[n] : G; }
+    template <bool P>
+    __device__ __forceinline__ int seg_base(int n) const {
+        if constexpr (!P) return n * G;
+        else return sp[n];
+    }
+    template <bool P>
+    __device__ __forceinline__ int segs(int n) const {
+        if constexpr (!P) return G;
+        else return sp[n + 1] - sp[n];
+    }
+    // Workspace slot of segment 0 of (sequence n, head h); a sequence's
+    // segments occupy consecutive slots.  Uniform batches keep them head by
+    // head in batch order ((n H + h) G); packed ones head-major over the
+    // global segment numbering (h NS + seg_base(n)).
+    template <bool P>
+    __device__ __forceinline__ long slot(int n, int h) const {
+        if constexpr (!P) return ((long)n * H + h) * G;
+        else return (long)h * NS + sp[n];
+    }
     // The sequence holding global segment vs (0 <= vs < NS): the largest n
     // with seg_base(n) <= vs.
+    template <bool P>
     __device__ __forceinline__ int seq_of(int vs) const {
-        if (!packed()) return vs / G;
-        int lo = 0, hi = N - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (sp[mid] <= vs) lo = mid;
-            else hi = mid - 1;
+        if constexpr (!P) {
+            return vs / G;
+        } else {
+            int lo = 0, hi = N - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (sp[mid] <= vs) lo = mid;
+                else hi = mid - 1;
+            }
+            return lo;
         }
-        return lo;
     }
     // The sequence holding the i-th segment that is not the last of its
     // sequence (0 <= i < NS - N): the largest n with seg_base(n) - n <= i.
+    template <bool P>
     __device__ __forceinline__ int seq_of_inner(int i) const {
-        if (!packed()) return i / (G - 1);
-        int lo = 0, hi = N - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (sp[mid] - mid <= i) lo = mid;
-            else hi = mid - 1;
+        if constexpr (!P) {
+            return i / (G - 1);
+        } else {
+            int lo = 0, hi = N - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (sp[mid] - mid <= i) lo = mid;
+                else hi = mid - 1;
+            }
+            return lo;
         }
-        return lo;
     }
 };
 

@@ -90,7 +90,7 @@ __device__ __forceinline__ void stage_rows_scaled(const ChunkRegs<bf16_t, D, NTH
 // gamma) V, from a zero state; l_g = the segment's sum of log2 alpha.  Wave w
 // owns dk rows 16 w RTW ..; the keys are staged already scaled by
 // gamma_C / gamma_t.  NPF chunks are in flight ahead of the one staged.
-template <int DK, int DV>
+template <int DK, int DV, bool PACKED>
 __global__ __launch_bounds__(NTHR) void ssd_segment_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                                                            const float* __restrict__ alpha, float* __restrict__ map_n,
                                                            float* __restrict__ map_l, SegMap sm) {
@@ -107,13 +107,22 @@ __global__ __launch_bounds__(NTHR) void ssd_segment_kernel(const bf16_t* __restr
     const int w = wave_id(tid);
     // (head, sequence, segment) of this workgroup: every segment but the
     // last of its sequence
-    const int npw = sm.NS - sm.N;
-    const int h = blockIdx.x / npw, wi = blockIdx.x % npw;
-    const int nseq = sm.seq_of_inner(wi);
-    const int vs = wi + nseq, seg = vs - sm.seg_base(nseq);
-    const long slot = (long)h * sm.NS + vs;
-    const long row0 = h * sm.hs + sm.start(nseq);
-    const int t0 = seg * sm.L, t1 = min(t0 + sm.L, sm.length(nseq));
+    int h, nseq, seg;
+    if constexpr (!PACKED) {  // (sequence, head)-major, segments consecutive
+        const int vh = blockIdx.x / (sm.G - 1);
+        seg = blockIdx.x % (sm.G - 1);
+        nseq = vh / sm.H;
+        h = vh % sm.H;
+    } else {
+        const int npw = sm.NS - sm.N;
+        const int wi = blockIdx.x % npw;
+        h = blockIdx.x / npw;
+        nseq = sm.seq_of_inner<true>(wi);
+        seg = wi + nseq - sm.seg_base<true>(nseq);
+    }
+    const long slot = sm.slot<PACKED>(nseq, h) + seg;
+    const long row0 = h * sm.hs + sm.start<PACKED>(nseq);
+    const int t0 = seg * sm.L, t1 = min(t0 + sm.L, sm.length<PACKED>(nseq));
     const rsrc_t rk = make_rsrc(k + row0 * DK, (uint32_t)t1 * DK * 2);
     const rsrc_t rv = make_rsrc(v + row0 * DV, (uint32_t)t1 * DV * 2);
     const rsrc_t ra = make_rsrc(alpha + row0, (uint32_t)t1 * 4);
@@ -187,7 +196,7 @@ __global__ __launch_bounds__(NTHR) void ssd_segment_kernel(const bf16_t* __restr
 // pair and walks that sequence's segments.  The
 // segments are taken in batches whose loads are all issued before the first
 // combine, so the serial chain costs one memory latency per batch.
-template <int E>
+template <int E, bool PACKED>
 __global__ __launch_bounds__(256) void ssd_compose_kernel(const float* __restrict__ map_n,
                                                           const float* __restrict__ map_l, const float* S0,
                                                           float* __restrict__ state_in, SegMap sm) {
@@ -197,9 +206,9 @@ __global__ __launch_bounds__(256) void ssd_compose_kernel(const float* __restric
     const int p = (int)(idx / (E / 4));  // the state's index in S0: sequence * H + head
     const int e = (int)(idx % (E / 4)) * 4;
     const int nseq = p / sm.H, h = p % sm.H;
-    const long base = (long)h * sm.NS + sm.seg_base(nseq);
-    int G = sm.segs(nseq);
-    G = G < 0 ? 0 : (G > sm.NS - sm.seg_base(nseq) ? sm.NS - sm.seg_base(nseq) : G);
+    const long base = sm.slot<PACKED>(nseq, h);
+    int G = sm.segs<PACKED>(nseq);
+    G = G < 0 ? 0 : (G > sm.NS - sm.seg_base<PACKED>(nseq) ? sm.NS - sm.seg_base<PACKED>(nseq) : G);
     if (G == 0) return;
     const float* nh = map_n + base * E + e;
     const float* lh = map_l + base;
@@ -414,7 +423,7 @@ __device__ __forceinline__ void ssd_output_pass(rsrc_t rq, rsrc_t rk, rsrc_t rv,
     }
 }
 
-template <int DK, int DV>
+template <int DK, int DV, bool PACKED>
 __global__ __launch_bounds__(NTHR) void ssd_output_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                           const bf16_t* __restrict__ v,
                                                           const float* __restrict__ alpha, bf16_t* __restrict__ o,
@@ -425,11 +434,21 @@ __global__ __launch_bounds__(NTHR) void ssd_output_kernel(const bf16_t* __restri
     __shared__ __align__(16) __bf16 lds[LY::LDS_BYTES / 2];
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int w = wave_id(tid);
-    const int h = blockIdx.x / sm.NS, vs = blockIdx.x % sm.NS;
-    const int nseq = sm.seq_of(vs), seg = vs - sm.seg_base(nseq);
-    const long slot = (long)h * sm.NS + vs;
-    const long row0 = h * sm.hs + sm.start(nseq);
-    const int t_beg = seg * sm.L, t_end = min(t_beg + sm.L, sm.length(nseq));
+    int h, nseq, seg;
+    if constexpr (!PACKED) {  // (sequence, head)-major, segments consecutive
+        const int vh = blockIdx.x / sm.G;
+        seg = blockIdx.x % sm.G;
+        nseq = vh / sm.H;
+        h = vh % sm.H;
+    } else {
+        const int vs = blockIdx.x % sm.NS;
+        h = blockIdx.x / sm.NS;
+        nseq = sm.seq_of<true>(vs);
+        seg = vs - sm.seg_base<true>(nseq);
+    }
+    const long slot = sm.slot<PACKED>(nseq, h) + seg;
+    const long row0 = h * sm.hs + sm.start<PACKED>(nseq);
+    const int t_beg = seg * sm.L, t_end = min(t_beg + sm.L, sm.length<PACKED>(nseq));
     const rsrc_t rq = make_rsrc(q + row0 * DK, (uint32_t)t_end * DK * 2);
     const rsrc_t rk = make_rsrc(k + row0 * DK, (uint32_t)t_end * DK * 2);
     const rsrc_t rv = make_rsrc(v + row0 * DV, (uint32_t)t_end * DV * 2);
@@ -454,7 +473,7 @@ __global__ __launch_bounds__(NTHR) void ssd_output_kernel(const bf16_t* __restri
         default: ssd_output_pass<DK, DV, 3>(rq, rk, rv, ra, ro, t_beg, t_end, S, first, lds, tid); break;
     }
 
-    if (seg == sm.segs(nseq) - 1 && S_out) {
+    if (seg == sm.segs<PACKED>(nseq) - 1 && S_out) {
         float* dst = S_out + ((long)nseq * sm.H + h) * DK * DV;
 #pragma unroll
         for (int i = 0; i < RTW; ++i)
@@ -465,8 +484,8 @@ __global__ __launch_bounds__(NTHR) void ssd_output_kernel(const bf16_t* __restri
     }
 }
 
-template <int DK, int DV>
-hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* alpha, const float* S0,
+template <int DK, int DV, bool PACKED>
+hipError_t launch_packing(const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* alpha, const float* S0,
                         bf16_t* o, float* S_out, const SegMap& sm, float* ws, hipStream_t stream) {
     const size_t slots = (size_t)sm.H * sm.NS;
     constexpr int E = DK * DV;
@@ -475,16 +494,23 @@ hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const
     float* map_l = state_in + slots * E;
     hipError_t err;
     if (sm.NS > sm.N) {
-        ssd_segment_kernel<DK, DV><<<dim3(sm.H * (sm.NS - sm.N)), dim3(NTHR), 0, stream>>>(k, v, alpha, map_n, map_l,
+        ssd_segment_kernel<DK, DV, PACKED><<<dim3(sm.H * (sm.NS - sm.N)), dim3(NTHR), 0, stream>>>(k, v, alpha, map_n, map_l,
                                                                                           sm);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     const long groups = (long)sm.N * sm.H * (E / 4);
-    ssd_compose_kernel<E><<<dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, stream>>>(map_n, map_l, S0,
+    ssd_compose_kernel<E, PACKED><<<dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, stream>>>(map_n, map_l, S0,
                                                                                            state_in, sm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    ssd_output_kernel<DK, DV><<<dim3(sm.H * sm.NS), dim3(NTHR), 0, stream>>>(q, k, v, alpha, o, state_in, S_out, sm);
+    ssd_output_kernel<DK, DV, PACKED><<<dim3(sm.H * sm.NS), dim3(NTHR), 0, stream>>>(q, k, v, alpha, o, state_in, S_out, sm);
     return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* alpha, const float* S0,
+                        bf16_t* o, float* S_out, const SegMap& sm, float* ws, hipStream_t stream) {
+    return sm.packed() ? launch_packing<DK, DV, true>(q, k, v, alpha, S0, o, S_out, sm, ws, stream)
+                       : launch_packing<DK, DV, false>(q, k, v, alpha, S0, o, S_out, sm, ws, stream);
 }
 
 }  // namespace
