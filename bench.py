@@ -12,10 +12,10 @@ The line printed is one JSON object:
   measured with HIP events on the launch stream;
 * cpu_baseline: the fp64 oracle (C, OpenMP over heads) timed on the host on
   the same workload;
-* extra: the other measured paths -- the long-stream LA workload, the delta,
-  gated delta and scalar-decay (SSD) prefills and the 1000-step decode chains
-  of the four rules (state-update GB/s) -- each with its own roofline
-  fraction.
+* extra: the other measured paths -- the long-stream LA workload, a packed
+  serving batch of mixed request lengths, the delta, gated delta and
+  scalar-decay (SSD) prefills and the 1000-step decode chains of the four
+  rules (state-update GB/s) -- each with its own roofline fraction.
 
 Inputs are synthetic (seeded, generated on the device) and rotate among
 several copies so that each step reads data evicted from the 256 MB
@@ -224,6 +224,27 @@ def bench_ssd_decode(w, lin, wl, n_steps=None):
             "gbs_wall": per * n / wall / 1e9, "gbs": per / (mean_ms * 1e-3) / 1e9}
 
 
+def bench_la_packed(w, steps, warmup, lin, wl):
+    """la_forward_packed on a serving batch of mixed request lengths."""
+    dev = torch.device("cuda:0")
+    q, k, v, cu = wl.make(w, dev)
+    cu_dev = cu.to(dev)
+    o = torch.empty((w.H, w.T, w.dv), dtype=w.dtype, device=dev)
+    S = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    z = torch.empty((w.B, w.H, w.dk), dtype=torch.float32, device=dev)
+    ws = torch.empty(lin.la_forward_packed_workspace_bytes(cu, w.H, w.dk, w.dv), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        lin.la_forward_packed(q, k, v, cu_dev, eps=1e-6, cu_seqlens_host=cu, o=o, S_out=S, z_out=z, workspace=ws)
+
+    wall, mean_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
+    nbytes = la_bytes(1, w.H, w.T, w.dk, w.dv, 2) + (w.B - 1) * w.H * (w.dk * w.dv + w.dk) * 4
+    lengths = (cu[1:] - cu[:-1]).tolist()
+    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "tokens_per_s": w.T * steps / wall,
+            "gbs": nbytes / (mean_ms * 1e-3) / 1e9, "requests": w.B, "min_len": min(lengths),
+            "max_len": max(lengths)}
+
+
 def bench_decode(w, lin, wl, n_steps=None):
     dev = torch.device("cuda:0")
     S, z, Q, K, V = wl.make(w, dev)
@@ -296,8 +317,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=4, help="input copies rotated through (cache eviction)")
-    ap.add_argument("--only", choices=["all", "la", "la_long", "delta", "gated_delta", "ssd", "decode", "delta_decode",
-                                       "gated_delta_decode", "ssd_decode"], default="all")
+    ap.add_argument("--only", choices=["all", "la", "la_long", "la_packed", "delta", "gated_delta", "ssd", "decode",
+                                       "delta_decode", "gated_delta_decode", "ssd_decode"], default="all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
@@ -328,6 +349,12 @@ def main():
         extra[wl_.name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
                            "hbm_gbs": r["gbs"], "hbm_frac": r["gbs"] / HBM_PEAK_GBS,
                            "mfma_tflops": r["tflops"], "mfma_frac": r["tflops"] / BF16_MFMA_PEAK_TFS}
+    if args.only in ("all", "la_packed"):
+        wp = wl.PACKED_LA_BF16
+        r = bench_la_packed(wp, max(3, args.steps // 2), 3, lin, wl)
+        extra[wp.name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
+                          "hbm_gbs": r["gbs"], "hbm_frac": r["gbs"] / HBM_PEAK_GBS, "requests": r["requests"],
+                          "request_len_min_max": [r["min_len"], r["max_len"]]}
     for key, wd in (("delta", wl.DELTA_BF16_PREFILL), ("gated_delta", wl.GATED_DELTA_BF16_PREFILL)):
         if args.only not in ("all", key):
             continue

@@ -56,6 +56,10 @@ SSD_BF16_PREFILL = Workload("ssd_bf16_b4_h8_t8192_d64", "ssd", 4, 8, 8192, 64, 6
 SSD_DECODE_BF16 = Workload("ssd_decode_bf16_n256_h32_d128_1000steps", "ssd_decode", 256, 32, 1000, 128, 128,
                            torch.bfloat16, 10)
 GATE_RATE = 1.0 / 16
+# A packed serving batch with the LA prefill configuration's token total
+# (4 x 8192 per head, 8 heads, d = 64): 48 requests of mixed lengths.
+PACKED_LA_BF16 = Workload("la_packed_bf16_h8_48req_32768tok_d64", "la_packed", 48, 8, 32768, 64, 64,
+                          torch.bfloat16, 12)
 
 
 def _gen(seed: int, device) -> torch.Generator:
@@ -128,6 +132,23 @@ def gates(shape, seed, device="cpu", rate=GATE_RATE):
     return torch.exp(-torch.nn.functional.softplus(_normal(shape, g, device)) * rate)
 
 
+def packed_lengths(n, total, seed):
+    """n request lengths >= 1 summing to `total`: log-normal shares (sigma
+    1), so a few long prompts and many short ones, rounded with the remainder
+    spread over the first requests."""
+    g = _gen(seed + 3000017, "cpu")
+    w = torch.exp(torch.empty(n, dtype=torch.float64).normal_(0.0, 1.0, generator=g))
+    share = (w / w.sum() * (total - n)).floor().to(torch.int64) + 1
+    rest = total - int(share.sum())
+    share[:rest] += 1
+    return share
+
+
+def packed_offsets(lengths):
+    """Sequence offsets [0, l0, l0 + l1, ...] (int32, host)."""
+    return torch.cat([torch.zeros(1, dtype=torch.int64), torch.cumsum(lengths, 0)]).to(torch.int32)
+
+
 def make(w: Workload, device="cpu"):
     """All inputs of a workload on `device`."""
     if w.kind == "la":
@@ -150,6 +171,9 @@ def make(w: Workload, device="cpu"):
         S, _ = decode_state(w.B, w.H, w.dk, w.dv, w.seed, device, std=0.1)
         return (S,) + decode_tokens(w.T, w.B, w.H, w.dk, w.dv, w.dtype, w.seed, device) + (
             gates((w.T, w.B, w.H), w.seed, device),)
+    if w.kind == "la_packed":
+        q, k, v = (x[0] for x in la_inputs(1, w.H, w.T, w.dk, w.dv, w.dtype, w.seed, device))
+        return q, k, v, packed_offsets(packed_lengths(w.B, w.T, w.seed))
     if w.kind == "gated_delta_decode":
         S, _ = decode_state(w.B, w.H, w.dk, w.dv, w.seed, device, std=0.1)
         return (S,) + delta_decode_tokens(w.T, w.B, w.H, w.dk, w.dv, w.dtype, w.seed, device) + (
