@@ -25,6 +25,12 @@ Functions and what pins them (the pins are in ``tests/test_oracle_pins.py``):
     The per-token query read o_t = S_t^T q_t is this build's reading (the
     pages print no such sequence): parity of that read is pinned only by the
     dense form and the orthonormal-key reduction.
+``la_backward`` -- the gradients of la_forward for a linear loss
+    sum dO . o + <dS_T, S_T> + <dz_T, z_T> (reverse-mode differentiation of
+    the same recurrence, per-token scalars kept, states recomputed).  Pinned
+    by central finite differences of la_forward for every input element, the
+    adjoint of the additive memory's linear map v -> o (brute force), and the
+    single-token closed forms of dv, dS0 and dz0.
 ``la_decode_step`` -- one in-place step; pinned by equality with one token of
     ``la_forward`` continued from the same state.
 ``gated_delta_forward`` / ``gated_delta_decode_step`` -- the delta rule with a
@@ -128,6 +134,8 @@ def _load():
             lib.oracle_l2_normalize_rows.restype = None
             lib.oracle_sigmoid.argtypes = [dp, dp, ctypes.c_long]
             lib.oracle_sigmoid.restype = None
+            lib.la_ref_backward.argtypes = [dp] * 13 + [i, i, i, i, i, ctypes.c_double, i, i]
+            lib.la_ref_backward.restype = None
             lib.oracle_phi.argtypes = [dp, dp, ctypes.c_long]
             lib.oracle_phi.restype = None
             lib.oracle_num_threads.argtypes = []
@@ -347,3 +355,18 @@ def delta_decode_step_ex(q, k, v, beta, S, alpha=None, normalize_qk=False, beta_
     _load().delta_ref_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S), _ptr(o), _ptr(pred),
                                      N, H, dk, dv)
     return o, S, pred
+
+
+def la_backward(q, k, v, dO, S0=None, z0=None, dS_T=None, dz_T=None, eps=1e-6, feature=PHI_ELU1, normalize=True):
+    """Gradients of L = sum dO . o + <dS_T, S_T> + <dz_T, z_T> for la_forward:
+    returns (dq, dk, dv, dS0, dz0)."""
+    q, k, v, dO, S0, z0, dS_T, dz_T = map(_f64, (q, k, v, dO, S0, z0, dS_T, dz_T))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and v.shape == (B, H, T, dv) and dO.shape == v.shape
+    dq, dkk, dvv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    dS0, dz0 = np.empty((B, H, dk, dv)), np.empty((B, H, dk))
+    _load().la_ref_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(S0), _ptr(z0), _ptr(dO), _ptr(dS_T), _ptr(dz_T),
+                            _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dS0), _ptr(dz0), B, H, T, dk, dv, float(eps),
+                            int(feature), 1 if normalize else 0)
+    return dq, dkk, dvv, dS0, dz0

@@ -365,6 +365,103 @@ void ssd_ref_decode_step(const double* q, const double* k, const double* v, cons
     }
 }
 
+/*
+ * Backward pass of la_ref_forward (reverse-mode differentiation of the same
+ * token recurrence).  [LinearMem] §03: storing every step's state makes
+ * training memory grow with the length; prefix sums, chunking and
+ * recomputation in the backward pass are the remedy.  This reference keeps
+ * only per-token scalars: a forward sweep recomputes S_t, z_t and gives the
+ * query gradients and d num_t, d den_t; a reverse sweep accumulates
+ *   G_S = dS_T + sum_{s >= t} phi(q_s) dnum_s^T,  G_z = dz_T + sum_{s >= t} phi(q_s) dden_s
+ * and gives the key and value gradients.  With the loss
+ *   L = sum_t dO_t . o_t + <dS_T, S_T> + <dz_T, z_T>:
+ *   dnum_t = dO_t / den_t,  dden_t = -(dO_t . num_t) / den_t^2   (normalize = 0: dnum = dO, dden = 0)
+ *   dphi(q_t) = S_t dnum_t + z_t dden_t
+ *   dphi(k_t) = G_S(t) v_t + G_z(t),  dv_t = G_S(t)^T phi(k_t)
+ *   dS_0 = G_S(0), dz_0 = G_z(0); d u = dphi(u) phi'(u), phi'(u) = 1 (u > 0), e^u (u <= 0).
+ * dS_T, dz_T may be NULL (zero); dS0, dz0 may be NULL (not returned).
+ */
+static double feature_grad(double u, int mode) {
+    return mode == ORACLE_PHI_IDENTITY ? 1.0 : (u > 0.0 ? 1.0 : exp(u));
+}
+
+void la_ref_backward(const double* q, const double* k, const double* v, const double* S0, const double* z0,
+                     const double* dO, const double* dS_T, const double* dz_T,
+                     double* dq, double* dk_out, double* dv_out, double* dS0, double* dz0,
+                     int B, int H, int T, int dk, int dv, double eps, int feature_mode, int normalize) {
+    const long heads = (long)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long h = 0; h < heads; ++h) {
+        double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+        double* z = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* fq = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* fk = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* num = (double*)malloc(sizeof(double) * (size_t)dv);
+        double* dnum = (double*)malloc(sizeof(double) * (size_t)T * dv);
+        double* dden = (double*)malloc(sizeof(double) * (size_t)T);
+        const double* qh = q + h * (long)T * dk;
+        const double* kh = k + h * (long)T * dk;
+        const double* vh = v + h * (long)T * dv;
+        const double* gh = dO + h * (long)T * dv;
+        for (long i = 0; i < (long)dk * dv; ++i) S[i] = S0 ? S0[h * dk * dv + i] : 0.0;
+        for (int i = 0; i < dk; ++i) z[i] = z0 ? z0[h * dk + i] : 0.0;
+        /* forward sweep: states, d num, d den and the query gradients */
+        for (int t = 0; t < T; ++t) {
+            for (int i = 0; i < dk; ++i) {
+                fk[i] = feature(kh[(long)t * dk + i], feature_mode);
+                fq[i] = feature(qh[(long)t * dk + i], feature_mode);
+            }
+            for (int i = 0; i < dk; ++i) {
+                for (int j = 0; j < dv; ++j) S[(long)i * dv + j] += fk[i] * vh[(long)t * dv + j];
+                z[i] += fk[i];
+            }
+            double den = eps;
+            for (int i = 0; i < dk; ++i) den += fq[i] * z[i];
+            double dot = 0.0;
+            for (int j = 0; j < dv; ++j) {
+                double a = 0.0;
+                for (int i = 0; i < dk; ++i) a += fq[i] * S[(long)i * dv + j];
+                num[j] = a;
+                dot += gh[(long)t * dv + j] * a;
+            }
+            for (int j = 0; j < dv; ++j)
+                dnum[(long)t * dv + j] = normalize ? gh[(long)t * dv + j] / den : gh[(long)t * dv + j];
+            dden[t] = normalize ? -dot / (den * den) : 0.0;
+            for (int i = 0; i < dk; ++i) {
+                double a = z[i] * dden[t];
+                for (int j = 0; j < dv; ++j) a += S[(long)i * dv + j] * dnum[(long)t * dv + j];
+                dq[(h * (long)T + t) * dk + i] = a * feature_grad(qh[(long)t * dk + i], feature_mode);
+            }
+        }
+        /* reverse sweep: G_S, G_z and the key and value gradients */
+        for (long i = 0; i < (long)dk * dv; ++i) S[i] = dS_T ? dS_T[h * dk * dv + i] : 0.0;  /* G_S */
+        for (int i = 0; i < dk; ++i) z[i] = dz_T ? dz_T[h * dk + i] : 0.0;                     /* G_z */
+        for (int t = T - 1; t >= 0; --t) {
+            for (int i = 0; i < dk; ++i) {
+                fq[i] = feature(qh[(long)t * dk + i], feature_mode);
+                fk[i] = feature(kh[(long)t * dk + i], feature_mode);
+            }
+            for (int i = 0; i < dk; ++i) {
+                for (int j = 0; j < dv; ++j) S[(long)i * dv + j] += fq[i] * dnum[(long)t * dv + j];
+                z[i] += fq[i] * dden[t];
+            }
+            for (int i = 0; i < dk; ++i) {
+                double a = z[i];
+                for (int j = 0; j < dv; ++j) a += S[(long)i * dv + j] * vh[(long)t * dv + j];
+                dk_out[(h * (long)T + t) * dk + i] = a * feature_grad(kh[(long)t * dk + i], feature_mode);
+            }
+            for (int j = 0; j < dv; ++j) {
+                double a = 0.0;
+                for (int i = 0; i < dk; ++i) a += S[(long)i * dv + j] * fk[i];
+                dv_out[(h * (long)T + t) * dv + j] = a;
+            }
+        }
+        if (dS0) memcpy(dS0 + h * (long)dk * dv, S, sizeof(double) * (size_t)dk * dv);
+        if (dz0) memcpy(dz0 + h * (long)dk, z, sizeof(double) * (size_t)dk);
+        free(S); free(z); free(fq); free(fk); free(num); free(dnum); free(dden);
+    }
+}
+
 /* The feature map alone, so tests can pin its branches directly. */
 void oracle_phi(const double* x, double* y, long n) {
     for (long i = 0; i < n; ++i) y[i] = phi_elu1(x[i]);

@@ -750,3 +750,67 @@ def test_transform_flags_reduce_to_the_plain_rule():
     # from a zero state the first prediction is zero
     _, _, p3 = oracle.delta_forward_ex(qn[:, :, :1], kn[:, :, :1], v[:, :, :1], np.ones((B, H, 1)))
     assert np.array_equal(p3, np.zeros_like(p3))
+
+
+# ------------------------------------------------------------------- backward
+
+def _la_loss(q, k, v, S0, z0, dO, dS_T, dz_T, feature, normalize, eps=1e-6):
+    o, S, z = oracle.la_forward(q, k, v, S0, z0, eps, feature=feature, normalize=normalize)
+    return float(np.sum(dO * o) + np.sum(dS_T * S) + np.sum(dz_T * z))
+
+
+@pytest.mark.parametrize("feature,normalize", [(oracle.PHI_ELU1, True), (oracle.PHI_IDENTITY, False),
+                                               (oracle.PHI_ELU1, False)])
+def test_la_backward_matches_central_differences(feature, normalize):
+    # Every gradient entry against (L(x + h) - L(x - h)) / 2h of the forward
+    # oracle, with a random linear loss on o, S_T and z_T.
+    rng = np.random.default_rng(100 + feature + 2 * normalize)
+    B, H, T, dk, dv = 1, 2, 9, 3, 4
+    q, k, v = rng.normal(size=(B, H, T, dk)), rng.normal(size=(B, H, T, dk)), rng.normal(size=(B, H, T, dv))
+    S0, z0 = rng.normal(size=(B, H, dk, dv)), rng.uniform(0.1, 1.0, size=(B, H, dk))
+    dO, dS_T, dz_T = rng.normal(size=(B, H, T, dv)), rng.normal(size=(B, H, dk, dv)), rng.normal(size=(B, H, dk))
+    grads = oracle.la_backward(q, k, v, dO, S0, z0, dS_T, dz_T, feature=feature, normalize=normalize)
+    inputs = [q, k, v, S0, z0]
+    h = 1e-6
+    for which, (x, g) in enumerate(zip(inputs, grads)):
+        fd = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + h
+            lp = _la_loss(*inputs, dO, dS_T, dz_T, feature, normalize)
+            x[idx] = keep - h
+            lm = _la_loss(*inputs, dO, dS_T, dz_T, feature, normalize)
+            x[idx] = keep
+            fd[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-7, err_msg=f"input {which}")
+
+
+def test_la_backward_value_gradient_is_the_adjoint_of_the_additive_map():
+    # Identity map, no normaliser: o_t = S0^T q_t + sum_{i<=t} (q_t . k_i) v_i,
+    # a linear map of v, so dv_i = sum_{t>=i} (q_t . k_i) dO_t (brute force).
+    rng = np.random.default_rng(104)
+    T, dk, dv = 15, 5, 3
+    q, k, v, dO = rng.normal(size=(T, dk)), rng.normal(size=(T, dk)), rng.normal(size=(T, dv)), rng.normal(size=(T, dv))
+    _, _, dvv, _, _ = oracle.la_backward(_h(q), _h(k), _h(v), _h(dO), feature=oracle.PHI_IDENTITY, normalize=False)
+    want = np.zeros((T, dv))
+    for i in range(T):
+        for t in range(i, T):
+            want[i] += (q[t] @ k[i]) * dO[t]
+    np.testing.assert_allclose(dvv[0, 0], want, rtol=1e-12, atol=1e-13)
+
+
+def test_la_backward_single_token_closed_form():
+    # T = 1, normalised: o = phi(q)^T (S0 + phi(k) v^T) / (phi(q) . (z0 + phi(k)) + eps),
+    # so dv_j = (phi(q) . phi(k)) dO_j / den, dS0 = phi(q) dO^T / den and
+    # dz0 = -phi(q) (dO . num) / den^2.
+    rng = np.random.default_rng(105)
+    dk, dv, eps = 4, 3, 1e-6
+    q, k, v, dO = rng.normal(size=dk), rng.normal(size=dk), rng.normal(size=dv), rng.normal(size=dv)
+    S0, z0 = rng.normal(size=(dk, dv)), rng.uniform(0.2, 1.0, size=dk)
+    fq, fk = oracle.phi(q), oracle.phi(k)
+    den = fq @ (z0 + fk) + eps
+    _, _, dvv, dS0, dz0 = oracle.la_backward(_h([q]), _h([k]), _h([v]), _h([dO]), S0[None, None], z0[None, None], eps=eps)
+    np.testing.assert_allclose(dvv[0, 0, 0], (fq @ fk) * dO / den, rtol=1e-13)
+    num = fq @ (S0 + np.outer(fk, v))
+    np.testing.assert_allclose(dS0[0, 0], np.outer(fq, dO) / den, rtol=1e-13)
+    np.testing.assert_allclose(dz0[0, 0], -fq * (dO @ num) / den ** 2, rtol=1e-12)
