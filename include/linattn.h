@@ -10,6 +10,7 @@
  *   delta_decode_step        one-token decode of the delta rule on a resident state
  *   gated_delta_decode_step  the same with a forgetting gate
  *   ssd_decode_step          one-token decode of the scalar-decay memory
+ *   la_backward              gradients of la_forward (training, with recomputation)
  * two delta-rule calls with serving options (input transforms, the
  * read-then-write prediction as an extra output): delta_forward_ex,
  * delta_decode_step_ex; and the prefills over packed batches of
@@ -251,6 +252,26 @@ la_status ssd_forward(const void* q, const void* k, const void* v, const float* 
  */
 la_status ssd_decode_step(const void* q, const void* k, const void* v, const float* alpha, float* S,
                           void* o, int N, int H, int dk, int dv, int dtype, void* stream);
+
+/*
+ * Backward pass of la_forward (training).  [LinearMem] §03: storing every
+ * step's state makes training memory grow with the length; chunking and
+ * recomputation in the backward pass remove that cost (§06: training and
+ * decoding are validated separately).  For the loss
+ *   L = sum_t dO_t . o_t + <dS_T, S_T> + <dz_T, z_T>
+ * this writes dq, dk [B][H][T][dk] and dv [B][H][T][dv] (dtype) and, if
+ * non-NULL, dS0 [B][H][dk][dv], dz0 [B][H][dk] (fp32).  q, k, v, S0, z0, eps
+ * as given to la_forward (its states are recomputed, nothing of the forward
+ * call is needed); dO [B][H][T][dv] (dtype); dS_T, dz_T fp32 or NULL (zero).
+ * Supported: dtype LA_BF16, dk, dv in {64, 128}, chunk 64.  Errors as
+ * la_forward; workspace size from la_backward_workspace_bytes.
+ */
+size_t la_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
+la_status la_backward(const void* q, const void* k, const void* v, const float* S0, const float* z0,
+                      const void* dO, const float* dS_T, const float* dz_T,
+                      void* dq, void* dk_out, void* dv_out, float* dS0, float* dz0,
+                      int B, int H, int T, int dk, int dv, int dtype, float eps, int chunk,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Packed batches ([LinearMem] §05: when a request ends only its own state is

@@ -1,0 +1,80 @@
+"""GPU parity tests of la_backward (through the C ABI) against the oracle's
+reverse-mode gradients (themselves pinned by finite differences)."""
+import pytest
+import torch
+
+import oracle
+from tests.parity import TOL, EPS, assert_parity
+from weight_recurrent_memory_amd import binding as lin
+from weight_recurrent_memory_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _inputs(B, H, T, dk, dv, seed, init):
+    q, k, v = wl.la_inputs(B, H, T, dk, dv, torch.bfloat16, seed=seed, device=DEV)
+    dO = wl.la_inputs(B, H, T, dv, dv, torch.bfloat16, seed=seed + 1, device=DEV)[0]
+    S0 = z0 = dS_T = dz_T = None
+    if init:
+        S0, z0 = wl.decode_state(B, H, dk, dv, seed=seed + 2, device=DEV, std=0.5)
+        z0 = z0.abs() + 0.1
+        dS_T, dz_T = wl.decode_state(B, H, dk, dv, seed=seed + 3, device=DEV, std=0.01)
+    return q, k, v, dO, S0, z0, dS_T, dz_T
+
+
+def _check(args, res, heads=None):
+    q, k, v, dO, S0, z0, dS_T, dz_T = args
+    B, H = q.shape[:2]
+    flat = lambda t: None if t is None else t.reshape(B * H, *t.shape[2:])
+    idx = list(range(B * H)) if heads is None else list(heads)
+    sel = lambda t: None if t is None else flat(t)[idx][None]
+    ref = oracle.la_backward(sel(q), sel(k), sel(v), sel(dO), sel(S0), sel(z0), sel(dS_T), sel(dz_T), eps=EPS)
+    tol = TOL[torch.bfloat16]
+    worst = {}
+    for name, x, r in zip(("dq", "dk", "dv", "dS0", "dz0"), res, ref):
+        worst[name] = assert_parity(sel(x), r, tol, name)
+    print("worst slice errors:", {n: f"{e:.2e}" for n, e in worst.items()})
+
+
+SHAPES = [
+    # B, H, T, dk, dv, with states
+    (1, 1, 1, 64, 64, True),
+    (1, 2, 63, 64, 64, False),
+    (2, 1, 65, 128, 128, True),
+    (1, 1, 200, 64, 128, True),
+    (1, 3, 700, 128, 64, False),
+    (2, 2, 1000, 64, 64, True),
+    (1, 2, 3000, 128, 128, True),
+    (1, 1, 4100, 64, 64, False),
+]
+
+
+@pytest.mark.parametrize("B,H,T,dk,dv,init", SHAPES)
+def test_la_backward_shapes(B, H, T, dk, dv, init):
+    print(f"la_backward B={B} H={H} T={T} dk={dk} dv={dv} init={init}", flush=True)
+    args = _inputs(B, H, T, dk, dv, seed=6000 + T, init=init)
+    q, k, v, dO, S0, z0, dS_T, dz_T = args
+    res = lin.la_backward(q, k, v, dO, S0, z0, dS_T, dz_T, eps=EPS)
+    torch.cuda.synchronize()
+    _check(args, res)
+
+
+def test_la_backward_config_sampled_heads():
+    w = wl.LA_BF16_PREFILL
+    print(f"la_backward {w.name}", flush=True)
+    args = _inputs(w.B, w.H, w.T, w.dk, w.dv, seed=61, init=False)
+    q, k, v, dO = args[:4]
+    res = lin.la_backward(q, k, v, dO, eps=EPS)
+    torch.cuda.synchronize()
+    _check(args, res, heads=(0, 17, 31))
+
+
+def test_la_backward_deterministic():
+    args = _inputs(1, 4, 2500, 64, 64, seed=62, init=True)
+    q, k, v, dO, S0, z0, dS_T, dz_T = args
+    a = lin.la_backward(q, k, v, dO, S0, z0, dS_T, dz_T, eps=EPS)
+    b = lin.la_backward(q, k, v, dO, S0, z0, dS_T, dz_T, eps=EPS)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)

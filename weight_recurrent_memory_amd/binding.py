@@ -88,6 +88,11 @@ def lib():
             L.delta_forward_packed.restype = i
             L.ssd_forward_packed.argtypes = [vp, vp, vp, fp, vp, vp, i, fp, vp, fp, i, i, i, i, i, i, vp, sz, vp]
             L.ssd_forward_packed.restype = i
+            L.la_backward_workspace_bytes.argtypes = [i, i, i, i, i, i]
+            L.la_backward_workspace_bytes.restype = sz
+            L.la_backward.argtypes = [vp, vp, vp, fp, fp, vp, fp, fp, vp, vp, vp, fp, fp, i, i, i, i, i, i,
+                                      ctypes.c_float, i, vp, sz, vp]
+            L.la_backward.restype = i
             L.la_status_string.argtypes = [i]
             L.la_status_string.restype = ctypes.c_char_p
             L.la_last_error.argtypes = []
@@ -528,3 +533,38 @@ def ssd_forward_packed(q, k, v, alpha, cu_seqlens, S0=None, chunk=CHUNK, *, cu_s
                                     _ptr(S0), _ptr(o), _ptr(S_out), H, T, dk, dv, code, int(chunk), _ptr(ws), wsb,
                                     _stream(dev)))
     return o, S_out
+
+
+def la_backward_workspace_bytes(B, H, T, dk, dv, chunk=CHUNK) -> int:
+    return int(lib().la_backward_workspace_bytes(B, H, T, dk, dv, chunk))
+
+
+def la_backward(q, k, v, dO, S0=None, z0=None, dS_T=None, dz_T=None, eps=1e-6, chunk=CHUNK, *, dq=None, dk=None,
+                dv=None, return_state_grads=True, workspace=None):
+    """Gradients of L = sum dO . o + <dS_T, S_T> + <dz_T, z_T> for la_forward
+    (bf16).  Returns (dq, dk, dv, dS0, dz0); dS0/dz0 are None when
+    return_state_grads is False."""
+    code = _dtype_code(q)
+    B, H, T, dkk = q.shape
+    dvv = v.shape[-1]
+    dev = q.device
+    _need(k, "k", q.dtype, (B, H, T, dkk), dev)
+    _need(v, "v", q.dtype, (B, H, T, dvv), dev)
+    _need(dO, "dO", q.dtype, (B, H, T, dvv), dev)
+    for t, name, shape in ((S0, "S0", (B, H, dkk, dvv)), (z0, "z0", (B, H, dkk)), (dS_T, "dS_T", (B, H, dkk, dvv)),
+                           (dz_T, "dz_T", (B, H, dkk))):
+        if t is not None:
+            _need(t, name, torch.float32, shape, dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, "dq", q.dtype, (B, H, T, dkk), dev)
+    _need(dk, "dk", q.dtype, (B, H, T, dkk), dev)
+    _need(dv, "dv", q.dtype, (B, H, T, dvv), dev)
+    dS0 = torch.empty((B, H, dkk, dvv), dtype=torch.float32, device=dev) if return_state_grads else None
+    dz0 = torch.empty((B, H, dkk), dtype=torch.float32, device=dev) if return_state_grads else None
+    ws, wsb = _workspace(la_backward_workspace_bytes(B, H, T, dkk, dvv, chunk), dev, workspace)
+    _check(lib().la_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(S0), _ptr(z0), _ptr(dO), _ptr(dS_T), _ptr(dz_T), _ptr(dq),
+                             _ptr(dk), _ptr(dv), _ptr(dS0), _ptr(dz0), B, H, T, dkk, dvv, code, float(eps), int(chunk),
+                             _ptr(ws), wsb, _stream(dev)))
+    return dq, dk, dv, dS0, dz0

@@ -452,6 +452,39 @@ la_status ssd_forward_packed(const void* q, const void* k, const void* v, const 
                             dv, dtype, chunk, workspace, workspace_bytes, stream);
 }
 
+// ---------------------------------------------------------------- backward
+
+size_t la_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {
+    if (check_batch("la_backward_workspace_bytes", uniform(B, H, T), dk, dv, LA_BF16, chunk) != LA_OK) return 0;
+    return sizeof(float) * la::la_backward_ws_floats(B * H, T, dk, dv, la::la_plan(B * H, T, dk, dv));
+}
+
+la_status la_backward(const void* q, const void* k, const void* v, const float* S0, const float* z0, const void* dO,
+                      const float* dS_T, const float* dz_T, void* dq, void* dk_out, void* dv_out, float* dS0,
+                      float* dz0, int B, int H, int T, int dk, int dv, int dtype, float eps, int chunk,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "la_backward";
+    if (!q || !k || !v || !dO || !dq || !dk_out || !dv_out)
+        return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, dO, dq, dk and dv must be non-NULL", fn);
+    if (!(eps > 0.f) || !isfinite(eps))
+        return fail(LA_ERR_INVALID_ARG, "%s: eps must be finite and > 0 (got %g)", fn, (double)eps);
+    const Batch b = uniform(B, H, T);
+    la_status st = check_batch(fn, b, dk, dv, dtype, chunk);
+    if (st != LA_OK) return st;
+    if (dtype != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "%s: only bf16 inputs are supported", fn);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(dq) || !aligned16(dk_out) ||
+        !aligned16(dv_out))
+        return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, dO, dq, dk and dv must be 16-byte aligned", fn);
+    const la::LaPlan plan = la::la_plan(B * H, T, dk, dv);
+    const size_t need = sizeof(float) * la::la_backward_ws_floats(B * H, T, dk, dv, plan);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
+        return fail(LA_ERR_WORKSPACE, "%s: workspace of %zu bytes (16-byte aligned) required, got %zu", fn, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    return hip_status(fn, la::launch_la_backward(q, k, v, S0, z0, dO, dS_T, dz_T, dq, dk_out, dv_out, dS0, dz0,
+                                                 B * H, T, dk, dv, dtype, eps, plan, static_cast<float*>(workspace),
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 // ---------------------------------------------------------------- decode
 
 la_status la_decode_step(const void* q, const void* k, const void* v, float* S, float* z, void* o, int N,

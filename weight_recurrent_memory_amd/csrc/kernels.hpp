@@ -60,6 +60,17 @@ hipError_t launch_ssd_forward(const void* q, const void* k, const void* v, const
                               int dtype, float* ws, hipStream_t stream);
 size_t ssd_ws_floats(long slots, int dk, int dv);
 
+// Backward pass of LA prefill (bf16, uniform batches): dq, dk, dv (bf16)
+// and optionally dS0, dz0 (fp32) for the loss sum dO . o + <dS_T, S_T> +
+// <dz_T, z_T>; recomputes the forward states.  ws holds
+// la_backward_ws_floats(...) floats.
+hipError_t launch_la_backward(const void* q, const void* k, const void* v, const float* S0, const float* z0,
+                              const void* dO, const float* dS_T, const float* dz_T, void* dq, void* dk, void* dv,
+                              float* dS0, float* dz0, int HT, int T, int dk_, int dv_, int dtype, float eps,
+                              const LaPlan& plan, float* ws, hipStream_t stream);
+size_t la_backward_ws_floats(int HT, int T, int dk, int dv, const LaPlan& plan);
+size_t la_backward_lds_bytes(int dk, int dv);
+
 // Delta-rule decode step on a resident fp32 state (in place); alpha (fp32
 // [NH]) selects the gated rule, NULL = ungated; beta NULL with alpha given
 // selects the scalar-decay rule (no correction).
