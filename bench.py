@@ -12,8 +12,9 @@ The line printed is one JSON object:
   measured with HIP events on the launch stream;
 * cpu_baseline: the fp64 oracle (C, OpenMP over heads) timed on the host on
   the same workload;
-* extra: the other measured paths -- the long-stream LA workload, a packed
-  serving batch of mixed request lengths, the delta, gated delta and
+* extra: the other measured paths -- the long-stream LA workload, the LA
+  backward pass on the bench workload, a packed serving batch of mixed
+  request lengths, the delta, gated delta and
   scalar-decay (SSD) prefills and the 1000-step decode chains of the four
   rules (state-update GB/s) -- each with its own roofline fraction.
 
@@ -224,6 +225,30 @@ def bench_ssd_decode(w, lin, wl, n_steps=None):
             "gbs_wall": per * n / wall / 1e9, "gbs": per / (mean_ms * 1e-3) / 1e9}
 
 
+def la_backward_bytes(B, H, T, dk, dv, el):
+    # q, k, v, dO read once; dq, dk, dv written once
+    return B * H * T * (2 * dk + 2 * dv) * el + B * H * T * (2 * dk + dv) * el
+
+
+def bench_la_backward(w, steps, warmup, copies, lin, wl):
+    """la_backward on the LA prefill workload (gradients of a random dO)."""
+    dev = torch.device("cuda:0")
+    sets = [wl.la_inputs(w.B, w.H, w.T, w.dk, w.dv, w.dtype, w.seed + 17 * i, dev)
+            + (wl.la_inputs(w.B, w.H, w.T, w.dv, w.dv, w.dtype, w.seed + 17 * i + 1, dev)[0],) for i in range(copies)]
+    grads = [tuple(torch.empty_like(x) for x in st[:3]) for st in sets]
+    ws = torch.empty(lin.la_backward_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        q, k, v, dO = sets[i % copies]
+        dq, dk, dv = grads[i % copies]
+        lin.la_backward(q, k, v, dO, eps=1e-6, dq=dq, dk=dk, dv=dv, return_state_grads=False, workspace=ws)
+
+    wall, mean_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
+    nbytes = la_backward_bytes(w.B, w.H, w.T, w.dk, w.dv, 2)
+    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "tokens_per_s": w.B * w.T * steps / wall,
+            "bytes": nbytes, "gbs": nbytes / (mean_ms * 1e-3) / 1e9}
+
+
 def bench_la_packed(w, steps, warmup, lin, wl):
     """la_forward_packed on a serving batch of mixed request lengths."""
     dev = torch.device("cuda:0")
@@ -317,8 +342,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=4, help="input copies rotated through (cache eviction)")
-    ap.add_argument("--only", choices=["all", "la", "la_long", "la_packed", "delta", "gated_delta", "ssd", "decode",
-                                       "delta_decode", "gated_delta_decode", "ssd_decode"], default="all")
+    ap.add_argument("--only", choices=["all", "la", "la_long", "la_packed", "la_backward", "delta", "gated_delta",
+                                       "ssd", "decode", "delta_decode", "gated_delta_decode", "ssd_decode"],
+                    default="all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
@@ -349,6 +375,11 @@ def main():
         extra[wl_.name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
                            "hbm_gbs": r["gbs"], "hbm_frac": r["gbs"] / HBM_PEAK_GBS,
                            "mfma_tflops": r["tflops"], "mfma_frac": r["tflops"] / BF16_MFMA_PEAK_TFS}
+    if args.only in ("all", "la_backward"):
+        r = bench_la_backward(w, max(3, args.steps // 2), 3, args.copies, lin, wl)
+        extra["la_backward_" + w.name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
+                                          "us_per_call": 1e3 * r["event_ms_mean"], "hbm_gbs": r["gbs"],
+                                          "hbm_frac": r["gbs"] / HBM_PEAK_GBS, "bytes_per_call": r["bytes"]}
     if args.only in ("all", "la_packed"):
         wp = wl.PACKED_LA_BF16
         r = bench_la_packed(wp, max(3, args.steps // 2), 3, lin, wl)

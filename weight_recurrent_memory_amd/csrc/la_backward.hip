@@ -170,7 +170,10 @@ __global__ __launch_bounds__(NT) void lab_segsum_kernel(const bf16_t* __restrict
 
 // ------------------------------------------------------------- lab_prefix / lab_suffix
 // S_in(0) = [S0 | z0] (or 0), S_in(g+1) = S_in(g) + A_g.  Thread i owns
-// element i of one head's state.
+// element i of one head's state; the segments are taken in batches whose
+// loads are all issued before the first add (one memory latency per batch).
+constexpr int kScanBatch = 8;
+
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void lab_prefix_kernel(const float* __restrict__ agg, const float* S0,
                                                          const float* z0, float* __restrict__ state_in, int HT,
@@ -179,15 +182,26 @@ __global__ __launch_bounds__(256) void lab_prefix_kernel(const float* __restrict
     const long idx = (long)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (long)HT * E) return;
     const int head = (int)(idx / E), e = (int)(idx % E);
+    const float* ah = agg + (long)head * G * E + e;
+    float* sh = state_in + (long)head * G * E + e;
     float s = e < DK * DV ? (S0 ? S0[(long)head * DK * DV + e] : 0.f) : (z0 ? z0[(long)head * DK + e - DK * DV] : 0.f);
-    for (int gi = 0; gi < G; ++gi) {
-        state_in[((long)head * G + gi) * E + e] = s;
-        if (gi + 1 < G) s += agg[((long)head * G + gi) * E + e];
+    sh[0] = s;
+    for (int g0 = 0; g0 + 1 < G; g0 += kScanBatch) {
+        float a[kScanBatch];
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u)
+            if (g0 + u + 1 < G) a[u] = ah[(long)(g0 + u) * E];
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u)
+            if (g0 + u + 1 < G) {
+                s += a[u];
+                sh[(long)(g0 + u + 1) * E] = s;
+            }
     }
 }
 
 // G_in(G-1) = [dS_T | dz_T] (or 0), G_in(g) = G_in(g+1) + Gseg(g+1); then
-// [dS_0 | dz_0] = G_in(0) + Gseg(0).
+// [dS_0 | dz_0] = G_in(0) + Gseg(0).  Batched like the prefix.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void lab_suffix_kernel(const float* __restrict__ gseg, const float* dS_T,
                                                          const float* dz_T, float* __restrict__ grad_in,
@@ -197,10 +211,20 @@ __global__ __launch_bounds__(256) void lab_suffix_kernel(const float* __restrict
     if (idx >= (long)HT * E) return;
     const int head = (int)(idx / E), e = (int)(idx % E);
     const bool sz = e < DK * DV;
+    const float* gh = gseg + (long)head * G * E + e;
+    float* oh = grad_in + (long)head * G * E + e;
     float s = sz ? (dS_T ? dS_T[(long)head * DK * DV + e] : 0.f) : (dz_T ? dz_T[(long)head * DK + e - DK * DV] : 0.f);
-    for (int gi = G - 1; gi >= 0; --gi) {
-        grad_in[((long)head * G + gi) * E + e] = s;
-        s += gseg[((long)head * G + gi) * E + e];
+    for (int g0 = G - 1; g0 >= 0; g0 -= kScanBatch) {
+        float a[kScanBatch];
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u)
+            if (g0 - u >= 0) a[u] = gh[(long)(g0 - u) * E];
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u)
+            if (g0 - u >= 0) {
+                oh[(long)(g0 - u) * E] = s;
+                s += a[u];
+            }
     }
     if (sz) {
         if (dS0) dS0[(long)head * DK * DV + e] = s;
