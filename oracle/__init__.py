@@ -31,6 +31,13 @@ Functions and what pins them (the pins are in ``tests/test_oracle_pins.py``):
     by central finite differences of la_forward for every input element, the
     adjoint of the additive memory's linear map v -> o (brute force), and the
     single-token closed forms of dv, dS0 and dz0.
+``delta_backward`` -- the gradients of the (gated) delta rule for a linear
+    loss sum dO . o + <dS_T, S_T>, by reverse-mode differentiation of the
+    token recurrence with states recomputed from 64-token checkpoints.
+    Pinned by central finite differences of the forward oracle for every
+    element of q, k, v, beta, alpha and S0, and by the orthonormal-key case,
+    where the rule is the additive memory and the value gradient is the
+    additive memory's adjoint.
 ``la_decode_step`` -- one in-place step; pinned by equality with one token of
     ``la_forward`` continued from the same state.
 ``gated_delta_forward`` / ``gated_delta_decode_step`` -- the delta rule with a
@@ -136,6 +143,8 @@ def _load():
             lib.oracle_sigmoid.restype = None
             lib.la_ref_backward.argtypes = [dp] * 13 + [i, i, i, i, i, ctypes.c_double, i, i]
             lib.la_ref_backward.restype = None
+            lib.delta_ref_backward.argtypes = [dp] * 14 + [i, i, i, i, i]
+            lib.delta_ref_backward.restype = None
             lib.oracle_phi.argtypes = [dp, dp, ctypes.c_long]
             lib.oracle_phi.restype = None
             lib.oracle_num_threads.argtypes = []
@@ -370,3 +379,19 @@ def la_backward(q, k, v, dO, S0=None, z0=None, dS_T=None, dz_T=None, eps=1e-6, f
                             _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dS0), _ptr(dz0), B, H, T, dk, dv, float(eps),
                             int(feature), 1 if normalize else 0)
     return dq, dkk, dvv, dS0, dz0
+
+
+def delta_backward(q, k, v, beta, dO, alpha=None, S0=None, dS_T=None):
+    """Gradients of L = sum dO . o + <dS_T, S_T> for the delta rule (gated
+    when alpha is given): returns (dq, dk, dv, dbeta, dalpha or None, dS0)."""
+    q, k, v, beta, dO, alpha, S0, dS_T = map(_f64, (q, k, v, beta, dO, alpha, S0, dS_T))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and v.shape == (B, H, T, dv) and dO.shape == v.shape and beta.shape == (B, H, T)
+    dq, dkk, dvv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    dbeta = np.empty((B, H, T))
+    dalpha = np.empty((B, H, T)) if alpha is not None else None
+    dS0 = np.empty((B, H, dk, dv))
+    _load().delta_ref_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S0), _ptr(dO), _ptr(dS_T),
+                               _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dbeta), _ptr(dalpha), _ptr(dS0), B, H, T, dk, dv)
+    return dq, dkk, dvv, dbeta, dalpha, dS0

@@ -462,6 +462,130 @@ void la_ref_backward(const double* q, const double* k, const double* v, const do
     }
 }
 
+/*
+ * Backward pass of the (optionally gated) delta rule, reverse-mode
+ * differentiation of the token recurrence of delta_gated_forward:
+ *   S~ = alpha_t S_{t-1},  u_t = v_t - S~^T k_t,  S_t = S~ + beta_t k_t u_t^T,  o_t = S_t^T q_t,
+ * for the loss L = sum_t dO_t . o_t + <dS_T, S_T>.  With G = dL/dS_t (running,
+ * from dS_T):
+ *   G += q_t dO_t^T,  dq_t = S_t dO_t,
+ *   dbeta_t = k_t^T G u_t,  du_t = beta_t G^T k_t,  dv_t = du_t,
+ *   dk_t = beta_t G u_t - S~ du_t,
+ *   dS~ = G - k_t du_t^T,  dalpha_t = <dS~, S_{t-1}>,  G <- alpha_t dS~.
+ * dS_0 = G at the end.  States are recomputed from checkpoints kept every 64
+ * tokens (the [LinearMem] §03 remedy for training memory), so the memory is
+ * O(T/64 dk dv + 64 dk dv) per head.  alpha NULL: the plain rule (dalpha not
+ * written); dS_T, dS0 and dalpha may be NULL.
+ */
+void delta_ref_backward(const double* q, const double* k, const double* v, const double* beta,
+                        const double* alpha, const double* S0, const double* dO, const double* dS_T,
+                        double* dq, double* dk_out, double* dv_out, double* dbeta, double* dalpha, double* dS0,
+                        int B, int H, int T, int dk, int dv) {
+    const long heads = (long)B * H;
+    const int CK = 64;
+    const int nck = (T + CK - 1) / CK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long h = 0; h < heads; ++h) {
+        const long E = (long)dk * dv;
+        double* ck = (double*)malloc(sizeof(double) * (size_t)nck * E);        /* state entering each block */
+        double* blk = (double*)malloc(sizeof(double) * (size_t)(CK + 1) * E);  /* states of one block */
+        double* us = (double*)malloc(sizeof(double) * (size_t)CK * dv);        /* its corrections */
+        double* G = (double*)malloc(sizeof(double) * (size_t)E);
+        double* dSt = (double*)malloc(sizeof(double) * (size_t)E);
+        double* du = (double*)malloc(sizeof(double) * (size_t)dv);
+        const double* qh = q + h * (long)T * dk;
+        const double* kh = k + h * (long)T * dk;
+        const double* vh = v + h * (long)T * dv;
+        const double* bh = beta + h * (long)T;
+        const double* ah = alpha ? alpha + h * (long)T : NULL;
+        const double* gh = dO + h * (long)T * dv;
+        /* forward sweep: checkpoints only */
+        for (long i = 0; i < E; ++i) blk[i] = S0 ? S0[h * E + i] : 0.0;
+        for (int t = 0; t < T; ++t) {
+            if (t % CK == 0) memcpy(ck + (long)(t / CK) * E, blk, sizeof(double) * (size_t)E);
+            const double* kt = kh + (long)t * dk;
+            if (ah) for (long i = 0; i < E; ++i) blk[i] *= ah[t];
+            for (int j = 0; j < dv; ++j) {
+                double p = 0.0;
+                for (int i = 0; i < dk; ++i) p += kt[i] * blk[(long)i * dv + j];
+                du[j] = vh[(long)t * dv + j] - p;
+            }
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j) blk[(long)i * dv + j] += bh[t] * kt[i] * du[j];
+        }
+        /* reverse sweep, block by block */
+        for (long i = 0; i < E; ++i) G[i] = dS_T ? dS_T[h * E + i] : 0.0;
+        for (int b = nck - 1; b >= 0; --b) {
+            const int t0 = b * CK, n = (T - t0) < CK ? (T - t0) : CK;
+            /* recompute the block: blk[s] = state before token t0 + s, us[s] = its correction */
+            memcpy(blk, ck + (long)b * E, sizeof(double) * (size_t)E);
+            for (int s2 = 0; s2 < n; ++s2) {
+                const int t = t0 + s2;
+                const double* kt = kh + (long)t * dk;
+                double* cur = blk + (long)s2 * E;
+                double* nxt = blk + (long)(s2 + 1) * E;
+                const double a = ah ? ah[t] : 1.0;
+                for (int j = 0; j < dv; ++j) {
+                    double p = 0.0;
+                    for (int i = 0; i < dk; ++i) p += kt[i] * a * cur[(long)i * dv + j];
+                    us[(long)s2 * dv + j] = vh[(long)t * dv + j] - p;
+                }
+                for (int i = 0; i < dk; ++i)
+                    for (int j = 0; j < dv; ++j)
+                        nxt[(long)i * dv + j] = a * cur[(long)i * dv + j] + bh[t] * kt[i] * us[(long)s2 * dv + j];
+            }
+            for (int s2 = n - 1; s2 >= 0; --s2) {
+                const int t = t0 + s2;
+                const double* kt = kh + (long)t * dk;
+                const double* qt = qh + (long)t * dk;
+                const double* prev = blk + (long)s2 * E;   /* S_{t-1} */
+                const double* post = blk + (long)(s2 + 1) * E;  /* S_t */
+                const double* ut = us + (long)s2 * dv;
+                const double a = ah ? ah[t] : 1.0;
+                /* the read o_t = S_t^T q_t */
+                for (int i = 0; i < dk; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < dv; ++j) {
+                        acc += post[(long)i * dv + j] * gh[(long)t * dv + j];
+                        G[(long)i * dv + j] += qt[i] * gh[(long)t * dv + j];
+                    }
+                    dq[(h * (long)T + t) * dk + i] = acc;
+                }
+                /* the write S_t = S~ + beta_t k_t u_t^T */
+                double db = 0.0;
+                for (int j = 0; j < dv; ++j) {
+                    double gk = 0.0;
+                    for (int i = 0; i < dk; ++i) gk += G[(long)i * dv + j] * kt[i];
+                    db += gk * ut[j];
+                    du[j] = bh[t] * gk;
+                    dv_out[(h * (long)T + t) * dv + j] = du[j];
+                }
+                dbeta[h * (long)T + t] = db;
+                for (int i = 0; i < dk; ++i) {
+                    double gu = 0.0, sd = 0.0;
+                    for (int j = 0; j < dv; ++j) {
+                        gu += G[(long)i * dv + j] * ut[j];
+                        sd += a * prev[(long)i * dv + j] * du[j];
+                    }
+                    dk_out[(h * (long)T + t) * dk + i] = bh[t] * gu - sd;
+                }
+                /* dS~ = G - k_t du^T, then through S~ = alpha_t S_{t-1} */
+                double dal = 0.0;
+                for (int i = 0; i < dk; ++i)
+                    for (int j = 0; j < dv; ++j) {
+                        const double x = G[(long)i * dv + j] - kt[i] * du[j];
+                        dSt[(long)i * dv + j] = x;
+                        dal += x * prev[(long)i * dv + j];
+                    }
+                if (dalpha && ah) dalpha[h * (long)T + t] = dal;
+                for (long i = 0; i < E; ++i) G[i] = a * dSt[i];
+            }
+        }
+        if (dS0) memcpy(dS0 + h * E, G, sizeof(double) * (size_t)E);
+        free(ck); free(blk); free(us); free(G); free(dSt); free(du);
+    }
+}
+
 /* The feature map alone, so tests can pin its branches directly. */
 void oracle_phi(const double* x, double* y, long n) {
     for (long i = 0; i < n; ++i) y[i] = phi_elu1(x[i]);

@@ -814,3 +814,84 @@ def test_la_backward_single_token_closed_form():
     num = fq @ (S0 + np.outer(fk, v))
     np.testing.assert_allclose(dS0[0, 0], np.outer(fq, dO) / den, rtol=1e-13)
     np.testing.assert_allclose(dz0[0, 0], -fq * (dO @ num) / den ** 2, rtol=1e-12)
+
+
+def _delta_loss(q, k, v, beta, alpha, S0, dO, dS_T):
+    if alpha is None:
+        o, S = oracle.delta_forward(q, k, v, beta, S0)
+    else:
+        o, S = oracle.gated_delta_forward(q, k, v, beta, alpha, S0)
+    return float(np.sum(dO * o) + np.sum(dS_T * S))
+
+
+def _unit_rows(x, norm):
+    return norm * x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_delta_backward_matches_central_differences(gated):
+    # Every gradient entry against (L(x + h) - L(x - h)) / 2h of the forward
+    # oracle; T = 70 crosses the backward's 64-token recomputation blocks.
+    rng = np.random.default_rng(110 + gated)
+    B, H, T, dk, dv = 1, 2, 70, 3, 4
+    q = rng.normal(size=(B, H, T, dk))
+    k = _unit_rows(rng.normal(size=(B, H, T, dk)), 0.9)
+    v = rng.normal(size=(B, H, T, dv))
+    beta = rng.uniform(0.1, 0.9, size=(B, H, T))
+    alpha = rng.uniform(0.8, 1.0, size=(B, H, T)) if gated else None
+    S0 = rng.normal(size=(B, H, dk, dv))
+    dO, dS_T = rng.normal(size=(B, H, T, dv)), rng.normal(size=(B, H, dk, dv))
+    dq, dkk, dvv, dbeta, dalpha, dS0 = oracle.delta_backward(q, k, v, beta, dO, alpha, S0, dS_T)
+    assert (dalpha is None) == (not gated)
+    cases = [(q, dq), (k, dkk), (v, dvv), (beta, dbeta), (S0, dS0)] + ([(alpha, dalpha)] if gated else [])
+    h = 1e-6
+    for which, (x, g) in enumerate(cases):
+        fd = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + h
+            lp = _delta_loss(q, k, v, beta, alpha, S0, dO, dS_T)
+            x[idx] = keep - h
+            lm = _delta_loss(q, k, v, beta, alpha, S0, dO, dS_T)
+            x[idx] = keep
+            fd[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(g, fd, rtol=1e-5, atol=1e-6, err_msg=f"input {which}")
+
+
+def test_delta_backward_orthonormal_keys_value_gradient_is_the_additive_adjoint():
+    # Orthonormal keys from a zero state: every correction reads zero, so
+    # o_t = sum_{i<=t} beta_i (q_t . k_i) v_i and dv_i = beta_i sum_{t>=i} (q_t . k_i) dO_t.
+    rng = np.random.default_rng(112)
+    T, dk, dv = 6, 6, 3
+    k, _ = np.linalg.qr(rng.normal(size=(dk, dk)))
+    k = k.T[:T]
+    q, v, dO = rng.normal(size=(T, dk)), rng.normal(size=(T, dv)), rng.normal(size=(T, dv))
+    beta = rng.uniform(0.2, 1.0, size=T)
+    _, _, dvv, dbeta, _, _ = oracle.delta_backward(_h(q), _h(k), _h(v), beta[None, None], _h(dO))
+    want = np.zeros((T, dv))
+    for i in range(T):
+        for t in range(i, T):
+            want[i] += beta[i] * (q[t] @ k[i]) * dO[t]
+    np.testing.assert_allclose(dvv[0, 0], want, rtol=1e-12, atol=1e-13)
+    # and dbeta_i = sum_{t>=i} (q_t . k_i) (v_i . dO_t)
+    wb = np.array([sum((q[t] @ k[i]) * (v[i] @ dO[t]) for t in range(i, T)) for i in range(T)])
+    np.testing.assert_allclose(dbeta[0, 0], wb, rtol=1e-12, atol=1e-13)
+
+
+def test_delta_backward_single_token_closed_form():
+    # T = 1: S_1 = a (I - b k k^T) S0 + b k v^T, o = S_1^T q, L = dO . o.
+    rng = np.random.default_rng(113)
+    dk, dv = 4, 3
+    q, k, v, dO = rng.normal(size=dk), rng.normal(size=dk), rng.normal(size=dv), rng.normal(size=dv)
+    S0 = rng.normal(size=(dk, dv))
+    a, b = 0.7, 0.4
+    P = np.eye(dk) - b * np.outer(k, k)
+    S1 = a * P @ S0 + b * np.outer(k, v)
+    u = v - a * S0.T @ k
+    dq, _, dvv, dbeta, dalpha, dS0 = oracle.delta_backward(
+        _h([q]), _h([k]), _h([v]), np.array([[[b]]]), _h([dO]), np.array([[[a]]]), S0[None, None])
+    np.testing.assert_allclose(dq[0, 0, 0], S1 @ dO, rtol=1e-13)
+    np.testing.assert_allclose(dvv[0, 0, 0], b * (q @ k) * dO, rtol=1e-13)
+    np.testing.assert_allclose(dbeta[0, 0, 0], (q @ k) * (u @ dO), rtol=1e-12)
+    np.testing.assert_allclose(dalpha[0, 0, 0], q @ P @ S0 @ dO, rtol=1e-12)
+    np.testing.assert_allclose(dS0[0, 0], a * np.outer(P @ q, dO), rtol=1e-12, atol=1e-14)
