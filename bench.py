@@ -249,6 +249,37 @@ def bench_la_backward(w, steps, warmup, copies, lin, wl):
             "bytes": nbytes, "gbs": nbytes / (mean_ms * 1e-3) / 1e9}
 
 
+def delta_backward_bytes(B, H, T, dk, dv, el, gated):
+    # q, k, v, dO, beta read once, dq, dk, dv written once, dbeta (fp32)
+    # written; gated: alpha read and dalpha written (fp32)
+    return (B * H * T * (2 * dk + 2 * dv + 1) * el + B * H * T * (2 * dk + dv) * el + B * H * T * 4
+            + (2 * B * H * T * 4 if gated else 0))
+
+
+def bench_delta_backward(w, steps, warmup, copies, lin, wl):
+    """delta_backward (gated for a gated workload): gradients of a random dO."""
+    dev = torch.device("cuda:0")
+    gated = w.kind == "gated_delta"
+    sets = []
+    for i in range(copies):
+        q, k, v, beta = wl.delta_inputs(w.B, w.H, w.T, w.dk, w.dv, w.dtype, w.seed + 17 * i, dev)
+        dO = wl.la_inputs(w.B, w.H, w.T, w.dv, w.dv, w.dtype, w.seed + 17 * i + 1, dev)[0]
+        alpha = wl.gates((w.B, w.H, w.T), w.seed + 17 * i, dev) if gated else None
+        sets.append((q, k, v, beta, dO, alpha))
+    grads = [tuple(torch.empty_like(x) for x in st[:3]) for st in sets]
+    ws = torch.empty(lin.delta_backward_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        q, k, v, beta, dO, alpha = sets[i % copies]
+        dq, dk, dv = grads[i % copies]
+        lin.delta_backward(q, k, v, beta, dO, alpha, dq=dq, dk=dk, dv=dv, return_state_grad=False, workspace=ws)
+
+    wall, mean_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
+    nbytes = delta_backward_bytes(w.B, w.H, w.T, w.dk, w.dv, 2, gated)
+    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "tokens_per_s": w.B * w.T * steps / wall,
+            "bytes": nbytes, "gbs": nbytes / (mean_ms * 1e-3) / 1e9}
+
+
 def bench_la_packed(w, steps, warmup, lin, wl):
     """la_forward_packed on a serving batch of mixed request lengths."""
     dev = torch.device("cuda:0")
@@ -343,7 +374,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=4, help="input copies rotated through (cache eviction)")
     ap.add_argument("--only", choices=["all", "la", "la_long", "la_packed", "la_backward", "delta", "gated_delta",
-                                       "ssd", "decode", "delta_decode", "gated_delta_decode", "ssd_decode"],
+                                       "delta_backward", "ssd", "decode", "delta_decode", "gated_delta_decode",
+                                       "ssd_decode"],
                     default="all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -396,6 +428,12 @@ def main():
                               "mfma_tflops": r["tflops"], "mfma_frac": r["tflops"] / BF16_MFMA_PEAK_TFS}
         except lin.LinAttnError as e:
             extra[wd.name] = {"error": str(e)}
+    if args.only in ("all", "delta_backward"):
+        for wd in (wl.DELTA_BF16_PREFILL, wl.GATED_DELTA_BF16_PREFILL):
+            r = bench_delta_backward(wd, max(3, args.steps // 10), 2, 2, lin, wl)
+            extra["delta_backward_" + wd.name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
+                                                  "us_per_call": 1e3 * r["event_ms_mean"], "hbm_gbs": r["gbs"],
+                                                  "hbm_frac": r["gbs"] / HBM_PEAK_GBS, "bytes_per_call": r["bytes"]}
     if args.only in ("all", "ssd"):
         ws_ = wl.SSD_BF16_PREFILL
         r = bench_ssd(ws_, max(3, args.steps // 2), 3, args.copies, lin, wl)

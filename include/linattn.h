@@ -11,6 +11,7 @@
  *   gated_delta_decode_step  the same with a forgetting gate
  *   ssd_decode_step          one-token decode of the scalar-decay memory
  *   la_backward              gradients of la_forward (training, with recomputation)
+ *   delta_backward           gradients of delta_forward / gated_delta_forward
  * two delta-rule calls with serving options (input transforms, the
  * read-then-write prediction as an extra output): delta_forward_ex,
  * delta_decode_step_ex; and the prefills over packed batches of
@@ -272,6 +273,29 @@ la_status la_backward(const void* q, const void* k, const void* v, const float* 
                       void* dq, void* dk_out, void* dv_out, float* dS0, float* dz0,
                       int B, int H, int T, int dk, int dv, int dtype, float eps, int chunk,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Gradients of delta_forward (alpha NULL) or gated_delta_forward (alpha
+ * given) for the linear loss L = sum_t dO_t . o_t + <dS_T, S_T>:
+ * [LinearMem] §03 (the corrective write, its decayed variant, and training
+ * by chunks with only chunk-boundary states kept and the rest recomputed).
+ * Inputs as in the forward call (q, k, v, beta bf16; alpha fp32 [B][H][T] or
+ * NULL; S0 fp32 or NULL = zero); dO bf16 [B][H][T][dv]; dS_T fp32
+ * [B][H][dk][dv] or NULL = zero.  Outputs: dq, dk_out [B][H][T][dk] and
+ * dv_out [B][H][T][dv] (bf16); dbeta fp32 [B][H][T]; dalpha fp32 [B][H][T],
+ * required exactly when alpha is given (the forward clamps log alpha_t at
+ * -20, so a gate below e^-20 gets gradient 0); dS0 fp32 [B][H][dk][dv] or
+ * NULL.  Every output is overwritten.  bf16 only; uniform batches only.
+ * The workspace (delta_backward_workspace_bytes) holds the forward's
+ * segment arrays plus every chunk's entering state and leaving state
+ * gradient (bf16), 4 * B * H * ceil(T / 64) * dk * dv bytes of it.
+ */
+size_t delta_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
+la_status delta_backward(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
+                         const float* S0, const void* dO, const float* dS_T,
+                         void* dq, void* dk_out, void* dv_out, float* dbeta, float* dalpha, float* dS0,
+                         int B, int H, int T, int dk, int dv, int dtype, int chunk,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Packed batches ([LinearMem] §05: when a request ends only its own state is

@@ -28,7 +28,8 @@ def test_header_declares_the_operations():
     fns = _declared_functions()
     for name in ("la_forward", "delta_forward", "la_decode_step", "delta_decode_step", "gated_delta_forward",
                  "gated_delta_decode_step", "ssd_forward", "ssd_decode_step", "delta_forward_ex",
-                 "delta_decode_step_ex", "la_forward_packed", "delta_forward_packed", "ssd_forward_packed"):
+                 "delta_decode_step_ex", "la_forward_packed", "delta_forward_packed", "ssd_forward_packed",
+                 "la_backward", "delta_backward"):
         assert name in fns
 
 
@@ -264,6 +265,52 @@ def test_packed_workspace_queries_and_rejects():
                                 None) == ST["INVALID_ARG"]  # alpha NULL
 
 
+def _lab(**kw):
+    a = dict(q=P, k=P, v=P, S0=None, z0=None, dO=P, dS_T=None, dz_T=None, dq=P, dk_out=P, dv_out=P, dS0=None,
+             dz0=None, B=1, H=1, T=8, dk=64, dv=64, dtype=1, eps=1e-6, chunk=64, ws=P, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lin.lib().la_backward(a["q"], a["k"], a["v"], a["S0"], a["z0"], a["dO"], a["dS_T"], a["dz_T"], a["dq"],
+                                 a["dk_out"], a["dv_out"], a["dS0"], a["dz0"], a["B"], a["H"], a["T"], a["dk"],
+                                 a["dv"], a["dtype"], a["eps"], a["chunk"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dO=None), "INVALID_ARG"), (dict(dq=None), "INVALID_ARG"), (dict(T=0), "INVALID_ARG"),
+    (dict(eps=0.0), "INVALID_ARG"), (dict(dtype=5), "INVALID_ARG"), (dict(dtype=0), "UNSUPPORTED"),
+    (dict(dk=96), "UNSUPPORTED"), (dict(dv_out=ctypes.c_void_p(0x10002)), "INVALID_ARG"),
+    (dict(ws=None), "WORKSPACE"), (dict(wsb=64), "WORKSPACE"),
+])
+def test_la_backward_rejects(kw, status):
+    assert _lab(**kw) == ST[status]
+    assert lin.lib().la_last_error().decode().startswith("la_backward")
+
+
+def _dlb(**kw):
+    a = dict(q=P, k=P, v=P, beta=P, alpha=None, S0=None, dO=P, dS_T=None, dq=P, dk_out=P, dv_out=P, dbeta=P,
+             dalpha=None, dS0=None, B=1, H=1, T=8, dk=128, dv=128, dtype=1, chunk=64, ws=P, wsb=1 << 30,
+             stream=None)
+    a.update(kw)
+    return lin.lib().delta_backward(a["q"], a["k"], a["v"], a["beta"], a["alpha"], a["S0"], a["dO"], a["dS_T"],
+                                    a["dq"], a["dk_out"], a["dv_out"], a["dbeta"], a["dalpha"], a["dS0"], a["B"],
+                                    a["H"], a["T"], a["dk"], a["dv"], a["dtype"], a["chunk"], a["ws"], a["wsb"],
+                                    a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(beta=None), "INVALID_ARG"), (dict(dbeta=None), "INVALID_ARG"), (dict(dO=None), "INVALID_ARG"),
+    (dict(alpha=P), "INVALID_ARG"),                      # alpha without dalpha
+    (dict(dalpha=P), "INVALID_ARG"),                     # dalpha without alpha
+    (dict(T=0), "INVALID_ARG"), (dict(dtype=4), "INVALID_ARG"), (dict(dtype=0), "UNSUPPORTED"),
+    (dict(dk=32), "UNSUPPORTED"), (dict(chunk=128), "UNSUPPORTED"),
+    (dict(beta=ctypes.c_void_p(0x10001)), "INVALID_ARG"), (dict(dbeta=ctypes.c_void_p(0x10002)), "INVALID_ARG"),
+    (dict(dq=ctypes.c_void_p(0x10008)), "INVALID_ARG"),
+    (dict(ws=None), "WORKSPACE"), (dict(wsb=1024), "WORKSPACE"),
+])
+def test_delta_backward_rejects(kw, status):
+    assert _dlb(**kw) == ST[status]
+    assert lin.lib().la_last_error().decode().startswith("delta_backward")
+
+
 def test_workspace_queries():
     L = lin.lib()
     assert L.la_forward_workspace_bytes(0, 1, 8, 64, 64, 64) == 0
@@ -273,6 +320,10 @@ def test_workspace_queries():
     assert L.delta_forward_workspace_bytes(2, 16, 16384, 128, 128, 64) > 0
     assert L.ssd_forward_workspace_bytes(4, 8, 8192, 64, 64, 64) > 0
     assert L.ssd_forward_workspace_bytes(4, 8, 8192, 64, 32, 64) == 0
+    # the backward holds two bf16 tiles per chunk beyond the forward's arrays
+    nb = L.delta_backward_workspace_bytes(2, 16, 16384, 128, 128, 64)
+    assert nb == L.delta_forward_workspace_bytes(2, 16, 16384, 128, 128, 64) + 4 * 32 * 256 * 128 * 128
+    assert L.delta_backward_workspace_bytes(2, 16, 16384, 128, 96, 64) == 0
 
 
 def test_status_strings():

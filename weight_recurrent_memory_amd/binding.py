@@ -93,6 +93,11 @@ def lib():
             L.la_backward.argtypes = [vp, vp, vp, fp, fp, vp, fp, fp, vp, vp, vp, fp, fp, i, i, i, i, i, i,
                                       ctypes.c_float, i, vp, sz, vp]
             L.la_backward.restype = i
+            L.delta_backward_workspace_bytes.argtypes = [i, i, i, i, i, i]
+            L.delta_backward_workspace_bytes.restype = sz
+            L.delta_backward.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, vp, vp, vp, fp, fp, fp, i, i, i, i, i, i,
+                                         i, vp, sz, vp]
+            L.delta_backward.restype = i
             L.la_status_string.argtypes = [i]
             L.la_status_string.restype = ctypes.c_char_p
             L.la_last_error.argtypes = []
@@ -568,3 +573,42 @@ def la_backward(q, k, v, dO, S0=None, z0=None, dS_T=None, dz_T=None, eps=1e-6, c
                              _ptr(dk), _ptr(dv), _ptr(dS0), _ptr(dz0), B, H, T, dkk, dvv, code, float(eps), int(chunk),
                              _ptr(ws), wsb, _stream(dev)))
     return dq, dk, dv, dS0, dz0
+
+
+def delta_backward_workspace_bytes(B, H, T, dk, dv, chunk=CHUNK) -> int:
+    return int(lib().delta_backward_workspace_bytes(B, H, T, dk, dv, chunk))
+
+
+def delta_backward(q, k, v, beta, dO, alpha=None, S0=None, dS_T=None, chunk=CHUNK, *, dq=None, dk=None, dv=None,
+                   return_state_grad=True, workspace=None):
+    """Gradients of L = sum dO . o + <dS_T, S_T> for delta_forward (alpha
+    None) or gated_delta_forward (bf16).  Returns (dq, dk, dv, dbeta,
+    dalpha, dS0); dbeta and dalpha are fp32 [B,H,T] (dalpha None for the
+    plain rule), dS0 None when return_state_grad is False."""
+    code = _dtype_code(q)
+    B, H, T, dkk = q.shape
+    dvv = v.shape[-1]
+    dev = q.device
+    _need(k, "k", q.dtype, (B, H, T, dkk), dev)
+    _need(v, "v", q.dtype, (B, H, T, dvv), dev)
+    _need(beta, "beta", q.dtype, (B, H, T), dev)
+    _need(dO, "dO", q.dtype, (B, H, T, dvv), dev)
+    if alpha is not None:
+        _need(alpha, "alpha", torch.float32, (B, H, T), dev)
+    for t, name in ((S0, "S0"), (dS_T, "dS_T")):
+        if t is not None:
+            _need(t, name, torch.float32, (B, H, dkk, dvv), dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, "dq", q.dtype, (B, H, T, dkk), dev)
+    _need(dk, "dk", q.dtype, (B, H, T, dkk), dev)
+    _need(dv, "dv", q.dtype, (B, H, T, dvv), dev)
+    dbeta = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    dalpha = torch.empty((B, H, T), dtype=torch.float32, device=dev) if alpha is not None else None
+    dS0 = torch.empty((B, H, dkk, dvv), dtype=torch.float32, device=dev) if return_state_grad else None
+    ws, wsb = _workspace(delta_backward_workspace_bytes(B, H, T, dkk, dvv, chunk), dev, workspace)
+    _check(lib().delta_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S0), _ptr(dO), _ptr(dS_T),
+                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dalpha), _ptr(dS0), B, H, T, dkk, dvv,
+                                code, int(chunk), _ptr(ws), wsb, _stream(dev)))
+    return dq, dk, dv, dbeta, dalpha, dS0

@@ -485,6 +485,45 @@ la_status la_backward(const void* q, const void* k, const void* v, const float* 
                                                  static_cast<hipStream_t>(stream)));
 }
 
+size_t delta_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {
+    const Batch b = uniform(B, H, T);
+    if (check_batch("delta_backward_workspace_bytes", b, dk, dv, LA_BF16, chunk) != LA_OK) return 0;
+    const Plan p = make_plan(kFamDelta, b, dk, dv);
+    return sizeof(float) * la::delta_backward_ws_floats((long)p.sm.H * p.sm.NS, B * H, T, dk, dv);
+}
+
+la_status delta_backward(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
+                         const float* S0, const void* dO, const float* dS_T, void* dq, void* dk_out, void* dv_out,
+                         float* dbeta, float* dalpha, float* dS0, int B, int H, int T, int dk, int dv, int dtype,
+                         int chunk, void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "delta_backward";
+    if (!q || !k || !v || !beta || !dO || !dq || !dk_out || !dv_out || !dbeta)
+        return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, beta, dO, dq, dk, dv and dbeta must be non-NULL", fn);
+    if (!alpha != !dalpha)
+        return fail(LA_ERR_INVALID_ARG, "%s: dalpha must be given exactly when alpha is (the gated rule)", fn);
+    const Batch b = uniform(B, H, T);
+    la_status st = check_batch(fn, b, dk, dv, dtype, chunk);
+    if (st != LA_OK) return st;
+    if (dtype != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "%s: only bf16 inputs are supported", fn);
+    if ((long)B * H * ((T + la::kChunk - 1) / la::kChunk) > 0x7fffffffL)
+        return fail(LA_ERR_UNSUPPORTED, "%s: B*H*ceil(T/%d) exceeds 2^31-1", fn, la::kChunk);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(dq) || !aligned16(dk_out) ||
+        !aligned16(dv_out))
+        return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, dO, dq, dk and dv must be 16-byte aligned", fn);
+    if ((reinterpret_cast<uintptr_t>(beta) & 1u) || ((reinterpret_cast<uintptr_t>(alpha) |
+         reinterpret_cast<uintptr_t>(dbeta) | reinterpret_cast<uintptr_t>(dalpha) | reinterpret_cast<uintptr_t>(S0) |
+         reinterpret_cast<uintptr_t>(dS_T) | reinterpret_cast<uintptr_t>(dS0)) & 3u))
+        return fail(LA_ERR_INVALID_ARG, "%s: beta must be 2-byte and the fp32 arrays 4-byte aligned", fn);
+    const Plan plan = make_plan(kFamDelta, b, dk, dv);
+    const size_t need = sizeof(float) * la::delta_backward_ws_floats((long)plan.sm.H * plan.sm.NS, B * H, T, dk, dv);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
+        return fail(LA_ERR_WORKSPACE, "%s: workspace of %zu bytes (16-byte aligned) required, got %zu", fn, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    return hip_status(fn, la::launch_delta_backward(q, k, v, beta, alpha, S0, dO, dS_T, dq, dk_out, dv_out, dbeta,
+                                                    dalpha, dS0, plan.sm, dk, dv, dtype,
+                                                    static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
+}
+
 // ---------------------------------------------------------------- decode
 
 la_status la_decode_step(const void* q, const void* k, const void* v, float* S, float* z, void* o, int N,

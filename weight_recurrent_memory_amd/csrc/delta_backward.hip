@@ -1,0 +1,709 @@
+// Backward pass of the delta rule and of its gated form on gfx950: the
+// gradients of L = sum_t dO_t . o_t + <dS_T, S_T> with respect to q, k, v,
+// beta, alpha (gated) and S_0, recomputing the forward states.
+//
+// The rule ("AIGC 基本功｜线性、循环与记忆架构-LinearMem" §03, the corrective
+// write and its decayed variant; "手撕：递推与记忆模型", "Delta-rule fast
+// weight"): S_t = alpha_t S_{t-1} + beta_t k_t (v_t - alpha_t S_{t-1}^T k_t)^T,
+// o_t = S_t^T q_t.  The page's remedy for training memory (§03: split the
+// sequence into chunks, keep only chunk-boundary states, recompute inside) is
+// the plan here.
+//
+// Chunk form (C = 64 tokens, state S entering the chunk, gamma the
+// chunk-local gate products, Gamma[t][i] = gamma_t / gamma_i, Gc = gamma_C /
+// gamma, T = (I + A)^{-1} as in delta_chunk.hpp, P = tril(Q K^T) o Gamma):
+//   R = V - diag(gamma) K S,   U = T R,   Ub = diag(beta) U,
+//   O = diag(gamma) Q S + P Ub,   S' = gamma_C S + K^T diag(Gc) Ub.
+// Given G' = dL/dS' and the chunk's dO, reverse mode gives
+//   dUb = P^T dO + diag(Gc) K G',   dU = diag(beta) dUb,   dR = T^T dU,   dV = dR,
+//   dA  = -tril_{-1}(dR U^T),   E1 = Gamma o tril(dO Ub^T),   E2 = Gamma o dA diag(beta),
+//   dQ  = diag(gamma) dO S^T + E1 K,
+//   dK  = E2 K - diag(gamma) dR S^T          (k_t as the row of A and R)
+//       + E1^T Q + E2^T K + diag(Gc) Ub G'^T (k_i as a column of A and P, and in S'),
+//   dbeta_t = U_t . dUb_t + sum_{t'} dA[t'][t] Gamma[t'][t] (k_t' . k_t),
+//   dS  = gamma_C G' + Q^T diag(gamma) dO - K^T diag(gamma) dR.
+// The state gradient is affine in G' with coefficients free of S, so it has
+// segment maps like the forward's.  Gates: every gamma dependence goes
+// through gamma_t q_t, gamma_t k_t, k_t / gamma_t and gamma_C, so with the
+// two parts of dK above written dKp (rows) and dKm (columns),
+//   dL/dl_t = q_t . dq_t + k_t . (dKp_t - dKm_t) + [t = C-1] <G', S'>,
+// l_t = log gamma_t, and dlog alpha_s = sum_{t >= s} dL/dl_t within the
+// chunk; <G', S'> = gamma_C <G', S> + sum_t Gc_t k_t . (G' Ub_t).  All
+// quantities are bounded (only ratios gamma_t / gamma_i with i <= t occur).
+//
+// Launches (uniform batches; G segments of L tokens per sequence):
+//   1-3  the forward sweep: segment maps, composition, then every chunk's
+//        entering state S_c as bf16 tiles (delta_prefill.hip)
+//   4    reverse chunk chain over segments 1..G-1 with state-gradient columns
+//        started at 0 (with dO) and at I (without): the maps c_g and M_g^T
+//   5    reverse composition: G_end(g-1) = M_g^T G_end(g) + c_g from dS_T
+//   6    reverse chunk chain from G_end(g): every chunk's G' as bf16 tiles,
+//        and dS_0 from segment 0
+//   7    every chunk independently: dq, dk, dv, dbeta, dalpha from (S_c, G'_c)
+#include "common.hpp"
+#include "delta_chunk.hpp"
+#include "kernels.hpp"
+
+namespace la {
+
+namespace {
+
+using dchunk::CH;
+using dchunk::LF;
+using dchunk::LT;
+using dchunk::NT;
+using dchunk::NWV;
+
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+// ------------------------------------------------------------- reverse chain
+
+template <int DK, int DV, bool MAP, bool GATED>
+struct RC {
+    static constexpr int LQ = DK + 8, LV = DV + 8;
+    static constexpr int KS = CH * LQ * 2, QS = CH * LQ * 2, OS = CH * LV * 2;
+    static constexpr int TS = CH * LT * 2, PS = CH * LT * 2;
+    static constexpr int AF = CH * LF * 4, AD = 4 * 256 * 4, YF = 4 * 256 * 4;
+    static constexpr int BS = CH * 4 * (GATED ? 4 : 1);
+    static constexpr int TOTAL = KS + QS + OS + TS + PS + AF + AD + YF + BS;
+    static_assert(TOTAL <= 160 * 1024, "LDS budget");
+    static constexpr int XR = DK / 16;
+    // Column tiles of the state gradient: NCN carry dO (c_g, or the gradient
+    // itself); MAP adds DK/16 identity-started columns without dO (M_g^T).
+    static constexpr int NCN = DV / 16;
+    static constexpr int NCT = MAP ? NCN + DK / 16 : NCN;
+    static constexpr int SLOTS = (NCT + NWV - 1) / NWV;
+};
+
+// One workgroup runs one segment's chunks from last to first.  Each wave
+// owns whole columns of the state gradient G (fp32, registers) and per chunk
+//   dU[:, c] = beta o (P^T dO[:, c] + Gc o K G[:, c])
+//   dR[:, c] = T^T dU[:, c]
+//   G[:, c]  = gamma_C G[:, c] + (diag(gamma) Q)^T dO[:, c] - K^T diag(gamma) dR[:, c]
+// with P, T and the staged rows shared through LDS.
+template <int DK, int DV, bool MAP, bool GATED>
+__global__ __launch_bounds__(NT) void dlb_chain_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ beta,
+    const float* __restrict__ alpha, const bf16_t* __restrict__ dO, const float* __restrict__ g_end,
+    float* __restrict__ map_c, float* __restrict__ map_mt, bf16_t* __restrict__ gst, float* __restrict__ dS0,
+    SegMap sm) {
+    using Y = RC<DK, DV, MAP, GATED>;
+    using M = Mma<bf16_t>;
+    constexpr int LQ = Y::LQ, LV = Y::LV, XR = Y::XR, SLOTS = Y::SLOTS;
+    __shared__ __align__(16) unsigned char smem[Y::TOTAL];
+    unsigned char* sp = smem;
+    __bf16* Ks = reinterpret_cast<__bf16*>(sp);  sp += Y::KS;
+    __bf16* Qs = reinterpret_cast<__bf16*>(sp);  sp += Y::QS;
+    __bf16* Os = reinterpret_cast<__bf16*>(sp);  sp += Y::OS;
+    __bf16* Ts = reinterpret_cast<__bf16*>(sp);  sp += Y::TS;
+    __bf16* Ps = reinterpret_cast<__bf16*>(sp);  sp += Y::PS;
+    float* Af = reinterpret_cast<float*>(sp);
+    float* Ad = Af + CH * LF;
+    float* Yf = Ad + 4 * 256;
+    float* Bs = Yf + 4 * 256;
+    float* Gl = Bs + CH;
+    float* Ge = Gl + CH;
+    float* Gc = Ge + CH;
+
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
+    const int w = wave_id(tid);
+    const int G1 = MAP ? sm.G - 1 : sm.G;
+    const int vh = blockIdx.x / G1;  // sequence * H + head
+    const int seg = blockIdx.x % G1 + (MAP ? 1 : 0);
+    const int nseq = vh / sm.H, h = vh % sm.H;
+    const long slot = sm.slot<false>(nseq, h) + seg;
+    const long row0 = h * sm.hs + sm.start<false>(nseq);
+    const int NC = (sm.T + CH - 1) / CH;
+
+    v4f X[SLOTS][XR];
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) {
+        const int id = w + NWV * j;
+        const bool is_m = id >= Y::NCN;
+        const int col = 16 * (is_m ? id - Y::NCN : id) + li;
+#pragma unroll
+        for (int i = 0; i < XR; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * i + 4 * g + r;
+                float x = 0.f;
+                if (id < Y::NCT) {
+                    if constexpr (MAP) x = (is_m && row == col) ? 1.f : 0.f;
+                    else x = g_end[(slot * DK + row) * DV + col];
+                }
+                X[j][i][r] = x;
+            }
+    }
+
+    const int t0 = seg * sm.L;
+    const int t_end = min((seg + 1) * sm.L, sm.T);
+    const rsrc_t rk = make_rsrc(k + row0 * DK, (uint32_t)t_end * DK * 2);
+    const rsrc_t rq = make_rsrc(q + row0 * DK, (uint32_t)t_end * DK * 2);
+    const rsrc_t ro = make_rsrc(dO + row0 * DV, (uint32_t)t_end * DV * 2);
+    const rsrc_t rb = make_rsrc(beta + row0, (uint32_t)t_end * 2);
+    const rsrc_t ra = make_rsrc(GATED ? alpha + row0 : nullptr, GATED ? (uint32_t)t_end * 4 : 0u);
+    ChunkRegs<bf16_t, DK, NT> kr, qr;
+    ChunkRegs<bf16_t, DV, NT> orr;
+    unsigned short bnext = 0;
+    unsigned anext = 0;
+    auto load_chunk = [&](int c) {
+        kr.load_buf(rk, c, tid);
+        qr.load_buf(rq, c, tid);
+        orr.load_buf(ro, c, tid);
+        if (tid < CH) {
+            bnext = __builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(c + tid) * 2, 0, 0);
+            if constexpr (GATED) anext = __builtin_amdgcn_raw_buffer_load_b32(ra, (uint32_t)(c + tid) * 4, 0, 0);
+        }
+    };
+    const int c_last = t0 + ((t_end - 1 - t0) / CH) * CH;
+    load_chunk(c_last);
+    dchunk::clear_upper(Ts, tid);
+    dchunk::clear_upper(Ps, tid);
+    for (int c0 = c_last; c0 >= t0; c0 -= CH) {
+        // Lane indices from an opaque copy, re-derived every chunk: the many
+        // per-lane LDS addresses built from them then live next to their uses
+        // instead of being hoisted out of the loop (and spilled).
+        int tid_v = threadIdx.x;
+        asm volatile("" : "+v"(tid_v));
+        const int tid = tid_v, lane = tid & 63, g = lane >> 4, li = lane & 15;
+        const int n = min(CH, t_end - c0);
+        if constexpr (!MAP) {  // the gradient of the state leaving this chunk
+            const long ci = (long)vh * NC + c0 / CH;
+#pragma unroll
+            for (int j = 0; j < SLOTS; ++j) {
+                const int id = w + NWV * j;
+                if (id >= Y::NCN) continue;
+#pragma unroll
+                for (int i = 0; i < XR; ++i) dchunk::put_tile(gst + dchunk::tile_offset<DK, DV>(ci, id, i, lane), X[j][i]);
+            }
+        }
+        stage_rows_raw<bf16_t, DK, NT>(kr, tid, Ks, LQ);
+        stage_rows_raw<bf16_t, DK, NT>(qr, tid, Qs, LQ);
+        stage_rows_raw<bf16_t, DV, NT>(orr, tid, Os, LV);
+        if (tid < CH) {
+            Bs[tid] = bf16_to_f32(bnext);
+            if constexpr (GATED) dchunk::gate_prefix(__uint_as_float(anext), tid, n, Gl, Ge, Gc);
+        }
+        if (c0 - CH >= t0) load_chunk(c0 - CH);
+        __syncthreads();
+        dchunk::build_T<DK, GATED, true>(Ks, Qs, Bs, Gl, Af, Ad, Yf, Ts, Ps, w, g, li);
+        if constexpr (GATED) {  // diag(gamma) Q for the dO term of the state gradient
+            for (int e = tid; e < CH * DK / 8; e += NT) {
+                const int row = e / (DK / 8), col = (e % (DK / 8)) * 8;
+                v8bf x = *reinterpret_cast<const v8bf*>(&Qs[row * LQ + col]);
+                const float s = Ge[row];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) x[u] = M::cvt((float)x[u] * s);
+                *reinterpret_cast<v8bf*>(&Qs[row * LQ + col]) = x;
+            }
+            __syncthreads();
+        }
+
+#pragma unroll
+        for (int j = 0; j < SLOTS; ++j) {
+            const int id = w + NWV * j;
+            if (id >= Y::NCT) continue;
+            const bool is_c = id < Y::NCN;
+            v4f dU[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                v4f acc = zero4(), kg = zero4();
+                if (is_c) {
+#pragma unroll
+                    for (int kb = 0; kb < CH / 32; ++kb) {
+                        if (32 * kb + 31 < 16 * tt) continue;  // P^T is upper triangular
+                        M::mma(acc, M::load_tr(Ps, LT, 32 * kb, 16 * tt, lane), M::load_tr(Os, LV, 32 * kb, 16 * id, lane));
+                    }
+                }
+#pragma unroll
+                for (int kb = 0; kb < DK / 32; ++kb)
+                    M::mma(kg, M::load(&Ks[(16 * tt + li) * LQ + 32 * kb], g), M::from_tiles(X[j][2 * kb], X[j][2 * kb + 1]));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int s = 16 * tt + 4 * g + r;
+                    dU[tt][r] = Bs[s] * (acc[r] + (GATED ? Gc[s] : 1.f) * kg[r]);
+                }
+            }
+            v4f dR[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                dR[tt] = zero4();
+#pragma unroll
+                for (int kb = 0; kb < CH / 32; ++kb) {
+                    if (32 * kb + 31 < 16 * tt) continue;  // T^T is upper triangular
+                    M::mma(dR[tt], M::load_tr(Ts, LT, 32 * kb, 16 * tt, lane), M::from_tiles(dU[2 * kb], dU[2 * kb + 1]));
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dR[tt][r] *= GATED ? -Ge[16 * tt + 4 * g + r] : -1.f;
+            }
+            if constexpr (GATED) {
+                const float gend = Ge[CH - 1];
+#pragma unroll
+                for (int i = 0; i < XR; ++i) X[j][i] *= gend;
+            }
+#pragma unroll
+            for (int i = 0; i < XR; ++i) {
+                if (is_c) {
+#pragma unroll
+                    for (int kb = 0; kb < CH / 32; ++kb)
+                        M::mma(X[j][i], M::load_tr(Qs, LQ, 32 * kb, 16 * i, lane), M::load_tr(Os, LV, 32 * kb, 16 * id, lane));
+                }
+#pragma unroll
+                for (int kb = 0; kb < CH / 32; ++kb)
+                    M::mma(X[j][i], M::load_tr(Ks, LQ, 32 * kb, 16 * i, lane), M::from_tiles(dR[2 * kb], dR[2 * kb + 1]));
+            }
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) {
+        const int id = w + NWV * j;
+        if (id >= Y::NCT) continue;
+        const bool is_m = id >= Y::NCN;
+        float* dst;
+        int ld, col;
+        if constexpr (MAP) {
+            dst = is_m ? map_mt + slot * DK * DK : map_c + slot * DK * DV;
+            ld = is_m ? DK : DV;
+            col = 16 * (is_m ? id - Y::NCN : id) + li;
+        } else {
+            if (seg != 0 || !dS0) continue;
+            dst = dS0 + (long)vh * DK * DV;
+            ld = DV;
+            col = 16 * id + li;
+        }
+#pragma unroll
+        for (int i = 0; i < XR; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(16 * i + 4 * g + r) * ld + col] = X[j][i][r];
+    }
+}
+
+// ------------------------------------------------------------- gradients
+
+template <int DK, int DV, bool GATED>
+struct GR {
+    static constexpr int LQ = DK + 8, LV = DV + 8, LB = DV + 8;
+    static constexpr int KS = CH * LQ * 2, QS = CH * LQ * 2, OS = CH * LV * 2, US = CH * LV * 2;
+    static constexpr int RS = cmax(CH * LV * 2, CH * LF * 4);   // dR rows, over the inverse's fp32 matrix
+    static constexpr int BG = cmax(DK * LB * 2, 2 * 4 * 256 * 4);  // G' or S rows, over its small blocks
+    static constexpr int TS = CH * LT * 2, PS = CH * LT * 2;
+    // beta; per-wave partials of dbeta (rows, then E2 tiles) and of dL/dl;
+    // per-wave partial sums; gates
+    static constexpr int SM = (CH + NWV * CH + 10 * 16 + NWV * CH + 2 * NWV + (GATED ? 3 * CH : 0)) * 4;
+    static constexpr int TOTAL = KS + QS + OS + US + RS + BG + TS + PS + SM;
+    static_assert(TOTAL <= 160 * 1024, "LDS budget");
+    static constexpr int XR = DK / 16;
+    static constexpr int NCN = DV / 16;
+    static constexpr int TPW = DK / 32;  // (dk tile, token tile) pairs per wave in the row phase
+};
+
+// One workgroup per chunk.  Phases:
+//   column phase (wave w < DV/16 owns value columns 16w..16w+15, with its
+//     tiles of S_c and G'_c in registers): U, dUb, dU, dR as above; U and
+//     dR rows to LDS, the U . dUb part of dbeta
+//   E phase: E1 and E2 (the lower 16x16 tiles, bf16, over P and T in LDS)
+//     and the column part of dbeta
+//   row phase: dK's column part with G' rows in LDS, then S rows replace
+//     them for dQ and dK's row part; dq, dk stored as transposed tiles (four
+//     consecutive features per lane) and the gate sums dL/dl_t formed
+template <int DK, int DV, bool GATED>
+__global__ __launch_bounds__(NT) void dlb_grad_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ beta, const float* __restrict__ alpha, const bf16_t* __restrict__ dO,
+    const bf16_t* __restrict__ sst, const bf16_t* __restrict__ gst, bf16_t* __restrict__ dq,
+    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, float* __restrict__ dbeta, float* __restrict__ dalpha, int T) {
+    using Y = GR<DK, DV, GATED>;
+    using M = Mma<bf16_t>;
+    constexpr int LQ = Y::LQ, LV = Y::LV, LB = Y::LB, XR = Y::XR, TPW = Y::TPW;
+    __shared__ __align__(16) unsigned char smem[Y::TOTAL];
+    unsigned char* sp = smem;
+    __bf16* Ks = reinterpret_cast<__bf16*>(sp);  sp += Y::KS;
+    __bf16* Qs = reinterpret_cast<__bf16*>(sp);  sp += Y::QS;
+    __bf16* Os = reinterpret_cast<__bf16*>(sp);  sp += Y::OS;
+    __bf16* Us = reinterpret_cast<__bf16*>(sp);  sp += Y::US;  // V, then U
+    unsigned char* rs = sp;                      sp += Y::RS;
+    __bf16* Rs = reinterpret_cast<__bf16*>(rs);                 // dR (after the inverse)
+    float* Af = reinterpret_cast<float*>(rs);                   // the inverse's work matrix
+    unsigned char* bg = sp;                      sp += Y::BG;
+    __bf16* Bg = reinterpret_cast<__bf16*>(bg);                 // G' rows, then S rows
+    float* Ad = reinterpret_cast<float*>(bg);
+    float* Yf = Ad + 4 * 256;
+    __bf16* Ts = reinterpret_cast<__bf16*>(sp);  sp += Y::TS;  // T, then E2
+    __bf16* Ps = reinterpret_cast<__bf16*>(sp);  sp += Y::PS;  // P, then E1
+    // Partial sums live in per-wave (or per-tile) slots and are added in a
+    // fixed order at the end, so results do not depend on wave timing.
+    float* Bs = reinterpret_cast<float*>(sp);
+    float* pB = Bs + CH;           // [wave][t]: U_t . dUb_t over the wave's columns
+    float* pE = pB + NWV * CH;     // [E2 tile][column]: column sums of dA o Gamma o K K^T
+    float* pL = pE + 10 * 16;      // [wave][t]: the wave's features of dL/dl_t
+    float* pS = pL + NWV * CH;     // [wave]: <G', S> over the wave's columns
+    float* pZ = pS + NWV;          // [wave]: sum Gc_t k_t . (G' Ub_t) over the wave's tiles
+    float* Gl = pZ + NWV;
+    float* Ge = Gl + CH;
+    float* Gc = Ge + CH;
+
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
+    const int w = wave_id(tid);
+    const int NC = (T + CH - 1) / CH;
+    const long ci = blockIdx.x;
+    const int vh = (int)(ci / NC);
+    const int c0 = (int)(ci % NC) * CH;
+    const int n = min(CH, T - c0);
+    const long row0 = (long)vh * T + c0;
+
+    {
+        const rsrc_t rk = make_rsrc(k + row0 * DK, (uint32_t)n * DK * 2);
+        const rsrc_t rq = make_rsrc(q + row0 * DK, (uint32_t)n * DK * 2);
+        const rsrc_t rv = make_rsrc(v + row0 * DV, (uint32_t)n * DV * 2);
+        const rsrc_t ro = make_rsrc(dO + row0 * DV, (uint32_t)n * DV * 2);
+        ChunkRegs<bf16_t, DK, NT> kr, qr;
+        ChunkRegs<bf16_t, DV, NT> vr, orr;
+        kr.load_buf(rk, 0, tid);
+        qr.load_buf(rq, 0, tid);
+        vr.load_buf(rv, 0, tid);
+        orr.load_buf(ro, 0, tid);
+        stage_rows_raw<bf16_t, DK, NT>(kr, tid, Ks, LQ);
+        stage_rows_raw<bf16_t, DK, NT>(qr, tid, Qs, LQ);
+        stage_rows_raw<bf16_t, DV, NT>(vr, tid, Us, LV);
+        stage_rows_raw<bf16_t, DV, NT>(orr, tid, Os, LV);
+    }
+    uint2 st[XR], gt[XR];  // this wave's tiles of S_c and G'_c
+    if (w < Y::NCN) {
+#pragma unroll
+        for (int i = 0; i < XR; ++i) {
+            st[i] = dchunk::get_tile(sst + dchunk::tile_offset<DK, DV>(ci, w, i, lane));
+            gt[i] = dchunk::get_tile(gst + dchunk::tile_offset<DK, DV>(ci, w, i, lane));
+        }
+    }
+    for (int e = tid; e < NWV * CH; e += NT) pL[e] = 0.f;  // waves write only their tokens
+    if (tid < CH) {
+        const rsrc_t rb = make_rsrc(beta + row0, (uint32_t)n * 2);
+        Bs[tid] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)tid * 2, 0, 0));
+        if constexpr (GATED) {
+            const rsrc_t ra = make_rsrc(alpha + row0, (uint32_t)n * 4);
+            dchunk::gate_prefix(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ra, (uint32_t)tid * 4, 0, 0)), tid,
+                                n, Gl, Ge, Gc);
+        }
+    }
+    dchunk::clear_upper(Ts, tid);
+    dchunk::clear_upper(Ps, tid);
+    __syncthreads();
+    dchunk::build_T<DK, GATED, true>(Ks, Qs, Bs, Gl, Af, Ad, Yf, Ts, Ps, w, g, li);
+
+    // ---- column phase
+    if (w < Y::NCN) {
+        const int col = 16 * w + li;
+        v4f U[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {  // R = V - diag(gamma) K S
+            v4f ks = zero4();
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb)
+                M::mma(ks, M::load(&Ks[(16 * tt + li) * LQ + 32 * kb], g), dchunk::tile_frag(st[2 * kb], st[2 * kb + 1]));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int s = 16 * tt + 4 * g + r;
+                U[tt][r] = (float)Us[s * LV + col] - (GATED ? Ge[s] : 1.f) * ks[r];
+            }
+        }
+        v4f Uo[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {  // U = T R
+            Uo[tt] = zero4();
+#pragma unroll
+            for (int kb = 0; kb < CH / 32; ++kb) {
+                if (32 * kb > 16 * tt + 15) continue;  // T is lower triangular
+                M::mma(Uo[tt], M::load(&Ts[(16 * tt + li) * LT + 32 * kb], g), M::from_tiles(U[2 * kb], U[2 * kb + 1]));
+            }
+        }
+        v4f dUb[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {  // dUb = P^T dO + diag(Gc) K G'
+            v4f acc = zero4(), kg = zero4();
+#pragma unroll
+            for (int kb = 0; kb < CH / 32; ++kb) {
+                if (32 * kb + 31 < 16 * tt) continue;
+                M::mma(acc, M::load_tr(Ps, LT, 32 * kb, 16 * tt, lane), M::load_tr(Os, LV, 32 * kb, 16 * w, lane));
+            }
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb)
+                M::mma(kg, M::load(&Ks[(16 * tt + li) * LQ + 32 * kb], g), dchunk::tile_frag(gt[2 * kb], gt[2 * kb + 1]));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dUb[tt][r] = acc[r] + (GATED ? Gc[16 * tt + 4 * g + r] : 1.f) * kg[r];
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)  // dbeta_t += U_t . dUb_t over this wave's columns
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float x = Uo[tt][r] * dUb[tt][r];
+#pragma unroll
+                for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m);
+                if (li == 0) pB[w * CH + 16 * tt + 4 * g + r] = x;
+                dUb[tt][r] *= Bs[16 * tt + 4 * g + r];  // dU
+            }
+        v4f dR[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {  // dR = T^T dU
+            dR[tt] = zero4();
+#pragma unroll
+            for (int kb = 0; kb < CH / 32; ++kb) {
+                if (32 * kb + 31 < 16 * tt) continue;
+                M::mma(dR[tt], M::load_tr(Ts, LT, 32 * kb, 16 * tt, lane), M::from_tiles(dUb[2 * kb], dUb[2 * kb + 1]));
+            }
+        }
+        if constexpr (GATED) {  // <G', S> over this wave's columns
+            float x = 0.f;
+#pragma unroll
+            for (int i = 0; i < XR; ++i) {
+                const v4f a = dchunk::tile_f32(st[i]), b = dchunk::tile_f32(gt[i]);
+                x += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+            }
+#pragma unroll
+            for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
+            if (lane == 0) pS[w] = x;
+        }
+        // U and dR rows (own columns; this wave alone read them as V), G' rows
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int s = 16 * tt + 4 * g + r;
+                Us[s * LV + col] = M::cvt(Uo[tt][r]);
+                Rs[s * LV + col] = M::cvt(dR[tt][r]);
+            }
+#pragma unroll
+        for (int i = 0; i < XR; ++i) {
+            const bf16_t e[4] = {(bf16_t)(gt[i].x & 0xffffu), (bf16_t)(gt[i].x >> 16), (bf16_t)(gt[i].y & 0xffffu),
+                                 (bf16_t)(gt[i].y >> 16)};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Bg[(16 * i + 4 * g + r) * LB + col] = __builtin_bit_cast(__bf16, e[r]);
+        }
+    }
+    __syncthreads();
+
+    // ---- dv rows, then E1, E2 and the column part of dbeta
+    for (int e = tid; e < CH * DV / 8; e += NT) {
+        const int row = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
+        if (row < n) *reinterpret_cast<uint4*>(dv + (row0 + row) * DV + c8) = *reinterpret_cast<const uint4*>(&Rs[row * LV + c8]);
+    }
+    for (int job = w; job < 20; job += NWV) {
+        int bt, bi;
+        dchunk::lower_tile(job % 10, bt, bi);
+        const bool e2 = job >= 10;
+        v4f acc = zero4();
+        const __bf16* lhs = e2 ? Rs : Os;
+#pragma unroll
+        for (int kb = 0; kb < DV / 32; ++kb)
+            M::mma(acc, M::load(&lhs[(16 * bt + li) * LV + 32 * kb], g), M::load(&Us[(16 * bi + li) * LV + 32 * kb], g));
+        const int i = 16 * bi + li;
+        if (!e2) {  // E1 = Gamma o tril(dO U^T) diag(beta)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * bt + 4 * g + r;
+                const float ratio = GATED ? __expf(Gl[t] - Gl[i]) : 1.f;
+                Ps[t * LT + i] = M::cvt(i <= t ? Bs[i] * ratio * acc[r] : 0.f);
+            }
+        } else {  // dA = -tril_{-1}(dR U^T); E2 = Gamma o dA diag(beta)
+            v4f kk = zero4();
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb)
+                M::mma(kk, M::load(&Ks[(16 * bt + li) * LQ + 32 * kb], g), M::load(&Ks[(16 * bi + li) * LQ + 32 * kb], g));
+            float cs = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * bt + 4 * g + r;
+                const float ratio = GATED ? __expf(Gl[t] - Gl[i]) : 1.f;
+                const float ga = -acc[r] * ratio;
+                Ts[t * LT + i] = M::cvt(i < t ? Bs[i] * ga : 0.f);
+                cs += i < t ? ga * kk[r] : 0.f;
+            }
+            cs += __shfl_xor(cs, 16);
+            cs += __shfl_xor(cs, 32);
+            if (g == 0) pE[(job - 10) * 16 + li] = cs;
+        }
+    }
+    __syncthreads();
+
+    // ---- row phase.  Wave w: dk tile it, token tiles tb .. tb + TPW - 1;
+    // accumulators hold transposed tiles (rows = features, column = token).
+    const int it = w % (DK / 16), tb = (w / (DK / 16)) * TPW;
+    v4f km[TPW];
+    float zs = 0.f;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {  // dKm = E1^T Q + E2^T K + diag(Gc beta) U G'^T
+        const int tt = tb + u;
+        km[u] = zero4();
+#pragma unroll
+        for (int kb = 0; kb < CH / 32; ++kb) {
+            if (32 * kb + 31 < 16 * tt) continue;  // E1, E2 vanish above the diagonal
+            M::mma(km[u], M::load_tr(Qs, LQ, 32 * kb, 16 * it, lane), M::load_tr(Ps, LT, 32 * kb, 16 * tt, lane));
+            M::mma(km[u], M::load_tr(Ks, LQ, 32 * kb, 16 * it, lane), M::load_tr(Ts, LT, 32 * kb, 16 * tt, lane));
+        }
+        v4f g3 = zero4();
+#pragma unroll
+        for (int kb = 0; kb < DV / 32; ++kb)
+            M::mma(g3, M::load(&Bg[(16 * it + li) * LB + 32 * kb], g), M::load(&Us[(16 * tt + li) * LV + 32 * kb], g));
+        const int t = 16 * tt + li;
+        const float sc = Bs[t] * (GATED ? Gc[t] : 1.f);
+        const v4bf kv = *reinterpret_cast<const v4bf*>(&Ks[t * LQ + 16 * it + 4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            km[u][r] += sc * g3[r];
+            zs += (float)kv[r] * sc * g3[r];
+        }
+    }
+    if constexpr (GATED) {
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) zs += __shfl_xor(zs, m);
+        if (lane == 0) pZ[w] = zs;
+    }
+    __syncthreads();
+    if (w < Y::NCN) {  // S rows replace G' rows
+#pragma unroll
+        for (int i = 0; i < XR; ++i) {
+            const bf16_t e[4] = {(bf16_t)(st[i].x & 0xffffu), (bf16_t)(st[i].x >> 16), (bf16_t)(st[i].y & 0xffffu),
+                                 (bf16_t)(st[i].y >> 16)};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Bg[(16 * i + 4 * g + r) * LB + 16 * w + li] = __builtin_bit_cast(__bf16, e[r]);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {  // dQ = diag(gamma) dO S^T + E1 K;  dKp = E2 K - diag(gamma) dR S^T
+        const int tt = tb + u;
+        v4f a1 = zero4(), a2 = zero4();
+#pragma unroll
+        for (int kb = 0; kb < DV / 32; ++kb) {
+            const M::frag sf = M::load(&Bg[(16 * it + li) * LB + 32 * kb], g);
+            M::mma(a1, sf, M::load(&Os[(16 * tt + li) * LV + 32 * kb], g));
+            M::mma(a2, sf, M::load(&Rs[(16 * tt + li) * LV + 32 * kb], g));
+        }
+        const int t = 16 * tt + li;
+        const float ge = GATED ? Ge[t] : 1.f;
+        v4f dqv = a1 * ge, kp = a2 * (-ge);
+#pragma unroll
+        for (int kb = 0; kb < CH / 32; ++kb) {
+            if (32 * kb > 16 * tt + 15) continue;  // E1, E2 rows end at the diagonal
+            const M::frag kt = M::load_tr(Ks, LQ, 32 * kb, 16 * it, lane);
+            M::mma(dqv, kt, M::load(&Ps[(16 * tt + li) * LT + 32 * kb], g));
+            M::mma(kp, kt, M::load(&Ts[(16 * tt + li) * LT + 32 * kb], g));
+        }
+        if (t < n) {
+            uint2 pq, pk;
+            pq.x = pack_bf16x2(dqv[0], dqv[1]);
+            pq.y = pack_bf16x2(dqv[2], dqv[3]);
+            pk.x = pack_bf16x2(kp[0] + km[u][0], kp[1] + km[u][1]);
+            pk.y = pack_bf16x2(kp[2] + km[u][2], kp[3] + km[u][3]);
+            *reinterpret_cast<uint2*>(dq + (row0 + t) * DK + 16 * it + 4 * g) = pq;
+            *reinterpret_cast<uint2*>(dk + (row0 + t) * DK + 16 * it + 4 * g) = pk;
+        }
+        if constexpr (GATED) {  // q_t . dq_t + k_t . (dKp_t - dKm_t), this wave's features
+            const v4bf qv = *reinterpret_cast<const v4bf*>(&Qs[t * LQ + 16 * it + 4 * g]);
+            const v4bf kv = *reinterpret_cast<const v4bf*>(&Ks[t * LQ + 16 * it + 4 * g]);
+            float x = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x += (float)qv[r] * dqv[r] + (float)kv[r] * (kp[r] - km[u][r]);
+            x += __shfl_xor(x, 16);
+            x += __shfl_xor(x, 32);
+            if (g == 0) pL[w * CH + t] = x;
+        }
+    }
+    __syncthreads();
+
+    if (tid < CH) {
+        const int t = tid;
+        float db = 0.f;
+        for (int u = 0; u < Y::NCN; ++u) db += pB[u * CH + t];
+        for (int j = 0; j < 10; ++j) {  // E2 tiles whose columns hold t
+            int bt, bi;
+            dchunk::lower_tile(j, bt, bi);
+            if (bi == t / 16) db += pE[j * 16 + t % 16];
+        }
+        if (t < n) dbeta[row0 + t] = db;
+        if constexpr (GATED) {
+            float x = 0.f, s0 = 0.f, z = 0.f;
+            for (int u = 0; u < NWV; ++u) {
+                x += pL[u * CH + t];
+                z += pZ[u];
+            }
+            for (int u = 0; u < Y::NCN; ++u) s0 += pS[u];
+            x += t == CH - 1 ? Ge[CH - 1] * s0 + z : 0.f;
+#pragma unroll
+            for (int off = 1; off < CH; off <<= 1) {  // suffix sums: dlog alpha_t = sum_{t' >= t} dL/dl_t'
+                const float y = __shfl_down(x, off);
+                x += t + off < CH ? y : 0.f;
+            }
+            if (t < n) {
+                const float a = alpha[row0 + t];
+                // the forward clamps log alpha at -20: no gradient below it
+                dalpha[row0 + t] = logf(a) > -20.f ? x / a : 0.f;
+            }
+        }
+    }
+}
+
+template <int DK, int DV, bool GATED>
+hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* beta, const float* alpha,
+                        const float* S0, const bf16_t* dO, const float* dS_T, bf16_t* dq, bf16_t* dk, bf16_t* dv,
+                        float* dbeta, float* dalpha, float* dS0, const SegMap& sm, float* ws, hipStream_t stream) {
+    const size_t slots = (size_t)sm.H * sm.NS;
+    const int HT = sm.N * sm.H, NC = (sm.T + CH - 1) / CH;
+    float* map_c = ws;                       // forward N_g, then c_g
+    float* map_mt = map_c + slots * DK * DV; // forward M_g, then M_g^T
+    float* g_end = map_mt + slots * DK * DK; // forward segment states, then segment-end gradients
+    bf16_t* sst = reinterpret_cast<bf16_t*>(g_end + slots * DK * DV);
+    bf16_t* gst = sst + (size_t)HT * NC * DK * DV;
+    hipError_t err = launch_delta_states(q, k, v, beta, alpha, S0, sst, sm, DK, DV, ws, stream);
+    if (err != hipSuccess) return err;
+    if (sm.G > 1) {
+        dlb_chain_kernel<DK, DV, true, GATED><<<dim3(HT * (sm.G - 1)), dim3(NT), 0, stream>>>(
+            q, k, beta, alpha, dO, nullptr, map_c, map_mt, nullptr, nullptr, sm);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    if ((err = launch_delta_compose_rev(map_c, map_mt, dS_T, g_end, sm, DK, DV, stream)) != hipSuccess) return err;
+    dlb_chain_kernel<DK, DV, false, GATED><<<dim3(HT * sm.G), dim3(NT), 0, stream>>>(q, k, beta, alpha, dO, g_end,
+                                                                                 nullptr, nullptr, gst, dS0, sm);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    dlb_grad_kernel<DK, DV, GATED><<<dim3(HT * NC), dim3(NT), 0, stream>>>(q, k, v, beta, alpha, dO, sst, gst, dq, dk,
+                                                                         dv, dbeta, dalpha, sm.T);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t delta_backward_ws_floats(long slots, int HT, int T, int dk, int dv) {
+    const size_t nc = (size_t)(T + CH - 1) / CH;
+    // the forward's per-slot arrays, then S_c and G'_c tiles (bf16, two per float)
+    return delta_ws_floats(slots, dk, dv) + (size_t)HT * nc * dk * dv;
+}
+
+hipError_t launch_delta_backward(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
+                                 const float* S0, const void* dO, const float* dS_T, void* dq, void* dk_, void* dv_,
+                                 float* dbeta, float* dalpha, float* dS0, const SegMap& sm, int dk, int dv, int dtype,
+                                 float* ws, hipStream_t stream) {
+    if (dtype != 1 || sm.packed()) return hipErrorInvalidValue;
+    const bf16_t* qb = static_cast<const bf16_t*>(q);
+    const bf16_t* kb = static_cast<const bf16_t*>(k);
+    const bf16_t* vb = static_cast<const bf16_t*>(v);
+    const bf16_t* bb = static_cast<const bf16_t*>(beta);
+    const bf16_t* ob = static_cast<const bf16_t*>(dO);
+    bf16_t* dqb = static_cast<bf16_t*>(dq);
+    bf16_t* dkb = static_cast<bf16_t*>(dk_);
+    bf16_t* dvb = static_cast<bf16_t*>(dv_);
+#define DLB_CASE(A, B)                                                                                         \
+    if (dk == A && dv == B)                                                                                    \
+        return alpha ? launch_typed<A, B, true>(qb, kb, vb, bb, alpha, S0, ob, dS_T, dqb, dkb, dvb, dbeta,     \
+                                                dalpha, dS0, sm, ws, stream)                                   \
+                     : launch_typed<A, B, false>(qb, kb, vb, bb, nullptr, S0, ob, dS_T, dqb, dkb, dvb, dbeta,  \
+                                                 nullptr, dS0, sm, ws, stream);
+    DLB_CASE(64, 64)
+    DLB_CASE(64, 128)
+    DLB_CASE(128, 64)
+    DLB_CASE(128, 128)
+#undef DLB_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace la

@@ -50,6 +50,7 @@
 // ("手撕：递推与记忆模型", "Delta-rule fast weight", which reads first and
 // then writes with the error).
 #include "common.hpp"
+#include "delta_chunk.hpp"
 #include "kernels.hpp"
 
 namespace la {
@@ -60,8 +61,13 @@ constexpr int CH = kChunk;
 constexpr int NT = 512;  // eight waves
 constexpr int NWV = 8;
 
-template <int DK, int NS, bool OUT, bool GATED>
+// What a run of delta_chunk computes: the segment maps, the outputs, or (for
+// the backward pass) only the state entering every chunk.
+enum { kMap = 0, kOut = 1, kStates = 2 };
+
+template <int DK, int NS, int MODE, bool GATED>
 struct DL {
+    static constexpr bool OUT = MODE == kOut, MAP = MODE == kMap;
     static constexpr int LQ = DK + 8;  // bf16 rows with k = dk
     static constexpr int LV = NS + 8;  // bf16 rows of V
     static constexpr int LT = CH + 8;  // bf16 rows with k = token
@@ -80,11 +86,11 @@ struct DL {
     static constexpr int TOTAL = KS + WS + QS + VS + TS + TG + PS + AF + AD + YF + BS;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
     static constexpr int XR = DK / 16;              // dk row tiles of a state column
-    // State column tiles: OUT carries S (NS columns); MAP carries N (NS
-    // columns, zero start, with values) and M (DK columns, identity start, no
-    // values).  Wave w owns tiles w, w + 8, ...
+    // State column tiles: OUT and STATES carry S (NS columns); MAP carries N
+    // (NS columns, zero start, with values) and M (DK columns, identity
+    // start, no values).  Wave w owns tiles w, w + 8, ...
     static constexpr int NCN = NS / 16;
-    static constexpr int NCT = OUT ? NCN : NCN + DK / 16;
+    static constexpr int NCT = MAP ? NCN + DK / 16 : NCN;
     static constexpr int SLOTS = (NCT + NWV - 1) / NWV;
     static constexpr int W_TPW = 4 * XR / NWV;      // W^T tiles per wave
 };
@@ -134,13 +140,15 @@ __host__ __device__ constexpr void lower_tile(int id, int& i, int& j) {
 //   S[:, c] += K^T (beta o U[:, c])
 // The shared, state-free part (A, P, T, W) is computed by all waves through
 // LDS.  MAP runs N and M in the same workgroup, so T and W are built once.
-template <int DK, int NS, bool OUT, bool GATED, bool PACKED>
+template <int DK, int NS, int MODE, bool GATED, bool PACKED>
 __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ beta, const float* __restrict__ alpha, bf16_t* __restrict__ o,
     const float* __restrict__ state_in, float* __restrict__ map_n, float* __restrict__ map_m,
-    float* __restrict__ S_out, bf16_t* __restrict__ pred, int flags, SegMap sm) {
-    using Y = DL<DK, NS, OUT, GATED>;
+    float* __restrict__ S_out, bf16_t* __restrict__ pred, bf16_t* __restrict__ states, int flags, SegMap sm) {
+    constexpr bool OUT = MODE == kOut, MAP = MODE == kMap;
+    static_assert(MODE != kStates || !PACKED, "chunk states are for uniform batches");
+    using Y = DL<DK, NS, MODE, GATED>;
     using M = Mma<bf16_t>;
     using MF = Mma<float>;
     typedef M::frag frag;
@@ -168,17 +176,17 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     // segment of every sequence; its result is the sequence's final state.
     int h, nseq, seg;
     if constexpr (!PACKED) {  // (sequence, head)-major, segments consecutive
-        const int G1 = OUT ? sm.G : sm.G - 1;
+        const int G1 = MAP ? sm.G - 1 : sm.G;
         const int vh = blockIdx.x / G1;
         seg = blockIdx.x % G1;
         nseq = vh / sm.H;
         h = vh % sm.H;
     } else {
-        const int npw = OUT ? sm.NS : sm.NS - sm.N;  // workgroups per head
+        const int npw = MAP ? sm.NS - sm.N : sm.NS;  // workgroups per head
         const int wi = blockIdx.x % npw;
         h = blockIdx.x / npw;
-        nseq = OUT ? sm.seq_of<true>(wi) : sm.seq_of_inner<true>(wi);
-        seg = (OUT ? wi : wi + nseq) - sm.seg_base<true>(nseq);
+        nseq = MAP ? sm.seq_of_inner<true>(wi) : sm.seq_of<true>(wi);
+        seg = (MAP ? wi + nseq : wi) - sm.seg_base<true>(nseq);
     }
     const long slot = sm.slot<PACKED>(nseq, h) + seg;  // workspace slot
     const long row0 = h * sm.hs + sm.start<PACKED>(nseq); // first input row of the sequence
@@ -188,7 +196,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     const bf16_t* bh = beta + row0;
 
     // this wave's state column tiles: slot j holds tile id w + 8j (if < NCT);
-    // ids below NCN are columns of S (OUT) or N (MAP), the rest columns of M
+    // ids below NCN are columns of S (OUT, STATES) or N (MAP), the rest columns of M
     v4f X[SLOTS][XR];
 #pragma unroll
     for (int j = 0; j < SLOTS; ++j) {
@@ -202,7 +210,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
                 const int row = 16 * i + 4 * g + r;
                 float x = 0.f;
                 if (id < Y::NCT) {
-                    if constexpr (OUT) x = state_in[(slot * DK + row) * NS + col];
+                    if constexpr (!MAP) x = state_in[(slot * DK + row) * NS + col];
                     else x = (is_m && row == col) ? 1.f : 0.f;
                 }
                 X[j][i][r] = x;
@@ -261,6 +269,16 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         if constexpr (GATED) asm volatile("" : "+v"(tid_v));
         const int tid = tid_v, lane = tid & 63, g = lane >> 4, li = lane & 15;
         const int n = min(CH, t_end - c0);
+        if constexpr (MODE == kStates) {  // the state entering this chunk, as bf16 tiles
+            const long ci = ((long)nseq * sm.H + h) * ((sm.T + CH - 1) / CH) + c0 / CH;
+#pragma unroll
+            for (int j = 0; j < SLOTS; ++j) {
+                const int id = w + NWV * j;
+                if (id >= Y::NCN) continue;
+#pragma unroll
+                for (int i = 0; i < XR; ++i) dchunk::put_tile(states + dchunk::tile_offset<DK, NS>(ci, id, i, lane), X[j][i]);
+            }
+        }
         // ---- stage the chunk row-major (transposed operands are read with
         // transpose loads)
         if (flags & kNormQK) {
@@ -588,6 +606,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     }
 
     // ---- the segment's result: S_T (OUT, last segment) or the maps (MAP)
+    if constexpr (MODE == kStates) return;
 #pragma unroll
     for (int j = 0; j < SLOTS; ++j) {
         const int id = w + NWV * j;
@@ -614,8 +633,9 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
 
 // S_in(0) = S0 (or 0); S_in(g+1) = M_g S_in(g) + N_g in fp32 MFMA.  One
 // workgroup per (16-column block of the state, sequence and head); serial
-// over the sequence's segments.
-template <int DK, int DV, bool PACKED>
+// over the sequence's segments.  REV runs the same recurrence from the last
+// segment down (the backward pass: G(G-1) = S0, G(g-1) = M_g G(g) + N_g).
+template <int DK, int DV, bool PACKED, bool REV = false>
 __global__ __launch_bounds__(256) void delta_compose_kernel(const float* __restrict__ map_n,
                                                             const float* __restrict__ map_m,
                                                             const float* S0, float* __restrict__ state_in,
@@ -640,13 +660,15 @@ __global__ __launch_bounds__(256) void delta_compose_kernel(const float* __restr
             const float x = S0 ? S0[((long)p * DK + row) * DV + col] : 0.f;
             acc[i][r] = x;
             Sb[row][li] = x;
-            state_in[(base * DK + row) * DV + col] = x;
+            state_in[((REV ? base + G - 1 : base) * DK + row) * DV + col] = x;
         }
     }
     __syncthreads();
     for (int s = 0; s + 1 < G; ++s) {
-        const float* Mg = map_m + (base + s) * DK * DK;
-        const float* Ng = map_n + (base + s) * DK * DV;
+        const long from = REV ? base + G - 1 - s : base + s;  // the map applied
+        const long to = REV ? from - 1 : from + 1;            // the state it produces
+        const float* Mg = map_m + from * DK * DK;
+        const float* Ng = map_n + from * DK * DV;
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             const int rt = w * RPW + i;
@@ -673,7 +695,7 @@ __global__ __launch_bounds__(256) void delta_compose_kernel(const float* __restr
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * rt + 4 * g + r;
                 Sb[row][li] = acc[i][r];
-                state_in[((base + s + 1) * DK + row) * DV + col] = acc[i][r];
+                state_in[(to * DK + row) * DV + col] = acc[i][r];
             }
         }
         __syncthreads();
@@ -690,15 +712,38 @@ hipError_t launch_packing(const bf16_t* q, const bf16_t* k, const bf16_t* v, con
     float* state_in = map_m + slots * DK * DK;
     hipError_t err;
     if (sm.NS > sm.N) {
-        delta_chunk_kernel<DK, DV, false, GATED, PACKED><<<dim3(sm.H * (sm.NS - sm.N)), dim3(NT), 0, stream>>>(
-            q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, nullptr, flags, sm);
+        delta_chunk_kernel<DK, DV, kMap, GATED, PACKED><<<dim3(sm.H * (sm.NS - sm.N)), dim3(NT), 0, stream>>>(
+            q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, nullptr, nullptr, flags, sm);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     delta_compose_kernel<DK, DV, PACKED><<<dim3(DV / 16, sm.N * sm.H), dim3(256), 0, stream>>>(map_n, map_m, S0, state_in,
                                                                                       sm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    delta_chunk_kernel<DK, DV, true, GATED, PACKED><<<dim3(sm.H * sm.NS), dim3(NT), 0, stream>>>(
-        q, k, v, beta, alpha, o, state_in, nullptr, nullptr, S_out, pred, flags, sm);
+    delta_chunk_kernel<DK, DV, kOut, GATED, PACKED><<<dim3(sm.H * sm.NS), dim3(NT), 0, stream>>>(
+        q, k, v, beta, alpha, o, state_in, nullptr, nullptr, S_out, pred, nullptr, flags, sm);
+    return hipGetLastError();
+}
+
+// The backward pass's forward sweep (uniform batches): maps, composition,
+// then every chunk's entering state as bf16 tiles.
+template <int DK, int DV, bool GATED>
+hipError_t launch_states(const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* beta, const float* alpha,
+                         const float* S0, bf16_t* states, const SegMap& sm, float* ws, hipStream_t stream) {
+    const size_t slots = (size_t)sm.H * sm.NS;
+    float* map_n = ws;
+    float* map_m = map_n + slots * DK * DV;
+    float* state_in = map_m + slots * DK * DK;
+    hipError_t err;
+    if (sm.NS > sm.N) {
+        delta_chunk_kernel<DK, DV, kMap, GATED, false><<<dim3(sm.H * (sm.NS - sm.N)), dim3(NT), 0, stream>>>(
+            q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, nullptr, nullptr, 0, sm);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    delta_compose_kernel<DK, DV, false><<<dim3(DV / 16, sm.N * sm.H), dim3(256), 0, stream>>>(map_n, map_m, S0,
+                                                                                          state_in, sm);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    delta_chunk_kernel<DK, DV, kStates, GATED, false><<<dim3(sm.H * sm.NS), dim3(NT), 0, stream>>>(
+        q, k, v, beta, alpha, nullptr, state_in, nullptr, nullptr, nullptr, nullptr, states, 0, sm);
     return hipGetLastError();
 }
 
@@ -712,6 +757,44 @@ hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const
 }
 
 }  // namespace
+
+hipError_t launch_delta_states(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
+                               const float* S0, void* states, const SegMap& sm, int dk, int dv, float* ws,
+                               hipStream_t stream) {
+    const bf16_t* qb = static_cast<const bf16_t*>(q);
+    const bf16_t* kb = static_cast<const bf16_t*>(k);
+    const bf16_t* vb = static_cast<const bf16_t*>(v);
+    const bf16_t* bb = static_cast<const bf16_t*>(beta);
+    bf16_t* st = static_cast<bf16_t*>(states);
+    if (sm.packed()) return hipErrorInvalidValue;
+#define STATES_CASE(A, B)                                                                         \
+    if (dk == A && dv == B)                                                                       \
+        return alpha ? launch_states<A, B, true>(qb, kb, vb, bb, alpha, S0, st, sm, ws, stream)   \
+                     : launch_states<A, B, false>(qb, kb, vb, bb, nullptr, S0, st, sm, ws, stream);
+    STATES_CASE(64, 64)
+    STATES_CASE(64, 128)
+    STATES_CASE(128, 64)
+    STATES_CASE(128, 128)
+#undef STATES_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_delta_compose_rev(const float* map_c, const float* map_mt, const float* G_last, float* g_end,
+                                    const SegMap& sm, int dk, int dv, hipStream_t stream) {
+    if (sm.packed()) return hipErrorInvalidValue;
+#define REV_CASE(A, B)                                                                                        \
+    if (dk == A && dv == B) {                                                                                 \
+        delta_compose_kernel<A, B, false, true><<<dim3(B / 16, sm.N * sm.H), dim3(256), 0, stream>>>(        \
+            map_c, map_mt, G_last, g_end, sm);                                                                \
+        return hipGetLastError();                                                                             \
+    }
+    REV_CASE(64, 64)
+    REV_CASE(64, 128)
+    REV_CASE(128, 64)
+    REV_CASE(128, 128)
+#undef REV_CASE
+    return hipErrorInvalidValue;
+}
 
 size_t delta_ws_floats(long slots, int dk, int dv) {
     return (size_t)slots * ((size_t)dk * dv + (size_t)dk * dk + (size_t)dk * dv);

@@ -53,6 +53,27 @@ hipError_t launch_delta_forward(const void* q, const void* k, const void* v,
                                 int dk, int dv, int dtype, float* ws, hipStream_t stream);
 size_t delta_ws_floats(long slots, int dk, int dv);
 
+// The backward pass's forward sweep (uniform batches, bf16): every chunk's
+// entering state as bf16 tiles in `states` (layout in delta_chunk.hpp);
+// ws as for launch_delta_forward.
+hipError_t launch_delta_states(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
+                               const float* S0, void* states, const SegMap& sm, int dk, int dv, float* ws,
+                               hipStream_t stream);
+// The segment composition run backwards: g_end[last] = G_last (or 0),
+// g_end[g-1] = map_mt[g] g_end[g] + map_c[g].
+hipError_t launch_delta_compose_rev(const float* map_c, const float* map_mt, const float* G_last, float* g_end,
+                                    const SegMap& sm, int dk, int dv, hipStream_t stream);
+
+// Backward pass of the delta rule (gated when alpha is non-NULL; uniform
+// batches, bf16): dq, dk, dv (bf16), dbeta, dalpha (fp32 [HT][T]) and
+// optionally dS0 (fp32) for the loss sum dO . o + <dS_T, S_T>.  ws holds
+// delta_backward_ws_floats(...) floats.
+hipError_t launch_delta_backward(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
+                                 const float* S0, const void* dO, const float* dS_T, void* dq, void* dk_, void* dv_,
+                                 float* dbeta, float* dalpha, float* dS0, const SegMap& sm, int dk, int dv, int dtype,
+                                 float* ws, hipStream_t stream);
+size_t delta_backward_ws_floats(long slots, int HT, int T, int dk, int dv);
+
 // Scalar-decay (Mamba-2 / SSD) prefill: segment maps -> elementwise
 // composition -> chunked outputs.  alpha fp32 [HT][T].  Segments as la_plan.
 hipError_t launch_ssd_forward(const void* q, const void* k, const void* v, const float* alpha,
