@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace la {
@@ -185,6 +187,21 @@ template <> struct Mma<float> {
 };
 
 __device__ __forceinline__ v4f zero4() { return v4f{0.f, 0.f, 0.f, 0.f}; }
+
+// Sum over the 16 lanes of each row of the wave (lanes 16r .. 16r + 15), in
+// every lane of the row: four DPP adds (quad swaps, then half-row and row
+// mirrors), no LDS traffic.  Needs all lanes of the row active.
+__device__ __forceinline__ float row16_sum(float x) {
+    auto dpp = [](float v, auto ctrl) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), decltype(ctrl)::value,
+                                                                  0xF, 0xF, false));
+    };
+    x += dpp(x, std::integral_constant<int, 0xB1>{});   // quad_perm [1, 0, 3, 2]
+    x += dpp(x, std::integral_constant<int, 0x4E>{});   // quad_perm [2, 3, 0, 1]
+    x += dpp(x, std::integral_constant<int, 0x141>{});  // row_half_mirror
+    x += dpp(x, std::integral_constant<int, 0x140>{});  // row_mirror
+    return x;
+}
 
 // The wave's index in its workgroup, as a value the compiler knows to be
 // uniform across the wave.  MFMA instructions ignore the EXEC mask, so a

@@ -313,7 +313,8 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ beta, const float* __restrict__ alpha, const bf16_t* __restrict__ dO,
     const bf16_t* __restrict__ sst, const bf16_t* __restrict__ gst, bf16_t* __restrict__ dq,
-    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, float* __restrict__ dbeta, float* __restrict__ dalpha, int T) {
+    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, float* __restrict__ dbeta, float* __restrict__ dalpha, int HT,
+    int T) {
     using Y = GR<DK, DV, GATED>;
     using M = Mma<bf16_t>;
     constexpr int LQ = Y::LQ, LV = Y::LV, LB = Y::LB, XR = Y::XR, TPW = Y::TPW;
@@ -347,50 +348,71 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int w = wave_id(tid);
     const int NC = (T + CH - 1) / CH;
-    const long ci = blockIdx.x;
+    const long total = (long)HT * NC;
+
+    // Persistent: workgroup b takes chunks b, b + gridDim.x, ...  The next
+    // chunk's rows and per-token inputs are loaded into registers while this
+    // one is computed; its state tiles once this chunk's are consumed.
+    ChunkRegs<bf16_t, DK, NT> kr, qr;
+    ChunkRegs<bf16_t, DV, NT> vr, orr;
+    uint2 st[XR], gt[XR];  // this wave's tiles of S_c and G'_c
+    unsigned short bnext = 0;
+    unsigned anext = 0;
+    auto load_rows = [&](long c) {  // rows past the sequence end read as zero
+        const int c0_ = (int)(c % NC) * CH, n_ = min(CH, T - c0_);
+        const long r0 = (c / NC) * T + c0_;
+        kr.load_buf(make_rsrc(k + r0 * DK, (uint32_t)n_ * DK * 2), 0, tid);
+        qr.load_buf(make_rsrc(q + r0 * DK, (uint32_t)n_ * DK * 2), 0, tid);
+        vr.load_buf(make_rsrc(v + r0 * DV, (uint32_t)n_ * DV * 2), 0, tid);
+        orr.load_buf(make_rsrc(dO + r0 * DV, (uint32_t)n_ * DV * 2), 0, tid);
+        if (tid < CH) {
+            bnext = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(beta + r0, (uint32_t)n_ * 2), (uint32_t)tid * 2, 0, 0);
+            if constexpr (GATED)
+                anext = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(alpha + r0, (uint32_t)n_ * 4), (uint32_t)tid * 4,
+                                                             0, 0);
+        }
+    };
+    auto load_tiles = [&](long c) {
+        if (w < Y::NCN) {
+#pragma unroll
+            for (int i = 0; i < XR; ++i) {
+                st[i] = dchunk::get_tile(sst + dchunk::tile_offset<DK, DV>(c, w, i, lane));
+                gt[i] = dchunk::get_tile(gst + dchunk::tile_offset<DK, DV>(c, w, i, lane));
+            }
+        }
+    };
+    long ci = blockIdx.x;
+    if (ci < total) {
+        load_rows(ci);
+        load_tiles(ci);
+    }
+    dchunk::clear_upper(Ts, tid);
+    dchunk::clear_upper(Ps, tid);
+    for (; ci < total; ci += gridDim.x) {
+    // lane indices re-derived per chunk from an opaque copy, so the per-lane
+    // LDS addresses are not hoisted out of the loop and held (spilled)
+    int tid_v = threadIdx.x;
+    asm volatile("" : "+v"(tid_v));
+    const int tid = tid_v, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int vh = (int)(ci / NC);
     const int c0 = (int)(ci % NC) * CH;
     const int n = min(CH, T - c0);
     const long row0 = (long)vh * T + c0;
+    const long cn = ci + gridDim.x;  // the next chunk of this workgroup
 
-    {
-        const rsrc_t rk = make_rsrc(k + row0 * DK, (uint32_t)n * DK * 2);
-        const rsrc_t rq = make_rsrc(q + row0 * DK, (uint32_t)n * DK * 2);
-        const rsrc_t rv = make_rsrc(v + row0 * DV, (uint32_t)n * DV * 2);
-        const rsrc_t ro = make_rsrc(dO + row0 * DV, (uint32_t)n * DV * 2);
-        ChunkRegs<bf16_t, DK, NT> kr, qr;
-        ChunkRegs<bf16_t, DV, NT> vr, orr;
-        kr.load_buf(rk, 0, tid);
-        qr.load_buf(rq, 0, tid);
-        vr.load_buf(rv, 0, tid);
-        orr.load_buf(ro, 0, tid);
-        stage_rows_raw<bf16_t, DK, NT>(kr, tid, Ks, LQ);
-        stage_rows_raw<bf16_t, DK, NT>(qr, tid, Qs, LQ);
-        stage_rows_raw<bf16_t, DV, NT>(vr, tid, Us, LV);
-        stage_rows_raw<bf16_t, DV, NT>(orr, tid, Os, LV);
-    }
-    uint2 st[XR], gt[XR];  // this wave's tiles of S_c and G'_c
-    if (w < Y::NCN) {
-#pragma unroll
-        for (int i = 0; i < XR; ++i) {
-            st[i] = dchunk::get_tile(sst + dchunk::tile_offset<DK, DV>(ci, w, i, lane));
-            gt[i] = dchunk::get_tile(gst + dchunk::tile_offset<DK, DV>(ci, w, i, lane));
-        }
-    }
+    stage_rows_raw<bf16_t, DK, NT>(kr, tid, Ks, LQ);
+    stage_rows_raw<bf16_t, DK, NT>(qr, tid, Qs, LQ);
+    stage_rows_raw<bf16_t, DV, NT>(vr, tid, Us, LV);
+    stage_rows_raw<bf16_t, DV, NT>(orr, tid, Os, LV);
     for (int e = tid; e < NWV * CH; e += NT) pL[e] = 0.f;  // waves write only their tokens
     if (tid < CH) {
-        const rsrc_t rb = make_rsrc(beta + row0, (uint32_t)n * 2);
-        Bs[tid] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)tid * 2, 0, 0));
-        if constexpr (GATED) {
-            const rsrc_t ra = make_rsrc(alpha + row0, (uint32_t)n * 4);
-            dchunk::gate_prefix(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ra, (uint32_t)tid * 4, 0, 0)), tid,
-                                n, Gl, Ge, Gc);
-        }
+        Bs[tid] = bf16_to_f32(bnext);
+        if constexpr (GATED) dchunk::gate_prefix(__uint_as_float(anext), tid, n, Gl, Ge, Gc);
     }
-    dchunk::clear_upper(Ts, tid);
-    dchunk::clear_upper(Ps, tid);
+    if (cn < total) load_rows(cn);
     __syncthreads();
-    dchunk::build_T<DK, GATED, true>(Ks, Qs, Bs, Gl, Af, Ad, Yf, Ts, Ps, w, g, li);
+    v4f kk[2];  // raw K K^T of the lower tiles w and w + 8, for dbeta
+    dchunk::build_T<DK, GATED, true, true>(Ks, Qs, Bs, Gl, Af, Ad, Yf, Ts, Ps, w, g, li, kk);
 
     // ---- column phase
     if (w < Y::NCN) {
@@ -437,9 +459,7 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
         for (int tt = 0; tt < 4; ++tt)  // dbeta_t += U_t . dUb_t over this wave's columns
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                float x = Uo[tt][r] * dUb[tt][r];
-#pragma unroll
-                for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m);
+                const float x = row16_sum(Uo[tt][r] * dUb[tt][r]);
                 if (li == 0) pB[w * CH + 16 * tt + 4 * g + r] = x;
                 dUb[tt][r] *= Bs[16 * tt + 4 * g + r];  // dU
             }
@@ -460,8 +480,9 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
                 const v4f a = dchunk::tile_f32(st[i]), b = dchunk::tile_f32(gt[i]);
                 x += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
             }
-#pragma unroll
-            for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
+            x = row16_sum(x);
+            x += __shfl_xor(x, 16);
+            x += __shfl_xor(x, 32);
             if (lane == 0) pS[w] = x;
         }
         // U and dR rows (own columns; this wave alone read them as V), G' rows
@@ -488,10 +509,11 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
         const int row = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
         if (row < n) *reinterpret_cast<uint4*>(dv + (row0 + row) * DV + c8) = *reinterpret_cast<const uint4*>(&Rs[row * LV + c8]);
     }
-    for (int job = w; job < 20; job += NWV) {
+    // E2 tile j goes to wave j % 8 (which holds its K K^T from the inverse),
+    // E1 tiles to the waves with fewer: at most three tiles per wave.
+    auto e_tile = [&](int j, bool e2, const v4f& kkt) {
         int bt, bi;
-        dchunk::lower_tile(job % 10, bt, bi);
-        const bool e2 = job >= 10;
+        dchunk::lower_tile(j, bt, bi);
         v4f acc = zero4();
         const __bf16* lhs = e2 ? Rs : Os;
 #pragma unroll
@@ -506,10 +528,6 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
                 Ps[t * LT + i] = M::cvt(i <= t ? Bs[i] * ratio * acc[r] : 0.f);
             }
         } else {  // dA = -tril_{-1}(dR U^T); E2 = Gamma o dA diag(beta)
-            v4f kk = zero4();
-#pragma unroll
-            for (int kb = 0; kb < DK / 32; ++kb)
-                M::mma(kk, M::load(&Ks[(16 * bt + li) * LQ + 32 * kb], g), M::load(&Ks[(16 * bi + li) * LQ + 32 * kb], g));
             float cs = 0.f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -517,13 +535,17 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
                 const float ratio = GATED ? __expf(Gl[t] - Gl[i]) : 1.f;
                 const float ga = -acc[r] * ratio;
                 Ts[t * LT + i] = M::cvt(i < t ? Bs[i] * ga : 0.f);
-                cs += i < t ? ga * kk[r] : 0.f;
+                cs += i < t ? ga * kkt[r] : 0.f;
             }
             cs += __shfl_xor(cs, 16);
             cs += __shfl_xor(cs, 32);
-            if (g == 0) pE[(job - 10) * 16 + li] = cs;
+            if (g == 0) pE[j * 16 + li] = cs;
         }
-    }
+    };
+    e_tile(w, true, kk[0]);
+    if (w < 2) e_tile(w + NWV, true, kk[1]);
+    if (w >= 2) e_tile(w - 2, false, kk[0]);
+    if (w >= 2 && w < 6) e_tile(w + 4, false, kk[0]);
     __syncthreads();
 
     // ---- row phase.  Wave w: dk tile it, token tiles tb .. tb + TPW - 1;
@@ -531,6 +553,15 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
     const int it = w % (DK / 16), tb = (w / (DK / 16)) * TPW;
     v4f km[TPW];
     float zs = 0.f;
+    // operands of the wave's feature tile, shared by its token tiles
+    M::frag qT[CH / 32], kT[CH / 32], rf[DV / 32];
+#pragma unroll
+    for (int kb = 0; kb < CH / 32; ++kb) {
+        qT[kb] = M::load_tr(Qs, LQ, 32 * kb, 16 * it, lane);
+        kT[kb] = M::load_tr(Ks, LQ, 32 * kb, 16 * it, lane);
+    }
+#pragma unroll
+    for (int kb = 0; kb < DV / 32; ++kb) rf[kb] = M::load(&Bg[(16 * it + li) * LB + 32 * kb], g);  // G' rows
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {  // dKm = E1^T Q + E2^T K + diag(Gc beta) U G'^T
         const int tt = tb + u;
@@ -538,13 +569,12 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
 #pragma unroll
         for (int kb = 0; kb < CH / 32; ++kb) {
             if (32 * kb + 31 < 16 * tt) continue;  // E1, E2 vanish above the diagonal
-            M::mma(km[u], M::load_tr(Qs, LQ, 32 * kb, 16 * it, lane), M::load_tr(Ps, LT, 32 * kb, 16 * tt, lane));
-            M::mma(km[u], M::load_tr(Ks, LQ, 32 * kb, 16 * it, lane), M::load_tr(Ts, LT, 32 * kb, 16 * tt, lane));
+            M::mma(km[u], qT[kb], M::load_tr(Ps, LT, 32 * kb, 16 * tt, lane));
+            M::mma(km[u], kT[kb], M::load_tr(Ts, LT, 32 * kb, 16 * tt, lane));
         }
         v4f g3 = zero4();
 #pragma unroll
-        for (int kb = 0; kb < DV / 32; ++kb)
-            M::mma(g3, M::load(&Bg[(16 * it + li) * LB + 32 * kb], g), M::load(&Us[(16 * tt + li) * LV + 32 * kb], g));
+        for (int kb = 0; kb < DV / 32; ++kb) M::mma(g3, rf[kb], M::load(&Us[(16 * tt + li) * LV + 32 * kb], g));
         const int t = 16 * tt + li;
         const float sc = Bs[t] * (GATED ? Gc[t] : 1.f);
         const v4bf kv = *reinterpret_cast<const v4bf*>(&Ks[t * LQ + 16 * it + 4 * g]);
@@ -555,8 +585,9 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
         }
     }
     if constexpr (GATED) {
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) zs += __shfl_xor(zs, m);
+        zs = row16_sum(zs);
+        zs += __shfl_xor(zs, 16);
+        zs += __shfl_xor(zs, 32);
         if (lane == 0) pZ[w] = zs;
     }
     __syncthreads();
@@ -569,16 +600,19 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
             for (int r = 0; r < 4; ++r) Bg[(16 * i + 4 * g + r) * LB + 16 * w + li] = __builtin_bit_cast(__bf16, e[r]);
         }
     }
+    if (cn < total) load_tiles(cn);  // this chunk's tiles are consumed
     __syncthreads();
+#pragma unroll
+    for (int kb = 0; kb < DV / 32; ++kb) rf[kb] = M::load(&Bg[(16 * it + li) * LB + 32 * kb], g);  // S rows
+    float xl[TPW];
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {  // dQ = diag(gamma) dO S^T + E1 K;  dKp = E2 K - diag(gamma) dR S^T
         const int tt = tb + u;
         v4f a1 = zero4(), a2 = zero4();
 #pragma unroll
         for (int kb = 0; kb < DV / 32; ++kb) {
-            const M::frag sf = M::load(&Bg[(16 * it + li) * LB + 32 * kb], g);
-            M::mma(a1, sf, M::load(&Os[(16 * tt + li) * LV + 32 * kb], g));
-            M::mma(a2, sf, M::load(&Rs[(16 * tt + li) * LV + 32 * kb], g));
+            M::mma(a1, rf[kb], M::load(&Os[(16 * tt + li) * LV + 32 * kb], g));
+            M::mma(a2, rf[kb], M::load(&Rs[(16 * tt + li) * LV + 32 * kb], g));
         }
         const int t = 16 * tt + li;
         const float ge = GATED ? Ge[t] : 1.f;
@@ -586,9 +620,8 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
 #pragma unroll
         for (int kb = 0; kb < CH / 32; ++kb) {
             if (32 * kb > 16 * tt + 15) continue;  // E1, E2 rows end at the diagonal
-            const M::frag kt = M::load_tr(Ks, LQ, 32 * kb, 16 * it, lane);
-            M::mma(dqv, kt, M::load(&Ps[(16 * tt + li) * LT + 32 * kb], g));
-            M::mma(kp, kt, M::load(&Ts[(16 * tt + li) * LT + 32 * kb], g));
+            M::mma(dqv, kT[kb], M::load(&Ps[(16 * tt + li) * LT + 32 * kb], g));
+            M::mma(kp, kT[kb], M::load(&Ts[(16 * tt + li) * LT + 32 * kb], g));
         }
         if (t < n) {
             uint2 pq, pk;
@@ -605,9 +638,17 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
             float x = 0.f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) x += (float)qv[r] * dqv[r] + (float)kv[r] * (kp[r] - km[u][r]);
-            x += __shfl_xor(x, 16);
-            x += __shfl_xor(x, 32);
-            if (g == 0) pL[w * CH + t] = x;
+            xl[u] = x;
+        }
+    }
+    if constexpr (GATED) {  // the four lane groups hold different features of token 16 tt + li
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) xl[u] += __shfl_xor(xl[u], 16);
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) xl[u] += __shfl_xor(xl[u], 32);
+        if (g == 0) {
+#pragma unroll
+            for (int u = 0; u < TPW; ++u) pL[w * CH + 16 * (tb + u) + li] = xl[u];
         }
     }
     __syncthreads();
@@ -642,6 +683,8 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
             }
         }
     }
+    __syncthreads();  // the partial sums and gates are read above before the next chunk overwrites them
+    }
 }
 
 template <int DK, int DV, bool GATED>
@@ -666,8 +709,13 @@ hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const
     dlb_chain_kernel<DK, DV, false, GATED><<<dim3(HT * sm.G), dim3(NT), 0, stream>>>(q, k, beta, alpha, dO, g_end,
                                                                                  nullptr, nullptr, gst, dS0, sm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    dlb_grad_kernel<DK, DV, GATED><<<dim3(HT * NC), dim3(NT), 0, stream>>>(q, k, v, beta, alpha, dO, sst, gst, dq, dk,
-                                                                         dv, dbeta, dalpha, sm.T);
+    // one workgroup per compute unit (the LDS allows one), each looping over chunks
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const long total = (long)HT * NC;
+    const int grid = (int)(total < cus ? total : cus);
+    dlb_grad_kernel<DK, DV, GATED><<<dim3(grid), dim3(NT), 0, stream>>>(q, k, v, beta, alpha, dO, sst, gst, dq, dk, dv,
+                                                                       dbeta, dalpha, HT, sm.T);
     return hipGetLastError();
 }
 

@@ -94,21 +94,26 @@ __device__ __forceinline__ void clear_upper(__bf16* X, int tid) {
 // staged chunk rows ([C][DK + 8] bf16; rows past the chunk end zero); Bs:
 // betas; Gl: cumulative log-gates (GATED).  Af ([C][LF] fp32), Ad and Yf
 // (4 x 256 fp32 each) are scratch.  Called by all threads of the workgroup
-// after the chunk is staged and visible; ends with a barrier.
+// after the chunk is staged and visible; ends with a barrier.  With KEEP,
+// keep[j] receives the raw K K^T tile (lower tile w + 8 j, j = 0, 1, when
+// below 10) that this wave computed for A.
 //
 // A's diagonal 16x16 blocks are inverted by forward substitution (wave 0,
 // one column per lane); the rest by 2x2 block doubling: the inverse of
 // [[M11, 0], [M21, M22]] is [[M11^-1, 0], [-M22^-1 M21 M11^-1, M22^-1]],
 // first on the 32x32 diagonal blocks, then on the lower-left 32x32 block.
-template <int DK, bool GATED, bool WANT_P>
+template <int DK, bool GATED, bool WANT_P, bool KEEP = false>
 __device__ __forceinline__ void build_T(const __bf16* Ks, const __bf16* Qs, const float* Bs, const float* Gl,
                                         float* Af, float* Ad, float* Yf, __bf16* Ts, __bf16* Ps, int w, int g,
-                                        int li) {
+                                        int li, v4f* keep = nullptr) {
     using M = Mma<bf16_t>;
     using MF = Mma<float>;
     constexpr int LQ = DK + 8;
     constexpr int NTILE = WANT_P ? 20 : 10;
-    for (int id = w; id < NTILE; id += NWV) {
+#pragma unroll
+    for (int jj = 0; jj < 3; ++jj) {
+        const int id = w + NWV * jj;
+        if (id >= NTILE) break;
         int bi, bj;
         lower_tile(id % 10, bi, bj);
         v4f acc = zero4();
@@ -116,6 +121,9 @@ __device__ __forceinline__ void build_T(const __bf16* Ks, const __bf16* Qs, cons
 #pragma unroll
             for (int kb = 0; kb < DK / 32; ++kb)
                 M::mma(acc, M::load(&Ks[(16 * bi + li) * LQ + 32 * kb], g), M::load(&Ks[(16 * bj + li) * LQ + 32 * kb], g));
+            if constexpr (KEEP) {
+                if (jj < 2) keep[jj] = acc;
+            }
             v4f a;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
