@@ -49,10 +49,11 @@ METRIC = "prefill tokens/sec (MFMA % peak); decode state-update GB/s (% HBM peak
 LA_TRAFFIC = {
     "sources": ["weight_recurrent_memory_amd/csrc/la_prefill.hip",
                 "weight_recurrent_memory_amd/csrc/common.hpp",
-                "weight_recurrent_memory_amd/csrc/kernels.hpp"],
-    "sha256": "76c1977a0deec08c1d2e7bcd02abfa8cf1f8b7d3ad500ecc2b9b3b7c114d2888",
-    "fetch_kib": 86720.0, "fetch_scale": 2.0,
-    "write_kib": 56826.0, "write_scale": 1.0,
+                "weight_recurrent_memory_amd/csrc/kernels.hpp",
+                "weight_recurrent_memory_amd/csrc/segments.hpp"],
+    "sha256": "2acc9b5f1fe0ce2ee502130715b530df60480f52243c7af92221744c74eae477",
+    "fetch_kib": 86635.9, "fetch_scale": 2.0,
+    "write_kib": 56660.5, "write_scale": 1.0,
 }
 
 
