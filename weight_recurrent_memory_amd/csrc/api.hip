@@ -116,7 +116,7 @@ Plan make_plan(Family f, const Batch& b, int dk, int dv) {
     }
     const long slots = (long)sm.H * sm.NS;
     p.fam_floats = f == kFamLA ? la::la_ws_floats(slots, dk, dv)
-                 : f == kFamDelta ? la::delta_ws_floats(slots, dk, dv)
+                 : f == kFamDelta ? la::delta_ws_floats(slots, (long)sm.H * sm.chunk_recs_per_head(la::kChunk), dk, dv)
                                   : la::ssd_ws_floats(slots, dk, dv);
     return p;
 }
@@ -489,7 +489,9 @@ size_t delta_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int c
     const Batch b = uniform(B, H, T);
     if (check_batch("delta_backward_workspace_bytes", b, dk, dv, LA_BF16, chunk) != LA_OK) return 0;
     const Plan p = make_plan(kFamDelta, b, dk, dv);
-    return sizeof(float) * la::delta_backward_ws_floats((long)p.sm.H * p.sm.NS, B * H, T, dk, dv);
+    return sizeof(float) * la::delta_backward_ws_floats((long)p.sm.H * p.sm.NS,
+                                                        (long)p.sm.H * p.sm.chunk_recs_per_head(la::kChunk), B * H, T,
+                                                        dk, dv);
 }
 
 la_status delta_backward(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
@@ -515,7 +517,9 @@ la_status delta_backward(const void* q, const void* k, const void* v, const void
          reinterpret_cast<uintptr_t>(dS_T) | reinterpret_cast<uintptr_t>(dS0)) & 3u))
         return fail(LA_ERR_INVALID_ARG, "%s: beta must be 2-byte and the fp32 arrays 4-byte aligned", fn);
     const Plan plan = make_plan(kFamDelta, b, dk, dv);
-    const size_t need = sizeof(float) * la::delta_backward_ws_floats((long)plan.sm.H * plan.sm.NS, B * H, T, dk, dv);
+    const size_t need = sizeof(float) * la::delta_backward_ws_floats((long)plan.sm.H * plan.sm.NS,
+                                                                     (long)plan.sm.H * plan.sm.chunk_recs_per_head(la::kChunk),
+                                                                     B * H, T, dk, dv);
     if (!workspace || workspace_bytes < need || !aligned16(workspace))
         return fail(LA_ERR_WORKSPACE, "%s: workspace of %zu bytes (16-byte aligned) required, got %zu", fn, need,
                     workspace ? workspace_bytes : (size_t)0);

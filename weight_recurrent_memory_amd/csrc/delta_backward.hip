@@ -696,7 +696,8 @@ hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const
     float* map_c = ws;                       // forward N_g, then c_g
     float* map_mt = map_c + slots * DK * DV; // forward M_g, then M_g^T
     float* g_end = map_mt + slots * DK * DK; // forward segment states, then segment-end gradients
-    bf16_t* sst = reinterpret_cast<bf16_t*>(g_end + slots * DK * DV);
+    bf16_t* sst = reinterpret_cast<bf16_t*>(ws + delta_ws_floats((long)slots, (long)sm.H * sm.chunk_recs_per_head(CH),
+                                                                 DK, DV));
     bf16_t* gst = sst + (size_t)HT * NC * DK * DV;
     hipError_t err = launch_delta_states(q, k, v, beta, alpha, S0, sst, sm, DK, DV, ws, stream);
     if (err != hipSuccess) return err;
@@ -721,10 +722,11 @@ hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const
 
 }  // namespace
 
-size_t delta_backward_ws_floats(long slots, int HT, int T, int dk, int dv) {
+size_t delta_backward_ws_floats(long slots, long recs, int HT, int T, int dk, int dv) {
     const size_t nc = (size_t)(T + CH - 1) / CH;
-    // the forward's per-slot arrays, then S_c and G'_c tiles (bf16, two per float)
-    return delta_ws_floats(slots, dk, dv) + (size_t)HT * nc * dk * dv;
+    // the forward's arrays (per slot, per chunk record), then S_c and G'_c
+    // tiles (bf16, two per float)
+    return delta_ws_floats(slots, recs, dk, dv) + (size_t)HT * nc * dk * dv;
 }
 
 hipError_t launch_delta_backward(const void* q, const void* k, const void* v, const void* beta, const float* alpha,

@@ -71,19 +71,15 @@ struct DL {
     static constexpr int LQ = DK + 8;  // bf16 rows with k = dk
     static constexpr int LV = NS + 8;  // bf16 rows of V
     static constexpr int LT = CH + 8;  // bf16 rows with k = token
-    static constexpr int LF = CH + 4;  // fp32 rows of the C x C work matrix
     static constexpr int KS = CH * LQ * 2;          // K_c rows (read transposed too)
     static constexpr int WS = CH * LQ * 2;          // W rows
     static constexpr int QS = OUT ? CH * LQ * 2 : 0;
     static constexpr int VS = CH * LV * 2;          // V_c rows (read transposed)
-    static constexpr int TS = CH * LT * 2;          // T (bf16)
-    static constexpr int TG = GATED ? CH * LT * 2 : 0;  // gated: T diag(gamma) (bf16)
+    static constexpr int TS = CH * LT * 2;          // T (bf16, from the chunk's record)
+    static constexpr int TG = GATED ? CH * LT * 2 : 0;  // gated: T diag(gamma) (bf16, record)
     static constexpr int PS = OUT ? CH * LT * 2 : 0;  // tril(Q K^T), rows = queries
-    static constexpr int AF = CH * LF * 4;          // A, then T blocks (fp32)
-    static constexpr int AD = 4 * 256 * 4;          // diagonal blocks of A, transposed (fp32)
-    static constexpr int YF = 4 * 256 * 4;          // A_BL T_TL tiles of the inverse (fp32)
     static constexpr int BS = CH * 4 * (GATED ? 4 : 1);  // beta; gated: log-gates, gamma, gamma_C/gamma (fp32)
-    static constexpr int TOTAL = KS + WS + QS + VS + TS + TG + PS + AF + AD + YF + BS;
+    static constexpr int TOTAL = KS + WS + QS + VS + TS + TG + PS + BS;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
     static constexpr int XR = DK / 16;              // dk row tiles of a state column
     // State column tiles: OUT and STATES carry S (NS columns); MAP carries N
@@ -131,6 +127,81 @@ __host__ __device__ constexpr void lower_tile(int id, int& i, int& j) {
     else { i = 3; j = 0; }                         // (3,0)
 }
 
+constexpr int kRecElems = CH * CH;  // one chunk record: a 64 x 64 bf16 matrix, row-major
+
+// T = (I + A)^{-1} of every chunk, and for the gated rule T diag(gamma):
+// the state-free, latency-bound part of the chunk recurrence, done once per
+// chunk by a fully parallel pass (one workgroup per chunk record) instead of
+// inside every serial chunk loop that needs it.  Rows past the sequence end
+// are zero, as in the loops; the input transforms (kNormQK on k,
+// kBetaSigmoid on beta) are applied as there.
+template <int DK, bool GATED, bool PACKED>
+__global__ __launch_bounds__(NT) void delta_tinv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ beta,
+                                                        const float* __restrict__ alpha, bf16_t* __restrict__ trec,
+                                                        bf16_t* __restrict__ tgrec, int flags, SegMap sm) {
+    constexpr int LQ = DK + 8, LT = dchunk::LT, LF = dchunk::LF;
+    __shared__ __align__(16) __bf16 Ks[CH * LQ];
+    __shared__ __align__(16) __bf16 Ts[CH * LT];
+    __shared__ __align__(16) __bf16 Tgs[GATED ? CH * LT : 8];
+    __shared__ __align__(16) float Af[CH * LF];
+    __shared__ __align__(16) float Ad[4 * 256];
+    __shared__ __align__(16) float Yf[4 * 256];
+    __shared__ float Bs[CH], Gl[CH], Ge[CH], Gc[CH];
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
+    const int w = wave_id(tid);
+    const long rec = blockIdx.x;
+    int n, h, c;
+    if constexpr (!PACKED) {
+        const int ncs = (sm.T + CH - 1) / CH;
+        const int vh = (int)(rec / ncs);
+        c = (int)(rec % ncs);
+        n = vh / sm.H;
+        h = vh % sm.H;
+    } else {  // invert the record map: the largest n with floor(start(n) / C) + n <= r
+        const int R = sm.T / CH + sm.N;
+        h = (int)(rec / R);
+        const int r = (int)(rec % R);
+        int lo = 0, hi = sm.N - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sm.start<true>(mid) / CH + mid <= r) lo = mid;
+            else hi = mid - 1;
+        }
+        n = lo;
+        c = r - (int)(sm.start<true>(n) / CH) - n;
+        if (c < 0 || c * CH >= sm.length<true>(n)) return;  // a gap between sequences
+    }
+    const int c0 = c * CH;
+    const int rows = min(CH, sm.length<PACKED>(n) - c0);
+    const long row0 = h * sm.hs + sm.start<PACKED>(n) + c0;
+    ChunkRegs<bf16_t, DK, NT> kr;
+    kr.load_buf(make_rsrc(k + row0 * DK, (uint32_t)rows * DK * 2), 0, tid);
+    if (flags & kNormQK) stage_rows_l2<DK>(kr, tid, Ks, LQ);
+    else stage_rows_raw<bf16_t, DK, NT>(kr, tid, Ks, LQ);
+    if (tid < CH) {
+        const float braw = bf16_to_f32(
+            __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(beta + row0, (uint32_t)rows * 2), (uint32_t)tid * 2, 0, 0));
+        Bs[tid] = (flags & kBetaSigmoid) ? 1.f / (1.f + __expf(-braw)) : braw;
+        if constexpr (GATED) {
+            const unsigned a = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(alpha + row0, (uint32_t)rows * 4),
+                                                                    (uint32_t)tid * 4, 0, 0);
+            dchunk::gate_prefix(__uint_as_float(a), tid, rows, Gl, Ge, Gc);
+        }
+    }
+    dchunk::clear_upper(Ts, tid);
+    if constexpr (GATED) dchunk::clear_upper(Tgs, tid);
+    __syncthreads();
+    dchunk::build_T<DK, GATED, false, false, GATED>(Ks, nullptr, Bs, Gl, Af, Ad, Yf, Ts, nullptr, w, g, li, nullptr,
+                                                    Tgs, Ge);
+    // one 16-byte row piece per thread: row tid / 8, columns 8 (tid % 8) ..
+    const int row = tid >> 3, col = (tid & 7) * 8;
+    *reinterpret_cast<uint4*>(trec + rec * kRecElems + row * CH + col) =
+        *reinterpret_cast<const uint4*>(&Ts[row * LT + col]);
+    if constexpr (GATED)
+        *reinterpret_cast<uint4*>(tgrec + rec * kRecElems + row * CH + col) =
+            *reinterpret_cast<const uint4*>(&Tgs[row * LT + col]);
+}
+
 // One workgroup runs one segment's chunk loop.  The state-dependent part of
 // a chunk is column-parallel (state columns evolve independently), so each
 // wave owns whole state columns and keeps them, its corrections U and its
@@ -145,14 +216,14 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ beta, const float* __restrict__ alpha, bf16_t* __restrict__ o,
     const float* __restrict__ state_in, float* __restrict__ map_n, float* __restrict__ map_m,
-    float* __restrict__ S_out, bf16_t* __restrict__ pred, bf16_t* __restrict__ states, int flags, SegMap sm) {
+    float* __restrict__ S_out, bf16_t* __restrict__ pred, bf16_t* __restrict__ states,
+    const bf16_t* __restrict__ trec, const bf16_t* __restrict__ tgrec, int flags, SegMap sm) {
     constexpr bool OUT = MODE == kOut, MAP = MODE == kMap;
     static_assert(MODE != kStates || !PACKED, "chunk states are for uniform batches");
     using Y = DL<DK, NS, MODE, GATED>;
     using M = Mma<bf16_t>;
-    using MF = Mma<float>;
     typedef M::frag frag;
-    constexpr int LQ = Y::LQ, LV = Y::LV, LT = Y::LT, LF = Y::LF, XR = Y::XR, SLOTS = Y::SLOTS;
+    constexpr int LQ = Y::LQ, LV = Y::LV, LT = Y::LT, XR = Y::XR, SLOTS = Y::SLOTS;
     __shared__ __align__(16) unsigned char smem[Y::TOTAL];
     unsigned char* sp = smem;
     __bf16* Ks = reinterpret_cast<__bf16*>(sp);  sp += Y::KS;
@@ -162,10 +233,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     __bf16* Ts = reinterpret_cast<__bf16*>(sp);  sp += Y::TS;
     __bf16* Tg = reinterpret_cast<__bf16*>(sp);  sp += Y::TG;
     __bf16* Ps = reinterpret_cast<__bf16*>(sp);  sp += Y::PS;
-    float* Af = reinterpret_cast<float*>(sp);
-    float* Ad = Af + CH * LF;
-    float* Yf = Ad + 4 * 256;
-    float* Bs = Yf + 4 * 256;
+    float* Bs = reinterpret_cast<float*>(sp);
     float* Gl = Bs + CH;  // gated: chunk-local cumulative log-gate
     float* Ge = Gl + CH;  //        gamma_t = exp(Gl[t])
     float* Gc = Ge + CH;  //        gamma_C / gamma_t
@@ -232,25 +300,23 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     ChunkRegs<bf16_t, NS, NT> vr;
     unsigned short bnext = 0;
     unsigned anext = 0;
+    uint4 tnext, tgnext;  // this thread's 16 bytes of the chunk's T (and T diag(gamma)) record
     auto load_chunk = [&](int c, int tid) {
         kr.load_buf(rk, c, tid);
         if constexpr (OUT) qr.load_buf(rq, c, tid);
         vr.load_buf(rv, c, tid);
+        const long rec = sm.chunk_rec<PACKED>(nseq, h, c / CH, CH) * kRecElems + tid * 8;
+        tnext = *reinterpret_cast<const uint4*>(trec + rec);
+        if constexpr (GATED) tgnext = *reinterpret_cast<const uint4*>(tgrec + rec);
         if (tid < CH) {
             bnext = __builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(c + tid) * 2, 0, 0);
             if constexpr (GATED) anext = __builtin_amdgcn_raw_buffer_load_b32(ra, (uint32_t)(c + tid) * 4, 0, 0);
         }
     };
     load_chunk(seg * L, tid);
-    // Upper blocks of T and, for outputs, of P (keys after every query of
-    // the tile) are read as zero operands and never written: clear them once.
-    for (int e = tid; e < 6 * 256; e += NT) {
-        const int tile = e >> 8, r = (e >> 4) & 15, c = e & 15;
-        const int bi = tile < 3 ? 0 : tile < 5 ? 1 : 2;
-        const int bj = tile < 3 ? tile + 1 : tile < 5 ? tile - 1 : 3;
-        Ts[(16 * bi + r) * LT + 16 * bj + c] = M::cvt(0.f);
-        if constexpr (GATED) Tg[(16 * bi + r) * LT + 16 * bj + c] = M::cvt(0.f);
-    }
+    // Upper blocks of P (keys after every query of the tile) are read as
+    // zero operands and never written: clear them once.  (T's records carry
+    // their zero blocks.)
     if constexpr (OUT) {
         for (int e = tid; e < 6 * 256; e += NT) {
             const int tile = e >> 8, r = (e >> 4) & 15, c = e & 15;
@@ -289,6 +355,8 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
             if constexpr (OUT) stage_rows_raw<bf16_t, DK, NT>(qr, tid, Qs, LQ);
         }
         stage_rows_raw<bf16_t, NS, NT>(vr, tid, Vs, LV);
+        *reinterpret_cast<uint4*>(&Ts[(tid >> 3) * LT + (tid & 7) * 8]) = tnext;
+        if constexpr (GATED) *reinterpret_cast<uint4*>(&Tg[(tid >> 3) * LT + (tid & 7) * 8]) = tgnext;
         if (tid < CH) {  // wave 0
             const float braw = bf16_to_f32(bnext);
             Bs[tid] = (flags & kBetaSigmoid) ? 1.f / (1.f + __expf(-braw)) : braw;
@@ -310,194 +378,47 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         if (c0 + CH < t_end) load_chunk(c0 + CH, tid);
         __syncthreads();
 
-        // ---- A = tril_{-1}(K K^T) diag(beta) (fp32) and, for outputs, the
-        // causal scores P = tril(Q K^T) (bf16, rows = queries), computed as
-        // transposed tiles so each lane writes four consecutive keys
-        // Wave w builds tiles w, w + 8, w + 16 (compile-time ids, so the
-        // loads of all its tiles can be issued up front).  Diagonal blocks of
-        // A also go to Ad transposed (row m = column m of the block), for the
-        // column-oriented substitution below.
-        auto ap_tile = [&](auto idc) {
-            constexpr int id = decltype(idc)::value;
-            constexpr int NTILE = OUT ? 20 : 10;
-            if constexpr (id < NTILE) {
-                constexpr int bi = id % 10 < 4 ? id % 10 : id % 10 < 7 ? id % 10 - 3 : id % 10 < 9 ? id % 10 - 5 : 3;
-                constexpr int bj = id % 10 < 4 ? id % 10 : id % 10 < 7 ? id % 10 - 4 : id % 10 < 9 ? id % 10 - 7 : 0;
-                v4f acc = zero4();
-                if constexpr (id < 10) {
-#pragma unroll
-                    for (int kb = 0; kb < DK / 32; ++kb)
-                        M::mma(acc, M::load(&Ks[(16 * bi + li) * LQ + 32 * kb], g),
-                               M::load(&Ks[(16 * bj + li) * LQ + 32 * kb], g));
-                    v4f a;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int t = 16 * bi + 4 * g + r, i = 16 * bj + li;
-                        float x = Bs[i] * acc[r];
-                        // (above the diagonal the ratio may overflow: the select drops it)
-                        if constexpr (GATED) x *= __expf(Gl[t] - Gl[i]);
-                        a[r] = (i < t) ? x : 0.f;
-                        Af[t * LF + i] = a[r];
-                    }
-                    if constexpr (bi == bj) *reinterpret_cast<v4f*>(&Ad[bi * 256 + li * 16 + 4 * g]) = a;
-                } else {
-                    // keys of tile bj (rows) x queries of tile bi (columns)
-#pragma unroll
-                    for (int kb = 0; kb < DK / 32; ++kb)
-                        M::mma(acc, M::load(&Ks[(16 * bj + li) * LQ + 32 * kb], g),
-                               M::load(&Qs[(16 * bi + li) * LQ + 32 * kb], g));
-                    if constexpr (GATED) {  // gamma_query / gamma_key
-                        const float gq = Gl[16 * bi + li];
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[r] *= __expf(gq - Gl[16 * bj + 4 * g + r]);
-                    }
-                    uint2 pk;
-                    pk.x = pack_bf16x2((bi == bj && 4 * g + 0 > li) ? 0.f : acc[0],
-                                       (bi == bj && 4 * g + 1 > li) ? 0.f : acc[1]);
-                    pk.y = pack_bf16x2((bi == bj && 4 * g + 2 > li) ? 0.f : acc[2],
-                                       (bi == bj && 4 * g + 3 > li) ? 0.f : acc[3]);
-                    *reinterpret_cast<uint2*>(&Ps[(16 * bi + li) * LT + 16 * bj + 4 * g]) = pk;
-                }
-            }
-        };
-        auto ap_wave = [&](auto wc) {
-            constexpr int W = decltype(wc)::value;
-            ap_tile(std::integral_constant<int, W>{});
-            ap_tile(std::integral_constant<int, W + 8>{});
-            ap_tile(std::integral_constant<int, W + 16>{});
-        };
-        switch (w) {
-            case 0: ap_wave(std::integral_constant<int, 0>{}); break;
-            case 1: ap_wave(std::integral_constant<int, 1>{}); break;
-            case 2: ap_wave(std::integral_constant<int, 2>{}); break;
-            case 3: ap_wave(std::integral_constant<int, 3>{}); break;
-            case 4: ap_wave(std::integral_constant<int, 4>{}); break;
-            case 5: ap_wave(std::integral_constant<int, 5>{}); break;
-            case 6: ap_wave(std::integral_constant<int, 6>{}); break;
-            default: ap_wave(std::integral_constant<int, 7>{}); break;
-        }
-        __syncthreads();
-
-        // outputs, first half: O^T = S^T Q^T with the state entering the chunk
-        // (waves 1.. here, while wave 0 inverts the diagonal blocks; wave 0
-        // while waves 1..3 build the off-diagonal blocks)
+        // ---- outputs: the causal scores P = tril(Q K^T) (bf16, rows =
+        // queries; gated: o Gamma), computed as transposed tiles so each lane
+        // writes four consecutive keys; wave w builds lower tiles w, w + 8;
+        // then O^T = S^T Q^T with the state entering the chunk
         v4f Oq[OUT ? 4 : 1];
-        auto out_first_half = [&]() {
-            if constexpr (OUT) {
+        if constexpr (OUT) {
 #pragma unroll
-                for (int qt = 0; qt < 4; ++qt) {
-                    Oq[qt] = zero4();
-                    if (w < Y::NCT) {
+            for (int jj = 0; jj < 2; ++jj) {
+                const int id = w + NWV * jj;
+                if (id >= 10) break;
+                int bi, bj;
+                lower_tile(id, bi, bj);
+                v4f acc = zero4();
 #pragma unroll
-                        for (int kb = 0; kb < DK / 32; ++kb)
-                            M::mma(Oq[qt], M::from_tiles(X[0][2 * kb], X[0][2 * kb + 1]),
-                                   M::load(&Qs[(16 * qt + li) * LQ + 32 * kb], g));
-                    }
-                    if constexpr (GATED) Oq[qt] *= Ge[16 * qt + li];  // diag(gamma) Q S
+                for (int kb = 0; kb < DK / 32; ++kb)
+                    M::mma(acc, M::load(&Ks[(16 * bj + li) * LQ + 32 * kb], g),
+                           M::load(&Qs[(16 * bi + li) * LQ + 32 * kb], g));
+                if constexpr (GATED) {  // gamma_query / gamma_key
+                    const float gq = Gl[16 * bi + li];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[r] *= __expf(gq - Gl[16 * bj + 4 * g + r]);
                 }
+                uint2 pk;
+                pk.x = pack_bf16x2((bi == bj && 4 * g + 0 > li) ? 0.f : acc[0],
+                                   (bi == bj && 4 * g + 1 > li) ? 0.f : acc[1]);
+                pk.y = pack_bf16x2((bi == bj && 4 * g + 2 > li) ? 0.f : acc[2],
+                                   (bi == bj && 4 * g + 3 > li) ? 0.f : acc[3]);
+                *reinterpret_cast<uint2*>(&Ps[(16 * bi + li) * LT + 16 * bj + 4 * g]) = pk;
             }
-        };
-        if (w != 0) out_first_half();
-
-        // ---- diagonal blocks of T: (I + A_bb)^{-1} by forward substitution,
-        // column-oriented: wave 0, lane 16b+j holds column j of block b; at
-        // step m every later entry takes its A_bb[i][m] d[m] term at once, so
-        // the dependent chain is one multiply-add per step.  The block goes
-        // to Af (fp32, for the off-diagonal blocks) and Ts (bf16).
-        if (w == 0) {
-            const int b = g, j = li;
-            float d[16];
 #pragma unroll
-            for (int m = 0; m < 16; ++m) d[m] = (m == j) ? 1.f : 0.f;
+            for (int qt = 0; qt < 4; ++qt) {
+                Oq[qt] = zero4();
+                if (w < Y::NCT) {
 #pragma unroll
-            for (int m = 0; m < 15; ++m) {
-                const v4f* col = reinterpret_cast<const v4f*>(&Ad[b * 256 + m * 16]);  // A_bb[.][m]
-                const v4f c[4] = {col[0], col[1], col[2], col[3]};
-#pragma unroll
-                for (int i = m + 1; i < 16; ++i) d[i] -= c[i >> 2][i & 3] * d[m];
-            }
-            const float gj = GATED ? Ge[16 * b + j] : 1.f;
-#pragma unroll
-            for (int m = 0; m < 16; ++m) {
-                Af[(16 * b + m) * LF + 16 * b + j] = d[m];
-                Ts[(16 * b + m) * LT + 16 * b + j] = M::cvt(d[m]);
-                if constexpr (GATED) Tg[(16 * b + m) * LT + 16 * b + j] = M::cvt(d[m] * gj);
+                    for (int kb = 0; kb < DK / 32; ++kb)
+                        M::mma(Oq[qt], M::from_tiles(X[0][2 * kb], X[0][2 * kb + 1]),
+                               M::load(&Qs[(16 * qt + li) * LQ + 32 * kb], g));
+                }
+                if constexpr (GATED) Oq[qt] *= Ge[16 * qt + li];  // diag(gamma) Q S
             }
         }
-        __syncthreads();
-        if (w == 0) out_first_half();
-
-        // ---- off-diagonal blocks by 2x2 block doubling.  The inverse of a
-        // block lower-triangular [[M11, 0], [M21, M22]] is [[M11^-1, 0],
-        // [-M22^-1 M21 M11^-1, M22^-1]]: first the two 32x32 diagonal blocks
-        // (T10 = -D1 A10 D0, T32 = -D3 A32 D2), then the lower-left 32x32
-        // block -T_BR (A_BL T_TL) in two steps of four 16x16 tiles.  Blocks:
-        // D_b at rows 16b, cols 16b of Af; A_ij (i > j) at rows 16i, cols 16j;
-        // T10 and T32 stored at rows 16j, cols 16i (the unused upper half).
-        auto rowA = [&](int r0, int c0) {  // row-layout operand of the block at (r0, c0)
-            return *reinterpret_cast<const v4f*>(&Af[(r0 + li) * LF + c0 + 4 * g]);
-        };
-        auto colB = [&](int r0, int c0) {  // output-layout operand of the block at (r0, c0)
-            v4f bb;
-#pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) bb[s2] = Af[(r0 + 4 * g + s2) * LF + c0 + li];
-            return bb;
-        };
-        auto yB = [&](int t) {
-            v4f bb;
-#pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) bb[s2] = Yf[t * 256 + (4 * g + s2) * 16 + li];
-            return bb;
-        };
-        auto put_T = [&](int bi, int bj, const v4f& x) {  // T block (bi, bj), bi > bj, to Ts (bf16)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Ts[(16 * bi + 4 * g + r) * LT + 16 * bj + li] = M::cvt(x[r]);
-            if constexpr (GATED) {  // and T diag(gamma) to Tg
-                const float gc = Ge[16 * bj + li];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) Tg[(16 * bi + 4 * g + r) * LT + 16 * bj + li] = M::cvt(x[r] * gc);
-            }
-        };
-        if (w == 1 || w == 2) {
-            const int lo = w == 1 ? 0 : 32;  // T10 (w 1) or T32 (w 2)
-            v4f P = zero4(), X = zero4();
-            MF::mma(P, rowA(lo + 16, lo), colB(lo, lo));
-            MF::mma(X, rowA(lo + 16, lo + 16), P);
-            X = -X;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Af[(lo + 4 * g + r) * LF + lo + 16 + li] = X[r];
-            put_T(lo / 16 + 1, lo / 16, X);
-        }
-        __syncthreads();
-        if (w >= 1 && w <= 4) {
-            // Y = A_BL T_TL: Y00 = A20 D0 + A21 T10, Y01 = A21 D1,
-            // Y10 = A30 D0 + A31 T10, Y11 = A31 D1
-            const int t = w - 1, yr = t >> 1, yc = t & 1;
-            v4f Y = zero4();
-            if (yc == 0) {
-                MF::mma(Y, rowA(32 + 16 * yr, 0), colB(0, 0));
-                MF::mma(Y, rowA(32 + 16 * yr, 16), colB(0, 16));
-            } else {
-                MF::mma(Y, rowA(32 + 16 * yr, 16), colB(16, 16));
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Yf[t * 256 + (4 * g + r) * 16 + li] = Y[r];
-        }
-        __syncthreads();
-        if (w >= 1 && w <= 4) {
-            // T20 = -D2 Y00, T21 = -D2 Y01, T30 = -(T32 Y00 + D3 Y10),
-            // T31 = -(T32 Y01 + D3 Y11)
-            const int t = w - 1, xr = t >> 1, xc = t & 1;
-            v4f X = zero4();
-            if (xr == 0) {
-                MF::mma(X, rowA(32, 32), yB(xc));
-            } else {
-                MF::mma(X, rowA(32, 48), yB(xc));
-                MF::mma(X, rowA(48, 48), yB(2 + xc));
-            }
-            put_T(2 + xr, xc, -X);
-        }
-        __syncthreads();
 
         // ---- W = T K (gated: T diag(gamma) K, from Tg; computed as
         // transposed tiles, rows land as 8-byte stores) and this wave's
@@ -710,17 +631,22 @@ hipError_t launch_packing(const bf16_t* q, const bf16_t* k, const bf16_t* v, con
     float* map_n = ws;
     float* map_m = map_n + slots * DK * DV;
     float* state_in = map_m + slots * DK * DK;
+    bf16_t* trec = reinterpret_cast<bf16_t*>(state_in + slots * DK * DV);
+    const long recs = (long)sm.H * sm.chunk_recs_per_head(CH);
+    bf16_t* tgrec = GATED ? trec + recs * kRecElems : nullptr;
     hipError_t err;
+    delta_tinv_kernel<DK, GATED, PACKED><<<dim3(recs), dim3(NT), 0, stream>>>(k, beta, alpha, trec, tgrec, flags, sm);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
     if (sm.NS > sm.N) {
         delta_chunk_kernel<DK, DV, kMap, GATED, PACKED><<<dim3(sm.H * (sm.NS - sm.N)), dim3(NT), 0, stream>>>(
-            q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, nullptr, nullptr, flags, sm);
+            q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, nullptr, nullptr, trec, tgrec, flags, sm);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     delta_compose_kernel<DK, DV, PACKED><<<dim3(DV / 16, sm.N * sm.H), dim3(256), 0, stream>>>(map_n, map_m, S0, state_in,
                                                                                       sm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     delta_chunk_kernel<DK, DV, kOut, GATED, PACKED><<<dim3(sm.H * sm.NS), dim3(NT), 0, stream>>>(
-        q, k, v, beta, alpha, o, state_in, nullptr, nullptr, S_out, pred, nullptr, flags, sm);
+        q, k, v, beta, alpha, o, state_in, nullptr, nullptr, S_out, pred, nullptr, trec, tgrec, flags, sm);
     return hipGetLastError();
 }
 
@@ -733,17 +659,22 @@ hipError_t launch_states(const bf16_t* q, const bf16_t* k, const bf16_t* v, cons
     float* map_n = ws;
     float* map_m = map_n + slots * DK * DV;
     float* state_in = map_m + slots * DK * DK;
+    bf16_t* trec = reinterpret_cast<bf16_t*>(state_in + slots * DK * DV);
+    const long recs = (long)sm.H * sm.chunk_recs_per_head(CH);
+    bf16_t* tgrec = GATED ? trec + recs * kRecElems : nullptr;
     hipError_t err;
+    delta_tinv_kernel<DK, GATED, false><<<dim3(recs), dim3(NT), 0, stream>>>(k, beta, alpha, trec, tgrec, 0, sm);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
     if (sm.NS > sm.N) {
         delta_chunk_kernel<DK, DV, kMap, GATED, false><<<dim3(sm.H * (sm.NS - sm.N)), dim3(NT), 0, stream>>>(
-            q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, nullptr, nullptr, 0, sm);
+            q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, nullptr, nullptr, trec, tgrec, 0, sm);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     delta_compose_kernel<DK, DV, false><<<dim3(DV / 16, sm.N * sm.H), dim3(256), 0, stream>>>(map_n, map_m, S0,
                                                                                           state_in, sm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     delta_chunk_kernel<DK, DV, kStates, GATED, false><<<dim3(sm.H * sm.NS), dim3(NT), 0, stream>>>(
-        q, k, v, beta, alpha, nullptr, state_in, nullptr, nullptr, nullptr, nullptr, states, 0, sm);
+        q, k, v, beta, alpha, nullptr, state_in, nullptr, nullptr, nullptr, nullptr, states, trec, tgrec, 0, sm);
     return hipGetLastError();
 }
 
@@ -796,8 +727,9 @@ hipError_t launch_delta_compose_rev(const float* map_c, const float* map_mt, con
     return hipErrorInvalidValue;
 }
 
-size_t delta_ws_floats(long slots, int dk, int dv) {
-    return (size_t)slots * ((size_t)dk * dv + (size_t)dk * dk + (size_t)dk * dv);
+size_t delta_ws_floats(long slots, long recs, int dk, int dv) {
+    // per slot: N_g, M_g, S_in; per chunk record: T and T diag(gamma), bf16
+    return (size_t)slots * ((size_t)dk * dv + (size_t)dk * dk + (size_t)dk * dv) + (size_t)recs * kRecElems;
 }
 
 hipError_t launch_delta_forward(const void* q, const void* k, const void* v, const void* beta,

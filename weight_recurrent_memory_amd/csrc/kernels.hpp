@@ -43,15 +43,17 @@ hipError_t launch_segment_prefix(const int* cu, int N, int T_total, int L, int* 
 constexpr int kNormQK = 1;        // q, k rows scaled to unit L2 norm in the kernel
 constexpr int kBetaSigmoid = 2;   // beta holds logits; the kernel applies a sigmoid
 
-// Delta-rule prefill: segment affine maps -> serial composition -> chunked
-// outputs.  alpha (fp32 [HT][T]) selects the gated rule; NULL = ungated.
+// Delta-rule prefill: every chunk's T = (I + A)^{-1} (a parallel pass) ->
+// segment affine maps -> serial composition -> chunked outputs.  alpha (fp32
+// [HT][T]) selects the gated rule; NULL = ungated.
 // pred (optional, [HT][T][dv] in the input dtype) receives the prediction
 // made before each write.
 hipError_t launch_delta_forward(const void* q, const void* k, const void* v,
                                 const void* beta, const float* alpha, const float* S0,
                                 void* o, float* S_out, void* pred, int flags, const SegMap& sm,
                                 int dk, int dv, int dtype, float* ws, hipStream_t stream);
-size_t delta_ws_floats(long slots, int dk, int dv);
+// recs = H * sm.chunk_recs_per_head(kChunk) chunk records.
+size_t delta_ws_floats(long slots, long recs, int dk, int dv);
 
 // The backward pass's forward sweep (uniform batches, bf16): every chunk's
 // entering state as bf16 tiles in `states` (layout in delta_chunk.hpp);
@@ -72,7 +74,7 @@ hipError_t launch_delta_backward(const void* q, const void* k, const void* v, co
                                  const float* S0, const void* dO, const float* dS_T, void* dq, void* dk_, void* dv_,
                                  float* dbeta, float* dalpha, float* dS0, const SegMap& sm, int dk, int dv, int dtype,
                                  float* ws, hipStream_t stream);
-size_t delta_backward_ws_floats(long slots, int HT, int T, int dk, int dv);
+size_t delta_backward_ws_floats(long slots, long recs, int HT, int T, int dk, int dv);
 
 // Scalar-decay (Mamba-2 / SSD) prefill: segment maps -> elementwise
 // composition -> chunked outputs.  alpha fp32 [HT][T].  Segments as la_plan.

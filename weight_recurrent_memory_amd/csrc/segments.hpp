@@ -76,6 +76,20 @@ struct SegMap {
         if constexpr (!P) return ((long)n * H + h) * G;
         else return (long)h * NS + sp[n];
     }
+    // Per-chunk records (one per head, sequence and chunk of C tokens):
+    // chunk c of sequence n in head h.  Uniform: (n H + h) ceil(T / C) + c.
+    // Packed: h R + floor(start(n) / C) + n + c with R = floor(T / C) + N
+    // records per head -- increasing in (n, c) and below R, since
+    // floor(a / C) + ceil(b / C) <= floor((a + b) / C) + 1; the gaps between
+    // sequences stay unused.
+    __host__ __device__ long chunk_recs_per_head(int C) const {
+        return packed() ? (long)(T / C + N) : (long)N * ((T + C - 1) / C);
+    }
+    template <bool P>
+    __device__ __forceinline__ long chunk_rec(int n, int h, int c, int C) const {
+        if constexpr (!P) return ((long)n * H + h) * ((T + C - 1) / C) + c;
+        else return (long)h * (T / C + N) + start<true>(n) / C + n + c;
+    }
     // The sequence holding global segment vs (0 <= vs < NS): the largest n
     // with seg_base(n) <= vs.
     template <bool P>
