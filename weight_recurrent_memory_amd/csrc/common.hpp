@@ -284,15 +284,23 @@ __device__ __forceinline__ void stage_rows_phi(const ChunkRegs<TIn, D, NT>& cr, 
     }
 }
 
-// Raw copy of a staged chunk into LDS (operand type == input type).
-template <typename TIn, int D, int NT>
+// Raw copy of a staged chunk into LDS (operand type == input type).  SPLIT8:
+// two 8-byte stores per 16 bytes, for row strides that keep rows only
+// 8-byte aligned.
+template <typename TIn, int D, int NT, bool SPLIT8 = false>
 __device__ __forceinline__ void stage_rows_raw(const ChunkRegs<TIn, D, NT>& cr, int tid,
                                                typename Mma<TIn>::op_t* rm, int ld) {
 #pragma unroll
     for (int j = 0; j < ChunkRegs<TIn, D, NT>::NV; ++j) {
         const int row = ChunkRegs<TIn, D, NT>::row_of(j, tid);
         const int col = ChunkRegs<TIn, D, NT>::col_of(j, tid);
-        *reinterpret_cast<uint4*>(rm + row * ld + col) = cr.r[j];
+        if constexpr (SPLIT8) {
+            uint2* d = reinterpret_cast<uint2*>(rm + row * ld + col);
+            d[0] = make_uint2(cr.r[j].x, cr.r[j].y);
+            d[1] = make_uint2(cr.r[j].z, cr.r[j].w);
+        } else {
+            *reinterpret_cast<uint4*>(rm + row * ld + col) = cr.r[j];
+        }
     }
 }
 

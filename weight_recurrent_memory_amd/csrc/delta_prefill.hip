@@ -65,15 +65,21 @@ constexpr int NWV = 8;
 // the backward pass) only the state entering every chunk.
 enum { kMap = 0, kOut = 1, kStates = 2 };
 
-template <int DK, int NS, int MODE, bool GATED>
+template <int DK, int NS, int MODE, bool GATED, int NWV = 8>
 struct DL {
     static constexpr bool OUT = MODE == kOut, MAP = MODE == kMap;
-    static constexpr int LQ = DK + 8;  // bf16 rows with k = dk
-    static constexpr int LV = NS + 8;  // bf16 rows of V
-    static constexpr int LT = CH + 8;  // bf16 rows with k = token
+    // Row strides (bf16 elements).  Matrices read only as row fragments
+    // (W, Q, T, P) are padded by 4 elements, so the 16 rows of a fragment
+    // start 2 words apart and spread over the banks; K and V, also read with
+    // transpose loads, by 8.  (4-element padding leaves rows 8-byte aligned:
+    // those matrices are staged with 8-byte stores.)
+    static constexpr int LQ = DK + 8;  // K rows
+    static constexpr int LW = DK + 4;  // W and Q rows
+    static constexpr int LV = NS + 8;  // V rows
+    static constexpr int LT = CH + 4;  // T, T diag(gamma) and P rows
     static constexpr int KS = CH * LQ * 2;          // K_c rows (read transposed too)
-    static constexpr int WS = CH * LQ * 2;          // W rows
-    static constexpr int QS = OUT ? CH * LQ * 2 : 0;
+    static constexpr int WS = CH * LW * 2;          // W rows
+    static constexpr int QS = OUT ? CH * LW * 2 : 0;
     static constexpr int VS = CH * LV * 2;          // V_c rows (read transposed)
     static constexpr int TS = CH * LT * 2;          // T (bf16, from the chunk's record)
     static constexpr int TG = GATED ? CH * LT * 2 : 0;  // gated: T diag(gamma) (bf16, record)
@@ -94,13 +100,13 @@ struct DL {
 // Chunk rows of a [T][D] bf16 matrix into LDS scaled to unit L2 norm (a zero
 // row stays zero).  The D/8 threads holding a row are consecutive lanes, so
 // the row's sum of squares is a shuffle reduction within their group.
-template <int D>
-__device__ __forceinline__ void stage_rows_l2(const ChunkRegs<bf16_t, D, NT>& cr, int tid, __bf16* rm, int ld) {
+template <int D, int NTH = NT, bool SPLIT8 = false>
+__device__ __forceinline__ void stage_rows_l2(const ChunkRegs<bf16_t, D, NTH>& cr, int tid, __bf16* rm, int ld) {
     constexpr int TPR = D / 8;
 #pragma unroll
-    for (int j = 0; j < ChunkRegs<bf16_t, D, NT>::NV; ++j) {
-        const int row = ChunkRegs<bf16_t, D, NT>::row_of(j, tid);
-        const int col = ChunkRegs<bf16_t, D, NT>::col_of(j, tid);
+    for (int j = 0; j < ChunkRegs<bf16_t, D, NTH>::NV; ++j) {
+        const int row = ChunkRegs<bf16_t, D, NTH>::row_of(j, tid);
+        const int col = ChunkRegs<bf16_t, D, NTH>::col_of(j, tid);
         float x[8], ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -115,7 +121,13 @@ __device__ __forceinline__ void stage_rows_l2(const ChunkRegs<bf16_t, D, NT>& cr
         y.y = pack_bf16x2(x[2] * inv, x[3] * inv);
         y.z = pack_bf16x2(x[4] * inv, x[5] * inv);
         y.w = pack_bf16x2(x[6] * inv, x[7] * inv);
-        *reinterpret_cast<uint4*>(rm + row * ld + col) = y;
+        if constexpr (SPLIT8) {
+            uint2* d = reinterpret_cast<uint2*>(rm + row * ld + col);
+            d[0] = make_uint2(y.x, y.y);
+            d[1] = make_uint2(y.z, y.w);
+        } else {
+            *reinterpret_cast<uint4*>(rm + row * ld + col) = y;
+        }
     }
 }
 
@@ -211,8 +223,8 @@ __global__ __launch_bounds__(NT) void delta_tinv_kernel(const bf16_t* __restrict
 //   S[:, c] += K^T (beta o U[:, c])
 // The shared, state-free part (A, P, T, W) is computed by all waves through
 // LDS.  MAP runs N and M in the same workgroup, so T and W are built once.
-template <int DK, int NS, int MODE, bool GATED, bool PACKED>
-__global__ __launch_bounds__(NT) void delta_chunk_kernel(
+template <int DK, int NS, int MODE, bool GATED, bool PACKED, int NWV = 8>
+__global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ beta, const float* __restrict__ alpha, bf16_t* __restrict__ o,
     const float* __restrict__ state_in, float* __restrict__ map_n, float* __restrict__ map_m,
@@ -220,7 +232,8 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
     const bf16_t* __restrict__ trec, const bf16_t* __restrict__ tgrec, int flags, SegMap sm) {
     constexpr bool OUT = MODE == kOut, MAP = MODE == kMap;
     static_assert(MODE != kStates || !PACKED, "chunk states are for uniform batches");
-    using Y = DL<DK, NS, MODE, GATED>;
+    constexpr int NT = NWV * 64;  // this instantiation's threads (eight or sixteen waves)
+    using Y = DL<DK, NS, MODE, GATED, NWV>;
     using M = Mma<bf16_t>;
     typedef M::frag frag;
     constexpr int LQ = Y::LQ, LV = Y::LV, LT = Y::LT, XR = Y::XR, SLOTS = Y::SLOTS;
@@ -305,9 +318,11 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         kr.load_buf(rk, c, tid);
         if constexpr (OUT) qr.load_buf(rq, c, tid);
         vr.load_buf(rv, c, tid);
-        const long rec = sm.chunk_rec<PACKED>(nseq, h, c / CH, CH) * kRecElems + tid * 8;
-        tnext = *reinterpret_cast<const uint4*>(trec + rec);
-        if constexpr (GATED) tgnext = *reinterpret_cast<const uint4*>(tgrec + rec);
+        if (NT == 512 || tid < 512) {  // 512 x 16 bytes: one record
+            const long rec = sm.chunk_rec<PACKED>(nseq, h, c / CH, CH) * kRecElems + tid * 8;
+            tnext = *reinterpret_cast<const uint4*>(trec + rec);
+            if constexpr (GATED) tgnext = *reinterpret_cast<const uint4*>(tgrec + rec);
+        }
         if (tid < CH) {
             bnext = __builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(c + tid) * 2, 0, 0);
             if constexpr (GATED) anext = __builtin_amdgcn_raw_buffer_load_b32(ra, (uint32_t)(c + tid) * 4, 0, 0);
@@ -330,9 +345,10 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         // chunk.  Otherwise the many per-lane LDS addresses built from them
         // are hoisted out of the loop and held, then spilled, for its whole
         // length; recomputed here they live only next to their uses.  (The
-        // ungated kernels fit with hoisted addresses and run faster so.)
+        // ungated eight-wave kernels fit with hoisted addresses and run
+        // faster so; sixteen-wave ones have half the registers.)
         int tid_v = threadIdx.x;
-        if constexpr (GATED) asm volatile("" : "+v"(tid_v));
+        if constexpr (GATED || NWV == 16) asm volatile("" : "+v"(tid_v));
         const int tid = tid_v, lane = tid & 63, g = lane >> 4, li = lane & 15;
         const int n = min(CH, t_end - c0);
         if constexpr (MODE == kStates) {  // the state entering this chunk, as bf16 tiles
@@ -348,15 +364,23 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         // ---- stage the chunk row-major (transposed operands are read with
         // transpose loads)
         if (flags & kNormQK) {
-            stage_rows_l2<DK>(kr, tid, Ks, LQ);
-            if constexpr (OUT) stage_rows_l2<DK>(qr, tid, Qs, LQ);
+            stage_rows_l2<DK, NT>(kr, tid, Ks, LQ);
+            if constexpr (OUT) stage_rows_l2<DK, NT, true>(qr, tid, Qs, Y::LW);
         } else {
             stage_rows_raw<bf16_t, DK, NT>(kr, tid, Ks, LQ);
-            if constexpr (OUT) stage_rows_raw<bf16_t, DK, NT>(qr, tid, Qs, LQ);
+            if constexpr (OUT) stage_rows_raw<bf16_t, DK, NT, true>(qr, tid, Qs, Y::LW);
         }
         stage_rows_raw<bf16_t, NS, NT>(vr, tid, Vs, LV);
-        *reinterpret_cast<uint4*>(&Ts[(tid >> 3) * LT + (tid & 7) * 8]) = tnext;
-        if constexpr (GATED) *reinterpret_cast<uint4*>(&Tg[(tid >> 3) * LT + (tid & 7) * 8]) = tgnext;
+        if (NT == 512 || tid < 512) {
+            uint2* dt = reinterpret_cast<uint2*>(&Ts[(tid >> 3) * LT + (tid & 7) * 8]);
+            dt[0] = make_uint2(tnext.x, tnext.y);
+            dt[1] = make_uint2(tnext.z, tnext.w);
+            if constexpr (GATED) {
+                uint2* dg = reinterpret_cast<uint2*>(&Tg[(tid >> 3) * LT + (tid & 7) * 8]);
+                dg[0] = make_uint2(tgnext.x, tgnext.y);
+                dg[1] = make_uint2(tgnext.z, tgnext.w);
+            }
+        }
         if (tid < CH) {  // wave 0
             const float braw = bf16_to_f32(bnext);
             Bs[tid] = (flags & kBetaSigmoid) ? 1.f / (1.f + __expf(-braw)) : braw;
@@ -394,7 +418,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
 #pragma unroll
                 for (int kb = 0; kb < DK / 32; ++kb)
                     M::mma(acc, M::load(&Ks[(16 * bj + li) * LQ + 32 * kb], g),
-                           M::load(&Qs[(16 * bi + li) * LQ + 32 * kb], g));
+                           M::load(&Qs[(16 * bi + li) * Y::LW + 32 * kb], g));
                 if constexpr (GATED) {  // gamma_query / gamma_key
                     const float gq = Gl[16 * bi + li];
 #pragma unroll
@@ -414,7 +438,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
 #pragma unroll
                     for (int kb = 0; kb < DK / 32; ++kb)
                         M::mma(Oq[qt], M::from_tiles(X[0][2 * kb], X[0][2 * kb + 1]),
-                               M::load(&Qs[(16 * qt + li) * LQ + 32 * kb], g));
+                               M::load(&Qs[(16 * qt + li) * Y::LW + 32 * kb], g));
                 }
                 if constexpr (GATED) Oq[qt] *= Ge[16 * qt + li];  // diag(gamma) Q S
             }
@@ -433,7 +457,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
                 M::mma(acc, M::load_tr(Ks, LQ, 32 * kb, 16 * dkt, lane),
                        M::load(&(GATED ? Tg : Ts)[(16 * tt + li) * LT + 32 * kb], g));
             }
-            __bf16* dst = &Ws[(16 * tt + li) * LQ + 16 * dkt + 4 * g];
+            __bf16* dst = &Ws[(16 * tt + li) * Y::LW + 16 * dkt + 4 * g];
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[r] = M::cvt(acc[r]);
         }
@@ -456,21 +480,29 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
         }
         __syncthreads();
 
-        // ---- the state chain, per owned column tile
+        // ---- the state chain over this wave's column tiles.  The chain is
+        // bound by LDS reads, so every operand fragment (a row block of W, a
+        // transposed row block of K) is read once and applied to all of the
+        // wave's tiles.
+        // U = U_v - W S, then beta o U (and, if wanted, the predictions V - U)
 #pragma unroll
-        for (int j = 0; j < SLOTS; ++j) {
-            const int id = w + NWV * j;
-            if (id >= Y::NCT) continue;
-            // U = U_v - W S, then beta o U (and, if wanted, the predictions V - U)
+        for (int tt = 0; tt < 4; ++tt) {
+            v4f ws_[SLOTS];
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                v4f ws_ = zero4();
+            for (int j = 0; j < SLOTS; ++j) ws_[j] = zero4();
 #pragma unroll
-                for (int kb = 0; kb < DK / 32; ++kb)
-                    M::mma(ws_, M::load(&Ws[(16 * tt + li) * LQ + 32 * kb], g),
-                           M::from_tiles(X[j][2 * kb], X[j][2 * kb + 1]));
+            for (int kb = 0; kb < DK / 32; ++kb) {
+                const frag wf = M::load(&Ws[(16 * tt + li) * Y::LW + 32 * kb], g);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) U[j][tt][r] -= ws_[r];
+                for (int j = 0; j < SLOTS; ++j)
+                    if (w + NWV * j < Y::NCT) M::mma(ws_[j], wf, M::from_tiles(X[j][2 * kb], X[j][2 * kb + 1]));
+            }
+#pragma unroll
+            for (int j = 0; j < SLOTS; ++j) {
+                const int id = w + NWV * j;
+                if (id >= Y::NCT) continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) U[j][tt][r] -= ws_[j][r];
                 if constexpr (OUT) {
                     if (pred) {  // rows past the segment end are dropped by the resource
                         const rsrc_t rp = make_rsrc(pred + row0 * NS, (uint32_t)t_end * NS * 2);
@@ -486,6 +518,11 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) U[j][tt][r] *= Bs[16 * tt + 4 * g + r];
             }
+        }
+#pragma unroll
+        for (int j = 0; j < SLOTS; ++j) {
+            const int id = w + NWV * j;
+            if (id >= Y::NCT) continue;
             if constexpr (OUT) {
                 // outputs, second half: O^T += (beta o U)^T P^T, stored
                 bf16_t* oh = o + (row0 + c0) * NS + 16 * id + 4 * g;
@@ -506,7 +543,7 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
                     }
                 }
             }
-            // S += K^T (beta o U); gated: S = gamma_C S + K^T (beta gamma_C / gamma o U)
+            // gated: S = gamma_C S + K^T (beta gamma_C / gamma o U)
             if constexpr (GATED) {
                 const float gend = Ge[CH - 1];
 #pragma unroll
@@ -516,13 +553,17 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
 #pragma unroll
                 for (int i = 0; i < XR; ++i) X[j][i] *= gend;
             }
-#pragma unroll
-            for (int i = 0; i < XR; ++i)
-#pragma unroll
-                for (int kb = 0; kb < CH / 32; ++kb)
-                    M::mma(X[j][i], M::load_tr(Ks, LQ, 32 * kb, 16 * i, lane),
-                           M::from_tiles(U[j][2 * kb], U[j][2 * kb + 1]));
         }
+        // S += K^T (beta o U)
+#pragma unroll
+        for (int i = 0; i < XR; ++i)
+#pragma unroll
+            for (int kb = 0; kb < CH / 32; ++kb) {
+                const frag kf = M::load_tr(Ks, LQ, 32 * kb, 16 * i, lane);
+#pragma unroll
+                for (int j = 0; j < SLOTS; ++j)
+                    if (w + NWV * j < Y::NCT) M::mma(X[j][i], kf, M::from_tiles(U[j][2 * kb], U[j][2 * kb + 1]));
+            }
         __syncthreads();
     }
 
@@ -551,6 +592,12 @@ __global__ __launch_bounds__(NT) void delta_chunk_kernel(
             for (int r = 0; r < 4; ++r) dst[(16 * i + 4 * g + r) * ld + col] = X[j][i][r];
     }
 }
+
+// Waves per workgroup of the map pass: with dk = dv = 128 it carries 16
+// state column tiles, one per wave of a sixteen-wave workgroup (twice the
+// waves per SIMD to hide LDS-operand latency, half the registers per wave).
+template <int DK, int DV>
+constexpr int kMapWaves = (DK == 128 && DV == 128) ? 16 : 8;
 
 // S_in(0) = S0 (or 0); S_in(g+1) = M_g S_in(g) + N_g in fp32 MFMA.  One
 // workgroup per (16-column block of the state, sequence and head); serial
@@ -638,7 +685,8 @@ hipError_t launch_packing(const bf16_t* q, const bf16_t* k, const bf16_t* v, con
     delta_tinv_kernel<DK, GATED, PACKED><<<dim3(recs), dim3(NT), 0, stream>>>(k, beta, alpha, trec, tgrec, flags, sm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (sm.NS > sm.N) {
-        delta_chunk_kernel<DK, DV, kMap, GATED, PACKED><<<dim3(sm.H * (sm.NS - sm.N)), dim3(NT), 0, stream>>>(
+        constexpr int NWM = kMapWaves<DK, DV>;
+        delta_chunk_kernel<DK, DV, kMap, GATED, PACKED, NWM><<<dim3(sm.H * (sm.NS - sm.N)), dim3(NWM * 64), 0, stream>>>(
             q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, nullptr, nullptr, trec, tgrec, flags, sm);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
@@ -666,7 +714,8 @@ hipError_t launch_states(const bf16_t* q, const bf16_t* k, const bf16_t* v, cons
     delta_tinv_kernel<DK, GATED, false><<<dim3(recs), dim3(NT), 0, stream>>>(k, beta, alpha, trec, tgrec, 0, sm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (sm.NS > sm.N) {
-        delta_chunk_kernel<DK, DV, kMap, GATED, false><<<dim3(sm.H * (sm.NS - sm.N)), dim3(NT), 0, stream>>>(
+        constexpr int NWM = kMapWaves<DK, DV>;
+        delta_chunk_kernel<DK, DV, kMap, GATED, false, NWM><<<dim3(sm.H * (sm.NS - sm.N)), dim3(NWM * 64), 0, stream>>>(
             q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, nullptr, nullptr, trec, tgrec, 0, sm);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
