@@ -91,7 +91,8 @@ __device__ __forceinline__ void clear_upper(__bf16* X, int tid) {
 //
 // Builds T = (I + A)^{-1} (bf16, lower blocks of Ts) and, with WANT_P, the
 // causal scores P (bf16, lower blocks of Ps, rows = queries).  Ks, Qs: the
-// staged chunk rows ([C][DK + 8] bf16; rows past the chunk end zero); Bs:
+// staged chunk rows ([C][LQ] bf16, LQ = DK + 8 unless given; rows past the
+// chunk end zero); Bs:
 // betas; Gl: cumulative log-gates (GATED).  Af ([C][LF] fp32), Ad and Yf
 // (4 x 256 fp32 each) are scratch.  Called by all threads of the workgroup
 // after the chunk is staged and visible; ends with a barrier.  With KEEP,
@@ -103,14 +104,13 @@ __device__ __forceinline__ void clear_upper(__bf16* X, int tid) {
 // one column per lane); the rest by 2x2 block doubling: the inverse of
 // [[M11, 0], [M21, M22]] is [[M11^-1, 0], [-M22^-1 M21 M11^-1, M22^-1]],
 // first on the 32x32 diagonal blocks, then on the lower-left 32x32 block.
-template <int DK, bool GATED, bool WANT_P, bool KEEP = false, bool TG = false>
+template <int DK, bool GATED, bool WANT_P, bool KEEP = false, bool TG = false, int LQ = DK + 8>
 __device__ __forceinline__ void build_T(const __bf16* Ks, const __bf16* Qs, const float* Bs, const float* Gl,
                                         float* Af, float* Ad, float* Yf, __bf16* Ts, __bf16* Ps, int w, int g,
                                         int li, v4f* keep = nullptr, __bf16* Tg = nullptr,
                                         const float* Ge = nullptr) {
     using M = Mma<bf16_t>;
     using MF = Mma<float>;
-    constexpr int LQ = DK + 8;
     constexpr int NTILE = WANT_P ? 20 : 10;
 #pragma unroll
     for (int jj = 0; jj < 3; ++jj) {

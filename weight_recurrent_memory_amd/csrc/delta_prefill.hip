@@ -151,7 +151,10 @@ template <int DK, bool GATED, bool PACKED>
 __global__ __launch_bounds__(NT) void delta_tinv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ beta,
                                                         const float* __restrict__ alpha, bf16_t* __restrict__ trec,
                                                         bf16_t* __restrict__ tgrec, int flags, SegMap sm) {
-    constexpr int LQ = DK + 8, LT = dchunk::LT, LF = dchunk::LF;
+    // K is read only as row fragments here (K K^T tiles): rows padded by 4
+    // elements spread a fragment's 16 rows over the banks (staged with
+    // 8-byte stores)
+    constexpr int LQ = DK + 4, LT = dchunk::LT, LF = dchunk::LF;
     __shared__ __align__(16) __bf16 Ks[CH * LQ];
     __shared__ __align__(16) __bf16 Ts[CH * LT];
     __shared__ __align__(16) __bf16 Tgs[GATED ? CH * LT : 8];
@@ -188,8 +191,8 @@ __global__ __launch_bounds__(NT) void delta_tinv_kernel(const bf16_t* __restrict
     const long row0 = h * sm.hs + sm.start<PACKED>(n) + c0;
     ChunkRegs<bf16_t, DK, NT> kr;
     kr.load_buf(make_rsrc(k + row0 * DK, (uint32_t)rows * DK * 2), 0, tid);
-    if (flags & kNormQK) stage_rows_l2<DK>(kr, tid, Ks, LQ);
-    else stage_rows_raw<bf16_t, DK, NT>(kr, tid, Ks, LQ);
+    if (flags & kNormQK) stage_rows_l2<DK, NT, true>(kr, tid, Ks, LQ);
+    else stage_rows_raw<bf16_t, DK, NT, true>(kr, tid, Ks, LQ);
     if (tid < CH) {
         const float braw = bf16_to_f32(
             __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(beta + row0, (uint32_t)rows * 2), (uint32_t)tid * 2, 0, 0));
@@ -203,8 +206,8 @@ __global__ __launch_bounds__(NT) void delta_tinv_kernel(const bf16_t* __restrict
     dchunk::clear_upper(Ts, tid);
     if constexpr (GATED) dchunk::clear_upper(Tgs, tid);
     __syncthreads();
-    dchunk::build_T<DK, GATED, false, false, GATED>(Ks, nullptr, Bs, Gl, Af, Ad, Yf, Ts, nullptr, w, g, li, nullptr,
-                                                    Tgs, Ge);
+    dchunk::build_T<DK, GATED, false, false, GATED, LQ>(Ks, nullptr, Bs, Gl, Af, Ad, Yf, Ts, nullptr, w, g, li,
+                                                        nullptr, Tgs, Ge);
     // one 16-byte row piece per thread: row tid / 8, columns 8 (tid % 8) ..
     const int row = tid >> 3, col = (tid & 7) * 8;
     *reinterpret_cast<uint4*>(trec + rec * kRecElems + row * CH + col) =
