@@ -49,7 +49,6 @@ namespace la {
 namespace {
 
 using dchunk::CH;
-using dchunk::LF;
 using dchunk::LT;
 using dchunk::NT;
 using dchunk::NWV;
@@ -63,9 +62,8 @@ struct RC {
     static constexpr int LQ = DK + 8, LV = DV + 8;
     static constexpr int KS = CH * LQ * 2, QS = CH * LQ * 2, OS = CH * LV * 2;
     static constexpr int TS = CH * LT * 2, PS = CH * LT * 2;
-    static constexpr int AF = CH * LF * 4, AD = 4 * 256 * 4, YF = 4 * 256 * 4;
     static constexpr int BS = CH * 4 * (GATED ? 4 : 1);
-    static constexpr int TOTAL = KS + QS + OS + TS + PS + AF + AD + YF + BS;
+    static constexpr int TOTAL = KS + QS + OS + TS + PS + BS;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
     static constexpr int XR = DK / 16;
     // Column tiles of the state gradient: NCN carry dO (c_g, or the gradient
@@ -80,13 +78,14 @@ struct RC {
 //   dU[:, c] = beta o (P^T dO[:, c] + Gc o K G[:, c])
 //   dR[:, c] = T^T dU[:, c]
 //   G[:, c]  = gamma_C G[:, c] + (diag(gamma) Q)^T dO[:, c] - K^T diag(gamma) dR[:, c]
-// with P, T and the staged rows shared through LDS.
+// with P, T (from the chunk records of the forward sweep) and the staged rows
+// shared through LDS.
 template <int DK, int DV, bool MAP, bool GATED>
 __global__ __launch_bounds__(NT) void dlb_chain_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ beta,
     const float* __restrict__ alpha, const bf16_t* __restrict__ dO, const float* __restrict__ g_end,
     float* __restrict__ map_c, float* __restrict__ map_mt, bf16_t* __restrict__ gst, float* __restrict__ dS0,
-    SegMap sm) {
+    const bf16_t* __restrict__ trec, SegMap sm) {
     using Y = RC<DK, DV, MAP, GATED>;
     using M = Mma<bf16_t>;
     constexpr int LQ = Y::LQ, LV = Y::LV, XR = Y::XR, SLOTS = Y::SLOTS;
@@ -97,10 +96,7 @@ __global__ __launch_bounds__(NT) void dlb_chain_kernel(
     __bf16* Os = reinterpret_cast<__bf16*>(sp);  sp += Y::OS;
     __bf16* Ts = reinterpret_cast<__bf16*>(sp);  sp += Y::TS;
     __bf16* Ps = reinterpret_cast<__bf16*>(sp);  sp += Y::PS;
-    float* Af = reinterpret_cast<float*>(sp);
-    float* Ad = Af + CH * LF;
-    float* Yf = Ad + 4 * 256;
-    float* Bs = Yf + 4 * 256;
+    float* Bs = reinterpret_cast<float*>(sp);
     float* Gl = Bs + CH;
     float* Ge = Gl + CH;
     float* Gc = Ge + CH;
@@ -146,10 +142,12 @@ __global__ __launch_bounds__(NT) void dlb_chain_kernel(
     ChunkRegs<bf16_t, DV, NT> orr;
     unsigned short bnext = 0;
     unsigned anext = 0;
+    uint4 tnext;
     auto load_chunk = [&](int c) {
         kr.load_buf(rk, c, tid);
         qr.load_buf(rq, c, tid);
         orr.load_buf(ro, c, tid);
+        tnext = dchunk::load_rec(trec + sm.chunk_rec<false>(nseq, h, c / CH, CH) * dchunk::kRecElems, tid);
         if (tid < CH) {
             bnext = __builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(c + tid) * 2, 0, 0);
             if constexpr (GATED) anext = __builtin_amdgcn_raw_buffer_load_b32(ra, (uint32_t)(c + tid) * 4, 0, 0);
@@ -157,8 +155,7 @@ __global__ __launch_bounds__(NT) void dlb_chain_kernel(
     };
     const int c_last = t0 + ((t_end - 1 - t0) / CH) * CH;
     load_chunk(c_last);
-    dchunk::clear_upper(Ts, tid);
-    dchunk::clear_upper(Ps, tid);
+    dchunk::clear_upper(Ps, tid);  // (the records carry T's zero blocks)
     for (int c0 = c_last; c0 >= t0; c0 -= CH) {
         // Lane indices from an opaque copy, re-derived every chunk: the many
         // per-lane LDS addresses built from them then live next to their uses
@@ -180,13 +177,15 @@ __global__ __launch_bounds__(NT) void dlb_chain_kernel(
         stage_rows_raw<bf16_t, DK, NT>(kr, tid, Ks, LQ);
         stage_rows_raw<bf16_t, DK, NT>(qr, tid, Qs, LQ);
         stage_rows_raw<bf16_t, DV, NT>(orr, tid, Os, LV);
+        dchunk::stage_rec(Ts, tnext, tid);
         if (tid < CH) {
             Bs[tid] = bf16_to_f32(bnext);
             if constexpr (GATED) dchunk::gate_prefix(__uint_as_float(anext), tid, n, Gl, Ge, Gc);
         }
         if (c0 - CH >= t0) load_chunk(c0 - CH);
         __syncthreads();
-        dchunk::build_T<DK, GATED, true>(Ks, Qs, Bs, Gl, Af, Ad, Yf, Ts, Ps, w, g, li);
+        dchunk::build_P<DK, GATED>(Ks, Qs, Gl, Ps, w, g, li);
+        __syncthreads();
         if constexpr (GATED) {  // diag(gamma) Q for the dO term of the state gradient
             for (int e = tid; e < CH * DK / 8; e += NT) {
                 const int row = e / (DK / 8), col = (e % (DK / 8)) * 8;
@@ -286,8 +285,8 @@ template <int DK, int DV, bool GATED>
 struct GR {
     static constexpr int LQ = DK + 8, LV = DV + 8, LB = DV + 8;
     static constexpr int KS = CH * LQ * 2, QS = CH * LQ * 2, OS = CH * LV * 2, US = CH * LV * 2;
-    static constexpr int RS = cmax(CH * LV * 2, CH * LF * 4);   // dR rows, over the inverse's fp32 matrix
-    static constexpr int BG = cmax(DK * LB * 2, 2 * 4 * 256 * 4);  // G' or S rows, over its small blocks
+    static constexpr int RS = CH * LV * 2;   // dR rows
+    static constexpr int BG = DK * LB * 2;   // G' or S rows
     static constexpr int TS = CH * LT * 2, PS = CH * LT * 2;
     // beta; per-wave partials of dbeta (rows, then E2 tiles) and of dL/dl;
     // per-wave partial sums; gates
@@ -313,8 +312,8 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ beta, const float* __restrict__ alpha, const bf16_t* __restrict__ dO,
     const bf16_t* __restrict__ sst, const bf16_t* __restrict__ gst, bf16_t* __restrict__ dq,
-    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, float* __restrict__ dbeta, float* __restrict__ dalpha, int HT,
-    int T) {
+    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, float* __restrict__ dbeta, float* __restrict__ dalpha,
+    const bf16_t* __restrict__ trec, int HT, int T) {
     using Y = GR<DK, DV, GATED>;
     using M = Mma<bf16_t>;
     constexpr int LQ = Y::LQ, LV = Y::LV, LB = Y::LB, XR = Y::XR, TPW = Y::TPW;
@@ -324,13 +323,8 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
     __bf16* Qs = reinterpret_cast<__bf16*>(sp);  sp += Y::QS;
     __bf16* Os = reinterpret_cast<__bf16*>(sp);  sp += Y::OS;
     __bf16* Us = reinterpret_cast<__bf16*>(sp);  sp += Y::US;  // V, then U
-    unsigned char* rs = sp;                      sp += Y::RS;
-    __bf16* Rs = reinterpret_cast<__bf16*>(rs);                 // dR (after the inverse)
-    float* Af = reinterpret_cast<float*>(rs);                   // the inverse's work matrix
-    unsigned char* bg = sp;                      sp += Y::BG;
-    __bf16* Bg = reinterpret_cast<__bf16*>(bg);                 // G' rows, then S rows
-    float* Ad = reinterpret_cast<float*>(bg);
-    float* Yf = Ad + 4 * 256;
+    __bf16* Rs = reinterpret_cast<__bf16*>(sp);  sp += Y::RS;  // dR
+    __bf16* Bg = reinterpret_cast<__bf16*>(sp);  sp += Y::BG;  // G' rows, then S rows
     __bf16* Ts = reinterpret_cast<__bf16*>(sp);  sp += Y::TS;  // T, then E2
     __bf16* Ps = reinterpret_cast<__bf16*>(sp);  sp += Y::PS;  // P, then E1
     // Partial sums live in per-wave (or per-tile) slots and are added in a
@@ -358,9 +352,11 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
     uint2 st[XR], gt[XR];  // this wave's tiles of S_c and G'_c
     unsigned short bnext = 0;
     unsigned anext = 0;
+    uint4 tnext;  // this thread's 16 bytes of the chunk's T record (record index = chunk index)
     auto load_rows = [&](long c) {  // rows past the sequence end read as zero
         const int c0_ = (int)(c % NC) * CH, n_ = min(CH, T - c0_);
         const long r0 = (c / NC) * T + c0_;
+        tnext = dchunk::load_rec(trec + c * dchunk::kRecElems, tid);
         kr.load_buf(make_rsrc(k + r0 * DK, (uint32_t)n_ * DK * 2), 0, tid);
         qr.load_buf(make_rsrc(q + r0 * DK, (uint32_t)n_ * DK * 2), 0, tid);
         vr.load_buf(make_rsrc(v + r0 * DV, (uint32_t)n_ * DV * 2), 0, tid);
@@ -386,8 +382,7 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
         load_rows(ci);
         load_tiles(ci);
     }
-    dchunk::clear_upper(Ts, tid);
-    dchunk::clear_upper(Ps, tid);
+    dchunk::clear_upper(Ps, tid);  // (the records carry T's zero blocks; E2 and E1 reuse lower tiles only)
     for (; ci < total; ci += gridDim.x) {
     // lane indices re-derived per chunk from an opaque copy, so the per-lane
     // LDS addresses are not hoisted out of the loop and held (spilled)
@@ -404,6 +399,7 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
     stage_rows_raw<bf16_t, DK, NT>(qr, tid, Qs, LQ);
     stage_rows_raw<bf16_t, DV, NT>(vr, tid, Us, LV);
     stage_rows_raw<bf16_t, DV, NT>(orr, tid, Os, LV);
+    dchunk::stage_rec(Ts, tnext, tid);
     for (int e = tid; e < NWV * CH; e += NT) pL[e] = 0.f;  // waves write only their tokens
     if (tid < CH) {
         Bs[tid] = bf16_to_f32(bnext);
@@ -412,7 +408,8 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
     if (cn < total) load_rows(cn);
     __syncthreads();
     v4f kk[2];  // raw K K^T of the lower tiles w and w + 8, for dbeta
-    dchunk::build_T<DK, GATED, true, true>(Ks, Qs, Bs, Gl, Af, Ad, Yf, Ts, Ps, w, g, li, kk);
+    dchunk::build_P<DK, GATED, true>(Ks, Qs, Gl, Ps, w, g, li, kk);
+    __syncthreads();
 
     // ---- column phase
     if (w < Y::NCN) {
@@ -696,6 +693,8 @@ hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const
     float* map_c = ws;                       // forward N_g, then c_g
     float* map_mt = map_c + slots * DK * DV; // forward M_g, then M_g^T
     float* g_end = map_mt + slots * DK * DK; // forward segment states, then segment-end gradients
+    // the chunk records of T left by the forward sweep, then the chunk-state tiles
+    const bf16_t* trec = reinterpret_cast<const bf16_t*>(g_end + slots * DK * DV);
     bf16_t* sst = reinterpret_cast<bf16_t*>(ws + delta_ws_floats((long)slots, (long)sm.H * sm.chunk_recs_per_head(CH),
                                                                  DK, DV));
     bf16_t* gst = sst + (size_t)HT * NC * DK * DV;
@@ -703,12 +702,12 @@ hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const
     if (err != hipSuccess) return err;
     if (sm.G > 1) {
         dlb_chain_kernel<DK, DV, true, GATED><<<dim3(HT * (sm.G - 1)), dim3(NT), 0, stream>>>(
-            q, k, beta, alpha, dO, nullptr, map_c, map_mt, nullptr, nullptr, sm);
+            q, k, beta, alpha, dO, nullptr, map_c, map_mt, nullptr, nullptr, trec, sm);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if ((err = launch_delta_compose_rev(map_c, map_mt, dS_T, g_end, sm, DK, DV, stream)) != hipSuccess) return err;
     dlb_chain_kernel<DK, DV, false, GATED><<<dim3(HT * sm.G), dim3(NT), 0, stream>>>(q, k, beta, alpha, dO, g_end,
-                                                                                 nullptr, nullptr, gst, dS0, sm);
+                                                                                 nullptr, nullptr, gst, dS0, trec, sm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     // one workgroup per compute unit (the LDS allows one), each looping over chunks
     int dev = 0, cus = 256;
@@ -716,7 +715,7 @@ hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const
     const long total = (long)HT * NC;
     const int grid = (int)(total < cus ? total : cus);
     dlb_grad_kernel<DK, DV, GATED><<<dim3(grid), dim3(NT), 0, stream>>>(q, k, v, beta, alpha, dO, sst, gst, dq, dk, dv,
-                                                                       dbeta, dalpha, HT, sm.T);
+                                                                       dbeta, dalpha, trec, HT, sm.T);
     return hipGetLastError();
 }
 

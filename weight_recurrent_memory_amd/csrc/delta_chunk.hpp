@@ -235,5 +235,52 @@ __device__ __forceinline__ void build_T(const __bf16* Ks, const __bf16* Qs, cons
     __syncthreads();
 }
 
+// The causal scores P (bf16, lower blocks of Ps, rows = queries; gated: o
+// Gamma) alone, for loops that load T from the chunk records; wave w builds
+// lower tiles w and w + 8.  With KEEP, keep[j] receives the raw K K^T tile
+// w + 8 j (j = 0, 1, when below 10).  No barrier.
+template <int DK, bool GATED, bool KEEP = false, int LQ = DK + 8>
+__device__ __forceinline__ void build_P(const __bf16* Ks, const __bf16* Qs, const float* Gl, __bf16* Ps, int w, int g,
+                                        int li, v4f* keep = nullptr) {
+    using M = Mma<bf16_t>;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const int id = w + NWV * jj;
+        if (id >= 10) break;
+        int bi, bj;
+        lower_tile(id, bi, bj);
+        v4f acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb)
+            M::mma(acc, M::load(&Ks[(16 * bj + li) * LQ + 32 * kb], g), M::load(&Qs[(16 * bi + li) * LQ + 32 * kb], g));
+        if constexpr (GATED) {
+            const float gq = Gl[16 * bi + li];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] *= __expf(gq - Gl[16 * bj + 4 * g + r]);
+        }
+        uint2 pk;
+        pk.x = pack_bf16x2((bi == bj && 4 * g + 0 > li) ? 0.f : acc[0], (bi == bj && 4 * g + 1 > li) ? 0.f : acc[1]);
+        pk.y = pack_bf16x2((bi == bj && 4 * g + 2 > li) ? 0.f : acc[2], (bi == bj && 4 * g + 3 > li) ? 0.f : acc[3]);
+        *reinterpret_cast<uint2*>(&Ps[(16 * bi + li) * LT + 16 * bj + 4 * g]) = pk;
+        if constexpr (KEEP) {
+            v4f kk = zero4();
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb)
+                M::mma(kk, M::load(&Ks[(16 * bi + li) * LQ + 32 * kb], g), M::load(&Ks[(16 * bj + li) * LQ + 32 * kb], g));
+            keep[jj] = kk;
+        }
+    }
+}
+
+// A chunk record (a 64 x 64 bf16 matrix, row-major, upper blocks zero) into
+// LDS rows of stride LT; 512 threads, 16 bytes each.
+constexpr int kRecElems = CH * CH;
+__device__ __forceinline__ uint4 load_rec(const bf16_t* rec, int tid) {
+    return *reinterpret_cast<const uint4*>(rec + tid * 8);
+}
+__device__ __forceinline__ void stage_rec(__bf16* Xs, uint4 x, int tid) {
+    *reinterpret_cast<uint4*>(&Xs[(tid >> 3) * LT + (tid & 7) * 8]) = x;
+}
+
 }  // namespace dchunk
 }  // namespace la

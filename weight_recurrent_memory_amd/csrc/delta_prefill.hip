@@ -139,7 +139,7 @@ __host__ __device__ constexpr void lower_tile(int id, int& i, int& j) {
     else { i = 3; j = 0; }                         // (3,0)
 }
 
-constexpr int kRecElems = CH * CH;  // one chunk record: a 64 x 64 bf16 matrix, row-major
+using dchunk::kRecElems;  // one chunk record: a 64 x 64 bf16 matrix, row-major
 
 // T = (I + A)^{-1} of every chunk, and for the gated rule T diag(gamma):
 // the state-free, latency-bound part of the chunk recurrence, done once per
