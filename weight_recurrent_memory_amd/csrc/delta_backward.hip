@@ -283,9 +283,12 @@ __global__ __launch_bounds__(NT) void dlb_chain_kernel(
 
 template <int DK, int DV, bool GATED>
 struct GR {
-    static constexpr int LQ = DK + 8, LV = DV + 8, LB = DV + 8;
+    // row strides: K, Q, dO and U (V) are also read with transpose loads or
+    // staged with 16-byte stores (padding 8); dR and the S / G' rows are read
+    // only as row fragments (padding 4: a fragment's rows start 2 words apart)
+    static constexpr int LQ = DK + 8, LV = DV + 8, LR = DV + 4, LB = DV + 4;
     static constexpr int KS = CH * LQ * 2, QS = CH * LQ * 2, OS = CH * LV * 2, US = CH * LV * 2;
-    static constexpr int RS = CH * LV * 2;   // dR rows
+    static constexpr int RS = CH * LR * 2;   // dR rows
     static constexpr int BG = DK * LB * 2;   // G' or S rows
     static constexpr int TS = CH * LT * 2, PS = CH * LT * 2;
     // beta; per-wave partials of dbeta (rows, then E2 tiles) and of dL/dl;
@@ -316,7 +319,7 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
     const bf16_t* __restrict__ trec, int HT, int T) {
     using Y = GR<DK, DV, GATED>;
     using M = Mma<bf16_t>;
-    constexpr int LQ = Y::LQ, LV = Y::LV, LB = Y::LB, XR = Y::XR, TPW = Y::TPW;
+    constexpr int LQ = Y::LQ, LV = Y::LV, LR = Y::LR, LB = Y::LB, XR = Y::XR, TPW = Y::TPW;
     __shared__ __align__(16) unsigned char smem[Y::TOTAL];
     unsigned char* sp = smem;
     __bf16* Ks = reinterpret_cast<__bf16*>(sp);  sp += Y::KS;
@@ -489,7 +492,7 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
             for (int r = 0; r < 4; ++r) {
                 const int s = 16 * tt + 4 * g + r;
                 Us[s * LV + col] = M::cvt(Uo[tt][r]);
-                Rs[s * LV + col] = M::cvt(dR[tt][r]);
+                Rs[s * LR + col] = M::cvt(dR[tt][r]);
             }
 #pragma unroll
         for (int i = 0; i < XR; ++i) {
@@ -502,9 +505,9 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
     __syncthreads();
 
     // ---- dv rows, then E1, E2 and the column part of dbeta
-    for (int e = tid; e < CH * DV / 8; e += NT) {
-        const int row = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
-        if (row < n) *reinterpret_cast<uint4*>(dv + (row0 + row) * DV + c8) = *reinterpret_cast<const uint4*>(&Rs[row * LV + c8]);
+    for (int e = tid; e < CH * DV / 4; e += NT) {  // 8-byte pieces (dR rows are 8-byte aligned)
+        const int row = e / (DV / 4), c4 = (e % (DV / 4)) * 4;
+        if (row < n) *reinterpret_cast<uint2*>(dv + (row0 + row) * DV + c4) = *reinterpret_cast<const uint2*>(&Rs[row * LR + c4]);
     }
     // E2 tile j goes to wave j % 8 (which holds its K K^T from the inverse),
     // E1 tiles to the waves with fewer: at most three tiles per wave.
@@ -513,9 +516,10 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
         dchunk::lower_tile(j, bt, bi);
         v4f acc = zero4();
         const __bf16* lhs = e2 ? Rs : Os;
+        const int ldl = e2 ? LR : LV;
 #pragma unroll
         for (int kb = 0; kb < DV / 32; ++kb)
-            M::mma(acc, M::load(&lhs[(16 * bt + li) * LV + 32 * kb], g), M::load(&Us[(16 * bi + li) * LV + 32 * kb], g));
+            M::mma(acc, M::load(&lhs[(16 * bt + li) * ldl + 32 * kb], g), M::load(&Us[(16 * bi + li) * LV + 32 * kb], g));
         const int i = 16 * bi + li;
         if (!e2) {  // E1 = Gamma o tril(dO U^T) diag(beta)
 #pragma unroll
@@ -609,7 +613,7 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
 #pragma unroll
         for (int kb = 0; kb < DV / 32; ++kb) {
             M::mma(a1, rf[kb], M::load(&Os[(16 * tt + li) * LV + 32 * kb], g));
-            M::mma(a2, rf[kb], M::load(&Rs[(16 * tt + li) * LV + 32 * kb], g));
+            M::mma(a2, rf[kb], M::load(&Rs[(16 * tt + li) * LR + 32 * kb], g));
         }
         const int t = 16 * tt + li;
         const float ge = GATED ? Ge[t] : 1.f;
