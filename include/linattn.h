@@ -111,7 +111,13 @@ la_status la_forward(const void* q, const void* k, const void* v,
                      int B, int H, int T, int dk, int dv, int dtype, float eps, int chunk,
                      void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace delta_forward needs; 0 if the sizes are invalid. */
+/*
+ * Bytes of device workspace delta_forward (and gated_delta_forward,
+ * delta_forward_ex) needs; 0 if the sizes are invalid.  The workspace holds
+ * the per-segment affine maps and states (fp32) and one record per 64-token
+ * chunk of the chunk's triangular inverse T = (I + A)^{-1} and, for the
+ * gated rule, T diag(gamma) (bf16, 16 KiB per chunk).
+ */
 size_t delta_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
 
 /*
@@ -287,8 +293,8 @@ la_status la_backward(const void* q, const void* k, const void* v, const float* 
  * -20, so a gate below e^-20 gets gradient 0); dS0 fp32 [B][H][dk][dv] or
  * NULL.  Every output is overwritten.  bf16 only; uniform batches only.
  * The workspace (delta_backward_workspace_bytes) holds the forward's
- * segment arrays plus every chunk's entering state and leaving state
- * gradient (bf16), 4 * B * H * ceil(T / 64) * dk * dv bytes of it.
+ * workspace plus every chunk's entering state and leaving state gradient
+ * (bf16), 4 * B * H * ceil(T / 64) * dk * dv bytes of it.
  */
 size_t delta_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
 la_status delta_backward(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
