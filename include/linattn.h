@@ -115,8 +115,7 @@ la_status la_forward(const void* q, const void* k, const void* v,
  * Bytes of device workspace delta_forward (and gated_delta_forward,
  * delta_forward_ex) needs; 0 if the sizes are invalid.  The workspace holds
  * the per-segment affine maps and states (fp32) and one record per 64-token
- * chunk of the chunk's triangular inverse T = (I + A)^{-1} and, for the
- * gated rule, T diag(gamma) (bf16, 16 KiB per chunk).
+ * chunk of the chunk's triangular inverse T = (I + A)^{-1} (bf16, 8 KiB).
  */
 size_t delta_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
 

@@ -97,18 +97,16 @@ __device__ __forceinline__ void clear_upper(__bf16* X, int tid) {
 // (4 x 256 fp32 each) are scratch.  Called by all threads of the workgroup
 // after the chunk is staged and visible; ends with a barrier.  With KEEP,
 // keep[j] receives the raw K K^T tile (lower tile w + 8 j, j = 0, 1, when
-// below 10) that this wave computed for A.  With TG, Tg receives
-// T diag(gamma) (bf16, lower blocks; Ge = gamma).
+// below 10) that this wave computed for A.
 //
 // A's diagonal 16x16 blocks are inverted by forward substitution (wave 0,
 // one column per lane); the rest by 2x2 block doubling: the inverse of
 // [[M11, 0], [M21, M22]] is [[M11^-1, 0], [-M22^-1 M21 M11^-1, M22^-1]],
 // first on the 32x32 diagonal blocks, then on the lower-left 32x32 block.
-template <int DK, bool GATED, bool WANT_P, bool KEEP = false, bool TG = false, int LQ = DK + 8>
+template <int DK, bool GATED, bool WANT_P, bool KEEP = false, int LQ = DK + 8>
 __device__ __forceinline__ void build_T(const __bf16* Ks, const __bf16* Qs, const float* Bs, const float* Gl,
                                         float* Af, float* Ad, float* Yf, __bf16* Ts, __bf16* Ps, int w, int g,
-                                        int li, v4f* keep = nullptr, __bf16* Tg = nullptr,
-                                        const float* Ge = nullptr) {
+                                        int li, v4f* keep = nullptr) {
     using M = Mma<bf16_t>;
     using MF = Mma<float>;
     constexpr int NTILE = WANT_P ? 20 : 10;
@@ -166,12 +164,10 @@ __device__ __forceinline__ void build_T(const __bf16* Ks, const __bf16* Qs, cons
 #pragma unroll
             for (int i = m + 1; i < 16; ++i) d[i] -= c[i >> 2][i & 3] * d[m];
         }
-        const float gj = TG ? Ge[16 * b + j] : 1.f;
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
             Af[(16 * b + m) * LF + 16 * b + j] = d[m];
             Ts[(16 * b + m) * LT + 16 * b + j] = M::cvt(d[m]);
-            if constexpr (TG) Tg[(16 * b + m) * LT + 16 * b + j] = M::cvt(d[m] * gj);
         }
     }
     __syncthreads();
@@ -191,11 +187,6 @@ __device__ __forceinline__ void build_T(const __bf16* Ks, const __bf16* Qs, cons
     auto put_T = [&](int bi, int bj, const v4f& x) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) Ts[(16 * bi + 4 * g + r) * LT + 16 * bj + li] = M::cvt(x[r]);
-        if constexpr (TG) {
-            const float gc = Ge[16 * bj + li];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Tg[(16 * bi + 4 * g + r) * LT + 16 * bj + li] = M::cvt(x[r] * gc);
-        }
     };
     if (w == 1 || w == 2) {  // T10 = -D1 A10 D0 (wave 1), T32 = -D3 A32 D2 (wave 2)
         const int lo = w == 1 ? 0 : 32;

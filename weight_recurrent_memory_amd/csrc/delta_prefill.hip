@@ -76,16 +76,15 @@ struct DL {
     static constexpr int LQ = DK + 8;  // K rows
     static constexpr int LW = DK + 4;  // W and Q rows
     static constexpr int LV = NS + 8;  // V rows
-    static constexpr int LT = CH + 4;  // T, T diag(gamma) and P rows
+    static constexpr int LT = CH + 4;  // T and P rows
     static constexpr int KS = CH * LQ * 2;          // K_c rows (read transposed too)
     static constexpr int WS = CH * LW * 2;          // W rows
     static constexpr int QS = OUT ? CH * LW * 2 : 0;
     static constexpr int VS = CH * LV * 2;          // V_c rows (read transposed)
     static constexpr int TS = CH * LT * 2;          // T (bf16, from the chunk's record)
-    static constexpr int TG = GATED ? CH * LT * 2 : 0;  // gated: T diag(gamma) (bf16, record)
     static constexpr int PS = OUT ? CH * LT * 2 : 0;  // tril(Q K^T), rows = queries
     static constexpr int BS = CH * 4 * (GATED ? 4 : 1);  // beta; gated: log-gates, gamma, gamma_C/gamma (fp32)
-    static constexpr int TOTAL = KS + WS + QS + VS + TS + TG + PS + BS;
+    static constexpr int TOTAL = KS + WS + QS + VS + TS + PS + BS;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
     static constexpr int XR = DK / 16;              // dk row tiles of a state column
     // State column tiles: OUT and STATES carry S (NS columns); MAP carries N
@@ -141,8 +140,8 @@ __host__ __device__ constexpr void lower_tile(int id, int& i, int& j) {
 
 using dchunk::kRecElems;  // one chunk record: a 64 x 64 bf16 matrix, row-major
 
-// T = (I + A)^{-1} of every chunk, and for the gated rule T diag(gamma):
-// the state-free, latency-bound part of the chunk recurrence, done once per
+// T = (I + A)^{-1} of every chunk: the state-free, latency-bound part of
+// the chunk recurrence (for the gated rule with the decay ratios in A), done once per
 // chunk by a fully parallel pass (one workgroup per chunk record) instead of
 // inside every serial chunk loop that needs it.  Rows past the sequence end
 // are zero, as in the loops; the input transforms (kNormQK on k,
@@ -150,14 +149,13 @@ using dchunk::kRecElems;  // one chunk record: a 64 x 64 bf16 matrix, row-major
 template <int DK, bool GATED, bool PACKED>
 __global__ __launch_bounds__(NT) void delta_tinv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ beta,
                                                         const float* __restrict__ alpha, bf16_t* __restrict__ trec,
-                                                        bf16_t* __restrict__ tgrec, int flags, SegMap sm) {
+                                                        int flags, SegMap sm) {
     // K is read only as row fragments here (K K^T tiles): rows padded by 4
     // elements spread a fragment's 16 rows over the banks (staged with
     // 8-byte stores)
     constexpr int LQ = DK + 4, LT = dchunk::LT, LF = dchunk::LF;
     __shared__ __align__(16) __bf16 Ks[CH * LQ];
     __shared__ __align__(16) __bf16 Ts[CH * LT];
-    __shared__ __align__(16) __bf16 Tgs[GATED ? CH * LT : 8];
     __shared__ __align__(16) float Af[CH * LF];
     __shared__ __align__(16) float Ad[4 * 256];
     __shared__ __align__(16) float Yf[4 * 256];
@@ -204,17 +202,12 @@ __global__ __launch_bounds__(NT) void delta_tinv_kernel(const bf16_t* __restrict
         }
     }
     dchunk::clear_upper(Ts, tid);
-    if constexpr (GATED) dchunk::clear_upper(Tgs, tid);
     __syncthreads();
-    dchunk::build_T<DK, GATED, false, false, GATED, LQ>(Ks, nullptr, Bs, Gl, Af, Ad, Yf, Ts, nullptr, w, g, li,
-                                                        nullptr, Tgs, Ge);
+    dchunk::build_T<DK, GATED, false, false, LQ>(Ks, nullptr, Bs, Gl, Af, Ad, Yf, Ts, nullptr, w, g, li);
     // one 16-byte row piece per thread: row tid / 8, columns 8 (tid % 8) ..
     const int row = tid >> 3, col = (tid & 7) * 8;
     *reinterpret_cast<uint4*>(trec + rec * kRecElems + row * CH + col) =
         *reinterpret_cast<const uint4*>(&Ts[row * LT + col]);
-    if constexpr (GATED)
-        *reinterpret_cast<uint4*>(tgrec + rec * kRecElems + row * CH + col) =
-            *reinterpret_cast<const uint4*>(&Tgs[row * LT + col]);
 }
 
 // One workgroup runs one segment's chunk loop.  The state-dependent part of
@@ -232,7 +225,7 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
     const bf16_t* __restrict__ beta, const float* __restrict__ alpha, bf16_t* __restrict__ o,
     const float* __restrict__ state_in, float* __restrict__ map_n, float* __restrict__ map_m,
     float* __restrict__ S_out, bf16_t* __restrict__ pred, bf16_t* __restrict__ states,
-    const bf16_t* __restrict__ trec, const bf16_t* __restrict__ tgrec, int flags, SegMap sm) {
+    const bf16_t* __restrict__ trec, int flags, SegMap sm) {
     constexpr bool OUT = MODE == kOut, MAP = MODE == kMap;
     static_assert(MODE != kStates || !PACKED, "chunk states are for uniform batches");
     constexpr int NT = NWV * 64;  // this instantiation's threads (eight or sixteen waves)
@@ -247,7 +240,6 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
     __bf16* Qs = reinterpret_cast<__bf16*>(sp);  sp += Y::QS;
     __bf16* Vs = reinterpret_cast<__bf16*>(sp);  sp += Y::VS;
     __bf16* Ts = reinterpret_cast<__bf16*>(sp);  sp += Y::TS;
-    __bf16* Tg = reinterpret_cast<__bf16*>(sp);  sp += Y::TG;
     __bf16* Ps = reinterpret_cast<__bf16*>(sp);  sp += Y::PS;
     float* Bs = reinterpret_cast<float*>(sp);
     float* Gl = Bs + CH;  // gated: chunk-local cumulative log-gate
@@ -316,7 +308,7 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
     ChunkRegs<bf16_t, NS, NT> vr;
     unsigned short bnext = 0;
     unsigned anext = 0;
-    uint4 tnext, tgnext;  // this thread's 16 bytes of the chunk's T (and T diag(gamma)) record
+    uint4 tnext;  // this thread's 16 bytes of the chunk's T record
     auto load_chunk = [&](int c, int tid) {
         kr.load_buf(rk, c, tid);
         if constexpr (OUT) qr.load_buf(rq, c, tid);
@@ -324,7 +316,6 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
         if (NT == 512 || tid < 512) {  // 512 x 16 bytes: one record
             const long rec = sm.chunk_rec<PACKED>(nseq, h, c / CH, CH) * kRecElems + tid * 8;
             tnext = *reinterpret_cast<const uint4*>(trec + rec);
-            if constexpr (GATED) tgnext = *reinterpret_cast<const uint4*>(tgrec + rec);
         }
         if (tid < CH) {
             bnext = __builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(c + tid) * 2, 0, 0);
@@ -378,11 +369,6 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
             uint2* dt = reinterpret_cast<uint2*>(&Ts[(tid >> 3) * LT + (tid & 7) * 8]);
             dt[0] = make_uint2(tnext.x, tnext.y);
             dt[1] = make_uint2(tnext.z, tnext.w);
-            if constexpr (GATED) {
-                uint2* dg = reinterpret_cast<uint2*>(&Tg[(tid >> 3) * LT + (tid & 7) * 8]);
-                dg[0] = make_uint2(tgnext.x, tgnext.y);
-                dg[1] = make_uint2(tgnext.z, tgnext.w);
-            }
         }
         if (tid < CH) {  // wave 0
             const float braw = bf16_to_f32(bnext);
@@ -447,9 +433,9 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
             }
         }
 
-        // ---- W = T K (gated: T diag(gamma) K, from Tg; computed as
-        // transposed tiles, rows land as 8-byte stores) and this wave's
-        // U_v = T V columns
+        // ---- W = T K (gated: T diag(gamma) K, gamma applied to the T
+        // fragment's columns in registers; computed as transposed tiles, rows
+        // land as 8-byte stores) and this wave's U_v = T V columns
 #pragma unroll
         for (int c = 0; c < Y::W_TPW; ++c) {
             const int dkt = w % XR, tt = (w / XR) * Y::W_TPW + c;
@@ -457,8 +443,17 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
 #pragma unroll
             for (int kb = 0; kb < CH / 32; ++kb) {
                 if (32 * kb > 16 * tt + 15) continue;  // T is lower triangular
-                M::mma(acc, M::load_tr(Ks, LQ, 32 * kb, 16 * dkt, lane),
-                       M::load(&(GATED ? Tg : Ts)[(16 * tt + li) * LT + 32 * kb], g));
+                frag tf = M::load(&Ts[(16 * tt + li) * LT + 32 * kb], g);
+                if constexpr (GATED) {  // slot s <-> column 32 kb + 4g + s (s < 4), 32 kb + 16 + 4g + s - 4
+                    const v4f g0 = *reinterpret_cast<const v4f*>(&Ge[32 * kb + 4 * g]);
+                    const v4f g1 = *reinterpret_cast<const v4f*>(&Ge[32 * kb + 16 + 4 * g]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        tf[e] = M::cvt((float)tf[e] * g0[e]);
+                        tf[4 + e] = M::cvt((float)tf[4 + e] * g1[e]);
+                    }
+                }
+                M::mma(acc, M::load_tr(Ks, LQ, 32 * kb, 16 * dkt, lane), tf);
             }
             __bf16* dst = &Ws[(16 * tt + li) * Y::LW + 16 * dkt + 4 * g];
 #pragma unroll
@@ -683,21 +678,20 @@ hipError_t launch_packing(const bf16_t* q, const bf16_t* k, const bf16_t* v, con
     float* state_in = map_m + slots * DK * DK;
     bf16_t* trec = reinterpret_cast<bf16_t*>(state_in + slots * DK * DV);
     const long recs = (long)sm.H * sm.chunk_recs_per_head(CH);
-    bf16_t* tgrec = GATED ? trec + recs * kRecElems : nullptr;
     hipError_t err;
-    delta_tinv_kernel<DK, GATED, PACKED><<<dim3(recs), dim3(NT), 0, stream>>>(k, beta, alpha, trec, tgrec, flags, sm);
+    delta_tinv_kernel<DK, GATED, PACKED><<<dim3(recs), dim3(NT), 0, stream>>>(k, beta, alpha, trec, flags, sm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (sm.NS > sm.N) {
         constexpr int NWM = kMapWaves<DK, DV>;
         delta_chunk_kernel<DK, DV, kMap, GATED, PACKED, NWM><<<dim3(sm.H * (sm.NS - sm.N)), dim3(NWM * 64), 0, stream>>>(
-            q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, nullptr, nullptr, trec, tgrec, flags, sm);
+            q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, nullptr, nullptr, trec, flags, sm);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     delta_compose_kernel<DK, DV, PACKED><<<dim3(DV / 16, sm.N * sm.H), dim3(256), 0, stream>>>(map_n, map_m, S0, state_in,
                                                                                       sm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     delta_chunk_kernel<DK, DV, kOut, GATED, PACKED><<<dim3(sm.H * sm.NS), dim3(NT), 0, stream>>>(
-        q, k, v, beta, alpha, o, state_in, nullptr, nullptr, S_out, pred, nullptr, trec, tgrec, flags, sm);
+        q, k, v, beta, alpha, o, state_in, nullptr, nullptr, S_out, pred, nullptr, trec, flags, sm);
     return hipGetLastError();
 }
 
@@ -712,21 +706,20 @@ hipError_t launch_states(const bf16_t* q, const bf16_t* k, const bf16_t* v, cons
     float* state_in = map_m + slots * DK * DK;
     bf16_t* trec = reinterpret_cast<bf16_t*>(state_in + slots * DK * DV);
     const long recs = (long)sm.H * sm.chunk_recs_per_head(CH);
-    bf16_t* tgrec = GATED ? trec + recs * kRecElems : nullptr;
     hipError_t err;
-    delta_tinv_kernel<DK, GATED, false><<<dim3(recs), dim3(NT), 0, stream>>>(k, beta, alpha, trec, tgrec, 0, sm);
+    delta_tinv_kernel<DK, GATED, false><<<dim3(recs), dim3(NT), 0, stream>>>(k, beta, alpha, trec, 0, sm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (sm.NS > sm.N) {
         constexpr int NWM = kMapWaves<DK, DV>;
         delta_chunk_kernel<DK, DV, kMap, GATED, false, NWM><<<dim3(sm.H * (sm.NS - sm.N)), dim3(NWM * 64), 0, stream>>>(
-            q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, nullptr, nullptr, trec, tgrec, 0, sm);
+            q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, nullptr, nullptr, trec, 0, sm);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     delta_compose_kernel<DK, DV, false><<<dim3(DV / 16, sm.N * sm.H), dim3(256), 0, stream>>>(map_n, map_m, S0,
                                                                                           state_in, sm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     delta_chunk_kernel<DK, DV, kStates, GATED, false><<<dim3(sm.H * sm.NS), dim3(NT), 0, stream>>>(
-        q, k, v, beta, alpha, nullptr, state_in, nullptr, nullptr, nullptr, nullptr, states, trec, tgrec, 0, sm);
+        q, k, v, beta, alpha, nullptr, state_in, nullptr, nullptr, nullptr, nullptr, states, trec, 0, sm);
     return hipGetLastError();
 }
 
@@ -780,8 +773,8 @@ hipError_t launch_delta_compose_rev(const float* map_c, const float* map_mt, con
 }
 
 size_t delta_ws_floats(long slots, long recs, int dk, int dv) {
-    // per slot: N_g, M_g, S_in; per chunk record: T and T diag(gamma), bf16
-    return (size_t)slots * ((size_t)dk * dv + (size_t)dk * dk + (size_t)dk * dv) + (size_t)recs * kRecElems;
+    // per slot: N_g, M_g, S_in; per chunk record: T (bf16, two per float)
+    return (size_t)slots * ((size_t)dk * dv + (size_t)dk * dk + (size_t)dk * dv) + (size_t)recs * kRecElems / 2;
 }
 
 hipError_t launch_delta_forward(const void* q, const void* k, const void* v, const void* beta,
