@@ -14,16 +14,18 @@
 //   S' += K^T (beta o U)
 // (beta o U scales row t of U by beta_t).  T, W and U_v depend only on the
 // chunk's own keys, values and betas; the state enters through W S alone.
-// T is built in fp32: the four 16x16 diagonal blocks by forward substitution
-// in registers, the off-diagonal blocks level by level,
-//   T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj.
+// T is built once per chunk by a parallel pass (delta_tinv, the construction
+// in delta_chunk.hpp: 16x16 diagonal blocks by forward substitution, then
+// 2x2 block doubling in fp32) into per-chunk records, which the serial chunk
+// loops below load with each chunk's rows.
 //
 // Sequence parallelism.  Over a segment of chunks the rule is affine in the
 // incoming state: S_out = M_g S_in + N_g.  Running the same chunk recurrence
 // on a state started at 0 with the segment's values gives N_g; running it on a
 // state started at I with zero values gives M_g.  Each state column evolves
 // independently, so both ride in one workgroup as extra columns and share the
-// chunk's T and W.  Three launches:
+// chunk's T and W.  Four launches:
+//   delta_tinv        every chunk's T record
 //   delta_chunk<MAP>  (M_g, N_g) for every segment but the last
 //   delta_compose     S_in(g+1) = M_g S_in(g) + N_g, fp32 MFMA, serial in g
 //   delta_chunk<OUT>  the chunk loop from S_in(g), writing O (and S_T last)
@@ -39,8 +41,8 @@
 //   S' = gamma_C S + K^T diag(beta gamma_C / gamma) U.
 // Ratios are exponentials of differences of chunk-local cumulative log-gates
 // (each log clamped at -20), so no ratio divides by an underflowed product.
-// The segment maps stay affine in the incoming state, so the three launches
-// are unchanged.
+// The segment maps stay affine in the incoming state, so the launches are
+// unchanged.
 //
 // Serving input transforms (LinearMem §05 and §08: the L2 normalisation of
 // q and k and the beta transform run inside the kernel): with kNormQK each
@@ -130,13 +132,7 @@ __device__ __forceinline__ void stage_rows_l2(const ChunkRegs<bf16_t, D, NTH>& c
     }
 }
 
-// The ten lower 16x16 tiles of a 64x64 matrix: diagonal first.
-__host__ __device__ constexpr void lower_tile(int id, int& i, int& j) {
-    if (id < 4) { i = id; j = id; }                // (0,0) (1,1) (2,2) (3,3)
-    else if (id < 7) { i = id - 3; j = id - 4; }   // (1,0) (2,1) (3,2)
-    else if (id < 9) { i = id - 5; j = id - 7; }   // (2,0) (3,1)
-    else { i = 3; j = 0; }                         // (3,0)
-}
+using dchunk::lower_tile;
 
 using dchunk::kRecElems;  // one chunk record: a 64 x 64 bf16 matrix, row-major
 
