@@ -43,6 +43,8 @@ SHAPES = [
     (1, 2, 3000, 128, 128, True),
     (1, 1, 2500, 128, 64, False),
     (1, 1, 2049, 64, 128, True),
+    (2, 160, 300, 128, 128, True),   # 320 heads: one segment per sequence, no map pass
+    (1, 64, 1000, 128, 128, True),   # four segments per head: the sixteen-wave map pass
 ]
 
 
