@@ -283,11 +283,12 @@ __global__ __launch_bounds__(NT) void dlb_chain_kernel(
 
 template <int DK, int DV, bool GATED>
 struct GR {
-    // row strides: K, Q, dO and U (V) are also read with transpose loads or
-    // staged with 16-byte stores (padding 8); dR and the S / G' rows are read
-    // only as row fragments (padding 4: a fragment's rows start 2 words apart)
-    static constexpr int LQ = DK + 8, LV = DV + 8, LR = DV + 4, LB = DV + 4;
-    static constexpr int KS = CH * LQ * 2, QS = CH * LQ * 2, OS = CH * LV * 2, US = CH * LV * 2;
+    // row strides: K, Q and dO are also read with transpose loads (padding
+    // 8); dR, U (staged from V with 8-byte stores) and the S / G' rows are
+    // read only as row fragments or scalars (padding 4: a fragment's rows
+    // start 2 words apart)
+    static constexpr int LQ = DK + 8, LV = DV + 8, LR = DV + 4, LB = DV + 4, LU = DV + 4;
+    static constexpr int KS = CH * LQ * 2, QS = CH * LQ * 2, OS = CH * LV * 2, US = CH * LU * 2;
     static constexpr int RS = CH * LR * 2;   // dR rows
     static constexpr int BG = DK * LB * 2;   // G' or S rows
     static constexpr int TS = CH * LT * 2, PS = CH * LT * 2;
@@ -319,7 +320,7 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
     const bf16_t* __restrict__ trec, int HT, int T) {
     using Y = GR<DK, DV, GATED>;
     using M = Mma<bf16_t>;
-    constexpr int LQ = Y::LQ, LV = Y::LV, LR = Y::LR, LB = Y::LB, XR = Y::XR, TPW = Y::TPW;
+    constexpr int LQ = Y::LQ, LV = Y::LV, LR = Y::LR, LB = Y::LB, LU = Y::LU, XR = Y::XR, TPW = Y::TPW;
     __shared__ __align__(16) unsigned char smem[Y::TOTAL];
     unsigned char* sp = smem;
     __bf16* Ks = reinterpret_cast<__bf16*>(sp);  sp += Y::KS;
@@ -400,7 +401,7 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
 
     stage_rows_raw<bf16_t, DK, NT>(kr, tid, Ks, LQ);
     stage_rows_raw<bf16_t, DK, NT>(qr, tid, Qs, LQ);
-    stage_rows_raw<bf16_t, DV, NT>(vr, tid, Us, LV);
+    stage_rows_raw<bf16_t, DV, NT, true>(vr, tid, Us, LU);
     stage_rows_raw<bf16_t, DV, NT>(orr, tid, Os, LV);
     dchunk::stage_rec(Ts, tnext, tid);
     for (int e = tid; e < NWV * CH; e += NT) pL[e] = 0.f;  // waves write only their tokens
@@ -427,7 +428,7 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int s = 16 * tt + 4 * g + r;
-                U[tt][r] = (float)Us[s * LV + col] - (GATED ? Ge[s] : 1.f) * ks[r];
+                U[tt][r] = (float)Us[s * LU + col] - (GATED ? Ge[s] : 1.f) * ks[r];
             }
         }
         v4f Uo[4];
@@ -491,7 +492,7 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int s = 16 * tt + 4 * g + r;
-                Us[s * LV + col] = M::cvt(Uo[tt][r]);
+                Us[s * LU + col] = M::cvt(Uo[tt][r]);
                 Rs[s * LR + col] = M::cvt(dR[tt][r]);
             }
 #pragma unroll
@@ -519,7 +520,7 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
         const int ldl = e2 ? LR : LV;
 #pragma unroll
         for (int kb = 0; kb < DV / 32; ++kb)
-            M::mma(acc, M::load(&lhs[(16 * bt + li) * ldl + 32 * kb], g), M::load(&Us[(16 * bi + li) * LV + 32 * kb], g));
+            M::mma(acc, M::load(&lhs[(16 * bt + li) * ldl + 32 * kb], g), M::load(&Us[(16 * bi + li) * LU + 32 * kb], g));
         const int i = 16 * bi + li;
         if (!e2) {  // E1 = Gamma o tril(dO U^T) diag(beta)
 #pragma unroll
@@ -575,7 +576,7 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
         }
         v4f g3 = zero4();
 #pragma unroll
-        for (int kb = 0; kb < DV / 32; ++kb) M::mma(g3, rf[kb], M::load(&Us[(16 * tt + li) * LV + 32 * kb], g));
+        for (int kb = 0; kb < DV / 32; ++kb) M::mma(g3, rf[kb], M::load(&Us[(16 * tt + li) * LU + 32 * kb], g));
         const int t = 16 * tt + li;
         const float sc = Bs[t] * (GATED ? Gc[t] : 1.f);
         const v4bf kv = *reinterpret_cast<const v4bf*>(&Ks[t * LQ + 16 * it + 4 * g]);

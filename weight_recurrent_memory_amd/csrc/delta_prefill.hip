@@ -304,15 +304,17 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
     ChunkRegs<bf16_t, NS, NT> vr;
     unsigned short bnext = 0;
     unsigned anext = 0;
-    uint4 tnext;  // this thread's 16 bytes of the chunk's T record
+    constexpr int RPT = (512 + NT - 1) / NT;  // 16-byte pieces of a T record per thread
+    uint4 tnext[RPT];  // this thread's pieces of the chunk's T record
     auto load_chunk = [&](int c, int tid) {
         kr.load_buf(rk, c, tid);
         if constexpr (OUT) qr.load_buf(rq, c, tid);
         vr.load_buf(rv, c, tid);
-        if (NT == 512 || tid < 512) {  // 512 x 16 bytes: one record
-            const long rec = sm.chunk_rec<PACKED>(nseq, h, c / CH, CH) * kRecElems + tid * 8;
-            tnext = *reinterpret_cast<const uint4*>(trec + rec);
-        }
+        const long rec = sm.chunk_rec<PACKED>(nseq, h, c / CH, CH) * kRecElems;
+#pragma unroll
+        for (int e = 0; e < RPT; ++e)  // 512 x 16 bytes: one record
+            if (NT * (e + 1) <= 512 || tid + NT * e < 512)
+                tnext[e] = *reinterpret_cast<const uint4*>(trec + rec + (tid + NT * e) * 8);
         if (tid < CH) {
             bnext = __builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(c + tid) * 2, 0, 0);
             if constexpr (GATED) anext = __builtin_amdgcn_raw_buffer_load_b32(ra, (uint32_t)(c + tid) * 4, 0, 0);
@@ -361,10 +363,14 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
             if constexpr (OUT) stage_rows_raw<bf16_t, DK, NT, true>(qr, tid, Qs, Y::LW);
         }
         stage_rows_raw<bf16_t, NS, NT>(vr, tid, Vs, LV);
-        if (NT == 512 || tid < 512) {
-            uint2* dt = reinterpret_cast<uint2*>(&Ts[(tid >> 3) * LT + (tid & 7) * 8]);
-            dt[0] = make_uint2(tnext.x, tnext.y);
-            dt[1] = make_uint2(tnext.z, tnext.w);
+#pragma unroll
+        for (int e = 0; e < RPT; ++e) {
+            const int p = tid + NT * e;
+            if (NT * (e + 1) <= 512 || p < 512) {
+                uint2* dt = reinterpret_cast<uint2*>(&Ts[(p >> 3) * LT + (p & 7) * 8]);
+                dt[0] = make_uint2(tnext[e].x, tnext[e].y);
+                dt[1] = make_uint2(tnext[e].z, tnext[e].w);
+            }
         }
         if (tid < CH) {  // wave 0
             const float braw = bf16_to_f32(bnext);
@@ -394,7 +400,7 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
         v4f Oq[OUT ? 4 : 1];
         if constexpr (OUT) {
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
+            for (int jj = 0; jj < (10 + NWV - 1) / NWV; ++jj) {
                 const int id = w + NWV * jj;
                 if (id >= 10) break;
                 int bi, bj;
@@ -592,6 +598,9 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
 // waves per SIMD to hide LDS-operand latency, half the registers per wave).
 template <int DK, int DV>
 constexpr int kMapWaves = (DK == 128 && DV == 128) ? 16 : 8;
+// Waves per workgroup of the output pass.
+template <int DK, int DV>
+constexpr int kOutWaves = 8;
 
 // S_in(0) = S0 (or 0); S_in(g+1) = M_g S_in(g) + N_g in fp32 MFMA.  One
 // workgroup per (16-column block of the state, sequence and head); serial
@@ -686,7 +695,8 @@ hipError_t launch_packing(const bf16_t* q, const bf16_t* k, const bf16_t* v, con
     delta_compose_kernel<DK, DV, PACKED><<<dim3(DV / 16, sm.N * sm.H), dim3(256), 0, stream>>>(map_n, map_m, S0, state_in,
                                                                                       sm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    delta_chunk_kernel<DK, DV, kOut, GATED, PACKED><<<dim3(sm.H * sm.NS), dim3(NT), 0, stream>>>(
+    constexpr int NWO = kOutWaves<DK, DV>;
+    delta_chunk_kernel<DK, DV, kOut, GATED, PACKED, NWO><<<dim3(sm.H * sm.NS), dim3(NWO * 64), 0, stream>>>(
         q, k, v, beta, alpha, o, state_in, nullptr, nullptr, S_out, pred, nullptr, trec, flags, sm);
     return hipGetLastError();
 }
