@@ -20,7 +20,7 @@ The line printed is one JSON object:
 
 Inputs are synthetic (seeded, generated on the device) and rotate among
 several copies so that each step reads data evicted from the 256 MB
-Infinity Cache.  --gpus above 1 is refused: this build runs on one GPU.
+Infinity Cache.  --gpus above 1 is refused: the benchmark runs on one GPU.
 """
 from __future__ import annotations
 
@@ -383,7 +383,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} refused: this build runs on one GPU "
+        print(f"bench.py: --gpus {args.gpus} refused: the benchmark runs on one GPU "
               "(sharding is described, not run)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
@@ -423,7 +423,7 @@ def main():
         if args.only not in ("all", key):
             continue
         try:
-            r = bench_delta(wd, max(3, args.steps // 5), 2, 2, lin, wl)
+            r = bench_delta(wd, max(5, args.steps // 2), 5, 2, lin, wl)
             extra[wd.name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
                               "hbm_gbs": r["gbs"], "hbm_frac": r["gbs"] / HBM_PEAK_GBS,
                               "mfma_tflops": r["tflops"], "mfma_frac": r["tflops"] / BF16_MFMA_PEAK_TFS}
@@ -431,7 +431,7 @@ def main():
             extra[wd.name] = {"error": str(e)}
     if args.only in ("all", "delta_backward"):
         for wd in (wl.DELTA_BF16_PREFILL, wl.GATED_DELTA_BF16_PREFILL):
-            r = bench_delta_backward(wd, max(3, args.steps // 10), 2, 2, lin, wl)
+            r = bench_delta_backward(wd, max(5, args.steps // 5), 3, 2, lin, wl)
             extra["delta_backward_" + wd.name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
                                                   "us_per_call": 1e3 * r["event_ms_mean"], "hbm_gbs": r["gbs"],
                                                   "hbm_frac": r["gbs"] / HBM_PEAK_GBS, "bytes_per_call": r["bytes"]}

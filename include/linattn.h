@@ -74,7 +74,7 @@ enum { LA_NORMALIZE_QK = 1, LA_BETA_SIGMOID = 2 };
 typedef enum {
     LA_OK = 0,
     LA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, eps <= 0, bad dtype or chunk */
-    LA_ERR_UNSUPPORTED = 2, /* a valid configuration this build has no kernel for           */
+    LA_ERR_UNSUPPORTED = 2, /* a valid configuration the library has no kernel for         */
     LA_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than the *_workspace_bytes query   */
     LA_ERR_HIP = 4          /* a HIP launch failed; la_last_error() has the HIP message      */
 } la_status;

@@ -22,7 +22,7 @@ Functions and what pins them (the pins are in ``tests/test_oracle_pins.py``):
     invariant, the EMA closed form, the dense triangular-solve form via
     LAPACK, the orthonormal-key reduction to the additive memory and the
     Kaczmarz limit equal to the memory-capacity page's least-squares W*.
-    The per-token query read o_t = S_t^T q_t is this build's reading (the
+    The per-token query read o_t = S_t^T q_t is a reading taken here (the
     pages print no such sequence): parity of that read is pinned only by the
     dense form and the orthonormal-key reduction.
 ``la_backward`` -- the gradients of la_forward for a linear loss

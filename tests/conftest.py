@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests are skipped (not failed) on a machine without a GPU so the CPU
-    # suite can run everywhere; on the GPU machine they run.
+    # suite can run everywhere; on a machine with the GPU they run.
     try:
         import torch
         has_gpu = torch.cuda.is_available()
