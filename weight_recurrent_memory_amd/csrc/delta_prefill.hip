@@ -80,7 +80,7 @@ struct DL {
     static constexpr int LV = NS + 8;  // V rows
     static constexpr int LT = CH + 4;  // T and P rows
     static constexpr int KS = CH * LQ * 2;          // K_c rows (read transposed too)
-    static constexpr int WS = CH * LW * 2;          // W rows
+    static constexpr int WS = MAP ? CH * LW * 2 : 0;  // W rows (map pass)
     static constexpr int QS = OUT ? CH * LW * 2 : 0;
     static constexpr int VS = CH * LV * 2;          // V_c rows (read transposed)
     static constexpr int TS = CH * LT * 2;          // T (bf16, from the chunk's record)
@@ -95,7 +95,7 @@ struct DL {
     static constexpr int NCN = NS / 16;
     static constexpr int NCT = MAP ? NCN + DK / 16 : NCN;
     static constexpr int SLOTS = (NCT + NWV - 1) / NWV;
-    static constexpr int W_TPW = 4 * XR / NWV;      // W^T tiles per wave
+    static constexpr int W_TPW = 4 * XR / NWV;      // W^T tiles per wave (map pass)
 };
 
 // Chunk rows of a [T][D] bf16 matrix into LDS scaled to unit L2 norm (a zero
@@ -435,74 +435,134 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
             }
         }
 
-        // ---- W = T K (gated: T diag(gamma) K, gamma applied to the T
-        // fragment's columns in registers; computed as transposed tiles, rows
-        // land as 8-byte stores) and this wave's U_v = T V columns
-#pragma unroll
-        for (int c = 0; c < Y::W_TPW; ++c) {
-            const int dkt = w % XR, tt = (w / XR) * Y::W_TPW + c;
-            v4f acc = zero4();
-#pragma unroll
-            for (int kb = 0; kb < CH / 32; ++kb) {
-                if (32 * kb > 16 * tt + 15) continue;  // T is lower triangular
-                frag tf = M::load(&Ts[(16 * tt + li) * LT + 32 * kb], g);
-                if constexpr (GATED) {  // slot s <-> column 32 kb + 4g + s (s < 4), 32 kb + 16 + 4g + s - 4
-                    const v4f g0 = *reinterpret_cast<const v4f*>(&Ge[32 * kb + 4 * g]);
-                    const v4f g1 = *reinterpret_cast<const v4f*>(&Ge[32 * kb + 16 + 4 * g]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        tf[e] = M::cvt((float)tf[e] * g0[e]);
-                        tf[4 + e] = M::cvt((float)tf[4 + e] * g1[e]);
-                    }
-                }
-                M::mma(acc, M::load_tr(Ks, LQ, 32 * kb, 16 * dkt, lane), tf);
-            }
-            __bf16* dst = &Ws[(16 * tt + li) * Y::LW + 16 * dkt + 4 * g];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dst[r] = M::cvt(acc[r]);
-        }
         v4f U[SLOTS][4];
+        if constexpr (MAP) {
+            // ---- the map pass (sixteen waves at d = 128, each with one
+            // tile): W = T K (gated: T diag(gamma) K, gamma applied to the T
+            // fragment's columns in registers) is built once by all waves as
+            // transposed tiles (rows land as 8-byte stores), with this wave's
+            // U_v = T V columns; then U = U_v - W S
 #pragma unroll
-        for (int j = 0; j < SLOTS; ++j) {
-            const int id = w + NWV * j;
+            for (int c = 0; c < Y::W_TPW; ++c) {
+                const int dkt = w % XR, tt = (w / XR) * Y::W_TPW + c;
+                v4f acc = zero4();
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                U[j][tt] = zero4();
-                if (id < Y::NCN) {
+                for (int kb = 0; kb < CH / 32; ++kb) {
+                    if (32 * kb > 16 * tt + 15) continue;  // T is lower triangular
+                    frag tf = M::load(&Ts[(16 * tt + li) * LT + 32 * kb], g);
+                    if constexpr (GATED) {  // slot s <-> column 32 kb + 4g + s (s < 4), 32 kb + 16 + 4g + s - 4
+                        const v4f g0 = *reinterpret_cast<const v4f*>(&Ge[32 * kb + 4 * g]);
+                        const v4f g1 = *reinterpret_cast<const v4f*>(&Ge[32 * kb + 16 + 4 * g]);
 #pragma unroll
-                    for (int kb = 0; kb < CH / 32; ++kb) {
-                        if (32 * kb > 16 * tt + 15) continue;
-                        M::mma(U[j][tt], M::load(&Ts[(16 * tt + li) * LT + 32 * kb], g),
-                               M::load_tr(Vs, LV, 32 * kb, 16 * id, lane));
+                        for (int e = 0; e < 4; ++e) {
+                            tf[e] = M::cvt((float)tf[e] * g0[e]);
+                            tf[4 + e] = M::cvt((float)tf[4 + e] * g1[e]);
+                        }
                     }
+                    M::mma(acc, M::load_tr(Ks, LQ, 32 * kb, 16 * dkt, lane), tf);
                 }
-            }
-        }
-        __syncthreads();
-
-        // ---- the state chain over this wave's column tiles.  The chain is
-        // bound by LDS reads, so every operand fragment (a row block of W, a
-        // transposed row block of K) is read once and applied to all of the
-        // wave's tiles.
-        // U = U_v - W S, then beta o U (and, if wanted, the predictions V - U)
+                __bf16* dst = &Ws[(16 * tt + li) * Y::LW + 16 * dkt + 4 * g];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            v4f ws_[SLOTS];
-#pragma unroll
-            for (int j = 0; j < SLOTS; ++j) ws_[j] = zero4();
-#pragma unroll
-            for (int kb = 0; kb < DK / 32; ++kb) {
-                const frag wf = M::load(&Ws[(16 * tt + li) * Y::LW + 32 * kb], g);
-#pragma unroll
-                for (int j = 0; j < SLOTS; ++j)
-                    if (w + NWV * j < Y::NCT) M::mma(ws_[j], wf, M::from_tiles(X[j][2 * kb], X[j][2 * kb + 1]));
+                for (int r = 0; r < 4; ++r) dst[r] = M::cvt(acc[r]);
             }
 #pragma unroll
             for (int j = 0; j < SLOTS; ++j) {
                 const int id = w + NWV * j;
-                if (id >= Y::NCT) continue;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) U[j][tt][r] -= ws_[j][r];
+                for (int tt = 0; tt < 4; ++tt) {
+                    U[j][tt] = zero4();
+                    if (id < Y::NCN) {
+#pragma unroll
+                        for (int kb = 0; kb < CH / 32; ++kb) {
+                            if (32 * kb > 16 * tt + 15) continue;
+                            M::mma(U[j][tt], M::load(&Ts[(16 * tt + li) * LT + 32 * kb], g),
+                                   M::load_tr(Vs, LV, 32 * kb, 16 * id, lane));
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                v4f ws_[SLOTS];
+#pragma unroll
+                for (int j = 0; j < SLOTS; ++j) ws_[j] = zero4();
+#pragma unroll
+                for (int kb = 0; kb < DK / 32; ++kb) {
+                    const frag wf = M::load(&Ws[(16 * tt + li) * Y::LW + 32 * kb], g);
+#pragma unroll
+                    for (int j = 0; j < SLOTS; ++j)
+                        if (w + NWV * j < Y::NCT) M::mma(ws_[j], wf, M::from_tiles(X[j][2 * kb], X[j][2 * kb + 1]));
+                }
+#pragma unroll
+                for (int j = 0; j < SLOTS; ++j) U[j][tt] -= ws_[j];
+            }
+        } else {
+            // ---- output and state passes: U = T (V - diag(gamma) K S) per
+            // column tile, without W (measured faster at eight waves, slower
+            // for the sixteen-wave map pass)
+            // ---- this wave's corrections U = T (V - diag(gamma) K S), per column
+            // tile: R = V - diag(gamma) K S (K rows from LDS, S from registers),
+            // then U = T R.  Every K and T fragment is read once for all of the
+            // wave's tiles; the state-free W = T K never goes through LDS.
+            {
+                v4f ks[SLOTS][4];
+#pragma unroll
+                for (int j = 0; j < SLOTS; ++j)
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) ks[j][tt] = zero4();
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                    for (int kb = 0; kb < DK / 32; ++kb) {
+                        const frag kf = M::load(&Ks[(16 * tt + li) * LQ + 32 * kb], g);
+#pragma unroll
+                        for (int j = 0; j < SLOTS; ++j)
+                            if (w + NWV * j < Y::NCT) M::mma(ks[j][tt], kf, M::from_tiles(X[j][2 * kb], X[j][2 * kb + 1]));
+                    }
+                frag rf[SLOTS][CH / 32];  // R as B operands (the slot order of from_tiles and load_tr)
+#pragma unroll
+                for (int j = 0; j < SLOTS; ++j) {
+                    const int id = w + NWV * j;
+#pragma unroll
+                    for (int kb = 0; kb < CH / 32; ++kb) {
+                        frag vf = M::zero();
+                        if (id < Y::NCN) vf = M::load_tr(Vs, LV, 32 * kb, 16 * id, lane);  // M columns: no values
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int h = e >> 2, r = e & 3, t = 32 * kb + 16 * h + 4 * g + r;
+                            rf[j][kb][e] = M::cvt((float)vf[e] - (GATED ? Ge[t] : 1.f) * ks[j][2 * kb + h][r]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+                    for (int j = 0; j < SLOTS; ++j) U[j][tt] = zero4();
+#pragma unroll
+                    for (int kb = 0; kb < CH / 32; ++kb) {
+                        if (32 * kb > 16 * tt + 15) continue;  // T is lower triangular
+                        const frag tf = M::load(&Ts[(16 * tt + li) * LT + 32 * kb], g);
+#pragma unroll
+                        for (int j = 0; j < SLOTS; ++j)
+                            if (w + NWV * j < Y::NCT) M::mma(U[j][tt], tf, rf[j][kb]);
+                    }
+                }
+            }
+        }
+        if constexpr (OUT) __syncthreads();  // P of every wave
+
+        // ---- the state chain over this wave's column tiles.  The chain is
+        // bound by LDS reads, so every operand fragment (a transposed row
+        // block of K, a row block of P) is read once and applied to all of
+        // the wave's tiles.
+        // beta o U (and, if wanted, the predictions V - U)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+            for (int j = 0; j < SLOTS; ++j) {
+                const int id = w + NWV * j;
+                if (id >= Y::NCT) continue;
                 if constexpr (OUT) {
                     if (pred) {  // rows past the segment end are dropped by the resource
                         const rsrc_t rp = make_rsrc(pred + row0 * NS, (uint32_t)t_end * NS * 2);
