@@ -51,9 +51,9 @@ LA_TRAFFIC = {
                 "weight_recurrent_memory_amd/csrc/common.hpp",
                 "weight_recurrent_memory_amd/csrc/kernels.hpp",
                 "weight_recurrent_memory_amd/csrc/segments.hpp"],
-    "sha256": "2acc9b5f1fe0ce2ee502130715b530df60480f52243c7af92221744c74eae477",
-    "fetch_kib": 86635.9, "fetch_scale": 2.0,
-    "write_kib": 56660.5, "write_scale": 1.0,
+    "sha256": "be78534f2748856acd5724280d83c79d8787afa9804f00b8742dab8532e06007",
+    "fetch_kib": 86678.9, "fetch_scale": 2.0,
+    "write_kib": 56808.3, "write_scale": 1.0,
 }
 
 
