@@ -73,9 +73,13 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ v4u buf_load16(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
-// Non-temporal (streaming) 16-byte store: for results this kernel never reads.
-__device__ __forceinline__ void buf_store16_nt(rsrc_t r, uint32_t off, v4u x) {
-    __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, /*nt*/ 2);
+// Streaming 16-byte store for results this kernel never reads: non-temporal
+// and written through the L2 (cache policy sc1 | nt), so output lines do not
+// stay dirty in the L2 beside the input stream.  On the LA prefill this
+// measured 44 us per launch against 50 us with the non-temporal hint alone.
+constexpr int kStreamWT = 16 | 2;
+__device__ __forceinline__ void buf_store16_stream(rsrc_t r, uint32_t off, v4u x) {
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, kStreamWT);
 }
 
 template <typename T> struct Elem;

@@ -127,19 +127,42 @@ struct Published {
     }
 };
 
-// acc += phi(K)^T [V | 1] over tokens [t0, t1).  NPF chunks are in flight
-// ahead of the one being staged (a streaming reduction needs that many bytes
-// outstanding to cover the memory latency); the two LDS chunk buffers
+// Chunks of keys and values held in flight by the aggregate pass: enough
+// bytes outstanding per workgroup to cover the memory latency of a streaming
+// reduction.
+template <typename TIn, int DK, int DV>
+constexpr int kPrefetch = (DK + DV) * (int)sizeof(TIn) <= 256 ? 4 : 2;
+
+// acc += phi(K)^T [V | 1] for the chunk staged in LDS at Ks, Vs.
+template <typename TIn, int DK, int DV>
+__device__ __forceinline__ void add_staged(const typename Mma<TIn>::op_t* Ks, const typename Mma<TIn>::op_t* Vs,
+                                           v4f (&acc)[Layout<TIn, DK, DV>::RTW][Layout<TIn, DK, DV>::NCT],
+                                           int lane, int w) {
+    using M = Mma<TIn>;
+    using LY = Layout<TIn, DK, DV>;
+    constexpr int NVT = DV / 16;
+#pragma unroll
+    for (int j = 0; j < CH / M::KB; ++j) {
+#pragma unroll
+        for (int i = 0; i < LY::RTW; ++i) {
+            const typename M::frag a = M::load_tr(Ks, LY::LQ, j * M::KB, 16 * (w * LY::RTW + i), lane);
+#pragma unroll
+            for (int c = 0; c < LY::NCT; ++c)
+                M::mma(acc[i][c], a, c < NVT ? M::load_tr(Vs, LY::LV, j * M::KB, 16 * c, lane) : M::ones());
+        }
+    }
+}
+
+// acc += phi(K)^T [V | 1] over tokens [t0, t1), chunks in order.  NPF chunks
+// are in flight ahead of the one being staged; the two LDS chunk buffers
 // alternate, so one barrier per chunk suffices.  Rows at or past t1 read as
 // zero through the buffer resources.
 template <typename TIn, int DK, int DV>
 __device__ __forceinline__ void accumulate_kv(const TIn* kh, const TIn* vh, int t0, int t1,
                                               v4f (&acc)[Layout<TIn, DK, DV>::RTW][Layout<TIn, DK, DV>::NCT],
                                               typename Mma<TIn>::op_t* Kb, typename Mma<TIn>::op_t* Vb, int tid) {
-    using M = Mma<TIn>;
     using LY = Layout<TIn, DK, DV>;
-    constexpr int NPF = (DK + DV) * sizeof(TIn) <= 256 ? 4 : 2;
-    constexpr int NVT = DV / 16;
+    constexpr int NPF = kPrefetch<TIn, DK, DV>;
     const int lane = tid & 63, w = wave_id(tid);
     if (t0 >= t1) return;
     const rsrc_t rk = make_rsrc(kh, (uint32_t)t1 * DK * sizeof(TIn));
@@ -153,23 +176,14 @@ __device__ __forceinline__ void accumulate_kv(const TIn* kh, const TIn* vh, int 
     }
     auto body = [&](auto slot, int c0) {
         constexpr int sl = decltype(slot)::value, b = sl & 1;
-        typename M::op_t* Ks = Kb + b * LY::KSZ;
-        typename M::op_t* Vs = Vb + b * LY::VSZ;
+        typename Mma<TIn>::op_t* Ks = Kb + b * LY::KSZ;
+        typename Mma<TIn>::op_t* Vs = Vb + b * LY::VSZ;
         stage_rows_phi<TIn, DK, NTHR>(kr[sl], t1 - c0, tid, Ks, LY::LQ);
         stage_rows_raw<TIn, DV, NTHR>(vr[sl], tid, Vs, LY::LV);
         kr[sl].load_buf(rk, c0 + NPF * CH, tid);
         vr[sl].load_buf(rv, c0 + NPF * CH, tid);
         __syncthreads();
-#pragma unroll
-        for (int j = 0; j < CH / M::KB; ++j) {
-#pragma unroll
-            for (int i = 0; i < LY::RTW; ++i) {
-                const typename M::frag a = M::load_tr(Ks, LY::LQ, j * M::KB, 16 * (w * LY::RTW + i), lane);
-#pragma unroll
-                for (int c = 0; c < LY::NCT; ++c)
-                    M::mma(acc[i][c], a, c < NVT ? M::load_tr(Vs, LY::LV, j * M::KB, 16 * c, lane) : M::ones());
-            }
-        }
+        add_staged<TIn, DK, DV>(Ks, Vs, acc, lane, w);
     };
     // Whole groups of NPF chunks, with no exit inside a group: the wait
     // counts then stay exact across the loop's back edge (a group reaching
@@ -182,6 +196,65 @@ __device__ __forceinline__ void accumulate_kv(const TIn* kh, const TIn* vh, int 
             body(std::integral_constant<int, 3>{}, c0 + 3 * CH);
         }
     }
+    __syncthreads();  // the caller reuses the buffers
+}
+
+// The raw key and value rows of a segment's first NPF chunks, kept in
+// registers from the aggregate pass to the output pass so that they are read
+// from memory once.
+template <typename TIn, int DK, int DV>
+struct KeptChunks {
+    static constexpr int N = kPrefetch<TIn, DK, DV>;
+    static constexpr int VGPRS = N * (ChunkRegs<TIn, DK, NTHR>::NV + ChunkRegs<TIn, DV, NTHR>::NV) * 4;
+    ChunkRegs<TIn, DK, NTHR> k[N];
+    ChunkRegs<TIn, DV, NTHR> v[N];
+};
+
+// The segment's aggregate phi(K)^T [V | 1] over [t0, t1), its groups of NPF
+// chunks taken last to first: the group loaded last is the segment's first
+// NPF chunks, which stay in `kept`.  Same pipelining as accumulate_kv; the
+// order of the sum is fixed, so results do not depend on timing.
+template <typename TIn, int DK, int DV>
+__device__ __forceinline__ void aggregate_keep(const TIn* kh, const TIn* vh, int t0, int t1,
+                                               v4f (&acc)[Layout<TIn, DK, DV>::RTW][Layout<TIn, DK, DV>::NCT],
+                                               typename Mma<TIn>::op_t* Kb, typename Mma<TIn>::op_t* Vb,
+                                               KeptChunks<TIn, DK, DV>& kept, int tid) {
+    using LY = Layout<TIn, DK, DV>;
+    constexpr int NPF = KeptChunks<TIn, DK, DV>::N, GS = NPF * CH;
+    const int lane = tid & 63, w = wave_id(tid);
+    const rsrc_t rk = make_rsrc(kh, (uint32_t)t1 * DK * sizeof(TIn));
+    const rsrc_t rv = make_rsrc(vh, (uint32_t)t1 * DV * sizeof(TIn));
+    // first chunk of the last group (t0 itself for a segment of at most one
+    // group, or an empty one, whose rows all read as zero)
+    int c0 = t0 + (t1 - t0 > GS ? (t1 - t0 - 1) / GS * GS : 0);
+#pragma unroll
+    for (int p = 0; p < NPF; ++p) {
+        kept.k[p].load_buf(rk, c0 + p * CH, tid);
+        kept.v[p].load_buf(rv, c0 + p * CH, tid);
+    }
+    auto body = [&](auto slot, auto reload, int c) {
+        constexpr int sl = decltype(slot)::value, b = sl & 1;
+        typename Mma<TIn>::op_t* Ks = Kb + b * LY::KSZ;
+        typename Mma<TIn>::op_t* Vs = Vb + b * LY::VSZ;
+        stage_rows_phi<TIn, DK, NTHR>(kept.k[sl], t1 - c, tid, Ks, LY::LQ);
+        stage_rows_raw<TIn, DV, NTHR>(kept.v[sl], tid, Vs, LY::LV);
+        if constexpr (decltype(reload)::value) {
+            kept.k[sl].load_buf(rk, c - GS, tid);
+            kept.v[sl].load_buf(rv, c - GS, tid);
+        }
+        __syncthreads();
+        add_staged<TIn, DK, DV>(Ks, Vs, acc, lane, w);
+    };
+    auto group = [&](auto reload, int cg) {
+        body(std::integral_constant<int, 0>{}, reload, cg);
+        body(std::integral_constant<int, 1>{}, reload, cg + CH);
+        if constexpr (NPF == 4) {
+            body(std::integral_constant<int, 2>{}, reload, cg + 2 * CH);
+            body(std::integral_constant<int, 3>{}, reload, cg + 3 * CH);
+        }
+    };
+    for (; c0 > t0; c0 -= GS) group(std::true_type{}, c0);
+    group(std::false_type{}, t0);
     __syncthreads();  // the caller reuses the buffers
 }
 
@@ -198,6 +271,11 @@ struct OutChunk {
         const int lane = tid & 63, g = lane >> 4, li = lane & 15;
         kr.load_buf(rk, c0, tid);
         vr.load_buf(rv, c0, tid);
+        load_q(rq, c0, w, tid);
+    }
+    __device__ __forceinline__ void load_q(rsrc_t rq, int c0, int w, int tid) {
+        constexpr int KB = Mma<TIn>::KB;
+        const int lane = tid & 63, g = lane >> 4, li = lane & 15;
 #pragma unroll
         for (int kk = 0; kk < QF; ++kk)
             qraw[kk] = buf_load16(rq, (uint32_t)(((c0 + 16 * w + li) * DK + kk * KB + g * (KB / 4)) * (int)sizeof(TIn)));
@@ -217,11 +295,14 @@ struct OutChunk {
 // bf16 copy of S^T are shared through LDS.  The LDS chunk buffers are double
 // buffered: while the matrix cores work on chunk c, the same instruction
 // stream stages chunk c + 1 (its loads were issued one chunk earlier) and
-// issues the loads of chunk c + 2, so one barrier per chunk suffices.
+// issues the loads of chunk c + 2, so one barrier per chunk suffices.  The
+// segment's first chunks take their keys and values from `kept` (only their
+// queries are loaded); `in` arrives holding the first chunk's queries.
 template <typename TIn, int DK, int DV, int W>
 __device__ __forceinline__ void output_pass(rsrc_t rq, rsrc_t rk, rsrc_t rv, rsrc_t ro, int t_beg, int t_end,
                                             float eps, v4f (&S)[Layout<TIn, DK, DV>::RTW][Layout<TIn, DK, DV>::NCT],
-                                            OutChunk<TIn, DK, DV>& in, typename Mma<TIn>::op_t* lds, int tid) {
+                                            const KeptChunks<TIn, DK, DV>& kept, OutChunk<TIn, DK, DV>& in,
+                                            typename Mma<TIn>::op_t* lds, int tid) {
     using M = Mma<TIn>;
     using op = typename M::op_t;
     using frag = typename M::frag;
@@ -234,6 +315,7 @@ __device__ __forceinline__ void output_pass(rsrc_t rq, rsrc_t rk, rsrc_t rv, rsr
     constexpr int NJ = W / KT + 1;          // key fragments reaching query block W
     constexpr int NJC = CH / KB;            // key fragments per chunk
     constexpr int SZ = (int)sizeof(TIn);
+    constexpr int NK = KeptChunks<TIn, DK, DV>::N;  // chunks kept from the aggregate pass
     // V^T fragments are kept for the state update when they fit in 32 VGPRs.
     constexpr bool kKeepV = NVT * NJC * (int)(sizeof(frag) / 4) <= 32;
     const int lane = tid & 63, g = lane >> 4, li = lane & 15;
@@ -242,7 +324,6 @@ __device__ __forceinline__ void output_pass(rsrc_t rq, rsrc_t rk, rsrc_t rv, rsr
     op* Sb = Vb + 2 * LY::VSZ;
 
     frag qf[2][QF];
-    auto load_chunk = [&](int c0) { in.load(rq, rk, rv, c0, W, tid); };
     auto write_st = [&](op* st) {
 #pragma unroll
         for (int i = 0; i < RTW; ++i)
@@ -253,24 +334,32 @@ __device__ __forceinline__ void output_pass(rsrc_t rq, rsrc_t rk, rsrc_t rv, rsr
                 for (int r = 0; r < 4; ++r) dst[r] = M::cvt(S[i][c][r]);
             }
     };
-    // Stage chunk c0 (already in registers) into buffer set b.
-    auto stage = [&](auto bconst, int c0) {
+    // Stage chunk c0 (keys and values kr, vr and the queries of `in`, all in
+    // registers) into buffer set b.
+    auto stage = [&](auto bconst, int c0, const ChunkRegs<TIn, DK, NTHR>& kr, const ChunkRegs<TIn, DV, NTHR>& vr) {
         constexpr int b = decltype(bconst)::value;
-        stage_rows_phi<TIn, DK, NTHR>(in.kr, t_end - c0, tid, Kb + b * LY::KSZ, LQ);
-        stage_rows_raw<TIn, DV, NTHR>(in.vr, tid, Vb + b * LY::VSZ, LV);
+        stage_rows_phi<TIn, DK, NTHR>(kr, t_end - c0, tid, Kb + b * LY::KSZ, LQ);
+        stage_rows_raw<TIn, DV, NTHR>(vr, tid, Vb + b * LY::VSZ, LV);
 #pragma unroll
         for (int kk = 0; kk < QF; ++kk) qf[b][kk] = M::phi_frag(in.qraw[kk]);
     };
+    // Loads of segment chunk n (starting at c0): queries only while it is kept.
+    auto load_chunk = [&](auto nconst, int c0) {
+        if constexpr (decltype(nconst)::value < NK) in.load_q(rq, c0, W, tid);
+        else in.load(rq, rk, rv, c0, W, tid);
+    };
 
-    // prologue (chunk t_beg arrives in registers): chunk t_beg staged, chunk
-    // t_beg + CH in flight
-    stage(std::integral_constant<int, 0>{}, t_beg);
+    // prologue: chunk 0 staged, chunk 1 in flight
+    stage(std::integral_constant<int, 0>{}, t_beg, kept.k[0], kept.v[0]);
     write_st(Sb);
-    load_chunk(t_beg + CH);
+    load_chunk(std::integral_constant<int, 1>{}, t_beg + CH);
     __syncthreads();
 
-    auto iter = [&](auto bconst, int c0) {
+    // One chunk; n is the segment index of the next chunk when that is a kept
+    // one (n < NK), else NK.
+    auto iter = [&](auto bconst, auto nconst, int c0) {
         constexpr int b = decltype(bconst)::value;
+        constexpr int n = decltype(nconst)::value;
         const op* Kc = Kb + b * LY::KSZ;
         const op* Vc = Vb + b * LY::VSZ;
         const op* Sc = Sb + (NST == 2 ? b : 0) * LY::SSZ;
@@ -335,13 +424,13 @@ __device__ __forceinline__ void output_pass(rsrc_t rq, rsrc_t rk, rsrc_t rv, rsr
                 const auto s1 = __builtin_amdgcn_permlane16_swap(a1, b1, false, false);
                 const v4u x = v4u{(uint32_t)s0[0], (uint32_t)s1[0], (uint32_t)s0[1], (uint32_t)s1[1]};
                 const int col = 16 * c + 16 * (g & 1) + 8 * (g >> 1);
-                buf_store16_nt(ro, (uint32_t)((orow * DV + col) * SZ), x);
+                buf_store16_stream(ro, (uint32_t)((orow * DV + col) * SZ), x);
             }
         } else {
 #pragma unroll
             for (int c = 0; c < NVT; ++c) {
                 const v4f n = num_tile(c);
-                buf_store16_nt(ro, (uint32_t)((orow * DV + 16 * c + 4 * g) * SZ),
+                buf_store16_stream(ro, (uint32_t)((orow * DV + 16 * c + 4 * g) * SZ),
                                v4u{__float_as_uint(n[0]), __float_as_uint(n[1]), __float_as_uint(n[2]),
                                    __float_as_uint(n[3])});
             }
@@ -359,18 +448,26 @@ __device__ __forceinline__ void output_pass(rsrc_t rq, rsrc_t rk, rsrc_t rv, rsr
 
         // next chunk: stage it, start the one after (reads past the segment
         // end return zero without memory traffic)
-        stage(std::integral_constant<int, b ^ 1>{}, c0 + CH);
-        load_chunk(c0 + 2 * CH);
+        if constexpr (n < NK) stage(std::integral_constant<int, b ^ 1>{}, c0 + CH, kept.k[n], kept.v[n]);
+        else stage(std::integral_constant<int, b ^ 1>{}, c0 + CH, in.kr, in.vr);
+        load_chunk(std::integral_constant<int, n + 1>{}, c0 + 2 * CH);
         if constexpr (NST == 1) __syncthreads();  // all reads of S^T done
         write_st(Sb + (NST == 2 ? (b ^ 1) : 0) * LY::SSZ);
         __syncthreads();
     };
-    // Pairs of chunks with no exit between them, so the wait counts stay
-    // exact across the back edge; a chunk past t_end reads zeros, adds
-    // nothing to the state and has its stores dropped.
-    for (int c0 = t_beg; c0 < t_end; c0 += 2 * CH) {
-        iter(std::integral_constant<int, 0>{}, c0);
-        iter(std::integral_constant<int, 1>{}, c0 + CH);
+    // The kept chunks (run whatever the segment's length), then pairs of
+    // chunks with no exit between them, so the wait counts stay exact across
+    // the back edge; a chunk past t_end reads zeros, adds nothing to the
+    // state and has its stores dropped.
+    iter(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, t_beg);
+    iter(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{}, t_beg + CH);
+    if constexpr (NK == 4) {
+        iter(std::integral_constant<int, 0>{}, std::integral_constant<int, 3>{}, t_beg + 2 * CH);
+        iter(std::integral_constant<int, 1>{}, std::integral_constant<int, 4>{}, t_beg + 3 * CH);
+    }
+    for (int c0 = t_beg + NK * CH; c0 < t_end; c0 += 2 * CH) {
+        iter(std::integral_constant<int, 0>{}, std::integral_constant<int, NK>{}, c0);
+        iter(std::integral_constant<int, 1>{}, std::integral_constant<int, NK>{}, c0 + CH);
     }
 }
 
@@ -431,17 +528,18 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
     for (int i = 0; i < RTW; ++i)
 #pragma unroll
         for (int c = 0; c < NCT; ++c) A[i][c] = zero4();
-    accumulate_kv<TIn, DK, DV>(kh, vh, t_beg, t_end, A, Kb, Vb, tid);
+    KeptChunks<TIn, DK, DV> kept;
+    aggregate_keep<TIn, DK, DV>(kh, vh, t_beg, t_end, A, Kb, Vb, kept, tid);
 
-    // The first chunk of the output pass is fetched now, so its latency
-    // overlaps the look-back.  Buffer resources end at the segment end: reads
+    // The first chunk's queries are fetched now, so their latency overlaps
+    // the look-back.  Buffer resources end at the segment end: reads
     // past it are zero, writes past it are dropped.
     const rsrc_t rq = make_rsrc(q + row0 * DK, (uint32_t)t_end * DK * sizeof(TIn));
     const rsrc_t rk = make_rsrc(kh, (uint32_t)t_end * DK * sizeof(TIn));
     const rsrc_t rv = make_rsrc(vh, (uint32_t)t_end * DV * sizeof(TIn));
     const rsrc_t ro = make_rsrc(o + row0 * DV, (uint32_t)t_end * DV * sizeof(TIn));
     OutChunk<TIn, DK, DV> first;
-    first.load(rq, rk, rv, t_beg, w, tid);
+    first.load_q(rq, t_beg, w, tid);
 
     // ---- 2. publish the aggregate, then walk back for the incoming state
     v4f S[RTW][NCT];
@@ -513,7 +611,9 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
             PUB::load(incl + (sbase + jstar) * E, S, w, lane);
             // Aggregates in batches: every load of a batch is issued before
             // the first add, so the walk costs one memory latency per batch.
-            constexpr int BATCH = 160 / (RTW * NCT * 4) >= 8 ? 8 : 160 / (RTW * NCT * 4) >= 2 ? 160 / (RTW * NCT * 4) : 1;
+            // (A batch fits in the registers left beside the kept chunks.)
+            constexpr int BUDGET = 160 - KeptChunks<TIn, DK, DV>::VGPRS;
+            constexpr int BATCH = BUDGET / (RTW * NCT * 4) >= 8 ? 8 : BUDGET / (RTW * NCT * 4) >= 2 ? BUDGET / (RTW * NCT * 4) : 1;
             for (int p = jstar + 1; p < seg; p += BATCH) {
                 v4f t[BATCH][RTW][NCT];
 #pragma unroll
@@ -573,10 +673,10 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
 
     // ---- 4. the chunk loop from the incoming state
     switch (w) {
-        case 0: output_pass<TIn, DK, DV, 0>(rq, rk, rv, ro, t_beg, t_end, eps, S, first, lds, tid); break;
-        case 1: output_pass<TIn, DK, DV, 1>(rq, rk, rv, ro, t_beg, t_end, eps, S, first, lds, tid); break;
-        case 2: output_pass<TIn, DK, DV, 2>(rq, rk, rv, ro, t_beg, t_end, eps, S, first, lds, tid); break;
-        default: output_pass<TIn, DK, DV, 3>(rq, rk, rv, ro, t_beg, t_end, eps, S, first, lds, tid); break;
+        case 0: output_pass<TIn, DK, DV, 0>(rq, rk, rv, ro, t_beg, t_end, eps, S, kept, first, lds, tid); break;
+        case 1: output_pass<TIn, DK, DV, 1>(rq, rk, rv, ro, t_beg, t_end, eps, S, kept, first, lds, tid); break;
+        case 2: output_pass<TIn, DK, DV, 2>(rq, rk, rv, ro, t_beg, t_end, eps, S, kept, first, lds, tid); break;
+        default: output_pass<TIn, DK, DV, 3>(rq, rk, rv, ro, t_beg, t_end, eps, S, kept, first, lds, tid); break;
     }
 }
 

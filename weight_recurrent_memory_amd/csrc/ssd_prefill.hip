@@ -380,7 +380,7 @@ __device__ __forceinline__ void ssd_output_pass(rsrc_t rq, rsrc_t rk, rsrc_t rv,
             const auto s1 = __builtin_amdgcn_permlane16_swap(a1, b1, false, false);
             const v4u x = v4u{(uint32_t)s0[0], (uint32_t)s1[0], (uint32_t)s0[1], (uint32_t)s1[1]};
             const int col = 16 * c + 16 * (g & 1) + 8 * (g >> 1);
-            buf_store16_nt(ro, (uint32_t)((orow * DV + col) * 2), x);
+            buf_store16_stream(ro, (uint32_t)((orow * DV + col) * 2), x);
         }
 
         // state update (this wave's dk rows): decay, then the keys scaled by
