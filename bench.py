@@ -52,8 +52,8 @@ LA_TRAFFIC = {
                 "weight_recurrent_memory_amd/csrc/common.hpp",
                 "weight_recurrent_memory_amd/csrc/kernels.hpp",
                 "weight_recurrent_memory_amd/csrc/segments.hpp"],
-    "sha256": "e4b1a927be7239a9122413339b1d0a462e50fc3fc090dfd1a1d02c2a5086a17f",
-    "fetch_kib": 70528.9, "fetch_scale": 2.0,
+    "sha256": "8a1c05f785bc34ee923c50a50735c4808e955abc50d893e23f3736166ef11e64",
+    "fetch_kib": 70050.5, "fetch_scale": 2.0,
     "write_kib": 48397.1, "write_scale": 1.0,
 }
 

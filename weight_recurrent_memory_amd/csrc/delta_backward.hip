@@ -716,7 +716,9 @@ hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const
     if ((err = hipGetLastError()) != hipSuccess) return err;
     // one workgroup per compute unit (the LDS allows one), each looping over chunks
     int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;  // the grid size only sets the work split
     const long total = (long)HT * NC;
     const int grid = (int)(total < cus ? total : cus);
     dlb_grad_kernel<DK, DV, GATED><<<dim3(grid), dim3(NT), 0, stream>>>(q, k, v, beta, alpha, dO, sst, gst, dq, dk, dv,
