@@ -662,63 +662,106 @@ constexpr int kMapWaves = (DK == 128 && DV == 128) ? 16 : 8;
 template <int DK, int DV>
 constexpr int kOutWaves = 8;
 
+// XCDs of the chip: dispatch places block b on XCD b mod 8.
+constexpr int kXcds = 8;
+
+// Blocks of delta_compose_kernel for NH states.
+template <int DV>
+inline unsigned compose_blocks(int NH) { return (unsigned)(((NH + kXcds - 1) / kXcds) * kXcds * (DV / 16)); }
+
 // S_in(0) = S0 (or 0); S_in(g+1) = M_g S_in(g) + N_g in fp32 MFMA.  One
 // workgroup per (16-column block of the state, sequence and head); serial
 // over the sequence's segments.  REV runs the same recurrence from the last
 // segment down (the backward pass: G(G-1) = S0, G(g-1) = M_g G(g) + N_g).
+// Every column block of a head reads the whole of each M_g, so the blocks of
+// one head are numbered to land on one XCD (dispatch places block b on XCD
+// b mod 8, and each XCD has its own L2): M_g then comes from memory once per
+// head instead of once per column block.  M_g is staged in LDS, and M_{g+1},
+// N_{g+1} are loaded into registers while step g runs; the staged rows are
+// DK + 4 floats apart, so the 16-byte row reads of each eight consecutive
+// lanes fall in distinct banks.
 template <int DK, int DV, bool PACKED, bool REV = false>
 __global__ __launch_bounds__(256) void delta_compose_kernel(const float* __restrict__ map_n,
                                                             const float* __restrict__ map_m,
                                                             const float* S0, float* __restrict__ state_in,
                                                             SegMap sm) {
-    constexpr int RPW = DK / 64;  // row tiles per wave
+    constexpr int RPW = DK / 64;              // row tiles per wave
+    constexpr int LM = DK + 4;                // row stride of the staged map
+    constexpr int MV = DK * DK / (4 * 256);   // 16-byte pieces of a map per thread
     __shared__ float Sb[DK][17];
+    __shared__ __align__(16) float Ms[DK * LM];
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int w = wave_id(tid);
-    const int ct = blockIdx.x, col = 16 * ct + li;
-    const int p = blockIdx.y, nseq = p / sm.H, h = p % sm.H;  // p = the state's index in S0
+    // block b = (p / 8) (8 NCB) + ct 8 + p % 8
+    constexpr int NCB = DV / 16;
+    const int b = blockIdx.x, xcd = b % kXcds, rest = b / kXcds;
+    const int ct = rest % NCB, col = 16 * ct + li;
+    const int p = (rest / NCB) * kXcds + xcd;  // the state's index in S0
+    if (p >= sm.N * sm.H) return;
+    const int nseq = p / sm.H, h = p % sm.H;
     const long base = sm.slot<PACKED>(nseq, h);  // slot of the sequence's first segment
     int G = sm.segs<PACKED>(nseq);
     G = G < 0 ? 0 : (G > sm.NS - sm.seg_base<PACKED>(nseq) ? sm.NS - sm.seg_base<PACKED>(nseq) : G);
     if (G == 0) return;
+    auto map_of = [&](int s) -> long { return REV ? base + G - 1 - s : base + s; };  // the map of step s
+    v4f mreg[MV];
+    v4f nreg[RPW];
+    auto load_map = [&](long from) {
+        const float* Mg = map_m + from * DK * DK;
+        const float* Ng = map_n + from * DK * DV;
+#pragma unroll
+        for (int j = 0; j < MV; ++j) mreg[j] = *reinterpret_cast<const v4f*>(Mg + 4 * (j * 256 + tid));
+#pragma unroll
+        for (int i = 0; i < RPW; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) nreg[i][r] = Ng[(16 * (w * RPW + i) + 4 * g + r) * DV + col];
+    };
+    // The initial state: every load issued before the first store (a load
+    // behind a store would wait for that store, as both count in vmcnt).
     v4f acc[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) acc[i] = zero4();
+    if (S0) {
+#pragma unroll
+        for (int i = 0; i < RPW; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][r] = S0[((long)p * DK + 16 * (w * RPW + i) + 4 * g + r) * DV + col];
+    }
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
         const int rt = w * RPW + i;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * rt + 4 * g + r;
-            const float x = S0 ? S0[((long)p * DK + row) * DV + col] : 0.f;
-            acc[i][r] = x;
-            Sb[row][li] = x;
-            state_in[((REV ? base + G - 1 : base) * DK + row) * DV + col] = x;
+            Sb[row][li] = acc[i][r];
+            state_in[((REV ? base + G - 1 : base) * DK + row) * DV + col] = acc[i][r];
         }
     }
-    __syncthreads();
+    if (G > 1) load_map(map_of(0));
     for (int s = 0; s + 1 < G; ++s) {
-        const long from = REV ? base + G - 1 - s : base + s;  // the map applied
-        const long to = REV ? from - 1 : from + 1;            // the state it produces
-        const float* Mg = map_m + from * DK * DK;
-        const float* Ng = map_n + from * DK * DV;
+        const long to = REV ? map_of(s) - 1 : map_of(s) + 1;  // the state step s produces
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) {
-            const int rt = w * RPW + i;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][r] = Ng[(16 * rt + 4 * g + r) * DV + col];
+        for (int j = 0; j < MV; ++j) {
+            const int e = 4 * (j * 256 + tid), row = e / DK, c = e % DK;
+            *reinterpret_cast<v4f*>(&Ms[row * LM + c]) = mreg[j];
         }
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) acc[i] = nreg[i];
+        __syncthreads();  // Ms and Sb written
+        if (s + 2 < G) load_map(map_of(s + 1));
 #pragma unroll 4
         for (int kb = 0; kb < DK / 16; ++kb) {
-            v4f b;
+            v4f bb;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) b[e] = Sb[16 * kb + 4 * g + e][li];
+            for (int e = 0; e < 4; ++e) bb[e] = Sb[16 * kb + 4 * g + e][li];
 #pragma unroll
             for (int i = 0; i < RPW; ++i) {
                 const int rt = w * RPW + i;
-                const v4f a = *reinterpret_cast<const v4f*>(&Mg[(16 * rt + li) * DK + 16 * kb + 4 * g]);
-                Mma<float>::mma(acc[i], a, b);
+                const v4f a = *reinterpret_cast<const v4f*>(&Ms[(16 * rt + li) * LM + 16 * kb + 4 * g]);
+                Mma<float>::mma(acc[i], a, bb);
             }
         }
-        __syncthreads();
+        __syncthreads();  // every read of Ms and Sb done
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             const int rt = w * RPW + i;
@@ -729,7 +772,6 @@ __global__ __launch_bounds__(256) void delta_compose_kernel(const float* __restr
                 state_in[(to * DK + row) * DV + col] = acc[i][r];
             }
         }
-        __syncthreads();
     }
 }
 
@@ -752,7 +794,7 @@ hipError_t launch_packing(const bf16_t* q, const bf16_t* k, const bf16_t* v, con
             q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, nullptr, nullptr, trec, flags, sm);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    delta_compose_kernel<DK, DV, PACKED><<<dim3(DV / 16, sm.N * sm.H), dim3(256), 0, stream>>>(map_n, map_m, S0, state_in,
+    delta_compose_kernel<DK, DV, PACKED><<<dim3(compose_blocks<DV>(sm.N * sm.H)), dim3(256), 0, stream>>>(map_n, map_m, S0, state_in,
                                                                                       sm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     constexpr int NWO = kOutWaves<DK, DV>;
@@ -781,7 +823,7 @@ hipError_t launch_states(const bf16_t* q, const bf16_t* k, const bf16_t* v, cons
             q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, nullptr, nullptr, trec, 0, sm);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    delta_compose_kernel<DK, DV, false><<<dim3(DV / 16, sm.N * sm.H), dim3(256), 0, stream>>>(map_n, map_m, S0,
+    delta_compose_kernel<DK, DV, false><<<dim3(compose_blocks<DV>(sm.N * sm.H)), dim3(256), 0, stream>>>(map_n, map_m, S0,
                                                                                           state_in, sm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     delta_chunk_kernel<DK, DV, kStates, GATED, false><<<dim3(sm.H * sm.NS), dim3(NT), 0, stream>>>(
@@ -826,7 +868,7 @@ hipError_t launch_delta_compose_rev(const float* map_c, const float* map_mt, con
     if (sm.packed()) return hipErrorInvalidValue;
 #define REV_CASE(A, B)                                                                                        \
     if (dk == A && dv == B) {                                                                                 \
-        delta_compose_kernel<A, B, false, true><<<dim3(B / 16, sm.N * sm.H), dim3(256), 0, stream>>>(        \
+        delta_compose_kernel<A, B, false, true><<<dim3(compose_blocks<B>(sm.N * sm.H)), dim3(256), 0, stream>>>(        \
             map_c, map_mt, G_last, g_end, sm);                                                                \
         return hipGetLastError();                                                                             \
     }
