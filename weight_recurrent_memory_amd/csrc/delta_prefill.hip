@@ -794,8 +794,8 @@ hipError_t launch_packing(const bf16_t* q, const bf16_t* k, const bf16_t* v, con
             q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, nullptr, nullptr, trec, flags, sm);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    delta_compose_kernel<DK, DV, PACKED><<<dim3(compose_blocks<DV>(sm.N * sm.H)), dim3(256), 0, stream>>>(map_n, map_m, S0, state_in,
-                                                                                      sm);
+    delta_compose_kernel<DK, DV, PACKED><<<dim3(compose_blocks<DV>(sm.N * sm.H)), dim3(256), 0, stream>>>(
+        map_n, map_m, S0, state_in, sm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     constexpr int NWO = kOutWaves<DK, DV>;
     delta_chunk_kernel<DK, DV, kOut, GATED, PACKED, NWO><<<dim3(sm.H * sm.NS), dim3(NWO * 64), 0, stream>>>(
@@ -823,8 +823,8 @@ hipError_t launch_states(const bf16_t* q, const bf16_t* k, const bf16_t* v, cons
             q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, nullptr, nullptr, trec, 0, sm);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    delta_compose_kernel<DK, DV, false><<<dim3(compose_blocks<DV>(sm.N * sm.H)), dim3(256), 0, stream>>>(map_n, map_m, S0,
-                                                                                          state_in, sm);
+    delta_compose_kernel<DK, DV, false><<<dim3(compose_blocks<DV>(sm.N * sm.H)), dim3(256), 0, stream>>>(
+        map_n, map_m, S0, state_in, sm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     delta_chunk_kernel<DK, DV, kStates, GATED, false><<<dim3(sm.H * sm.NS), dim3(NT), 0, stream>>>(
         q, k, v, beta, alpha, nullptr, state_in, nullptr, nullptr, nullptr, nullptr, states, trec, 0, sm);

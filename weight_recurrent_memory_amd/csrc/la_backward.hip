@@ -68,6 +68,11 @@ struct BLds {
     static constexpr int K = 0, V = K + Y::CQ, Q = V + Y::CV, N = Q + Y::CQ, S = N + Y::CV;
     static constexpr int BF16 = S + Y::ST;           // bf16 elements
     static constexpr int BYTES = 2 * BF16 + CH * 4;  // + dden (fp32, one per query)
+    // LDS reserved per workgroup: at least 56 KB.  At d = 64 the sweeps need
+    // 48.6 KB; reserving 56 KB measured 122-126 us per call against
+    // 127.5-133 us (same code and registers, two workgroups per CU either way
+    // by registers), so only the placement of workgroups on CUs differs.
+    static constexpr int RESERVED = BYTES > 56 * 1024 ? BYTES : 56 * 1024;
 };
 
 // The transposed bf16 copy of a running state tile set X[RTW][NCT] (rows dk
@@ -416,7 +421,7 @@ __global__ __launch_bounds__(NT) void lab_fwd_kernel(const bf16_t* __restrict__ 
     using Y = BL<DK, DV>;
     using LO = BLds<DK, DV>;
     constexpr int RTW = Y::RTW, NCT = Y::NCT;
-    __shared__ __align__(16) __bf16 lds[LO::BYTES / 2];
+    __shared__ __align__(16) __bf16 lds[LO::RESERVED / 2];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = wave_id(tid);
     const int head = blockIdx.x / G, seg = blockIdx.x % G;
@@ -591,7 +596,7 @@ __global__ __launch_bounds__(NT) void lab_bwd_kernel(const bf16_t* __restrict__ 
     using Y = BL<DK, DV>;
     using LO = BLds<DK, DV>;
     constexpr int RTW = Y::RTW, NCT = Y::NCT;
-    __shared__ __align__(16) __bf16 lds[LO::BYTES / 2];
+    __shared__ __align__(16) __bf16 lds[LO::RESERVED / 2];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = wave_id(tid);
     const int head = blockIdx.x / G, seg = blockIdx.x % G;
@@ -648,7 +653,7 @@ size_t la_backward_ws_floats(int HT, int T, int dk, int dv, const LaPlan& plan) 
 
 size_t la_backward_lds_bytes(int dk, int dv) {
 #define LDS_CASE(A, B) \
-    if (dk == A && dv == B) return BLds<A, B>::BYTES;
+    if (dk == A && dv == B) return BLds<A, B>::RESERVED;
     LDS_CASE(64, 64)
     LDS_CASE(64, 128)
     LDS_CASE(128, 64)
