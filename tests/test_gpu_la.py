@@ -60,6 +60,24 @@ def test_la_small_shapes(B, H, T, dk, dv, dtype, init):
     _check(q, k, v, o, S, z, S0, z0)
 
 
+# 32 (sequence, head) pairs with lengths that give segments of 2, 3, 5, 6 and 7
+# chunks (the plan takes chunks x heads / 512 chunks per segment): the
+# aggregate pass takes whole groups of four chunks from the segment end, the
+# first four chunks stay in registers for the output pass, and the last
+# segment of each sequence is shorter still.
+@pytest.mark.parametrize("T,init", [(2500, False), (3500, True), (5100, False), (6500, True), (7900, False)])
+def test_la_segment_lengths(T, init):
+    B, H = 2, 16
+    print(f"la_forward B={B} H={H} T={T} init={init}", flush=True)
+    q, k, v = wl.la_inputs(B, H, T, 64, 64, torch.bfloat16, seed=4000 + T, device=DEV)
+    S0 = z0 = None
+    if init:
+        S0, z0 = wl.decode_state(B, H, 64, 64, seed=78, device=DEV, std=0.5)
+        z0 = z0.abs() + 1.0
+    o, S, z = _run(q, k, v, S0, z0)
+    _check(q, k, v, o, S, z, S0, z0)
+
+
 def test_la_fp32_config_full():
     w = wl.LA_FP32_SMALL
     print(f"la_forward {w.name}", flush=True)
