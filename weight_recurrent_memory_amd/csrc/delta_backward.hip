@@ -345,6 +345,7 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int w = wave_id(tid);
+    __builtin_assume(w >= 0 && w < NT / 64);  // lets per-wave tile guards fold away
     const int NC = (T + CH - 1) / CH;
     const long total = (long)HT * NC;
 

@@ -158,6 +158,7 @@ __global__ __launch_bounds__(NT) void delta_tinv_kernel(const bf16_t* __restrict
     __shared__ float Bs[CH], Gl[CH], Ge[CH], Gc[CH];
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int w = wave_id(tid);
+    __builtin_assume(w >= 0 && w < NT / 64);  // lets per-wave tile guards fold away
     const long rec = blockIdx.x;
     int n, h, c;
     if constexpr (!PACKED) {
@@ -244,6 +245,7 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int w = wave_id(tid);
+    __builtin_assume(w >= 0 && w < NWV);  // lets per-wave tile guards fold away
     // This workgroup's (head, sequence, segment).  MAP skips the last
     // segment of every sequence; its result is the sequence's final state.
     int h, nseq, seg;
@@ -692,6 +694,7 @@ __global__ __launch_bounds__(256) void delta_compose_kernel(const float* __restr
     __shared__ __align__(16) float Ms[DK * LM];
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int w = wave_id(tid);
+    __builtin_assume(w >= 0 && w < 4);  // four waves
     // block b = (p / 8) (8 NCB) + ct 8 + p % 8
     constexpr int NCB = DV / 16;
     const int b = blockIdx.x, xcd = b % kXcds, rest = b / kXcds;
