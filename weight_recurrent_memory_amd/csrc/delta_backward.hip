@@ -103,6 +103,9 @@ __global__ __launch_bounds__(NT) void dlb_chain_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int w = wave_id(tid);
+    // The wave index's range lets per-wave tile guards fold away; the map
+    // variant is left as it is (folded, its code spilled registers).
+    if constexpr (!MAP) __builtin_assume(w >= 0 && w < NT / 64);
     const int G1 = MAP ? sm.G - 1 : sm.G;
     const int vh = blockIdx.x / G1;  // sequence * H + head
     const int seg = blockIdx.x % G1 + (MAP ? 1 : 0);
