@@ -103,15 +103,51 @@ __device__ __forceinline__ void clear_upper(__bf16* X, int tid) {
 // one column per lane); the rest by 2x2 block doubling: the inverse of
 // [[M11, 0], [M21, M22]] is [[M11^-1, 0], [-M22^-1 M21 M11^-1, M22^-1]],
 // first on the 32x32 diagonal blocks, then on the lower-left 32x32 block.
-template <int DK, bool GATED, bool WANT_P, bool KEEP = false, int LQ = DK + 8>
+//
+// K_DEAD: Af may occupy the same LDS as Ks (K is not needed afterwards):
+// every K K^T tile is then computed before the first write of A.
+template <int DK, bool GATED, bool WANT_P, bool KEEP = false, int LQ = DK + 8, bool K_DEAD = false>
 __device__ __forceinline__ void build_T(const __bf16* Ks, const __bf16* Qs, const float* Bs, const float* Gl,
                                         float* Af, float* Ad, float* Yf, __bf16* Ts, __bf16* Ps, int w, int g,
                                         int li, v4f* keep = nullptr) {
     using M = Mma<bf16_t>;
     using MF = Mma<float>;
     constexpr int NTILE = WANT_P ? 20 : 10;
+    if constexpr (K_DEAD) {
+        static_assert(!WANT_P && !KEEP, "K_DEAD builds T alone");
+        v4f kk[2];
 #pragma unroll
-    for (int jj = 0; jj < 3; ++jj) {
+        for (int jj = 0; jj < 2; ++jj) {  // eight or more waves: at most two of the ten tiles each
+            const int id = w + NWV * jj;
+            if (id >= 10) break;
+            int bi, bj;
+            lower_tile(id, bi, bj);
+            kk[jj] = zero4();
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb)
+                M::mma(kk[jj], M::load(&Ks[(16 * bi + li) * LQ + 32 * kb], g), M::load(&Ks[(16 * bj + li) * LQ + 32 * kb], g));
+        }
+        __syncthreads();  // every read of Ks done: its LDS now holds A
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int id = w + NWV * jj;
+            if (id >= 10) break;
+            int bi, bj;
+            lower_tile(id, bi, bj);
+            v4f a;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * bi + 4 * g + r, i = 16 * bj + li;
+                float x = Bs[i] * kk[jj][r];
+                if constexpr (GATED) x *= __expf(Gl[t] - Gl[i]);  // dropped above the diagonal by the select
+                a[r] = (i < t) ? x : 0.f;
+                Af[t * LF + i] = a[r];
+            }
+            if (bi == bj) *reinterpret_cast<v4f*>(&Ad[bi * 256 + li * 16 + 4 * g]) = a;
+        }
+    }
+#pragma unroll
+    for (int jj = 0; jj < (K_DEAD ? 0 : 3); ++jj) {
         const int id = w + NWV * jj;
         if (id >= NTILE) break;
         int bi, bj;

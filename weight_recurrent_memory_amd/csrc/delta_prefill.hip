@@ -149,10 +149,15 @@ __global__ __launch_bounds__(NT) void delta_tinv_kernel(const bf16_t* __restrict
     // K is read only as row fragments here (K K^T tiles): rows padded by 4
     // elements spread a fragment's 16 rows over the banks (staged with
     // 8-byte stores)
+    // K is dead once A = K K^T is formed, so A takes K's LDS (one buffer of
+    // the larger size): 35 KB instead of 52 KB per workgroup, four
+    // workgroups per CU instead of three.
     constexpr int LQ = DK + 4, LT = dchunk::LT, LF = dchunk::LF;
-    __shared__ __align__(16) __bf16 Ks[CH * LQ];
+    constexpr int KA_BYTES = CH * LQ * 2 > CH * LF * 4 ? CH * LQ * 2 : CH * LF * 4;
+    __shared__ __align__(16) unsigned char KAs[KA_BYTES];
+    __bf16* Ks = reinterpret_cast<__bf16*>(KAs);
+    float* Af = reinterpret_cast<float*>(KAs);
     __shared__ __align__(16) __bf16 Ts[CH * LT];
-    __shared__ __align__(16) float Af[CH * LF];
     __shared__ __align__(16) float Ad[4 * 256];
     __shared__ __align__(16) float Yf[4 * 256];
     __shared__ float Bs[CH], Gl[CH], Ge[CH], Gc[CH];
@@ -200,7 +205,7 @@ __global__ __launch_bounds__(NT) void delta_tinv_kernel(const bf16_t* __restrict
     }
     dchunk::clear_upper(Ts, tid);
     __syncthreads();
-    dchunk::build_T<DK, GATED, false, false, LQ>(Ks, nullptr, Bs, Gl, Af, Ad, Yf, Ts, nullptr, w, g, li);
+    dchunk::build_T<DK, GATED, false, false, LQ, true>(Ks, nullptr, Bs, Gl, Af, Ad, Yf, Ts, nullptr, w, g, li);
     // one 16-byte row piece per thread: row tid / 8, columns 8 (tid % 8) ..
     const int row = tid >> 3, col = (tid & 7) * 8;
     *reinterpret_cast<uint4*>(trec + rec * kRecElems + row * CH + col) =
