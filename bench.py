@@ -2,25 +2,35 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-A step is one la_forward call over the bf16 prefill workload B=4, H=8,
-T=8192, d=64 (chunk 64, fp32 state): the whole hot path of that workload.
-The line printed is one JSON object:
+A step is one la_forward call over the long-stream workload B=1, H=32,
+T=65536, d=64 (bf16 inputs, fp32 state, chunk 64, outputs plus the final
+S/z): the whole prefill hot path of the largest configuration.  The line
+printed is one JSON object:
 
-* value / unit: prefill tokens per second (B*T per step) of the timed steps;
-* roofline: HBM roofline of the la_forward call -- algorithmic bytes (inputs
-  read once, outputs and final state written once) over the mean duration
-  measured with HIP events on the launch stream;
+* value / unit: prefill tokens per second (B*T per step) over the wall time
+  of the K timed steps;
+* roofline: HBM roofline of la_fused_kernel (la_forward's one launch) --
+  algorithmic bytes (inputs read once, outputs and final state written once)
+  over the mean per-call duration from HIP event pairs on the launch stream;
+  traffic from rocprofv3 FETCH_SIZE / WRITE_SIZE counters of the same
+  kernel on the same workload, while the sources still match;
 * cpu_baseline: the fp64 oracle (C, OpenMP over heads) timed on the host on
-  the same workload;
-* extra: the other measured paths -- the long-stream LA workload, the LA
-  backward pass on the bench workload, a packed serving batch of mixed
-  request lengths, the delta, gated delta and
-  scalar-decay (SSD) prefills and the 1000-step decode chains of the four
-  rules (state-update GB/s) -- each with its own roofline fraction.
+  every head of the same workload;
+* decode: the other half of the metric -- the 1000-step decode chain (256
+  sequences x 32 heads, d = 128, resident fp32 state) as state-update GB/s,
+  with its own roofline and oracle baseline;
+* extra: the other measured paths -- the bf16 prefill B=4 H=8 T=8192, the LA
+  backward pass, a packed serving batch of mixed request lengths, the delta,
+  gated delta and scalar-decay (SSD) prefills, the delta backward and the
+  decode chains of the other three rules -- each with its own roofline
+  fraction.
 
-Inputs are synthetic (seeded, generated on the device) and rotate among
-several copies so that each step reads data evicted from the 256 MB
-Infinity Cache.  --gpus above 1 is refused: the benchmark runs on one GPU.
+Timing (per call): one HIP event pair around each call on the launch
+stream, after the warm-up calls; the mean and the median of the per-call
+durations are reported.  Inputs are synthetic (seeded, generated on the
+device) and rotate among copies whose total exceeds the 256 MB Infinity
+Cache, so each step reads from HBM.  --gpus above 1 is refused: the
+benchmark runs on one GPU.
 """
 from __future__ import annotations
 
@@ -40,34 +50,45 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFS = 2516.6  # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
 METRIC = "prefill tokens/sec (MFMA % peak); decode state-update GB/s (% HBM peak)"
 
-# HBM traffic of one la_fused_kernel launch on the bf16 prefill workload:
-# rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch, mean of the
-# dispatches of `bench.py --only la --steps 5 --warmup 2 --no-cpu`), each
-# scaled by what the same counter reads for a 1 GiB device copy
-# (`bench.py --calibrate-copy`: FETCH_SIZE 524302 KiB -> x2.0, WRITE_SIZE
-# 1048576 KiB -> x1.0).  Valid only for the kernel sources it was measured
-# on (their SHA-256 below); the roofline reports null traffic otherwise.
-LA_TRAFFIC = {
-    "sources": ["weight_recurrent_memory_amd/csrc/la_prefill.hip",
-                "weight_recurrent_memory_amd/csrc/common.hpp",
-                "weight_recurrent_memory_amd/csrc/kernels.hpp",
-                "weight_recurrent_memory_amd/csrc/segments.hpp"],
-    "sha256": "8a1c05f785bc34ee923c50a50735c4808e955abc50d893e23f3736166ef11e64",
-    "fetch_kib": 70050.5, "fetch_scale": 2.0,
-    "write_kib": 48397.1, "write_scale": 1.0,
+# Counter readings per (kernel, workload): rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE (KiB per dispatch, mean over the dispatches of the command in
+# the profile of the same name under profiles/), each scaled by what the same
+# counter reads for a 1 GiB device copy (`bench.py --calibrate-copy`:
+# FETCH_SIZE 524302 KiB -> x2.0, WRITE_SIZE 1048576 KiB -> x1.0), so that
+# traffic is HBM-side bytes per launch.  A reading is valid only for the
+# kernel sources it was taken on (their SHA-256 below); the roofline reports
+# null traffic otherwise.
+_CSRC = "weight_recurrent_memory_amd/csrc/"
+LA_SOURCES = [_CSRC + f for f in ("la_prefill.hip", "common.hpp", "kernels.hpp", "segments.hpp")]
+LA_DECODE_SOURCES = [_CSRC + f for f in ("la_decode.hip", "common.hpp", "kernels.hpp")]
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+COUNTERS = {
+    # workload name -> kernel, sources, sha256 of the sources, KiB per dispatch
+    "la_bf16_b1_h32_t65536_d64": {"kernel": "la_fused_kernel", "sources": LA_SOURCES, "sha256": None,
+                                  "fetch_kib": None, "write_kib": None},
+    "la_bf16_b4_h8_t8192_d64": {"kernel": "la_fused_kernel", "sources": LA_SOURCES, "sha256": None,
+                                "fetch_kib": None, "write_kib": None},
+    "decode_bf16_n256_h32_d128_1000steps": {"kernel": "la_decode_kernel", "sources": LA_DECODE_SOURCES,
+                                            "sha256": None, "fetch_kib": None, "write_kib": None},
 }
 
 
-def la_traffic_bytes():
+def sources_sha256(sources):
     import hashlib
     h = hashlib.sha256()
-    for f in LA_TRAFFIC["sources"]:
+    for f in sources:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
-    if h.hexdigest() != LA_TRAFFIC["sha256"]:
+    return h.hexdigest()
+
+
+def traffic_bytes(workload):
+    """HBM bytes per launch from the stored counters, or None when none were
+    taken on the current sources."""
+    c = COUNTERS.get(workload)
+    if not c or c["fetch_kib"] is None or c["sha256"] != sources_sha256(c["sources"]):
         return None
-    return 1024 * (LA_TRAFFIC["fetch_kib"] * LA_TRAFFIC["fetch_scale"]
-                   + LA_TRAFFIC["write_kib"] * LA_TRAFFIC["write_scale"])
+    return 1024 * (c["fetch_kib"] * FETCH_SCALE + c["write_kib"] * WRITE_SCALE)
 
 
 def la_bytes(B, H, T, dk, dv, el):
@@ -114,20 +135,16 @@ def ssd_decode_bytes(N, H, dk, dv, el):
     return N * H * (2 * dk * dv * 4 + (2 * dk + dv) * el + 4 + dv * el)
 
 
-def _events(n):
-    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-
-
 def time_calls(fn, n_calls, warmup, stream):
-    """Run fn(i) warmup + n_calls times; returns (wall seconds of the timed
-    calls, mean device time per call in ms).  The device time comes from two
-    HIP events on the launch stream around the whole timed region, so it is
-    the average launch duration including the gaps between launches, and the
-    host's own per-call overhead overlaps the device work."""
+    """Run fn(i) warmup + n_calls times.  Returns (wall seconds of the timed
+    calls, mean and median device time per call in ms).  Each timed call is
+    bracketed by its own pair of HIP events on the launch stream, so a call's
+    duration is its kernels' time on the device (plus the event overhead),
+    not the host's enqueue time, which overlaps the device work."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    start, end = _events(2)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
     # A garbage-collection pause while the calls are being queued would leave
     # the device idle inside the timed region.
     gc_was_on = gc.isenabled()
@@ -135,16 +152,18 @@ def time_calls(fn, n_calls, warmup, stream):
     gc.disable()
     try:
         t0 = time.perf_counter()
-        start.record(stream)
         for i in range(n_calls):
+            ev[i][0].record(stream)
             fn(i)
-        end.record(stream)
+            ev[i][1].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
     finally:
         if gc_was_on:
             gc.enable()
-    return wall, start.elapsed_time(end) / n_calls
+    d = sorted(a.elapsed_time(b) for a, b in ev)
+    med = d[len(d) // 2] if len(d) % 2 else 0.5 * (d[len(d) // 2 - 1] + d[len(d) // 2])
+    return wall, sum(d) / len(d), med
 
 
 def bench_la(w, steps, warmup, copies, lin, wl):
@@ -161,10 +180,10 @@ def bench_la(w, steps, warmup, copies, lin, wl):
         lin.la_forward(q, k, v, eps=1e-6, o=outs[i % copies], S_out=S, z_out=z, workspace=ws)
 
     stream = torch.cuda.current_stream(dev)
-    wall, mean_ms = time_calls(step, steps, warmup, stream)
+    wall, mean_ms, med_ms = time_calls(step, steps, warmup, stream)
     nbytes = la_bytes(w.B, w.H, w.T, w.dk, w.dv, el)
     return {
-        "wall_s": wall, "ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms,
+        "wall_s": wall, "ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms,
         "tokens_per_s": w.B * w.T * steps / wall,
         "bytes": nbytes, "flops": la_flops(w.B, w.H, w.T, w.dk, w.dv),
         "gbs": nbytes / (mean_ms * 1e-3) / 1e9,
@@ -191,10 +210,10 @@ def bench_delta(w, steps, warmup, copies, lin, wl):
             q, k, v, beta = sets[i % copies]
             lin.delta_forward(q, k, v, beta, o=outs[i % copies], S_out=S, workspace=ws)
 
-    wall, mean_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
+    wall, mean_ms, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
     nbytes = delta_bytes(w.B, w.H, w.T, w.dk, w.dv, el, gated)
     fl = delta_flops(w.B, w.H, w.T, w.dk, w.dv)
-    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "tokens_per_s": w.B * w.T * steps / wall,
+    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "tokens_per_s": w.B * w.T * steps / wall,
             "bytes": nbytes, "flops": fl, "gbs": nbytes / (mean_ms * 1e-3) / 1e9,
             "tflops": fl / (mean_ms * 1e-3) / 1e12}
 
@@ -212,10 +231,10 @@ def bench_ssd(w, steps, warmup, copies, lin, wl):
         q, k, v, alpha = sets[i % copies]
         lin.ssd_forward(q, k, v, alpha, o=outs[i % copies], S_out=S, workspace=ws)
 
-    wall, mean_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
+    wall, mean_ms, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
     nbytes = ssd_bytes(w.B, w.H, w.T, w.dk, w.dv, el)
     fl = ssd_flops(w.B, w.H, w.T, w.dk, w.dv)
-    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "tokens_per_s": w.B * w.T * steps / wall,
+    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "tokens_per_s": w.B * w.T * steps / wall,
             "bytes": nbytes, "flops": fl, "gbs": nbytes / (mean_ms * 1e-3) / 1e9,
             "tflops": fl / (mean_ms * 1e-3) / 1e12}
 
@@ -230,9 +249,9 @@ def bench_ssd_decode(w, lin, wl, n_steps=None):
         j = i % w.T
         lin.ssd_decode_step(Q[j], K[j], V[j], At[j], S, o=o)
 
-    wall, mean_ms = time_calls(step, n, 10, torch.cuda.current_stream(dev))
+    wall, mean_ms, med_ms = time_calls(step, n, 10, torch.cuda.current_stream(dev))
     per = ssd_decode_bytes(w.B, w.H, w.dk, w.dv, 2)
-    return {"steps": n, "ms_per_step": 1e3 * wall / n, "event_ms_mean": mean_ms, "bytes_per_step": per,
+    return {"steps": n, "ms_per_step": 1e3 * wall / n, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "bytes_per_step": per,
             "gbs_wall": per * n / wall / 1e9, "gbs": per / (mean_ms * 1e-3) / 1e9}
 
 
@@ -254,9 +273,9 @@ def bench_la_backward(w, steps, warmup, copies, lin, wl):
         dq, dk, dv = grads[i % copies]
         lin.la_backward(q, k, v, dO, eps=1e-6, dq=dq, dk=dk, dv=dv, return_state_grads=False, workspace=ws)
 
-    wall, mean_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
+    wall, mean_ms, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
     nbytes = la_backward_bytes(w.B, w.H, w.T, w.dk, w.dv, 2)
-    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "tokens_per_s": w.B * w.T * steps / wall,
+    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "tokens_per_s": w.B * w.T * steps / wall,
             "bytes": nbytes, "gbs": nbytes / (mean_ms * 1e-3) / 1e9}
 
 
@@ -285,9 +304,9 @@ def bench_delta_backward(w, steps, warmup, copies, lin, wl):
         dq, dk, dv = grads[i % copies]
         lin.delta_backward(q, k, v, beta, dO, alpha, dq=dq, dk=dk, dv=dv, return_state_grad=False, workspace=ws)
 
-    wall, mean_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
+    wall, mean_ms, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
     nbytes = delta_backward_bytes(w.B, w.H, w.T, w.dk, w.dv, 2, gated)
-    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "tokens_per_s": w.B * w.T * steps / wall,
+    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "tokens_per_s": w.B * w.T * steps / wall,
             "bytes": nbytes, "gbs": nbytes / (mean_ms * 1e-3) / 1e9}
 
 
@@ -304,10 +323,10 @@ def bench_la_packed(w, steps, warmup, lin, wl):
     def step(i):
         lin.la_forward_packed(q, k, v, cu_dev, eps=1e-6, cu_seqlens_host=cu, o=o, S_out=S, z_out=z, workspace=ws)
 
-    wall, mean_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
+    wall, mean_ms, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
     nbytes = la_bytes(1, w.H, w.T, w.dk, w.dv, 2) + (w.B - 1) * w.H * (w.dk * w.dv + w.dk) * 4
     lengths = (cu[1:] - cu[:-1]).tolist()
-    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "tokens_per_s": w.T * steps / wall,
+    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "tokens_per_s": w.T * steps / wall,
             "gbs": nbytes / (mean_ms * 1e-3) / 1e9, "requests": w.B, "min_len": min(lengths),
             "max_len": max(lengths)}
 
@@ -321,9 +340,9 @@ def bench_decode(w, lin, wl, n_steps=None):
     def step(i):
         lin.la_decode_step(Q[i % w.T], K[i % w.T], V[i % w.T], S, z, eps=1e-6, o=o)
 
-    wall, mean_ms = time_calls(step, n, 10, torch.cuda.current_stream(dev))
+    wall, mean_ms, med_ms = time_calls(step, n, 10, torch.cuda.current_stream(dev))
     per = decode_bytes(w.B, w.H, w.dk, w.dv, 2)
-    return {"steps": n, "ms_per_step": 1e3 * wall / n, "event_ms_mean": mean_ms, "bytes_per_step": per,
+    return {"steps": n, "ms_per_step": 1e3 * wall / n, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "bytes_per_step": per,
             "gbs_wall": per * n / wall / 1e9, "gbs": per / (mean_ms * 1e-3) / 1e9}
 
 
@@ -345,32 +364,58 @@ def bench_delta_decode(w, lin, wl, n_steps=None):
         else:
             lin.delta_decode_step(Q[j], K[j], V[j], Bt[j], S, o=o)
 
-    wall, mean_ms = time_calls(step, n, 10, torch.cuda.current_stream(dev))
+    wall, mean_ms, med_ms = time_calls(step, n, 10, torch.cuda.current_stream(dev))
     per = delta_decode_bytes(w.B, w.H, w.dk, w.dv, 2, gated)
-    return {"steps": n, "ms_per_step": 1e3 * wall / n, "event_ms_mean": mean_ms, "bytes_per_step": per,
+    return {"steps": n, "ms_per_step": 1e3 * wall / n, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "bytes_per_step": per,
             "gbs_wall": per * n / wall / 1e9, "gbs": per / (mean_ms * 1e-3) / 1e9}
 
 
-def cpu_baseline(w, oracle, wl, heads=None):
-    """The fp64 oracle on the host, same workload recipe (generated on the CPU)."""
-    q, k, v = wl.la_inputs(w.B, w.H, w.T, w.dk, w.dv, w.dtype, w.seed, "cpu")
-    BH = w.B * w.H
-    heads = BH if heads is None else heads
-    flat = lambda t: t.reshape(BH, *t.shape[2:])[:heads][None]
-    qs, ks, vs = (oracle._f64(flat(t)) for t in (q, k, v))
-    # Whole passes until about a second has run (at most 30 passes), so that
-    # a fast pass is not timed once on its own.
+def _timed_passes(run, min_seconds, max_passes):
+    """Whole passes of run() until min_seconds of wall time (at least one)."""
     passes, total = 0, 0.0
-    while passes < 30 and (passes == 0 or total < 1.0):
+    while passes < max_passes and (passes == 0 or total < min_seconds):
         t0 = time.perf_counter()
-        oracle.la_forward(qs, ks, vs, eps=1e-6)
+        run()
         total += time.perf_counter() - t0
         passes += 1
+    return passes, total
+
+
+def cpu_baseline(w, oracle, wl, min_seconds=5.0):
+    """The fp64 oracle on the host over every head of the prefill workload
+    (inputs from the same recipe, generated on the CPU), repeated in whole
+    passes until about min_seconds have run."""
+    q, k, v = wl.la_inputs(w.B, w.H, w.T, w.dk, w.dv, w.dtype, w.seed, "cpu")
+    qs, ks, vs = (oracle._f64(t) for t in (q, k, v))
+    del q, k, v
+    passes, total = _timed_passes(lambda: oracle.la_forward(qs, ks, vs, eps=1e-6), min_seconds, 30)
     dt = total / passes
-    tokens = w.T * heads / w.H  # token rate scaled to the metric's B*T per step
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{heads} of {BH} heads x T={w.T} (all heads = the whole workload), {passes} passes; "
+    return {"value": w.B * w.T / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"the whole workload (all {w.B * w.H} heads x T={w.T}), {passes} passes; "
                       f"{total:.2f} s wall in total, {dt:.3f} s per pass", "seconds": dt}
+
+
+def cpu_baseline_decode(w, oracle, wl, min_seconds=5.0):
+    """The fp64 oracle's decode step on the host over every state of the
+    decode workload, step after step, until about min_seconds have run;
+    reported as steps/s and as the equivalent state-update GB/s."""
+    S, z = wl.decode_state(w.B, w.H, w.dk, w.dv, w.seed, "cpu")
+    nt = 8
+    Q, K, V = wl.decode_tokens(nt, w.B, w.H, w.dk, w.dv, w.dtype, w.seed, "cpu")
+    st = {"S": oracle._f64(S), "z": oracle._f64(z), "i": 0}
+    toks = [tuple(oracle._f64(x[j]) for x in (Q, K, V)) for j in range(nt)]
+
+    def one():
+        q, k, v = toks[st["i"] % nt]
+        _, st["S"], st["z"] = oracle.la_decode_step(q, k, v, st["S"], st["z"], eps=1e-6)
+        st["i"] += 1
+
+    steps, total = _timed_passes(one, min_seconds, 200)
+    per = decode_bytes(w.B, w.H, w.dk, w.dv, 2)
+    return {"value": per * steps / total / 1e9, "unit": "GB/s", "steps_per_s": steps / total,
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"all {w.B * w.H} states, {steps} consecutive steps (of the chain's {w.T}); "
+                      f"{total:.2f} s wall in total", "seconds_per_step": total / steps}
 
 
 def calibrate_copy(nbytes=1 << 30):
@@ -384,17 +429,28 @@ def calibrate_copy(nbytes=1 << 30):
     print(json.dumps({"calibration_copy_bytes": nbytes, "launches": 3}))
 
 
+def hbm_roofline(nbytes, r, workload, kernel):
+    """The HBM roofline object of one launch: algorithmic bytes over the mean
+    per-call duration, and the counter traffic when taken on these sources."""
+    gbs = nbytes / (r["event_ms_mean"] * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+            "traffic": traffic_bytes(workload),
+            "traffic_unit": "HBM bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
+            "kernel": kernel, "algorithmic_bytes_per_launch": nbytes,
+            "event_ms_mean": r["event_ms_mean"], "event_ms_median": r["event_ms_median"],
+            "frac_at_median": nbytes / (r["event_ms_median"] * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--copies", type=int, default=4, help="input copies rotated through (cache eviction)")
     ap.add_argument("--only", choices=["all", "la", "la_long", "la_packed", "la_backward", "delta", "gated_delta",
                                        "delta_backward", "ssd", "decode", "delta_decode", "gated_delta_decode",
                                        "ssd_decode"],
                     default="all")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baselines")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
 
@@ -413,21 +469,26 @@ def main():
     from weight_recurrent_memory_amd import workloads as wl
 
     lin.lib()  # fail loudly if the HIP library is missing
-    w = wl.LA_BF16_PREFILL
-    main_res = None
+    head = wl.LA_BF16_LONG
+    main_res = dec_res = None
     extra = {}
-    if args.only in ("all", "la"):
-        main_res = bench_la(w, args.steps, args.warmup, args.copies, lin, wl)
     if args.only in ("all", "la_long"):
-        wl_ = wl.LA_BF16_LONG
-        r = bench_la(wl_, max(3, args.steps // 10), 2, 2, lin, wl)
-        extra[wl_.name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
-                           "hbm_gbs": r["gbs"], "hbm_frac": r["gbs"] / HBM_PEAK_GBS,
-                           "mfma_tflops": r["tflops"], "mfma_frac": r["tflops"] / BF16_MFMA_PEAK_TFS}
+        # two rotating copies of the inputs (1.6 GB) keep every step's reads out of the Infinity Cache
+        main_res = bench_la(head, args.steps, args.warmup, 2, lin, wl)
+    if args.only in ("all", "decode"):
+        dec_res = bench_decode(wl.DECODE_BF16, lin, wl)
+    if args.only in ("all", "la"):
+        w = wl.LA_BF16_PREFILL
+        r = bench_la(w, max(20, args.steps), args.warmup, 4, lin, wl)
+        extra[w.name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
+                         "roofline": hbm_roofline(r["bytes"], r, w.name, "la_fused_kernel<bf16, 64, 64>"),
+                         "mfma_tflops": r["tflops"], "mfma_frac": r["tflops"] / BF16_MFMA_PEAK_TFS}
     if args.only in ("all", "la_backward"):
-        r = bench_la_backward(w, max(3, args.steps // 2), 3, args.copies, lin, wl)
+        w = wl.LA_BF16_PREFILL
+        r = bench_la_backward(w, max(3, args.steps // 2), 3, 4, lin, wl)
         extra["la_backward_" + w.name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
-                                          "us_per_call": 1e3 * r["event_ms_mean"], "hbm_gbs": r["gbs"],
+                                          "us_per_call": 1e3 * r["event_ms_mean"],
+                                          "us_per_call_median": 1e3 * r["event_ms_median"], "hbm_gbs": r["gbs"],
                                           "hbm_frac": r["gbs"] / HBM_PEAK_GBS, "bytes_per_call": r["bytes"]}
     if args.only in ("all", "la_packed"):
         wp = wl.PACKED_LA_BF16
@@ -438,57 +499,62 @@ def main():
     for key, wd in (("delta", wl.DELTA_BF16_PREFILL), ("gated_delta", wl.GATED_DELTA_BF16_PREFILL)):
         if args.only not in ("all", key):
             continue
-        try:
-            r = bench_delta(wd, max(5, args.steps // 2), 5, 2, lin, wl)
-            extra[wd.name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
-                              "hbm_gbs": r["gbs"], "hbm_frac": r["gbs"] / HBM_PEAK_GBS,
-                              "mfma_tflops": r["tflops"], "mfma_frac": r["tflops"] / BF16_MFMA_PEAK_TFS}
-        except lin.LinAttnError as e:
-            extra[wd.name] = {"error": str(e)}
+        r = bench_delta(wd, max(5, args.steps // 2), 5, 2, lin, wl)
+        extra[wd.name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
+                          "us_per_call": 1e3 * r["event_ms_mean"], "us_per_call_median": 1e3 * r["event_ms_median"],
+                          "hbm_gbs": r["gbs"], "hbm_frac": r["gbs"] / HBM_PEAK_GBS,
+                          "mfma_tflops": r["tflops"], "mfma_frac": r["tflops"] / BF16_MFMA_PEAK_TFS}
     if args.only in ("all", "delta_backward"):
         for wd in (wl.DELTA_BF16_PREFILL, wl.GATED_DELTA_BF16_PREFILL):
             r = bench_delta_backward(wd, max(5, args.steps // 5), 3, 2, lin, wl)
             extra["delta_backward_" + wd.name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
-                                                  "us_per_call": 1e3 * r["event_ms_mean"], "hbm_gbs": r["gbs"],
+                                                  "us_per_call": 1e3 * r["event_ms_mean"],
+                                                  "us_per_call_median": 1e3 * r["event_ms_median"],
+                                                  "hbm_gbs": r["gbs"],
                                                   "hbm_frac": r["gbs"] / HBM_PEAK_GBS, "bytes_per_call": r["bytes"]}
     if args.only in ("all", "ssd"):
         ws_ = wl.SSD_BF16_PREFILL
-        r = bench_ssd(ws_, max(3, args.steps // 2), 3, args.copies, lin, wl)
+        r = bench_ssd(ws_, max(3, args.steps // 2), 3, 4, lin, wl)
         extra[ws_.name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
-                           "hbm_gbs": r["gbs"], "hbm_frac": r["gbs"] / HBM_PEAK_GBS,
+                           "us_per_call": 1e3 * r["event_ms_mean"], "hbm_gbs": r["gbs"],
+                           "hbm_frac": r["gbs"] / HBM_PEAK_GBS,
                            "mfma_tflops": r["tflops"], "mfma_frac": r["tflops"] / BF16_MFMA_PEAK_TFS}
-    if args.only in ("all", "decode"):
-        wdec = wl.DECODE_BF16
-        r = bench_decode(wdec, lin, wl)
-        extra[wdec.name] = {"state_update_gbs": r["gbs"], "hbm_frac": r["gbs"] / HBM_PEAK_GBS,
-                            "gbs_wall_incl_launch_gaps": r["gbs_wall"], "us_per_step": 1e3 * r["event_ms_mean"],
-                            "steps": r["steps"], "bytes_per_step": r["bytes_per_step"]}
-
     for key, wdd in (("delta_decode", wl.DELTA_DECODE_BF16), ("gated_delta_decode", wl.GATED_DELTA_DECODE_BF16)):
         if args.only not in ("all", key):
             continue
         r = bench_delta_decode(wdd, lin, wl)
         extra[wdd.name] = {"state_update_gbs": r["gbs"], "hbm_frac": r["gbs"] / HBM_PEAK_GBS,
                            "gbs_wall_incl_launch_gaps": r["gbs_wall"], "us_per_step": 1e3 * r["event_ms_mean"],
+                           "us_per_step_median": 1e3 * r["event_ms_median"],
                            "steps": r["steps"], "bytes_per_step": r["bytes_per_step"]}
     if args.only in ("all", "ssd_decode"):
         wsd = wl.SSD_DECODE_BF16
         r = bench_ssd_decode(wsd, lin, wl)
         extra[wsd.name] = {"state_update_gbs": r["gbs"], "hbm_frac": r["gbs"] / HBM_PEAK_GBS,
                            "gbs_wall_incl_launch_gaps": r["gbs_wall"], "us_per_step": 1e3 * r["event_ms_mean"],
+                           "us_per_step_median": 1e3 * r["event_ms_median"],
                            "steps": r["steps"], "bytes_per_step": r["bytes_per_step"]}
 
+    decode = None
+    if dec_res is not None:
+        wd = wl.DECODE_BF16
+        decode = {"metric": "decode state-update GB/s", "value": dec_res["gbs_wall"], "unit": "GB/s",
+                  "workload": wd.name, "steps": dec_res["steps"], "us_per_step": 1e3 * dec_res["ms_per_step"],
+                  "roofline": hbm_roofline(dec_res["bytes_per_step"], dec_res, wd.name,
+                                           "la_decode_kernel<bf16, 128, 128> (the one launch of la_decode_step)"),
+                  "cpu_baseline": None}
+        if not args.no_cpu:
+            import oracle  # test infrastructure, used only for the CPU baseline legs
+            decode["cpu_baseline"] = cpu_baseline_decode(wd, oracle, wl)
     if main_res is None:
-        print(json.dumps({"extra": extra}))
+        print(json.dumps({"decode": decode, "extra": extra}))
         return
 
     cpu = None
     if not args.no_cpu:
-        import oracle  # test infrastructure, used only for this CPU baseline leg
-        cpu = cpu_baseline(w, oracle, wl)
+        import oracle  # test infrastructure, used only for the CPU baseline legs
+        cpu = cpu_baseline(head, oracle, wl)
 
-    gbs = main_res["gbs"]
-    traffic = la_traffic_bytes()
     line = {
         "metric": METRIC,
         "value": main_res["tokens_per_s"],
@@ -501,17 +567,14 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) q,k,v; generated on device; %d rotating copies)" % args.copies,
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv, "chunk": 64,
-                   "state": "fp32"},
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "traffic_unit": "bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
-                     "kernel": "la_fused_kernel<bf16, 64, 64> (the one launch of la_forward)",
-                     "algorithmic_bytes_per_launch": main_res["bytes"],
-                     "event_ms_mean": main_res["event_ms_mean"],
-                     "mfma_tflops": main_res["tflops"], "mfma_frac": main_res["tflops"] / BF16_MFMA_PEAK_TFS},
+        "data": "synthetic (seeded N(0,1) q,k,v; generated on device; 2 rotating copies)",
+        "config": {"workload": head.name, "B": head.B, "H": head.H, "T": head.T, "dk": head.dk, "dv": head.dv,
+                   "chunk": 64, "state": "fp32"},
+        "roofline": dict(hbm_roofline(main_res["bytes"], main_res, head.name,
+                                      "la_fused_kernel<bf16, 64, 64> (the one launch of la_forward)"),
+                         mfma_tflops=main_res["tflops"], mfma_frac=main_res["tflops"] / BF16_MFMA_PEAK_TFS),
         "cpu_baseline": cpu,
+        "decode": decode,
         "extra": extra,
     }
     print(json.dumps(line))

@@ -81,8 +81,9 @@ typedef enum {
 
 /*
  * Bytes of device workspace la_forward needs for these sizes; 0 if the
- * sizes are invalid.  The workspace holds 64-bit look-back flags and two fp32
- * (S, z) per head and segment of the sequence.  Its contents need no
+ * sizes are invalid.  The workspace holds 64-bit look-back flags, two fp32
+ * (S, z) per head and segment of the sequence, and room for one copy of the
+ * initial state (taken when S_out, z_out alias S0, z0).  Its contents need no
  * initialisation: each flag carries the tag of the call that wrote it, and a
  * call recorded into a HIP graph (replayed with one tag) clears the flags in
  * a launch of its own first.
@@ -110,6 +111,25 @@ la_status la_forward(const void* q, const void* k, const void* v,
                      void* o, float* S_out, float* z_out,
                      int B, int H, int T, int dk, int dv, int dtype, float eps, int chunk,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * TEST HOOK: la_forward with the look-back's wait bound chosen by the caller.
+ * la_forward cuts each sequence into segments, one workgroup each; a
+ * workgroup finds the state entering its segment by polling its
+ * predecessors' published sums ([Recurrence] "Chunked scan": only the state
+ * crosses a boundary), at most `lookback_polls` times per window of
+ * predecessors (la_forward uses 4000), and otherwise recomputes that state
+ * from the inputs with the same additions in the same order, so the result
+ * is the same bit for bit.  lookback_polls < 0 skips the polling: every
+ * segment but the first of its sequence recomputes.  Meant for tests of that
+ * path; the recomputation costs O(segments^2) per sequence.  Arguments,
+ * workspace and errors are those of la_forward.
+ */
+la_status la_forward_lookback_polls(const void* q, const void* k, const void* v,
+                                    const float* S0, const float* z0,
+                                    void* o, float* S_out, float* z_out,
+                                    int B, int H, int T, int dk, int dv, int dtype, float eps, int chunk,
+                                    void* workspace, size_t workspace_bytes, void* stream, int lookback_polls);
 
 /*
  * Bytes of device workspace delta_forward (and gated_delta_forward,

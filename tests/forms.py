@@ -4,10 +4,11 @@ None of these is the oracle's sequential token loop; each reaches the same
 function by a different route, so a dropped term, a swapped order or a
 transposed operand in the oracle shows up as a mismatch.
 
-* ``la_quadratic`` -- the explicit causal form: the full T x T kernel matrix
-  phi(Q) phi(K)^T masked to i <= t, numerator and denominator summed over
-  the history ("AIGC 基本功｜线性、循环与记忆架构-LinearMem", §03, the
-  ratio-of-sums definition of o_t; §04 describes the same explicit check).
+* ``la_quadratic`` -- the ratio-of-sums definition of o_t taken term by
+  term ("AIGC 基本功｜线性、循环与记忆架构-LinearMem", §03): for every query
+  t, a loop over the history i <= t adds w_ti v_i to the numerator and w_ti
+  to the denominator, w_ti = phi(q_t) . phi(k_i), then divides.  No matrix of
+  all pairs is formed and no mask is applied.
 * ``delta_dense`` -- the delta rule solved in one shot.  Unrolling
   S_{t-1} = S_0 + sum_{i<t} beta_i k_i u_i^T in u_t = v_t - S_{t-1}^T k_t gives
   the unit lower-triangular system (I + A) U = V - K S_0 with
@@ -23,22 +24,30 @@ import numpy as np
 
 
 def phi(x):
+    """ELU+1 written as ELU(x) + 1, with ELU(x) = x (x > 0), e^x - 1 (x <= 0)
+    through expm1: the same function as the oracle's exp form, another
+    rounding path (they differ by at most an ulp near 0-)."""
     x = np.asarray(x, dtype=np.float64)
-    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+    return np.where(x > 0, x, np.expm1(np.minimum(x, 0.0))) + 1.0
 
 
 def la_quadratic(q, k, v, S0=None, z0=None, eps=1e-6):
-    """Single head: q, k [T, dk]; v [T, dv]."""
-    fq, fk = phi(q), phi(k)
-    T = q.shape[0]
-    w = (fq @ fk.T) * np.tril(np.ones((T, T)))
-    num = w @ v
-    den = w.sum(axis=1) + eps
-    if S0 is not None:
-        num = num + fq @ S0
-    if z0 is not None:
-        den = den + fq @ z0
-    return num / den[:, None]
+    """Single head: q, k [T, dk]; v [T, dv].  For each t,
+    o_t = (phi(q_t)^T S0 + sum_{i<=t} w_ti v_i) / (phi(q_t)^T z0 + sum_{i<=t} w_ti + eps)
+    with w_ti = phi(q_t) . phi(k_i), accumulated one history term at a time."""
+    T, dv = q.shape[0], v.shape[1]
+    fk = [phi(k[i]) for i in range(T)]
+    out = np.empty((T, dv))
+    for t in range(T):
+        fq = phi(q[t])
+        num = np.zeros(dv) if S0 is None else fq @ S0
+        den = eps if z0 is None else eps + float(fq @ z0)
+        for i in range(t + 1):
+            w = float(np.dot(fq, fk[i]))
+            num = num + w * v[i]
+            den += w
+        out[t] = num / den
+    return out
 
 
 def delta_dense(q, k, v, beta, S0=None):

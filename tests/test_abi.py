@@ -311,6 +311,30 @@ def test_delta_backward_rejects(kw, status):
     assert lin.lib().la_last_error().decode().startswith("delta_backward")
 
 
+@pytest.mark.parametrize("dk,dv,dtype", [(128, 128, 1), (64, 64, 1), (64, 128, 0)])
+def test_rows_beyond_32_bit_offsets_are_unsupported(dk, dv, dtype):
+    # one (sequence, head)'s rows, plus four chunks of read-ahead, must span
+    # < 2 GiB: the kernels address them with 32-bit buffer offsets
+    el = 2 if dtype == 1 else 4
+    t_max = (1 << 31) // (max(dk, dv) * el) - 4 * 64 - 1  # the longest accepted T
+    assert _la(T=t_max + 1, dk=dk, dv=dv, dtype=dtype) == ST["UNSUPPORTED"]
+    assert "too long" in lin.lib().la_last_error().decode()
+    assert _la(T=t_max, dk=dk, dv=dv, dtype=dtype, wsb=16) == ST["WORKSPACE"]  # passes the size check
+    if dtype == 1:
+        assert _delta(T=t_max + 1, dk=dk, dv=dv) == ST["UNSUPPORTED"]
+        assert _delta(T=t_max, dk=dk, dv=dv, wsb=16) == ST["WORKSPACE"]
+    assert lin.lib().la_forward_workspace_bytes(1, 1, t_max + 1, dk, dv, 64) == 0 or dtype == 0
+
+
+def test_lookback_test_hook_validates_like_la_forward():
+    L = lin.lib()
+    args = [P, P, P, None, None, P, None, None, 1, 1, 8, 64, 64, 1, 1e-6, 64, P, 16, None]
+    assert L.la_forward_lookback_polls(*args, -1) == ST["WORKSPACE"]
+    args[10] = 0
+    assert L.la_forward_lookback_polls(*args, 5) == ST["INVALID_ARG"]
+    assert lin.lib().la_last_error().decode().startswith("la_forward_lookback_polls")
+
+
 def test_workspace_queries():
     L = lin.lib()
     assert L.la_forward_workspace_bytes(0, 1, 8, 64, 64, 64) == 0

@@ -16,8 +16,11 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 def test_traffic_is_reported_only_for_the_measured_sources(monkeypatch):
     import bench
-    ok = bench.la_traffic_bytes()
-    assert ok is None or ok > bench.la_bytes(4, 8, 8192, 64, 64, 2) * 0.9
-    # a source other than the measured one reads as unmeasured
-    monkeypatch.setitem(bench.LA_TRAFFIC, "sha256", "0" * 64)
-    assert bench.la_traffic_bytes() is None
+    for name, c in bench.COUNTERS.items():
+        t = bench.traffic_bytes(name)
+        assert t is None or t > 0
+        if c["fetch_kib"] is not None:
+            # another source than the measured one reads as unmeasured
+            monkeypatch.setitem(c, "sha256", "0" * 64)
+            assert bench.traffic_bytes(name) is None
+    assert bench.traffic_bytes("no such workload") is None

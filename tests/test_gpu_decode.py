@@ -24,7 +24,7 @@ def test_decode_step_shapes(N, H, dk, dv, dtype):
     torch.cuda.synchronize()
     ro, rS, rz = oracle.la_decode_step(q, k, v, S_ref, z_ref, eps=EPS)
     tol = TOL[dtype]
-    assert_parity(o, ro, tol, "o")
+    assert_parity(o, ro, tol, "o", rows=True)
     assert_parity(S, rS, 1e-6, "S")   # fp32 state: one fma per element
     assert_parity(z, rz, 1e-6, "z")
 
@@ -51,7 +51,7 @@ def test_decode_config_chain_sampled_states():
     worst = 0.0
     for t in range(w.T):
         ro, S_ref, z_ref = oracle.la_decode_step(qs[t][None], ks[t][None], vs[t][None], S_ref, z_ref, eps=EPS)
-        worst = max(worst, assert_parity(outs[t][None], ro, tol, f"o step {t}", axes=(2,)))
+        worst = max(worst, assert_parity(outs[t][None], ro, tol, f"o step {t}", axes=(2,), rows=True))
     assert_parity(S[n_idx, h_idx][None], S_ref, tol, "S final")
     assert_parity(z[n_idx, h_idx][None], z_ref, tol, "z final")
     print(f"worst per-step slice error of o: {worst:.2e}")
@@ -68,6 +68,6 @@ def test_decode_chain_equals_prefill():
     o, Sf, zf = lin.la_forward(seq(Q), seq(K), seq(V), S0, z0, eps=EPS)
     torch.cuda.synchronize()
     tol = TOL[torch.float32]
-    assert_parity(outs, to64(o), tol, "o")
+    assert_parity(outs, to64(o), tol, "o", rows=True)
     assert_parity(S, to64(Sf), tol, "S")
     assert_parity(z, to64(zf), tol, "z")

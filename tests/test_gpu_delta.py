@@ -26,7 +26,7 @@ def _check(q, k, v, beta, o, S, S0=None, heads=None):
     idx = list(range(B * H)) if heads is None else list(heads)
     sel = lambda t: None if t is None else t[idx][None]
     ro, rS = oracle.delta_forward(sel(qf), sel(kf), sel(vf), sel(bf), sel(S0f))
-    e1 = assert_parity(sel(of), ro, tol, "o")
+    e1 = assert_parity(sel(of), ro, tol, "o", rows=True)
     e2 = assert_parity(sel(Sf), rS, tol, "S_T")
     print(f"worst slice errors: o {e1:.2e}  S {e2:.2e}")
 
@@ -59,12 +59,12 @@ def test_delta_small_shapes(B, H, T, dk, dv, init):
     _check(q, k, v, beta, o, S, S0)
 
 
-def test_delta_config_sampled_heads():
+def test_delta_config_all_heads():
     w = wl.DELTA_BF16_PREFILL
     print(f"delta_forward {w.name}", flush=True)
     q, k, v, beta = wl.make(w, DEV)
     o, S = _run(q, k, v, beta)
-    _check(q, k, v, beta, o, S, heads=(0, 15, 31))
+    _check(q, k, v, beta, o, S)
 
 
 def test_delta_exact_overwrite_basis_keys():
@@ -106,7 +106,7 @@ def test_delta_deterministic_and_resume():
     ob, Sb = _run(cut(q, slice(T1, None)), cut(k, slice(T1, None)), cut(v, slice(T1, None)),
                   cut(beta, slice(T1, None)), Sa)
     tol = TOL[torch.bfloat16]
-    assert_parity(torch.cat([oa, ob], 2), to64(a[0]), tol, "o")
+    assert_parity(torch.cat([oa, ob], 2), to64(a[0]), tol, "o", rows=True)
     assert_parity(Sb, to64(a[1]), tol, "S")
 
 

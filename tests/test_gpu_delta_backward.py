@@ -24,7 +24,15 @@ def _inputs(B, H, T, dk, dv, seed, init, gated, rate=wl.GATE_RATE):
     return q, k, v, beta, dO, alpha, S0, dS_T
 
 
-def _check(args, res, heads=None):
+# Row check of dq, dk, dv: each token's row against its own norm, floored at a
+# quarter of the median row norm of its (batch, head).  Rows far below the
+# median are single inner products that bf16 operands cannot resolve to 2 %
+# of their own size -- the last token's dk, for one, has only its own output
+# to come from (no dS_T), at about a hundredth of the median row.
+ROW_FLOOR = 1 / 4
+
+
+def _check(args, res, heads=None, row_floor=ROW_FLOOR):
     q, k, v, beta, dO, alpha, S0, dS_T = args
     B, H = q.shape[:2]
     flat = lambda t: None if t is None else t.reshape(B * H, *t.shape[2:])
@@ -38,7 +46,8 @@ def _check(args, res, heads=None):
             assert x is None, name
             continue
         axes = (2,) if x.dim() == 3 else None  # dbeta, dalpha: one slice per (batch, head)
-        worst[name] = assert_parity(sel(x), r, tol, name, axes=axes)
+        worst[name] = assert_parity(sel(x), r, tol, name, axes=axes, rows=name in ("dq", "dk", "dv"),
+                                    row_floor=row_floor)
     print("worst slice errors:", {n: f"{e:.2e}" for n, e in worst.items()})
 
 
@@ -70,22 +79,27 @@ def test_delta_backward_shapes(B, H, T, dk, dv, init, gated):
 
 def test_delta_backward_strong_gates():
     # Gates well below one (rate 1: alpha down to about e^-5 per token), so
-    # chunk-local products span many orders of magnitude.
+    # chunk-local products span many orders of magnitude.  The state then
+    # holds little more than the last write, beta k u^T, and dq_t = S_t dO_t
+    # nearly cancels on tokens where u_t . dO_t is small: rounding S to the
+    # bf16 MFMA operand alone (all else exact, fp64) gives those rows errors
+    # of 3-4 % of their own norm, at about a tenth of the median row norm.
+    # Here the row check's floor is half the median row norm.
     print("delta_backward strong gates", flush=True)
     args = _inputs(1, 2, 600, 128, 128, seed=71, init=True, gated=True, rate=1.0)
     res = lin.delta_backward(*args[:5], alpha=args[5], S0=args[6], dS_T=args[7])
     torch.cuda.synchronize()
-    _check(args, res)
+    _check(args, res, row_floor=1 / 2)
 
 
 @pytest.mark.parametrize("gated", [False, True])
-def test_delta_backward_config_sampled_heads(gated):
+def test_delta_backward_config_all_heads(gated):
     w = wl.DELTA_BF16_PREFILL
     print(f"delta_backward {w.name} gated={gated}", flush=True)
     args = _inputs(w.B, w.H, w.T, w.dk, w.dv, seed=72, init=False, gated=gated)
     res = lin.delta_backward(*args[:5], alpha=args[5])
     torch.cuda.synchronize()
-    _check(args, res, heads=(0, 31))
+    _check(args, res)
 
 
 def test_delta_backward_deterministic():

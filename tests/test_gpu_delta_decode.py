@@ -23,7 +23,7 @@ def test_delta_decode_step_shapes(N, H, dk, dv, dtype):
     o = lin.delta_decode_step(q, k, v, beta, S)
     torch.cuda.synchronize()
     ro, rS = oracle.delta_decode_step(q, k, v, beta, S_ref)
-    assert_parity(o, ro, TOL[dtype], "o")
+    assert_parity(o, ro, TOL[dtype], "o", rows=True)
     assert_parity(S, rS, 1e-5, "S")  # fp32 state: a dk-term dot product, then one fma
 
 
@@ -65,7 +65,7 @@ def test_delta_decode_config_chain_sampled_states():
     worst = 0.0
     for t in range(steps):
         ro, S_ref = oracle.delta_decode_step(qs[t][None], ks[t][None], vs[t][None], bs[t][None], S_ref)
-        worst = max(worst, assert_parity(outs[t][None], ro, tol, f"o step {t}", axes=(2,)))
+        worst = max(worst, assert_parity(outs[t][None], ro, tol, f"o step {t}", axes=(2,), rows=True))
     assert_parity(S[n_idx, h_idx][None], S_ref, tol, "S final")
     print(f"worst per-step slice error of o: {worst:.2e}")
 
@@ -80,5 +80,5 @@ def test_delta_decode_chain_equals_prefill():
     o, Sf = lin.delta_forward(seq(Q), seq(K), seq(V), Bt.permute(1, 2, 0).contiguous(), S0)
     torch.cuda.synchronize()
     tol = TOL[torch.bfloat16]
-    assert_parity(outs, to64(o), tol, "o")
+    assert_parity(outs, to64(o), tol, "o", rows=True)
     assert_parity(S, to64(Sf), tol, "S")

@@ -21,6 +21,21 @@ def _raw_inputs(B, H, T, dk, dv, seed):
     return bf(3 * q), bf(2 * k), bf(v), bf(logits)
 
 
+# With LA_NORMALIZE_QK the kernel rounds each normalised q and k row to bf16
+# before its products, while the oracle normalises the bf16 inputs in fp64:
+# o_0 = beta_0 (q_0 . k_0) v_0 then carries the error of a nearly cancelling
+# dot product (12 % of its own size where q_0 . k_0 is ~1e-3, a thousandth of
+# the median row).  The row check of o floors each row's norm at 1/8 of the
+# median row norm of its (batch, head) in that mode.
+O_ROW_FLOOR = 1 / 8
+# PRED_NOTE: the prediction is formed as v_t - u_t from the correction u_t
+# the chunked update computes anyway (bf16 operands, fp32 sums).  Where the
+# prediction is much smaller than v_t (a short memory: the gated cases), its
+# error is that of u_t, i.e. relative to |v_t|: rows at 0.2-0.3 of the median
+# row norm reach errors of 10-14 % of their own size.  The prediction is
+# therefore held to the slice check only (error within 2e-2 of its largest
+# value per (batch, head)).
+
 CASES = [
     # B, H, T, dk, dv, gated, normalize, logits, init
     (1, 1, 1, 128, 128, False, True, True, True),
@@ -47,9 +62,9 @@ def test_delta_forward_ex_parity(B, H, T, dk, dv, gated, norm, logits, init):
     torch.cuda.synchronize()
     ro, rS, rp = oracle.delta_forward_ex(q, k, v, b, alpha, S0, normalize_qk=norm, beta_logits=logits)
     tol = TOL[torch.bfloat16]
-    assert_parity(o, ro, tol, "o")
+    assert_parity(o, ro, tol, "o", rows=True, row_floor=O_ROW_FLOOR if norm else 0.0)
     assert_parity(S, rS, tol, "S_T")
-    assert_parity(pred, rp, tol, "pred")
+    assert_parity(pred, rp, tol, "pred")  # slice check only: see PRED_NOTE
 
 
 def test_delta_forward_ex_without_options_is_delta_forward_bitwise():
@@ -65,19 +80,18 @@ def test_delta_forward_ex_without_options_is_delta_forward_bitwise():
     assert torch.equal(o3, o4) and torch.equal(S3, S4)
 
 
-def test_delta_forward_ex_config_sampled_heads():
+def test_delta_forward_ex_config_all_heads():
     w = wl.DELTA_BF16_PREFILL
     print(f"delta_forward_ex on {w.name} with raw q/k and beta logits", flush=True)
     q, k, v, b = _raw_inputs(w.B, w.H, w.T, w.dk, w.dv, seed=54)
     o, S, pred = lin.delta_forward_ex(q, k, v, b, normalize_qk=True, beta_logits=True, return_pred=True)
     torch.cuda.synchronize()
-    heads = [0, 31]
-    flat = lambda t: t.reshape(w.B * w.H, *t.shape[2:])[heads][None]
+    flat = lambda t: t.reshape(w.B * w.H, *t.shape[2:])[None]
     ro, rS, rp = oracle.delta_forward_ex(flat(q), flat(k), flat(v), flat(b), normalize_qk=True, beta_logits=True)
     tol = TOL[torch.bfloat16]
-    assert_parity(flat(o), ro, tol, "o")
+    assert_parity(flat(o), ro, tol, "o", rows=True, row_floor=O_ROW_FLOOR)
     assert_parity(flat(S), rS, tol, "S_T")
-    assert_parity(flat(pred), rp, tol, "pred")
+    assert_parity(flat(pred), rp, tol, "pred")  # slice check only: see PRED_NOTE
 
 
 @pytest.mark.parametrize("N,H,dk,dv,dtype,gated,norm,logits", [
@@ -97,8 +111,8 @@ def test_delta_decode_step_ex_parity(N, H, dk, dv, dtype, gated, norm, logits):
                                        return_pred=True)
     torch.cuda.synchronize()
     ro, rS, rp = oracle.delta_decode_step_ex(q, k, v, b, S_ref, alpha, normalize_qk=norm, beta_logits=logits)
-    assert_parity(o, ro, TOL[dtype], "o")
-    assert_parity(pred, rp, TOL[dtype], "pred")
+    assert_parity(o, ro, TOL[dtype], "o", rows=True)
+    assert_parity(pred, rp, TOL[dtype], "pred", rows=True)
     assert_parity(S, rS, 1e-5, "S")
 
 

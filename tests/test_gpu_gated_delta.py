@@ -28,7 +28,7 @@ def _check(q, k, v, beta, alpha, o, S, S0=None, heads=None):
     idx = list(range(B * H)) if heads is None else list(heads)
     sel = lambda t: None if t is None else t[idx][None]
     ro, rS = oracle.gated_delta_forward(sel(qf), sel(kf), sel(vf), sel(bf), sel(af), sel(S0f))
-    e1 = assert_parity(sel(of), ro, tol, "o")
+    e1 = assert_parity(sel(of), ro, tol, "o", rows=True)
     e2 = assert_parity(sel(Sf), rS, tol, "S_T")
     print(f"worst slice errors: o {e1:.2e}  S {e2:.2e}")
 
@@ -60,12 +60,12 @@ def test_gated_delta_small_shapes(B, H, T, dk, dv, init, rate):
     _check(q, k, v, beta, alpha, o, S, S0)
 
 
-def test_gated_delta_config_sampled_heads():
+def test_gated_delta_config_all_heads():
     w = wl.GATED_DELTA_BF16_PREFILL
     print(f"gated_delta_forward {w.name}", flush=True)
     q, k, v, beta, alpha = wl.make(w, DEV)
     o, S = _run(q, k, v, beta, alpha)
-    _check(q, k, v, beta, alpha, o, S, heads=(0, 15, 31))
+    _check(q, k, v, beta, alpha, o, S)
 
 
 def test_gated_delta_alpha_one_is_delta_forward():
@@ -130,7 +130,7 @@ def test_gated_delta_deterministic_and_resume():
     oa, Sa = _run(cut(q, h1), cut(k, h1), cut(v, h1), cut(beta, h1), cut(alpha, h1))
     ob, Sb = _run(cut(q, h2), cut(k, h2), cut(v, h2), cut(beta, h2), cut(alpha, h2), Sa)
     tol = TOL[torch.bfloat16]
-    assert_parity(torch.cat([oa, ob], 2), to64(a[0]), tol, "o")
+    assert_parity(torch.cat([oa, ob], 2), to64(a[0]), tol, "o", rows=True)
     assert_parity(Sb, to64(a[1]), tol, "S")
 
 
@@ -148,7 +148,7 @@ def test_gated_delta_decode_step_shapes(N, H, dk, dv, dtype):
     o = lin.gated_delta_decode_step(q, k, v, beta, alpha, S)
     torch.cuda.synchronize()
     ro, rS = oracle.gated_delta_decode_step(q, k, v, beta, alpha, S_ref)
-    assert_parity(o, ro, TOL[dtype], "o")
+    assert_parity(o, ro, TOL[dtype], "o", rows=True)
     assert_parity(S, rS, 1e-5, "S")  # fp32 state: a dk-term dot product, then two products and a sum
 
 
@@ -162,7 +162,7 @@ def test_gated_delta_decode_zero_alpha_resets():
     torch.cuda.synchronize()
     ro, rS = oracle.gated_delta_decode_step(q, k, v, beta, alpha, np.zeros((N, H, d, d)))
     assert_parity(S, rS, 1e-6, "S")
-    assert_parity(o, ro, 1e-5, "o")
+    assert_parity(o, ro, 1e-5, "o", rows=True)
 
 
 def test_gated_delta_decode_config_chain_sampled_states():
@@ -188,7 +188,7 @@ def test_gated_delta_decode_config_chain_sampled_states():
     for t in range(steps):
         ro, S_ref = oracle.gated_delta_decode_step(qs[t][None], ks[t][None], vs[t][None], bs[t][None],
                                                    als[t][None], S_ref)
-        worst = max(worst, assert_parity(outs[t][None], ro, tol, f"o step {t}", axes=(2,)))
+        worst = max(worst, assert_parity(outs[t][None], ro, tol, f"o step {t}", axes=(2,), rows=True))
     assert_parity(S[n_idx, h_idx][None], S_ref, tol, "S final")
     print(f"worst per-step slice error of o: {worst:.2e}")
 
@@ -205,5 +205,5 @@ def test_gated_delta_decode_chain_equals_prefill():
     o, Sf = lin.gated_delta_forward(seq(Q), seq(K), seq(V), seq3(Bt), seq3(At), S0)
     torch.cuda.synchronize()
     tol = TOL[torch.bfloat16]
-    assert_parity(outs, to64(o), tol, "o")
+    assert_parity(outs, to64(o), tol, "o", rows=True)
     assert_parity(S, to64(Sf), tol, "S")

@@ -27,7 +27,7 @@ def _check(q, k, v, o, S, z, S0=None, z0=None, heads=None):
     idx = list(range(B * H)) if heads is None else list(heads)
     sel = lambda t: None if t is None else t[idx][None]
     ro, rS, rz = oracle.la_forward(sel(qf), sel(kf), sel(vf), sel(S0f), sel(z0f), eps=EPS)
-    e1 = assert_parity(sel(of), ro, tol, "o")
+    e1 = assert_parity(sel(of), ro, tol, "o", rows=True)
     e2 = assert_parity(sel(Sf), rS, tol, "S_T")
     e3 = assert_parity(sel(zf), rz, tol, "z_T")
     print(f"worst slice errors: o {e1:.2e}  S {e2:.2e}  z {e3:.2e}")
@@ -86,12 +86,12 @@ def test_la_fp32_config_full():
     _check(q, k, v, o, S, z)
 
 
-@pytest.mark.parametrize("w,heads", [(wl.LA_BF16_PREFILL, (0, 13, 31)), (wl.LA_BF16_LONG, (0, 17, 31))])
-def test_la_bf16_configs_sampled_heads(w, heads):
-    print(f"la_forward {w.name} heads {heads}", flush=True)
+@pytest.mark.parametrize("w", [wl.LA_BF16_PREFILL, wl.LA_BF16_LONG])
+def test_la_bf16_configs_all_heads(w):
+    print(f"la_forward {w.name}, every head", flush=True)
     q, k, v = wl.make(w, DEV)
     o, S, z = _run(q, k, v)
-    _check(q, k, v, o, S, z, heads=heads)
+    _check(q, k, v, o, S, z)
 
 
 def test_la_causality_bitwise():
@@ -129,7 +129,7 @@ def test_la_resume_matches_single_call():
     oa, Sa, za = _run(q[:, :, :T1].contiguous(), k[:, :, :T1].contiguous(), v[:, :, :T1].contiguous())
     ob, Sb, zb = _run(q[:, :, T1:].contiguous(), k[:, :, T1:].contiguous(), v[:, :, T1:].contiguous(), Sa, za)
     tol = TOL[torch.float32]
-    assert_parity(torch.cat([oa, ob], 2), to64(o), tol, "o")
+    assert_parity(torch.cat([oa, ob], 2), to64(o), tol, "o", rows=True)
     assert_parity(Sb, to64(S), tol, "S")
     assert_parity(zb, to64(z), tol, "z")
 
@@ -153,7 +153,7 @@ def test_la_heads_isolated_and_plan_independent():
     o, S, z = _run(q, k, v)
     o1, S1, z1 = _run(q[:, 5:6].contiguous(), k[:, 5:6].contiguous(), v[:, 5:6].contiguous())
     tol = TOL[torch.bfloat16]
-    assert_parity(o1, to64(o[:, 5:6]), tol, "o")
+    assert_parity(o1, to64(o[:, 5:6]), tol, "o", rows=True)
     assert_parity(S1, to64(S[:, 5:6]), tol, "S")
     v2 = v.clone()
     v2[:, 6] += 1.0
@@ -217,3 +217,31 @@ def test_la_graph_replays_match_eager():
         torch.cuda.synchronize()
         for got, ref in zip((o, S, z), want):
             assert torch.equal(got, ref), f"replay {rep}"
+
+
+@pytest.mark.parametrize("polls", [-1, 0, 1])
+@pytest.mark.parametrize("init,alias", [(False, False), (True, False), (True, True)])
+def test_la_lookback_give_up_path_is_bitwise_equal(polls, init, alias):
+    """With the look-back's wait bound forced to (almost) nothing, later
+    segments recompute their incoming state from the inputs; the sum is taken
+    in the look-back's own order, so every output and the final state must
+    equal the normal call bit for bit -- also when S_out, z_out alias S0, z0
+    (the recomputation reads the initial state while the last segment may be
+    writing the final one)."""
+    B, H, T = 2, 16, 5100  # 16 segments of 5 chunks per sequence
+    print(f"la_forward give-up path polls={polls} init={init} alias={alias}", flush=True)
+    q, k, v = wl.la_inputs(B, H, T, 64, 64, torch.bfloat16, seed=90, device=DEV)
+    S0 = z0 = None
+    if init:
+        S0, z0 = wl.decode_state(B, H, 64, 64, seed=91, device=DEV, std=0.5)
+        z0 = z0.abs() + 1.0
+    ref = _run(q, k, v, None if S0 is None else S0.clone(), None if z0 is None else z0.clone())
+    if alias:
+        S, z = S0.clone(), z0.clone()
+        o, _, _ = lin.la_forward(q, k, v, S, z, eps=EPS, S_out=S, z_out=z, lookback_polls=polls)
+    else:
+        o, S, z = lin.la_forward(q, k, v, S0, z0, eps=EPS, lookback_polls=polls)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref[0]) and torch.equal(S, ref[1]) and torch.equal(z, ref[2])
+    if polls == -1 and not alias:
+        _check(q, k, v, o, S, z, S0, z0)

@@ -34,7 +34,16 @@ def _check(args, res, heads=None):
     worst = {}
     for name, x, r in zip(("dq", "dk", "dv", "dS0", "dz0"), res, ref):
         worst[name] = assert_parity(sel(x), r, tol, name)
-    print("worst slice errors:", {n: f"{e:.2e}" for n, e in worst.items()})
+        if name in ("dq", "dk", "dv"):
+            # Row check of every token; without an initial state, dq_0 is
+            # excluded: o_0 = v_0 w / (w + eps) depends on q_0 only through eps,
+            # so the exact dq_0 is O(eps) times the two terms that cancel to
+            # give it, below fp32 resolution of either (the slice check still
+            # bounds it).
+            t0 = 1 if (name == "dq" and S0 is None) else 0
+            xs, rs = sel(x)[:, :, t0:], r[:, :, t0:]
+            worst[name] = max(worst[name], assert_parity(xs, rs, tol, name, rows=True))
+    print("worst slice and row errors:", {n: f"{e:.2e}" for n, e in worst.items()})
 
 
 SHAPES = [
@@ -60,14 +69,14 @@ def test_la_backward_shapes(B, H, T, dk, dv, init):
     _check(args, res)
 
 
-def test_la_backward_config_sampled_heads():
+def test_la_backward_config_all_heads():
     w = wl.LA_BF16_PREFILL
     print(f"la_backward {w.name}", flush=True)
     args = _inputs(w.B, w.H, w.T, w.dk, w.dv, seed=61, init=False)
     q, k, v, dO = args[:4]
     res = lin.la_backward(q, k, v, dO, eps=EPS)
     torch.cuda.synchronize()
-    _check(args, res, heads=(0, 17, 31))
+    _check(args, res)
 
 
 def test_la_backward_deterministic():

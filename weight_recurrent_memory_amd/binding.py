@@ -54,6 +54,8 @@ def lib():
             L.la_forward.argtypes = [vp, vp, vp, fp, fp, vp, fp, fp, i, i, i, i, i, i,
                                      ctypes.c_float, i, vp, sz, vp]
             L.la_forward.restype = i
+            L.la_forward_lookback_polls.argtypes = L.la_forward.argtypes + [i]
+            L.la_forward_lookback_polls.restype = i
             L.delta_forward.argtypes = [vp, vp, vp, vp, fp, vp, fp, i, i, i, i, i, i, i, vp, sz, vp]
             L.delta_forward.restype = i
             L.la_decode_step.argtypes = [vp, vp, vp, fp, fp, vp, i, i, i, i, i, ctypes.c_float, vp]
@@ -160,10 +162,12 @@ def _workspace(nbytes, device, workspace):
 
 
 def la_forward(q, k, v, S0=None, z0=None, eps=1e-6, chunk=CHUNK, *, o=None, S_out=None,
-               z_out=None, workspace=None, return_state=True):
+               z_out=None, workspace=None, return_state=True, lookback_polls=None):
     """Causal ELU+1 linear attention prefill.  q, k: [B,H,T,dk]; v: [B,H,T,dv]
     (bf16 or fp32, CUDA/HIP tensors).  Returns (o, S_T, z_T); S_T/z_T are fp32
-    and None when return_state is False.  S_out/z_out may be S0/z0."""
+    and None when return_state is False.  S_out/z_out may be S0/z0.
+    lookback_polls (tests only) calls la_forward_lookback_polls with that
+    wait bound instead of la_forward."""
     code = _dtype_code(q)
     B, H, T, dk = q.shape
     dv = v.shape[-1]
@@ -186,9 +190,12 @@ def la_forward(q, k, v, S0=None, z0=None, eps=1e-6, chunk=CHUNK, *, o=None, S_ou
         _need(S_out, "S_out", torch.float32, (B, H, dk, dv), dev)
         _need(z_out, "z_out", torch.float32, (B, H, dk), dev)
     ws, wsb = _workspace(la_forward_workspace_bytes(B, H, T, dk, dv, chunk), dev, workspace)
-    _check(lib().la_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(S0), _ptr(z0), _ptr(o), _ptr(S_out),
-                            _ptr(z_out), B, H, T, dk, dv, code, float(eps), int(chunk),
-                            _ptr(ws), wsb, _stream(dev)))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(S0), _ptr(z0), _ptr(o), _ptr(S_out), _ptr(z_out),
+            B, H, T, dk, dv, code, float(eps), int(chunk), _ptr(ws), wsb, _stream(dev))
+    if lookback_polls is None:
+        _check(lib().la_forward(*args))
+    else:
+        _check(lib().la_forward_lookback_polls(*args, int(lookback_polls)))
     return o, S_out, z_out
 
 

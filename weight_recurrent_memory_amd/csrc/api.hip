@@ -12,6 +12,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "api_internal.hpp"
 #include "kernels.hpp"
 #include "linattn.h"
 
@@ -115,7 +116,7 @@ Plan make_plan(Family f, const Batch& b, int dk, int dv) {
         p.sp_floats = ((size_t)b.N + 1 + 63) / 64 * 64;
     }
     const long slots = (long)sm.H * sm.NS;
-    p.fam_floats = f == kFamLA ? la::la_ws_floats(slots, dk, dv)
+    p.fam_floats = f == kFamLA ? la::la_ws_floats(slots, (long)b.N * b.H, dk, dv)
                  : f == kFamDelta ? la::delta_ws_floats(slots, (long)sm.H * sm.chunk_recs_per_head(la::kChunk), dk, dv)
                                   : la::ssd_ws_floats(slots, dk, dv);
     return p;
@@ -147,9 +148,23 @@ la_status check_batch(const char* fn, const Batch& b, int dk, int dv, int dtype,
         return fail(LA_ERR_UNSUPPORTED, "%s: dk=%d dv=%d not in {64, 128}", fn, dk, dv);
     if (chunk != la::kChunk)
         return fail(LA_ERR_UNSUPPORTED, "%s: chunk=%d not supported (only %d)", fn, chunk, la::kChunk);
+    // The kernels address one (sequence, head)'s rows through buffer
+    // resources of 32-bit size with 32-bit signed byte offsets, and read up
+    // to four chunks ahead of the row being processed: every such offset must
+    // stay below 2 GiB (fp32 gates and 8-byte per-token records are smaller).
     const long elem = dtype == LA_BF16 ? 2 : 4;
-    if (((long)b.T + la::kChunk) * (dk > dv ? dk : dv) * elem >= (1L << 31))
+    if (((long)b.T + 4 * la::kChunk) * (dk > dv ? dk : dv) * elem >= (1L << 31))
         return fail(LA_ERR_UNSUPPORTED, "%s: T=%d too long (one head's rows must span < 2 GiB)", fn, b.T);
+    return LA_OK;
+}
+
+// The launch grids number (head, segment) units and chunk records with 32-bit
+// indices.
+la_status check_plan(const char* fn, const Plan& p) {
+    const long units = (long)p.sm.H * p.sm.NS;
+    const long recs = (long)p.sm.H * p.sm.chunk_recs_per_head(la::kChunk);
+    if (units > 0x7fffffffL || recs > 0x7fffffffL)
+        return fail(LA_ERR_UNSUPPORTED, "%s: %ld (head, segment) units or %ld chunks exceed 2^31-1", fn, units, recs);
     return LA_OK;
 }
 
@@ -234,7 +249,8 @@ Batch packed(const int* cu_dev, const int* cu_host, int N, int H, int T_total) {
 
 la_status la_forward_impl(const char* fn, const void* q, const void* k, const void* v, const float* S0,
                           const float* z0, void* o, float* S_out, float* z_out, const Batch& b, int dk, int dv,
-                          int dtype, float eps, int chunk, void* workspace, size_t workspace_bytes, void* stream) {
+                          int dtype, float eps, int chunk, void* workspace, size_t workspace_bytes, void* stream,
+                          int poll_limit = la::kLaPollLimit) {
     if (!q || !k || !v || !o) return fail(LA_ERR_INVALID_ARG, "%s: q, k, v and o must be non-NULL", fn);
     if (!(eps > 0.f) || !isfinite(eps))
         return fail(LA_ERR_INVALID_ARG, "%s: eps must be finite and > 0 (got %g)", fn, (double)eps);
@@ -245,13 +261,14 @@ la_status la_forward_impl(const char* fn, const void* q, const void* k, const vo
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return fail(LA_ERR_INVALID_ARG, "%s: q, k, v and o must be 16-byte aligned", fn);
     Plan plan = make_plan(kFamLA, b, dk, dv);
+    if ((st = check_plan(fn, plan)) != LA_OK) return st;
     if ((st = check_workspace(fn, plan, workspace, workspace_bytes)) != LA_OK) return st;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     float* ws = nullptr;
     hipError_t e = bind_workspace(plan, b, workspace, hs, &ws);
     if (e == hipSuccess)
         e = la::launch_la_forward(q, k, v, S0, z0, o, S_out, z_out, plan.sm, dk, dv, dtype, eps, ws, next_tag(),
-                                  stream_capturing(hs), hs);
+                                  stream_capturing(hs), poll_limit, hs);
     return hip_status(fn, e);
 }
 
@@ -273,6 +290,7 @@ la_status delta_forward_impl(const char* fn, const void* q, const void* k, const
         (reinterpret_cast<uintptr_t>(pred) & 1u))
         return fail(LA_ERR_INVALID_ARG, "%s: beta, alpha and pred must be aligned to their element size", fn);
     Plan plan = make_plan(kFamDelta, b, dk, dv);
+    if ((st = check_plan(fn, plan)) != LA_OK) return st;
     if ((st = check_workspace(fn, plan, workspace, workspace_bytes)) != LA_OK) return st;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     float* ws = nullptr;
@@ -295,6 +313,7 @@ la_status ssd_forward_impl(const char* fn, const void* q, const void* k, const v
     if ((reinterpret_cast<uintptr_t>(alpha) & 3u) || !aligned16(S0))
         return fail(LA_ERR_INVALID_ARG, "%s: alpha must be 4-byte and S0 16-byte aligned", fn);
     Plan plan = make_plan(kFamSsd, b, dk, dv);
+    if ((st = check_plan(fn, plan)) != LA_OK) return st;
     if ((st = check_workspace(fn, plan, workspace, workspace_bytes)) != LA_OK) return st;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     float* ws = nullptr;
@@ -321,7 +340,24 @@ la_status delta_decode_impl(const char* fn, const void* q, const void* k, const 
 
 }  // namespace
 
+namespace la_api {
+// la_forward for other translation units of the library (the no-allocation
+// variant): the same validation and launch, a caller-chosen workspace, and
+// workspace_query's answer for the size.
+la_status la_forward_ws(const char* fn, const void* q, const void* k, const void* v, const float* S0,
+                        const float* z0, void* o, float* S_out, float* z_out, int B, int H, int T, int dk, int dv,
+                        int dtype, float eps, int chunk, void* workspace, size_t workspace_bytes, void* stream) {
+    return la_forward_impl(fn, q, k, v, S0, z0, o, S_out, z_out, uniform(B, H, T), dk, dv, dtype, eps, chunk,
+                           workspace, workspace_bytes, stream);
+}
+size_t la_forward_ws_bytes(const char* fn, int B, int H, int T, int dk, int dv, int chunk) {
+    return workspace_query(fn, kFamLA, uniform(B, H, T), dk, dv, chunk);
+}
+la_status set_error(la_status st, const char* msg) { return fail(st, "%s", msg); }
+}  // namespace la_api
+
 extern "C" {
+
 
 const char* la_status_string(int status) {
     switch (status) {
@@ -379,6 +415,14 @@ la_status la_forward(const void* q, const void* k, const void* v, const float* S
                      void* stream) {
     return la_forward_impl("la_forward", q, k, v, S0, z0, o, S_out, z_out, uniform(B, H, T), dk, dv, dtype, eps,
                            chunk, workspace, workspace_bytes, stream);
+}
+
+la_status la_forward_lookback_polls(const void* q, const void* k, const void* v, const float* S0, const float* z0,
+                                    void* o, float* S_out, float* z_out, int B, int H, int T, int dk, int dv,
+                                    int dtype, float eps, int chunk, void* workspace, size_t workspace_bytes,
+                                    void* stream, int lookback_polls) {
+    return la_forward_impl("la_forward_lookback_polls", q, k, v, S0, z0, o, S_out, z_out, uniform(B, H, T), dk, dv,
+                           dtype, eps, chunk, workspace, workspace_bytes, stream, lookback_polls);
 }
 
 la_status la_forward_packed(const void* q, const void* k, const void* v, const int* cu_seqlens,
@@ -476,6 +520,8 @@ la_status la_backward(const void* q, const void* k, const void* v, const float* 
         !aligned16(dv_out))
         return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, dO, dq, dk and dv must be 16-byte aligned", fn);
     const la::LaPlan plan = la::la_plan(B * H, T, dk, dv);
+    if ((long)B * H * plan.G > 0x7fffffffL)
+        return fail(LA_ERR_UNSUPPORTED, "%s: %ld (head, segment) units exceed 2^31-1", fn, (long)B * H * plan.G);
     const size_t need = sizeof(float) * la::la_backward_ws_floats(B * H, T, dk, dv, plan);
     if (!workspace || workspace_bytes < need || !aligned16(workspace))
         return fail(LA_ERR_WORKSPACE, "%s: workspace of %zu bytes (16-byte aligned) required, got %zu", fn, need,

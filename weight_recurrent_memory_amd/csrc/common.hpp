@@ -138,6 +138,19 @@ template <> struct Mma<bf16_t> {
         return frag{f32_to_bf(t0[0]), f32_to_bf(t0[1]), f32_to_bf(t0[2]), f32_to_bf(t0[3]),
                     f32_to_bf(t1[0]), f32_to_bf(t1[1]), f32_to_bf(t1[2]), f32_to_bf(t1[3])};
     }
+    // The same pair of tiles as two fragments whose sum carries about 16
+    // significant bits: hi = bf16(x), lo = bf16(x - hi).  For operands whose
+    // products cancel against another term, where one bf16 rounding would
+    // set the error of the difference.
+    static __device__ __forceinline__ void split_tiles(v4f t0, v4f t1, frag& hi, frag& lo) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            hi[r] = f32_to_bf(t0[r]);
+            hi[4 + r] = f32_to_bf(t1[r]);
+            lo[r] = f32_to_bf(t0[r] - (float)hi[r]);
+            lo[4 + r] = f32_to_bf(t1[r] - (float)hi[4 + r]);
+        }
+    }
     // Fragment of 16 contiguous bytes: slot s of group g <-> k = 8g + s.  Used
     // where both operands are rows with a contiguous contraction index.
     static __device__ __forceinline__ frag load16(const op_t* row, int g) {

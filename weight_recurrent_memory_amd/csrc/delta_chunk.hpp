@@ -115,6 +115,8 @@ __device__ __forceinline__ void build_T(const __bf16* Ks, const __bf16* Qs, cons
     constexpr int NTILE = WANT_P ? 20 : 10;
     if constexpr (K_DEAD) {
         static_assert(!WANT_P && !KEEP, "K_DEAD builds T alone");
+        // every one of the ten K K^T tiles must be formed before A overwrites K
+        static_assert(2 * NWV >= 10, "K_DEAD needs at least five waves");
         v4f kk[2];
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {  // eight or more waves: at most two of the ten tiles each
@@ -270,6 +272,7 @@ template <int DK, bool GATED, bool KEEP = false, int LQ = DK + 8>
 __device__ __forceinline__ void build_P(const __bf16* Ks, const __bf16* Qs, const float* Gl, __bf16* Ps, int w, int g,
                                         int li, v4f* keep = nullptr) {
     using M = Mma<bf16_t>;
+    static_assert(2 * NWV >= 10, "two tiles per wave must cover the ten lower tiles");
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
         const int id = w + NWV * jj;

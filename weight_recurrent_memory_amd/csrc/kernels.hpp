@@ -21,19 +21,24 @@ struct LaPlan {
 
 // Linear attention prefill: one fused launch (segment aggregate, look-back,
 // chunked outputs).  dtype 0 = fp32, 1 = bf16 (raw bits).  ws holds
-// la_ws_floats(...) floats: the look-back flags, then per-slot aggregate and
-// inclusive states.  tag (nonzero, < 2^62) must differ from the tag of every
+// la_ws_floats(...) floats: the look-back flags, per-slot aggregate and
+// inclusive states, then room for a copy of S0, z0 (used when S_out, z_out
+// alias them).  tag (nonzero, < 2^62) must differ from the tag of every
 // earlier call that used ws, unless clear_flags is set (a flag-clearing
-// launch first, for launches recorded into a graph).
+// launch first, for launches recorded into a graph).  poll_limit bounds the
+// look-back's polls per window (kLaPollLimit in production; a negative
+// value makes every later segment recompute its incoming state instead).
+constexpr int kLaPollLimit = 4000;
 hipError_t launch_la_forward(const void* q, const void* k, const void* v,
                              const float* S0, const float* z0, void* o,
                              float* S_out, float* z_out, const SegMap& sm, int dk,
                              int dv, int dtype, float eps, float* ws,
-                             unsigned long long tag, bool clear_flags, hipStream_t stream);
+                             unsigned long long tag, bool clear_flags, int poll_limit, hipStream_t stream);
 size_t la_lds_bytes(int dk, int dv, int dtype);
 LaPlan la_plan(int HT, int T, int dk, int dv);
 size_t la_flag_words(long slots);
-size_t la_ws_floats(long slots, int dk, int dv);
+// slots = H * NS (head, segment) units; states = N * H (sequence, head) pairs.
+size_t la_ws_floats(long slots, long states, int dk, int dv);
 
 // Packed batches: sp[n] = segments of sequences 0..n-1 (L tokens per
 // segment, lengths from the clamped offsets cu), n = 0..N, on the device.

@@ -65,8 +65,13 @@ struct BL {
 template <int DK, int DV>
 struct BLds {
     using Y = BL<DK, DV>;
-    static constexpr int K = 0, V = K + Y::CQ, Q = V + Y::CV, N = Q + Y::CQ, S = N + Y::CV;
-    static constexpr int BF16 = S + Y::ST;           // bf16 elements
+    // N, NL: dN' as hi and lo bf16 parts (the reverse sweep's M tiles use both).
+    // S, SL: the transposed state copy, hi and lo parts; the lo part (used by
+    // the forward sweep's dq) only where the LDS has room for it.
+    static constexpr int K = 0, V = K + Y::CQ, Q = V + Y::CV, N = Q + Y::CQ, NL = N + Y::CV, S = NL + Y::CV;
+    static constexpr bool STATE_LO = 2 * (S + 2 * Y::ST) + CH * 4 <= 160 * 1024;
+    static constexpr int SL = S + Y::ST;
+    static constexpr int BF16 = S + (STATE_LO ? 2 : 1) * Y::ST;  // bf16 elements
     static constexpr int BYTES = 2 * BF16 + CH * 4;  // + dden (fp32, one per query)
     // LDS reserved per workgroup: at least 56 KB.  At d = 64 the sweeps need
     // 48.6 KB; reserving 56 KB measured 122-126 us per call against
@@ -77,18 +82,23 @@ struct BLds {
 
 // The transposed bf16 copy of a running state tile set X[RTW][NCT] (rows dk
 // 16 (w RTW + i) + 4g + r, columns 16c + li) into st: row = column of X.
+// With lo non-null, also the rounding remainder: lo = bf16(x - hi).
 template <int DK, int DV>
 __device__ __forceinline__ void write_state_t(const v4f (&X)[BL<DK, DV>::RTW][BL<DK, DV>::NCT], __bf16* st, int w,
-                                              int lane) {
+                                              int lane, __bf16* lo = nullptr) {
     using Y = BL<DK, DV>;
     const int g = lane >> 4, li = lane & 15;
 #pragma unroll
     for (int i = 0; i < Y::RTW; ++i)
 #pragma unroll
         for (int c = 0; c < Y::NCT; ++c) {
-            __bf16* dst = &st[(16 * c + li) * Y::LQ + 16 * (w * Y::RTW + i) + 4 * g];
+            const int off = (16 * c + li) * Y::LQ + 16 * (w * Y::RTW + i) + 4 * g;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dst[r] = Mma<bf16_t>::cvt(X[i][c][r]);
+            for (int r = 0; r < 4; ++r) {
+                const __bf16 hi = Mma<bf16_t>::cvt(X[i][c][r]);
+                st[off + r] = hi;
+                if (lo) lo[off + r] = Mma<bf16_t>::cvt(X[i][c][r] - (float)hi);
+            }
         }
 }
 
@@ -266,6 +276,7 @@ __device__ __forceinline__ void lab_fwd_pass(rsrc_t rq, rsrc_t rk, rsrc_t rv, rs
     __bf16* Qs = lds + LO::Q;
     __bf16* Ns = lds + LO::N;
     __bf16* Sts = lds + LO::S;
+    __bf16* Stl = LO::STATE_LO ? lds + LO::SL : nullptr;
     float* Dd = reinterpret_cast<float*>(lds + LO::BF16);
 
     ChunkRegs<bf16_t, DK, NT> kr, qr;
@@ -295,7 +306,7 @@ __device__ __forceinline__ void lab_fwd_pass(rsrc_t rq, rsrc_t rk, rsrc_t rv, rs
         stage_rows_phi<bf16_t, DK, NT>(kr, t_end - c0, tid_v, Ks, LQ);
         stage_rows_phi<bf16_t, DK, NT>(qr, t_end - c0, tid_v, Qs, LQ);
         stage_rows_raw<bf16_t, DV, NT>(vr, tid_v, Vs, LV);
-        write_state_t<DK, DV>(S, Sts, W, lane);
+        write_state_t<DK, DV>(S, Sts, W, lane, Stl);
         v4f dOt[NVT];
 #pragma unroll
         for (int c = 0; c < NVT; ++c) {
@@ -360,15 +371,23 @@ __device__ __forceinline__ void lab_fwd_pass(rsrc_t rq, rsrc_t rk, rsrc_t rv, rs
             *reinterpret_cast<uint2*>(&Ns[(16 * W + li) * LV + 16 * c + 4 * g]) = pk;
         }
 
-        // ---- M^T tiles (keys 16kb.. x this wave's queries): V dN^T + dden, causal
+        // ---- M^T tiles (keys 16kb.. x this wave's queries): V dN^T + dden, causal.
+        // M[t][i] = dN_t . (v_i - o_t) cancels where v_i is near o_t (the
+        // first tokens above all): dN enters as hi + lo bf16 parts, so its
+        // rounding does not set the error of the difference.
+        frag dnh[NVT / 2], dnl[NVT / 2];
+#pragma unroll
+        for (int cc = 0; cc < NVT / 2; ++cc) M::split_tiles(dNt[2 * cc], dNt[2 * cc + 1], dnh[cc], dnl[cc]);
         v4f Mt[W + 1];
 #pragma unroll
         for (int kb = 0; kb <= W; ++kb) {
             Mt[kb] = zero4();
 #pragma unroll
-            for (int cc = 0; cc < NVT / 2; ++cc)
-                M::mma(Mt[kb], M::load(&Vs[(16 * kb + li) * LV + 32 * cc], g),
-                       M::from_tiles(dNt[2 * cc], dNt[2 * cc + 1]));
+            for (int cc = 0; cc < NVT / 2; ++cc) {
+                const frag va = M::load(&Vs[(16 * kb + li) * LV + 32 * cc], g);
+                M::mma(Mt[kb], va, dnh[cc]);
+                M::mma(Mt[kb], va, dnl[cc]);
+            }
             Mt[kb] += dden;
         }
 #pragma unroll
@@ -383,14 +402,27 @@ __device__ __forceinline__ void lab_fwd_pass(rsrc_t rq, rsrc_t rk, rsrc_t rv, rs
             for (int j = 0; j < NJ; ++j)
                 M::mma(acc, M::load_tr(Ks, LQ, 32 * j, 16 * t, lane),
                        M::from_tiles(Mt[2 * j], (2 * j + 1 <= W) ? Mt[(2 * j + 1) <= W ? 2 * j + 1 : W] : zero4()));
+            // S dN + z dden nearly cancel where o is near the history's mean
+            // value: state and dN both enter as hi + lo parts (where the
+            // state's lo part fits in LDS)
 #pragma unroll
-            for (int cc = 0; cc < NVT / 2; ++cc)
-                M::mma(acc, M::load_tr(Sts, LQ, 32 * cc, 16 * t, lane), M::from_tiles(dNt[2 * cc], dNt[2 * cc + 1]));
+            for (int cc = 0; cc < NVT / 2; ++cc) {
+                const frag sa = M::load_tr(Sts, LQ, 32 * cc, 16 * t, lane);
+                M::mma(acc, sa, dnh[cc]);
+                M::mma(acc, sa, dnl[cc]);
+                if constexpr (LO::STATE_LO) M::mma(acc, M::load_tr(Stl, LQ, 32 * cc, 16 * t, lane), dnh[cc]);
+            }
             const v4bf zr = *reinterpret_cast<const v4bf*>(&Sts[DV * LQ + 16 * t + 4 * g]);
+            v4f zf = v4f{(float)zr[0], (float)zr[1], (float)zr[2], (float)zr[3]};
+            if constexpr (LO::STATE_LO) {
+                const v4bf zl = *reinterpret_cast<const v4bf*>(&Stl[DV * LQ + 16 * t + 4 * g]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) zf[r] += (float)zl[r];
+            }
             const v4bf fq = *reinterpret_cast<const v4bf*>(&Qs[(16 * W + li) * LQ + 16 * t + 4 * g]);
             float o4[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) o4[r] = (acc[r] + (float)zr[r] * dden) * fminf((float)fq[r], 1.f);
+            for (int r = 0; r < 4; ++r) o4[r] = (acc[r] + zf[r] * dden) * fminf((float)fq[r], 1.f);
             store4_bf16(rdq, (uint32_t)(((c0 + 16 * W + li) * DK + 16 * t + 4 * g) * 2), o4);
         }
         __syncthreads();  // dN' of every wave in LDS
@@ -466,6 +498,7 @@ __device__ __forceinline__ void lab_bwd_pass(rsrc_t rq, rsrc_t rk, rsrc_t rv, rs
     __bf16* Vs = lds + LO::V;
     __bf16* Qs = lds + LO::Q;
     __bf16* Ns = lds + LO::N;
+    __bf16* Nl = lds + LO::NL;
     __bf16* Gts = lds + LO::S;
     float* Dd = reinterpret_cast<float*>(lds + LO::BF16);
 
@@ -501,19 +534,31 @@ __device__ __forceinline__ void lab_bwd_pass(rsrc_t rq, rsrc_t rk, rsrc_t rv, rs
         for (int j = 0; j < ChunkRegs<bf16_t, DV, NT>::NV; ++j) {
             const int row = ChunkRegs<bf16_t, DV, NT>::row_of(j, tid_v);
             const int col = ChunkRegs<bf16_t, DV, NT>::col_of(j, tid_v);
-            uint4 x;
-            x.x = pack_bf16x2(dr.get(j, 0) * tinv[j], dr.get(j, 1) * tinv[j]);
-            x.y = pack_bf16x2(dr.get(j, 2) * tinv[j], dr.get(j, 3) * tinv[j]);
-            x.z = pack_bf16x2(dr.get(j, 4) * tinv[j], dr.get(j, 5) * tinv[j]);
-            x.w = pack_bf16x2(dr.get(j, 6) * tinv[j], dr.get(j, 7) * tinv[j]);
+            float dn[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dn[e] = dr.get(j, e) * tinv[j];
+            uint4 x, y;
+            x.x = pack_bf16x2(dn[0], dn[1]);
+            x.y = pack_bf16x2(dn[2], dn[3]);
+            x.z = pack_bf16x2(dn[4], dn[5]);
+            x.w = pack_bf16x2(dn[6], dn[7]);
+            const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+            uint32_t ys[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ys[e] = pack_bf16x2(dn[2 * e] - __uint_as_float(xs[e] << 16),
+                                    dn[2 * e + 1] - __uint_as_float(xs[e] & 0xffff0000u));
+            y = make_uint4(ys[0], ys[1], ys[2], ys[3]);
             *reinterpret_cast<uint4*>(&Ns[row * LV + col]) = x;
+            *reinterpret_cast<uint4*>(&Nl[row * LV + col]) = y;
         }
         if (tid_v < CH) Dd[tid_v] = tdd;
         write_state_t<DK, DV>(Gp, Gts, W, lane);
         if (it + 1 < nch) load_chunk(c0 - CH);
         __syncthreads();
 
-        // ---- M tiles (queries 16qb.. x this wave's keys): dN V^T + dden, causal (query >= key)
+        // ---- M tiles (queries 16qb.. x this wave's keys): dN V^T + dden, causal (query >= key);
+        // dN as hi + lo parts, as in the forward sweep (M cancels where v is near o)
         v4f Mq[CH / 16], Pq[CH / 16];
 #pragma unroll
         for (int qb = 0; qb < CH / 16; ++qb) {
@@ -521,9 +566,11 @@ __device__ __forceinline__ void lab_bwd_pass(rsrc_t rq, rsrc_t rk, rsrc_t rv, rs
             Pq[qb] = zero4();
             if (qb >= W) {
 #pragma unroll
-                for (int cc = 0; cc < NVT / 2; ++cc)
-                    M::mma(Mq[qb], M::load(&Ns[(16 * qb + li) * LV + 32 * cc], g),
-                           M::load(&Vs[(16 * W + li) * LV + 32 * cc], g));
+                for (int cc = 0; cc < NVT / 2; ++cc) {
+                    const frag vb = M::load(&Vs[(16 * W + li) * LV + 32 * cc], g);
+                    M::mma(Mq[qb], M::load(&Ns[(16 * qb + li) * LV + 32 * cc], g), vb);
+                    M::mma(Mq[qb], M::load(&Nl[(16 * qb + li) * LV + 32 * cc], g), vb);
+                }
                 const v4f dd = *reinterpret_cast<const v4f*>(&Dd[16 * qb + 4 * g]);
                 Mq[qb] += dd;
 #pragma unroll

@@ -69,12 +69,15 @@ struct Layout {
 //   4. run the chunk loop from that state, writing the outputs.
 // Published states are written and read with accesses coherent across the
 // chip's L2s; the flag is stored only after the data stores have completed.
-// Every wait is bounded: a workgroup that times out recomputes its incoming
-// state from the inputs (sum over all earlier tokens), so progress never
-// depends on the dispatch order.
+// Every wait is bounded (poll_limit polls of one window; a negative limit
+// skips the look-back altogether): a workgroup that gives up recomputes its
+// incoming state from the inputs, so progress never depends on the dispatch
+// order.  It recomputes every predecessor's aggregate with the routine that
+// predecessor used and adds them to S0 left to right -- the same operations
+// in the same order as the look-back's sum -- so the result is the same bit
+// for bit on either path.
 
 enum : int { kFlagNone = 0, kFlagAggregate = 1, kFlagInclusive = 2 };
-constexpr int kPollLimit = 4000;  // polls of one window before giving up (~ms)
 
 // A flag word is (tag << 2) | state; a word with another call's tag is absent.
 typedef unsigned long long flag_t;
@@ -153,52 +156,6 @@ __device__ __forceinline__ void add_staged(const typename Mma<TIn>::op_t* Ks, co
     }
 }
 
-// acc += phi(K)^T [V | 1] over tokens [t0, t1), chunks in order.  NPF chunks
-// are in flight ahead of the one being staged; the two LDS chunk buffers
-// alternate, so one barrier per chunk suffices.  Rows at or past t1 read as
-// zero through the buffer resources.
-template <typename TIn, int DK, int DV>
-__device__ __forceinline__ void accumulate_kv(const TIn* kh, const TIn* vh, int t0, int t1,
-                                              v4f (&acc)[Layout<TIn, DK, DV>::RTW][Layout<TIn, DK, DV>::NCT],
-                                              typename Mma<TIn>::op_t* Kb, typename Mma<TIn>::op_t* Vb, int tid) {
-    using LY = Layout<TIn, DK, DV>;
-    constexpr int NPF = kPrefetch<TIn, DK, DV>;
-    const int lane = tid & 63, w = wave_id(tid);
-    if (t0 >= t1) return;
-    const rsrc_t rk = make_rsrc(kh, (uint32_t)t1 * DK * sizeof(TIn));
-    const rsrc_t rv = make_rsrc(vh, (uint32_t)t1 * DV * sizeof(TIn));
-    ChunkRegs<TIn, DK, NTHR> kr[NPF];
-    ChunkRegs<TIn, DV, NTHR> vr[NPF];
-#pragma unroll
-    for (int p = 0; p < NPF; ++p) {
-        kr[p].load_buf(rk, t0 + p * CH, tid);
-        vr[p].load_buf(rv, t0 + p * CH, tid);
-    }
-    auto body = [&](auto slot, int c0) {
-        constexpr int sl = decltype(slot)::value, b = sl & 1;
-        typename Mma<TIn>::op_t* Ks = Kb + b * LY::KSZ;
-        typename Mma<TIn>::op_t* Vs = Vb + b * LY::VSZ;
-        stage_rows_phi<TIn, DK, NTHR>(kr[sl], t1 - c0, tid, Ks, LY::LQ);
-        stage_rows_raw<TIn, DV, NTHR>(vr[sl], tid, Vs, LY::LV);
-        kr[sl].load_buf(rk, c0 + NPF * CH, tid);
-        vr[sl].load_buf(rv, c0 + NPF * CH, tid);
-        __syncthreads();
-        add_staged<TIn, DK, DV>(Ks, Vs, acc, lane, w);
-    };
-    // Whole groups of NPF chunks, with no exit inside a group: the wait
-    // counts then stay exact across the loop's back edge (a group reaching
-    // past t1 stages zero rows, which add nothing).
-    for (int c0 = t0; c0 < t1; c0 += NPF * CH) {
-        body(std::integral_constant<int, 0>{}, c0);
-        body(std::integral_constant<int, 1>{}, c0 + CH);
-        if constexpr (NPF == 4) {
-            body(std::integral_constant<int, 2>{}, c0 + 2 * CH);
-            body(std::integral_constant<int, 3>{}, c0 + 3 * CH);
-        }
-    }
-    __syncthreads();  // the caller reuses the buffers
-}
-
 // The raw key and value rows of a segment's first NPF chunks, kept in
 // registers from the aggregate pass to the output pass so that they are read
 // from memory once.
@@ -212,8 +169,11 @@ struct KeptChunks {
 
 // The segment's aggregate phi(K)^T [V | 1] over [t0, t1), its groups of NPF
 // chunks taken last to first: the group loaded last is the segment's first
-// NPF chunks, which stay in `kept`.  Same pipelining as accumulate_kv; the
-// order of the sum is fixed, so results do not depend on timing.
+// NPF chunks, which stay in `kept`.  NPF chunks are in flight ahead of the
+// one being staged and the two LDS chunk buffers alternate, so one barrier
+// per chunk suffices; rows at or past t1 read as zero through the buffer
+// resources.  The order of the sum is fixed, so results do not depend on
+// timing.
 template <typename TIn, int DK, int DV>
 __device__ __forceinline__ void aggregate_keep(const TIn* kh, const TIn* vh, int t0, int t1,
                                                v4f (&acc)[Layout<TIn, DK, DV>::RTW][Layout<TIn, DK, DV>::NCT],
@@ -256,6 +216,36 @@ __device__ __forceinline__ void aggregate_keep(const TIn* kh, const TIn* vh, int
     for (; c0 > t0; c0 -= GS) group(std::true_type{}, c0);
     group(std::false_type{}, t0);
     __syncthreads();  // the caller reuses the buffers
+}
+
+// The same sum as aggregate_keep -- the same chunks, staged the same way and
+// added in the same order, so the result is the same bit for bit -- with one
+// chunk in flight and nothing kept: for the look-back's give-up path, which
+// recomputes predecessors' aggregates and must not add register pressure.
+template <typename TIn, int DK, int DV>
+__device__ __forceinline__ void aggregate_again(const TIn* kh, const TIn* vh, int t0, int t1,
+                                                v4f (&acc)[Layout<TIn, DK, DV>::RTW][Layout<TIn, DK, DV>::NCT],
+                                                typename Mma<TIn>::op_t* Kb, typename Mma<TIn>::op_t* Vb, int tid) {
+    using LY = Layout<TIn, DK, DV>;
+    constexpr int NPF = KeptChunks<TIn, DK, DV>::N, GS = NPF * CH;
+    const int lane = tid & 63, w = wave_id(tid);
+    const rsrc_t rk = make_rsrc(kh, (uint32_t)t1 * DK * sizeof(TIn));
+    const rsrc_t rv = make_rsrc(vh, (uint32_t)t1 * DV * sizeof(TIn));
+    const int last = t0 + (t1 - t0 > GS ? (t1 - t0 - 1) / GS * GS : 0);
+    for (int cg = last; cg >= t0; cg -= GS) {
+        for (int p = 0; p < NPF; ++p) {
+            const int c = cg + p * CH;
+            ChunkRegs<TIn, DK, NTHR> kr;
+            ChunkRegs<TIn, DV, NTHR> vr;
+            kr.load_buf(rk, c, tid);
+            vr.load_buf(rv, c, tid);
+            stage_rows_phi<TIn, DK, NTHR>(kr, t1 - c, tid, Kb, LY::LQ);
+            stage_rows_raw<TIn, DV, NTHR>(vr, tid, Vb, LY::LV);
+            __syncthreads();
+            add_staged<TIn, DK, DV>(Kb, Vb, acc, lane, w);
+            __syncthreads();
+        }
+    }
 }
 
 // Registers of one output-pass chunk in flight: phi(K) and V rows for the
@@ -478,7 +468,8 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
                                                         const float* S0, const float* z0,
                                                         TIn* __restrict__ o, float* S_out, float* z_out,
                                                         flag_t* __restrict__ flags, flag_t tag, float* __restrict__ agg,
-                                                        float* __restrict__ incl, SegMap sm, float eps) {
+                                                        float* __restrict__ incl, SegMap sm, float eps,
+                                                        int poll_limit) {
     using M = Mma<TIn>;
     using op = typename M::op_t;
     using LY = Layout<TIn, DK, DV>;
@@ -522,7 +513,8 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
     const TIn* kh = k + row0 * DK;
     const TIn* vh = v + row0 * DV;
     const int L = sm.L;
-    const int t_beg = seg * L, t_end = min((seg + 1) * L, sm.length<PACKED>(nseq));
+    const int len = sm.length<PACKED>(nseq);
+    const int t_beg = seg * L, t_end = min((seg + 1) * L, len);
     flag_t* hflags = flags + sbase;
 
     // element of the (dk x (dv + 1)) state held in tile (i, c), register r
@@ -578,8 +570,8 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
         // segment base - j.  Segment 0 always publishes an inclusive state,
         // so the walk ends.
         int jstar = -1;
-        bool timeout = false;
-        for (int base = seg - 1; base >= 0; base -= 64) {
+        bool timeout = poll_limit < 0;
+        for (int base = seg - 1; base >= 0 && !timeout; base -= 64) {
             if (w == 0) {
                 const int p = base - lane;
                 int polls = 0, found = -1, to = 0;
@@ -595,7 +587,7 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
                         found = incl_mask ? base - stop : -1;
                         break;
                     }
-                    if (++polls > kPollLimit) {
+                    if (++polls > poll_limit) {
                         to = 1;
                         break;
                     }
@@ -638,7 +630,14 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
                     }
             }
         } else {
-            // recompute the incoming state from the inputs
+            // Gave up: S_in = S0 + A_0 + ... + A_{seg-1}, left to right, each
+            // predecessor aggregate A_j recomputed as segment j computed it
+            // (same chunk order, same MFMA chains).  The running sum
+            // waits in this segment's own inclusive slot, which no other
+            // workgroup reads before this one publishes it (step 3), so that
+            // only A_j occupies registers during each recomputation.  S0 is
+            // read here while the last segment may already be writing S_out:
+            // the host passes a snapshot when the two alias.
 #pragma unroll
             for (int i = 0; i < RTW; ++i)
 #pragma unroll
@@ -651,7 +650,25 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
                         else { if (z0) x = z0[(long)head * DK + (e - DK * DV)]; }
                         S[i][c][r] = x;
                     }
-            accumulate_kv<TIn, DK, DV>(kh, vh, 0, t_beg, S, Kb, Vb, tid);
+            float* run = incl + (sbase + seg) * E;
+            PUB::store(run, S, w, lane);
+            for (int j = 0; j < seg; ++j) {
+#pragma unroll
+                for (int i = 0; i < RTW; ++i)
+#pragma unroll
+                    for (int c = 0; c < NCT; ++c) S[i][c] = zero4();
+                aggregate_again<TIn, DK, DV>(kh, vh, j * L, min((j + 1) * L, len), S, Kb, Vb, tid);
+                __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the wave's own stores of `run`
+                v4f X[RTW][NCT];
+                PUB::load(run, X, w, lane);
+#pragma unroll
+                for (int i = 0; i < RTW; ++i)
+#pragma unroll
+                    for (int c = 0; c < NCT; ++c) X[i][c] += S[i][c];
+                PUB::store(run, X, w, lane);
+            }
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            PUB::load(run, S, w, lane);
         }
     }
 
@@ -699,12 +716,28 @@ __global__ void la_flags_clear_kernel(flag_t* flags, int n) {
 template <typename TIn, int DK, int DV>
 hipError_t launch_typed(const void* q, const void* k, const void* v, const float* S0,
                         const float* z0, void* o, float* S_out, float* z_out, const SegMap& sm,
-                        float eps, float* ws, unsigned long long tag, bool clear_flags,
+                        float eps, float* ws, unsigned long long tag, bool clear_flags, int poll_limit,
                         hipStream_t stream) {
     const long slots = (long)sm.H * sm.NS;
     flag_t* flags = reinterpret_cast<flag_t*>(ws);
     float* agg = ws + la_flag_words(slots);
     float* incl = agg + (size_t)slots * (DK * DV + DK);
+    // In-place continuation (S_out == S0 or z_out == z0) with more than one
+    // segment in some sequence: a workgroup that gives up on the look-back
+    // reads S0, z0 while the last segment may already have written S_out,
+    // z_out, so the kernel reads copies taken before it starts.
+    if (sm.NS > sm.N && ((S0 && S0 == S_out) || (z0 && z0 == z_out))) {
+        const long states = (long)sm.N * sm.H;
+        float* S0c = incl + (size_t)slots * (DK * DV + DK);
+        float* z0c = S0c + (size_t)states * DK * DV;
+        hipError_t err = hipSuccess;
+        if (S0) err = hipMemcpyAsync(S0c, S0, (size_t)states * DK * DV * 4, hipMemcpyDeviceToDevice, stream);
+        if (err == hipSuccess && z0)
+            err = hipMemcpyAsync(z0c, z0, (size_t)states * DK * 4, hipMemcpyDeviceToDevice, stream);
+        if (err != hipSuccess) return err;
+        if (S0) S0 = S0c;
+        if (z0) z0 = z0c;
+    }
     if (clear_flags) {
         la_flags_clear_kernel<<<dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, stream>>>(flags, (int)slots);
         const hipError_t err = hipGetLastError();
@@ -713,7 +746,7 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
     auto kern = sm.packed() ? la_fused_kernel<TIn, DK, DV, true> : la_fused_kernel<TIn, DK, DV, false>;
     kern<<<dim3((unsigned)slots), dim3(NTHR), 0, stream>>>(
         static_cast<const TIn*>(q), static_cast<const TIn*>(k), static_cast<const TIn*>(v), S0, z0,
-        static_cast<TIn*>(o), S_out, z_out, flags, (flag_t)tag, agg, incl, sm, eps);
+        static_cast<TIn*>(o), S_out, z_out, flags, (flag_t)tag, agg, incl, sm, eps, poll_limit);
     return hipGetLastError();
 }
 
@@ -736,8 +769,8 @@ LaPlan la_plan(int HT, int T, int dk, int dv) {
     return p;
 }
 
-size_t la_ws_floats(long slots, int dk, int dv) {
-    return la_flag_words(slots) + (size_t)2 * slots * ((size_t)dk * dv + dk);
+size_t la_ws_floats(long slots, long states, int dk, int dv) {
+    return la_flag_words(slots) + (size_t)(2 * slots + states) * ((size_t)dk * dv + dk);
 }
 
 size_t la_lds_bytes(int dk, int dv, int dtype) {
@@ -758,10 +791,11 @@ size_t la_lds_bytes(int dk, int dv, int dtype) {
 hipError_t launch_la_forward(const void* q, const void* k, const void* v, const float* S0,
                              const float* z0, void* o, float* S_out, float* z_out, const SegMap& sm,
                              int dk, int dv, int dtype, float eps, float* ws,
-                             unsigned long long tag, bool clear_flags, hipStream_t stream) {
+                             unsigned long long tag, bool clear_flags, int poll_limit, hipStream_t stream) {
 #define LA_CASE(TY, DT, A, B)                                                                                \
     if (dtype == DT && dk == A && dv == B)                                                                   \
-        return launch_typed<TY, A, B>(q, k, v, S0, z0, o, S_out, z_out, sm, eps, ws, tag, clear_flags, stream);
+        return launch_typed<TY, A, B>(q, k, v, S0, z0, o, S_out, z_out, sm, eps, ws, tag, clear_flags,       \
+                                      poll_limit, stream);
     LA_CASE(bf16_t, 1, 64, 64)
     LA_CASE(bf16_t, 1, 64, 128)
     LA_CASE(bf16_t, 1, 128, 64)
