@@ -132,6 +132,27 @@ la_status la_forward_lookback_polls(const void* q, const void* k, const void* v,
                                     void* workspace, size_t workspace_bytes, void* stream, int lookback_polls);
 
 /*
+ * la_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation).  The workspace is a fixed scratch array in device
+ * memory, LA_NOALLOC_SCRATCH_BYTES per GPU the library runs on, held until
+ * the process ends; the call itself allocates and frees nothing.
+ * Arguments, results and errors are those of la_forward, plus
+ * LA_ERR_UNSUPPORTED when these sizes need more workspace than the scratch
+ * holds (la_forward_workspace_bytes(...) > LA_NOALLOC_SCRATCH_BYTES; the
+ * long-stream size B=1, H=32, T=65536, dk=dv=64 fits).
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap on
+ * one GPU (other streams, other host threads) race and must not be issued.
+ * What a call leaves in the scratch never changes a later call's result.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES (72u << 20)
+la_status la_forward_noalloc(const void* q, const void* k, const void* v,
+                             const float* S0, const float* z0,
+                             void* o, float* S_out, float* z_out,
+                             int B, int H, int T, int dk, int dv, int dtype, float eps, int chunk,
+                             void* stream);
+
+/*
  * Bytes of device workspace delta_forward (and gated_delta_forward,
  * delta_forward_ex) needs; 0 if the sizes are invalid.  The workspace holds
  * the per-segment affine maps and states (fp32) and one record per 64-token

@@ -56,6 +56,8 @@ def lib():
             L.la_forward.restype = i
             L.la_forward_lookback_polls.argtypes = L.la_forward.argtypes + [i]
             L.la_forward_lookback_polls.restype = i
+            L.la_forward_noalloc.argtypes = [vp, vp, vp, fp, fp, vp, fp, fp, i, i, i, i, i, i, ctypes.c_float, i, vp]
+            L.la_forward_noalloc.restype = i
             L.delta_forward.argtypes = [vp, vp, vp, vp, fp, vp, fp, i, i, i, i, i, i, i, vp, sz, vp]
             L.delta_forward.restype = i
             L.la_decode_step.argtypes = [vp, vp, vp, fp, fp, vp, i, i, i, i, i, ctypes.c_float, vp]
@@ -196,6 +198,34 @@ def la_forward(q, k, v, S0=None, z0=None, eps=1e-6, chunk=CHUNK, *, o=None, S_ou
         _check(lib().la_forward(*args))
     else:
         _check(lib().la_forward_lookback_polls(*args, int(lookback_polls)))
+    return o, S_out, z_out
+
+
+def la_forward_noalloc(q, k, v, S0=None, z0=None, eps=1e-6, chunk=CHUNK, *, o=None, S_out=None, z_out=None):
+    """la_forward on the library's fixed per-GPU scratch instead of a
+    workspace: the call allocates nothing when o, S_out and z_out are given.
+    Returns (o, S_T, z_T)."""
+    code = _dtype_code(q)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(k, "k", q.dtype, (B, H, T, dk), dev)
+    _need(v, "v", q.dtype, (B, H, T, dv), dev)
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (B, H, dk, dv), dev)
+    if z0 is not None:
+        _need(z0, "z0", torch.float32, (B, H, dk), dev)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
+    if S_out is None:
+        S_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if z_out is None:
+        z_out = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+    _need(o, "o", q.dtype, (B, H, T, dv), dev)
+    _need(S_out, "S_out", torch.float32, (B, H, dk, dv), dev)
+    _need(z_out, "z_out", torch.float32, (B, H, dk), dev)
+    _check(lib().la_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(S0), _ptr(z0), _ptr(o), _ptr(S_out),
+                                    _ptr(z_out), B, H, T, dk, dv, code, float(eps), int(chunk), _stream(dev)))
     return o, S_out, z_out
 
 
