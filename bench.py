@@ -25,9 +25,10 @@ printed is one JSON object:
   decode chains of the other three rules -- each with its own roofline
   fraction.
 
-Timing (per call): one HIP event pair around each call on the launch
-stream, after the warm-up calls; the mean and the median of the per-call
-durations are reported.  Inputs are synthetic (seeded, generated on the
+Timing: after the warm-up calls, K calls enqueued back to back give the
+wall-clock throughput; K more calls, each bracketed by its own HIP event
+pair on the launch stream, give the per-call device durations (mean and
+median reported).  Inputs are synthetic (seeded, generated on the
 device) and rotate among copies whose total exceeds the 256 MB Infinity
 Cache, so each step reads from HBM.  --gpus above 1 is refused: the
 benchmark runs on one GPU.
@@ -136,11 +137,14 @@ def ssd_decode_bytes(N, H, dk, dv, el):
 
 
 def time_calls(fn, n_calls, warmup, stream):
-    """Run fn(i) warmup + n_calls times.  Returns (wall seconds of the timed
-    calls, mean and median device time per call in ms).  Each timed call is
-    bracketed by its own pair of HIP events on the launch stream, so a call's
-    duration is its kernels' time on the device (plus the event overhead),
-    not the host's enqueue time, which overlaps the device work."""
+    """Run fn(i) warmup + 2 n_calls times.  Returns (wall seconds of the
+    first n_calls timed calls, mean and median device time per call in ms).
+    The first timed pass enqueues the calls back to back (its wall time is
+    the throughput figure); the second brackets each call with its own pair
+    of HIP events on the launch stream, so a call's duration is its kernels'
+    time on the device plus the event overhead, free of the host's enqueue
+    time (which the extra event records would otherwise add to the wall
+    time of short steps)."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -153,11 +157,14 @@ def time_calls(fn, n_calls, warmup, stream):
     try:
         t0 = time.perf_counter()
         for i in range(n_calls):
+            fn(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        for i in range(n_calls):
             ev[i][0].record(stream)
             fn(i)
             ev[i][1].record(stream)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
     finally:
         if gc_was_on:
             gc.enable()
@@ -451,6 +458,8 @@ def main():
                                        "ssd_decode"],
                     default="all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baselines")
+    ap.add_argument("--decode-steps", type=int, default=None,
+                    help="steps of each decode chain (default: the workload's 1000; fewer for profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
 
@@ -476,7 +485,7 @@ def main():
         # two rotating copies of the inputs (1.6 GB) keep every step's reads out of the Infinity Cache
         main_res = bench_la(head, args.steps, args.warmup, 2, lin, wl)
     if args.only in ("all", "decode"):
-        dec_res = bench_decode(wl.DECODE_BF16, lin, wl)
+        dec_res = bench_decode(wl.DECODE_BF16, lin, wl, args.decode_steps)
     if args.only in ("all", "la"):
         w = wl.LA_BF16_PREFILL
         r = bench_la(w, max(20, args.steps), args.warmup, 4, lin, wl)
@@ -522,14 +531,14 @@ def main():
     for key, wdd in (("delta_decode", wl.DELTA_DECODE_BF16), ("gated_delta_decode", wl.GATED_DELTA_DECODE_BF16)):
         if args.only not in ("all", key):
             continue
-        r = bench_delta_decode(wdd, lin, wl)
+        r = bench_delta_decode(wdd, lin, wl, args.decode_steps)
         extra[wdd.name] = {"state_update_gbs": r["gbs"], "hbm_frac": r["gbs"] / HBM_PEAK_GBS,
                            "gbs_wall_incl_launch_gaps": r["gbs_wall"], "us_per_step": 1e3 * r["event_ms_mean"],
                            "us_per_step_median": 1e3 * r["event_ms_median"],
                            "steps": r["steps"], "bytes_per_step": r["bytes_per_step"]}
     if args.only in ("all", "ssd_decode"):
         wsd = wl.SSD_DECODE_BF16
-        r = bench_ssd_decode(wsd, lin, wl)
+        r = bench_ssd_decode(wsd, lin, wl, args.decode_steps)
         extra[wsd.name] = {"state_update_gbs": r["gbs"], "hbm_frac": r["gbs"] / HBM_PEAK_GBS,
                            "gbs_wall_incl_launch_gaps": r["gbs_wall"], "us_per_step": 1e3 * r["event_ms_mean"],
                            "us_per_step_median": 1e3 * r["event_ms_median"],
