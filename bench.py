@@ -25,10 +25,11 @@ printed is one JSON object:
   decode chains of the other three rules -- each with its own roofline
   fraction.
 
-Timing: after the warm-up calls, K calls enqueued back to back give the
-wall-clock throughput; K more calls, each bracketed by its own HIP event
-pair on the launch stream, give the per-call device durations (mean and
-median reported).  Inputs are synthetic (seeded, generated on the
+Timing: after the warm-up calls, K calls enqueued back to back between one
+HIP event pair on the launch stream give the wall-clock throughput and the
+average launch duration (what a kernel trace of the calls averages); K more
+calls, each bracketed by its own event pair, give the median per call.
+Inputs are synthetic (seeded, generated on the
 device) and rotate among copies whose total exceeds the 256 MB Infinity
 Cache, so each step reads from HBM.  --gpus above 1 is refused: the
 benchmark runs on one GPU.
@@ -65,12 +66,15 @@ LA_DECODE_SOURCES = [_CSRC + f for f in ("la_decode.hip", "common.hpp", "kernels
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COUNTERS = {
     # workload name -> kernel, sources, sha256 of the sources, KiB per dispatch
-    "la_bf16_b1_h32_t65536_d64": {"kernel": "la_fused_kernel", "sources": LA_SOURCES, "sha256": None,
-                                  "fetch_kib": None, "write_kib": None},
-    "la_bf16_b4_h8_t8192_d64": {"kernel": "la_fused_kernel", "sources": LA_SOURCES, "sha256": None,
-                                "fetch_kib": None, "write_kib": None},
+    "la_bf16_b1_h32_t65536_d64": {"kernel": "la_fused_kernel", "sources": LA_SOURCES,
+                                  "sha256": "fe652223e6eb6bbecc74fbbf4e11d2279a460550984288b666c06c193eef9a26",
+                                  "fetch_kib": 611573.1, "write_kib": 327789.0},
+    "la_bf16_b4_h8_t8192_d64": {"kernel": "la_fused_kernel", "sources": LA_SOURCES,
+                                "sha256": "fe652223e6eb6bbecc74fbbf4e11d2279a460550984288b666c06c193eef9a26",
+                                "fetch_kib": 70045.8, "write_kib": 48397.0},
     "decode_bf16_n256_h32_d128_1000steps": {"kernel": "la_decode_kernel", "sources": LA_DECODE_SOURCES,
-                                            "sha256": None, "fetch_kib": None, "write_kib": None},
+                                            "sha256": "2b6264c6ad0b66bdd1f8c4a63952026813985e3f50f7c32f5ecbc80d44005f0f",
+                                            "fetch_kib": 267307.5, "write_kib": 530469.3},
 }
 
 
@@ -138,16 +142,21 @@ def ssd_decode_bytes(N, H, dk, dv, el):
 
 def time_calls(fn, n_calls, warmup, stream):
     """Run fn(i) warmup + 2 n_calls times.  Returns (wall seconds of the
-    first n_calls timed calls, mean and median device time per call in ms).
-    The first timed pass enqueues the calls back to back (its wall time is
-    the throughput figure); the second brackets each call with its own pair
-    of HIP events on the launch stream, so a call's duration is its kernels'
-    time on the device plus the event overhead, free of the host's enqueue
-    time (which the extra event records would otherwise add to the wall
-    time of short steps)."""
+    first n_calls timed calls, mean device time per call in ms over that
+    region, and the mean and median of per-call device times in ms).
+
+    The first timed pass enqueues the calls back to back between one pair of
+    HIP events on the launch stream: its wall time is the throughput figure
+    and its event time divided by the calls is the average launch duration
+    (the gaps between consecutive launches included, about a microsecond),
+    which is what a kernel trace of the same calls averages.  The second
+    pass brackets each call with its own event pair, for the median of at
+    least 20 repetitions; each pair adds a few microseconds of its own, so
+    those per-call figures run a little above the trace's."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
     # A garbage-collection pause while the calls are being queued would leave
     # the device idle inside the timed region.
@@ -156,8 +165,10 @@ def time_calls(fn, n_calls, warmup, stream):
     gc.disable()
     try:
         t0 = time.perf_counter()
+        start.record(stream)
         for i in range(n_calls):
             fn(i)
+        end.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         for i in range(n_calls):
@@ -170,7 +181,7 @@ def time_calls(fn, n_calls, warmup, stream):
             gc.enable()
     d = sorted(a.elapsed_time(b) for a, b in ev)
     med = d[len(d) // 2] if len(d) % 2 else 0.5 * (d[len(d) // 2 - 1] + d[len(d) // 2])
-    return wall, sum(d) / len(d), med
+    return wall, start.elapsed_time(end) / n_calls, sum(d) / len(d), med
 
 
 def bench_la(w, steps, warmup, copies, lin, wl):
@@ -187,10 +198,10 @@ def bench_la(w, steps, warmup, copies, lin, wl):
         lin.la_forward(q, k, v, eps=1e-6, o=outs[i % copies], S_out=S, z_out=z, workspace=ws)
 
     stream = torch.cuda.current_stream(dev)
-    wall, mean_ms, med_ms = time_calls(step, steps, warmup, stream)
+    wall, mean_ms, pc_mean, med_ms = time_calls(step, steps, warmup, stream)
     nbytes = la_bytes(w.B, w.H, w.T, w.dk, w.dv, el)
     return {
-        "wall_s": wall, "ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms,
+        "wall_s": wall, "ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "event_ms_mean_per_call": pc_mean,
         "tokens_per_s": w.B * w.T * steps / wall,
         "bytes": nbytes, "flops": la_flops(w.B, w.H, w.T, w.dk, w.dv),
         "gbs": nbytes / (mean_ms * 1e-3) / 1e9,
@@ -217,10 +228,10 @@ def bench_delta(w, steps, warmup, copies, lin, wl):
             q, k, v, beta = sets[i % copies]
             lin.delta_forward(q, k, v, beta, o=outs[i % copies], S_out=S, workspace=ws)
 
-    wall, mean_ms, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
+    wall, mean_ms, pc_mean, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
     nbytes = delta_bytes(w.B, w.H, w.T, w.dk, w.dv, el, gated)
     fl = delta_flops(w.B, w.H, w.T, w.dk, w.dv)
-    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "tokens_per_s": w.B * w.T * steps / wall,
+    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "event_ms_mean_per_call": pc_mean, "tokens_per_s": w.B * w.T * steps / wall,
             "bytes": nbytes, "flops": fl, "gbs": nbytes / (mean_ms * 1e-3) / 1e9,
             "tflops": fl / (mean_ms * 1e-3) / 1e12}
 
@@ -238,10 +249,10 @@ def bench_ssd(w, steps, warmup, copies, lin, wl):
         q, k, v, alpha = sets[i % copies]
         lin.ssd_forward(q, k, v, alpha, o=outs[i % copies], S_out=S, workspace=ws)
 
-    wall, mean_ms, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
+    wall, mean_ms, pc_mean, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
     nbytes = ssd_bytes(w.B, w.H, w.T, w.dk, w.dv, el)
     fl = ssd_flops(w.B, w.H, w.T, w.dk, w.dv)
-    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "tokens_per_s": w.B * w.T * steps / wall,
+    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "event_ms_mean_per_call": pc_mean, "tokens_per_s": w.B * w.T * steps / wall,
             "bytes": nbytes, "flops": fl, "gbs": nbytes / (mean_ms * 1e-3) / 1e9,
             "tflops": fl / (mean_ms * 1e-3) / 1e12}
 
@@ -256,9 +267,9 @@ def bench_ssd_decode(w, lin, wl, n_steps=None):
         j = i % w.T
         lin.ssd_decode_step(Q[j], K[j], V[j], At[j], S, o=o)
 
-    wall, mean_ms, med_ms = time_calls(step, n, 10, torch.cuda.current_stream(dev))
+    wall, mean_ms, pc_mean, med_ms = time_calls(step, n, 10, torch.cuda.current_stream(dev))
     per = ssd_decode_bytes(w.B, w.H, w.dk, w.dv, 2)
-    return {"steps": n, "ms_per_step": 1e3 * wall / n, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "bytes_per_step": per,
+    return {"steps": n, "ms_per_step": 1e3 * wall / n, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "event_ms_mean_per_call": pc_mean, "bytes_per_step": per,
             "gbs_wall": per * n / wall / 1e9, "gbs": per / (mean_ms * 1e-3) / 1e9}
 
 
@@ -280,9 +291,9 @@ def bench_la_backward(w, steps, warmup, copies, lin, wl):
         dq, dk, dv = grads[i % copies]
         lin.la_backward(q, k, v, dO, eps=1e-6, dq=dq, dk=dk, dv=dv, return_state_grads=False, workspace=ws)
 
-    wall, mean_ms, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
+    wall, mean_ms, pc_mean, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
     nbytes = la_backward_bytes(w.B, w.H, w.T, w.dk, w.dv, 2)
-    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "tokens_per_s": w.B * w.T * steps / wall,
+    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "event_ms_mean_per_call": pc_mean, "tokens_per_s": w.B * w.T * steps / wall,
             "bytes": nbytes, "gbs": nbytes / (mean_ms * 1e-3) / 1e9}
 
 
@@ -311,9 +322,9 @@ def bench_delta_backward(w, steps, warmup, copies, lin, wl):
         dq, dk, dv = grads[i % copies]
         lin.delta_backward(q, k, v, beta, dO, alpha, dq=dq, dk=dk, dv=dv, return_state_grad=False, workspace=ws)
 
-    wall, mean_ms, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
+    wall, mean_ms, pc_mean, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
     nbytes = delta_backward_bytes(w.B, w.H, w.T, w.dk, w.dv, 2, gated)
-    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "tokens_per_s": w.B * w.T * steps / wall,
+    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "event_ms_mean_per_call": pc_mean, "tokens_per_s": w.B * w.T * steps / wall,
             "bytes": nbytes, "gbs": nbytes / (mean_ms * 1e-3) / 1e9}
 
 
@@ -330,10 +341,10 @@ def bench_la_packed(w, steps, warmup, lin, wl):
     def step(i):
         lin.la_forward_packed(q, k, v, cu_dev, eps=1e-6, cu_seqlens_host=cu, o=o, S_out=S, z_out=z, workspace=ws)
 
-    wall, mean_ms, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
+    wall, mean_ms, pc_mean, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
     nbytes = la_bytes(1, w.H, w.T, w.dk, w.dv, 2) + (w.B - 1) * w.H * (w.dk * w.dv + w.dk) * 4
     lengths = (cu[1:] - cu[:-1]).tolist()
-    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "tokens_per_s": w.T * steps / wall,
+    return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "event_ms_mean_per_call": pc_mean, "tokens_per_s": w.T * steps / wall,
             "gbs": nbytes / (mean_ms * 1e-3) / 1e9, "requests": w.B, "min_len": min(lengths),
             "max_len": max(lengths)}
 
@@ -347,9 +358,9 @@ def bench_decode(w, lin, wl, n_steps=None):
     def step(i):
         lin.la_decode_step(Q[i % w.T], K[i % w.T], V[i % w.T], S, z, eps=1e-6, o=o)
 
-    wall, mean_ms, med_ms = time_calls(step, n, 10, torch.cuda.current_stream(dev))
+    wall, mean_ms, pc_mean, med_ms = time_calls(step, n, 10, torch.cuda.current_stream(dev))
     per = decode_bytes(w.B, w.H, w.dk, w.dv, 2)
-    return {"steps": n, "ms_per_step": 1e3 * wall / n, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "bytes_per_step": per,
+    return {"steps": n, "ms_per_step": 1e3 * wall / n, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "event_ms_mean_per_call": pc_mean, "bytes_per_step": per,
             "gbs_wall": per * n / wall / 1e9, "gbs": per / (mean_ms * 1e-3) / 1e9}
 
 
@@ -371,9 +382,9 @@ def bench_delta_decode(w, lin, wl, n_steps=None):
         else:
             lin.delta_decode_step(Q[j], K[j], V[j], Bt[j], S, o=o)
 
-    wall, mean_ms, med_ms = time_calls(step, n, 10, torch.cuda.current_stream(dev))
+    wall, mean_ms, pc_mean, med_ms = time_calls(step, n, 10, torch.cuda.current_stream(dev))
     per = delta_decode_bytes(w.B, w.H, w.dk, w.dv, 2, gated)
-    return {"steps": n, "ms_per_step": 1e3 * wall / n, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "bytes_per_step": per,
+    return {"steps": n, "ms_per_step": 1e3 * wall / n, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "event_ms_mean_per_call": pc_mean, "bytes_per_step": per,
             "gbs_wall": per * n / wall / 1e9, "gbs": per / (mean_ms * 1e-3) / 1e9}
 
 
@@ -444,8 +455,9 @@ def hbm_roofline(nbytes, r, workload, kernel):
             "traffic": traffic_bytes(workload),
             "traffic_unit": "HBM bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
             "kernel": kernel, "algorithmic_bytes_per_launch": nbytes,
-            "event_ms_mean": r["event_ms_mean"], "event_ms_median": r["event_ms_median"],
-            "frac_at_median": nbytes / (r["event_ms_median"] * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            "event_ms_mean": r["event_ms_mean"],
+            "event_ms_per_call": {"median": r["event_ms_median"], "mean": r["event_ms_mean_per_call"],
+                                  "note": "one event pair per call; each pair adds a few microseconds"}}
 
 
 def main():
