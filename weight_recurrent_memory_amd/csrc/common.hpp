@@ -94,6 +94,21 @@ template <> struct Elem<bf16_t> {
 
 // ---------------------------------------------------------------- MFMA
 
+// Group-permuted row layout of a bf16 LDS matrix read as row fragments.  A
+// fragment gives lane group g the contraction columns 4g..4g+3 and
+// 16+4g..16+4g+3 of a 32-column block, two 8-byte pieces 32 bytes apart; on
+// gfx950 such paired reads move about half the bytes per clock of one
+// 16-byte read per lane and conflict two ways at the 8-element padding.
+// Storing the 4-column groups of every 32-column block in the order 0, 4, 1,
+// 5, 2, 6, 3, 7 makes the two pieces adjacent: physical column of logical
+// column c (whole 4-column groups stay contiguous, so 8-byte stores and
+// transpose reads of single groups still work).  With a row stride of D + 16
+// elements the 16-byte reads are conflict-free.
+__device__ __forceinline__ constexpr int pcol(int c) {
+    return (c & ~31) + 4 * (2 * ((c >> 2) & 3) + ((c >> 4) & 1)) + (c & 3);
+}
+
+
 // Operand element type in LDS: bf16 for bf16 inputs, fp32 for fp32 inputs.
 template <typename TIn> struct Mma;
 
@@ -108,6 +123,11 @@ template <> struct Mma<bf16_t> {
         v4bf lo = *reinterpret_cast<const v4bf*>(row + 4 * g);
         v4bf hi = *reinterpret_cast<const v4bf*>(row + 16 + 4 * g);
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    // The same fragment from a row stored in the group-permuted layout (pcol
+    // below): one 16-byte read.
+    static __device__ __forceinline__ frag load_p(const op_t* row, int g) {
+        return *reinterpret_cast<const frag*>(row + 8 * g);
     }
     // Fragment whose contraction index runs down the ROWS of a row-major
     // [k][n] LDS matrix (row stride ld elements): rows k0..k0+31, columns
@@ -301,17 +321,52 @@ __device__ __forceinline__ void stage_rows_phi(const ChunkRegs<TIn, D, NT>& cr, 
     }
 }
 
+// Row layout of a bf16 LDS matrix: row stride LD elements, natural or
+// group-permuted (pcol).  frag() reads the row fragment of contraction block
+// k0 (a multiple of 32) of one row; tr() the transposed fragment of rows
+// k0..k0+31, columns n0..n0+15 (n0 a multiple of 16).  Each source lane of
+// a transpose read fetches one whole 4-column group, so on permuted rows it
+// only points at that group's place; the exchange between lanes is the same.
+template <int LD_, bool PERM_ = false>
+struct RowLayout {
+    static constexpr int LD = LD_;
+    static constexpr bool PERM = PERM_;
+    static_assert(!PERM || LD % 32 == 16, "permuted rows: 16 elements of padding past a multiple of 32");
+    static __device__ __forceinline__ int at(int row, int col) { return row * LD + (PERM ? pcol(col) : col); }
+    static __device__ __forceinline__ Mma<bf16_t>::frag frag(const __bf16* X, int row, int k0, int g) {
+        if constexpr (PERM) return Mma<bf16_t>::load_p(X + row * LD + k0, g);
+        else return Mma<bf16_t>::load(X + row * LD + k0, g);
+    }
+    static __device__ __forceinline__ Mma<bf16_t>::frag tr(const __bf16* X, int k0, int n0, int lane) {
+        if constexpr (!PERM) {
+            return Mma<bf16_t>::load_tr(X, LD, k0, n0, lane);
+        } else {
+            typedef short v4s __attribute__((ext_vector_type(4)));
+            typedef __attribute__((address_space(3))) v4s lds_v4s;
+            const int g = lane >> 4, j = lane & 15;
+            const __bf16* p0 = X + (k0 + 4 * g + (j >> 2)) * LD + pcol(n0 + 4 * (j & 3));
+            const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p0));
+            const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p0 + 16 * LD));
+            return __builtin_bit_cast(Mma<bf16_t>::frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    }
+};
+
 // Raw copy of a staged chunk into LDS (operand type == input type).  SPLIT8:
 // two 8-byte stores per 16 bytes, for row strides that keep rows only
-// 8-byte aligned.
-template <typename TIn, int D, int NT, bool SPLIT8 = false>
+// 8-byte aligned.  PERM: rows in the group-permuted layout (pcol; bf16).
+template <typename TIn, int D, int NT, bool SPLIT8 = false, bool PERM = false>
 __device__ __forceinline__ void stage_rows_raw(const ChunkRegs<TIn, D, NT>& cr, int tid,
                                                typename Mma<TIn>::op_t* rm, int ld) {
+    static_assert(!PERM || sizeof(TIn) == 2, "the permuted layout is for bf16 rows");
 #pragma unroll
     for (int j = 0; j < ChunkRegs<TIn, D, NT>::NV; ++j) {
         const int row = ChunkRegs<TIn, D, NT>::row_of(j, tid);
         const int col = ChunkRegs<TIn, D, NT>::col_of(j, tid);
-        if constexpr (SPLIT8) {
+        if constexpr (PERM) {
+            *reinterpret_cast<uint2*>(rm + row * ld + pcol(col)) = make_uint2(cr.r[j].x, cr.r[j].y);
+            *reinterpret_cast<uint2*>(rm + row * ld + pcol(col + 4)) = make_uint2(cr.r[j].z, cr.r[j].w);
+        } else if constexpr (SPLIT8) {
             uint2* d = reinterpret_cast<uint2*>(rm + row * ld + col);
             d[0] = make_uint2(cr.r[j].x, cr.r[j].y);
             d[1] = make_uint2(cr.r[j].z, cr.r[j].w);

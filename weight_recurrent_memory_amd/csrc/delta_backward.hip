@@ -34,9 +34,13 @@
 // Launches (uniform batches; G segments of L tokens per sequence):
 //   1-3  the forward sweep: segment maps, composition, then every chunk's
 //        entering state S_c as bf16 tiles (delta_prefill.hip)
-//   4    reverse chunk chain over segments 1..G-1 with state-gradient columns
-//        started at 0 (with dO) and at I (without): the maps c_g and M_g^T
-//   5    reverse composition: G_end(g-1) = M_g^T G_end(g) + c_g from dS_T
+//   4    reverse chunk chain over segments 1..G-1 with the state gradient
+//        started at 0: the constant parts c_g of the segments' reverse maps
+//   5    reverse composition: G_end(g-1) = M_g^T G_end(g) + c_g from dS_T.
+//        The G'-dependent part of dS above is A_c^T G' with A_c = gamma_C I -
+//        K^T diag(beta Gc) T diag(gamma) K, the forward's state transition:
+//        a segment's reverse map is the transpose of its forward map M_g,
+//        which the forward sweep computes for every segment
 //   6    reverse chunk chain from G_end(g): every chunk's G' as bf16 tiles,
 //        and dS_0 from segment 0
 //   7    every chunk independently: dq, dk, dv, dbeta, dalpha from (S_c, G'_c)
@@ -59,17 +63,25 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 template <int DK, int DV, bool MAP, bool GATED>
 struct RC {
-    static constexpr int LQ = DK + 8, LV = DV + 8;
-    static constexpr int KS = CH * LQ * 2, QS = CH * LQ * 2, OS = CH * LV * 2;
-    static constexpr int TS = CH * LT * 2, PS = CH * LT * 2;
+    // LDS layouts by use (gfx950 LDS probes): K is staged twice, group-
+    // permuted for its row fragments (K G and P's builder) and natural for
+    // the transpose loads of K^T dR; dO, P and T are read only with
+    // transpose loads (natural, padded by 16, where those are
+    // conflict-free); Q is read both ways and keeps the 8-element padding.
+    using KF = RowLayout<DK + 16, true>;
+    using KT = RowLayout<DK + 16>;
+    using QL = RowLayout<DK + 8>;
+    using OL = RowLayout<DV + 16>;
+    using PL = RowLayout<CH + 16>;  // P and T
+    static constexpr int KFS = CH * KF::LD * 2, KTS = CH * KT::LD * 2, QS = CH * QL::LD * 2, OS = CH * OL::LD * 2;
+    static constexpr int TS = CH * PL::LD * 2, PS = CH * PL::LD * 2;
     static constexpr int BS = CH * 4 * (GATED ? 4 : 1);
-    static constexpr int TOTAL = KS + QS + OS + TS + PS + BS;
+    static constexpr int TOTAL = KFS + KTS + QS + OS + TS + PS + BS;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
     static constexpr int XR = DK / 16;
-    // Column tiles of the state gradient: NCN carry dO (c_g, or the gradient
-    // itself); MAP adds DK/16 identity-started columns without dO (M_g^T).
+    // Column tiles of the state gradient (c_g, or the gradient itself)
     static constexpr int NCN = DV / 16;
-    static constexpr int NCT = MAP ? NCN + DK / 16 : NCN;
+    static constexpr int NCT = NCN;
     static constexpr int SLOTS = (NCT + NWV - 1) / NWV;
 };
 
@@ -84,14 +96,20 @@ template <int DK, int DV, bool MAP, bool GATED>
 __global__ __launch_bounds__(NT) void dlb_chain_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ beta,
     const float* __restrict__ alpha, const bf16_t* __restrict__ dO, const float* __restrict__ g_end,
-    float* __restrict__ map_c, float* __restrict__ map_mt, bf16_t* __restrict__ gst, float* __restrict__ dS0,
+    float* __restrict__ map_c, bf16_t* __restrict__ gst, float* __restrict__ dS0,
     const bf16_t* __restrict__ trec, SegMap sm) {
     using Y = RC<DK, DV, MAP, GATED>;
     using M = Mma<bf16_t>;
-    constexpr int LQ = Y::LQ, LV = Y::LV, XR = Y::XR, SLOTS = Y::SLOTS;
+    using KF = typename Y::KF;
+    using KT = typename Y::KT;
+    using QL = typename Y::QL;
+    using OL = typename Y::OL;
+    using PL = typename Y::PL;
+    constexpr int XR = Y::XR, SLOTS = Y::SLOTS;
     __shared__ __align__(16) unsigned char smem[Y::TOTAL];
     unsigned char* sp = smem;
-    __bf16* Ks = reinterpret_cast<__bf16*>(sp);  sp += Y::KS;
+    __bf16* Kf = reinterpret_cast<__bf16*>(sp);  sp += Y::KFS;
+    __bf16* Kt = reinterpret_cast<__bf16*>(sp);  sp += Y::KTS;
     __bf16* Qs = reinterpret_cast<__bf16*>(sp);  sp += Y::QS;
     __bf16* Os = reinterpret_cast<__bf16*>(sp);  sp += Y::OS;
     __bf16* Ts = reinterpret_cast<__bf16*>(sp);  sp += Y::TS;
@@ -103,9 +121,7 @@ __global__ __launch_bounds__(NT) void dlb_chain_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int w = wave_id(tid);
-    // The wave index's range lets per-wave tile guards fold away; the map
-    // variant is left as it is (folded, its code spilled registers).
-    if constexpr (!MAP) __builtin_assume(w >= 0 && w < NT / 64);
+    __builtin_assume(w >= 0 && w < NT / 64);  // lets per-wave tile guards fold away
     const int G1 = MAP ? sm.G - 1 : sm.G;
     const int vh = blockIdx.x / G1;  // sequence * H + head
     const int seg = blockIdx.x % G1 + (MAP ? 1 : 0);
@@ -118,19 +134,13 @@ __global__ __launch_bounds__(NT) void dlb_chain_kernel(
 #pragma unroll
     for (int j = 0; j < SLOTS; ++j) {
         const int id = w + NWV * j;
-        const bool is_m = id >= Y::NCN;
-        const int col = 16 * (is_m ? id - Y::NCN : id) + li;
+        const int col = 16 * id + li;
 #pragma unroll
         for (int i = 0; i < XR; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * i + 4 * g + r;
-                float x = 0.f;
-                if (id < Y::NCT) {
-                    if constexpr (MAP) x = (is_m && row == col) ? 1.f : 0.f;
-                    else x = g_end[(slot * DK + row) * DV + col];
-                }
-                X[j][i][r] = x;
+                X[j][i][r] = (!MAP && id < Y::NCT) ? g_end[(slot * DK + row) * DV + col] : 0.f;
             }
     }
 
@@ -158,7 +168,7 @@ __global__ __launch_bounds__(NT) void dlb_chain_kernel(
     };
     const int c_last = t0 + ((t_end - 1 - t0) / CH) * CH;
     load_chunk(c_last);
-    dchunk::clear_upper(Ps, tid);  // (the records carry T's zero blocks)
+    dchunk::clear_upper<PL>(Ps, tid);  // (the records carry T's zero blocks)
     for (int c0 = c_last; c0 >= t0; c0 -= CH) {
         // Lane indices from an opaque copy, re-derived every chunk: the many
         // per-lane LDS addresses built from them then live next to their uses
@@ -177,26 +187,27 @@ __global__ __launch_bounds__(NT) void dlb_chain_kernel(
                 for (int i = 0; i < XR; ++i) dchunk::put_tile(gst + dchunk::tile_offset<DK, DV>(ci, id, i, lane), X[j][i]);
             }
         }
-        stage_rows_raw<bf16_t, DK, NT>(kr, tid, Ks, LQ);
-        stage_rows_raw<bf16_t, DK, NT>(qr, tid, Qs, LQ);
-        stage_rows_raw<bf16_t, DV, NT>(orr, tid, Os, LV);
-        dchunk::stage_rec(Ts, tnext, tid);
+        stage_rows_raw<bf16_t, DK, NT, false, true>(kr, tid, Kf, KF::LD);
+        stage_rows_raw<bf16_t, DK, NT>(kr, tid, Kt, KT::LD);
+        stage_rows_raw<bf16_t, DK, NT>(qr, tid, Qs, QL::LD);
+        stage_rows_raw<bf16_t, DV, NT>(orr, tid, Os, OL::LD);
+        dchunk::stage_rec<PL>(Ts, tnext, tid);
         if (tid < CH) {
             Bs[tid] = bf16_to_f32(bnext);
             if constexpr (GATED) dchunk::gate_prefix(__uint_as_float(anext), tid, n, Gl, Ge, Gc);
         }
         if (c0 - CH >= t0) load_chunk(c0 - CH);
         __syncthreads();
-        dchunk::build_P<DK, GATED>(Ks, Qs, Gl, Ps, w, g, li);
+        dchunk::build_P<DK, GATED, false, KF, QL, PL>(Kf, Qs, Gl, Ps, w, g, li);
         __syncthreads();
         if constexpr (GATED) {  // diag(gamma) Q for the dO term of the state gradient
             for (int e = tid; e < CH * DK / 8; e += NT) {
                 const int row = e / (DK / 8), col = (e % (DK / 8)) * 8;
-                v8bf x = *reinterpret_cast<const v8bf*>(&Qs[row * LQ + col]);
+                v8bf x = *reinterpret_cast<const v8bf*>(&Qs[row * QL::LD + col]);
                 const float s = Ge[row];
 #pragma unroll
                 for (int u = 0; u < 8; ++u) x[u] = M::cvt((float)x[u] * s);
-                *reinterpret_cast<v8bf*>(&Qs[row * LQ + col]) = x;
+                *reinterpret_cast<v8bf*>(&Qs[row * QL::LD + col]) = x;
             }
             __syncthreads();
         }
@@ -205,21 +216,18 @@ __global__ __launch_bounds__(NT) void dlb_chain_kernel(
         for (int j = 0; j < SLOTS; ++j) {
             const int id = w + NWV * j;
             if (id >= Y::NCT) continue;
-            const bool is_c = id < Y::NCN;
             v4f dU[4];
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 v4f acc = zero4(), kg = zero4();
-                if (is_c) {
 #pragma unroll
-                    for (int kb = 0; kb < CH / 32; ++kb) {
-                        if (32 * kb + 31 < 16 * tt) continue;  // P^T is upper triangular
-                        M::mma(acc, M::load_tr(Ps, LT, 32 * kb, 16 * tt, lane), M::load_tr(Os, LV, 32 * kb, 16 * id, lane));
-                    }
+                for (int kb = 0; kb < CH / 32; ++kb) {
+                    if (32 * kb + 31 < 16 * tt) continue;  // P^T is upper triangular
+                    M::mma(acc, PL::tr(Ps, 32 * kb, 16 * tt, lane), OL::tr(Os, 32 * kb, 16 * id, lane));
                 }
 #pragma unroll
                 for (int kb = 0; kb < DK / 32; ++kb)
-                    M::mma(kg, M::load(&Ks[(16 * tt + li) * LQ + 32 * kb], g), M::from_tiles(X[j][2 * kb], X[j][2 * kb + 1]));
+                    M::mma(kg, KF::frag(Kf, 16 * tt + li, 32 * kb, g), M::from_tiles(X[j][2 * kb], X[j][2 * kb + 1]));
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int s = 16 * tt + 4 * g + r;
@@ -233,7 +241,7 @@ __global__ __launch_bounds__(NT) void dlb_chain_kernel(
 #pragma unroll
                 for (int kb = 0; kb < CH / 32; ++kb) {
                     if (32 * kb + 31 < 16 * tt) continue;  // T^T is upper triangular
-                    M::mma(dR[tt], M::load_tr(Ts, LT, 32 * kb, 16 * tt, lane), M::from_tiles(dU[2 * kb], dU[2 * kb + 1]));
+                    M::mma(dR[tt], PL::tr(Ts, 32 * kb, 16 * tt, lane), M::from_tiles(dU[2 * kb], dU[2 * kb + 1]));
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) dR[tt][r] *= GATED ? -Ge[16 * tt + 4 * g + r] : -1.f;
@@ -245,14 +253,12 @@ __global__ __launch_bounds__(NT) void dlb_chain_kernel(
             }
 #pragma unroll
             for (int i = 0; i < XR; ++i) {
-                if (is_c) {
-#pragma unroll
-                    for (int kb = 0; kb < CH / 32; ++kb)
-                        M::mma(X[j][i], M::load_tr(Qs, LQ, 32 * kb, 16 * i, lane), M::load_tr(Os, LV, 32 * kb, 16 * id, lane));
-                }
 #pragma unroll
                 for (int kb = 0; kb < CH / 32; ++kb)
-                    M::mma(X[j][i], M::load_tr(Ks, LQ, 32 * kb, 16 * i, lane), M::from_tiles(dR[2 * kb], dR[2 * kb + 1]));
+                    M::mma(X[j][i], QL::tr(Qs, 32 * kb, 16 * i, lane), OL::tr(Os, 32 * kb, 16 * id, lane));
+#pragma unroll
+                for (int kb = 0; kb < CH / 32; ++kb)
+                    M::mma(X[j][i], KT::tr(Kt, 32 * kb, 16 * i, lane), M::from_tiles(dR[2 * kb], dR[2 * kb + 1]));
             }
         }
         __syncthreads();
@@ -262,23 +268,18 @@ __global__ __launch_bounds__(NT) void dlb_chain_kernel(
     for (int j = 0; j < SLOTS; ++j) {
         const int id = w + NWV * j;
         if (id >= Y::NCT) continue;
-        const bool is_m = id >= Y::NCN;
         float* dst;
-        int ld, col;
         if constexpr (MAP) {
-            dst = is_m ? map_mt + slot * DK * DK : map_c + slot * DK * DV;
-            ld = is_m ? DK : DV;
-            col = 16 * (is_m ? id - Y::NCN : id) + li;
+            dst = map_c + slot * DK * DV;
         } else {
             if (seg != 0 || !dS0) continue;
             dst = dS0 + (long)vh * DK * DV;
-            ld = DV;
-            col = 16 * id + li;
         }
+        const int col = 16 * id + li;
 #pragma unroll
         for (int i = 0; i < XR; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(16 * i + 4 * g + r) * ld + col] = X[j][i][r];
+            for (int r = 0; r < 4; ++r) dst[(16 * i + 4 * g + r) * DV + col] = X[j][i][r];
     }
 }
 
@@ -286,15 +287,18 @@ __global__ __launch_bounds__(NT) void dlb_chain_kernel(
 
 template <int DK, int DV, bool GATED>
 struct GR {
-    // row strides: K, Q and dO are also read with transpose loads (padding
-    // 8); dR, U (staged from V with 8-byte stores) and the S / G' rows are
-    // read only as row fragments or scalars (padding 4: a fragment's rows
-    // start 2 words apart)
-    static constexpr int LQ = DK + 8, LV = DV + 8, LR = DV + 4, LB = DV + 4, LU = DV + 4;
-    static constexpr int KS = CH * LQ * 2, QS = CH * LQ * 2, OS = CH * LV * 2, US = CH * LU * 2;
-    static constexpr int RS = CH * LR * 2;   // dR rows
-    static constexpr int BG = DK * LB * 2;   // G' or S rows
-    static constexpr int TS = CH * LT * 2, PS = CH * LT * 2;
+    // Every bf16 matrix here is read as row fragments, most also with
+    // transpose loads or as single elements: all group-permuted with 16
+    // elements of padding (pcol), where fragment reads are single
+    // conflict-free 16-byte reads and transpose reads cost what they do on
+    // natural rows padded by 8 (gfx950 LDS probes).
+    using KL = RowLayout<DK + 16, true>;  // K, Q
+    using VL = RowLayout<DV + 16, true>;  // dO, V then U, dR, G' or S (DK rows)
+    using PL = RowLayout<CH + 16, true>;  // T then E2, P then E1
+    static constexpr int KS = CH * KL::LD * 2, QS = CH * KL::LD * 2, OS = CH * VL::LD * 2, US = CH * VL::LD * 2;
+    static constexpr int RS = CH * VL::LD * 2;   // dR rows
+    static constexpr int BG = DK * VL::LD * 2;   // G' or S rows
+    static constexpr int TS = CH * PL::LD * 2, PS = CH * PL::LD * 2;
     // beta; per-wave partials of dbeta (rows, then E2 tiles) and of dL/dl;
     // per-wave partial sums; gates
     static constexpr int SM = (CH + NWV * CH + 10 * 16 + NWV * CH + 2 * NWV + (GATED ? 3 * CH : 0)) * 4;
@@ -323,7 +327,10 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
     const bf16_t* __restrict__ trec, int HT, int T) {
     using Y = GR<DK, DV, GATED>;
     using M = Mma<bf16_t>;
-    constexpr int LQ = Y::LQ, LV = Y::LV, LR = Y::LR, LB = Y::LB, LU = Y::LU, XR = Y::XR, TPW = Y::TPW;
+    using KL = typename Y::KL;
+    using VL = typename Y::VL;
+    using PL = typename Y::PL;
+    constexpr int XR = Y::XR, TPW = Y::TPW;
     __shared__ __align__(16) unsigned char smem[Y::TOTAL];
     unsigned char* sp = smem;
     __bf16* Ks = reinterpret_cast<__bf16*>(sp);  sp += Y::KS;
@@ -390,7 +397,7 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
         load_rows(ci);
         load_tiles(ci);
     }
-    dchunk::clear_upper(Ps, tid);  // (the records carry T's zero blocks; E2 and E1 reuse lower tiles only)
+    dchunk::clear_upper<PL>(Ps, tid);  // (the records carry T's zero blocks; E2 and E1 reuse lower tiles only)
     for (; ci < total; ci += gridDim.x) {
     // lane indices re-derived per chunk from an opaque copy, so the per-lane
     // LDS addresses are not hoisted out of the loop and held (spilled)
@@ -403,11 +410,11 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
     const long row0 = (long)vh * T + c0;
     const long cn = ci + gridDim.x;  // the next chunk of this workgroup
 
-    stage_rows_raw<bf16_t, DK, NT>(kr, tid, Ks, LQ);
-    stage_rows_raw<bf16_t, DK, NT>(qr, tid, Qs, LQ);
-    stage_rows_raw<bf16_t, DV, NT, true>(vr, tid, Us, LU);
-    stage_rows_raw<bf16_t, DV, NT>(orr, tid, Os, LV);
-    dchunk::stage_rec(Ts, tnext, tid);
+    stage_rows_raw<bf16_t, DK, NT, false, true>(kr, tid, Ks, KL::LD);
+    stage_rows_raw<bf16_t, DK, NT, false, true>(qr, tid, Qs, KL::LD);
+    stage_rows_raw<bf16_t, DV, NT, false, true>(vr, tid, Us, VL::LD);
+    stage_rows_raw<bf16_t, DV, NT, false, true>(orr, tid, Os, VL::LD);
+    dchunk::stage_rec<PL>(Ts, tnext, tid);
     for (int e = tid; e < NWV * CH; e += NT) pL[e] = 0.f;  // waves write only their tokens
     if (tid < CH) {
         Bs[tid] = bf16_to_f32(bnext);
@@ -416,7 +423,7 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
     if (cn < total) load_rows(cn);
     __syncthreads();
     v4f kk[2];  // raw K K^T of the lower tiles w and w + 8, for dbeta
-    dchunk::build_P<DK, GATED, true>(Ks, Qs, Gl, Ps, w, g, li, kk);
+    dchunk::build_P<DK, GATED, true, KL, KL, PL>(Ks, Qs, Gl, Ps, w, g, li, kk);
     __syncthreads();
 
     // ---- column phase
@@ -428,11 +435,11 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
             v4f ks = zero4();
 #pragma unroll
             for (int kb = 0; kb < DK / 32; ++kb)
-                M::mma(ks, M::load(&Ks[(16 * tt + li) * LQ + 32 * kb], g), dchunk::tile_frag(st[2 * kb], st[2 * kb + 1]));
+                M::mma(ks, KL::frag(Ks, 16 * tt + li, 32 * kb, g), dchunk::tile_frag(st[2 * kb], st[2 * kb + 1]));
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int s = 16 * tt + 4 * g + r;
-                U[tt][r] = (float)Us[s * LU + col] - (GATED ? Ge[s] : 1.f) * ks[r];
+                U[tt][r] = (float)Us[VL::at(s, col)] - (GATED ? Ge[s] : 1.f) * ks[r];
             }
         }
         v4f Uo[4];
@@ -442,7 +449,7 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
 #pragma unroll
             for (int kb = 0; kb < CH / 32; ++kb) {
                 if (32 * kb > 16 * tt + 15) continue;  // T is lower triangular
-                M::mma(Uo[tt], M::load(&Ts[(16 * tt + li) * LT + 32 * kb], g), M::from_tiles(U[2 * kb], U[2 * kb + 1]));
+                M::mma(Uo[tt], PL::frag(Ts, 16 * tt + li, 32 * kb, g), M::from_tiles(U[2 * kb], U[2 * kb + 1]));
             }
         }
         v4f dUb[4];
@@ -452,11 +459,11 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
 #pragma unroll
             for (int kb = 0; kb < CH / 32; ++kb) {
                 if (32 * kb + 31 < 16 * tt) continue;
-                M::mma(acc, M::load_tr(Ps, LT, 32 * kb, 16 * tt, lane), M::load_tr(Os, LV, 32 * kb, 16 * w, lane));
+                M::mma(acc, PL::tr(Ps, 32 * kb, 16 * tt, lane), VL::tr(Os, 32 * kb, 16 * w, lane));
             }
 #pragma unroll
             for (int kb = 0; kb < DK / 32; ++kb)
-                M::mma(kg, M::load(&Ks[(16 * tt + li) * LQ + 32 * kb], g), dchunk::tile_frag(gt[2 * kb], gt[2 * kb + 1]));
+                M::mma(kg, KL::frag(Ks, 16 * tt + li, 32 * kb, g), dchunk::tile_frag(gt[2 * kb], gt[2 * kb + 1]));
 #pragma unroll
             for (int r = 0; r < 4; ++r) dUb[tt][r] = acc[r] + (GATED ? Gc[16 * tt + 4 * g + r] : 1.f) * kg[r];
         }
@@ -475,7 +482,7 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
 #pragma unroll
             for (int kb = 0; kb < CH / 32; ++kb) {
                 if (32 * kb + 31 < 16 * tt) continue;
-                M::mma(dR[tt], M::load_tr(Ts, LT, 32 * kb, 16 * tt, lane), M::from_tiles(dUb[2 * kb], dUb[2 * kb + 1]));
+                M::mma(dR[tt], PL::tr(Ts, 32 * kb, 16 * tt, lane), M::from_tiles(dUb[2 * kb], dUb[2 * kb + 1]));
             }
         }
         if constexpr (GATED) {  // <G', S> over this wave's columns
@@ -496,23 +503,23 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int s = 16 * tt + 4 * g + r;
-                Us[s * LU + col] = M::cvt(Uo[tt][r]);
-                Rs[s * LR + col] = M::cvt(dR[tt][r]);
+                Us[VL::at(s, col)] = M::cvt(Uo[tt][r]);
+                Rs[VL::at(s, col)] = M::cvt(dR[tt][r]);
             }
 #pragma unroll
         for (int i = 0; i < XR; ++i) {
             const bf16_t e[4] = {(bf16_t)(gt[i].x & 0xffffu), (bf16_t)(gt[i].x >> 16), (bf16_t)(gt[i].y & 0xffffu),
                                  (bf16_t)(gt[i].y >> 16)};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Bg[(16 * i + 4 * g + r) * LB + col] = __builtin_bit_cast(__bf16, e[r]);
+            for (int r = 0; r < 4; ++r) Bg[VL::at(16 * i + 4 * g + r, col)] = __builtin_bit_cast(__bf16, e[r]);
         }
     }
     __syncthreads();
 
     // ---- dv rows, then E1, E2 and the column part of dbeta
-    for (int e = tid; e < CH * DV / 4; e += NT) {  // 8-byte pieces (dR rows are 8-byte aligned)
+    for (int e = tid; e < CH * DV / 4; e += NT) {  // 8-byte pieces: whole 4-column groups of the permuted rows
         const int row = e / (DV / 4), c4 = (e % (DV / 4)) * 4;
-        if (row < n) *reinterpret_cast<uint2*>(dv + (row0 + row) * DV + c4) = *reinterpret_cast<const uint2*>(&Rs[row * LR + c4]);
+        if (row < n) *reinterpret_cast<uint2*>(dv + (row0 + row) * DV + c4) = *reinterpret_cast<const uint2*>(&Rs[VL::at(row, c4)]);
     }
     // E2 tile j goes to wave j % 8 (which holds its K K^T from the inverse),
     // E1 tiles to the waves with fewer: at most three tiles per wave.
@@ -521,17 +528,16 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
         dchunk::lower_tile(j, bt, bi);
         v4f acc = zero4();
         const __bf16* lhs = e2 ? Rs : Os;
-        const int ldl = e2 ? LR : LV;
 #pragma unroll
         for (int kb = 0; kb < DV / 32; ++kb)
-            M::mma(acc, M::load(&lhs[(16 * bt + li) * ldl + 32 * kb], g), M::load(&Us[(16 * bi + li) * LU + 32 * kb], g));
+            M::mma(acc, VL::frag(lhs, 16 * bt + li, 32 * kb, g), VL::frag(Us, 16 * bi + li, 32 * kb, g));
         const int i = 16 * bi + li;
         if (!e2) {  // E1 = Gamma o tril(dO U^T) diag(beta)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * bt + 4 * g + r;
                 const float ratio = GATED ? __expf(Gl[t] - Gl[i]) : 1.f;
-                Ps[t * LT + i] = M::cvt(i <= t ? Bs[i] * ratio * acc[r] : 0.f);
+                Ps[PL::at(t, i)] = M::cvt(i <= t ? Bs[i] * ratio * acc[r] : 0.f);
             }
         } else {  // dA = -tril_{-1}(dR U^T); E2 = Gamma o dA diag(beta)
             float cs = 0.f;
@@ -540,7 +546,7 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
                 const int t = 16 * bt + 4 * g + r;
                 const float ratio = GATED ? __expf(Gl[t] - Gl[i]) : 1.f;
                 const float ga = -acc[r] * ratio;
-                Ts[t * LT + i] = M::cvt(i < t ? Bs[i] * ga : 0.f);
+                Ts[PL::at(t, i)] = M::cvt(i < t ? Bs[i] * ga : 0.f);
                 cs += i < t ? ga * kkt[r] : 0.f;
             }
             cs += __shfl_xor(cs, 16);
@@ -563,11 +569,11 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
     M::frag qT[CH / 32], kT[CH / 32], rf[DV / 32];
 #pragma unroll
     for (int kb = 0; kb < CH / 32; ++kb) {
-        qT[kb] = M::load_tr(Qs, LQ, 32 * kb, 16 * it, lane);
-        kT[kb] = M::load_tr(Ks, LQ, 32 * kb, 16 * it, lane);
+        qT[kb] = KL::tr(Qs, 32 * kb, 16 * it, lane);
+        kT[kb] = KL::tr(Ks, 32 * kb, 16 * it, lane);
     }
 #pragma unroll
-    for (int kb = 0; kb < DV / 32; ++kb) rf[kb] = M::load(&Bg[(16 * it + li) * LB + 32 * kb], g);  // G' rows
+    for (int kb = 0; kb < DV / 32; ++kb) rf[kb] = VL::frag(Bg, 16 * it + li, 32 * kb, g);  // G' rows
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {  // dKm = E1^T Q + E2^T K + diag(Gc beta) U G'^T
         const int tt = tb + u;
@@ -575,15 +581,15 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
 #pragma unroll
         for (int kb = 0; kb < CH / 32; ++kb) {
             if (32 * kb + 31 < 16 * tt) continue;  // E1, E2 vanish above the diagonal
-            M::mma(km[u], qT[kb], M::load_tr(Ps, LT, 32 * kb, 16 * tt, lane));
-            M::mma(km[u], kT[kb], M::load_tr(Ts, LT, 32 * kb, 16 * tt, lane));
+            M::mma(km[u], qT[kb], PL::tr(Ps, 32 * kb, 16 * tt, lane));
+            M::mma(km[u], kT[kb], PL::tr(Ts, 32 * kb, 16 * tt, lane));
         }
         v4f g3 = zero4();
 #pragma unroll
-        for (int kb = 0; kb < DV / 32; ++kb) M::mma(g3, rf[kb], M::load(&Us[(16 * tt + li) * LU + 32 * kb], g));
+        for (int kb = 0; kb < DV / 32; ++kb) M::mma(g3, rf[kb], VL::frag(Us, 16 * tt + li, 32 * kb, g));
         const int t = 16 * tt + li;
         const float sc = Bs[t] * (GATED ? Gc[t] : 1.f);
-        const v4bf kv = *reinterpret_cast<const v4bf*>(&Ks[t * LQ + 16 * it + 4 * g]);
+        const v4bf kv = *reinterpret_cast<const v4bf*>(&Ks[KL::at(t, 16 * it + 4 * g)]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             km[u][r] += sc * g3[r];
@@ -603,13 +609,13 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
             const bf16_t e[4] = {(bf16_t)(st[i].x & 0xffffu), (bf16_t)(st[i].x >> 16), (bf16_t)(st[i].y & 0xffffu),
                                  (bf16_t)(st[i].y >> 16)};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Bg[(16 * i + 4 * g + r) * LB + 16 * w + li] = __builtin_bit_cast(__bf16, e[r]);
+            for (int r = 0; r < 4; ++r) Bg[VL::at(16 * i + 4 * g + r, 16 * w + li)] = __builtin_bit_cast(__bf16, e[r]);
         }
     }
     if (cn < total) load_tiles(cn);  // this chunk's tiles are consumed
     __syncthreads();
 #pragma unroll
-    for (int kb = 0; kb < DV / 32; ++kb) rf[kb] = M::load(&Bg[(16 * it + li) * LB + 32 * kb], g);  // S rows
+    for (int kb = 0; kb < DV / 32; ++kb) rf[kb] = VL::frag(Bg, 16 * it + li, 32 * kb, g);  // S rows
     float xl[TPW];
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {  // dQ = diag(gamma) dO S^T + E1 K;  dKp = E2 K - diag(gamma) dR S^T
@@ -617,8 +623,8 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
         v4f a1 = zero4(), a2 = zero4();
 #pragma unroll
         for (int kb = 0; kb < DV / 32; ++kb) {
-            M::mma(a1, rf[kb], M::load(&Os[(16 * tt + li) * LV + 32 * kb], g));
-            M::mma(a2, rf[kb], M::load(&Rs[(16 * tt + li) * LR + 32 * kb], g));
+            M::mma(a1, rf[kb], VL::frag(Os, 16 * tt + li, 32 * kb, g));
+            M::mma(a2, rf[kb], VL::frag(Rs, 16 * tt + li, 32 * kb, g));
         }
         const int t = 16 * tt + li;
         const float ge = GATED ? Ge[t] : 1.f;
@@ -626,8 +632,8 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
 #pragma unroll
         for (int kb = 0; kb < CH / 32; ++kb) {
             if (32 * kb > 16 * tt + 15) continue;  // E1, E2 rows end at the diagonal
-            M::mma(dqv, kT[kb], M::load(&Ps[(16 * tt + li) * LT + 32 * kb], g));
-            M::mma(kp, kT[kb], M::load(&Ts[(16 * tt + li) * LT + 32 * kb], g));
+            M::mma(dqv, kT[kb], PL::frag(Ps, 16 * tt + li, 32 * kb, g));
+            M::mma(kp, kT[kb], PL::frag(Ts, 16 * tt + li, 32 * kb, g));
         }
         if (t < n) {
             uint2 pq, pk;
@@ -639,8 +645,8 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
             *reinterpret_cast<uint2*>(dk + (row0 + t) * DK + 16 * it + 4 * g) = pk;
         }
         if constexpr (GATED) {  // q_t . dq_t + k_t . (dKp_t - dKm_t), this wave's features
-            const v4bf qv = *reinterpret_cast<const v4bf*>(&Qs[t * LQ + 16 * it + 4 * g]);
-            const v4bf kv = *reinterpret_cast<const v4bf*>(&Ks[t * LQ + 16 * it + 4 * g]);
+            const v4bf qv = *reinterpret_cast<const v4bf*>(&Qs[KL::at(t, 16 * it + 4 * g)]);
+            const v4bf kv = *reinterpret_cast<const v4bf*>(&Ks[KL::at(t, 16 * it + 4 * g)]);
             float x = 0.f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) x += (float)qv[r] * dqv[r] + (float)kv[r] * (kp[r] - km[u][r]);
@@ -700,7 +706,7 @@ hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const
     const size_t slots = (size_t)sm.H * sm.NS;
     const int HT = sm.N * sm.H, NC = (sm.T + CH - 1) / CH;
     float* map_c = ws;                       // forward N_g, then c_g
-    float* map_mt = map_c + slots * DK * DV; // forward M_g, then M_g^T
+    float* map_mt = map_c + slots * DK * DV; // forward M_g (the reverse composition reads it transposed)
     float* g_end = map_mt + slots * DK * DK; // forward segment states, then segment-end gradients
     // the chunk records of T left by the forward sweep, then the chunk-state tiles
     const bf16_t* trec = reinterpret_cast<const bf16_t*>(g_end + slots * DK * DV);
@@ -711,12 +717,12 @@ hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const
     if (err != hipSuccess) return err;
     if (sm.G > 1) {
         dlb_chain_kernel<DK, DV, true, GATED><<<dim3(HT * (sm.G - 1)), dim3(NT), 0, stream>>>(
-            q, k, beta, alpha, dO, nullptr, map_c, map_mt, nullptr, nullptr, trec, sm);
+            q, k, beta, alpha, dO, nullptr, map_c, nullptr, nullptr, trec, sm);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if ((err = launch_delta_compose_rev(map_c, map_mt, dS_T, g_end, sm, DK, DV, stream)) != hipSuccess) return err;
     dlb_chain_kernel<DK, DV, false, GATED><<<dim3(HT * sm.G), dim3(NT), 0, stream>>>(q, k, beta, alpha, dO, g_end,
-                                                                                 nullptr, nullptr, gst, dS0, trec, sm);
+                                                                                 nullptr, gst, dS0, trec, sm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     // one workgroup per compute unit (the LDS allows one), each looping over chunks
     int dev = 0, cus = 256;

@@ -76,14 +76,15 @@ __host__ __device__ constexpr void lower_tile(int id, int& i, int& j) {
     else { i = 3; j = 0; }
 }
 
-// Zero the six upper 16x16 tiles of a [C][LT] bf16 matrix (read as zero
-// operands, never written by the builders below).
+// Zero the six upper 16x16 tiles of a C x C bf16 matrix of layout XL
+// (read as zero operands, never written by the builders below).
+template <class XL = RowLayout<LT>>
 __device__ __forceinline__ void clear_upper(__bf16* X, int tid) {
     for (int e = tid; e < 6 * 256; e += NT) {
         const int tile = e >> 8, r = (e >> 4) & 15, c = e & 15;
         const int bi = tile < 3 ? 0 : tile < 5 ? 1 : 2;
         const int bj = tile < 3 ? tile + 1 : tile < 5 ? tile - 1 : 3;
-        X[(16 * bi + r) * LT + 16 * bj + c] = Mma<bf16_t>::cvt(0.f);
+        X[XL::at(16 * bi + r, 16 * bj + c)] = Mma<bf16_t>::cvt(0.f);
     }
 }
 
@@ -91,8 +92,8 @@ __device__ __forceinline__ void clear_upper(__bf16* X, int tid) {
 //
 // Builds T = (I + A)^{-1} (bf16, lower blocks of Ts) and, with WANT_P, the
 // causal scores P (bf16, lower blocks of Ps, rows = queries).  Ks, Qs: the
-// staged chunk rows ([C][LQ] bf16, LQ = DK + 8 unless given; rows past the
-// chunk end zero); Bs:
+// staged chunk rows (bf16, layout KL: RowLayout; rows past the chunk end
+// zero); Bs:
 // betas; Gl: cumulative log-gates (GATED).  Af ([C][LF] fp32), Ad and Yf
 // (4 x 256 fp32 each) are scratch.  Called by all threads of the workgroup
 // after the chunk is staged and visible; ends with a barrier.  With KEEP,
@@ -106,7 +107,7 @@ __device__ __forceinline__ void clear_upper(__bf16* X, int tid) {
 //
 // K_DEAD: Af may occupy the same LDS as Ks (K is not needed afterwards):
 // every K K^T tile is then computed before the first write of A.
-template <int DK, bool GATED, bool WANT_P, bool KEEP = false, int LQ = DK + 8, bool K_DEAD = false>
+template <int DK, bool GATED, bool WANT_P, bool KEEP = false, class KL = RowLayout<DK + 8>, bool K_DEAD = false>
 __device__ __forceinline__ void build_T(const __bf16* Ks, const __bf16* Qs, const float* Bs, const float* Gl,
                                         float* Af, float* Ad, float* Yf, __bf16* Ts, __bf16* Ps, int w, int g,
                                         int li, v4f* keep = nullptr) {
@@ -127,7 +128,7 @@ __device__ __forceinline__ void build_T(const __bf16* Ks, const __bf16* Qs, cons
             kk[jj] = zero4();
 #pragma unroll
             for (int kb = 0; kb < DK / 32; ++kb)
-                M::mma(kk[jj], M::load(&Ks[(16 * bi + li) * LQ + 32 * kb], g), M::load(&Ks[(16 * bj + li) * LQ + 32 * kb], g));
+                M::mma(kk[jj], KL::frag(Ks, 16 * bi + li, 32 * kb, g), KL::frag(Ks, 16 * bj + li, 32 * kb, g));
         }
         __syncthreads();  // every read of Ks done: its LDS now holds A
 #pragma unroll
@@ -158,7 +159,7 @@ __device__ __forceinline__ void build_T(const __bf16* Ks, const __bf16* Qs, cons
         if (id < 10) {
 #pragma unroll
             for (int kb = 0; kb < DK / 32; ++kb)
-                M::mma(acc, M::load(&Ks[(16 * bi + li) * LQ + 32 * kb], g), M::load(&Ks[(16 * bj + li) * LQ + 32 * kb], g));
+                M::mma(acc, KL::frag(Ks, 16 * bi + li, 32 * kb, g), KL::frag(Ks, 16 * bj + li, 32 * kb, g));
             if constexpr (KEEP) {
                 if (jj < 2) keep[jj] = acc;
             }
@@ -177,7 +178,7 @@ __device__ __forceinline__ void build_T(const __bf16* Ks, const __bf16* Qs, cons
             // writes four consecutive keys of one query row
 #pragma unroll
             for (int kb = 0; kb < DK / 32; ++kb)
-                M::mma(acc, M::load(&Ks[(16 * bj + li) * LQ + 32 * kb], g), M::load(&Qs[(16 * bi + li) * LQ + 32 * kb], g));
+                M::mma(acc, KL::frag(Ks, 16 * bj + li, 32 * kb, g), KL::frag(Qs, 16 * bi + li, 32 * kb, g));
             if constexpr (GATED) {
                 const float gq = Gl[16 * bi + li];
 #pragma unroll
@@ -267,8 +268,10 @@ __device__ __forceinline__ void build_T(const __bf16* Ks, const __bf16* Qs, cons
 // The causal scores P (bf16, lower blocks of Ps, rows = queries; gated: o
 // Gamma) alone, for loops that load T from the chunk records; wave w builds
 // lower tiles w and w + 8.  With KEEP, keep[j] receives the raw K K^T tile
-// w + 8 j (j = 0, 1, when below 10).  No barrier.
-template <int DK, bool GATED, bool KEEP = false, int LQ = DK + 8>
+// w + 8 j (j = 0, 1, when below 10).  KL, QL, PL: the LDS layouts of K, Q
+// and P (RowLayout).  No barrier.
+template <int DK, bool GATED, bool KEEP = false, class KL = RowLayout<DK + 8>, class QL = KL,
+          class PL = RowLayout<LT>>
 __device__ __forceinline__ void build_P(const __bf16* Ks, const __bf16* Qs, const float* Gl, __bf16* Ps, int w, int g,
                                         int li, v4f* keep = nullptr) {
     using M = Mma<bf16_t>;
@@ -282,7 +285,7 @@ __device__ __forceinline__ void build_P(const __bf16* Ks, const __bf16* Qs, cons
         v4f acc = zero4();
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb)
-            M::mma(acc, M::load(&Ks[(16 * bj + li) * LQ + 32 * kb], g), M::load(&Qs[(16 * bi + li) * LQ + 32 * kb], g));
+            M::mma(acc, KL::frag(Ks, 16 * bj + li, 32 * kb, g), QL::frag(Qs, 16 * bi + li, 32 * kb, g));
         if constexpr (GATED) {
             const float gq = Gl[16 * bi + li];
 #pragma unroll
@@ -291,25 +294,32 @@ __device__ __forceinline__ void build_P(const __bf16* Ks, const __bf16* Qs, cons
         uint2 pk;
         pk.x = pack_bf16x2((bi == bj && 4 * g + 0 > li) ? 0.f : acc[0], (bi == bj && 4 * g + 1 > li) ? 0.f : acc[1]);
         pk.y = pack_bf16x2((bi == bj && 4 * g + 2 > li) ? 0.f : acc[2], (bi == bj && 4 * g + 3 > li) ? 0.f : acc[3]);
-        *reinterpret_cast<uint2*>(&Ps[(16 * bi + li) * LT + 16 * bj + 4 * g]) = pk;
+        *reinterpret_cast<uint2*>(&Ps[PL::at(16 * bi + li, 16 * bj + 4 * g)]) = pk;
         if constexpr (KEEP) {
             v4f kk = zero4();
 #pragma unroll
             for (int kb = 0; kb < DK / 32; ++kb)
-                M::mma(kk, M::load(&Ks[(16 * bi + li) * LQ + 32 * kb], g), M::load(&Ks[(16 * bj + li) * LQ + 32 * kb], g));
+                M::mma(kk, KL::frag(Ks, 16 * bi + li, 32 * kb, g), KL::frag(Ks, 16 * bj + li, 32 * kb, g));
             keep[jj] = kk;
         }
     }
 }
 
 // A chunk record (a 64 x 64 bf16 matrix, row-major, upper blocks zero) into
-// LDS rows of stride LT; 512 threads, 16 bytes each.
+// LDS rows of layout XL; 512 threads, 16 bytes each.
 constexpr int kRecElems = CH * CH;
 __device__ __forceinline__ uint4 load_rec(const bf16_t* rec, int tid) {
     return *reinterpret_cast<const uint4*>(rec + tid * 8);
 }
+template <class XL = RowLayout<LT>>
 __device__ __forceinline__ void stage_rec(__bf16* Xs, uint4 x, int tid) {
-    *reinterpret_cast<uint4*>(&Xs[(tid >> 3) * LT + (tid & 7) * 8]) = x;
+    __bf16* row = &Xs[(tid >> 3) * XL::LD];
+    if constexpr (XL::PERM) {
+        *reinterpret_cast<uint2*>(row + pcol((tid & 7) * 8)) = make_uint2(x.x, x.y);
+        *reinterpret_cast<uint2*>(row + pcol((tid & 7) * 8 + 4)) = make_uint2(x.z, x.w);
+    } else {
+        *reinterpret_cast<uint4*>(row + (tid & 7) * 8) = x;
+    }
 }
 
 }  // namespace dchunk

@@ -70,23 +70,26 @@ enum { kMap = 0, kOut = 1, kStates = 2 };
 template <int DK, int NS, int MODE, bool GATED, int NWV = 8>
 struct DL {
     static constexpr bool OUT = MODE == kOut, MAP = MODE == kMap;
-    // Row strides (bf16 elements).  Matrices read only as row fragments
-    // (W, Q, T, P) are padded by 4 elements, so the 16 rows of a fragment
-    // start 2 words apart and spread over the banks; K and V, also read with
-    // transpose loads, by 8.  (4-element padding leaves rows 8-byte aligned:
-    // those matrices are staged with 8-byte stores.)
-    static constexpr int LQ = DK + 8;  // K rows
-    static constexpr int LW = DK + 4;  // W and Q rows
-    static constexpr int LV = NS + 8;  // V rows
-    static constexpr int LT = CH + 4;  // T and P rows
-    static constexpr int KS = CH * LQ * 2;          // K_c rows (read transposed too)
+    // Row strides (bf16 elements), by how each matrix is read (LDS probes on
+    // gfx950): matrices read as row fragments (W, Q, T, P) are stored
+    // group-permuted (pcol) with 16 elements of padding, so a fragment is one
+    // conflict-free 16-byte read; matrices read only with transpose loads (V,
+    // K) keep the natural layout, also padded by 16, where those reads are
+    // conflict-free.  The output and state passes read K both ways and stage
+    // it twice: natural (Ks) and permuted (Kf, for the row fragments).
+    static constexpr int LQ = DK + 16;  // K rows (natural and permuted)
+    static constexpr int LW = DK + 16;  // W and Q rows (permuted)
+    static constexpr int LV = NS + 16;  // V rows
+    static constexpr int LT = CH + 16;  // T and P rows (permuted)
+    static constexpr int KS = CH * LQ * 2;          // K_c rows, natural (transpose loads)
+    static constexpr int KF = MAP ? 0 : CH * LQ * 2;  // K_c rows, permuted (row fragments)
     static constexpr int WS = MAP ? CH * LW * 2 : 0;  // W rows (map pass)
     static constexpr int QS = OUT ? CH * LW * 2 : 0;
     static constexpr int VS = CH * LV * 2;          // V_c rows (read transposed)
     static constexpr int TS = CH * LT * 2;          // T (bf16, from the chunk's record)
     static constexpr int PS = OUT ? CH * LT * 2 : 0;  // tril(Q K^T), rows = queries
     static constexpr int BS = CH * 4 * (GATED ? 4 : 1);  // beta; gated: log-gates, gamma, gamma_C/gamma (fp32)
-    static constexpr int TOTAL = KS + WS + QS + VS + TS + PS + BS;
+    static constexpr int TOTAL = KS + KF + WS + QS + VS + TS + PS + BS;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
     static constexpr int XR = DK / 16;              // dk row tiles of a state column
     // State column tiles: OUT and STATES carry S (NS columns); MAP carries N
@@ -101,7 +104,7 @@ struct DL {
 // Chunk rows of a [T][D] bf16 matrix into LDS scaled to unit L2 norm (a zero
 // row stays zero).  The D/8 threads holding a row are consecutive lanes, so
 // the row's sum of squares is a shuffle reduction within their group.
-template <int D, int NTH = NT, bool SPLIT8 = false>
+template <int D, int NTH = NT, bool SPLIT8 = false, bool PERM = false>
 __device__ __forceinline__ void stage_rows_l2(const ChunkRegs<bf16_t, D, NTH>& cr, int tid, __bf16* rm, int ld) {
     constexpr int TPR = D / 8;
 #pragma unroll
@@ -122,7 +125,10 @@ __device__ __forceinline__ void stage_rows_l2(const ChunkRegs<bf16_t, D, NTH>& c
         y.y = pack_bf16x2(x[2] * inv, x[3] * inv);
         y.z = pack_bf16x2(x[4] * inv, x[5] * inv);
         y.w = pack_bf16x2(x[6] * inv, x[7] * inv);
-        if constexpr (SPLIT8) {
+        if constexpr (PERM) {  // group-permuted rows (pcol)
+            *reinterpret_cast<uint2*>(rm + row * ld + pcol(col)) = make_uint2(y.x, y.y);
+            *reinterpret_cast<uint2*>(rm + row * ld + pcol(col + 4)) = make_uint2(y.z, y.w);
+        } else if constexpr (SPLIT8) {
             uint2* d = reinterpret_cast<uint2*>(rm + row * ld + col);
             d[0] = make_uint2(y.x, y.y);
             d[1] = make_uint2(y.z, y.w);
@@ -146,13 +152,13 @@ template <int DK, bool GATED, bool PACKED>
 __global__ __launch_bounds__(NT) void delta_tinv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ beta,
                                                         const float* __restrict__ alpha, bf16_t* __restrict__ trec,
                                                         int flags, SegMap sm) {
-    // K is read only as row fragments here (K K^T tiles): rows padded by 4
-    // elements spread a fragment's 16 rows over the banks (staged with
-    // 8-byte stores)
+    // K is read only as row fragments here (K K^T tiles): group-permuted
+    // rows padded by 16 (pcol), one conflict-free 16-byte read a fragment
     // K is dead once A = K K^T is formed, so A takes K's LDS (one buffer of
     // the larger size): 35 KB instead of 52 KB per workgroup, four
     // workgroups per CU instead of three.
-    constexpr int LQ = DK + 4, LT = dchunk::LT, LF = dchunk::LF;
+    using KL = RowLayout<DK + 16, true>;
+    constexpr int LQ = KL::LD, LT = dchunk::LT, LF = dchunk::LF;
     constexpr int KA_BYTES = CH * LQ * 2 > CH * LF * 4 ? CH * LQ * 2 : CH * LF * 4;
     __shared__ __align__(16) unsigned char KAs[KA_BYTES];
     __bf16* Ks = reinterpret_cast<__bf16*>(KAs);
@@ -191,8 +197,8 @@ __global__ __launch_bounds__(NT) void delta_tinv_kernel(const bf16_t* __restrict
     const long row0 = h * sm.hs + sm.start<PACKED>(n) + c0;
     ChunkRegs<bf16_t, DK, NT> kr;
     kr.load_buf(make_rsrc(k + row0 * DK, (uint32_t)rows * DK * 2), 0, tid);
-    if (flags & kNormQK) stage_rows_l2<DK, NT, true>(kr, tid, Ks, LQ);
-    else stage_rows_raw<bf16_t, DK, NT, true>(kr, tid, Ks, LQ);
+    if (flags & kNormQK) stage_rows_l2<DK, NT, false, true>(kr, tid, Ks, LQ);
+    else stage_rows_raw<bf16_t, DK, NT, false, true>(kr, tid, Ks, LQ);
     if (tid < CH) {
         const float braw = bf16_to_f32(
             __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(beta + row0, (uint32_t)rows * 2), (uint32_t)tid * 2, 0, 0));
@@ -205,7 +211,7 @@ __global__ __launch_bounds__(NT) void delta_tinv_kernel(const bf16_t* __restrict
     }
     dchunk::clear_upper(Ts, tid);
     __syncthreads();
-    dchunk::build_T<DK, GATED, false, false, LQ, true>(Ks, nullptr, Bs, Gl, Af, Ad, Yf, Ts, nullptr, w, g, li);
+    dchunk::build_T<DK, GATED, false, false, KL, true>(Ks, nullptr, Bs, Gl, Af, Ad, Yf, Ts, nullptr, w, g, li);
     // one 16-byte row piece per thread: row tid / 8, columns 8 (tid % 8) ..
     const int row = tid >> 3, col = (tid & 7) * 8;
     *reinterpret_cast<uint4*>(trec + rec * kRecElems + row * CH + col) =
@@ -238,6 +244,7 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
     __shared__ __align__(16) unsigned char smem[Y::TOTAL];
     unsigned char* sp = smem;
     __bf16* Ks = reinterpret_cast<__bf16*>(sp);  sp += Y::KS;
+    __bf16* Kf = reinterpret_cast<__bf16*>(sp);  sp += Y::KF;
     __bf16* Ws = reinterpret_cast<__bf16*>(sp);  sp += Y::WS;
     __bf16* Qs = reinterpret_cast<__bf16*>(sp);  sp += Y::QS;
     __bf16* Vs = reinterpret_cast<__bf16*>(sp);  sp += Y::VS;
@@ -251,11 +258,14 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int w = wave_id(tid);
     __builtin_assume(w >= 0 && w < NWV);  // lets per-wave tile guards fold away
-    // This workgroup's (head, sequence, segment).  MAP skips the last
-    // segment of every sequence; its result is the sequence's final state.
+    // This workgroup's (head, sequence, segment).  The forward's MAP skips
+    // the last segment of every sequence (its result is the sequence's final
+    // state); the backward's forward sweep also wants that segment's M (the
+    // reverse composition runs on M^T), so for uniform batches MAP covers the
+    // segments the grid holds: G - 1 or G per sequence.
     int h, nseq, seg;
     if constexpr (!PACKED) {  // (sequence, head)-major, segments consecutive
-        const int G1 = MAP ? sm.G - 1 : sm.G;
+        const int G1 = MAP ? (int)(gridDim.x / ((unsigned)sm.N * sm.H)) : sm.G;
         const int vh = blockIdx.x / G1;
         seg = blockIdx.x % G1;
         nseq = vh / sm.H;
@@ -336,7 +346,7 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
             const int tile = e >> 8, r = (e >> 4) & 15, c = e & 15;
             const int bi = tile < 3 ? 0 : tile < 5 ? 1 : 2;
             const int bj = tile < 3 ? tile + 1 : tile < 5 ? tile - 1 : 3;
-            Ps[(16 * bi + r) * LT + 16 * bj + c] = M::cvt(0.f);
+            Ps[(16 * bi + r) * LT + pcol(16 * bj + c)] = M::cvt(0.f);
         }
     }
     for (int c0 = seg * L; c0 < t_end; c0 += CH) {
@@ -364,19 +374,21 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
         // transpose loads)
         if (flags & kNormQK) {
             stage_rows_l2<DK, NT>(kr, tid, Ks, LQ);
-            if constexpr (OUT) stage_rows_l2<DK, NT, true>(qr, tid, Qs, Y::LW);
+            if constexpr (!MAP) stage_rows_l2<DK, NT, false, true>(kr, tid, Kf, LQ);
+            if constexpr (OUT) stage_rows_l2<DK, NT, false, true>(qr, tid, Qs, Y::LW);
         } else {
             stage_rows_raw<bf16_t, DK, NT>(kr, tid, Ks, LQ);
-            if constexpr (OUT) stage_rows_raw<bf16_t, DK, NT, true>(qr, tid, Qs, Y::LW);
+            if constexpr (!MAP) stage_rows_raw<bf16_t, DK, NT, false, true>(kr, tid, Kf, LQ);
+            if constexpr (OUT) stage_rows_raw<bf16_t, DK, NT, false, true>(qr, tid, Qs, Y::LW);
         }
         stage_rows_raw<bf16_t, NS, NT>(vr, tid, Vs, LV);
 #pragma unroll
         for (int e = 0; e < RPT; ++e) {
             const int p = tid + NT * e;
             if (NT * (e + 1) <= 512 || p < 512) {
-                uint2* dt = reinterpret_cast<uint2*>(&Ts[(p >> 3) * LT + (p & 7) * 8]);
-                dt[0] = make_uint2(tnext[e].x, tnext[e].y);
-                dt[1] = make_uint2(tnext[e].z, tnext[e].w);
+                __bf16* dt = &Ts[(p >> 3) * LT];  // permuted rows
+                *reinterpret_cast<uint2*>(dt + pcol((p & 7) * 8)) = make_uint2(tnext[e].x, tnext[e].y);
+                *reinterpret_cast<uint2*>(dt + pcol((p & 7) * 8 + 4)) = make_uint2(tnext[e].z, tnext[e].w);
             }
         }
         if (tid < CH) {  // wave 0
@@ -415,8 +427,8 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
                 v4f acc = zero4();
 #pragma unroll
                 for (int kb = 0; kb < DK / 32; ++kb)
-                    M::mma(acc, M::load(&Ks[(16 * bj + li) * LQ + 32 * kb], g),
-                           M::load(&Qs[(16 * bi + li) * Y::LW + 32 * kb], g));
+                    M::mma(acc, M::load_p(&Kf[(16 * bj + li) * LQ + 32 * kb], g),
+                           M::load_p(&Qs[(16 * bi + li) * Y::LW + 32 * kb], g));
                 if constexpr (GATED) {  // gamma_query / gamma_key
                     const float gq = Gl[16 * bi + li];
 #pragma unroll
@@ -427,7 +439,7 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
                                    (bi == bj && 4 * g + 1 > li) ? 0.f : acc[1]);
                 pk.y = pack_bf16x2((bi == bj && 4 * g + 2 > li) ? 0.f : acc[2],
                                    (bi == bj && 4 * g + 3 > li) ? 0.f : acc[3]);
-                *reinterpret_cast<uint2*>(&Ps[(16 * bi + li) * LT + 16 * bj + 4 * g]) = pk;
+                *reinterpret_cast<uint2*>(&Ps[(16 * bi + li) * LT + pcol(16 * bj + 4 * g)]) = pk;
             }
 #pragma unroll
             for (int qt = 0; qt < 4; ++qt) {
@@ -436,7 +448,7 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
 #pragma unroll
                     for (int kb = 0; kb < DK / 32; ++kb)
                         M::mma(Oq[qt], M::from_tiles(X[0][2 * kb], X[0][2 * kb + 1]),
-                               M::load(&Qs[(16 * qt + li) * Y::LW + 32 * kb], g));
+                               M::load_p(&Qs[(16 * qt + li) * Y::LW + 32 * kb], g));
                 }
                 if constexpr (GATED) Oq[qt] *= Ge[16 * qt + li];  // diag(gamma) Q S
             }
@@ -456,7 +468,7 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
 #pragma unroll
                 for (int kb = 0; kb < CH / 32; ++kb) {
                     if (32 * kb > 16 * tt + 15) continue;  // T is lower triangular
-                    frag tf = M::load(&Ts[(16 * tt + li) * LT + 32 * kb], g);
+                    frag tf = M::load_p(&Ts[(16 * tt + li) * LT + 32 * kb], g);
                     if constexpr (GATED) {  // slot s <-> column 32 kb + 4g + s (s < 4), 32 kb + 16 + 4g + s - 4
                         const v4f g0 = *reinterpret_cast<const v4f*>(&Ge[32 * kb + 4 * g]);
                         const v4f g1 = *reinterpret_cast<const v4f*>(&Ge[32 * kb + 16 + 4 * g]);
@@ -468,7 +480,7 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
                     }
                     M::mma(acc, M::load_tr(Ks, LQ, 32 * kb, 16 * dkt, lane), tf);
                 }
-                __bf16* dst = &Ws[(16 * tt + li) * Y::LW + 16 * dkt + 4 * g];
+                __bf16* dst = &Ws[(16 * tt + li) * Y::LW + pcol(16 * dkt + 4 * g)];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) dst[r] = M::cvt(acc[r]);
             }
@@ -482,7 +494,7 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
 #pragma unroll
                         for (int kb = 0; kb < CH / 32; ++kb) {
                             if (32 * kb > 16 * tt + 15) continue;
-                            M::mma(U[j][tt], M::load(&Ts[(16 * tt + li) * LT + 32 * kb], g),
+                            M::mma(U[j][tt], M::load_p(&Ts[(16 * tt + li) * LT + 32 * kb], g),
                                    M::load_tr(Vs, LV, 32 * kb, 16 * id, lane));
                         }
                     }
@@ -496,7 +508,7 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
                 for (int j = 0; j < SLOTS; ++j) ws_[j] = zero4();
 #pragma unroll
                 for (int kb = 0; kb < DK / 32; ++kb) {
-                    const frag wf = M::load(&Ws[(16 * tt + li) * Y::LW + 32 * kb], g);
+                    const frag wf = M::load_p(&Ws[(16 * tt + li) * Y::LW + 32 * kb], g);
 #pragma unroll
                     for (int j = 0; j < SLOTS; ++j)
                         if (w + NWV * j < Y::NCT) M::mma(ws_[j], wf, M::from_tiles(X[j][2 * kb], X[j][2 * kb + 1]));
@@ -522,7 +534,7 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
                 for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
                     for (int kb = 0; kb < DK / 32; ++kb) {
-                        const frag kf = M::load(&Ks[(16 * tt + li) * LQ + 32 * kb], g);
+                        const frag kf = M::load_p(&Kf[(16 * tt + li) * LQ + 32 * kb], g);
 #pragma unroll
                         for (int j = 0; j < SLOTS; ++j)
                             if (w + NWV * j < Y::NCT) M::mma(ks[j][tt], kf, M::from_tiles(X[j][2 * kb], X[j][2 * kb + 1]));
@@ -549,7 +561,7 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
 #pragma unroll
                     for (int kb = 0; kb < CH / 32; ++kb) {
                         if (32 * kb > 16 * tt + 15) continue;  // T is lower triangular
-                        const frag tf = M::load(&Ts[(16 * tt + li) * LT + 32 * kb], g);
+                        const frag tf = M::load_p(&Ts[(16 * tt + li) * LT + 32 * kb], g);
 #pragma unroll
                         for (int j = 0; j < SLOTS; ++j)
                             if (w + NWV * j < Y::NCT) M::mma(U[j][tt], tf, rf[j][kb]);
@@ -599,7 +611,7 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
                     for (int kb = 0; kb < CH / 32; ++kb) {
                         if (32 * kb > 16 * qt + 15) continue;  // keys after these queries
                         M::mma(Oq[qt], M::from_tiles(U[j][2 * kb], U[j][2 * kb + 1]),
-                               M::load(&Ps[(16 * qt + li) * LT + 32 * kb], g));
+                               M::load_p(&Ps[(16 * qt + li) * LT + 32 * kb], g));
                     }
                     const int t = 16 * qt + li;
                     if (t < n) {
@@ -678,8 +690,9 @@ inline unsigned compose_blocks(int NH) { return (unsigned)(((NH + kXcds - 1) / k
 
 // S_in(0) = S0 (or 0); S_in(g+1) = M_g S_in(g) + N_g in fp32 MFMA.  One
 // workgroup per (16-column block of the state, sequence and head); serial
-// over the sequence's segments.  REV runs the same recurrence from the last
-// segment down (the backward pass: G(G-1) = S0, G(g-1) = M_g G(g) + N_g).
+// over the sequence's segments.  REV runs the transposed recurrence from the
+// last segment down (the backward pass: G(G-1) = S0, G(g-1) = M_g^T G(g) +
+// N_g, with M_g the forward's segment map as stored).
 // Every column block of a head reads the whole of each M_g, so the blocks of
 // one head are numbered to land on one XCD (dispatch places block b on XCD
 // b mod 8, and each XCD has its own L2): M_g then comes from memory once per
@@ -765,7 +778,13 @@ __global__ __launch_bounds__(256) void delta_compose_kernel(const float* __restr
 #pragma unroll
             for (int i = 0; i < RPW; ++i) {
                 const int rt = w * RPW + i;
-                const v4f a = *reinterpret_cast<const v4f*>(&Ms[(16 * rt + li) * LM + 16 * kb + 4 * g]);
+                v4f a;
+                if constexpr (REV) {  // (M^T)[16 rt + li][16 kb + 4 g + e]: lane groups g hit distinct banks
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) a[e] = Ms[(16 * kb + 4 * g + e) * LM + 16 * rt + li];
+                } else {
+                    a = *reinterpret_cast<const v4f*>(&Ms[(16 * rt + li) * LM + 16 * kb + 4 * g]);
+                }
                 Mma<float>::mma(acc[i], a, bb);
             }
         }
@@ -825,9 +844,9 @@ hipError_t launch_states(const bf16_t* q, const bf16_t* k, const bf16_t* v, cons
     hipError_t err;
     delta_tinv_kernel<DK, GATED, false><<<dim3(recs), dim3(NT), 0, stream>>>(k, beta, alpha, trec, 0, sm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (sm.NS > sm.N) {
+    if (sm.G > 1) {  // every segment's map: M_0..M_{G-2} for the composition below, M_1..M_{G-1} for the backward's
         constexpr int NWM = kMapWaves<DK, DV>;
-        delta_chunk_kernel<DK, DV, kMap, GATED, false, NWM><<<dim3(sm.H * (sm.NS - sm.N)), dim3(NWM * 64), 0, stream>>>(
+        delta_chunk_kernel<DK, DV, kMap, GATED, false, NWM><<<dim3(sm.H * sm.NS), dim3(NWM * 64), 0, stream>>>(
             q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, nullptr, nullptr, trec, 0, sm);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
