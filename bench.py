@@ -67,14 +67,14 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COUNTERS = {
     # workload name -> kernel, sources, sha256 of the sources, KiB per dispatch
     "la_bf16_b1_h32_t65536_d64": {"kernel": "la_fused_kernel", "sources": LA_SOURCES,
-                                  "sha256": "fe652223e6eb6bbecc74fbbf4e11d2279a460550984288b666c06c193eef9a26",
-                                  "fetch_kib": 611573.1, "write_kib": 327789.0},
+                                  "sha256": "e6570cd1bdf9d6073549e4a9585e916dfc4f6cb94f4394346c607b6def57f884",
+                                  "fetch_kib": 611282.2, "write_kib": 327789.0},
     "la_bf16_b4_h8_t8192_d64": {"kernel": "la_fused_kernel", "sources": LA_SOURCES,
-                                "sha256": "fe652223e6eb6bbecc74fbbf4e11d2279a460550984288b666c06c193eef9a26",
-                                "fetch_kib": 70045.8, "write_kib": 48397.0},
+                                "sha256": "e6570cd1bdf9d6073549e4a9585e916dfc4f6cb94f4394346c607b6def57f884",
+                                "fetch_kib": 70044.8, "write_kib": 48397.0},
     "decode_bf16_n256_h32_d128_1000steps": {"kernel": "la_decode_kernel", "sources": LA_DECODE_SOURCES,
-                                            "sha256": "2b6264c6ad0b66bdd1f8c4a63952026813985e3f50f7c32f5ecbc80d44005f0f",
-                                            "fetch_kib": 267307.5, "write_kib": 530469.3},
+                                            "sha256": "8232cc78c4f3cb7749a132aaa1d460fc2383a61bd5b1858a0a82ac5304a817ea",
+                                            "fetch_kib": 267307.3, "write_kib": 530465.6},
 }
 
 
