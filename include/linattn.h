@@ -43,9 +43,11 @@
  * - Validation first: arguments are checked before anything is launched; on
  *   any non-OK status nothing has been enqueued and no buffer was written.
  *   la_last_error() then describes the problem (per calling thread).
- * - Supported: dk, dv in {64, 128}; chunk == 64; dtype LA_BF16 everywhere and
- *   LA_F32 for la_forward (dk = 128 with dv = 128 excluded) and the decode
- *   steps.  Forgetting gates alpha are fp32 for every dtype.
+ * - Supported: dk, dv in {64, 128}; chunk == 64, and for la_forward on
+ *   uniform batches also 16, 32 and 128 (LA_F32: 16 and 32); dtype LA_BF16
+ *   everywhere and LA_F32 for la_forward (at chunk 64, dk = 128 with
+ *   dv = 128 excluded) and the decode steps.  Forgetting gates alpha are
+ *   fp32 for every dtype.
  *   Other valid-but-unsupported sizes return LA_ERR_UNSUPPORTED.
  * - Non-finite inputs are not checked and propagate.
  */
@@ -101,10 +103,16 @@ size_t la_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk
  *          may alias S0, z0 (continue a sequence in place, the initial/final
  *          state hand-off of [Recurrence] "Chunked scan").
  * eps      > 0; the pages use 1e-6.
- * chunk    tokens per chunk (64).
+ * chunk    tokens per chunk: 64 (one fused launch), or 16, 32, 128 (LA_F32:
+ *          16, 32), a blocked path of three launches (segment sums, their
+ *          prefix, chunk loops of `chunk` tokens).  The result does not
+ *          depend on it beyond rounding ([Recurrence] "Chunked scan": a scan
+ *          handed its state every few tokens equals one pass; [LA-SSM] §3,
+ *          the chunkwise form); the workspace size does
+ *          (la_forward_workspace_bytes with the same chunk).
  * Errors: LA_ERR_INVALID_ARG (q, k, v or o NULL; B, H, T, dk, dv < 1; eps not
- * > 0 or not finite; chunk < 1; dtype unknown), LA_ERR_UNSUPPORTED,
- * LA_ERR_WORKSPACE, LA_ERR_HIP.
+ * > 0 or not finite; chunk < 1; dtype unknown), LA_ERR_UNSUPPORTED (other
+ * chunk sizes, dims), LA_ERR_WORKSPACE, LA_ERR_HIP.
  */
 la_status la_forward(const void* q, const void* k, const void* v,
                      const float* S0, const float* z0,

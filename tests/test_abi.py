@@ -53,7 +53,8 @@ def _la(**kw):
     (dict(B=-1), "INVALID_ARG"), (dict(dk=0), "INVALID_ARG"), (dict(chunk=0), "INVALID_ARG"),
     (dict(eps=0.0), "INVALID_ARG"), (dict(eps=-1.0), "INVALID_ARG"), (dict(eps=float("nan")), "INVALID_ARG"),
     (dict(eps=float("inf")), "INVALID_ARG"), (dict(dtype=7), "INVALID_ARG"),
-    (dict(dk=96), "UNSUPPORTED"), (dict(dv=32), "UNSUPPORTED"), (dict(chunk=32), "UNSUPPORTED"),
+    (dict(dk=96), "UNSUPPORTED"), (dict(dv=32), "UNSUPPORTED"), (dict(chunk=48), "UNSUPPORTED"),
+    (dict(chunk=256), "UNSUPPORTED"), (dict(chunk=8), "UNSUPPORTED"), (dict(chunk=128, dtype=0), "UNSUPPORTED"),
     (dict(dtype=0, dk=128, dv=128), "UNSUPPORTED"),
     (dict(q=ctypes.c_void_p(0x10002)), "INVALID_ARG"),
     (dict(ws=None), "WORKSPACE"), (dict(wsb=16), "WORKSPACE"), (dict(ws=ctypes.c_void_p(0x10004)), "WORKSPACE"),
@@ -241,6 +242,7 @@ def _packed_la(cu_host, **kw):
     ([0, 5, 9], dict(cu=ctypes.c_void_p(0x10002)), "INVALID_ARG"),
     ([0, 5, 9], dict(N=0), "INVALID_ARG"),
     ([0, 5, 9], dict(dk=96), "UNSUPPORTED"),
+    ([0, 5, 9], dict(chunk=32), "UNSUPPORTED"),  # other chunk sizes: uniform batches only
     ([0, 5, 9], dict(ws=None), "WORKSPACE"),
 ])
 def test_la_forward_packed_rejects(cu_host, kw, status):
@@ -359,6 +361,28 @@ def test_workspace_queries():
     nb = L.delta_backward_workspace_bytes(2, 16, 16384, 128, 128, 64)
     assert nb == L.delta_forward_workspace_bytes(2, 16, 16384, 128, 128, 64) + 4 * 32 * 256 * 128 * 128
     assert L.delta_backward_workspace_bytes(2, 16, 16384, 128, 96, 64) == 0
+
+
+def test_chunk_size_workspace_queries():
+    # la_forward, uniform batches: chunks of 16, 32, 64 and 128 tokens; the
+    # blocked path (not 64) holds two [S | z] states per (head, segment)
+    L = lin.lib()
+    for C in (16, 32, 64, 128):
+        n = L.la_forward_workspace_bytes(2, 16, 6000, 64, 128, C)
+        assert n > 0 and n % 16 == 0, C
+    for C in (0, 8, 48, 96, 256):
+        assert L.la_forward_workspace_bytes(2, 16, 6000, 64, 64, C) == 0, C
+    # a 128-token chunk rounds the segments up to whole chunks; 16 and 32 keep
+    # the 64-token plan's segments
+    E = 64 * 128 + 64
+    n16 = L.la_forward_workspace_bytes(1, 1, 100000, 64, 128, 16)
+    assert n16 % (2 * 4 * E) == 0 and n16 == L.la_forward_workspace_bytes(1, 1, 100000, 64, 128, 32)
+    # the other families and the packed batches take 64 only
+    for C in (16, 32, 128):
+        assert L.delta_forward_workspace_bytes(2, 16, 16384, 128, 128, C) == 0
+        assert L.ssd_forward_workspace_bytes(4, 8, 8192, 64, 64, C) == 0
+        cu = (ctypes.c_int * 3)(0, 5, 9)
+        assert L.la_forward_packed_workspace_bytes(ctypes.cast(cu, ctypes.c_void_p), 2, 2, 9, 64, 64, C) == 0
 
 
 def test_status_strings():

@@ -14,6 +14,7 @@
 
 #include "api_internal.hpp"
 #include "kernels.hpp"
+#include "la_chunked.hpp"
 #include "linattn.h"
 
 namespace {
@@ -81,7 +82,7 @@ struct Plan {
     size_t bytes() const { return sizeof(float) * (sp_floats + fam_floats); }
 };
 
-Plan make_plan(Family f, const Batch& b, int dk, int dv) {
+Plan make_plan(Family f, const Batch& b, int dk, int dv, int chunk = la::kChunk) {
     Plan p;
     la::SegMap& sm = p.sm;
     sm.N = b.N;
@@ -99,6 +100,8 @@ Plan make_plan(Family f, const Batch& b, int dk, int dv) {
             sm.L = (int)((nch + want - 1) / want) * la::kChunk;
         } else {
             sm.L = la::la_plan(b.N * b.H, b.T, dk, dv).L;
+            // the blocked LA path (chunk != 64) needs whole chunks per segment
+            if (chunk > la::kChunk) sm.L = (sm.L + chunk - 1) / chunk * chunk;
         }
         sm.G = (b.T + sm.L - 1) / sm.L;
         sm.NS = b.N * sm.G;
@@ -116,14 +119,17 @@ Plan make_plan(Family f, const Batch& b, int dk, int dv) {
         p.sp_floats = ((size_t)b.N + 1 + 63) / 64 * 64;
     }
     const long slots = (long)sm.H * sm.NS;
-    p.fam_floats = f == kFamLA ? la::la_ws_floats(slots, (long)b.N * b.H, dk, dv)
+    p.fam_floats = f == kFamLA ? (chunk == la::kChunk ? la::la_ws_floats(slots, (long)b.N * b.H, dk, dv)
+                                                      : la::la_chunked_ws_floats(slots, dk, dv))
                  : f == kFamDelta ? la::delta_ws_floats(slots, (long)sm.H * sm.chunk_recs_per_head(la::kChunk), dk, dv)
                                   : la::ssd_ws_floats(slots, dk, dv);
     return p;
 }
 
 // Shape checks shared by every prefill call.  Returns LA_OK or a status.
-la_status check_batch(const char* fn, const Batch& b, int dk, int dv, int dtype, int chunk) {
+// blocked: the caller also runs the blocked LA path (uniform batches, chunk
+// sizes other than 64).
+la_status check_batch(const char* fn, const Batch& b, int dk, int dv, int dtype, int chunk, bool blocked = false) {
     if (b.N < 1 || b.H < 1 || b.T < 1 || dk < 1 || dv < 1)
         return fail(LA_ERR_INVALID_ARG, "%s: sizes must be >= 1 (%s=%d H=%d T=%d dk=%d dv=%d)", fn,
                     b.packed() ? "N" : "B", b.N, b.H, b.T, dk, dv);
@@ -146,8 +152,13 @@ la_status check_batch(const char* fn, const Batch& b, int dk, int dv, int dtype,
         return fail(LA_ERR_UNSUPPORTED, "%s: %ld (sequence, head) pairs exceed 2^24", fn, (long)b.N * b.H);
     if (!supported_dim(dk) || !supported_dim(dv))
         return fail(LA_ERR_UNSUPPORTED, "%s: dk=%d dv=%d not in {64, 128}", fn, dk, dv);
-    if (chunk != la::kChunk)
-        return fail(LA_ERR_UNSUPPORTED, "%s: chunk=%d not supported (only %d)", fn, chunk, la::kChunk);
+    if (chunk != la::kChunk) {
+        if (!blocked || b.packed())
+            return fail(LA_ERR_UNSUPPORTED, "%s: chunk=%d not supported (only %d)", fn, chunk, la::kChunk);
+        if (!la::la_chunked_supported(chunk, dtype == LA_BF16 ? 1 : 0))
+            return fail(LA_ERR_UNSUPPORTED,
+                        "%s: chunk=%d not supported (bf16: 16, 32, 64, 128; fp32: 16, 32, 64)", fn, chunk);
+    }
     // The kernels address one (sequence, head)'s rows through buffer
     // resources of 32-bit size with 32-bit signed byte offsets, and read up
     // to four chunks ahead of the row being processed: every such offset must
@@ -195,8 +206,8 @@ size_t workspace_query(const char* fn, Family f, const Batch& b, int dk, int dv,
     if (b.packed() && b.N < 1) return 0;
     Batch bb = b;
     if (b.packed() && !bb.cu_dev) bb.cu_dev = b.cu_host;  // only its presence is checked here
-    if (check_batch(fn, bb, dk, dv, LA_BF16, chunk) != LA_OK) return 0;
-    return make_plan(f, b, dk, dv).bytes();
+    if (check_batch(fn, bb, dk, dv, LA_BF16, chunk, f == kFamLA) != LA_OK) return 0;
+    return make_plan(f, b, dk, dv, chunk).bytes();
 }
 
 // Tags for the look-back flags of la_forward: a process-wide counter from a
@@ -254,21 +265,26 @@ la_status la_forward_impl(const char* fn, const void* q, const void* k, const vo
     if (!q || !k || !v || !o) return fail(LA_ERR_INVALID_ARG, "%s: q, k, v and o must be non-NULL", fn);
     if (!(eps > 0.f) || !isfinite(eps))
         return fail(LA_ERR_INVALID_ARG, "%s: eps must be finite and > 0 (got %g)", fn, (double)eps);
-    la_status st = check_batch(fn, b, dk, dv, dtype, chunk);
+    la_status st = check_batch(fn, b, dk, dv, dtype, chunk, true);
     if (st != LA_OK) return st;
-    if (dtype == LA_F32 && la::la_lds_bytes(dk, dv, dtype) > 160 * 1024)
+    if (chunk == la::kChunk && dtype == LA_F32 && la::la_lds_bytes(dk, dv, dtype) > 160 * 1024)
         return fail(LA_ERR_UNSUPPORTED, "%s: fp32 with dk=%d dv=%d exceeds the 160 KiB LDS", fn, dk, dv);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return fail(LA_ERR_INVALID_ARG, "%s: q, k, v and o must be 16-byte aligned", fn);
-    Plan plan = make_plan(kFamLA, b, dk, dv);
+    Plan plan = make_plan(kFamLA, b, dk, dv, chunk);
     if ((st = check_plan(fn, plan)) != LA_OK) return st;
     if ((st = check_workspace(fn, plan, workspace, workspace_bytes)) != LA_OK) return st;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     float* ws = nullptr;
     hipError_t e = bind_workspace(plan, b, workspace, hs, &ws);
-    if (e == hipSuccess)
-        e = la::launch_la_forward(q, k, v, S0, z0, o, S_out, z_out, plan.sm, dk, dv, dtype, eps, ws, next_tag(),
-                                  stream_capturing(hs), poll_limit, hs);
+    if (e == hipSuccess) {
+        if (chunk == la::kChunk)
+            e = la::launch_la_forward(q, k, v, S0, z0, o, S_out, z_out, plan.sm, dk, dv, dtype, eps, ws, next_tag(),
+                                      stream_capturing(hs), poll_limit, hs);
+        else  // the blocked path: segment sums, their prefix, chunk loops of `chunk` tokens
+            e = la::launch_la_forward_chunked(q, k, v, S0, z0, o, S_out, z_out, plan.sm, dk, dv,
+                                              dtype == LA_BF16 ? 1 : 0, eps, chunk, ws, hs);
+    }
     return hip_status(fn, e);
 }
 
