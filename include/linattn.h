@@ -43,8 +43,9 @@
  * - Validation first: arguments are checked before anything is launched; on
  *   any non-OK status nothing has been enqueued and no buffer was written.
  *   la_last_error() then describes the problem (per calling thread).
- * - Supported: dk, dv in {64, 128}; chunk == 64, and for la_forward on
- *   uniform batches also 16, 32 and 128 (LA_F32: 16 and 32); dtype LA_BF16
+ * - Supported: dk, dv in {64, 128}; chunk == 64, and for la_forward and
+ *   delta_forward on uniform batches also 16, 32 and 128 (la_forward with
+ *   LA_F32: 16 and 32); dtype LA_BF16
  *   everywhere and LA_F32 for la_forward (at chunk 64, dk = 128 with
  *   dv = 128 excluded) and the decode steps.  Forgetting gates alpha are
  *   fp32 for every dtype.
@@ -163,8 +164,8 @@ la_status la_forward_noalloc(const void* q, const void* k, const void* v,
 /*
  * Bytes of device workspace delta_forward (and gated_delta_forward,
  * delta_forward_ex) needs; 0 if the sizes are invalid.  The workspace holds
- * the per-segment affine maps and states (fp32) and one record per 64-token
- * chunk of the chunk's triangular inverse T = (I + A)^{-1} (bf16, 8 KiB).
+ * the per-segment affine maps and states (fp32) and, at chunk 64, one record
+ * per chunk of the chunk's triangular inverse T = (I + A)^{-1} (bf16, 8 KiB).
  */
 size_t delta_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
 
@@ -177,6 +178,11 @@ size_t delta_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int ch
  * overwrite property needs unit keys, which the caller provides.
  * beta     [B][H][T], dtype: the final per-token step size (no transform).
  * S0       initial state, NULL = zero.  S_out final state (may alias S0), or NULL.
+ * chunk    64, or 16, 32, 128: a blocked path (segment maps by chunk loops of
+ *          `chunk` tokens, their composition, chunk loops writing o) whose
+ *          result matches the 64-token one up to rounding ([Recurrence]
+ *          "Chunked scan").  gated_delta_forward, delta_forward_ex and the
+ *          packed batches take 64 only (others: LA_ERR_UNSUPPORTED).
  * Errors: as la_forward (beta NULL is LA_ERR_INVALID_ARG).
  */
 la_status delta_forward(const void* q, const void* k, const void* v, const void* beta,

@@ -76,6 +76,7 @@ def _delta(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(beta=None), "INVALID_ARG"), (dict(T=0), "INVALID_ARG"), (dict(chunk=-3), "INVALID_ARG"),
     (dict(dtype=3), "INVALID_ARG"), (dict(dk=100), "UNSUPPORTED"), (dict(dtype=0), "UNSUPPORTED"),
+    (dict(chunk=48), "UNSUPPORTED"), (dict(chunk=256), "UNSUPPORTED"),
     (dict(ws=None), "WORKSPACE"), (dict(wsb=0), "WORKSPACE"),
 ])
 def test_delta_forward_rejects(kw, status):
@@ -129,7 +130,8 @@ def _gdelta(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(alpha=None), "INVALID_ARG"), (dict(beta=None), "INVALID_ARG"), (dict(T=0), "INVALID_ARG"),
     (dict(alpha=ctypes.c_void_p(0x10002)), "INVALID_ARG"), (dict(dk=100), "UNSUPPORTED"),
-    (dict(dtype=0), "UNSUPPORTED"), (dict(ws=None), "WORKSPACE"), (dict(wsb=0), "WORKSPACE"),
+    (dict(dtype=0), "UNSUPPORTED"), (dict(chunk=32), "UNSUPPORTED"),  # other chunk sizes: the plain rule only
+    (dict(ws=None), "WORKSPACE"), (dict(wsb=0), "WORKSPACE"),
 ])
 def test_gated_delta_forward_rejects(kw, status):
     assert _gdelta(**kw) == ST[status]
@@ -199,7 +201,8 @@ def _dex(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(flags=4), "INVALID_ARG"), (dict(flags=-1), "INVALID_ARG"), (dict(beta=None), "INVALID_ARG"),
     (dict(pred=ctypes.c_void_p(0x10001)), "INVALID_ARG"), (dict(T=0), "INVALID_ARG"), (dict(dk=32), "UNSUPPORTED"),
-    (dict(dtype=0), "UNSUPPORTED"), (dict(ws=None), "WORKSPACE"),
+    (dict(dtype=0), "UNSUPPORTED"), (dict(chunk=16), "UNSUPPORTED"), (dict(chunk=128, flags=0, pred=P), "UNSUPPORTED"),
+    (dict(ws=None), "WORKSPACE"),
 ])
 def test_delta_forward_ex_rejects(kw, status):
     assert _dex(**kw) == ST[status]
@@ -377,9 +380,11 @@ def test_chunk_size_workspace_queries():
     E = 64 * 128 + 64
     n16 = L.la_forward_workspace_bytes(1, 1, 100000, 64, 128, 16)
     assert n16 % (2 * 4 * E) == 0 and n16 == L.la_forward_workspace_bytes(1, 1, 100000, 64, 128, 32)
-    # the other families and the packed batches take 64 only
+    # delta_forward too (three per-slot arrays, no chunk records); the
+    # scalar-decay rule and the packed batches take 64 only
     for C in (16, 32, 128):
-        assert L.delta_forward_workspace_bytes(2, 16, 16384, 128, 128, C) == 0
+        n = L.delta_forward_workspace_bytes(2, 16, 16384, 128, 128, C)
+        assert n > 0 and n % (4 * (2 * 128 * 128 + 128 * 128)) == 0, C
         assert L.ssd_forward_workspace_bytes(4, 8, 8192, 64, 64, C) == 0
         cu = (ctypes.c_int * 3)(0, 5, 9)
         assert L.la_forward_packed_workspace_bytes(ctypes.cast(cu, ctypes.c_void_p), 2, 2, 9, 64, 64, C) == 0

@@ -100,9 +100,9 @@ Plan make_plan(Family f, const Batch& b, int dk, int dv, int chunk = la::kChunk)
             sm.L = (int)((nch + want - 1) / want) * la::kChunk;
         } else {
             sm.L = la::la_plan(b.N * b.H, b.T, dk, dv).L;
-            // the blocked LA path (chunk != 64) needs whole chunks per segment
-            if (chunk > la::kChunk) sm.L = (sm.L + chunk - 1) / chunk * chunk;
         }
+        // the blocked paths (chunk != 64) need whole chunks per segment
+        if (chunk > la::kChunk) sm.L = (sm.L + chunk - 1) / chunk * chunk;
         sm.G = (b.T + sm.L - 1) / sm.L;
         sm.NS = b.N * sm.G;
     } else {
@@ -121,14 +121,17 @@ Plan make_plan(Family f, const Batch& b, int dk, int dv, int chunk = la::kChunk)
     const long slots = (long)sm.H * sm.NS;
     p.fam_floats = f == kFamLA ? (chunk == la::kChunk ? la::la_ws_floats(slots, (long)b.N * b.H, dk, dv)
                                                       : la::la_chunked_ws_floats(slots, dk, dv))
-                 : f == kFamDelta ? la::delta_ws_floats(slots, (long)sm.H * sm.chunk_recs_per_head(la::kChunk), dk, dv)
+                 : f == kFamDelta ? (chunk == la::kChunk
+                                         ? la::delta_ws_floats(slots, (long)sm.H * sm.chunk_recs_per_head(la::kChunk), dk, dv)
+                                         : la::delta_chunked_ws_floats(slots, dk, dv))
                                   : la::ssd_ws_floats(slots, dk, dv);
     return p;
 }
 
 // Shape checks shared by every prefill call.  Returns LA_OK or a status.
-// blocked: the caller also runs the blocked LA path (uniform batches, chunk
-// sizes other than 64).
+// blocked: the caller also runs a blocked path (uniform batches, chunk sizes
+// other than 64: la_forward, and delta_forward without gates, transforms or
+// predictions).
 la_status check_batch(const char* fn, const Batch& b, int dk, int dv, int dtype, int chunk, bool blocked = false) {
     if (b.N < 1 || b.H < 1 || b.T < 1 || dk < 1 || dv < 1)
         return fail(LA_ERR_INVALID_ARG, "%s: sizes must be >= 1 (%s=%d H=%d T=%d dk=%d dv=%d)", fn,
@@ -206,7 +209,7 @@ size_t workspace_query(const char* fn, Family f, const Batch& b, int dk, int dv,
     if (b.packed() && b.N < 1) return 0;
     Batch bb = b;
     if (b.packed() && !bb.cu_dev) bb.cu_dev = b.cu_host;  // only its presence is checked here
-    if (check_batch(fn, bb, dk, dv, LA_BF16, chunk, f == kFamLA) != LA_OK) return 0;
+    if (check_batch(fn, bb, dk, dv, LA_BF16, chunk, f == kFamLA || f == kFamDelta) != LA_OK) return 0;
     return make_plan(f, b, dk, dv, chunk).bytes();
 }
 
@@ -297,22 +300,30 @@ la_status delta_forward_impl(const char* fn, const void* q, const void* k, const
                              const Batch& b, int dk, int dv, int dtype, int chunk, void* workspace,
                              size_t workspace_bytes, void* stream) {
     if (flags & ~kKnownFlags) return fail(LA_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, flags);
-    la_status st = check_batch(fn, b, dk, dv, dtype, chunk);
+    la_status st = check_batch(fn, b, dk, dv, dtype, chunk, true);
     if (st != LA_OK) return st;
     if (dtype != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "%s: only bf16 inputs are supported", fn);
+    if (chunk != la::kChunk && (alpha || flags || pred))
+        return fail(LA_ERR_UNSUPPORTED, "%s: chunk=%d is for the plain rule without transforms (only %d here)", fn,
+                    chunk, la::kChunk);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return fail(LA_ERR_INVALID_ARG, "%s: q, k, v and o must be 16-byte aligned", fn);
     if ((reinterpret_cast<uintptr_t>(beta) & 1u) || (reinterpret_cast<uintptr_t>(alpha) & 3u) ||
         (reinterpret_cast<uintptr_t>(pred) & 1u))
         return fail(LA_ERR_INVALID_ARG, "%s: beta, alpha and pred must be aligned to their element size", fn);
-    Plan plan = make_plan(kFamDelta, b, dk, dv);
+    Plan plan = make_plan(kFamDelta, b, dk, dv, chunk);
     if ((st = check_plan(fn, plan)) != LA_OK) return st;
     if ((st = check_workspace(fn, plan, workspace, workspace_bytes)) != LA_OK) return st;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     float* ws = nullptr;
     hipError_t e = bind_workspace(plan, b, workspace, hs, &ws);
-    if (e == hipSuccess)
-        e = la::launch_delta_forward(q, k, v, beta, alpha, S0, o, S_out, pred, flags, plan.sm, dk, dv, dtype, ws, hs);
+    if (e == hipSuccess) {
+        if (chunk == la::kChunk)
+            e = la::launch_delta_forward(q, k, v, beta, alpha, S0, o, S_out, pred, flags, plan.sm, dk, dv, dtype, ws,
+                                         hs);
+        else  // the blocked path: segment maps, their composition, chunk loops of `chunk` tokens
+            e = la::launch_delta_forward_chunked(q, k, v, beta, S0, o, S_out, plan.sm, dk, dv, chunk, ws, hs);
+    }
     return hip_status(fn, e);
 }
 

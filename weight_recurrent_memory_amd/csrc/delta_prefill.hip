@@ -54,6 +54,7 @@
 #include "common.hpp"
 #include "delta_chunk.hpp"
 #include "kernels.hpp"
+#include "la_chunked.hpp"
 
 namespace la {
 
@@ -887,6 +888,23 @@ hipError_t launch_delta_states(const void* q, const void* k, const void* v, cons
     STATES_CASE(128, 64)
     STATES_CASE(128, 128)
 #undef STATES_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_delta_compose(const float* map_n, const float* map_m, const float* S0, float* state_in,
+                                const SegMap& sm, int dk, int dv, hipStream_t stream) {
+    if (sm.packed()) return hipErrorInvalidValue;
+#define FWD_CASE(A, B)                                                                                        \
+    if (dk == A && dv == B) {                                                                                 \
+        delta_compose_kernel<A, B, false><<<dim3(compose_blocks<B>(sm.N * sm.H)), dim3(256), 0, stream>>>(   \
+            map_n, map_m, S0, state_in, sm);                                                                  \
+        return hipGetLastError();                                                                             \
+    }
+    FWD_CASE(64, 64)
+    FWD_CASE(64, 128)
+    FWD_CASE(128, 64)
+    FWD_CASE(128, 128)
+#undef FWD_CASE
     return hipErrorInvalidValue;
 }
 
