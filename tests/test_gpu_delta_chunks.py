@@ -90,3 +90,13 @@ def test_delta_chunk_size_exact_overwrite_basis_keys():
     o, S = lin.delta_forward(k, k, v, beta, chunk=C)
     torch.cuda.synchronize()
     assert torch.equal(o.float().cpu(), v.float().cpu())
+
+
+@pytest.mark.parametrize("C", [16, 32, 128])
+def test_delta_chunk_size_is_bitwise_repeatable(C):
+    q, k, v, beta = wl.delta_inputs(2, 4, 2500, 128, 128, torch.bfloat16, seed=8200 + C, device=DEV)
+    S0, _ = wl.decode_state(2, 4, 128, 128, seed=82, device=DEV, std=0.5)
+    a = lin.delta_forward(q, k, v, beta, S0, chunk=C)
+    b = lin.delta_forward(q, k, v, beta, S0, chunk=C)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])

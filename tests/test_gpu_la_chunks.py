@@ -98,3 +98,14 @@ def test_la_chunk_size_continues_in_place(C):
                    o=o2, S_out=S, z_out=z)
     torch.cuda.synchronize()
     _check(q, k, v, torch.cat([o1, o2], dim=2), S, z)
+
+
+@pytest.mark.parametrize("C,dtype", [(16, torch.float32), (32, torch.bfloat16), (128, torch.bfloat16)])
+def test_la_chunk_size_is_bitwise_repeatable(C, dtype):
+    # fixed summation order, no atomics: the same inputs give the same bits
+    q, k, v = wl.la_inputs(2, 4, 3000, 64, 64, dtype, seed=7300 + C, device=DEV)
+    a = lin.la_forward(q, k, v, eps=EPS, chunk=C)
+    b = lin.la_forward(q, k, v, eps=EPS, chunk=C)
+    torch.cuda.synchronize()
+    for name, x, y in zip(("o", "S", "z"), a, b):
+        assert torch.equal(x, y), name

@@ -35,6 +35,17 @@ def test_noalloc_equals_la_forward_on_consecutive_calls(shapes):
             assert torch.equal(g, r), name
 
 
+@pytest.mark.parametrize("chunk", [16, 128])
+def test_noalloc_equals_la_forward_at_other_chunk_sizes(chunk):
+    # the blocked path on the scratch: segment sums and entering states
+    q, k, v, S0, z0 = _inputs(2, 3, 5000, seed=chunk, init=True)
+    ref = lin.la_forward(q, k, v, S0, z0, eps=EPS, chunk=chunk)
+    got = lin.la_forward_noalloc(q, k, v, S0, z0, eps=EPS, chunk=chunk)
+    torch.cuda.synchronize()
+    for name, g, r in zip(("o", "S", "z"), got, ref):
+        assert torch.equal(g, r), name
+
+
 def test_noalloc_in_place_continuation():
     q, k, v, S0, z0 = _inputs(2, 16, 5100, seed=5, init=True)
     ref = lin.la_forward(q, k, v, S0.clone(), z0.clone(), eps=EPS)
