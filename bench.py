@@ -328,6 +328,49 @@ def bench_delta_backward(w, steps, warmup, copies, lin, wl):
             "bytes": nbytes, "gbs": nbytes / (mean_ms * 1e-3) / 1e9}
 
 
+def bench_delta_train(w, steps, warmup, copies, lin, wl):
+    """One training step of the delta rule (gated for a gated workload):
+    the forward and the backward of a random dO, timed twice -- as
+    delta_forward + delta_backward (the backward recomputes the forward's
+    context) and as delta_forward_train + delta_backward_after_forward (the
+    forward keeps it)."""
+    dev = torch.device("cuda:0")
+    gated = w.kind == "gated_delta"
+    sets = []
+    for i in range(copies):
+        q, k, v, beta = wl.delta_inputs(w.B, w.H, w.T, w.dk, w.dv, w.dtype, w.seed + 17 * i, dev)
+        dO = wl.la_inputs(w.B, w.H, w.T, w.dv, w.dv, w.dtype, w.seed + 17 * i + 1, dev)[0]
+        alpha = wl.gates((w.B, w.H, w.T), w.seed + 17 * i, dev) if gated else None
+        sets.append((q, k, v, beta, dO, alpha))
+    outs = [torch.empty((w.B, w.H, w.T, w.dv), dtype=w.dtype, device=dev) for _ in range(copies)]
+    grads = [tuple(torch.empty_like(x) for x in st[:3]) for st in sets]
+    S = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(lin.delta_backward_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv), dtype=torch.uint8, device=dev)
+
+    def separate(i):
+        q, k, v, beta, dO, alpha = sets[i % copies]
+        dq, dk, dv = grads[i % copies]
+        if gated:
+            lin.gated_delta_forward(q, k, v, beta, alpha, o=outs[i % copies], S_out=S, workspace=ws)
+        else:
+            lin.delta_forward(q, k, v, beta, o=outs[i % copies], S_out=S, workspace=ws)
+        lin.delta_backward(q, k, v, beta, dO, alpha, dq=dq, dk=dk, dv=dv, return_state_grad=False, workspace=ws)
+
+    def paired(i):
+        q, k, v, beta, dO, alpha = sets[i % copies]
+        dq, dk, dv = grads[i % copies]
+        lin.delta_forward_train(q, k, v, beta, alpha, o=outs[i % copies], S_out=S, workspace=ws)
+        lin.delta_backward_after_forward(q, k, v, beta, dO, ws, alpha, dq=dq, dk=dk, dv=dv, return_state_grad=False)
+
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for name, fn in (("separate", separate), ("training_pair", paired)):
+        wall, mean_ms, pc_mean, med_ms = time_calls(fn, steps, warmup, stream)
+        res[name] = {"ms_per_step": 1e3 * wall / steps, "us_per_step": 1e3 * mean_ms,
+                     "us_per_step_median": 1e3 * med_ms, "tokens_per_s": w.B * w.T * steps / wall}
+    return res
+
+
 def bench_la_packed(w, steps, warmup, lin, wl):
     """la_forward_packed on a serving batch of mixed request lengths."""
     dev = torch.device("cuda:0")
@@ -466,8 +509,8 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", choices=["all", "la", "la_long", "la_packed", "la_backward", "delta", "gated_delta",
-                                       "delta_backward", "ssd", "decode", "delta_decode", "gated_delta_decode",
-                                       "ssd_decode"],
+                                       "delta_backward", "delta_train", "ssd", "decode", "delta_decode",
+                                       "gated_delta_decode", "ssd_decode"],
                     default="all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baselines")
     ap.add_argument("--decode-steps", type=int, default=None,
@@ -533,6 +576,9 @@ def main():
                                                   "us_per_call_median": 1e3 * r["event_ms_median"],
                                                   "hbm_gbs": r["gbs"],
                                                   "hbm_frac": r["gbs"] / HBM_PEAK_GBS, "bytes_per_call": r["bytes"]}
+    if args.only in ("all", "delta_train"):
+        for wd in (wl.DELTA_BF16_PREFILL, wl.GATED_DELTA_BF16_PREFILL):
+            extra["train_step_" + wd.name] = bench_delta_train(wd, max(5, args.steps // 5), 3, 2, lin, wl)
     if args.only in ("all", "ssd"):
         ws_ = wl.SSD_BF16_PREFILL
         r = bench_ssd(ws_, max(3, args.steps // 2), 3, 4, lin, wl)

@@ -12,6 +12,9 @@
  *   ssd_decode_step          one-token decode of the scalar-decay memory
  *   la_backward              gradients of la_forward (training, with recomputation)
  *   delta_backward           gradients of delta_forward / gated_delta_forward
+ * a training pair for the delta rule that keeps the forward's context for
+ * the backward instead of recomputing it: delta_forward_train,
+ * delta_backward_after_forward;
  * two delta-rule calls with serving options (input transforms, the
  * read-then-write prediction as an extra output): delta_forward_ex,
  * delta_decode_step_ex; and the prefills over packed batches of
@@ -356,6 +359,37 @@ la_status delta_backward(const void* q, const void* k, const void* v, const void
                          void* dq, void* dk_out, void* dv_out, float* dbeta, float* dalpha, float* dS0,
                          int B, int H, int T, int dk, int dv, int dtype, int chunk,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Training pair of the delta rule ([LinearMem] §03: in training by chunks,
+ * the states at chunk boundaries are what the backward pass needs; keeping
+ * them from the forward pass spares their recomputation).
+ *
+ * delta_forward_train: delta_forward (alpha NULL) or gated_delta_forward
+ * (alpha given), with the same arguments, outputs and errors, bf16 only,
+ * whose workspace is a delta_backward workspace (size from
+ * delta_backward_workspace_bytes, 16-byte aligned; LA_ERR_WORKSPACE if
+ * smaller).  Besides o and S_out it leaves in the workspace the context the
+ * backward pass reads: every chunk's correction record, every segment's
+ * affine map and entering state, and every 64-token chunk's entering state
+ * as bf16 tiles.  o and S_out equal delta_forward's bit for bit.
+ *
+ * delta_backward_after_forward: delta_backward with the same arguments,
+ * outputs and errors, given the workspace that a delta_forward_train call
+ * on the same q, k, v, beta, alpha, S0 and sizes filled, unchanged since.
+ * It skips the backward's forward sweep and returns delta_backward's results
+ * bit for bit.  With any other workspace contents the results are
+ * meaningless (nothing detects this); the workspace is overwritten, so a
+ * second backward needs a second forward.
+ */
+la_status delta_forward_train(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
+                              const float* S0, void* o, float* S_out, int B, int H, int T, int dk, int dv,
+                              int dtype, int chunk, void* workspace, size_t workspace_bytes, void* stream);
+la_status delta_backward_after_forward(const void* q, const void* k, const void* v, const void* beta,
+                                       const float* alpha, const float* S0, const void* dO, const float* dS_T,
+                                       void* dq, void* dk_out, void* dv_out, float* dbeta, float* dalpha,
+                                       float* dS0, int B, int H, int T, int dk, int dv, int dtype, int chunk,
+                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Packed batches ([LinearMem] §05: when a request ends only its own state is

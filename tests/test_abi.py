@@ -29,7 +29,7 @@ def test_header_declares_the_operations():
     for name in ("la_forward", "delta_forward", "la_decode_step", "delta_decode_step", "gated_delta_forward",
                  "gated_delta_decode_step", "ssd_forward", "ssd_decode_step", "delta_forward_ex",
                  "delta_decode_step_ex", "la_forward_packed", "delta_forward_packed", "ssd_forward_packed",
-                 "la_backward", "delta_backward"):
+                 "la_backward", "delta_backward", "delta_forward_train", "delta_backward_after_forward"):
         assert name in fns
 
 
@@ -290,12 +290,12 @@ def test_la_backward_rejects(kw, status):
     assert lin.lib().la_last_error().decode().startswith("la_backward")
 
 
-def _dlb(**kw):
+def _dlb(entry="delta_backward", **kw):
     a = dict(q=P, k=P, v=P, beta=P, alpha=None, S0=None, dO=P, dS_T=None, dq=P, dk_out=P, dv_out=P, dbeta=P,
              dalpha=None, dS0=None, B=1, H=1, T=8, dk=128, dv=128, dtype=1, chunk=64, ws=P, wsb=1 << 30,
              stream=None)
     a.update(kw)
-    return lin.lib().delta_backward(a["q"], a["k"], a["v"], a["beta"], a["alpha"], a["S0"], a["dO"], a["dS_T"],
+    return getattr(lin.lib(), entry)(a["q"], a["k"], a["v"], a["beta"], a["alpha"], a["S0"], a["dO"], a["dS_T"],
                                     a["dq"], a["dk_out"], a["dv_out"], a["dbeta"], a["dalpha"], a["dS0"], a["B"],
                                     a["H"], a["T"], a["dk"], a["dv"], a["dtype"], a["chunk"], a["ws"], a["wsb"],
                                     a["stream"])
@@ -314,6 +314,43 @@ def _dlb(**kw):
 def test_delta_backward_rejects(kw, status):
     assert _dlb(**kw) == ST[status]
     assert lin.lib().la_last_error().decode().startswith("delta_backward")
+    # the variant that reads a training forward's context checks the same
+    assert _dlb("delta_backward_after_forward", **kw) == ST[status]
+    assert lin.lib().la_last_error().decode().startswith("delta_backward_after_forward")
+
+
+def _dft(**kw):
+    a = dict(q=P, k=P, v=P, beta=P, alpha=None, S0=None, o=P, S_out=None, B=1, H=1, T=8, dk=128, dv=128, dtype=1,
+             chunk=64, ws=P, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lin.lib().delta_forward_train(a["q"], a["k"], a["v"], a["beta"], a["alpha"], a["S0"], a["o"],
+                                         a["S_out"], a["B"], a["H"], a["T"], a["dk"], a["dv"], a["dtype"],
+                                         a["chunk"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), "INVALID_ARG"), (dict(beta=None), "INVALID_ARG"), (dict(o=None), "INVALID_ARG"),
+    (dict(T=0), "INVALID_ARG"), (dict(H=-1), "INVALID_ARG"), (dict(dtype=3), "INVALID_ARG"),
+    (dict(dtype=0), "UNSUPPORTED"), (dict(dk=96), "UNSUPPORTED"), (dict(chunk=32), "UNSUPPORTED"),
+    (dict(o=ctypes.c_void_p(0x10008)), "INVALID_ARG"), (dict(beta=ctypes.c_void_p(0x10001)), "INVALID_ARG"),
+    (dict(alpha=ctypes.c_void_p(0x10002)), "INVALID_ARG"), (dict(S_out=ctypes.c_void_p(0x10002)), "INVALID_ARG"),
+    (dict(ws=None), "WORKSPACE"), (dict(ws=ctypes.c_void_p(0x10008)), "WORKSPACE"),
+])
+def test_delta_forward_train_rejects(kw, status):
+    assert _dft(**kw) == ST[status]
+    assert lin.lib().la_last_error().decode().startswith("delta_forward_train")
+
+
+def test_delta_forward_train_needs_the_backward_workspace():
+    # a forward-sized workspace is too small: the training forward also
+    # keeps every chunk's entering state for the backward
+    L = lin.lib()
+    B, H, T = 2, 4, 1000
+    fwd = L.delta_forward_workspace_bytes(B, H, T, 128, 128, 64)
+    bwd = L.delta_backward_workspace_bytes(B, H, T, 128, 128, 64)
+    assert 0 < fwd < bwd
+    assert _dft(B=B, H=H, T=T, wsb=fwd) == ST["WORKSPACE"]
+    assert str(bwd) in L.la_last_error().decode()
 
 
 @pytest.mark.parametrize("dk,dv,dtype", [(128, 128, 1), (64, 64, 1), (64, 128, 0)])

@@ -102,6 +102,10 @@ def lib():
             L.delta_backward.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, vp, vp, vp, fp, fp, fp, i, i, i, i, i, i,
                                          i, vp, sz, vp]
             L.delta_backward.restype = i
+            L.delta_forward_train.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, i, i, i, i, i, i, i, vp, sz, vp]
+            L.delta_forward_train.restype = i
+            L.delta_backward_after_forward.argtypes = L.delta_backward.argtypes
+            L.delta_backward_after_forward.restype = i
             L.la_status_string.argtypes = [i]
             L.la_status_string.restype = ctypes.c_char_p
             L.la_last_error.argtypes = []
@@ -622,6 +626,53 @@ def delta_backward(q, k, v, beta, dO, alpha=None, S0=None, dS_T=None, chunk=CHUN
     None) or gated_delta_forward (bf16).  Returns (dq, dk, dv, dbeta,
     dalpha, dS0); dbeta and dalpha are fp32 [B,H,T] (dalpha None for the
     plain rule), dS0 None when return_state_grad is False."""
+    return _delta_backward("delta_backward", q, k, v, beta, dO, alpha, S0, dS_T, chunk, dq, dk, dv,
+                           return_state_grad, workspace)
+
+
+def delta_forward_train(q, k, v, beta, alpha=None, S0=None, chunk=CHUNK, *, o=None, S_out=None, workspace=None,
+                        return_state=True):
+    """delta_forward (alpha None) or gated_delta_forward that also leaves the
+    backward pass's context in its workspace (a delta_backward workspace,
+    allocated when None).  Returns (o, S_T, workspace); hand the workspace to
+    delta_backward_after_forward with the same inputs."""
+    code = _dtype_code(q)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(k, "k", q.dtype, (B, H, T, dk), dev)
+    _need(v, "v", q.dtype, (B, H, T, dv), dev)
+    _need(beta, "beta", q.dtype, (B, H, T), dev)
+    _need(q, "q", q.dtype, (B, H, T, dk), dev)
+    if alpha is not None:
+        _need(alpha, "alpha", torch.float32, (B, H, T), dev)
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (B, H, dk, dv), dev)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
+    _need(o, "o", q.dtype, (B, H, T, dv), dev)
+    if return_state:
+        if S_out is None:
+            S_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        _need(S_out, "S_out", torch.float32, (B, H, dk, dv), dev)
+    ws, wsb = _workspace(delta_backward_workspace_bytes(B, H, T, dk, dv, chunk), dev, workspace)
+    _check(lib().delta_forward_train(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S0), _ptr(o),
+                                     _ptr(S_out), B, H, T, dk, dv, code, int(chunk), _ptr(ws), wsb, _stream(dev)))
+    return o, S_out, ws
+
+
+def delta_backward_after_forward(q, k, v, beta, dO, workspace, alpha=None, S0=None, dS_T=None, chunk=CHUNK, *,
+                                 dq=None, dk=None, dv=None, return_state_grad=True):
+    """delta_backward on the workspace a delta_forward_train call with the
+    same inputs filled (its forward sweep is not run again; the workspace's
+    context is consumed).  Returns what delta_backward returns."""
+    if workspace is None:
+        raise ValueError("delta_backward_after_forward needs the workspace of delta_forward_train")
+    return _delta_backward("delta_backward_after_forward", q, k, v, beta, dO, alpha, S0, dS_T, chunk, dq, dk, dv,
+                           return_state_grad, workspace)
+
+
+def _delta_backward(entry, q, k, v, beta, dO, alpha, S0, dS_T, chunk, dq, dk, dv, return_state_grad, workspace):
     code = _dtype_code(q)
     B, H, T, dkk = q.shape
     dvv = v.shape[-1]
@@ -645,7 +696,7 @@ def delta_backward(q, k, v, beta, dO, alpha=None, S0=None, dS_T=None, chunk=CHUN
     dalpha = torch.empty((B, H, T), dtype=torch.float32, device=dev) if alpha is not None else None
     dS0 = torch.empty((B, H, dkk, dvv), dtype=torch.float32, device=dev) if return_state_grad else None
     ws, wsb = _workspace(delta_backward_workspace_bytes(B, H, T, dkk, dvv, chunk), dev, workspace)
-    _check(lib().delta_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S0), _ptr(dO), _ptr(dS_T),
-                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dalpha), _ptr(dS0), B, H, T, dkk, dvv,
-                                code, int(chunk), _ptr(ws), wsb, _stream(dev)))
+    _check(getattr(lib(), entry)(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S0), _ptr(dO), _ptr(dS_T),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dalpha), _ptr(dS0), B, H, T, dkk,
+                                 dvv, code, int(chunk), _ptr(ws), wsb, _stream(dev)))
     return dq, dk, dv, dbeta, dalpha, dS0

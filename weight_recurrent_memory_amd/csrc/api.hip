@@ -567,11 +567,17 @@ size_t delta_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int c
                                                         dk, dv);
 }
 
-la_status delta_backward(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
-                         const float* S0, const void* dO, const float* dS_T, void* dq, void* dk_out, void* dv_out,
-                         float* dbeta, float* dalpha, float* dS0, int B, int H, int T, int dk, int dv, int dtype,
-                         int chunk, void* workspace, size_t workspace_bytes, void* stream) {
-    const char* fn = "delta_backward";
+}  // extern "C"
+
+namespace {
+
+// delta_backward's checks and launch; after_forward: the workspace holds the
+// context of delta_forward_train on the same inputs.
+la_status delta_backward_impl(const char* fn, const void* q, const void* k, const void* v, const void* beta,
+                              const float* alpha, const float* S0, const void* dO, const float* dS_T, void* dq,
+                              void* dk_out, void* dv_out, float* dbeta, float* dalpha, float* dS0, int B, int H,
+                              int T, int dk, int dv, int dtype, int chunk, void* workspace, size_t workspace_bytes,
+                              void* stream, bool after_forward) {
     if (!q || !k || !v || !beta || !dO || !dq || !dk_out || !dv_out || !dbeta)
         return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, beta, dO, dq, dk, dv and dbeta must be non-NULL", fn);
     if (!alpha != !dalpha)
@@ -598,7 +604,58 @@ la_status delta_backward(const void* q, const void* k, const void* v, const void
                     workspace ? workspace_bytes : (size_t)0);
     return hip_status(fn, la::launch_delta_backward(q, k, v, beta, alpha, S0, dO, dS_T, dq, dk_out, dv_out, dbeta,
                                                     dalpha, dS0, plan.sm, dk, dv, dtype,
-                                                    static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
+                                                    static_cast<float*>(workspace), static_cast<hipStream_t>(stream),
+                                                    after_forward));
+}
+
+}  // namespace
+
+extern "C" {
+
+la_status delta_backward(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
+                         const float* S0, const void* dO, const float* dS_T, void* dq, void* dk_out, void* dv_out,
+                         float* dbeta, float* dalpha, float* dS0, int B, int H, int T, int dk, int dv, int dtype,
+                         int chunk, void* workspace, size_t workspace_bytes, void* stream) {
+    return delta_backward_impl("delta_backward", q, k, v, beta, alpha, S0, dO, dS_T, dq, dk_out, dv_out, dbeta,
+                               dalpha, dS0, B, H, T, dk, dv, dtype, chunk, workspace, workspace_bytes, stream, false);
+}
+
+la_status delta_backward_after_forward(const void* q, const void* k, const void* v, const void* beta,
+                                       const float* alpha, const float* S0, const void* dO, const float* dS_T,
+                                       void* dq, void* dk_out, void* dv_out, float* dbeta, float* dalpha,
+                                       float* dS0, int B, int H, int T, int dk, int dv, int dtype, int chunk,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+    return delta_backward_impl("delta_backward_after_forward", q, k, v, beta, alpha, S0, dO, dS_T, dq, dk_out,
+                               dv_out, dbeta, dalpha, dS0, B, H, T, dk, dv, dtype, chunk, workspace, workspace_bytes,
+                               stream, true);
+}
+
+la_status delta_forward_train(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
+                              const float* S0, void* o, float* S_out, int B, int H, int T, int dk, int dv, int dtype,
+                              int chunk, void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "delta_forward_train";
+    if (!q || !k || !v || !beta || !o) return fail(LA_ERR_INVALID_ARG, "%s: q, k, v, beta and o must be non-NULL", fn);
+    const Batch b = uniform(B, H, T);
+    la_status st = check_batch(fn, b, dk, dv, dtype, chunk);
+    if (st != LA_OK) return st;
+    if (dtype != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "%s: only bf16 inputs are supported", fn);
+    if ((long)B * H * ((T + la::kChunk - 1) / la::kChunk) > 0x7fffffffL)
+        return fail(LA_ERR_UNSUPPORTED, "%s: B*H*ceil(T/%d) exceeds 2^31-1", fn, la::kChunk);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(LA_ERR_INVALID_ARG, "%s: q, k, v and o must be 16-byte aligned", fn);
+    if ((reinterpret_cast<uintptr_t>(beta) & 1u) ||
+        ((reinterpret_cast<uintptr_t>(alpha) | reinterpret_cast<uintptr_t>(S0) | reinterpret_cast<uintptr_t>(S_out)) & 3u))
+        return fail(LA_ERR_INVALID_ARG, "%s: beta must be 2-byte and the fp32 arrays 4-byte aligned", fn);
+    const Plan plan = make_plan(kFamDelta, b, dk, dv);
+    if ((st = check_plan(fn, plan)) != LA_OK) return st;
+    const size_t need = delta_backward_workspace_bytes(B, H, T, dk, dv, chunk);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
+        return fail(LA_ERR_WORKSPACE, "%s: workspace of %zu bytes (16-byte aligned; delta_backward_workspace_bytes) "
+                    "required, got %zu", fn, need, workspace ? workspace_bytes : (size_t)0);
+    float* ws = static_cast<float*>(workspace);
+    return hip_status(fn, la::launch_delta_forward_train(q, k, v, beta, alpha, S0, o, S_out,
+                                                         la::delta_backward_states(ws, plan.sm, dk, dv), plan.sm, dk,
+                                                         dv, ws, static_cast<hipStream_t>(stream)));
 }
 
 // ---------------------------------------------------------------- decode

@@ -702,7 +702,8 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
 template <int DK, int DV, bool GATED>
 hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* beta, const float* alpha,
                         const float* S0, const bf16_t* dO, const float* dS_T, bf16_t* dq, bf16_t* dk, bf16_t* dv,
-                        float* dbeta, float* dalpha, float* dS0, const SegMap& sm, float* ws, hipStream_t stream) {
+                        float* dbeta, float* dalpha, float* dS0, const SegMap& sm, float* ws, hipStream_t stream,
+                        bool after_forward) {
     const size_t slots = (size_t)sm.H * sm.NS;
     const int HT = sm.N * sm.H, NC = (sm.T + CH - 1) / CH;
     float* map_c = ws;                       // forward N_g, then c_g
@@ -710,11 +711,13 @@ hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const
     float* g_end = map_mt + slots * DK * DK; // forward segment states, then segment-end gradients
     // the chunk records of T left by the forward sweep, then the chunk-state tiles
     const bf16_t* trec = reinterpret_cast<const bf16_t*>(g_end + slots * DK * DV);
-    bf16_t* sst = reinterpret_cast<bf16_t*>(ws + delta_ws_floats((long)slots, (long)sm.H * sm.chunk_recs_per_head(CH),
-                                                                 DK, DV));
+    bf16_t* sst = static_cast<bf16_t*>(delta_backward_states(ws, sm, DK, DV));
     bf16_t* gst = sst + (size_t)HT * NC * DK * DV;
-    hipError_t err = launch_delta_states(q, k, v, beta, alpha, S0, sst, sm, DK, DV, ws, stream);
-    if (err != hipSuccess) return err;
+    hipError_t err;
+    if (!after_forward) {  // else a training forward left these arrays and the chunk states in ws
+        err = launch_delta_states(q, k, v, beta, alpha, S0, sst, sm, DK, DV, ws, stream);
+        if (err != hipSuccess) return err;
+    }
     if (sm.G > 1) {
         dlb_chain_kernel<DK, DV, true, GATED><<<dim3(HT * (sm.G - 1)), dim3(NT), 0, stream>>>(
             q, k, beta, alpha, dO, nullptr, map_c, nullptr, nullptr, trec, sm);
@@ -745,10 +748,15 @@ size_t delta_backward_ws_floats(long slots, long recs, int HT, int T, int dk, in
     return delta_ws_floats(slots, recs, dk, dv) + (size_t)HT * nc * dk * dv;
 }
 
+void* delta_backward_states(float* ws, const SegMap& sm, int dk, int dv) {
+    const long slots = (long)sm.H * sm.NS;
+    return ws + delta_ws_floats(slots, (long)sm.H * sm.chunk_recs_per_head(CH), dk, dv);
+}
+
 hipError_t launch_delta_backward(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
                                  const float* S0, const void* dO, const float* dS_T, void* dq, void* dk_, void* dv_,
                                  float* dbeta, float* dalpha, float* dS0, const SegMap& sm, int dk, int dv, int dtype,
-                                 float* ws, hipStream_t stream) {
+                                 float* ws, hipStream_t stream, bool after_forward) {
     if (dtype != 1 || sm.packed()) return hipErrorInvalidValue;
     const bf16_t* qb = static_cast<const bf16_t*>(q);
     const bf16_t* kb = static_cast<const bf16_t*>(k);
@@ -761,9 +769,9 @@ hipError_t launch_delta_backward(const void* q, const void* k, const void* v, co
 #define DLB_CASE(A, B)                                                                                         \
     if (dk == A && dv == B)                                                                                    \
         return alpha ? launch_typed<A, B, true>(qb, kb, vb, bb, alpha, S0, ob, dS_T, dqb, dkb, dvb, dbeta,     \
-                                                dalpha, dS0, sm, ws, stream)                                   \
+                                                dalpha, dS0, sm, ws, stream, after_forward)                    \
                      : launch_typed<A, B, false>(qb, kb, vb, bb, nullptr, S0, ob, dS_T, dqb, dkb, dvb, dbeta,  \
-                                                 nullptr, dS0, sm, ws, stream);
+                                                 nullptr, dS0, sm, ws, stream, after_forward);
     DLB_CASE(64, 64)
     DLB_CASE(64, 128)
     DLB_CASE(128, 64)

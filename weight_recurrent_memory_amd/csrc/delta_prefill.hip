@@ -361,7 +361,9 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
         if constexpr (GATED || NWV == 16) asm volatile("" : "+v"(tid_v));
         const int tid = tid_v, lane = tid & 63, g = lane >> 4, li = lane & 15;
         const int n = min(CH, t_end - c0);
-        if constexpr (MODE == kStates) {  // the state entering this chunk, as bf16 tiles
+        // the state entering this chunk, as bf16 tiles: the state pass, and the
+        // output pass of a training forward (uniform batches) when given
+        if (MODE == kStates || (OUT && !PACKED && states != nullptr)) {
             const long ci = ((long)nseq * sm.H + h) * ((sm.T + CH - 1) / CH) + c0 / CH;
 #pragma unroll
             for (int j = 0; j < SLOTS; ++j) {
@@ -803,10 +805,14 @@ __global__ __launch_bounds__(256) void delta_compose_kernel(const float* __restr
     }
 }
 
+// states (uniform batches only; NULL otherwise): a training forward, which
+// also leaves the backward pass's context in ws -- the maps of every segment
+// (the last one's M_g too) and every chunk's entering state as bf16 tiles in
+// `states`.
 template <int DK, int DV, bool GATED, bool PACKED>
 hipError_t launch_packing(const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* beta,
                         const float* alpha, const float* S0, bf16_t* o, float* S_out, bf16_t* pred, int flags,
-                        const SegMap& sm, float* ws, hipStream_t stream) {
+                        const SegMap& sm, float* ws, hipStream_t stream, bf16_t* states = nullptr) {
     const size_t slots = (size_t)sm.H * sm.NS;
     float* map_n = ws;
     float* map_m = map_n + slots * DK * DV;
@@ -816,9 +822,11 @@ hipError_t launch_packing(const bf16_t* q, const bf16_t* k, const bf16_t* v, con
     hipError_t err;
     delta_tinv_kernel<DK, GATED, PACKED><<<dim3(recs), dim3(NT), 0, stream>>>(k, beta, alpha, trec, flags, sm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (sm.NS > sm.N) {
+    const bool train = !PACKED && states != nullptr;
+    if (sm.NS > sm.N) {  // training: every segment's map (M_g of the last for the backward's reverse composition)
         constexpr int NWM = kMapWaves<DK, DV>;
-        delta_chunk_kernel<DK, DV, kMap, GATED, PACKED, NWM><<<dim3(sm.H * (sm.NS - sm.N)), dim3(NWM * 64), 0, stream>>>(
+        const int maps = train ? sm.H * sm.NS : sm.H * (sm.NS - sm.N);
+        delta_chunk_kernel<DK, DV, kMap, GATED, PACKED, NWM><<<dim3(maps), dim3(NWM * 64), 0, stream>>>(
             q, k, v, beta, alpha, nullptr, nullptr, map_n, map_m, nullptr, nullptr, nullptr, trec, flags, sm);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
@@ -827,7 +835,7 @@ hipError_t launch_packing(const bf16_t* q, const bf16_t* k, const bf16_t* v, con
     if ((err = hipGetLastError()) != hipSuccess) return err;
     constexpr int NWO = kOutWaves<DK, DV>;
     delta_chunk_kernel<DK, DV, kOut, GATED, PACKED, NWO><<<dim3(sm.H * sm.NS), dim3(NWO * 64), 0, stream>>>(
-        q, k, v, beta, alpha, o, state_in, nullptr, nullptr, S_out, pred, nullptr, trec, flags, sm);
+        q, k, v, beta, alpha, o, state_in, nullptr, nullptr, S_out, pred, train ? states : nullptr, trec, flags, sm);
     return hipGetLastError();
 }
 
@@ -868,7 +876,37 @@ hipError_t launch_typed(const bf16_t* q, const bf16_t* k, const bf16_t* v, const
                : launch_packing<DK, DV, GATED, false>(q, k, v, beta, alpha, S0, o, S_out, pred, flags, sm, ws, stream);
 }
 
+template <int DK, int DV>
+hipError_t launch_train(const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* beta, const float* alpha,
+                        const float* S0, bf16_t* o, float* S_out, const SegMap& sm, float* ws, bf16_t* states,
+                        hipStream_t stream) {
+    return alpha ? launch_packing<DK, DV, true, false>(q, k, v, beta, alpha, S0, o, S_out, nullptr, 0, sm, ws, stream,
+                                                       states)
+                 : launch_packing<DK, DV, false, false>(q, k, v, beta, nullptr, S0, o, S_out, nullptr, 0, sm, ws,
+                                                        stream, states);
+}
+
 }  // namespace
+
+hipError_t launch_delta_forward_train(const void* q, const void* k, const void* v, const void* beta,
+                                      const float* alpha, const float* S0, void* o, float* S_out, void* states,
+                                      const SegMap& sm, int dk, int dv, float* ws, hipStream_t stream) {
+    if (sm.packed() || !states) return hipErrorInvalidValue;
+    const bf16_t* qb = static_cast<const bf16_t*>(q);
+    const bf16_t* kb = static_cast<const bf16_t*>(k);
+    const bf16_t* vb = static_cast<const bf16_t*>(v);
+    const bf16_t* bb = static_cast<const bf16_t*>(beta);
+    bf16_t* ob = static_cast<bf16_t*>(o);
+    bf16_t* st = static_cast<bf16_t*>(states);
+#define TRAIN_CASE(A, B) \
+    if (dk == A && dv == B) return launch_train<A, B>(qb, kb, vb, bb, alpha, S0, ob, S_out, sm, ws, st, stream);
+    TRAIN_CASE(64, 64)
+    TRAIN_CASE(64, 128)
+    TRAIN_CASE(128, 64)
+    TRAIN_CASE(128, 128)
+#undef TRAIN_CASE
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_delta_states(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
                                const float* S0, void* states, const SegMap& sm, int dk, int dv, float* ws,

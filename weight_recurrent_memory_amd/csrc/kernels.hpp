@@ -71,14 +71,27 @@ hipError_t launch_delta_states(const void* q, const void* k, const void* v, cons
 hipError_t launch_delta_compose_rev(const float* map_c, const float* map_mt, const float* G_last, float* g_end,
                                     const SegMap& sm, int dk, int dv, hipStream_t stream);
 
+// A training forward of the delta rule (uniform batches, bf16, gated when
+// alpha is non-NULL): delta_forward's outputs, and the backward pass's
+// context left in ws (delta_backward_ws_floats(...) floats): the chunk
+// records, every segment's maps and entering state, and every chunk's
+// entering state as bf16 tiles at `states` (= the tiles region of ws).
+hipError_t launch_delta_forward_train(const void* q, const void* k, const void* v, const void* beta,
+                                      const float* alpha, const float* S0, void* o, float* S_out, void* states,
+                                      const SegMap& sm, int dk, int dv, float* ws, hipStream_t stream);
+
 // Backward pass of the delta rule (gated when alpha is non-NULL; uniform
 // batches, bf16): dq, dk, dv (bf16), dbeta, dalpha (fp32 [HT][T]) and
 // optionally dS0 (fp32) for the loss sum dO . o + <dS_T, S_T>.  ws holds
-// delta_backward_ws_floats(...) floats.
+// delta_backward_ws_floats(...) floats.  after_forward: ws already holds the
+// context a training forward on the same inputs left; the forward sweep
+// (T records, maps, composition, chunk states) is not run again.
 hipError_t launch_delta_backward(const void* q, const void* k, const void* v, const void* beta, const float* alpha,
                                  const float* S0, const void* dO, const float* dS_T, void* dq, void* dk_, void* dv_,
                                  float* dbeta, float* dalpha, float* dS0, const SegMap& sm, int dk, int dv, int dtype,
-                                 float* ws, hipStream_t stream);
+                                 float* ws, hipStream_t stream, bool after_forward = false);
+// The bf16 chunk-state tiles region of a delta_backward workspace.
+void* delta_backward_states(float* ws, const SegMap& sm, int dk, int dv);
 size_t delta_backward_ws_floats(long slots, long recs, int HT, int T, int dk, int dv);
 
 // Scalar-decay (Mamba-2 / SSD) prefill: segment maps -> elementwise
