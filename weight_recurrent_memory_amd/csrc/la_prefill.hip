@@ -167,6 +167,31 @@ struct KeptChunks {
     ChunkRegs<TIn, DV, NTHR> v[N];
 };
 
+// One more chunk kept, raw, in LDS: chunk N of the segment (the first chunk
+// after the register-kept ones), where two workgroups per CU still fit with
+// it.  Each thread stores and reloads its own 16-byte pieces, so no barrier
+// orders the two.
+template <typename TIn, int DK, int DV>
+struct LdsKept {
+    static constexpr int NVK = ChunkRegs<TIn, DK, NTHR>::NV, NVV = ChunkRegs<TIn, DV, NTHR>::NV;
+    static constexpr int BYTES = (NVK + NVV) * NTHR * 16;
+    static constexpr bool ON = 2 * (Layout<TIn, DK, DV>::LDS_BYTES + BYTES) <= 160 * 1024;
+    static __device__ __forceinline__ void put(uint4* buf, const ChunkRegs<TIn, DK, NTHR>& kr,
+                                               const ChunkRegs<TIn, DV, NTHR>& vr, int tid) {
+#pragma unroll
+        for (int j = 0; j < NVK; ++j) buf[j * NTHR + tid] = kr.r[j];
+#pragma unroll
+        for (int j = 0; j < NVV; ++j) buf[(NVK + j) * NTHR + tid] = vr.r[j];
+    }
+    static __device__ __forceinline__ void get(const uint4* buf, ChunkRegs<TIn, DK, NTHR>& kr,
+                                               ChunkRegs<TIn, DV, NTHR>& vr, int tid) {
+#pragma unroll
+        for (int j = 0; j < NVK; ++j) kr.r[j] = buf[j * NTHR + tid];
+#pragma unroll
+        for (int j = 0; j < NVV; ++j) vr.r[j] = buf[(NVK + j) * NTHR + tid];
+    }
+};
+
 // The segment's aggregate phi(K)^T [V | 1] over [t0, t1), its groups of NPF
 // chunks taken last to first: the group loaded last is the segment's first
 // NPF chunks, which stay in `kept`.  NPF chunks are in flight ahead of the
@@ -178,7 +203,7 @@ template <typename TIn, int DK, int DV>
 __device__ __forceinline__ void aggregate_keep(const TIn* kh, const TIn* vh, int t0, int t1,
                                                v4f (&acc)[Layout<TIn, DK, DV>::RTW][Layout<TIn, DK, DV>::NCT],
                                                typename Mma<TIn>::op_t* Kb, typename Mma<TIn>::op_t* Vb,
-                                               KeptChunks<TIn, DK, DV>& kept, int tid) {
+                                               KeptChunks<TIn, DK, DV>& kept, uint4* keep_lds, int tid) {
     using LY = Layout<TIn, DK, DV>;
     constexpr int NPF = KeptChunks<TIn, DK, DV>::N, GS = NPF * CH;
     const int lane = tid & 63, w = wave_id(tid);
@@ -198,6 +223,9 @@ __device__ __forceinline__ void aggregate_keep(const TIn* kh, const TIn* vh, int
         typename Mma<TIn>::op_t* Vs = Vb + b * LY::VSZ;
         stage_rows_phi<TIn, DK, NTHR>(kept.k[sl], t1 - c, tid, Ks, LY::LQ);
         stage_rows_raw<TIn, DV, NTHR>(kept.v[sl], tid, Vs, LY::LV);
+        if constexpr (LdsKept<TIn, DK, DV>::ON && sl == 0 && decltype(reload)::value) {
+            if (c == t0 + GS) LdsKept<TIn, DK, DV>::put(keep_lds, kept.k[0], kept.v[0], tid);
+        }
         if constexpr (decltype(reload)::value) {
             kept.k[sl].load_buf(rk, c - GS, tid);
             kept.v[sl].load_buf(rv, c - GS, tid);
@@ -291,8 +319,8 @@ struct OutChunk {
 template <typename TIn, int DK, int DV, int W>
 __device__ __forceinline__ void output_pass(rsrc_t rq, rsrc_t rk, rsrc_t rv, rsrc_t ro, int t_beg, int t_end,
                                             float eps, v4f (&S)[Layout<TIn, DK, DV>::RTW][Layout<TIn, DK, DV>::NCT],
-                                            const KeptChunks<TIn, DK, DV>& kept, OutChunk<TIn, DK, DV>& in,
-                                            typename Mma<TIn>::op_t* lds, int tid) {
+                                            const KeptChunks<TIn, DK, DV>& kept, const uint4* keep_lds,
+                                            OutChunk<TIn, DK, DV>& in, typename Mma<TIn>::op_t* lds, int tid) {
     using M = Mma<TIn>;
     using op = typename M::op_t;
     using frag = typename M::frag;
@@ -333,10 +361,26 @@ __device__ __forceinline__ void output_pass(rsrc_t rq, rsrc_t rk, rsrc_t rv, rsr
 #pragma unroll
         for (int kk = 0; kk < QF; ++kk) qf[b][kk] = M::phi_frag(in.qraw[kk]);
     };
-    // Loads of segment chunk n (starting at c0): queries only while it is kept.
+    // Loads of segment chunk n (starting at c0): queries only while it is kept
+    // (chunk NK: keys and values from the LDS keep, which holds them when the
+    // segment reaches that chunk).
     auto load_chunk = [&](auto nconst, int c0) {
-        if constexpr (decltype(nconst)::value < NK) in.load_q(rq, c0, W, tid);
-        else in.load(rq, rk, rv, c0, W, tid);
+        constexpr int nn = decltype(nconst)::value;
+        if constexpr (nn < NK) {
+            in.load_q(rq, c0, W, tid);
+        } else if constexpr (nn == NK && LdsKept<TIn, DK, DV>::ON) {
+            in.load_q(rq, c0, W, tid);
+            if (c0 < t_end) {
+                LdsKept<TIn, DK, DV>::get(keep_lds, in.kr, in.vr, tid);
+            } else {
+#pragma unroll
+                for (int j = 0; j < LdsKept<TIn, DK, DV>::NVK; ++j) in.kr.r[j] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+                for (int j = 0; j < LdsKept<TIn, DK, DV>::NVV; ++j) in.vr.r[j] = make_uint4(0u, 0u, 0u, 0u);
+            }
+        } else {
+            in.load(rq, rk, rv, c0, W, tid);
+        }
     };
 
     // prologue: chunk 0 staged, chunk 1 in flight
@@ -478,6 +522,7 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
     op* Kb = lds;                    // the two phi(K) chunk buffers, then the two V buffers
     op* Vb = lds + 2 * LY::KSZ;
     __shared__ int lb_count, lb_timeout;   // look-back result (wave 0 -> block)
+    __shared__ uint4 keep_lds[LdsKept<TIn, DK, DV>::ON ? LdsKept<TIn, DK, DV>::BYTES / 16 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int w = wave_id(tid);
@@ -530,7 +575,7 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
 #pragma unroll
         for (int c = 0; c < NCT; ++c) A[i][c] = zero4();
     KeptChunks<TIn, DK, DV> kept;
-    aggregate_keep<TIn, DK, DV>(kh, vh, t_beg, t_end, A, Kb, Vb, kept, tid);
+    aggregate_keep<TIn, DK, DV>(kh, vh, t_beg, t_end, A, Kb, Vb, kept, keep_lds, tid);
 
     // The first chunk's queries are fetched now, so their latency overlaps
     // the look-back.  Buffer resources end at the segment end: reads
@@ -699,10 +744,10 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
 
     // ---- 4. the chunk loop from the incoming state
     switch (w) {
-        case 0: output_pass<TIn, DK, DV, 0>(rq, rk, rv, ro, t_beg, t_end, eps, S, kept, first, lds, tid); break;
-        case 1: output_pass<TIn, DK, DV, 1>(rq, rk, rv, ro, t_beg, t_end, eps, S, kept, first, lds, tid); break;
-        case 2: output_pass<TIn, DK, DV, 2>(rq, rk, rv, ro, t_beg, t_end, eps, S, kept, first, lds, tid); break;
-        default: output_pass<TIn, DK, DV, 3>(rq, rk, rv, ro, t_beg, t_end, eps, S, kept, first, lds, tid); break;
+        case 0: output_pass<TIn, DK, DV, 0>(rq, rk, rv, ro, t_beg, t_end, eps, S, kept, keep_lds, first, lds, tid); break;
+        case 1: output_pass<TIn, DK, DV, 1>(rq, rk, rv, ro, t_beg, t_end, eps, S, kept, keep_lds, first, lds, tid); break;
+        case 2: output_pass<TIn, DK, DV, 2>(rq, rk, rv, ro, t_beg, t_end, eps, S, kept, keep_lds, first, lds, tid); break;
+        default: output_pass<TIn, DK, DV, 3>(rq, rk, rv, ro, t_beg, t_end, eps, S, kept, keep_lds, first, lds, tid); break;
     }
 }
 
@@ -775,7 +820,8 @@ size_t la_ws_floats(long slots, long states, int dk, int dv) {
 
 size_t la_lds_bytes(int dk, int dv, int dtype) {
 #define LDS_CASE(TY, DT, A, B) \
-    if (dtype == DT && dk == A && dv == B) return Layout<TY, A, B>::LDS_BYTES;
+    if (dtype == DT && dk == A && dv == B)   \
+        return Layout<TY, A, B>::LDS_BYTES + (LdsKept<TY, A, B>::ON ? LdsKept<TY, A, B>::BYTES : 0);
     LDS_CASE(bf16_t, 1, 64, 64)
     LDS_CASE(bf16_t, 1, 64, 128)
     LDS_CASE(bf16_t, 1, 128, 64)
