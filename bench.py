@@ -67,14 +67,14 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COUNTERS = {
     # workload name -> kernel, sources, sha256 of the sources, KiB per dispatch
     "la_bf16_b1_h32_t65536_d64": {"kernel": "la_fused_kernel", "sources": LA_SOURCES,
-                                  "sha256": "e6570cd1bdf9d6073549e4a9585e916dfc4f6cb94f4394346c607b6def57f884",
-                                  "fetch_kib": 611282.2, "write_kib": 327789.0},
+                                  "sha256": "e82e19711bce78f54d8706656390dc891af37aaafcf6201ebb9da52ae788cd36",
+                                  "fetch_kib": 594478.1, "write_kib": 327789.0},
     "la_bf16_b4_h8_t8192_d64": {"kernel": "la_fused_kernel", "sources": LA_SOURCES,
-                                "sha256": "e6570cd1bdf9d6073549e4a9585e916dfc4f6cb94f4394346c607b6def57f884",
-                                "fetch_kib": 70044.8, "write_kib": 48397.0},
+                                "sha256": "e82e19711bce78f54d8706656390dc891af37aaafcf6201ebb9da52ae788cd36",
+                                "fetch_kib": 65915.7, "write_kib": 48397.0},
     "decode_bf16_n256_h32_d128_1000steps": {"kernel": "la_decode_kernel", "sources": LA_DECODE_SOURCES,
-                                            "sha256": "8232cc78c4f3cb7749a132aaa1d460fc2383a61bd5b1858a0a82ac5304a817ea",
-                                            "fetch_kib": 267307.3, "write_kib": 530465.6},
+                                            "sha256": "6a650c38b901f6bae18a1c386b5cc801e3311568291c7a03399c545612d14728",
+                                            "fetch_kib": 267306.9, "write_kib": 530465.6},
 }
 
 
@@ -362,12 +362,17 @@ def bench_delta_train(w, steps, warmup, copies, lin, wl):
         lin.delta_forward_train(q, k, v, beta, alpha, o=outs[i % copies], S_out=S, workspace=ws)
         lin.delta_backward_after_forward(q, k, v, beta, dO, ws, alpha, dq=dq, dk=dk, dv=dv, return_state_grad=False)
 
+    def forward_only(i):  # the training forward alone: the pair less this is the backward
+        q, k, v, beta, dO, alpha = sets[i % copies]
+        lin.delta_forward_train(q, k, v, beta, alpha, o=outs[i % copies], S_out=S, workspace=ws)
+
     stream = torch.cuda.current_stream(dev)
     res = {}
-    for name, fn in (("separate", separate), ("training_pair", paired)):
+    for name, fn in (("separate", separate), ("training_pair", paired), ("forward_train", forward_only)):
         wall, mean_ms, pc_mean, med_ms = time_calls(fn, steps, warmup, stream)
         res[name] = {"ms_per_step": 1e3 * wall / steps, "us_per_step": 1e3 * mean_ms,
                      "us_per_step_median": 1e3 * med_ms, "tokens_per_s": w.B * w.T * steps / wall}
+    res["backward_after_forward_us"] = res["training_pair"]["us_per_step"] - res["forward_train"]["us_per_step"]
     return res
 
 
@@ -490,6 +495,19 @@ def calibrate_copy(nbytes=1 << 30):
     print(json.dumps({"calibration_copy_bytes": nbytes, "launches": 3}))
 
 
+def copy_reference(nbytes=1 << 30, calls=20):
+    """What a plain device copy reaches on this GPU (bytes read + bytes
+    written per second), as the practical ceiling the HBM fractions above
+    are read against."""
+    dev = torch.device("cuda:0")
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    wall, mean_ms, pc_mean, med_ms = time_calls(lambda i: b.copy_(a), calls, 5, torch.cuda.current_stream(dev))
+    gbs = 2 * nbytes / (mean_ms * 1e-3) / 1e9
+    return {"bytes_moved_per_copy": 2 * nbytes, "gbs": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS,
+            "us_per_copy": 1e3 * mean_ms}
+
+
 def hbm_roofline(nbytes, r, workload, kernel):
     """The HBM roofline object of one launch: algorithmic bytes over the mean
     per-call duration, and the counter traffic when taken on these sources."""
@@ -509,7 +527,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", choices=["all", "la", "la_long", "la_packed", "la_backward", "delta", "gated_delta",
-                                       "delta_backward", "delta_train", "ssd", "decode", "delta_decode",
+                                       "delta_backward", "delta_train", "copy", "ssd", "decode", "delta_decode",
                                        "gated_delta_decode", "ssd_decode"],
                     default="all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baselines")
@@ -579,6 +597,8 @@ def main():
     if args.only in ("all", "delta_train"):
         for wd in (wl.DELTA_BF16_PREFILL, wl.GATED_DELTA_BF16_PREFILL):
             extra["train_step_" + wd.name] = bench_delta_train(wd, max(5, args.steps // 5), 3, 2, lin, wl)
+    if args.only in ("all", "copy"):
+        extra["hbm_copy_reference_1gib"] = copy_reference()
     if args.only in ("all", "ssd"):
         ws_ = wl.SSD_BF16_PREFILL
         r = bench_ssd(ws_, max(3, args.steps // 2), 3, 4, lin, wl)
