@@ -157,7 +157,7 @@ la_status la_forward_lookback_polls(const void* q, const void* k, const void* v,
  * one GPU (other streams, other host threads) race and must not be issued.
  * What a call leaves in the scratch never changes a later call's result.
  */
-#define LA_NOALLOC_SCRATCH_BYTES (72u << 20)
+#define LA_NOALLOC_SCRATCH_BYTES (96u << 20)
 la_status la_forward_noalloc(const void* q, const void* k, const void* v,
                              const float* S0, const float* z0,
                              void* o, float* S_out, float* z_out,

@@ -380,12 +380,12 @@ def test_lookback_test_hook_validates_like_la_forward():
 def test_noalloc_refuses_beyond_its_scratch_before_touching_the_device():
     L = lin.lib()
     args = [P, P, P, None, None, P, None, None, 1, 64, 65536, 64, 64, 1, 1e-6, 64, None]
-    assert L.la_forward_workspace_bytes(1, 64, 65536, 64, 64, 64) > (72 << 20)
+    assert L.la_forward_workspace_bytes(1, 64, 65536, 64, 64, 64) > (96 << 20)
     assert L.la_forward_noalloc(*args) == ST["UNSUPPORTED"]
     assert "scratch" in L.la_last_error().decode()
     args[10] = 0  # invalid sizes are reported as such
     assert L.la_forward_noalloc(*args) == ST["INVALID_ARG"]
-    assert L.la_forward_workspace_bytes(1, 32, 65536, 64, 64, 64) <= (72 << 20)  # the long-stream size fits
+    assert L.la_forward_workspace_bytes(1, 32, 65536, 64, 64, 64) <= (96 << 20)  # the long-stream size fits
 
 
 def test_workspace_queries():
