@@ -38,7 +38,9 @@
  *   library allocates no device memory; its only state between calls is a
  *   process-wide counter that tags la_forward's look-back flags.  No result
  *   carries over from one call to the next unless passed in as an initial
- *   state ([LinearMem] §05: reset per request by zeroing a slot).  One
+ *   state ([LinearMem] §05: reset per request by zeroing a slot), with one
+ *   exception: delta_backward_after_forward reads the context that
+ *   delta_forward_train left in the workspace passed to both.  One
  *   workspace must not serve two calls that may run at the same time.
  * - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null
  *   stream) and the call returns without synchronising.  Execution-time
