@@ -168,7 +168,8 @@ __global__ __launch_bounds__(NT) void dlb_chain_kernel(
     };
     const int c_last = t0 + ((t_end - 1 - t0) / CH) * CH;
     load_chunk(c_last);
-    dchunk::clear_upper<PL>(Ps, tid);  // (the records carry T's zero blocks)
+    dchunk::clear_upper<PL>(Ps, tid);  // upper blocks of P and of T (the records hold its lower tiles)
+    dchunk::clear_upper<PL>(Ts, tid);
     for (int c0 = c_last; c0 >= t0; c0 -= CH) {
         // Lane indices from an opaque copy, re-derived every chunk: the many
         // per-lane LDS addresses built from them then live next to their uses
@@ -397,7 +398,10 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
         load_rows(ci);
         load_tiles(ci);
     }
-    dchunk::clear_upper<PL>(Ps, tid);  // (the records carry T's zero blocks; E2 and E1 reuse lower tiles only)
+    // upper blocks of P and T (the records hold T's lower tiles; E1 reuses
+    // P's lower tiles only, E2 writes T's zeros back with its own)
+    dchunk::clear_upper<PL>(Ps, tid);
+    dchunk::clear_upper<PL>(Ts, tid);
     for (; ci < total; ci += gridDim.x) {
     // lane indices re-derived per chunk from an opaque copy, so the per-lane
     // LDS addresses are not hoisted out of the loop and held (spilled)

@@ -305,20 +305,37 @@ __device__ __forceinline__ void build_P(const __bf16* Ks, const __bf16* Qs, cons
     }
 }
 
-// A chunk record (a 64 x 64 bf16 matrix, row-major, upper blocks zero) into
-// LDS rows of layout XL; 512 threads, 16 bytes each.
-constexpr int kRecElems = CH * CH;
-__device__ __forceinline__ uint4 load_rec(const bf16_t* rec, int tid) {
-    return *reinterpret_cast<const uint4*>(rec + tid * 8);
+// A chunk record: the ten lower 16 x 16 tiles of a lower block-triangular
+// 64 x 64 bf16 matrix (the upper tiles are zero and not stored), in
+// lower_tile order, each tile's rows of 16 contiguous: 320 pieces of 16
+// bytes (5 KB instead of 8).  Piece p holds row 16 bi + (p / 2) % 16,
+// columns 16 bj + 8 (p % 2) .. + 7 of tile p / 32.  Readers clear the upper
+// tiles of their LDS copy once (clear_upper) and stage only these pieces.
+constexpr int kRecTiles = 10;
+constexpr int kRecElems = kRecTiles * 256;
+constexpr int kRecPieces = kRecElems / 8;
+__device__ __forceinline__ void rec_piece(int p, int& row, int& col) {
+    int bi, bj;
+    lower_tile(p >> 5, bi, bj);
+    row = 16 * bi + ((p >> 1) & 15);
+    col = 16 * bj + 8 * (p & 1);
 }
+// this thread's piece of a record (threads kRecPieces.. hold none)
+__device__ __forceinline__ uint4 load_rec(const bf16_t* rec, int tid) {
+    return tid < kRecPieces ? *reinterpret_cast<const uint4*>(rec + tid * 8) : make_uint4(0u, 0u, 0u, 0u);
+}
+// the piece into LDS rows of layout XL (natural or group-permuted)
 template <class XL = RowLayout<LT>>
 __device__ __forceinline__ void stage_rec(__bf16* Xs, uint4 x, int tid) {
-    __bf16* row = &Xs[(tid >> 3) * XL::LD];
+    if (tid >= kRecPieces) return;
+    int r, c;
+    rec_piece(tid, r, c);
+    __bf16* row = &Xs[r * XL::LD];
     if constexpr (XL::PERM) {
-        *reinterpret_cast<uint2*>(row + pcol((tid & 7) * 8)) = make_uint2(x.x, x.y);
-        *reinterpret_cast<uint2*>(row + pcol((tid & 7) * 8 + 4)) = make_uint2(x.z, x.w);
+        *reinterpret_cast<uint2*>(row + pcol(c)) = make_uint2(x.x, x.y);
+        *reinterpret_cast<uint2*>(row + pcol(c + 4)) = make_uint2(x.z, x.w);
     } else {
-        *reinterpret_cast<uint4*>(row + (tid & 7) * 8) = x;
+        *reinterpret_cast<uint4*>(row + c) = x;
     }
 }
 

@@ -141,7 +141,8 @@ __device__ __forceinline__ void stage_rows_l2(const ChunkRegs<bf16_t, D, NTH>& c
 
 using dchunk::lower_tile;
 
-using dchunk::kRecElems;  // one chunk record: a 64 x 64 bf16 matrix, row-major
+using dchunk::kRecElems;    // one chunk record: T's ten lower 16 x 16 tiles
+using dchunk::kRecPieces;  // its 16-byte pieces
 
 // T = (I + A)^{-1} of every chunk: the state-free, latency-bound part of
 // the chunk recurrence (for the gated rule with the decay ratios in A), done once per
@@ -213,10 +214,13 @@ __global__ __launch_bounds__(NT) void delta_tinv_kernel(const bf16_t* __restrict
     dchunk::clear_upper(Ts, tid);
     __syncthreads();
     dchunk::build_T<DK, GATED, false, false, KL, true>(Ks, nullptr, Bs, Gl, Af, Ad, Yf, Ts, nullptr, w, g, li);
-    // one 16-byte row piece per thread: row tid / 8, columns 8 (tid % 8) ..
-    const int row = tid >> 3, col = (tid & 7) * 8;
-    *reinterpret_cast<uint4*>(trec + rec * kRecElems + row * CH + col) =
-        *reinterpret_cast<const uint4*>(&Ts[row * LT + col]);
+    // the record: T's lower tiles, one 16-byte piece per thread
+    if (tid < kRecPieces) {
+        int row, col;
+        dchunk::rec_piece(tid, row, col);
+        *reinterpret_cast<uint4*>(trec + rec * kRecElems + tid * 8) =
+            *reinterpret_cast<const uint4*>(&Ts[row * LT + col]);
+    }
 }
 
 // One workgroup runs one segment's chunk loop.  The state-dependent part of
@@ -322,7 +326,7 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
     ChunkRegs<bf16_t, NS, NT> vr;
     unsigned short bnext = 0;
     unsigned anext = 0;
-    constexpr int RPT = (512 + NT - 1) / NT;  // 16-byte pieces of a T record per thread
+    constexpr int RPT = (kRecPieces + NT - 1) / NT;  // 16-byte pieces of a T record per thread
     uint4 tnext[RPT];  // this thread's pieces of the chunk's T record
     auto load_chunk = [&](int c, int tid) {
         kr.load_buf(rk, c, tid);
@@ -330,8 +334,8 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
         vr.load_buf(rv, c, tid);
         const long rec = sm.chunk_rec<PACKED>(nseq, h, c / CH, CH) * kRecElems;
 #pragma unroll
-        for (int e = 0; e < RPT; ++e)  // 512 x 16 bytes: one record
-            if (NT * (e + 1) <= 512 || tid + NT * e < 512)
+        for (int e = 0; e < RPT; ++e)  // kRecPieces x 16 bytes: one record
+            if (NT * (e + 1) <= kRecPieces || tid + NT * e < kRecPieces)
                 tnext[e] = *reinterpret_cast<const uint4*>(trec + rec + (tid + NT * e) * 8);
         if (tid < CH) {
             bnext = __builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(c + tid) * 2, 0, 0);
@@ -339,9 +343,9 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
         }
     };
     load_chunk(seg * L, tid);
-    // Upper blocks of P (keys after every query of the tile) are read as
-    // zero operands and never written: clear them once.  (T's records carry
-    // their zero blocks.)
+    // Upper blocks of P (keys after every query of the tile) and of T are
+    // read as zero operands and never written: clear them once.
+    dchunk::clear_upper<RowLayout<LT, true>>(Ts, tid);
     if constexpr (OUT) {
         for (int e = tid; e < 6 * 256; e += NT) {
             const int tile = e >> 8, r = (e >> 4) & 15, c = e & 15;
@@ -388,10 +392,12 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
 #pragma unroll
         for (int e = 0; e < RPT; ++e) {
             const int p = tid + NT * e;
-            if (NT * (e + 1) <= 512 || p < 512) {
-                __bf16* dt = &Ts[(p >> 3) * LT];  // permuted rows
-                *reinterpret_cast<uint2*>(dt + pcol((p & 7) * 8)) = make_uint2(tnext[e].x, tnext[e].y);
-                *reinterpret_cast<uint2*>(dt + pcol((p & 7) * 8 + 4)) = make_uint2(tnext[e].z, tnext[e].w);
+            if (NT * (e + 1) <= kRecPieces || p < kRecPieces) {
+                int row, col;
+                dchunk::rec_piece(p, row, col);
+                __bf16* dt = &Ts[row * LT];  // permuted rows
+                *reinterpret_cast<uint2*>(dt + pcol(col)) = make_uint2(tnext[e].x, tnext[e].y);
+                *reinterpret_cast<uint2*>(dt + pcol(col + 4)) = make_uint2(tnext[e].z, tnext[e].w);
             }
         }
         if (tid < CH) {  // wave 0
