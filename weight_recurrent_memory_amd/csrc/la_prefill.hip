@@ -32,6 +32,7 @@ namespace {
 
 constexpr int CH = kChunk;
 constexpr int NTHR = 256;  // four waves; wave w owns query rows 16w..16w+15
+constexpr unsigned kResidentGroups = 512;  // la_fused workgroups resident at once: two per CU, 256 CUs
 
 template <typename TIn, int DK, int DV>
 struct Layout {
@@ -543,11 +544,22 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
         seg = vs - sm.seg_base<PACKED>(nseq);
     }
     const int G = sm.segs<PACKED>(nseq);                        // segments of this sequence
-    // Later segments sum more predecessors in the look-back, so they sit on
-    // the kernel's critical path: their waves get a higher issue priority
-    // (by quarter of the sequence), which measured about 3 % faster.
-    {
-        const int quarter = (4 * seg) / (G > 0 ? G : 1);
+    // Issue priorities.  Uniform batches dispatch segment-major, so about
+    // 512 / (N H) consecutive segments of each sequence are resident at once;
+    // while computing its aggregate, a segment early in that window runs
+    // first (the later ones will wait for its aggregate).  Once it has
+    // published, later segments of the sequence (by quarter) run first: they
+    // sum more predecessors in the look-back and sit on the critical path.
+    // (Measured on B=1 H=32 T=65536: 283.4 -> 274.5 us; the post-publish
+    // scheme alone had measured about 3 % before the per-phase split.)
+    const int quarter = (4 * seg) / (G > 0 ? G : 1);
+    if constexpr (!PACKED) {
+        const int win = (int)(kResidentGroups / (unsigned)(sm.N * sm.H));
+        const int pos = win >= 4 ? (4 * (seg % win)) / win : 0;  // quarter of the resident window
+        if (pos == 0) __builtin_amdgcn_s_setprio(3);
+        else if (pos == 1) __builtin_amdgcn_s_setprio(2);
+        else if (pos == 2) __builtin_amdgcn_s_setprio(1);
+    } else {
         if (quarter >= 3) __builtin_amdgcn_s_setprio(3);
         else if (quarter == 2) __builtin_amdgcn_s_setprio(2);
         else if (quarter == 1) __builtin_amdgcn_s_setprio(1);
@@ -602,6 +614,12 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
                 S[i][c][r] = seg == 0 ? x : 0.f;
             }
     using PUB = Published<DK, DV>;
+    if constexpr (!PACKED) {
+        if (quarter >= 3) __builtin_amdgcn_s_setprio(3);
+        else if (quarter == 2) __builtin_amdgcn_s_setprio(2);
+        else if (quarter == 1) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+    }
     if (seg > 0 && seg + 1 < G) {
         PUB::store(agg + (sbase + seg) * E, A, w, lane);
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -807,7 +825,7 @@ LaPlan la_plan(int HT, int T, int dk, int dv) {
     // 11, 13, 14): five of the chunks are kept, and shorter workgroups leave
     // a shorter tail.
     const int nch = (T + CH - 1) / CH;
-    const long occ = ((long)nch * HT) / 512;
+    const long occ = ((long)nch * HT) / kResidentGroups;
     const long cap = (dk == 64 && dv == 64) ? 12 : (256L * 1024) / ((long)(dk + dv) * 2 * CH);
     long cps = occ < cap ? occ : cap;
     if (cps < 1) cps = 1;
