@@ -73,6 +73,13 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ v4u buf_load16(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
+// Cache policy of a load: 0 default; kLastUse (non-temporal) for data read
+// for the last time, so its lines are the first the L2 gives up.
+constexpr int kLastUse = 2;
+template <int CP>
+__device__ __forceinline__ v4u buf_load16_cp(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CP);
+}
 // Streaming 16-byte store for results this kernel never reads: non-temporal
 // and written through the L2 (cache policy sc1 | nt), so output lines do not
 // stay dirty in the L2 beside the input stream.  On the LA prefill this
@@ -270,13 +277,14 @@ struct ChunkRegs {
     }
     // Same rows through a buffer resource: rows past the resource's end read
     // as zero (no row guard, no branch).
+    template <int CP = 0>
     __device__ __forceinline__ void load_buf(rsrc_t rs, int c0, int tid) {
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
             const int idx = j * NT + tid;
             const int row = idx / (D / VEC);
             const int col = (idx % (D / VEC)) * VEC;
-            const v4u x = buf_load16(rs, (uint32_t)(((c0 + row) * D + col) * (int)sizeof(TIn)));
+            const v4u x = buf_load16_cp<CP>(rs, (uint32_t)(((c0 + row) * D + col) * (int)sizeof(TIn)));
             r[j] = make_uint4(x[0], x[1], x[2], x[3]);
         }
     }
