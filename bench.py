@@ -67,14 +67,14 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COUNTERS = {
     # workload name -> kernel, sources, sha256 of the sources, KiB per dispatch
     "la_bf16_b1_h32_t65536_d64": {"kernel": "la_fused_kernel", "sources": LA_SOURCES,
-                                  "sha256": "fab69b1bf364bf487f63338bf6ab6cf4e868c1a606d17edde24d34a84c2de83a",
-                                  "fetch_kib": 574223.5, "write_kib": 350713.0},
+                                  "sha256": "d274b94b6ae4b8ea7a55c784428c859fa796faa876002cc2b2f085c4509dcb51",
+                                  "fetch_kib": 574383.5, "write_kib": 350713.0},
     "la_bf16_b4_h8_t8192_d64": {"kernel": "la_fused_kernel", "sources": LA_SOURCES,
-                                "sha256": "fab69b1bf364bf487f63338bf6ab6cf4e868c1a606d17edde24d34a84c2de83a",
-                                "fetch_kib": 66476.6, "write_kib": 48397.0},
+                                "sha256": "d274b94b6ae4b8ea7a55c784428c859fa796faa876002cc2b2f085c4509dcb51",
+                                "fetch_kib": 66447.6, "write_kib": 48397.0},
     "decode_bf16_n256_h32_d128_1000steps": {"kernel": "la_decode_kernel", "sources": LA_DECODE_SOURCES,
-                                            "sha256": "6a650c38b901f6bae18a1c386b5cc801e3311568291c7a03399c545612d14728",
-                                            "fetch_kib": 267307.1, "write_kib": 530464.7},
+                                            "sha256": "3f6ff15dd06ccadb10a9e713196c85c9a832099ca4ea57f6b52e4ba8e306e996",
+                                            "fetch_kib": 267307.3, "write_kib": 530467.0},
 }
 
 
