@@ -373,10 +373,11 @@ __global__ __launch_bounds__(NT) void dlb_grad_kernel(
         const int c0_ = (int)(c % NC) * CH, n_ = min(CH, T - c0_);
         const long r0 = (c / NC) * T + c0_;
         tnext = dchunk::load_rec(trec + c * dchunk::kRecElems, tid);
-        kr.load_buf(make_rsrc(k + r0 * DK, (uint32_t)n_ * DK * 2), 0, tid);
-        qr.load_buf(make_rsrc(q + r0 * DK, (uint32_t)n_ * DK * 2), 0, tid);
-        vr.load_buf(make_rsrc(v + r0 * DV, (uint32_t)n_ * DV * 2), 0, tid);
-        orr.load_buf(make_rsrc(dO + r0 * DV, (uint32_t)n_ * DV * 2), 0, tid);
+        // the last reads of these rows: non-temporal
+        kr.template load_buf<kLastUse>(make_rsrc(k + r0 * DK, (uint32_t)n_ * DK * 2), 0, tid);
+        qr.template load_buf<kLastUse>(make_rsrc(q + r0 * DK, (uint32_t)n_ * DK * 2), 0, tid);
+        vr.template load_buf<kLastUse>(make_rsrc(v + r0 * DV, (uint32_t)n_ * DV * 2), 0, tid);
+        orr.template load_buf<kLastUse>(make_rsrc(dO + r0 * DV, (uint32_t)n_ * DV * 2), 0, tid);
         if (tid < CH) {
             bnext = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(beta + r0, (uint32_t)n_ * 2), (uint32_t)tid * 2, 0, 0);
             if constexpr (GATED)

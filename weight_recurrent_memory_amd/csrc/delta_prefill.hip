@@ -329,9 +329,11 @@ __global__ __launch_bounds__(NWV * 64) void delta_chunk_kernel(
     constexpr int RPT = (kRecPieces + NT - 1) / NT;  // 16-byte pieces of a T record per thread
     uint4 tnext[RPT];  // this thread's pieces of the chunk's T record
     auto load_chunk = [&](int c, int tid) {
-        kr.load_buf(rk, c, tid);
-        if constexpr (OUT) qr.load_buf(rq, c, tid);
-        vr.load_buf(rv, c, tid);
+        // the output pass reads its rows for the last time: non-temporal
+        constexpr int CP = OUT ? kLastUse : 0;
+        kr.template load_buf<CP>(rk, c, tid);
+        if constexpr (OUT) qr.template load_buf<CP>(rq, c, tid);
+        vr.template load_buf<CP>(rv, c, tid);
         const long rec = sm.chunk_rec<PACKED>(nseq, h, c / CH, CH) * kRecElems;
 #pragma unroll
         for (int e = 0; e < RPT; ++e)  // kRecPieces x 16 bytes: one record
