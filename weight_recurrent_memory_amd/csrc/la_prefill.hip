@@ -200,7 +200,7 @@ struct LdsKept {
 // per chunk suffices; rows at or past t1 read as zero through the buffer
 // resources.  The order of the sum is fixed, so results do not depend on
 // timing.
-template <typename TIn, int DK, int DV>
+template <typename TIn, int DK, int DV, bool KEEP_LAST>
 __device__ __forceinline__ void aggregate_keep(const TIn* kh, const TIn* vh, int t0, int t1,
                                                v4f (&acc)[Layout<TIn, DK, DV>::RTW][Layout<TIn, DK, DV>::NCT],
                                                typename Mma<TIn>::op_t* Kb, typename Mma<TIn>::op_t* Vb,
@@ -228,8 +228,13 @@ __device__ __forceinline__ void aggregate_keep(const TIn* kh, const TIn* vh, int
             if (c == t0 + GS) LdsKept<TIn, DK, DV>::put(keep_lds, kept.k[0], kept.v[0], tid);
         }
         if constexpr (decltype(reload)::value) {
-            kept.k[sl].load_buf(rk, c - GS, tid);
-            kept.v[sl].load_buf(rv, c - GS, tid);
+            if (KEEP_LAST && c - GS < t0 + GS) {  // the kept first group: its last read from memory
+                kept.k[sl].template load_buf<kLastUse>(rk, c - GS, tid);
+                kept.v[sl].template load_buf<kLastUse>(rv, c - GS, tid);
+            } else {
+                kept.k[sl].load_buf(rk, c - GS, tid);
+                kept.v[sl].load_buf(rv, c - GS, tid);
+            }
         }
         __syncthreads();
         add_staged<TIn, DK, DV>(Ks, Vs, acc, lane, w);
@@ -507,9 +512,10 @@ __device__ __forceinline__ void output_pass(rsrc_t rq, rsrc_t rk, rsrc_t rv, rsr
     }
 }
 
-// CP: cache policy of the output pass's loads (the last reads of q, and of
-// the keys and values not kept from the aggregate pass).
-template <typename TIn, int DK, int DV, bool PACKED, int CP>
+// The output pass's loads (the last reads of q, and of the keys and values
+// not kept from the aggregate pass) are non-temporal; with KEEP_LAST so are
+// the aggregate pass's loads of the chunks it keeps.
+template <typename TIn, int DK, int DV, bool PACKED, bool KEEP_LAST>
 __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ q,
                                                         const TIn* __restrict__ k,
                                                         const TIn* __restrict__ v,
@@ -590,7 +596,7 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
 #pragma unroll
         for (int c = 0; c < NCT; ++c) A[i][c] = zero4();
     KeptChunks<TIn, DK, DV> kept;
-    aggregate_keep<TIn, DK, DV>(kh, vh, t_beg, t_end, A, Kb, Vb, kept, keep_lds, tid);
+    aggregate_keep<TIn, DK, DV, KEEP_LAST>(kh, vh, t_beg, t_end, A, Kb, Vb, kept, keep_lds, tid);
 
     // The first chunk's queries are fetched now, so their latency overlaps
     // the look-back.  Buffer resources end at the segment end: reads
@@ -599,6 +605,7 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
     const rsrc_t rk = make_rsrc(kh, (uint32_t)t_end * DK * sizeof(TIn));
     const rsrc_t rv = make_rsrc(vh, (uint32_t)t_end * DV * sizeof(TIn));
     const rsrc_t ro = make_rsrc(o + row0 * DV, (uint32_t)t_end * DV * sizeof(TIn));
+    constexpr int CP = kLastUse;
     OutChunk<TIn, DK, DV, CP> first;
     first.load_q(rq, t_beg, w, tid);
 
@@ -809,14 +816,14 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    // When every (head, segment) workgroup is resident at once, the output
-    // pass's loads are the last reads of their rows and are marked so, which
-    // keeps the L2 for the keys and values still to be re-read (measured on
-    // B=4 H=8 T=8192: 44.7 -> 42.2 us; with several rounds of workgroups,
-    // as on T=65536, the default policy measured 0.5-1 % faster).
+    // Last reads are non-temporal, so the L2 keeps the keys and values still
+    // to be read again (measured, ten interleaved rounds each: B=4 H=8
+    // T=8192 44.7 -> 42.2 us per call with the output pass's loads so marked;
+    // B=1 H=32 T=65536 275.7 -> 270.8 us with the kept chunks' loads too,
+    // which cost 3 % where every workgroup is resident at once).
     const bool one_round = slots <= (long)kResidentGroups;
-    auto kern = sm.packed() ? (one_round ? la_fused_kernel<TIn, DK, DV, true, kLastUse> : la_fused_kernel<TIn, DK, DV, true, 0>)
-                            : (one_round ? la_fused_kernel<TIn, DK, DV, false, kLastUse> : la_fused_kernel<TIn, DK, DV, false, 0>);
+    auto kern = sm.packed() ? (one_round ? la_fused_kernel<TIn, DK, DV, true, false> : la_fused_kernel<TIn, DK, DV, true, true>)
+                            : (one_round ? la_fused_kernel<TIn, DK, DV, false, false> : la_fused_kernel<TIn, DK, DV, false, true>);
     kern<<<dim3((unsigned)slots), dim3(NTHR), 0, stream>>>(
         static_cast<const TIn*>(q), static_cast<const TIn*>(k), static_cast<const TIn*>(v), S0, z0,
         static_cast<TIn*>(o), S_out, z_out, flags, (flag_t)tag, agg, incl, sm, eps, poll_limit);
