@@ -67,14 +67,14 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COUNTERS = {
     # workload name -> kernel, sources, sha256 of the sources, KiB per dispatch
     "la_bf16_b1_h32_t65536_d64": {"kernel": "la_fused_kernel", "sources": LA_SOURCES,
-                                  "sha256": "1f1ce9e1690bb45e8d5d51eaecec663a8f61d2baee011e46e16378cc9ff259b8",
-                                  "fetch_kib": 572142.2, "write_kib": 350713.0},
+                                  "sha256": "dea79e9da54a16e00c32689de5d002d36447d767b570acbf82e9d40877a9f156",
+                                  "fetch_kib": 572178.1, "write_kib": 350713.0},
     "la_bf16_b4_h8_t8192_d64": {"kernel": "la_fused_kernel", "sources": LA_SOURCES,
-                                "sha256": "1f1ce9e1690bb45e8d5d51eaecec663a8f61d2baee011e46e16378cc9ff259b8",
-                                "fetch_kib": 66410.4, "write_kib": 48397.0},
+                                "sha256": "dea79e9da54a16e00c32689de5d002d36447d767b570acbf82e9d40877a9f156",
+                                "fetch_kib": 66439.5, "write_kib": 48397.0},
     "decode_bf16_n256_h32_d128_1000steps": {"kernel": "la_decode_kernel", "sources": LA_DECODE_SOURCES,
                                             "sha256": "3f6ff15dd06ccadb10a9e713196c85c9a832099ca4ea57f6b52e4ba8e306e996",
-                                            "fetch_kib": 267307.1, "write_kib": 530464.7},
+                                            "fetch_kib": 267306.9, "write_kib": 530466.8},
 }
 
 

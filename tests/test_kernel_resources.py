@@ -22,11 +22,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # (source, mangled-name prefix, minimum waves per SIMD)
 BUDGETS = [
     # linear attention, bf16, dk = dv = 64: two four-wave workgroups per CU
-    # (uniform and packed batches, kept chunks' loads non-temporal or not)
-    ("la_prefill.hip", "_ZN2la12_GLOBAL__N_115la_fused_kernelItLi64ELi64ELb0ELb0E", 2),
-    ("la_prefill.hip", "_ZN2la12_GLOBAL__N_115la_fused_kernelItLi64ELi64ELb0ELb1E", 2),
-    ("la_prefill.hip", "_ZN2la12_GLOBAL__N_115la_fused_kernelItLi64ELi64ELb1ELb0E", 2),
-    ("la_prefill.hip", "_ZN2la12_GLOBAL__N_115la_fused_kernelItLi64ELi64ELb1ELb1E", 2),
+    # (uniform batches with the two last-read policies, packed batches)
+    ("la_prefill.hip", "_ZN2la12_GLOBAL__N_115la_fused_kernelItLi64ELi64ELb0ELi1E", 2),
+    ("la_prefill.hip", "_ZN2la12_GLOBAL__N_115la_fused_kernelItLi64ELi64ELb0ELi2E", 2),
+    ("la_prefill.hip", "_ZN2la12_GLOBAL__N_115la_fused_kernelItLi64ELi64ELb1ELi0E", 2),
     # delta rule, dk = dv = 128: T pass four eight-wave workgroups per CU,
     # map pass one sixteen-wave workgroup, output and state passes one
     # eight-wave workgroup

@@ -512,10 +512,11 @@ __device__ __forceinline__ void output_pass(rsrc_t rq, rsrc_t rk, rsrc_t rv, rsr
     }
 }
 
-// The output pass's loads (the last reads of q, and of the keys and values
-// not kept from the aggregate pass) are non-temporal; with KEEP_LAST so are
-// the aggregate pass's loads of the chunks it keeps.
-template <typename TIn, int DK, int DV, bool PACKED, bool KEEP_LAST>
+// Cache policy of last reads (POL): 0 default; 1 the output pass's loads
+// (the last reads of q, and of the keys and values not kept from the
+// aggregate pass) non-temporal; 2 also the aggregate pass's loads of the
+// chunks it keeps.
+template <typename TIn, int DK, int DV, bool PACKED, int POL>
 __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ q,
                                                         const TIn* __restrict__ k,
                                                         const TIn* __restrict__ v,
@@ -596,7 +597,7 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
 #pragma unroll
         for (int c = 0; c < NCT; ++c) A[i][c] = zero4();
     KeptChunks<TIn, DK, DV> kept;
-    aggregate_keep<TIn, DK, DV, KEEP_LAST>(kh, vh, t_beg, t_end, A, Kb, Vb, kept, keep_lds, tid);
+    aggregate_keep<TIn, DK, DV, POL == 2>(kh, vh, t_beg, t_end, A, Kb, Vb, kept, keep_lds, tid);
 
     // The first chunk's queries are fetched now, so their latency overlaps
     // the look-back.  Buffer resources end at the segment end: reads
@@ -605,7 +606,7 @@ __global__ __launch_bounds__(NTHR) void la_fused_kernel(const TIn* __restrict__ 
     const rsrc_t rk = make_rsrc(kh, (uint32_t)t_end * DK * sizeof(TIn));
     const rsrc_t rv = make_rsrc(vh, (uint32_t)t_end * DV * sizeof(TIn));
     const rsrc_t ro = make_rsrc(o + row0 * DV, (uint32_t)t_end * DV * sizeof(TIn));
-    constexpr int CP = kLastUse;
+    constexpr int CP = POL >= 1 ? kLastUse : 0;
     OutChunk<TIn, DK, DV, CP> first;
     first.load_q(rq, t_beg, w, tid);
 
@@ -816,14 +817,17 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    // Last reads are non-temporal, so the L2 keeps the keys and values still
-    // to be read again (measured, ten interleaved rounds each: B=4 H=8
-    // T=8192 44.7 -> 42.2 us per call with the output pass's loads so marked;
-    // B=1 H=32 T=65536 275.7 -> 270.8 us with the kept chunks' loads too,
-    // which cost 3 % where every workgroup is resident at once).
+    // Last reads non-temporal, so the L2 keeps the keys and values still to
+    // be read again -- chosen by measurement (interleaved rounds, per call):
+    // uniform batches with every workgroup resident at once (B=4 H=8 T=8192)
+    // 44.7 -> 42.2 us with the output pass's loads so marked, the kept
+    // chunks' loads too costing 3 %; uniform batches over several rounds
+    // (B=1 H=32 T=65536) 275.6 -> 268.5 us with both; the packed serving
+    // batch (48 requests, 32768 tokens x 8 heads) 58 -> 62.5 us with both,
+    // so packed batches keep the default policy.
     const bool one_round = slots <= (long)kResidentGroups;
-    auto kern = sm.packed() ? (one_round ? la_fused_kernel<TIn, DK, DV, true, false> : la_fused_kernel<TIn, DK, DV, true, true>)
-                            : (one_round ? la_fused_kernel<TIn, DK, DV, false, false> : la_fused_kernel<TIn, DK, DV, false, true>);
+    auto kern = sm.packed() ? la_fused_kernel<TIn, DK, DV, true, 0>
+                            : (one_round ? la_fused_kernel<TIn, DK, DV, false, 1> : la_fused_kernel<TIn, DK, DV, false, 2>);
     kern<<<dim3((unsigned)slots), dim3(NTHR), 0, stream>>>(
         static_cast<const TIn*>(q), static_cast<const TIn*>(k), static_cast<const TIn*>(v), S0, z0,
         static_cast<TIn*>(o), S_out, z_out, flags, (flag_t)tag, agg, incl, sm, eps, poll_limit);
