@@ -25,7 +25,10 @@ printed is one JSON object:
   decode chains of the other three rules -- each with its own roofline
   fraction.
 
-Timing: after the warm-up calls, K calls enqueued back to back between one
+Timing: after the warm-up calls (by default enough to bring a cold device
+to its steady clocks; the secondary workloads warm up for at least 60 ms,
+and nothing idles the device between the warm-up and the timed calls), K
+calls enqueued back to back between one
 HIP event pair on the launch stream give the wall-clock throughput and the
 average launch duration (what a kernel trace of the calls averages); K more
 calls, each bracketed by its own event pair, give the median per call.
@@ -51,6 +54,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFS = 2516.6  # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
 METRIC = "prefill tokens/sec (MFMA % peak); decode state-update GB/s (% HBM peak)"
+# Warm-up floor of the secondary workloads: a device that idled for a few
+# milliseconds (input generation, the previous workload's bookkeeping) drops
+# its clocks, and some 50 ms of sustained load bring them back.
+WARM_S = 0.06
 
 # Counter readings per (kernel, workload): rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE (KiB per dispatch, mean over the dispatches of the command in
@@ -140,10 +147,13 @@ def ssd_decode_bytes(N, H, dk, dv, el):
     return N * H * (2 * dk * dv * 4 + (2 * dk + dv) * el + 4 + dv * el)
 
 
-def time_calls(fn, n_calls, warmup, stream):
-    """Run fn(i) warmup + 2 n_calls times.  Returns (wall seconds of the
-    first n_calls timed calls, mean device time per call in ms over that
-    region, and the mean and median of per-call device times in ms).
+def time_calls(fn, n_calls, warmup, stream, warm_s=0.0):
+    """Run fn(i) warmup + 2 n_calls times (more warm-up calls, in groups of
+    ten, while less than warm_s seconds of warm-up have run: the secondary
+    workloads' calls are short, and a fixed count of them would not bring the
+    device back to its steady clocks).  Returns (wall seconds of the first
+    n_calls timed calls, mean device time per call in ms over that region,
+    and the mean and median of per-call device times in ms).
 
     The first timed pass enqueues the calls back to back between one pair of
     HIP events on the launch stream: its wall time is the throughput figure
@@ -153,17 +163,24 @@ def time_calls(fn, n_calls, warmup, stream):
     pass brackets each call with its own event pair, for the median of at
     least 20 repetitions; each pair adds a few microseconds of its own, so
     those per-call figures run a little above the trace's."""
-    for i in range(warmup):
-        fn(i)
-    torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
     # A garbage-collection pause while the calls are being queued would leave
-    # the device idle inside the timed region.
+    # the device idle inside the timed region; it is taken before the warm-up,
+    # so that only the synchronisation separates the warm-up from the timed
+    # calls (an idle device drops its clocks within milliseconds).
     gc_was_on = gc.isenabled()
     gc.collect()
     gc.disable()
     try:
+        t0 = time.perf_counter()
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        while time.perf_counter() - t0 < warm_s:
+            for i in range(10):
+                fn(i)
+            torch.cuda.synchronize()
         t0 = time.perf_counter()
         start.record(stream)
         for i in range(n_calls):
@@ -184,7 +201,7 @@ def time_calls(fn, n_calls, warmup, stream):
     return wall, start.elapsed_time(end) / n_calls, sum(d) / len(d), med
 
 
-def bench_la(w, steps, warmup, copies, lin, wl):
+def bench_la(w, steps, warmup, copies, lin, wl, warm_s=0.0):
     dev = torch.device("cuda:0")
     el = 2 if w.dtype == torch.bfloat16 else 4
     sets = [wl.la_inputs(w.B, w.H, w.T, w.dk, w.dv, w.dtype, w.seed + 17 * i, dev) for i in range(copies)]
@@ -198,7 +215,7 @@ def bench_la(w, steps, warmup, copies, lin, wl):
         lin.la_forward(q, k, v, eps=1e-6, o=outs[i % copies], S_out=S, z_out=z, workspace=ws)
 
     stream = torch.cuda.current_stream(dev)
-    wall, mean_ms, pc_mean, med_ms = time_calls(step, steps, warmup, stream)
+    wall, mean_ms, pc_mean, med_ms = time_calls(step, steps, warmup, stream, warm_s)
     nbytes = la_bytes(w.B, w.H, w.T, w.dk, w.dv, el)
     return {
         "wall_s": wall, "ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "event_ms_mean_per_call": pc_mean,
@@ -228,7 +245,7 @@ def bench_delta(w, steps, warmup, copies, lin, wl):
             q, k, v, beta = sets[i % copies]
             lin.delta_forward(q, k, v, beta, o=outs[i % copies], S_out=S, workspace=ws)
 
-    wall, mean_ms, pc_mean, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
+    wall, mean_ms, pc_mean, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev), WARM_S)
     nbytes = delta_bytes(w.B, w.H, w.T, w.dk, w.dv, el, gated)
     fl = delta_flops(w.B, w.H, w.T, w.dk, w.dv)
     return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "event_ms_mean_per_call": pc_mean, "tokens_per_s": w.B * w.T * steps / wall,
@@ -249,7 +266,7 @@ def bench_ssd(w, steps, warmup, copies, lin, wl):
         q, k, v, alpha = sets[i % copies]
         lin.ssd_forward(q, k, v, alpha, o=outs[i % copies], S_out=S, workspace=ws)
 
-    wall, mean_ms, pc_mean, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
+    wall, mean_ms, pc_mean, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev), WARM_S)
     nbytes = ssd_bytes(w.B, w.H, w.T, w.dk, w.dv, el)
     fl = ssd_flops(w.B, w.H, w.T, w.dk, w.dv)
     return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "event_ms_mean_per_call": pc_mean, "tokens_per_s": w.B * w.T * steps / wall,
@@ -267,7 +284,7 @@ def bench_ssd_decode(w, lin, wl, n_steps=None):
         j = i % w.T
         lin.ssd_decode_step(Q[j], K[j], V[j], At[j], S, o=o)
 
-    wall, mean_ms, pc_mean, med_ms = time_calls(step, n, 10, torch.cuda.current_stream(dev))
+    wall, mean_ms, pc_mean, med_ms = time_calls(step, n, 10, torch.cuda.current_stream(dev), WARM_S)
     per = ssd_decode_bytes(w.B, w.H, w.dk, w.dv, 2)
     return {"steps": n, "ms_per_step": 1e3 * wall / n, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "event_ms_mean_per_call": pc_mean, "bytes_per_step": per,
             "gbs_wall": per * n / wall / 1e9, "gbs": per / (mean_ms * 1e-3) / 1e9}
@@ -291,7 +308,7 @@ def bench_la_backward(w, steps, warmup, copies, lin, wl):
         dq, dk, dv = grads[i % copies]
         lin.la_backward(q, k, v, dO, eps=1e-6, dq=dq, dk=dk, dv=dv, return_state_grads=False, workspace=ws)
 
-    wall, mean_ms, pc_mean, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
+    wall, mean_ms, pc_mean, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev), WARM_S)
     nbytes = la_backward_bytes(w.B, w.H, w.T, w.dk, w.dv, 2)
     return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "event_ms_mean_per_call": pc_mean, "tokens_per_s": w.B * w.T * steps / wall,
             "bytes": nbytes, "gbs": nbytes / (mean_ms * 1e-3) / 1e9}
@@ -322,7 +339,7 @@ def bench_delta_backward(w, steps, warmup, copies, lin, wl):
         dq, dk, dv = grads[i % copies]
         lin.delta_backward(q, k, v, beta, dO, alpha, dq=dq, dk=dk, dv=dv, return_state_grad=False, workspace=ws)
 
-    wall, mean_ms, pc_mean, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
+    wall, mean_ms, pc_mean, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev), WARM_S)
     nbytes = delta_backward_bytes(w.B, w.H, w.T, w.dk, w.dv, 2, gated)
     return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "event_ms_mean_per_call": pc_mean, "tokens_per_s": w.B * w.T * steps / wall,
             "bytes": nbytes, "gbs": nbytes / (mean_ms * 1e-3) / 1e9}
@@ -369,7 +386,7 @@ def bench_delta_train(w, steps, warmup, copies, lin, wl):
     stream = torch.cuda.current_stream(dev)
     res = {}
     for name, fn in (("separate", separate), ("training_pair", paired), ("forward_train", forward_only)):
-        wall, mean_ms, pc_mean, med_ms = time_calls(fn, steps, warmup, stream)
+        wall, mean_ms, pc_mean, med_ms = time_calls(fn, steps, warmup, stream, WARM_S)
         res[name] = {"ms_per_step": 1e3 * wall / steps, "us_per_step": 1e3 * mean_ms,
                      "us_per_step_median": 1e3 * med_ms, "tokens_per_s": w.B * w.T * steps / wall}
     res["backward_after_forward_us"] = res["training_pair"]["us_per_step"] - res["forward_train"]["us_per_step"]
@@ -389,7 +406,7 @@ def bench_la_packed(w, steps, warmup, lin, wl):
     def step(i):
         lin.la_forward_packed(q, k, v, cu_dev, eps=1e-6, cu_seqlens_host=cu, o=o, S_out=S, z_out=z, workspace=ws)
 
-    wall, mean_ms, pc_mean, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev))
+    wall, mean_ms, pc_mean, med_ms = time_calls(step, steps, warmup, torch.cuda.current_stream(dev), WARM_S)
     nbytes = la_bytes(1, w.H, w.T, w.dk, w.dv, 2) + (w.B - 1) * w.H * (w.dk * w.dv + w.dk) * 4
     lengths = (cu[1:] - cu[:-1]).tolist()
     return {"ms_per_step": 1e3 * wall / steps, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "event_ms_mean_per_call": pc_mean, "tokens_per_s": w.T * steps / wall,
@@ -406,7 +423,7 @@ def bench_decode(w, lin, wl, n_steps=None):
     def step(i):
         lin.la_decode_step(Q[i % w.T], K[i % w.T], V[i % w.T], S, z, eps=1e-6, o=o)
 
-    wall, mean_ms, pc_mean, med_ms = time_calls(step, n, 10, torch.cuda.current_stream(dev))
+    wall, mean_ms, pc_mean, med_ms = time_calls(step, n, 10, torch.cuda.current_stream(dev), WARM_S)
     per = decode_bytes(w.B, w.H, w.dk, w.dv, 2)
     return {"steps": n, "ms_per_step": 1e3 * wall / n, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "event_ms_mean_per_call": pc_mean, "bytes_per_step": per,
             "gbs_wall": per * n / wall / 1e9, "gbs": per / (mean_ms * 1e-3) / 1e9}
@@ -430,7 +447,7 @@ def bench_delta_decode(w, lin, wl, n_steps=None):
         else:
             lin.delta_decode_step(Q[j], K[j], V[j], Bt[j], S, o=o)
 
-    wall, mean_ms, pc_mean, med_ms = time_calls(step, n, 10, torch.cuda.current_stream(dev))
+    wall, mean_ms, pc_mean, med_ms = time_calls(step, n, 10, torch.cuda.current_stream(dev), WARM_S)
     per = delta_decode_bytes(w.B, w.H, w.dk, w.dv, 2, gated)
     return {"steps": n, "ms_per_step": 1e3 * wall / n, "event_ms_mean": mean_ms, "event_ms_median": med_ms, "event_ms_mean_per_call": pc_mean, "bytes_per_step": per,
             "gbs_wall": per * n / wall / 1e9, "gbs": per / (mean_ms * 1e-3) / 1e9}
@@ -524,8 +541,13 @@ def hbm_roofline(nbytes, r, workload, kernel):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=10)
+    # A cold device takes about 100 back-to-back launches (some 30 ms of
+    # sustained load) to reach its steady clocks: on the long-stream
+    # workload groups of ten launches measured 524, 321, 309, 294, 280 ... us
+    # each, then 262-268 us from the ninth group on.  The default warm-up
+    # covers that, so the timed steps measure the sustained rate.
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--only", choices=["all", "la", "la_long", "la_packed", "la_backward", "delta", "gated_delta",
                                        "delta_backward", "delta_train", "copy", "ssd", "decode", "delta_decode",
                                        "gated_delta_decode", "ssd_decode"],
@@ -561,7 +583,7 @@ def main():
         dec_res = bench_decode(wl.DECODE_BF16, lin, wl, args.decode_steps)
     if args.only in ("all", "la"):
         w = wl.LA_BF16_PREFILL
-        r = bench_la(w, max(20, args.steps), args.warmup, 4, lin, wl)
+        r = bench_la(w, max(20, args.steps), args.warmup, 4, lin, wl, WARM_S)
         extra[w.name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
                          "roofline": hbm_roofline(r["bytes"], r, w.name, "la_fused_kernel<bf16, 64, 64>"),
                          "mfma_tflops": r["tflops"], "mfma_frac": r["tflops"] / BF16_MFMA_PEAK_TFS}
